@@ -1,0 +1,212 @@
+"""Planted mistakes in the oracle must each fail at least one pin (CPU only).
+
+Each mutant below is a plausible slip -- a dropped term, an off-by-one, a
+wrong sign or index, a transposed operand -- patched into the oracle for the
+duration of one test.  ``pin_battery`` runs a fast subset of the pins of
+test_oracle_levels.py and test_oracle_forms.py through the (patched) module
+attributes and reports which ones fail.  The unpatched oracle passes all.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from fenwick_tree_hierarchical_amd.workloads import WORKLOADS, make_inputs
+from oracle import forms, levels, metrics, special
+
+
+def _inputs(T, d=3, variant=None, seed=11):
+    x = make_inputs(WORKLOADS["tiny_f32"], B=1, H=1, T=T, variant=variant, seed=seed)
+    g = torch.Generator().manual_seed(seed)
+    # d_k == d_v on purpose, so that a transposed state still type-checks.
+    x["q"] = torch.randn(1, 1, T, d, generator=g)
+    x["k"] = torch.randn(1, 1, T, d, generator=g)
+    x["v"] = torch.randn(1, 1, T, d, generator=g)
+    return x
+
+
+def pin_battery():
+    fails = []
+    # levels: two derivations
+    if not np.array_equal(levels.level_table_walk(64), levels.level_table(64)):
+        fails.append("walk_vs_closed")
+    # brute force (walk buckets, explicit gate product)
+    x = _inputs(13)
+    xn = {k: v.double().numpy() for k, v in x.items()}
+    bf = special.brute_force(xn["q"][0, 0], xn["k"][0, 0], xn["v"][0, 0], np.exp(xn["log_a"][0, 0]),
+                             xn["lam"][0, 0])
+    oq = forms.forward_quadratic(x["q"], x["k"], x["v"], x["log_a"], x["lam"])
+    orr, _ = forms.forward_recurrent(x["q"], x["k"], x["v"], x["lam"], log_a=x["log_a"])
+    if not np.allclose(oq[0, 0], bf, rtol=1e-10, atol=1e-12):
+        fails.append("quadratic_vs_brute")
+    if not np.allclose(orr[0, 0], bf, rtol=1e-10, atol=1e-12):
+        fails.append("recurrent_vs_brute")
+    # two forms on a longer sequence
+    x = _inputs(37)
+    oq = forms.forward_quadratic(x["q"], x["k"], x["v"], x["log_a"], x["lam"])
+    orr, _ = forms.forward_recurrent(x["q"], x["k"], x["v"], x["lam"], log_a=x["log_a"])
+    if metrics.rel_l2(orr, oq) > 1e-10:
+        fails.append("quadratic_vs_recurrent")
+    # constant lambda -> Mamba-2
+    x = _inputs(21, variant="const:1.0")
+    ref = special.mamba2(x["q"], x["k"], x["v"], x["log_a"])
+    if metrics.rel_l2(forms.forward_quadratic(x["q"], x["k"], x["v"], x["log_a"], x["lam"]), ref) > 1e-10:
+        fails.append("mamba2_quadratic")
+    if metrics.rel_l2(forms.forward_recurrent(x["q"], x["k"], x["v"], x["lam"], log_a=x["log_a"])[0], ref) > 1e-10:
+        fails.append("mamba2_recurrent")
+    # closed forms on scalars
+    T = 40
+    one = torch.ones(1, 1, T, 1, dtype=torch.float64)
+    L = levels.num_levels(T)
+    alpha = 0.9
+    la = torch.full((1, 1, T), math.log(alpha), dtype=torch.float64)
+    lam1 = torch.ones(1, 1, T, L, dtype=torch.float64)
+    geo = np.array([(1 - alpha ** (t + 1)) / (1 - alpha) for t in range(T)])
+    if not np.allclose(forms.forward_quadratic(one, one, one, la, lam1)[0, 0, :, 0], geo, rtol=1e-10):
+        fails.append("geometric_quadratic")
+    if not np.allclose(forms.forward_recurrent(one, one, one, lam1, log_a=la)[0][0, 0, :, 0], geo, rtol=1e-10):
+        fails.append("geometric_recurrent")
+    lamb = torch.tensor([[0.5 ** lv for lv in range(L)]] * T, dtype=torch.float64)[None, None]
+    z = torch.zeros(1, 1, T, dtype=torch.float64)
+    pc = np.array([1 + bin(t).count("1") / 2 for t in range(T)])
+    if not np.allclose(forms.forward_quadratic(one, one, one, z, lamb)[0, 0, :, 0], pc):
+        fails.append("popcount_quadratic")
+    if not np.allclose(forms.forward_recurrent(one, one, one, lamb, log_a=z)[0][0, 0, :, 0], pc):
+        fails.append("popcount_recurrent")
+    return fails
+
+
+def test_unpatched_oracle_passes_battery():
+    assert pin_battery() == []
+
+
+# ----------------------------------------------------------------- mutants
+_real_table = levels.level_table
+_real_decay = forms.decay_matrix
+_real_step = forms.recurrent_step
+_real_quad = forms.forward_quadratic
+
+
+def m_level_no_plus_one(T, rows=None):
+    tab = _real_table(T, rows).astype(np.int64)
+    return np.where(tab > 0, tab - 1, tab).astype(np.int8)
+
+
+def m_level_one_indexed(T, rows=None):
+    """The rejected textbook 1-indexed reading msb((t+1) xor s)."""
+    t = np.arange(T) if rows is None else np.asarray(rows)
+    s = np.arange(T)
+    x = (t[:, None] + 1) ^ s[None, :]
+    tab = np.floor(np.log2(np.maximum(x, 1))).astype(np.int64)
+    tab[s[None, :] > t[:, None]] = -1
+    return tab.astype(np.int8)
+
+
+def m_decay_includes_own_gate(log_a, rows=None):
+    la = np.asarray(log_a, dtype=np.float64)
+    shifted = np.concatenate([[0.0], np.cumsum(la)[:-1]])      # exclusive cumsum
+    T = la.shape[-1]
+    t = np.arange(T) if rows is None else np.asarray(rows)
+    s = np.arange(T)
+    causal = s[None, :] <= t[:, None]
+    return np.exp(np.where(causal, np.cumsum(la)[t][:, None] - shifted[None, :], -np.inf))
+
+
+def m_decay_sign(log_a, rows=None):
+    m = _real_decay(log_a, rows)
+    with np.errstate(divide="ignore"):
+        return np.where(m > 0, 1.0 / m, 0.0)
+
+
+def m_step_decay_after_output(st, q_t, k_t, v_t, a_t, lam_t):
+    ones = np.ones_like(a_t)
+    o = _real_step(st, q_t, k_t, v_t, ones, lam_t)
+    for lv in range(1, st.slots.shape[1]):
+        st.slots[:, lv] *= 1.0                                    # gate forgotten
+    return o
+
+
+def m_step_wrong_carry(st, q_t, k_t, v_t, a_t, lam_t):
+    t = st.t
+    act = [lv for lv in levels.active_levels(t) if lv >= 1]
+    for lv in act:
+        st.slots[:, lv] *= a_t[:, None, None]
+    o = (lam_t[:, 0] * np.einsum("bi,bi->b", q_t, k_t))[:, None] * v_t
+    for lv in act:
+        o += lam_t[:, lv][:, None] * np.einsum("bij,bi->bj", st.slots[:, lv], q_t)
+    kstar = (t & -t).bit_length() - 1 if t > 0 else 0           # ctz(t) instead of ctz(t+1)
+    merged = np.einsum("bi,bj->bij", k_t, v_t)
+    for lv in range(1, kstar + 1):
+        merged += st.slots[:, lv]
+        st.slots[:, lv] = 0.0
+    st.slots[:, kstar + 1] += merged
+    st.t = t + 1
+    return o
+
+
+def m_step_transposed_state(st, q_t, k_t, v_t, a_t, lam_t):
+    t = st.t
+    act = [lv for lv in levels.active_levels(t) if lv >= 1]
+    for lv in act:
+        st.slots[:, lv] *= a_t[:, None, None]
+    o = (lam_t[:, 0] * np.einsum("bi,bi->b", q_t, k_t))[:, None] * v_t
+    for lv in act:
+        o += lam_t[:, lv][:, None] * np.einsum("bij,bj->bi", st.slots[:, lv], q_t)   # S q, not S^T q
+    kstar = ((t + 1) & -(t + 1)).bit_length() - 1
+    merged = np.einsum("bi,bj->bij", k_t, v_t)
+    for lv in range(1, kstar + 1):
+        merged += st.slots[:, lv]
+        st.slots[:, lv] = 0.0
+    st.slots[:, kstar + 1] = merged
+    st.t = t + 1
+    return o
+
+
+def m_step_drop_level0(st, q_t, k_t, v_t, a_t, lam_t):
+    lam2 = lam_t.copy()
+    lam2[:, 0] = 0.0
+    return _real_step(st, q_t, k_t, v_t, a_t, lam2)
+
+
+def m_quad_lambda_by_key(q, k, v, log_a, lam, rows=None, chunk=None, pair=None, block=1024):
+    lam = forms._f64(lam)
+    B, H, T, L = lam.shape
+    out = np.zeros((B, H, T, forms._f64(v).shape[-1]))
+    qq, kk, vv, la = (forms._f64(x) for x in (q, k, v, log_a))
+    for b in range(B):
+        for h in range(H):
+            lev = levels.level_table(T).astype(np.int64)
+            causal = lev >= 0
+            # weight of the *key's* row instead of the query's
+            mh = np.where(causal, lam[b, h][np.arange(T)[None, :], np.where(causal, lev, 0)], 0.0)
+            out[b, h] = ((qq[b, h] @ kk[b, h].T) * forms.decay_matrix(la[b, h]) * mh) @ vv[b, h]
+    return out
+
+
+def m_quad_transposed_scores(q, k, v, log_a, lam, **kw):
+    return _real_quad(k, q, v, log_a, lam, **kw)
+
+
+MUTANTS = {
+    "level_no_plus_one": (levels, "level_table", m_level_no_plus_one),
+    "level_one_indexed_reading": (levels, "level_table", m_level_one_indexed),
+    "decay_includes_own_gate": (forms, "decay_matrix", m_decay_includes_own_gate),
+    "decay_sign": (forms, "decay_matrix", m_decay_sign),
+    "step_gate_forgotten": (forms, "recurrent_step", m_step_decay_after_output),
+    "step_wrong_carry": (forms, "recurrent_step", m_step_wrong_carry),
+    "step_transposed_state": (forms, "recurrent_step", m_step_transposed_state),
+    "step_drop_level0": (forms, "recurrent_step", m_step_drop_level0),
+    "quad_lambda_by_key": (forms, "forward_quadratic", m_quad_lambda_by_key),
+    "quad_transposed_scores": (forms, "forward_quadratic", m_quad_transposed_scores),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    mod, attr, fn = MUTANTS[name]
+    monkeypatch.setattr(mod, attr, fn)
+    with np.errstate(all="ignore"):
+        fails = pin_battery()
+    assert fails, f"mutant {name} passed every pin"
