@@ -1,0 +1,166 @@
+// C ABI of liblogattn: argument checks on the host, then launches.
+// Every check happens before anything is enqueued; on error nothing runs.
+#include <hip/hip_runtime.h>
+
+#include "../../include/logattn.h"
+#include "la_fwd_impl.hpp"
+#include "la_internal.hpp"
+#include "la_plan.hpp"
+
+using namespace la;
+
+namespace {
+
+int fwd_common(const void* q, const void* k, const void* v, const float* log_a, const float* lambda,
+               void* out, int B, int H, int64_t T, int dk, int dv, int C, int L, int dtype, void* ws,
+               size_t ws_bytes, void* const* events, int n_events, la_stream_t stream) {
+  FwdPlan p;
+  int rc = plan_fwd(B, H, T, dk, dv, C, dtype, L, &p);
+  if (rc != kOK) return rc;
+  if (events && n_events != p.n_stages + 1) return kEINVAL;
+  if (p.n_stages == 0) {   // empty problem: nothing to read or write
+    if (events)
+      for (int i = 0; i < n_events; ++i)
+        if (hipEventRecord((hipEvent_t)events[i], (hipStream_t)stream) != hipSuccess) return kEHIP;
+    return kOK;
+  }
+  if (p.n_groups * p.BH > (int64_t)0x7fffffff) return kESHAPE;
+  if (!q || !k || !v || !log_a || !lambda || !out) return kEINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return kEALIGN;
+  if (!aligned(log_a, 4) || !aligned(lambda, 4)) return kEALIGN;
+  if (p.ws_bytes > 0) {
+    if (!ws || ws_bytes < p.ws_bytes) return kEWORKSPACE;
+    if (!aligned(ws, 256)) return kEALIGN;
+  }
+  char* w = static_cast<char*>(ws);
+  FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.log_a = log_a; a.lam = lambda; a.out = out;
+  a.gstate = p.n_groups > 1 ? reinterpret_cast<float*>(w + p.off_gstate) : nullptr;
+  a.gtot = p.n_groups > 1 ? reinterpret_cast<float*>(w + p.off_gtot) : nullptr;
+  a.gprefix = p.n_groups > 1 ? reinterpret_cast<double*>(w + p.off_gprefix) : nullptr;
+  a.nodes = p.n_groups > 1 ? static_cast<void*>(w + p.off_nodes) : nullptr;
+  a.T = T; a.n_chunks = p.n_chunks; a.n_groups = p.n_groups; a.L = L;
+  const hipEvent_t* ev = reinterpret_cast<const hipEvent_t*>(events);
+  hipStream_t s = (hipStream_t)stream;
+  return dtype == kBF16 ? launch_fwd_bf16(p, a, s, ev) : launch_fwd_f32(p, a, s, ev);
+}
+
+}  // namespace
+
+extern "C" {
+
+LA_API const char* loglinear_strerror(int code) {
+  switch (code) {
+    case LA_OK: return "ok";
+    case LA_EINVAL: return "invalid argument (null pointer or negative count)";
+    case LA_ESHAPE: return "unsupported shape (head dim, chunk size, level count or size limit)";
+    case LA_EDTYPE: return "unsupported dtype code";
+    case LA_EALIGN: return "misaligned pointer";
+    case LA_EWORKSPACE: return "workspace missing or too small";
+    case LA_ECAPACITY: return "decode state has too few slots for this position";
+    case LA_EHIP: return "HIP runtime or kernel launch error";
+    default: return "unknown status code";
+  }
+}
+
+LA_API int loglinear_version(void) { return 100; }
+
+LA_API int loglinear_fwd_workspace(int B, int H, int64_t T, int dk, int dv, int C, int dtype,
+                                   size_t* bytes) {
+  if (!bytes) return kEINVAL;
+  FwdPlan p;
+  int rc = plan_fwd(B, H, T, dk, dv, C, dtype, -1, &p);
+  if (rc != kOK) return rc;
+  *bytes = p.ws_bytes;
+  return kOK;
+}
+
+LA_API int loglinear_fwd_num_stages(int B, int H, int64_t T, int dk, int dv, int C, int dtype,
+                                    int* n_stages) {
+  if (!n_stages) return kEINVAL;
+  FwdPlan p;
+  int rc = plan_fwd(B, H, T, dk, dv, C, dtype, -1, &p);
+  if (rc != kOK) return rc;
+  *n_stages = p.n_stages;
+  return kOK;
+}
+
+LA_API int loglinear_fwd(const void* q, const void* k, const void* v, const float* log_a,
+                         const float* lambda, void* out, int B, int H, int64_t T, int dk, int dv,
+                         int C, int L, int dtype, void* workspace, size_t workspace_bytes,
+                         la_stream_t stream) {
+  return fwd_common(q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, L, dtype, workspace,
+                    workspace_bytes, nullptr, 0, stream);
+}
+
+LA_API int loglinear_fwd_staged(const void* q, const void* k, const void* v, const float* log_a,
+                                const float* lambda, void* out, int B, int H, int64_t T, int dk,
+                                int dv, int C, int L, int dtype, void* workspace,
+                                size_t workspace_bytes, void* const* events, int n_events,
+                                la_stream_t stream) {
+  if (!events) return kEINVAL;
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return kEINVAL;
+  return fwd_common(q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, L, dtype, workspace,
+                    workspace_bytes, events, n_events, stream);
+}
+
+LA_API int loglinear_state_bytes(int B, int H, int dk, int dv, int S, size_t* slot_bytes,
+                                 size_t* scale_bytes) {
+  if (!slot_bytes || !scale_bytes) return kEINVAL;
+  int rc = check_state_shape(B, H, dk, dv, S);
+  if (rc != kOK) return rc;
+  *slot_bytes = (size_t)B * H * S * dk * dv * sizeof(float);
+  *scale_bytes = (size_t)B * H * S * sizeof(float);
+  return kOK;
+}
+
+LA_API int loglinear_state_init(la_state* st, int B, int H, int dk, int dv, int S, float* slots,
+                                float* scale, la_stream_t stream) {
+  if (!st) return kEINVAL;
+  int rc = check_state_shape(B, H, dk, dv, S);
+  if (rc != kOK) return rc;
+  const int64_t BH = (int64_t)B * H;
+  if (BH > 0) {
+    if (!slots || !scale) return kEINVAL;
+    if (!aligned(slots, 16) || !aligned(scale, 16)) return kEALIGN;
+  }
+  st->t = 0; st->B = B; st->H = H; st->dk = dk; st->dv = dv; st->S = S;
+  st->slots = slots; st->scale = scale;
+  if (BH == 0) return kOK;
+  return launch_state_init(slots, BH * S * dk * dv, scale, BH * S, (hipStream_t)stream);
+}
+
+LA_API int loglinear_decode_step(la_state* st, const void* q, const void* k, const void* v,
+                                 const float* a, const float* lambda, void* out, int dtype,
+                                 la_stream_t stream) {
+  if (!st) return kEINVAL;
+  if (dtype != kF32 && dtype != kBF16) return kEDTYPE;
+  int rc = check_state_shape(st->B, st->H, st->dk, st->dv, st->S);
+  if (rc != kOK) return rc;
+  if (st->t < 0) return kEINVAL;
+  const int kstar = trailing_ones(st->t);
+  if (kstar + 1 > st->S || bit_length(st->t) > st->S) return kECAPACITY;
+  const int64_t BH = (int64_t)st->B * st->H;
+  if (BH > 0) {
+    if (!st->slots || !st->scale || !q || !k || !v || !a || !lambda || !out) return kEINVAL;
+    if (!aligned(st->slots, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+        !aligned(out, 16))
+      return kEALIGN;
+    if (!aligned(st->scale, 4) || !aligned(a, 4) || !aligned(lambda, 4)) return kEALIGN;
+    rc = launch_decode(st, q, k, v, a, lambda, out, dtype, kstar, (hipStream_t)stream);
+    if (rc != kOK) return rc;
+  }
+  st->t += 1;
+  return kOK;
+}
+
+LA_API int loglinear_level_table(int64_t T, int C, int8_t* out, la_stream_t stream) {
+  if (T < 1 || C < 1) return kEINVAL;
+  if (T > kMaxTableT) return kESHAPE;
+  if (!is_pow2(C) || C > (1 << 20)) return kESHAPE;
+  if (!out) return kEINVAL;
+  return launch_level_table(T, ilog2(C), out, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,9 @@
+// bfloat16 instantiations of the forward kernels.
+#include "la_fwd_impl.hpp"
+#include "la_internal.hpp"
+
+namespace la {
+int launch_fwd_bf16(const FwdPlan& p, const FwdArgs& a, hipStream_t s, hipEvent_t const* ev) {
+  return launch_fwd_dtype<true>(p, a, s, ev);
+}
+}  // namespace la

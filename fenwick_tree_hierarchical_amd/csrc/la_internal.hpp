@@ -1,0 +1,24 @@
+// Internal launch entry points of liblogattn (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/logattn.h"
+#include "la_plan.hpp"
+
+namespace la {
+
+struct FwdArgs;
+
+// Forward: enqueue the stages of `p` on stream s; ev (nullable) holds
+// p.n_stages + 1 events recorded around the stages.
+int launch_fwd_bf16(const FwdPlan& p, const FwdArgs& a, hipStream_t s, hipEvent_t const* ev);
+int launch_fwd_f32(const FwdPlan& p, const FwdArgs& a, hipStream_t s, hipEvent_t const* ev);
+
+int launch_decode(const la_state* st, const void* q, const void* k, const void* v, const float* a,
+                  const float* lam, void* out, int dtype, int kstar, hipStream_t s);
+int launch_state_init(float* slots, int64_t n_slots, float* scale, int64_t n_scale, hipStream_t s);
+int launch_level_table(int64_t T, int log2C, int8_t* out, hipStream_t s);
+
+}  // namespace la

@@ -69,45 +69,50 @@ def levels_for(T: int) -> int:
 
 
 def make_inputs(w: Workload, device="cpu", B=None, H=None, T=None, L=None,
-                variant: str | None = None, seed: int | None = None):
+                variant: str | None = None, seed: int | None = None, d: int | None = None,
+                dtype: str | None = None):
     """Draw one seeded input set for workload ``w``.
 
-    B, H, T, L override the workload's sizes (reduced-size parity cases).
+    B, H, T, L, d (d_k = d_v) and dtype ("f32"/"bf16") override the
+    workload's (reduced-size and shape-sweep parity cases).
     ``variant`` changes the gates or weights after the draw:
       "weak_decay"  log_a <- 0.01 * log_a   (far buckets matter)
       "no_decay"    log_a <- 0
       "onehot:<l>"  lambda <- 1 on level l, 0 elsewhere
       "const:<c>"   lambda <- c everywhere
+    joined with "+" to combine (e.g. "weak_decay+onehot:9").
     Returns a dict of tensors q, k, v (layer dtype), log_a, lam (float32).
     """
     B = w.B if B is None else B
     H = w.H if H is None else H
     T = w.T if T is None else T
     L = (w.L if T == w.T else levels_for(T)) if L is None else L
+    dk = w.dk if d is None else d
+    dv = w.dv if d is None else d
     g = torch.Generator(device=device)
     g.manual_seed(w.seed if seed is None else seed)
     f32 = dict(device=device, dtype=torch.float32, generator=g)
-    q = torch.randn(B, H, T, w.dk, **f32) * (1.0 / math.sqrt(w.dk))
-    k = torch.randn(B, H, T, w.dk, **f32) * (1.0 / math.sqrt(w.dk))
-    v = torch.randn(B, H, T, w.dv, **f32)
+    q = torch.randn(B, H, T, dk, **f32) * (1.0 / math.sqrt(dk))
+    k = torch.randn(B, H, T, dk, **f32) * (1.0 / math.sqrt(dk))
+    v = torch.randn(B, H, T, dv, **f32)
     x = torch.randn(B, H, T, **f32)
     log_a = -F.softplus(x) if w.dist == "A" else -F.softplus(0.5 * x + 1.0)
     lam = F.softplus(torch.randn(B, H, T, L, **f32))
     q = q / q.norm(dim=-1, keepdim=True)
     k = k / k.norm(dim=-1, keepdim=True)
-    if variant:
-        if variant == "weak_decay":
+    for var in (variant.split("+") if variant else []):
+        if var == "weak_decay":
             log_a = 0.01 * log_a
-        elif variant == "no_decay":
+        elif var == "no_decay":
             log_a = torch.zeros_like(log_a)
-        elif variant.startswith("onehot:"):
-            lev = int(variant.split(":")[1])
+        elif var.startswith("onehot:"):
+            lev = int(var.split(":")[1])
             lam = torch.zeros_like(lam)
             lam[..., lev] = 1.0
-        elif variant.startswith("const:"):
-            lam = torch.full_like(lam, float(variant.split(":")[1]))
+        elif var.startswith("const:"):
+            lam = torch.full_like(lam, float(var.split(":")[1]))
         else:
-            raise ValueError(f"unknown variant {variant!r}")
-    dt = torch_dtype(w.dtype)
+            raise ValueError(f"unknown variant {var!r}")
+    dt = torch_dtype(w.dtype if dtype is None else dtype)
     return dict(q=q.to(dt).contiguous(), k=k.to(dt).contiguous(), v=v.to(dt).contiguous(),
                 log_a=log_a.contiguous(), lam=lam.contiguous())

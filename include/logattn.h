@@ -1,0 +1,198 @@
+/*
+ * liblogattn -- log-linear attention in its Mamba-2 form on AMD CDNA4 (gfx950).
+ *
+ * The operator, per (batch b, head h), with 0-based query t and key s:
+ *
+ *   o_t = sum_{s<=t} lambda[t, l(t,s)] * M^S[t,s] * (q_t . k_s) * v_s
+ *
+ *   M^S[t,s] = prod_{s<r<=t} a_r,  a_r = exp(log_a[r])   -- the Mamba-2 scalar
+ *              gate ("Log-Linear Attention", Spanish summary, technical
+ *              section 2, "Variantes", item 1; Italian summary, technical
+ *              section 2, item 2: semiseparable mask of Mamba-2).
+ *   l(t,s)   = 0 if s == t, else 1 + msb(t XOR s): the Fenwick-tree bucket
+ *              holding key s as seen from query t; bucket l >= 1 holds
+ *              2^(l-1) keys, recent keys in small buckets, old keys in large
+ *              ones (Italian summary, technical section 2, item 1; Spanish
+ *              summary, technical section 2, "Conceptos clave").
+ *   lambda   = per-token, per-level weights: the hierarchical mask that
+ *              replaces the causal mask (Italian summary, technical
+ *              section 2, item 2).
+ *
+ * No softmax, no 1/sqrt(d) scale, no normaliser.
+ *
+ * Conventions for every call:
+ *  - Return value: LA_OK (0) or a negative la_status.  Arguments are checked
+ *    on the host before anything is enqueued; on error nothing is launched
+ *    and no output is written.
+ *  - Pointers are device pointers unless stated otherwise.  The caller
+ *    allocates and owns every buffer; the library allocates no device memory
+ *    and keeps no global mutable state.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
+ *    stream).  Faults inside kernels surface at the caller's next
+ *    synchronisation.  NaN/Inf inputs are not checked; they propagate.
+ *  - Tensors are dense and contiguous in the stated layouts.
+ *  - Calls that share a workspace or a state must not overlap in time.
+ */
+#ifndef LOGATTN_H
+#define LOGATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_API __attribute__((visibility("default")))
+
+typedef enum la_status {
+  LA_OK = 0,
+  LA_EINVAL = -1,      /* null pointer or a non-positive count where one is required */
+  LA_ESHAPE = -2,      /* unsupported head dim / chunk size, too few levels, size limit */
+  LA_EDTYPE = -3,      /* dtype code not one of la_dtype */
+  LA_EALIGN = -4,      /* a pointer is not aligned as documented */
+  LA_EWORKSPACE = -5,  /* workspace pointer null or smaller than the queried size */
+  LA_ECAPACITY = -6,   /* decode state has too few slots for the next merge */
+  LA_EHIP = -7         /* a HIP runtime call or kernel launch failed */
+} la_status;
+
+typedef enum la_dtype {
+  LA_F32 = 0,          /* q, k, v, out in float32; float32 matrix-core products */
+  LA_BF16 = 1          /* q, k, v, out in bfloat16; bf16 matrix-core products,
+                          float32 accumulation */
+} la_dtype;
+
+typedef void* la_stream_t; /* hipStream_t */
+
+/* Human-readable text for a status code (static storage; never NULL). */
+LA_API const char* loglinear_strerror(int code);
+
+/* Library version as 10000*major + 100*minor + patch. */
+LA_API int loglinear_version(void);
+
+/*
+ * Workspace size for loglinear_fwd.
+ *
+ * Writes to *bytes (host pointer) the number of device bytes loglinear_fwd
+ * needs for the given shape (0 is possible).  Supported shapes are those
+ * loglinear_fwd accepts; others return the same error code it would.
+ */
+LA_API int loglinear_fwd_workspace(int B, int H, int64_t T, int dk, int dv, int C,
+                                   int dtype, size_t* bytes);
+
+/*
+ * Chunkwise-parallel forward ("Log-Linear Attention", Italian summary,
+ * technical section 2, item 3 "Training"; Spanish summary, technical
+ * section 2, "Forma paralela" and "Algoritmo de entrenamiento"): the
+ * sequence is cut into chunks of C tokens; pairs inside a chunk are formed
+ * densely, pairs across chunks go through per-chunk states combined along the
+ * Fenwick levels.  The result is the operator above, exactly up to rounding.
+ *
+ *   q      [B, H, T, dk]  dtype          16-byte aligned
+ *   k      [B, H, T, dk]  dtype          16-byte aligned
+ *   v      [B, H, T, dv]  dtype          16-byte aligned
+ *   log_a  [B, H, T]      float32 (<= 0 in the model; any finite value works)
+ *   lambda [B, H, T, L]   float32, level index innermost; L >= ceil(log2 T)+1
+ *                         (levels >= ceil(log2 T)+1 are never read)
+ *   out    [B, H, T, dv]  dtype, written   16-byte aligned
+ *
+ * Supported: dk == dv in {16, 32, 64, 128}; C in {16, 32, 64, 128} with
+ * C <= max(16, dk) * 2 ... see loglinear_fwd_workspace (it rejects the rest
+ * with LA_ESHAPE); T >= 0 (T == 0, B == 0 or H == 0 is a no-op); T need not
+ * be a multiple of C (the last chunk is partial).  T <= 2^31 - 1.
+ * workspace: device memory of at least loglinear_fwd_workspace() bytes,
+ * 256-byte aligned; its contents on entry do not matter.
+ */
+LA_API int loglinear_fwd(const void* q, const void* k, const void* v, const float* log_a,
+                         const float* lambda, void* out, int B, int H, int64_t T, int dk, int dv,
+                         int C, int L, int dtype, void* workspace, size_t workspace_bytes,
+                         la_stream_t stream);
+
+/* Number of kernel stages loglinear_fwd enqueues for this shape (host only). */
+LA_API int loglinear_fwd_num_stages(int B, int H, int64_t T, int dk, int dv, int C, int dtype,
+                                    int* n_stages);
+
+/*
+ * loglinear_fwd with per-stage timing: `events` is a host array of
+ * n_stages + 1 hipEvent_t handles created by the caller; events[i] is
+ * recorded on `stream` before stage i and events[n_stages] after the last
+ * stage.  Same arguments, results and errors as loglinear_fwd otherwise.
+ */
+LA_API int loglinear_fwd_staged(const void* q, const void* k, const void* v, const float* log_a,
+                                const float* lambda, void* out, int B, int H, int64_t T, int dk,
+                                int dv, int C, int L, int dtype, void* workspace,
+                                size_t workspace_bytes, void* const* events, int n_events,
+                                la_stream_t stream);
+
+/*
+ * Recurrent (decode) state: one d_k x d_v float32 matrix per Fenwick level
+ * ("Log-Linear Attention", Italian summary, technical section 2, item 3
+ * "Decoding": O(log T) separate recurrent states, one per level).
+ *
+ *   t      number of tokens already consumed (host integer)
+ *   slots  [B, H, S, dk, dv] float32 device memory; slot i holds level i+1
+ *   scale  [B, H, S] float32 device memory; the true bucket matrix is
+ *          scale[i] * slots[i] (the gate is applied lazily to the scalar)
+ * Level l >= 1 holds a bucket exactly when bit l-1 of t is set; other slots
+ * are ignored.  The struct lives in host memory and is owned by the caller;
+ * saving and restoring a state is copying t, slots and scale.
+ */
+typedef struct la_state {
+  int64_t t;
+  int B, H, dk, dv, S;
+  float* slots;
+  float* scale;
+} la_state;
+
+/* Device bytes of the slots and scale arrays for a state of this shape. */
+LA_API int loglinear_state_bytes(int B, int H, int dk, int dv, int S, size_t* slot_bytes,
+                                 size_t* scale_bytes);
+
+/*
+ * Initialise *st (host struct) to the empty state (t = 0) over caller-owned
+ * device arrays `slots` and `scale` (16-byte aligned, sizes from
+ * loglinear_state_bytes).  Enqueues a kernel that zeroes slots and sets
+ * scale to 1 on `stream`.  dk == dv in {16, 32, 64, 128}; 1 <= S <= 40.
+ */
+LA_API int loglinear_state_init(la_state* st, int B, int H, int dk, int dv, int S, float* slots,
+                                float* scale, la_stream_t stream);
+
+/*
+ * One decode step for every (b, h) at position t = st->t (Italian summary,
+ * technical section 2, item 3 "Decoding"; lay part "L'essenziale": only the
+ * smallest box is updated and, when needed, merged into the bigger boxes):
+ *   1. every stored bucket decays by a (lazily, through scale);
+ *   2. out = lambda[0] (q . k) v + sum over stored levels l of
+ *      lambda[l] * scale_l * slots_l^T q;
+ *   3. binary-counter carry: with k* the number of trailing one bits of t,
+ *      the token and levels 1..k* merge into level k*+1 (scale 1).
+ * Then st->t is incremented on the host.
+ *
+ *   q      [B, H, dk]   dtype      16-byte aligned
+ *   k      [B, H, dk]   dtype      16-byte aligned
+ *   v      [B, H, dv]   dtype      16-byte aligned
+ *   a      [B, H]       float32    the gate exp(log_a) of this token, in (0, 1]
+ *   lambda [B, H, S+1]  float32    weights of levels 0..S for this token
+ *   out    [B, H, dv]   dtype      written, 16-byte aligned
+ * LA_ECAPACITY when level k*+1 would exceed S (st->t is then unchanged).
+ */
+LA_API int loglinear_decode_step(la_state* st, const void* q, const void* k, const void* v,
+                                 const float* a, const float* lambda, void* out, int dtype,
+                                 la_stream_t stream);
+
+/*
+ * Fenwick level table for checking: out[t * T + s] = l(t, s) for s <= t and
+ * -1 for s > t, as int8, computed on the device by the same level function
+ * the forward kernels use, with the chunk factorisation for chunk size C:
+ * inside a chunk the level comes from the bit pattern of the in-chunk
+ * offsets, across chunks it is log2(C) + 1 + msb(chunk_t XOR chunk_s).
+ *   out  [T, T] int8 device memory; 1 <= T <= 16384; C a power of two
+ *        in [1, 2^20].
+ */
+LA_API int loglinear_level_table(int64_t T, int C, int8_t* out, la_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOGATTN_H */

@@ -1,0 +1,163 @@
+"""Host-side checks of the C ABI (CPU only: no kernel is launched).
+
+The library must load, export every function include/logattn.h declares, and
+return each documented error code from its host-side checks, which run before
+anything is enqueued.  Pointers below are fake addresses: the calls must fail
+validation before any of them is used.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (binds the library to torch's HIP runtime)
+
+import fenwick_tree_hierarchical_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "logattn.h")
+
+OK, EINVAL, ESHAPE, EDTYPE, EALIGN, EWS, ECAP = 0, -1, -2, -3, -4, -5, -6
+A = 1 << 20          # a fake, 256-byte aligned "device" address
+L = la.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return re.findall(r"LA_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_strerror_and_version():
+    for code in (OK, EINVAL, ESHAPE, EDTYPE, EALIGN, EWS, ECAP, -7):
+        assert la.loglinear_strerror(code)
+    assert "unknown" in la.loglinear_strerror(12345)
+    assert L.loglinear_version() >= 100
+
+
+def ws(B, H, T, d, C, dt=1):
+    n = ctypes.c_size_t(0)
+    rc = L.loglinear_fwd_workspace(B, H, T, d, d, C, dt, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_query():
+    rc, n = ws(8, 16, 16384, 64, 64)
+    assert rc == OK
+    # group states (fp32) + gate totals + prefix + nodes (bf16): 32 groups of 8 chunks
+    ng, BH, DD = 32, 128, 64 * 64
+    assert n >= BH * ng * DD * 4 + BH * ng * DD * 2
+    assert n < 2 * (BH * ng * DD * 4 + BH * ng * DD * 2)
+    assert ws(1, 1, 64, 16, 16, 0)[0] == OK
+    assert ws(1, 1, 100, 16, 16, 0)[0] == OK        # ragged T is accepted
+    assert ws(0, 4, 100, 64, 64)[1] == 0             # empty problem needs nothing
+    assert ws(1, 1, 64, 16, 16, 7)[0] == EDTYPE
+    assert ws(1, 1, 64, 24, 64)[0] == ESHAPE          # unsupported head dim
+    assert ws(1, 1, 64, 64, 48)[0] == ESHAPE          # unsupported chunk
+    assert ws(1, 1, 64, 128, 128, 0)[0] in (OK, ESHAPE)
+    assert ws(-1, 1, 64, 64, 64)[0] == EINVAL
+    assert L.loglinear_fwd_workspace(1, 1, 64, 64, 32, 64, 1, ctypes.byref(ctypes.c_size_t())) == ESHAPE
+    assert L.loglinear_fwd_workspace(1, 1, 64, 64, 64, 64, 1, None) == EINVAL
+
+
+def test_f32_largest_tile_rejected_but_bf16_accepted():
+    assert ws(1, 1, 256, 128, 128, 0)[0] == ESHAPE   # fp32 128x128 tiles exceed LDS
+    assert ws(1, 1, 256, 128, 128, 1)[0] == OK
+
+
+def fwd(q=A, k=A, v=A, la_=A, lam=A, out=A, B=1, H=1, T=64, d=16, C=16, Lv=7, dt=0, w=A, wb=1 << 30):
+    return L.loglinear_fwd(q, k, v, la_, lam, out, B, H, T, d, d, C, Lv, dt, w, wb, None)
+
+
+def test_fwd_validation_codes():
+    assert fwd(q=None) == EINVAL
+    assert fwd(out=None) == EINVAL
+    assert fwd(lam=None) == EINVAL
+    assert fwd(q=A + 8) == EALIGN
+    assert fwd(out=A + 4) == EALIGN
+    assert fwd(la_=A + 2) == EALIGN
+    assert fwd(dt=5) == EDTYPE
+    assert fwd(Lv=6) == ESHAPE                           # T=64 needs 7 levels
+    assert fwd(Lv=33) == ESHAPE
+    assert fwd(d=48) == ESHAPE
+    assert fwd(C=8) == ESHAPE
+    assert fwd(T=-1) == EINVAL
+    # workspace: T=1024 with C=16 has several groups, so a workspace is needed
+    assert fwd(T=1024, Lv=11, w=None) == EWS
+    assert fwd(T=1024, Lv=11, wb=16) == EWS
+    assert fwd(T=1024, Lv=11, w=A + 16) == EALIGN
+    # empty problems return OK without touching any pointer
+    assert fwd(q=None, k=None, v=None, la_=None, lam=None, out=None, B=0) == OK
+    assert fwd(q=None, k=None, v=None, la_=None, lam=None, out=None, T=0, Lv=0) == OK
+
+
+def test_num_stages():
+    n = ctypes.c_int(-1)
+    assert L.loglinear_fwd_num_stages(1, 1, 64, 16, 16, 16, 0, ctypes.byref(n)) == OK and n.value == 1
+    assert L.loglinear_fwd_num_stages(8, 16, 16384, 64, 64, 64, 1, ctypes.byref(n)) == OK and n.value == 3
+    assert L.loglinear_fwd_num_stages(0, 16, 16384, 64, 64, 64, 1, ctypes.byref(n)) == OK and n.value == 0
+
+
+def test_staged_requires_matching_event_count():
+    ev = (ctypes.c_void_p * 2)(A, A)
+    rc = L.loglinear_fwd_staged(A, A, A, A, A, A, 8, 16, 16384, 64, 64, 64, 15, 1, A, 1 << 34, ev, 2, None)
+    assert rc == EINVAL                                   # three stages need four events
+    ev0 = (ctypes.c_void_p * 4)(A, None, A, A)
+    rc = L.loglinear_fwd_staged(A, A, A, A, A, A, 8, 16, 16384, 64, 64, 64, 15, 1, A, 1 << 34, ev0, 4, None)
+    assert rc == EINVAL
+
+
+def test_state_bytes_and_init_validation():
+    sb, cb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.loglinear_state_bytes(64, 16, 64, 64, 16, ctypes.byref(sb), ctypes.byref(cb)) == OK
+    assert sb.value == 64 * 16 * 16 * 64 * 64 * 4 and cb.value == 64 * 16 * 16 * 4
+    assert L.loglinear_state_bytes(1, 1, 64, 64, 0, ctypes.byref(sb), ctypes.byref(cb)) == ESHAPE
+    assert L.loglinear_state_bytes(1, 1, 64, 64, 41, ctypes.byref(sb), ctypes.byref(cb)) == ESHAPE
+    assert L.loglinear_state_bytes(1, 1, 64, 32, 4, ctypes.byref(sb), ctypes.byref(cb)) == ESHAPE
+    st = la._LaState()
+    assert L.loglinear_state_init(ctypes.byref(st), 1, 1, 64, 64, 4, None, A, None) == EINVAL
+    assert L.loglinear_state_init(ctypes.byref(st), 1, 1, 64, 64, 4, A + 4, A, None) == EALIGN
+    assert L.loglinear_state_init(None, 1, 1, 64, 64, 4, A, A, None) == EINVAL
+    # empty state: initialised on the host only
+    assert L.loglinear_state_init(ctypes.byref(st), 0, 4, 64, 64, 4, None, None, None) == OK
+    assert st.t == 0 and st.S == 4
+
+
+def test_decode_validation_codes():
+    st = la._LaState(0, 1, 1, 64, 64, 3, A, A)
+    step = lambda **kw: L.loglinear_decode_step(ctypes.byref(st), kw.get("q", A), A, A, A, A, kw.get("out", A),
+                                                kw.get("dt", 1), None)
+    assert step(dt=3) == EDTYPE
+    assert step(q=None) == EINVAL
+    assert step(out=A + 2) == EALIGN
+    st.t = 7                      # 0b111: merging needs level 4 > S = 3
+    assert step() == ECAP and st.t == 7
+    st.t = 8                      # level 4 occupied: already beyond capacity
+    assert step() == ECAP
+    st.t = -1
+    assert step() == EINVAL
+    # empty batch: only the host position advances
+    st0 = la._LaState(5, 0, 1, 64, 64, 3, None, None)
+    assert L.loglinear_decode_step(ctypes.byref(st0), None, None, None, None, None, None, 1, None) == OK
+    assert st0.t == 6
+
+
+def test_level_table_validation_codes():
+    assert L.loglinear_level_table(0, 16, A, None) == EINVAL
+    assert L.loglinear_level_table(64, 0, A, None) == EINVAL
+    assert L.loglinear_level_table(64, 24, A, None) == ESHAPE
+    assert L.loglinear_level_table(16385, 16, A, None) == ESHAPE
+    assert L.loglinear_level_table(64, 16, None, None) == EINVAL
+
+
+def test_binding_refuses_cpu_tensors():
+    x = torch.zeros(1, 1, 16, 16)
+    with pytest.raises(ValueError):
+        la.loglinear_fwd(x, x, x, torch.zeros(1, 1, 16), torch.zeros(1, 1, 16, 5))

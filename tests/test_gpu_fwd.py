@@ -1,0 +1,162 @@
+"""Forward parity: the HIP path against the float64 oracle (GPU).
+
+Bars (relative L2 over the compared outputs): 1e-4 for float32 inputs, 2e-2
+for bfloat16 inputs.  At the workloads' strong decays keys a chunk away are
+nearly invisible, so every shape class is also run with weak or no decay and
+with lambda one-hot on single levels, which makes each intra-chunk, chunk and
+group level carry the output on its own.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from fenwick_tree_hierarchical_amd.workloads import WORKLOADS, make_inputs
+from oracle import forms
+from tests.helpers import TOL, heads, need_gpu, rel_l2, say, to_cpu
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_fwd(x, C, dev):
+    import fenwick_tree_hierarchical_amd as la
+    xd = {k: v.to(dev) for k, v in x.items()}
+    out = la.loglinear_fwd(xd["q"], xd["k"], xd["v"], xd["log_a"], xd["lam"], chunk=C)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def oracle_fwd(x, rows=None):
+    return forms.forward_quadratic(x["q"], x["k"], x["v"], x["log_a"], x["lam"], rows=rows)
+
+
+def check(x, C, dtype, dev, label):
+    say(f"fwd {label}: shape={tuple(x['q'].shape)} C={C} dtype={dtype}")
+    got = gpu_fwd(x, C, dev)
+    ref = oracle_fwd(x)
+    err = rel_l2(got, ref)
+    say(f"   rel_l2={err:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= TOL[dtype], f"{label}: rel_l2 {err:.3e} > {TOL[dtype]}"
+    return err
+
+
+def test_tiny_f32_workload():
+    dev = need_gpu()
+    w = WORKLOADS["tiny_f32"]
+    check(make_inputs(w), w.C, "f32", dev, "tiny_f32")
+
+
+def test_small_bf16_workload():
+    dev = need_gpu()
+    w = WORKLOADS["small_bf16"]
+    check(make_inputs(w), w.C, "bf16", dev, "small_bf16")
+
+
+SHAPES = [(16, 16), (32, 32), (64, 64), (64, 16), (16, 128), (32, 64), (128, 64), (128, 16), (64, 128),
+          (128, 128)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d,C", SHAPES)
+def test_shapes_weak_decay_ragged(d, C, dtype):
+    """Several full groups, a partial group and a ragged last chunk."""
+    dev = need_gpu()
+    if dtype == "f32" and d == 128 and C == 128:
+        pytest.skip("float32 128x128 tiles exceed LDS (rejected with LA_ESHAPE)")
+    T = 21 * C + 5
+    x = make_inputs(WORKLOADS["small_bf16"], B=1, H=2, T=T, d=d, dtype=dtype, variant="weak_decay",
+                    seed=100 + d + C)
+    check(x, C, dtype, dev, f"d={d} C={C} T={T} weak_decay")
+
+
+@pytest.mark.parametrize("variant", ["weak_decay", "no_decay"])
+def test_small_bf16_coverage_variants(variant):
+    dev = need_gpu()
+    w = WORKLOADS["small_bf16"]
+    check(make_inputs(w, variant=variant), w.C, "bf16", dev, f"small_bf16 {variant}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("lev", list(range(12)))
+def test_onehot_level_sweep(lev, dtype):
+    """lambda one-hot on level `lev` of T = 2048 with C = 64: levels 0..6 live
+    inside a chunk, 7..9 are chunk levels inside a group, 10..11 group levels."""
+    dev = need_gpu()
+    x = make_inputs(WORKLOADS["small_bf16"], B=1, H=4, T=2048, dtype=dtype, variant=f"weak_decay+onehot:{lev}",
+                    seed=300 + lev)
+    check(x, 64, dtype, dev, f"onehot level {lev}")
+
+
+@pytest.mark.parametrize("T,C", [(1, 16), (2, 16), (15, 16), (17, 16), (100, 64), (1000, 64), (129, 128)])
+def test_short_and_ragged_sequences(T, C):
+    dev = need_gpu()
+    x = make_inputs(WORKLOADS["small_bf16"], B=2, H=3, T=T, dtype="f32", variant="weak_decay", seed=T)
+    check(x, C, "f32", dev, f"T={T} C={C}")
+
+
+def test_chunk_size_invariance_f32():
+    """The chunking is an exact reformulation: every C gives the operator."""
+    dev = need_gpu()
+    x = make_inputs(WORKLOADS["small_bf16"], B=1, H=2, T=1500, dtype="f32", variant="weak_decay", seed=5)
+    ref = oracle_fwd(x)
+    outs = {}
+    for C in (16, 32, 64, 128):
+        say(f"fwd C-invariance C={C}")
+        outs[C] = gpu_fwd(x, C, dev)
+        assert rel_l2(outs[C], ref) <= TOL["f32"]
+    for C in (32, 64, 128):
+        assert rel_l2(outs[C], outs[16]) <= 2 * TOL["f32"]
+
+
+def test_empty_problems():
+    dev = need_gpu()
+    import fenwick_tree_hierarchical_amd as la
+    for B, T in [(0, 64), (1, 0)]:
+        x = make_inputs(WORKLOADS["small_bf16"], B=B, H=2, T=T, L=7, device="cpu")
+        xd = {k: v.to(dev) for k, v in x.items()}
+        out = la.loglinear_fwd(xd["q"], xd["k"], xd["v"], xd["log_a"], xd["lam"], chunk=64)
+        assert out.shape == (B, 2, T, 64)
+
+
+def test_deterministic():
+    dev = need_gpu()
+    x = make_inputs(WORKLOADS["small_bf16"], variant="weak_decay")
+    a = gpu_fwd(x, 64, dev)
+    b = gpu_fwd(x, 64, dev)
+    assert np.array_equal(a, b)
+
+
+# --------------------------------------------------------------- full sizes
+def sampled_rows(T, C, G, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, C - 1, C, G * C - 1, G * C, G * C + C, 2 * G * C + 3, T // 2 - 1, T // 2, T - C - 1, T - 2, T - 1]
+    return np.unique(np.concatenate([[r for r in fixed if 0 <= r < T], rng.integers(0, T, 27)]))
+
+
+def full_size_check(name, variant, head_idx, seed):
+    dev = need_gpu()
+    import fenwick_tree_hierarchical_amd as la
+    w = WORKLOADS[name]
+    say(f"fwd full size {name} variant={variant}")
+    x = make_inputs(w, device=dev, variant=variant)
+    out = la.loglinear_fwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], chunk=w.C)
+    torch.cuda.synchronize()
+    rows = sampled_rows(w.T, w.C, 8, seed)
+    sub = to_cpu(heads(x, head_idx))
+    ref = forms.forward_quadratic(sub["q"], sub["k"], sub["v"], sub["log_a"], sub["lam"], rows=rows)
+    got = torch.stack([out[b, h, rows] for b, h in head_idx])[None].float().cpu().numpy()
+    err = rel_l2(got, ref)
+    say(f"   rel_l2={err:.3e} over {len(head_idx)} heads x {len(rows)} rows")
+    assert np.isfinite(out.float()).all().item()
+    assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("variant", [None, "weak_decay"])
+def test_train_16k_full_size_sampled(variant):
+    full_size_check("train_16k_bf16", variant, [(0, 0), (3, 7), (7, 15)], 16)
+
+
+@pytest.mark.parametrize("variant", [None, "weak_decay"])
+def test_long_128k_full_size_sampled(variant):
+    full_size_check("long_128k_bf16", variant, [(0, 5)], 128)
