@@ -1,0 +1,327 @@
+"""Benchmark of log-linear Mamba-2 attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+
+One step is one forward (``loglinear_fwd``, all of its kernels) over the
+training-shape layer B=8, H=16, T=16384, d_k=d_v=64, C=64 in bfloat16, with
+every input already resident in HBM.  Prints ONE JSON line:
+
+  value          tokens/s, a token being one sequence position across all
+                 H heads (B*T per step)
+  roofline       for the dominant kernel (the output kernel): algorithmic
+                 bytes per launch / its mean duration from HIP events
+                 recorded on the launch stream over the timed steps,
+                 against 8 TB/s; `traffic` is the counter-measured HBM
+                 bytes per launch from profiles/ when those counters were
+                 taken on the current kernel source, else null
+  cpu_baseline   the float64 oracle's Fenwick recurrence timed on the host
+                 on a bounded sample of the same workload
+  stages, mfma   per-kernel times and the matrix-core share
+  decode         256 decode steps of the decode workload (64 x 16 heads,
+                 positions 32768..33023)
+
+Other modes (profiling helpers):
+  --pmc-summary DIR   parse a rocprofv3 --pmc output directory (FETCH_SIZE
+                      or WRITE_SIZE) and print per-kernel counters
+  --copy-calibration  also run a plain 1 GiB device copy each step, so a
+                      counter run sees a kernel of known traffic
+  --rocpd-summary F   markdown table of kernel statistics from a rocprofv3
+                      results database (.db) or kernel_stats.csv
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd tokens/s, log-linear Mamba-2 attn, T=16K, H=16, d=64; % MFMA peak"
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
+KERNEL_SOURCES = ["fenwick_tree_hierarchical_amd/csrc/la_fwd_impl.hpp",
+                  "fenwick_tree_hierarchical_amd/csrc/la_device.hpp",
+                  "fenwick_tree_hierarchical_amd/csrc/la_plan.hpp"]
+PMC_FILE = os.path.join(ROOT, "profiles", "fwd_output_train16k_pmc.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_counts(w, B, H, T, d, C, L, es):
+    """Work the method itself does (no dense-equivalent inflation).
+
+    Bytes: the essential I/O, q, k, v, out in the layer dtype plus log_a and
+    lambda in float32.  Flops: the dense C x C intra-chunk tiles
+    2 C^2 (d_k + d_v) per chunk, one chunk state 2 C d_k d_v per chunk, and
+    2 C d_k d_v per chunk for each occupied chunk-or-group level
+    (popcount of the chunk index)."""
+    n_chunks = math.ceil(T / C)
+    per_head_token_bytes = 4 * d * es + 4 + 4 * L
+    bytes_total = B * H * T * per_head_token_bytes
+    intra = n_chunks * 2 * C * C * (d + d)
+    states = n_chunks * 2 * C * d * d
+    contr = sum(bin(c).count("1") for c in range(n_chunks)) * 2 * C * d * d
+    flops = B * H * (intra + states + contr)
+    return dict(per_head_token_bytes=per_head_token_bytes, bytes=bytes_total, flops_intra=B * H * intra,
+                flops_states=B * H * states, flops_contractions=B * H * contr, flops=flops)
+
+
+def cpu_baseline(w, heads: int):
+    """Time the oracle's token-by-token recurrence on `heads` (b,h) pairs of
+    the workload, full length, on the host."""
+    import torch
+    from fenwick_tree_hierarchical_amd.workloads import make_inputs
+    from oracle import forms
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:       # pragma: no cover
+        threadpool_limits = None
+    x = make_inputs(w, B=1, H=heads, device="cpu")
+    t0 = time.perf_counter()
+    if threadpool_limits:
+        with threadpool_limits(1):
+            forms.forward_recurrent(x["q"], x["k"], x["v"], x["lam"], log_a=x["log_a"])
+    else:
+        forms.forward_recurrent(x["q"], x["k"], x["v"], x["lam"], log_a=x["log_a"])
+    dt = time.perf_counter() - t0
+    tokens = heads * w.T / w.H          # positions across all H heads
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 Fenwick recurrence over {heads} of the {w.B * w.H} heads, full T={w.T} "
+                      f"({heads}/{w.H} of one sequence = {tokens:.0f} tokens) in {dt:.1f} s, one thread"}
+
+
+def pmc_traffic(src_hash: str, launches_bytes: float):
+    """HBM traffic per output-kernel launch from the committed counter summary,
+    when it was taken on the current kernel source."""
+    if not os.path.exists(PMC_FILE):
+        return None, "no counter summary"
+    with open(PMC_FILE) as f:
+        s = json.load(f)
+    if s.get("kernel_source_hash") != src_hash:
+        return None, "kernel changed since the counters were taken"
+    return s.get("traffic_bytes_per_launch"), None
+
+
+def bench_decode(la, torch, dev, steps=256):
+    from fenwick_tree_hierarchical_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS["decode_32k_bf16"]
+    S = 16
+    B, H, d = w.B, w.H, w.dk
+    st = la.loglinear_state_init(B, H, d, d, S, dev)
+    # timing depends only on which levels are occupied: fill the slots with
+    # values of the right scale and start at the workload's first step
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    st.slots.normal_(0, 0.01, generator=g)
+    st.t = w.prefix
+    x = make_inputs(w, device=dev, T=steps, L=S + 1)
+    a = torch.exp(x["log_a"])
+    per = [(x["q"][:, :, i].contiguous(), x["k"][:, :, i].contiguous(), x["v"][:, :, i].contiguous(),
+            a[:, :, i].contiguous(), x["lam"][:, :, i].contiguous(), torch.empty(B, H, d, dtype=x["q"].dtype,
+                                                                                    device=dev))
+           for i in range(steps)]
+    L = la.lib()
+    stream = torch.cuda.current_stream(dev)
+    args = [(ctypes_byref(la, st), q.data_ptr(), k.data_ptr(), v.data_ptr(), aa.data_ptr(), lm.data_ptr(),
+             o.data_ptr()) for q, k, v, aa, lm, o in per]
+    # warm-up on a copy so the timed steps start at the workload's position
+    warm = st.clone()
+    for i in range(8):
+        rc = L.loglinear_decode_step(ctypes_byref(la, warm), *args[i][1:], la.LA_BF16, stream.cuda_stream)
+        assert rc == 0, rc
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        rc = L.loglinear_decode_step(args[i][0], *args[i][1:], la.LA_BF16, stream.cuda_stream)
+        if rc:
+            raise RuntimeError(la.loglinear_strerror(rc))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    # algorithmic bytes: occupied slots read once, the merged slot written once,
+    # plus q, k, v, out, gate, lambda and the slot scales
+    slot = d * d * 4
+    tot = 0
+    for t in range(w.prefix, w.prefix + steps):
+        tot += (bin(t).count("1") + 1) * slot + 4 * d * 2 + 4 + (S + 1) * 4 + 2 * S * 4
+    tot *= B * H
+    return {"workload": w.name, "steps": steps, "launch": "eager, one launch per step",
+            "tokens_per_s": B * steps / wall, "us_per_step_wall": wall / steps * 1e6,
+            "us_per_step_gpu": gpu_ms / steps * 1e3,
+            "achieved_gbps": tot / (gpu_ms * 1e-3) / 1e9, "peak_gbps": HBM_PEAK_GBPS,
+            "frac": tot / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "alg_bytes_per_step": tot / steps}
+
+
+def ctypes_byref(la, st):
+    import ctypes
+    return ctypes.byref(st._st)
+
+
+def pmc_summary(d: str):
+    """Per-kernel mean of the counters in a rocprofv3 --pmc output directory."""
+    import csv
+    rows = []
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as f:
+            rows += list(csv.DictReader(f))
+    agg = {}
+    for r in rows:
+        key = (r.get("Kernel_Name", "?"), r.get("Counter_Name", "?"))
+        agg.setdefault(key, []).append(float(r.get("Counter_Value", 0)))
+    out = {}
+    for (k, c), v in agg.items():
+        out.setdefault(k[:120], {})[c] = {"mean": sum(v) / len(v), "n": len(v)}
+    print(json.dumps(out, indent=1))
+
+
+def rocpd_summary(path: str):
+    """Markdown table of per-kernel dispatch statistics from a rocprofv3
+    output (SQLite database from the default format, or a kernel_stats.csv)."""
+    rows = []
+    if path.endswith(".db"):
+        import sqlite3
+        cur = sqlite3.connect(path).cursor()
+        for name, calls, total, avg, pct in cur.execute(
+                "select name, total_calls, total_duration, average, percentage from top_kernels"):
+            # the top_kernels view reports microseconds
+            rows.append((name, int(calls), float(total) / 1e3, float(avg), float(pct)))
+    else:
+        import csv
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                rows.append((r["Name"], int(r["Calls"]), float(r["TotalDurationNs"]) / 1e6,
+                             float(r["AverageNs"]) / 1e3, float(r["Percentage"])))
+    print("| kernel | calls | total ms | average us | % of GPU time |")
+    print("|---|---|---|---|---|")
+    for name, calls, total, avg, pct in rows:
+        short = name if len(name) < 90 else name[:87] + "..."
+        print(f"| `{short}` | {calls} | {total:.3f} | {avg:.1f} | {pct:.1f} |")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--pmc-summary", default=None)
+    ap.add_argument("--rocpd-summary", default=None)
+    args = ap.parse_args()
+    if args.rocpd_summary:
+        rocpd_summary(args.rocpd_summary)
+        return
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import fenwick_tree_hierarchical_amd as la
+    from fenwick_tree_hierarchical_amd.workloads import WORKLOADS, make_inputs
+
+    dev = torch.device("cuda:0")
+    w = WORKLOADS["train_16k_bf16"]
+    log(f"bench: drawing {w.name} inputs on the GPU")
+    x = make_inputs(w, device=dev)
+    out = torch.empty_like(x["v"])
+    nws = la.loglinear_fwd_workspace(w.B, w.H, w.T, w.dk, w.dv, w.C, torch.bfloat16)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    n_st = la.loglinear_fwd_num_stages(w.B, w.H, w.T, w.dk, w.dv, w.C, torch.bfloat16)
+    stage_names = (["group_state", "group_tree", "output"] if n_st == 3 else ["output"])
+    copy_src = copy_dst = None
+    if args.copy_calibration:
+        copy_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        copy_dst = torch.empty_like(copy_src)
+
+    def step(events=None):
+        if events is None:
+            la.loglinear_fwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], out=out, chunk=w.C, workspace=ws)
+        else:
+            la.loglinear_fwd_staged(x["q"], x["k"], x["v"], x["log_a"], x["lam"], events, out=out, chunk=w.C,
+                                    workspace=ws)
+        if copy_dst is not None:
+            copy_dst.copy_(copy_src)
+
+    log(f"bench: warm-up {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)] for _ in range(args.steps)]
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(n_st)]
+    ms_per_step = wall / args.steps * 1e3
+    tokens = w.B * w.T
+    value = tokens / (wall / args.steps)
+    cnt = algorithmic_counts(w, w.B, w.H, w.T, w.dk, w.C, w.L, 2)
+    out_ms = stage_ms[-1]
+    achieved = cnt["bytes"] / (out_ms * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic, why = pmc_traffic(src_hash, cnt["bytes"])
+    fwd_ms = sum(stage_ms)
+    result = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d_k": w.dk, "d_v": w.dv, "chunk": w.C,
+                   "levels": w.L, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "fwd_output", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "alg_bytes_per_launch": cnt["bytes"],
+                     "alg_bytes_per_head_token": cnt["per_head_token_bytes"],
+                     "traffic_note": why, "kernel_source_hash": src_hash},
+        "stages": {n: {"ms": m} for n, m in zip(stage_names, stage_ms)},
+        "mfma": {"alg_tflop": cnt["flops"] / 1e12,
+                 "achieved_tflops_whole_fwd": cnt["flops"] / (fwd_ms * 1e-3) / 1e12,
+                 "frac_of_bf16_peak_whole_fwd": cnt["flops"] / (fwd_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                 "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+                 "split_tflop": {"intra": cnt["flops_intra"] / 1e12, "states": cnt["flops_states"] / 1e12,
+                                 "contractions": cnt["flops_contractions"] / 1e12}},
+    }
+    if not args.no_decode:
+        log("bench: decode 256 steps")
+        result["decode"] = bench_decode(la, torch, dev)
+    if not args.no_cpu:
+        log(f"bench: oracle CPU baseline on {args.cpu_heads} heads")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

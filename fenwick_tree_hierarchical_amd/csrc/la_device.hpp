@@ -42,6 +42,13 @@ template <> struct Elem<true> {
   static __device__ __forceinline__ Frag load(const T* p) {
     return __builtin_bit_cast(Frag, *reinterpret_cast<const u16x8*>(p));
   }
+  // Operand fragment whose k-slice starts at k0 in a contraction of length
+  // K: zero when the slice lies past the end (K = 16 < kStep).
+  template <int K>
+  static __device__ __forceinline__ Frag load_k(const T* p, int k0) {
+    if (K >= kStep || k0 < K) return load(p);
+    return __builtin_bit_cast(Frag, u16x8{0, 0, 0, 0, 0, 0, 0, 0});
+  }
   static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -55,6 +62,8 @@ template <> struct Elem<false> {
   static __device__ __forceinline__ float to_f32(T x) { return x; }
   static __device__ __forceinline__ T from_f32(float x) { return x; }
   static __device__ __forceinline__ Frag load(const T* p) { return *p; }
+  template <int K>
+  static __device__ __forceinline__ Frag load_k(const T* p, int) { return *p; }
   static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }

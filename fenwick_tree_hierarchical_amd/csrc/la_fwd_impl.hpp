@@ -158,10 +158,10 @@ __global__ __launch_bounds__(256) void fwd_group_state(FwdArgs a) {
       const int mb = w + m * kWaves;
       if (mb < DB) {
         for (int ks = 0; ks < C; ks += EL::kStep) {
-          const auto va = EL::load(VT + (16 * mb + lr) * lay.ld_t + ks + lq * EL::kPerLane);
+          const auto va = EL::template load_k<C>(VT + (16 * mb + lr) * lay.ld_t + ks + lq * EL::kPerLane, ks + lq * EL::kPerLane);
 #pragma unroll
           for (int n = 0; n < DB; ++n) {
-            const auto kf = EL::load(KTs + (16 * n + lr) * lay.ld_t + ks + lq * EL::kPerLane);
+            const auto kf = EL::template load_k<C>(KTs + (16 * n + lr) * lay.ld_t + ks + lq * EL::kPerLane, ks + lq * EL::kPerLane);
             h[m][n] = EL::mma(va, kf, h[m][n]);
           }
         }
@@ -331,8 +331,8 @@ __global__ __launch_bounds__(256) void fwd_output(FwdArgs a) {
         f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < D; ks += EL::kStep) {
-          const auto kf = EL::load(Ks + (16 * kb + lr) * lay.ld_row + ks + lq * KPL);
-          const auto qf = EL::load(Qs + iq * lay.ld_row + ks + lq * KPL);
+          const auto kf = EL::template load_k<D>(Ks + (16 * kb + lr) * lay.ld_row + ks + lq * KPL, ks + lq * KPL);
+          const auto qf = EL::template load_k<D>(Qs + iq * lay.ld_row + ks + lq * KPL, ks + lq * KPL);
           s = EL::mma(kf, qf, s);
         }
 #pragma unroll
@@ -386,10 +386,10 @@ __global__ __launch_bounds__(256) void fwd_output(FwdArgs a) {
         for (int n = 0; n < DB; ++n) tmp[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < D; ks += EL::kStep) {
-          const auto qf = EL::load(Qs + iq * lay.ld_row + ks + lq * KPL);
+          const auto qf = EL::template load_k<D>(Qs + iq * lay.ld_row + ks + lq * KPL, ks + lq * KPL);
 #pragma unroll
           for (int n = 0; n < DB; ++n) {
-            const auto nf = EL::load(nodeT + (16 * n + lr) * ldn + ks + lq * KPL);
+            const auto nf = EL::template load_k<D>(nodeT + (16 * n + lr) * ldn + ks + lq * KPL, ks + lq * KPL);
             tmp[n] = EL::mma(qf, nf, tmp[n]);
           }
         }
@@ -439,10 +439,10 @@ __global__ __launch_bounds__(256) void fwd_output(FwdArgs a) {
 #pragma unroll
           for (int n = 0; n < DB; ++n) hh[n] = f32x4{0.f, 0.f, 0.f, 0.f};
           for (int ks = 0; ks < C; ks += EL::kStep) {
-            const auto va = EL::load(VT + (16 * mb + lr) * lay.ld_t + ks + lq * KPL);
+            const auto va = EL::template load_k<C>(VT + (16 * mb + lr) * lay.ld_t + ks + lq * KPL, ks + lq * KPL);
 #pragma unroll
             for (int n = 0; n < DB; ++n) {
-              const auto kf = EL::load(KTs + (16 * n + lr) * lay.ld_t + ks + lq * KPL);
+              const auto kf = EL::template load_k<C>(KTs + (16 * n + lr) * lay.ld_t + ks + lq * KPL, ks + lq * KPL);
               hh[n] = EL::mma(va, kf, hh[n]);
             }
           }

@@ -148,7 +148,7 @@ def full_size_check(name, variant, head_idx, seed):
     got = torch.stack([out[b, h, rows] for b, h in head_idx])[None].float().cpu().numpy()
     err = rel_l2(got, ref)
     say(f"   rel_l2={err:.3e} over {len(head_idx)} heads x {len(rows)} rows")
-    assert np.isfinite(out.float()).all().item()
+    assert torch.isfinite(out.float()).all().item()
     assert err <= TOL[w.dtype]
 
 
