@@ -24,7 +24,6 @@ int fwd_common(const void* q, const void* k, const void* v, const float* log_a, 
         if (hipEventRecord((hipEvent_t)events[i], (hipStream_t)stream) != hipSuccess) return kEHIP;
     return kOK;
   }
-  if (p.n_groups * p.BH > (int64_t)0x7fffffff) return kESHAPE;
   if (!q || !k || !v || !log_a || !lambda || !out) return kEINVAL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return kEALIGN;
   if (!aligned(log_a, 4) || !aligned(lambda, 4)) return kEALIGN;
@@ -35,6 +34,8 @@ int fwd_common(const void* q, const void* k, const void* v, const float* log_a, 
   char* w = static_cast<char*>(ws);
   FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.log_a = log_a; a.lam = lambda; a.out = out;
+  a.nodes_in = p.n_chunks > 1 ? static_cast<void*>(w + p.off_nodes_in) : nullptr;
+  a.gch = p.n_chunks > 1 ? reinterpret_cast<float*>(w + p.off_gch) : nullptr;
   a.gstate = p.n_groups > 1 ? reinterpret_cast<float*>(w + p.off_gstate) : nullptr;
   a.gtot = p.n_groups > 1 ? reinterpret_cast<float*>(w + p.off_gtot) : nullptr;
   a.gprefix = p.n_groups > 1 ? reinterpret_cast<double*>(w + p.off_gprefix) : nullptr;

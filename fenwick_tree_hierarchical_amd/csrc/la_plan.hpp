@@ -43,52 +43,63 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Levels a sequence of length T uses: ceil(log2 T) + 1 (1 for T <= 1).
 inline int levels_needed(int64_t T) { return T <= 1 ? 1 : bit_length(T - 1) + 1; }
 
-// LDS carve-up of the forward kernels (byte offsets).  Rows of the bf16/f32
-// tiles are padded by 16 bytes so that the 16 rows read by one MFMA operand
-// fall in different LDS banks.
-struct LdsLayout {
-  int q, k, vt, kts, slots, lam, b2, ginfo, total;
-  int ld_row;   // elements per row of the [C][D] tiles (Q, K)
-  int ld_t;     // elements per row of the [D][C] tiles (VT, KTs)
-  int ld_node;  // elements per row of a [D][D] node
-};
-
-constexpr int lds_take(int& off, int bytes) {
-  const int r = off;
-  off += (bytes + 255) / 256 * 256;
-  return r;
+// ---------------------------------------------------------------------------
+// Kernel shapes shared by the host plan and the kernels.
+//
+// fwd_chunk_states: one workgroup per (b,h, group of G chunks); NW1 waves;
+// each wave owns TPW of the (D/16)^2 tiles of a d_v x d_k state, and keeps
+// the in-group Fenwick carry of those tiles in registers.
+LA_HD constexpr int state_waves(int D) { return D <= 32 ? 4 : (D == 64 ? 8 : 16); }
+LA_HD constexpr int state_tiles_per_wave(int D) {
+  return ((D / 16) * (D / 16) + state_waves(D) - 1) / state_waves(D);
 }
+// Chunks per group: the largest power of two <= 8 whose carry (log2 G slots
+// of TPW 16x16 fp32 tiles) fits in 32 registers per lane.
+LA_HD constexpr int state_group(int D) {
+  int G = 8;
+  while (G > 1) {
+    int ns = 0;
+    for (int g = G; g > 1; g >>= 1) ++ns;
+    if (ns * state_tiles_per_wave(D) * 4 <= 32) break;
+    G >>= 1;
+  }
+  return G;
+}
+// fwd_chunk_output: one workgroup per (b,h, chunk); one wave per 16-query
+// block (at least 4 waves).
+LA_HD constexpr int output_waves(int C) { return C / 16 > 4 ? C / 16 : 4; }
 
-// with_q: the output kernel (Q, K, lambda, chunk-level slots); otherwise the
-// group-state kernel (V^T and the gated K^T only).
-LA_HD constexpr LdsLayout lds_layout(int C, int D, int es, int G, int L, bool with_q) {
-  LdsLayout o{};
-  const int pad = 16 / es;
-  o.ld_row = D + pad;
-  o.ld_t = C + pad;
-  o.ld_node = D + pad;
-  int nslots = 0;                       // chunk levels 1..log2 G inside a group
-  for (int g = G; g > 1; g >>= 1) ++nslots;
+// LDS carve-up (byte offsets).  Tile rows are padded by 16 bytes so that the
+// 16 rows one MFMA operand reads fall in different LDS banks.
+struct StateLds {
+  int vt, kts, b2, total, ld_t;
+};
+LA_HD constexpr StateLds state_lds(int C, int D, int es, int G) {
+  StateLds o{};
+  o.ld_t = C + 16 / es;
   int off = 0;
-  o.q = with_q ? lds_take(off, C * o.ld_row * es) : -1;
-  o.k = with_q ? lds_take(off, C * o.ld_row * es) : -1;
-  o.vt = lds_take(off, D * o.ld_t * es);
-  o.kts = (G > 1 || !with_q) ? lds_take(off, D * o.ld_t * es) : -1;
-  o.slots = (with_q && nslots > 0) ? lds_take(off, nslots * D * o.ld_node * es) : -1;
-  o.lam = with_q ? lds_take(off, C * L * 4) : -1;
-  o.b2 = lds_take(off, G * C * 4);
-  o.ginfo = with_q ? lds_take(off, 64 * 8) : -1;   // group-level node list
+  o.vt = off;  off += (D * o.ld_t * es + 255) / 256 * 256;
+  o.kts = off; off += (D * o.ld_t * es + 255) / 256 * 256;
+  o.b2 = off;  off += (G * C * 4 + 255) / 256 * 256;
   o.total = off;
   return o;
 }
-
-// Chunks per workgroup of the output kernel: the largest power of two <= 8
-// whose tiles fit in LDS with the largest accepted lambda stage; 0 if even a
-// single chunk does not fit.
-LA_HD constexpr int choose_group(int C, int D, int es) {
-  for (int G = 8; G >= 1; G >>= 1)
-    if (lds_layout(C, D, es, G, kMaxLevels, true).total <= (int)kLdsLimit) return G;
-  return 0;
+struct OutLds {
+  int k, vt, lam, b2, list, total, ld_row, ld_t;
+};
+constexpr int kMaxListed = 48;        // occupied levels above the chunk, listed per chunk
+LA_HD constexpr OutLds output_lds(int C, int D, int es, int L) {
+  OutLds o{};
+  o.ld_row = D + 16 / es;
+  o.ld_t = C + 16 / es;
+  int off = 0;
+  o.k = off;    off += (C * o.ld_row * es + 255) / 256 * 256;
+  o.vt = off;   off += (D * o.ld_t * es + 255) / 256 * 256;
+  o.lam = off;  off += (C * L * 4 + 255) / 256 * 256;
+  o.b2 = off;   off += (C * 4 + 255) / 256 * 256;
+  o.list = off; off += (kMaxListed * 16 + 16 + 255) / 256 * 256;
+  o.total = off;
+  return o;
 }
 
 struct FwdPlan {
@@ -96,6 +107,7 @@ struct FwdPlan {
   int64_t T = 0, BH = 0, n_chunks = 0, n_groups = 0;
   int G = 1, log2G = 0, log2C = 0;
   int lds_out = 0, lds_state = 0;
+  size_t off_nodes_in = 0, off_gch = 0;
   size_t off_gstate = 0, off_gtot = 0, off_gprefix = 0, off_nodes = 0, ws_bytes = 0;
   int n_stages = 0;   // 0 for an empty problem
 };
@@ -121,14 +133,14 @@ inline int plan_fwd(int B, int H, int64_t T, int dk, int dv, int C, int dtype, i
   P.L = L < 0 ? kMaxLevels : L;
   P.BH = (int64_t)B * H;
   P.log2C = ilog2(C);
-  const int G = choose_group(C, dk, P.es);
-  if (G == 0) return kESHAPE;
-  P.G = G;
-  P.log2G = ilog2(G);
-  P.lds_out = lds_layout(C, dk, P.es, G, P.L, true).total;
-  P.lds_state = lds_layout(C, dk, P.es, G, P.L, false).total;
+  P.G = state_group(dk);
+  P.log2G = ilog2(P.G);
+  P.lds_state = state_lds(C, dk, P.es, P.G).total;
+  P.lds_out = output_lds(C, dk, P.es, P.L).total;
+  if (P.lds_state > kLdsLimit || output_lds(C, dk, P.es, kMaxLevels).total > kLdsLimit) return kESHAPE;
   P.n_chunks = (T + C - 1) / C;
-  P.n_groups = (P.n_chunks + G - 1) / G;
+  P.n_groups = (P.n_chunks + P.G - 1) / P.G;
+  if (P.n_chunks * P.BH > (int64_t)0x7fffffff) return kESHAPE;
   if (P.BH == 0 || T == 0) {
     P.n_stages = 0;
     *p = P;
@@ -136,15 +148,17 @@ inline int plan_fwd(int B, int H, int64_t T, int dk, int dv, int C, int dtype, i
   }
   const size_t DD = (size_t)dk * dv;
   size_t off = 0;
-  if (P.n_groups > 1) {
-    P.off_gstate = off; off = align_up(off + (size_t)P.BH * P.n_groups * DD * 4, 256);
-    P.off_gtot = off;   off = align_up(off + (size_t)P.BH * P.n_groups * 4, 256);
-    P.off_gprefix = off; off = align_up(off + (size_t)P.BH * (P.n_groups + 1) * 8, 256);
-    P.off_nodes = off;  off = align_up(off + (size_t)P.BH * P.n_groups * DD * P.es, 256);
-    P.n_stages = 3;
-  } else {
-    P.n_stages = 1;
+  if (P.n_chunks > 1) {
+    P.off_nodes_in = off; off = align_up(off + (size_t)P.BH * P.n_chunks * DD * P.es, 256);
+    P.off_gch = off;      off = align_up(off + (size_t)P.BH * P.n_chunks * 4, 256);
   }
+  if (P.n_groups > 1) {
+    P.off_gstate = off;  off = align_up(off + (size_t)P.BH * P.n_groups * DD * 4, 256);
+    P.off_gtot = off;    off = align_up(off + (size_t)P.BH * P.n_groups * 4, 256);
+    P.off_gprefix = off; off = align_up(off + (size_t)P.BH * (P.n_groups + 1) * 8, 256);
+    P.off_nodes = off;   off = align_up(off + (size_t)P.BH * P.n_groups * DD * P.es, 256);
+  }
+  P.n_stages = P.n_groups > 1 ? 3 : (P.n_chunks > 1 ? 2 : 1);
   P.ws_bytes = off;
   *p = P;
   return kOK;
