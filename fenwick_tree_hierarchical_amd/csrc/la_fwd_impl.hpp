@@ -288,23 +288,28 @@ __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
 }
 
 // ---------------------------------------------------------------------------
-// fwd_chunk_output: one workgroup per (b,h, chunk); wave w owns query block w
-// (16 queries) and all D/16 output column blocks.
+// fwd_chunk_output: one workgroup per (b,h, chunk).
 //
-// The score tile is formed transposed, S^T = K Q^T, so that after masking
-// each lane holds four consecutive keys of one query: the A operand of the
-// next product P V, with the same key order used for the V operand.  The
-// levels above the chunk are listed once per workgroup (node, gate, lambda
-// level) and each is one product Q node^T on the matrix cores, weighted per
-// query row by lambda and the gate and accumulated into the output.
+// Phase 1 forms the causal score tiles S^T = K Q^T (key block kb <= query
+// block qb), dealt round-robin over the waves, masks them with the gate and
+// the level weight of every (query, key) pair and writes the masked tile P
+// to LDS.  Phase 2 gives each wave a block of 16 output columns for all C
+// query rows: O = P V, then one product Q node^T per occupied level above
+// the chunk, weighted per query row by lambda and the gate.  Owning columns
+// means a wave reads only its 16 rows of each (d_v, d_k) node, so every node
+// crosses from L2 once per chunk.
 template <bool BF16, int C, int D>
 struct ChunkShape {
   using EL = Elem<BF16>;
   static constexpr int NW = output_waves(C), NT = 64 * NW;
   static constexpr int QB = C / 16, DB = D / 16;
-  static constexpr int KSD = (D + EL::kStep - 1) / EL::kStep;
+  static constexpr int NST = QB * (QB + 1) / 2;                // causal score tiles
+  static constexpr int NCB = DB > NW ? DB / NW : 1;           // column blocks per wave
+  static constexpr int KSD = (D + EL::kStep - 1) / EL::kStep;  // k-steps over d
+  static constexpr int KSC = (C + EL::kStep - 1) / EL::kStep;  // k-steps over keys
   static constexpr int EPV = 16 / (BF16 ? 2 : 4), VPR = D / EPV, NV = C * VPR;
   static constexpr int NPF = (NV + NT - 1) / NT;
+  static constexpr int NPL = (C * kMaxLevels + NT - 1) / NT;   // lambda values per thread (bound)
 };
 
 struct LevelEntry {   // one occupied level above the chunk
@@ -319,15 +324,17 @@ __global__ __launch_bounds__(64 * output_waves(C)) void fwd_chunk_output(FwdArgs
   using EL = Elem<BF16>;
   using E = typename EL::T;
   using Frag = typename EL::Frag;
-  constexpr int QB = SH::QB, DB = SH::DB, KSD = SH::KSD;
+  constexpr int QB = SH::QB, DB = SH::DB, KSD = SH::KSD, NCB = SH::NCB, NW = SH::NW;
   constexpr int KPL = EL::kPerLane, KST = EL::kStep, EPV = SH::EPV;
   constexpr int G = state_group(D);
   constexpr int LOG2C = cilog2(C), LOG2G = cilog2(G);
   extern __shared__ __align__(16) unsigned char smem[];
   const int L = a.L;
   const OutLds lay = output_lds(C, D, sizeof(E), L);
+  E* Qs = reinterpret_cast<E*>(smem + lay.q);
   E* Ks = reinterpret_cast<E*>(smem + lay.k);
   E* VT = reinterpret_cast<E*>(smem + lay.vt);
+  E* Ps = reinterpret_cast<E*>(smem + lay.p);
   float* lamS = reinterpret_cast<float*>(smem + lay.lam);
   float* b2c = reinterpret_cast<float*>(smem + lay.b2);
   LevelEntry* list = reinterpret_cast<LevelEntry*>(smem + lay.list);
@@ -346,6 +353,26 @@ __global__ __launch_bounds__(64 * output_waves(C)) void fwd_chunk_output(FwdArgs
   const E* vg = reinterpret_cast<const E*>(a.v) + (bh * T + tc) * D;
   E* og = reinterpret_cast<E*>(a.out) + (bh * T + tc) * D;
   const float* lg = a.lam + (bh * T + tc) * L;
+
+  // ---- loads of this chunk, all issued before the first LDS store
+  uint4 qx[SH::NPF], kx[SH::NPF], vx[SH::NPF];
+  float lx[SH::NPL];
+#pragma unroll
+  for (int p = 0; p < SH::NPF; ++p) {
+    const int idx = tid + p * SH::NT;
+    const int cv = idx / C, r = idx % C;          // rows fastest: transposed LDS writes hit one row
+    qx[p] = kx[p] = vx[p] = make_uint4(0, 0, 0, 0);
+    if (idx < SH::NV && r < nv) {
+      qx[p] = *reinterpret_cast<const uint4*>(qg + r * D + cv * EPV);
+      kx[p] = *reinterpret_cast<const uint4*>(kg + r * D + cv * EPV);
+      vx[p] = *reinterpret_cast<const uint4*>(vg + r * D + cv * EPV);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < SH::NPL; ++p) {
+    const int idx = tid + p * SH::NT;
+    lx[p] = idx < nv * L ? lg[idx] : 0.f;
+  }
 
   if (w == 0) chunk_gate_scan<C>(a.log_a + bh * T, tc, T, b2c);
   if (w == 1) {
@@ -397,147 +424,149 @@ __global__ __launch_bounds__(64 * output_waves(C)) void fwd_chunk_output(FwdArgs
     }
     if (lane == 0) *nlist = __popcll(m);
   }
-  // stage K (row-major), V^T and the lambda rows of this chunk
+  // ---- LDS stores: Q and K row-major, V^T, lambda rows
 #pragma unroll
   for (int p = 0; p < SH::NPF; ++p) {
     const int idx = tid + p * SH::NT;
     if (idx < SH::NV) {
       const int cv = idx / C, r = idx % C;
-      uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
-      if (r < nv) {
-        kx = *reinterpret_cast<const uint4*>(kg + r * D + cv * EPV);
-        vx = *reinterpret_cast<const uint4*>(vg + r * D + cv * EPV);
-      }
-      *reinterpret_cast<uint4*>(Ks + r * lay.ld_row + cv * EPV) = kx;
-      const E* ve = reinterpret_cast<const E*>(&vx);
+      *reinterpret_cast<uint4*>(Qs + r * lay.ld_row + cv * EPV) = qx[p];
+      *reinterpret_cast<uint4*>(Ks + r * lay.ld_row + cv * EPV) = kx[p];
+      const E* ve = reinterpret_cast<const E*>(&vx[p]);
 #pragma unroll
       for (int e = 0; e < EPV; ++e) VT[(cv * EPV + e) * lay.ld_t + r] = ve[e];
     }
   }
-  for (int idx = tid; idx < C * L; idx += SH::NT) lamS[idx] = idx < nv * L ? lg[idx] : 0.f;
-
-  const int qb = w;
-  const bool active = qb < QB;
-  const int iq = 16 * qb + lr;                     // this lane's query (operand side)
-  Frag qf[KSD];
-  if (active) {
 #pragma unroll
-    for (int s = 0; s < KSD; ++s) {
-      const int k0 = s * KST + lq * KPL;
-      if ((D >= KST || k0 < D) && iq < nv) {
-        qf[s] = EL::load(qg + (int64_t)iq * D + k0);
-      } else {
-        if constexpr (BF16) qf[s] = __builtin_bit_cast(Frag, u16x8{0, 0, 0, 0, 0, 0, 0, 0});
-        else qf[s] = 0.f;
-      }
-    }
+  for (int p = 0; p < SH::NPL; ++p) {
+    const int idx = tid + p * SH::NT;
+    if (idx < C * L) lamS[idx] = lx[p];
   }
   __syncthreads();
-  if (!active) return;
 
-  f32x4 acc[DB];
-#pragma unroll
-  for (int n = 0; n < DB; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // ---- masked score tile: S^T = K Q^T for key blocks kb <= qb
-  const float b2q = b2c[iq];
-  float P[QB][4];
-#pragma unroll
-  for (int kb = 0; kb < QB; ++kb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) P[kb][i] = 0.f;
-    if (kb > qb) continue;
+  // ---- phase 1: masked score tiles P[query][key] (bf16 or fp32) in LDS
+  for (int tau = w; tau < SH::NST; tau += NW) {
+    int qb = 0;
+    while ((qb + 1) * (qb + 2) / 2 <= tau) ++qb;
+    const int kb = tau - qb * (qb + 1) / 2;
+    const int iq = 16 * qb + lr;                   // query of this lane (column of S^T)
     f32x4 sv = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KSD; ++s) {
       const int k0 = s * KST + lq * KPL;
       const auto kf = EL::template load_k<D>(Ks + (16 * kb + lr) * lay.ld_row + k0, k0);
-      sv = EL::mma(kf, qf[s], sv);
+      const auto qf = EL::template load_k<D>(Qs + iq * lay.ld_row + k0, k0);
+      sv = EL::mma(kf, qf, sv);
     }
+    const float b2q = b2c[iq];
+    float pv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = 16 * kb + 4 * lq + i;          // key
+      pv[i] = 0.f;
       if (j <= iq && iq < nv) {
         const int lev = fenwick_level_local((unsigned)iq, (unsigned)j);
-        P[kb][i] = sv[i] * __builtin_amdgcn_exp2f(b2q - b2c[j]) * lamS[iq * L + lev];
+        pv[i] = sv[i] * __builtin_amdgcn_exp2f(b2q - b2c[j]) * lamS[iq * L + lev];
       }
+    }
+    E* prow = Ps + iq * lay.ld_p + 16 * kb + 4 * lq;
+    if constexpr (BF16) {
+      *reinterpret_cast<u16x4*>(prow) =
+          u16x4{f32_to_bf16(pv[0]), f32_to_bf16(pv[1]), f32_to_bf16(pv[2]), f32_to_bf16(pv[3])};
+    } else {
+      *reinterpret_cast<float4*>(prow) = make_float4(pv[0], pv[1], pv[2], pv[3]);
     }
   }
-  // ---- O = P V
-  if constexpr (BF16) {
+  __syncthreads();
+
+  // ---- phase 2: this wave's output columns for all query rows
+  const int cb0 = w * NCB;
+  if (cb0 >= DB) return;
+  f32x4 acc[QB][NCB];
 #pragma unroll
-    for (int kb = 0; kb < QB; kb += 2) {
-      if (kb > qb) continue;
-      const bool two = kb + 1 <= qb;
-      u16x8 pu;
+  for (int rb = 0; rb < QB; ++rb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pu[i] = f32_to_bf16(P[kb][i]);
-        pu[4 + i] = two ? f32_to_bf16(P[kb + 1][i]) : (unsigned short)0;
+    for (int n = 0; n < NCB; ++n) acc[rb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // O = P V over keys 0 .. 16 rb + 15 of each row block
+#pragma unroll
+  for (int rb = 0; rb < QB; ++rb) {
+#pragma unroll
+    for (int s = 0; s < SH::KSC; ++s) {
+      if (s * KST > 16 * rb + 15) break;
+      const int k0 = s * KST + lq * KPL;
+      Frag pa;
+      if (k0 / 16 <= rb) pa = EL::load(Ps + (16 * rb + lr) * lay.ld_p + k0);
+      else if constexpr (BF16) pa = __builtin_bit_cast(Frag, u16x8{0, 0, 0, 0, 0, 0, 0, 0});
+      else pa = 0.f;
+#pragma unroll
+      for (int n = 0; n < NCB; ++n) {
+        const auto vf = EL::template load_k<C>(VT + (16 * (cb0 + n) + lr) * lay.ld_t + k0, k0);
+        acc[rb][n] = EL::mma(pa, vf, acc[rb][n]);
       }
-      const bf16x8 pa = __builtin_bit_cast(bf16x8, pu);
-#pragma unroll
-      for (int n = 0; n < DB; ++n) {
-        const E* vrow = VT + (16 * n + lr) * lay.ld_t;
-        const u16x4 v0 = *reinterpret_cast<const u16x4*>(vrow + 16 * kb + 4 * lq);
-        u16x4 v1 = u16x4{0, 0, 0, 0};
-        if (two) v1 = *reinterpret_cast<const u16x4*>(vrow + 16 * (kb + 1) + 4 * lq);
-        const u16x8 vu = u16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        acc[n] = EL::mma(pa, __builtin_bit_cast(bf16x8, vu), acc[n]);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int kb = 0; kb < QB; ++kb) {
-      if (kb > qb) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int n = 0; n < DB; ++n)
-          acc[n] = EL::mma(P[kb][i], VT[(16 * n + lr) * lay.ld_t + 16 * kb + 4 * lq + i], acc[n]);
     }
   }
 
   // ---- occupied levels above the chunk: O += diag(lambda * gate) Q node^T.
   // The row gate exp2(b) and the bucket gate exp2(gate2) are both <= 1.
-  float erow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) erow[i] = __builtin_amdgcn_exp2f(b2c[16 * qb + 4 * lq + i]);
   const int n_lev = *nlist;
-  for (int li = 0; li < n_lev; ++li) {
+  float erow[QB][4];                               // exp2 of each row's in-chunk gate
+#pragma unroll
+  for (int rb = 0; rb < QB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) erow[rb][i] = __builtin_amdgcn_exp2f(b2c[16 * rb + 4 * lq + i]);
+  Frag nf_cur[KSD][NCB], nf_nxt[KSD][NCB];
+  auto load_node = [&](int li, Frag (&dst)[KSD][NCB]) {
     const E* nodeT = reinterpret_cast<const E*>(list[li].node);
+#pragma unroll
+    for (int s2 = 0; s2 < KSD; ++s2) {
+      const int k0 = s2 * KST + lq * KPL;
+#pragma unroll
+      for (int n = 0; n < NCB; ++n)
+        dst[s2][n] = EL::template load_k<D>(nodeT + (16 * (cb0 + n) + lr) * D + k0, k0);
+    }
+  };
+  if (n_lev > 0) load_node(0, nf_cur);
+  for (int li = 0; li < n_lev; ++li) {
+    if (li + 1 < n_lev) load_node(li + 1, nf_nxt);
     const float f = __builtin_amdgcn_exp2f(list[li].gate2);
     const int lev = list[li].lev;
-    f32x4 tmp[DB];
 #pragma unroll
-    for (int n = 0; n < DB; ++n) tmp[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < QB; ++rb) {
+      f32x4 tmp[NCB];
 #pragma unroll
-    for (int s = 0; s < KSD; ++s) {
-      const int k0 = s * KST + lq * KPL;
+      for (int n = 0; n < NCB; ++n) tmp[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int n = 0; n < DB; ++n) {
-        const auto nf = EL::template load_k<D>(nodeT + (16 * n + lr) * D + k0, k0);
-        tmp[n] = EL::mma(qf[s], nf, tmp[n]);
+      for (int s2 = 0; s2 < KSD; ++s2) {
+        const int k0 = s2 * KST + lq * KPL;
+        const auto qf = EL::template load_k<D>(Qs + (16 * rb + lr) * lay.ld_row + k0, k0);
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) tmp[n] = EL::mma(qf, nf_cur[s2][n], tmp[n]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rb + 4 * lq + i;
+        const float wgt = lamS[r * L + lev] * erow[rb][i] * f;
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) acc[rb][n][i] += wgt * tmp[n][i];
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * qb + 4 * lq + i;
-      const float wgt = lamS[r * L + lev] * erow[i] * f;
+    for (int s2 = 0; s2 < KSD; ++s2)
 #pragma unroll
-      for (int n = 0; n < DB; ++n) acc[n][i] += wgt * tmp[n][i];
-    }
+      for (int n = 0; n < NCB; ++n) nf_cur[s2][n] = nf_nxt[s2][n];
   }
 
   // ---- store
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * qb + 4 * lq + i;
-    if (r < nv) {
+  for (int rb = 0; rb < QB; ++rb)
 #pragma unroll
-      for (int n = 0; n < DB; ++n) og[(int64_t)r * D + 16 * n + lr] = EL::from_f32(acc[n][i]);
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rb + 4 * lq + i;
+      if (r < nv) {
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) og[(int64_t)r * D + 16 * (cb0 + n) + lr] = EL::from_f32(acc[rb][n][i]);
+      }
     }
-  }
 }
 
 // ---------------------------------------------------------------------------

@@ -85,16 +85,19 @@ LA_HD constexpr StateLds state_lds(int C, int D, int es, int G) {
   return o;
 }
 struct OutLds {
-  int k, vt, lam, b2, list, total, ld_row, ld_t;
+  int q, k, vt, p, lam, b2, list, total, ld_row, ld_t, ld_p;
 };
 constexpr int kMaxListed = 48;        // occupied levels above the chunk, listed per chunk
 LA_HD constexpr OutLds output_lds(int C, int D, int es, int L) {
   OutLds o{};
   o.ld_row = D + 16 / es;
   o.ld_t = C + 16 / es;
+  o.ld_p = C + 16 / es;
   int off = 0;
+  o.q = off;    off += (C * o.ld_row * es + 255) / 256 * 256;
   o.k = off;    off += (C * o.ld_row * es + 255) / 256 * 256;
   o.vt = off;   off += (D * o.ld_t * es + 255) / 256 * 256;
+  o.p = off;    off += (C * o.ld_p * es + 255) / 256 * 256;
   o.lam = off;  off += (C * L * 4 + 255) / 256 * 256;
   o.b2 = off;   off += (C * 4 + 255) / 256 * 256;
   o.list = off; off += (kMaxListed * 16 + 16 + 255) / 256 * 256;

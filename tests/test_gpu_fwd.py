@@ -62,6 +62,8 @@ SHAPES = [(16, 16), (32, 32), (64, 64), (64, 16), (16, 128), (32, 64), (128, 64)
 def test_shapes_weak_decay_ragged(d, C, dtype):
     """Several full groups, a partial group and a ragged last chunk."""
     dev = need_gpu()
+    if dtype == "f32" and C == 128 and d >= 64:
+        pytest.skip("float32 tiles with C = 128, d >= 64 exceed LDS (rejected with LA_ESHAPE)")
     T = 21 * C + 5
     x = make_inputs(WORKLOADS["small_bf16"], B=1, H=2, T=T, d=d, dtype=dtype, variant="weak_decay",
                     seed=100 + d + C)
@@ -89,14 +91,14 @@ def test_onehot_level_sweep(lev, dtype):
 @pytest.mark.parametrize("T,C", [(1, 16), (2, 16), (15, 16), (17, 16), (100, 64), (1000, 64), (129, 128)])
 def test_short_and_ragged_sequences(T, C):
     dev = need_gpu()
-    x = make_inputs(WORKLOADS["small_bf16"], B=2, H=3, T=T, dtype="f32", variant="weak_decay", seed=T)
+    x = make_inputs(WORKLOADS["small_bf16"], B=2, H=3, T=T, d=32, dtype="f32", variant="weak_decay", seed=T)
     check(x, C, "f32", dev, f"T={T} C={C}")
 
 
 def test_chunk_size_invariance_f32():
     """The chunking is an exact reformulation: every C gives the operator."""
     dev = need_gpu()
-    x = make_inputs(WORKLOADS["small_bf16"], B=1, H=2, T=1500, dtype="f32", variant="weak_decay", seed=5)
+    x = make_inputs(WORKLOADS["small_bf16"], B=1, H=2, T=1500, d=32, dtype="f32", variant="weak_decay", seed=5)
     ref = oracle_fwd(x)
     outs = {}
     for C in (16, 32, 64, 128):
