@@ -103,8 +103,6 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
   constexpr int KPL = EL::kPerLane, KST = EL::kStep, EPV = SH::EPV;
   constexpr StateLds lay = state_lds(C, D, sizeof(E), G);
   extern __shared__ __align__(16) unsigned char smem[];
-  E* VT = reinterpret_cast<E*>(smem + lay.vt);
-  E* KTs = reinterpret_cast<E*>(smem + lay.kts);
   float* b2s = reinterpret_cast<float*>(smem + lay.b2);
 
   const int64_t ng = a.n_groups, nc = a.n_chunks;
@@ -163,7 +161,12 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
 #pragma unroll
     for (int u = 0; u < G; ++u) gc = (u == c) ? gch[u] : gc;
     const float* b2c = b2s + c * C;
-    // stage V^T and K^T gated to the chunk end
+    // this chunk's buffer (selects, not indexing: the layout stays in registers)
+    E* VT = reinterpret_cast<E*>(smem + ((c & 1) ? lay.vt[1] : lay.vt[0]));
+    E* KTs = reinterpret_cast<E*>(smem + ((c & 1) ? lay.kts[1] : lay.kts[0]));
+    // stage V^T and K^T gated to the chunk end (with one buffer, the previous
+    // chunk's readers must be done first)
+    if (lay.nbuf == 1 && c > 0) __syncthreads();
 #pragma unroll
     for (int p = 0; p < SH::NPF; ++p) {
       const int idx = tid + p * SH::NT;
@@ -219,7 +222,8 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
     }
 #pragma unroll
     for (int j = 0; j < NS; ++j) sc2[j] = (j == kk) ? 0.f : sc2[j] + gc;
-    __syncthreads();                               // V^T / K^T of this chunk consumed
+    // with two buffers the next chunk is staged into the other one, which
+    // was last read before this chunk's barrier
   }
 }
 
@@ -227,9 +231,9 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
 // Group tree: per (b,h) and state element, walk the groups with the
 // binary-counter carry.  node[e] = A_e + sum_{j<=k} gate * bucket_j where
 // k = trailing ones of e: the bucket of 2^k groups ending at group e.
-constexpr int kMaxTreeLevels = 28;
-
-template <bool BF16>
+// MAXJ bounds the carry levels (bit length of the group count); the launcher
+// picks the smallest instantiation that covers the sequence.
+template <bool BF16, int MAXJ>
 __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
   using EL = Elem<BF16>;
   using E = typename EL::T;
@@ -240,10 +244,10 @@ __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
   const int elem = blk * 256 + threadIdx.x;
   const bool valid = elem < DD;
   const int64_t ng = a.n_groups;
-  float slot[kMaxTreeLevels];
-  float sc[kMaxTreeLevels];
+  float slot[MAXJ];
+  float sc[MAXJ];
 #pragma unroll
-  for (int j = 0; j < kMaxTreeLevels; ++j) { slot[j] = 0.f; sc[j] = 0.f; }
+  for (int j = 0; j < MAXJ; ++j) { slot[j] = 0.f; sc[j] = 0.f; }
   double pre = 0.0;
   const bool writer = blk == 0 && threadIdx.x == 0;
   const float* gs = a.gstate + bh * ng * DD;
@@ -271,10 +275,10 @@ __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
       for (int64_t x = e; x & 1; x >>= 1) ++kk;
       float nw = Av[u];
 #pragma unroll
-      for (int j = 0; j < kMaxTreeLevels; ++j)
+      for (int j = 0; j < MAXJ; ++j)
         if (j < kk) nw += __builtin_amdgcn_exp2f(sc[j] + g) * slot[j];
 #pragma unroll
-      for (int j = 0; j < kMaxTreeLevels; ++j) {
+      for (int j = 0; j < MAXJ; ++j) {
         if (j == kk) { slot[j] = nw; sc[j] = 0.f; }
         else sc[j] += g;
       }
@@ -444,20 +448,37 @@ __global__ __launch_bounds__(64 * output_waves(C)) void fwd_chunk_output(FwdArgs
   }
   __syncthreads();
 
-  // ---- phase 1: masked score tiles P[query][key] (bf16 or fp32) in LDS
-  for (int tau = w; tau < SH::NST; tau += NW) {
+  // ---- phase 1: masked score tiles P[query][key] (bf16 or fp32).  Every
+  // wave first forms its score tiles S^T = K Q^T; once all waves are past
+  // that point the K tile is dead and P is written over it.
+  constexpr int KT = (SH::NST + NW - 1) / NW;      // score tiles per wave (max)
+  f32x4 sv[KT];
+#pragma unroll
+  for (int u = 0; u < KT; ++u) {
+    sv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int tau = w + u * NW;
+    if (tau >= SH::NST) break;
     int qb = 0;
     while ((qb + 1) * (qb + 2) / 2 <= tau) ++qb;
     const int kb = tau - qb * (qb + 1) / 2;
-    const int iq = 16 * qb + lr;                   // query of this lane (column of S^T)
-    f32x4 sv = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int iq = 16 * qb + lr;
 #pragma unroll
     for (int s = 0; s < KSD; ++s) {
       const int k0 = s * KST + lq * KPL;
       const auto kf = EL::template load_k<D>(Ks + (16 * kb + lr) * lay.ld_row + k0, k0);
       const auto qf = EL::template load_k<D>(Qs + iq * lay.ld_row + k0, k0);
-      sv = EL::mma(kf, qf, sv);
+      sv[u] = EL::mma(kf, qf, sv[u]);
     }
+  }
+  __syncthreads();                                 // K tile no longer read
+#pragma unroll
+  for (int u = 0; u < KT; ++u) {
+    const int tau = w + u * NW;
+    if (tau >= SH::NST) break;
+    int qb = 0;
+    while ((qb + 1) * (qb + 2) / 2 <= tau) ++qb;
+    const int kb = tau - qb * (qb + 1) / 2;
+    const int iq = 16 * qb + lr;                   // query of this lane (column of S^T)
     const float b2q = b2c[iq];
     float pv[4];
 #pragma unroll
@@ -466,7 +487,7 @@ __global__ __launch_bounds__(64 * output_waves(C)) void fwd_chunk_output(FwdArgs
       pv[i] = 0.f;
       if (j <= iq && iq < nv) {
         const int lev = fenwick_level_local((unsigned)iq, (unsigned)j);
-        pv[i] = sv[i] * __builtin_amdgcn_exp2f(b2q - b2c[j]) * lamS[iq * L + lev];
+        pv[i] = sv[u][i] * __builtin_amdgcn_exp2f(b2q - b2c[j]) * lamS[iq * L + lev];
       }
     }
     E* prow = Ps + iq * lay.ld_p + 16 * kb + 4 * lq;
@@ -594,8 +615,14 @@ int launch_fwd_impl(const FwdPlan& p, FwdArgs a, hipStream_t s, hipEvent_t const
   }
   if (p.n_groups > 1) {
     mark();
-    hipLaunchKernelGGL((fwd_group_tree<BF16>), dim3((unsigned)(((D * D + 255) / 256) * p.BH)), dim3(256), 0,
-                       s, a, D);
+    const dim3 grid((unsigned)(((D * D + 255) / 256) * p.BH));
+    const int levels = bit_length(p.n_groups);        // carry levels the walk can reach
+    if (levels <= 8)
+      hipLaunchKernelGGL((fwd_group_tree<BF16, 8>), grid, dim3(256), 0, s, a, D);
+    else if (levels <= 16)
+      hipLaunchKernelGGL((fwd_group_tree<BF16, 16>), grid, dim3(256), 0, s, a, D);
+    else
+      hipLaunchKernelGGL((fwd_group_tree<BF16, 32>), grid, dim3(256), 0, s, a, D);
     ok = ok && hipGetLastError() == hipSuccess;
   }
   ok = ok && hipFuncSetAttribute((const void*)fwd_chunk_output<BF16, C, D>,

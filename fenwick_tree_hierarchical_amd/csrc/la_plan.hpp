@@ -71,23 +71,35 @@ LA_HD constexpr int output_waves(int C) { return C / 16 > 4 ? C / 16 : 4; }
 
 // LDS carve-up (byte offsets).  Tile rows are padded by 16 bytes so that the
 // 16 rows one MFMA operand reads fall in different LDS banks.
+// V^T and gated K^T of a chunk, double-buffered when both copies fit.
 struct StateLds {
-  int vt, kts, b2, total, ld_t;
+  int vt[2], kts[2], b2, total, ld_t, nbuf;
 };
 LA_HD constexpr StateLds state_lds(int C, int D, int es, int G) {
   StateLds o{};
   o.ld_t = C + 16 / es;
+  const int tile = (D * o.ld_t * es + 255) / 256 * 256;
+  const int b2 = (G * C * 4 + 255) / 256 * 256;
+  o.nbuf = 4 * tile + b2 <= kLdsLimit / 2 ? 2 : 1;   // keep two workgroups per CU
   int off = 0;
-  o.vt = off;  off += (D * o.ld_t * es + 255) / 256 * 256;
-  o.kts = off; off += (D * o.ld_t * es + 255) / 256 * 256;
-  o.b2 = off;  off += (G * C * 4 + 255) / 256 * 256;
+  for (int b = 0; b < 2; ++b) {
+    const int bb = b < o.nbuf ? b : 0;
+    if (b < o.nbuf) {
+      o.vt[b] = off;  off += tile;
+      o.kts[b] = off; off += tile;
+    } else {
+      o.vt[b] = o.vt[bb];
+      o.kts[b] = o.kts[bb];
+    }
+  }
+  o.b2 = off;  off += b2;
   o.total = off;
   return o;
 }
 struct OutLds {
   int q, k, vt, p, lam, b2, list, total, ld_row, ld_t, ld_p;
 };
-constexpr int kMaxListed = 48;        // occupied levels above the chunk, listed per chunk
+constexpr int kMaxListed = 40;        // occupied levels above the chunk, listed per chunk
 LA_HD constexpr OutLds output_lds(int C, int D, int es, int L) {
   OutLds o{};
   o.ld_row = D + 16 / es;
@@ -95,9 +107,14 @@ LA_HD constexpr OutLds output_lds(int C, int D, int es, int L) {
   o.ld_p = C + 16 / es;
   int off = 0;
   o.q = off;    off += (C * o.ld_row * es + 255) / 256 * 256;
-  o.k = off;    off += (C * o.ld_row * es + 255) / 256 * 256;
+  // the masked score tile P is written over the K tile once K is dead
+  o.k = off;
+  o.p = off;
+  {
+    const int kb = C * o.ld_row * es, pb = C * o.ld_p * es;
+    off += ((kb > pb ? kb : pb) + 255) / 256 * 256;
+  }
   o.vt = off;   off += (D * o.ld_t * es + 255) / 256 * 256;
-  o.p = off;    off += (C * o.ld_p * es + 255) / 256 * 256;
   o.lam = off;  off += (C * L * 4 + 255) / 256 * 256;
   o.b2 = off;   off += (C * 4 + 255) / 256 * 256;
   o.list = off; off += (kMaxListed * 16 + 16 + 255) / 256 * 256;

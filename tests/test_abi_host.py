@@ -69,12 +69,12 @@ def test_workspace_query():
 
 
 def test_tile_shapes_that_fit():
-    """Every bf16 tile shape fits in LDS; fp32 does too except C = 128 with
-    d >= 64 (its four fp32 tiles exceed 160 KB), which is rejected."""
+    """Every bf16 tile shape fits in LDS; fp32 does too except C = d = 128
+    (its fp32 tiles exceed 160 KB), which is rejected."""
     for dt in (0, 1):
         for d in (16, 32, 64, 128):
             for C in (16, 32, 64, 128):
-                want = ESHAPE if (dt == 0 and C == 128 and d >= 64) else OK
+                want = ESHAPE if (dt == 0 and C == 128 and d == 128) else OK
                 assert ws(1, 1, 1000, d, C, dt)[0] == want, (dt, d, C)
 
 
