@@ -322,8 +322,10 @@ struct LevelEntry {   // one occupied level above the chunk
   int lev;            // lambda level
 };
 
-template <bool BF16, int C, int D>
-__global__ __launch_bounds__(64 * output_waves(C)) void fwd_chunk_output(FwdArgs a) {
+// FULL: the chunk has C rows (every chunk but a ragged last one), so the
+// row bounds checks fold away.
+template <bool BF16, int C, int D, bool FULL>
+__device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned char* smem) {
   using SH = ChunkShape<BF16, C, D>;
   using EL = Elem<BF16>;
   using E = typename EL::T;
@@ -332,7 +334,6 @@ __global__ __launch_bounds__(64 * output_waves(C)) void fwd_chunk_output(FwdArgs
   constexpr int KPL = EL::kPerLane, KST = EL::kStep, EPV = SH::EPV;
   constexpr int G = state_group(D);
   constexpr int LOG2C = cilog2(C), LOG2G = cilog2(G);
-  extern __shared__ __align__(16) unsigned char smem[];
   const int L = a.L;
   const OutLds lay = output_lds(C, D, sizeof(E), L);
   E* Qs = reinterpret_cast<E*>(smem + lay.q);
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(64 * output_waves(C)) void fwd_chunk_output(FwdArgs
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id(), lq = lane >> 4, lr = lane & 15;
   const int64_t T = a.T;
   const int64_t tc = c * C;
-  const int nv = (int)(T - tc < C ? T - tc : C);
+  const int nv = FULL ? C : (int)(T - tc < C ? T - tc : C);
 
   const E* qg = reinterpret_cast<const E*>(a.q) + (bh * T + tc) * D;
   const E* kg = reinterpret_cast<const E*>(a.k) + (bh * T + tc) * D;
@@ -535,7 +536,7 @@ __global__ __launch_bounds__(64 * output_waves(C)) void fwd_chunk_output(FwdArgs
   for (int rb = 0; rb < QB; ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) erow[rb][i] = __builtin_amdgcn_exp2f(b2c[16 * rb + 4 * lq + i]);
-  Frag nf_cur[KSD][NCB], nf_nxt[KSD][NCB];
+  Frag nf_a[KSD][NCB], nf_b[KSD][NCB];
   auto load_node = [&](int li, Frag (&dst)[KSD][NCB]) {
     const E* nodeT = reinterpret_cast<const E*>(list[li].node);
 #pragma unroll
@@ -546,9 +547,7 @@ __global__ __launch_bounds__(64 * output_waves(C)) void fwd_chunk_output(FwdArgs
         dst[s2][n] = EL::template load_k<D>(nodeT + (16 * (cb0 + n) + lr) * D + k0, k0);
     }
   };
-  if (n_lev > 0) load_node(0, nf_cur);
-  for (int li = 0; li < n_lev; ++li) {
-    if (li + 1 < n_lev) load_node(li + 1, nf_nxt);
+  auto contract = [&](int li, const Frag (&nf)[KSD][NCB]) {
     const float f = __builtin_amdgcn_exp2f(list[li].gate2);
     const int lev = list[li].lev;
 #pragma unroll
@@ -561,7 +560,7 @@ __global__ __launch_bounds__(64 * output_waves(C)) void fwd_chunk_output(FwdArgs
         const int k0 = s2 * KST + lq * KPL;
         const auto qf = EL::template load_k<D>(Qs + (16 * rb + lr) * lay.ld_row + k0, k0);
 #pragma unroll
-        for (int n = 0; n < NCB; ++n) tmp[n] = EL::mma(qf, nf_cur[s2][n], tmp[n]);
+        for (int n = 0; n < NCB; ++n) tmp[n] = EL::mma(qf, nf[s2][n], tmp[n]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -571,10 +570,16 @@ __global__ __launch_bounds__(64 * output_waves(C)) void fwd_chunk_output(FwdArgs
         for (int n = 0; n < NCB; ++n) acc[rb][n][i] += wgt * tmp[n][i];
       }
     }
-#pragma unroll
-    for (int s2 = 0; s2 < KSD; ++s2)
-#pragma unroll
-      for (int n = 0; n < NCB; ++n) nf_cur[s2][n] = nf_nxt[s2][n];
+  };
+  // levels in pairs: the next level's fragments load while one is multiplied
+  if (n_lev > 0) load_node(0, nf_a);
+  for (int li = 0; li < n_lev; li += 2) {
+    if (li + 1 < n_lev) load_node(li + 1, nf_b);
+    contract(li, nf_a);
+    if (li + 1 < n_lev) {
+      if (li + 2 < n_lev) load_node(li + 2, nf_a);
+      contract(li + 1, nf_b);
+    }
   }
 
   // ---- store
@@ -588,6 +593,14 @@ __global__ __launch_bounds__(64 * output_waves(C)) void fwd_chunk_output(FwdArgs
         for (int n = 0; n < NCB; ++n) og[(int64_t)r * D + 16 * (cb0 + n) + lr] = EL::from_f32(acc[rb][n][i]);
       }
     }
+}
+
+template <bool BF16, int C, int D>
+__global__ __launch_bounds__(64 * output_waves(C)) void fwd_chunk_output(FwdArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int64_t c = blockIdx.x % a.n_chunks;
+  if ((c + 1) * C <= a.T) chunk_output_body<BF16, C, D, true>(a, smem);
+  else chunk_output_body<BF16, C, D, false>(a, smem);
 }
 
 // ---------------------------------------------------------------------------
