@@ -114,6 +114,26 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
   const int nch = (int)(nc - c0 < G ? nc - c0 : G);
   const int64_t t0 = c0 * C;
   const float* la_bh = a.log_a + bh * T;
+  const E* kb = reinterpret_cast<const E*>(a.k) + (bh * T + t0) * D;
+  const E* vb = reinterpret_cast<const E*>(a.v) + (bh * T + t0) * D;
+  uint4 pk[2][SH::NPF], pv[2][SH::NPF];
+  auto prefetch = [&](int c, uint4 (&dk)[SH::NPF], uint4 (&dv)[SH::NPF]) {
+    const int nv = (int)(T - t0 - (int64_t)c * C < C ? T - t0 - (int64_t)c * C : C);
+#pragma unroll
+    for (int p = 0; p < SH::NPF; ++p) {
+      const int idx = tid + p * SH::NT;
+      const int cv = idx / C, r = idx % C;       // rows fastest: transposed LDS writes hit one row
+      dk[p] = dv[p] = make_uint4(0, 0, 0, 0);
+      if (idx < SH::NV && r < nv) {
+        const int64_t off = ((int64_t)c * C + r) * D + cv * EPV;
+        dk[p] = *reinterpret_cast<const uint4*>(kb + off);
+        dv[p] = *reinterpret_cast<const uint4*>(vb + off);
+      }
+    }
+  };
+  // the first two chunks load while the gates are scanned
+  prefetch(0, pk[0], pv[0]);
+  if (nch > 1) prefetch(1, pk[1], pv[1]);
   for (int c = w; c < nch; c += NW) chunk_gate_scan<C>(la_bh, t0 + (int64_t)c * C, T, b2s + c * C);
   __syncthreads();
 
@@ -127,24 +147,6 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
   if (tid < nch) a.gch[bh * nc + c0 + tid] = b2s[tid * C + C - 1];
   if (tid == 0 && gam + 1 < ng) a.gtot[bh * ng + gam] = gt;
 
-  const E* kb = reinterpret_cast<const E*>(a.k) + (bh * T + t0) * D;
-  const E* vb = reinterpret_cast<const E*>(a.v) + (bh * T + t0) * D;
-  uint4 pk[SH::NPF], pv[SH::NPF];
-  auto prefetch = [&](int c) {
-    const int nv = (int)(T - t0 - (int64_t)c * C < C ? T - t0 - (int64_t)c * C : C);
-#pragma unroll
-    for (int p = 0; p < SH::NPF; ++p) {
-      const int idx = tid + p * SH::NT;
-      const int cv = idx / C, r = idx % C;       // rows fastest: transposed LDS writes hit one row
-      pk[p] = pv[p] = make_uint4(0, 0, 0, 0);
-      if (idx < SH::NV && r < nv) {
-        const int64_t off = ((int64_t)c * C + r) * D + cv * EPV;
-        pk[p] = *reinterpret_cast<const uint4*>(kb + off);
-        pv[p] = *reinterpret_cast<const uint4*>(vb + off);
-      }
-    }
-  };
-
   f32x4 sl[NS][TPW];   // in-group carry: bucket states of levels 1..NS, fp32
   float sc2[NS];       // their lazy log2 gates (from the bucket end to the current chunk start)
 #pragma unroll
@@ -155,8 +157,9 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
   }
   E* nin = reinterpret_cast<E*>(a.nodes_in) + (bh * nc + c0) * D * D;
 
-  prefetch(0);
-  for (int c = 0; c < nch; ++c) {
+#pragma unroll
+  for (int c = 0; c < G; ++c) {
+    if (c >= nch) break;
     float gc = 0.f;
 #pragma unroll
     for (int u = 0; u < G; ++u) gc = (u == c) ? gch[u] : gc;
@@ -172,8 +175,8 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
       const int idx = tid + p * SH::NT;
       if (idx < SH::NV) {
         const int cv = idx / C, r = idx % C;
-        const E* ke = reinterpret_cast<const E*>(&pk[p]);
-        const E* ve = reinterpret_cast<const E*>(&pv[p]);
+        const E* ke = reinterpret_cast<const E*>(&pk[c & 1][p]);
+        const E* ve = reinterpret_cast<const E*>(&pv[c & 1][p]);
         const float u = __builtin_amdgcn_exp2f(gc - b2c[r]);
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
       }
     }
     __syncthreads();
-    if (c + 1 < nch) prefetch(c + 1);
+    if (c + 2 < nch) prefetch(c + 2, pk[c & 1], pv[c & 1]);
 
     int kk = 0;                                   // trailing ones of c
     for (int x = c; x & 1; x >>= 1) ++kk;
@@ -314,18 +317,16 @@ struct ChunkShape {
   static constexpr int EPV = 16 / (BF16 ? 2 : 4), VPR = D / EPV, NV = C * VPR;
   static constexpr int NPF = (NV + NT - 1) / NT;
   static constexpr int NPL = (C * kMaxLevels + NT - 1) / NT;   // lambda values per thread (bound)
-};
-
-struct LevelEntry {   // one occupied level above the chunk
-  const void* node;   // (d_v, d_k) node in global memory
-  float gate2;        // log2 gate from the node's end to the chunk start
-  int lev;            // lambda level
+  static constexpr int NPRE = 2;                              // node fragment buffers per wave
+  // small tiles: the first NPRE levels' nodes load with the chunk; larger
+  // ones load them at the start of phase 2, where the registers are free
+  static constexpr bool EARLY = BF16 && C <= 64 && D <= 64;
 };
 
 // FULL: the chunk has C rows (every chunk but a ragged last one), so the
 // row bounds checks fold away.
 template <bool BF16, int C, int D, bool FULL>
-__device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned char* smem) {
+__device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned char* smem, int64_t item) {
   using SH = ChunkShape<BF16, C, D>;
   using EL = Elem<BF16>;
   using E = typename EL::T;
@@ -342,12 +343,11 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   E* Ps = reinterpret_cast<E*>(smem + lay.p);
   float* lamS = reinterpret_cast<float*>(smem + lay.lam);
   float* b2c = reinterpret_cast<float*>(smem + lay.b2);
-  LevelEntry* list = reinterpret_cast<LevelEntry*>(smem + lay.list);
-  int* nlist = reinterpret_cast<int*>(smem + lay.list + kMaxListed * sizeof(LevelEntry));
+  float* e2c = reinterpret_cast<float*>(smem + lay.e2);
 
   const int64_t nc = a.n_chunks, ng = a.n_groups;
-  const int64_t bh = blockIdx.x / nc;
-  const int64_t c = blockIdx.x % nc;
+  const int64_t bh = item / nc;
+  const int64_t c = item % nc;
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id(), lq = lane >> 4, lr = lane & 15;
   const int64_t T = a.T;
   const int64_t tc = c * C;
@@ -378,58 +378,81 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
     const int idx = tid + p * SH::NT;
     lx[p] = idx < nv * L ? lg[idx] : 0.f;
   }
-
-  if (w == 0) chunk_gate_scan<C>(a.log_a + bh * T, tc, T, b2c);
-  if (w == 1) {
-    // Occupied levels above the chunk, one lane per candidate level:
-    // lanes 1..LOG2G the chunk levels inside the group, lanes 32..62 the
-    // group levels; compacted into `list` with a ballot.
-    const int64_t gam = c / G, cg0 = gam * G;
-    const int ci = (int)(c - cg0);
-    // S[l] = gate from the group start to the start of in-group chunk l
-    const float x = (lane < ci) ? a.gch[bh * nc + cg0 + lane] : 0.f;
-    const float incl = wave_incl_scan(x);
-    float S = __shfl_up(incl, 1, 64);
-    if (lane == 0) S = 0.f;
-    const float pre = __shfl(S, ci, 64);              // group start -> chunk start
-    bool act = false;
-    const void* node = nullptr;
-    float g2 = 0.f;
-    int lev = 0;
-    int src = 0;
-    if (lane >= 1 && lane <= LOG2G) {
-      const int j = lane;
-      if ((ci >> (j - 1)) & 1) {
-        const int el = ((ci >> j) << j) + (1 << (j - 1)) - 1;   // in-group chunk of the node
-        act = true;
-        node = reinterpret_cast<const E*>(a.nodes_in) + (bh * nc + cg0 + el) * D * D;
-        src = el + 1;
-        lev = LOG2C + j;
-      }
-    }
-    const float Se = __shfl(S, src, 64);
-    if (act) g2 = pre - Se;                           // gate from the node's end to the chunk start
-    if (lane >= 32 && lane < 63) {
-      const int i = lane - 31;
-      if (gam > 0 && ((gam >> (i - 1)) & 1)) {
-        const int64_t e = ((gam >> i) << i) + (1ll << (i - 1)) - 1;
-        const double* gp = a.gprefix + bh * (ng + 1);
-        act = true;
-        node = reinterpret_cast<const E*>(a.nodes) + (bh * ng + e) * D * D;
-        g2 = (float)(gp[gam] - gp[e + 1]) + pre;
-        lev = LOG2C + LOG2G + i;
-      }
-    }
-    const unsigned long long m = __ballot(act);
-    if (act) {
-      const int pos = __popcll(m & ((1ull << lane) - 1ull));
-      list[pos].node = node;
-      list[pos].gate2 = g2;
-      list[pos].lev = lev;
-    }
-    if (lane == 0) *nlist = __popcll(m);
+  // wave 0: the chunk's log gates, KPG consecutive tokens per lane
+  constexpr int KPG = C <= 64 ? 1 : 2;
+  float lax[KPG];
+#pragma unroll
+  for (int u = 0; u < KPG; ++u) {
+    const int r = KPG * lane + u;
+    lax[u] = (w == 0 && r < C && tc + r < T) ? a.log_a[bh * T + tc + r] : 0.f;
   }
-  // ---- LDS stores: Q and K row-major, V^T, lambda rows
+
+  // ---- occupied levels above the chunk, found by every wave from the chunk
+  // index alone (lanes 1..LOG2G: chunk levels inside the group; lanes 32..62:
+  // group levels); their gates are loaded now and used at contraction time.
+  const int64_t gam = c / G, cg0 = gam * G;
+  const int ci = (int)(c - cg0);
+  bool act = false;
+  const E* node = nullptr;
+  int lev = 0, src = 0;
+  int64_t eg = 0;
+  if (lane >= 1 && lane <= LOG2G) {
+    const int j = lane;
+    if ((ci >> (j - 1)) & 1) {
+      const int el = ((ci >> j) << j) + (1 << (j - 1)) - 1;   // in-group chunk of the node
+      act = true;
+      node = reinterpret_cast<const E*>(a.nodes_in) + (bh * nc + cg0 + el) * D * D;
+      src = el + 1;
+      lev = LOG2C + j;
+    }
+  }
+  if (lane >= 32 && lane < 63) {
+    const int i = lane - 31;
+    if (gam > 0 && ((gam >> (i - 1)) & 1)) {
+      eg = ((gam >> i) << i) + (1ll << (i - 1)) - 1;
+      act = true;
+      node = reinterpret_cast<const E*>(a.nodes) + (bh * ng + eg) * D * D;
+      lev = LOG2C + LOG2G + i;
+    }
+  }
+  const unsigned long long lmask = __ballot(act);
+  const int n_lev = __popcll(lmask);
+  const float gx = (lane < ci) ? a.gch[bh * nc + cg0 + lane] : 0.f;
+  const double* gp = a.gprefix + bh * (ng + 1);
+  const bool grp = act && lane >= 32;
+  const double gpe = grp ? gp[eg + 1] : 0.0;
+  const double gpg = grp ? gp[gam] : 0.0;
+  auto lane_of = [&](int li) {                      // lane holding list entry li
+    unsigned long long mm = lmask;
+    for (int u = 0; u < li; ++u) mm &= mm - 1ull;
+    return (int)__builtin_ctzll(mm);
+  };
+  auto node_of = [&](int li) {
+    const int ln = lane_of(li);
+    const uint64_t pv = reinterpret_cast<uint64_t>(node);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)pv, ln);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(pv >> 32), ln);
+    return reinterpret_cast<const E*>(((uint64_t)hi << 32) | lo);
+  };
+  const int cb0 = w * NCB;
+  Frag nf[SH::NPRE][KSD][NCB];
+  auto load_node = [&](int li, Frag (&dst)[KSD][NCB]) {
+    const E* nodeT = node_of(li);
+#pragma unroll
+    for (int s2 = 0; s2 < KSD; ++s2) {
+      const int k0 = s2 * KST + lq * KPL;
+#pragma unroll
+      for (int n = 0; n < NCB; ++n)
+        dst[s2][n] = EL::template load_k<D>(nodeT + (16 * (cb0 + n) + lr) * D + k0, k0);
+    }
+  };
+  if (SH::EARLY && cb0 < DB) {
+#pragma unroll
+    for (int u = 0; u < SH::NPRE; ++u)
+      if (u < n_lev) load_node(u, nf[u]);
+  }
+
+  // ---- LDS stores: Q and K row-major, V^T, lambda rows, gate prefix
 #pragma unroll
   for (int p = 0; p < SH::NPF; ++p) {
     const int idx = tid + p * SH::NT;
@@ -446,6 +469,37 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   for (int p = 0; p < SH::NPL; ++p) {
     const int idx = tid + p * SH::NT;
     if (idx < C * L) lamS[idx] = lx[p];
+  }
+  if (w == 0) {
+    // in-chunk prefix of log2(a) and its exp2 (the row gate to the chunk start)
+    // (the same arithmetic as chunk_gate_scan)
+    float y[KPG];
+    if constexpr (KPG == 1) {
+      y[0] = wave_incl_scan(lax[0] * kLog2e);
+    } else {
+      const float x0 = lax[0] * kLog2e, x1 = lax[1] * kLog2e;
+      const float sc = wave_incl_scan(x0 + x1);
+      y[0] = sc - x1;
+      y[1] = sc;
+    }
+#pragma unroll
+    for (int u = 0; u < KPG; ++u) {
+      const int r = KPG * lane + u;
+      if (r < C) {
+        b2c[r] = y[u];
+        e2c[r] = __builtin_amdgcn_exp2f(y[u]);
+      }
+    }
+  }
+  // log2 gate of each level from the node's end to the chunk start
+  float g2 = 0.f;
+  {
+    const float incl = wave_incl_scan(gx);
+    float S = __shfl_up(incl, 1, 64);
+    if (lane == 0) S = 0.f;
+    const float pre = __shfl(S, ci, 64);            // group start -> chunk start
+    const float Se = __shfl(S, src, 64);
+    if (act) g2 = grp ? (float)(gpg - gpe) + pre : pre - Se;
   }
   __syncthreads();
 
@@ -502,8 +556,12 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   __syncthreads();
 
   // ---- phase 2: this wave's output columns for all query rows
-  const int cb0 = w * NCB;
   if (cb0 >= DB) return;
+  if (!SH::EARLY) {
+#pragma unroll
+    for (int u = 0; u < SH::NPRE; ++u)
+      if (u < n_lev) load_node(u, nf[u]);
+  }
   f32x4 acc[QB][NCB];
 #pragma unroll
   for (int rb = 0; rb < QB; ++rb)
@@ -526,30 +584,15 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
         acc[rb][n] = EL::mma(pa, vf, acc[rb][n]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- occupied levels above the chunk: O += diag(lambda * gate) Q node^T.
   // The row gate exp2(b) and the bucket gate exp2(gate2) are both <= 1.
-  const int n_lev = *nlist;
-  float erow[QB][4];                               // exp2 of each row's in-chunk gate
-#pragma unroll
-  for (int rb = 0; rb < QB; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) erow[rb][i] = __builtin_amdgcn_exp2f(b2c[16 * rb + 4 * lq + i]);
-  Frag nf_a[KSD][NCB], nf_b[KSD][NCB];
-  auto load_node = [&](int li, Frag (&dst)[KSD][NCB]) {
-    const E* nodeT = reinterpret_cast<const E*>(list[li].node);
-#pragma unroll
-    for (int s2 = 0; s2 < KSD; ++s2) {
-      const int k0 = s2 * KST + lq * KPL;
-#pragma unroll
-      for (int n = 0; n < NCB; ++n)
-        dst[s2][n] = EL::template load_k<D>(nodeT + (16 * (cb0 + n) + lr) * D + k0, k0);
-    }
-  };
-  auto contract = [&](int li, const Frag (&nf)[KSD][NCB]) {
-    const float f = __builtin_amdgcn_exp2f(list[li].gate2);
-    const int lev = list[li].lev;
+  auto contract = [&](int li, const Frag (&nfr)[KSD][NCB]) {
+    const int ln = lane_of(li);
+    const float f = __builtin_amdgcn_exp2f(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g2), ln)));
+    const int lv = __builtin_amdgcn_readlane(lev, ln);
 #pragma unroll
     for (int rb = 0; rb < QB; ++rb) {
       f32x4 tmp[NCB];
@@ -560,25 +603,29 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
         const int k0 = s2 * KST + lq * KPL;
         const auto qf = EL::template load_k<D>(Qs + (16 * rb + lr) * lay.ld_row + k0, k0);
 #pragma unroll
-        for (int n = 0; n < NCB; ++n) tmp[n] = EL::mma(qf, nf[s2][n], tmp[n]);
+        for (int n = 0; n < NCB; ++n) tmp[n] = EL::mma(qf, nfr[s2][n], tmp[n]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rb + 4 * lq + i;
-        const float wgt = lamS[r * L + lev] * erow[rb][i] * f;
+        const float wgt = lamS[r * L + lv] * e2c[r] * f;
 #pragma unroll
         for (int n = 0; n < NCB; ++n) acc[rb][n][i] += wgt * tmp[n][i];
       }
+      // keep the next row block's Q fragments from being hoisted: live ranges
+      // stay one row block long
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // levels in pairs: the next level's fragments load while one is multiplied
-  if (n_lev > 0) load_node(0, nf_a);
-  for (int li = 0; li < n_lev; li += 2) {
-    if (li + 1 < n_lev) load_node(li + 1, nf_b);
-    contract(li, nf_a);
-    if (li + 1 < n_lev) {
-      if (li + 2 < n_lev) load_node(li + 2, nf_a);
-      contract(li + 1, nf_b);
+  // ring of NPRE fragment buffers: level li uses buffer li % NPRE and, once
+  // multiplied, the buffer takes level li + NPRE
+  for (int base = 0; base < n_lev; base += SH::NPRE) {
+#pragma unroll
+    for (int u = 0; u < SH::NPRE; ++u) {
+      const int li = base + u;
+      if (li >= n_lev) break;
+      contract(li, nf[u]);
+      if (li + SH::NPRE < n_lev) load_node(li + SH::NPRE, nf[u]);
     }
   }
 
@@ -595,12 +642,30 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
     }
 }
 
+// Work item of a block.  Blocks are dealt to the 8 XCDs round-robin (block b
+// runs on XCD b % 8, each XCD with its own L2); renumbered so that every XCD
+// walks one contiguous run of (b,h, chunk) items, the chunks that share the
+// upper level nodes meet in one L2.
+__device__ __forceinline__ int64_t xcd_item(int64_t b, int64_t n) {
+  constexpr int X = 8;
+  const int64_t q = n / X, r = n % X, x = b % X, i = b / X;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
+// The kernel is bound by memory latency, so where the register budget of 4
+// waves per SIMD (128) costs no spills -- bf16 tiles up to 64 x 64, those
+// that load the first nodes early -- the compiler is held to it.
 template <bool BF16, int C, int D>
-__global__ __launch_bounds__(64 * output_waves(C)) void fwd_chunk_output(FwdArgs a) {
+constexpr int output_min_waves() { return ChunkShape<BF16, C, D>::EARLY ? 4 : 1; }
+
+template <bool BF16, int C, int D>
+__global__ __launch_bounds__(64 * output_waves(C)) __attribute__((amdgpu_waves_per_eu(output_min_waves<BF16, C, D>(), 8)))
+void fwd_chunk_output(FwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int64_t c = blockIdx.x % a.n_chunks;
-  if ((c + 1) * C <= a.T) chunk_output_body<BF16, C, D, true>(a, smem);
-  else chunk_output_body<BF16, C, D, false>(a, smem);
+  const int64_t item = xcd_item(blockIdx.x, gridDim.x);
+  const int64_t c = item % a.n_chunks;
+  if ((c + 1) * C <= a.T) chunk_output_body<BF16, C, D, true>(a, smem, item);
+  else chunk_output_body<BF16, C, D, false>(a, smem, item);
 }
 
 // ---------------------------------------------------------------------------

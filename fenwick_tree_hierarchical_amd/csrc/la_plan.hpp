@@ -97,9 +97,8 @@ LA_HD constexpr StateLds state_lds(int C, int D, int es, int G) {
   return o;
 }
 struct OutLds {
-  int q, k, vt, p, lam, b2, list, total, ld_row, ld_t, ld_p;
+  int q, k, vt, p, lam, b2, e2, total, ld_row, ld_t, ld_p;
 };
-constexpr int kMaxListed = 40;        // occupied levels above the chunk, listed per chunk
 LA_HD constexpr OutLds output_lds(int C, int D, int es, int L) {
   OutLds o{};
   o.ld_row = D + 16 / es;
@@ -117,7 +116,7 @@ LA_HD constexpr OutLds output_lds(int C, int D, int es, int L) {
   o.vt = off;   off += (D * o.ld_t * es + 255) / 256 * 256;
   o.lam = off;  off += (C * L * 4 + 255) / 256 * 256;
   o.b2 = off;   off += (C * 4 + 255) / 256 * 256;
-  o.list = off; off += (kMaxListed * 16 + 16 + 255) / 256 * 256;
+  o.e2 = off;   off += (C * 4 + 255) / 256 * 256;
   o.total = off;
   return o;
 }
