@@ -325,13 +325,18 @@ struct ChunkShape {
 
 // FULL: the chunk has C rows (every chunk but a ragged last one), so the
 // row bounds checks fold away.
+//
+// Phase 2 works on transposed tiles: with the MFMA operands swapped
+// (V^T P^T and node Q^T) a lane holds one query row and four consecutive
+// output columns, so each row weight is one value per lane and each output
+// row slice is one contiguous store.
 template <bool BF16, int C, int D, bool FULL>
 __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned char* smem, int64_t item) {
   using SH = ChunkShape<BF16, C, D>;
   using EL = Elem<BF16>;
   using E = typename EL::T;
   using Frag = typename EL::Frag;
-  constexpr int QB = SH::QB, DB = SH::DB, KSD = SH::KSD, NCB = SH::NCB, NW = SH::NW;
+  constexpr int QB = SH::QB, DB = SH::DB, KSD = SH::KSD, NCB = SH::NCB, NW = SH::NW, NPRE = SH::NPRE;
   constexpr int KPL = EL::kPerLane, KST = EL::kStep, EPV = SH::EPV;
   constexpr int G = state_group(D);
   constexpr int LOG2C = cilog2(C), LOG2G = cilog2(G);
@@ -375,8 +380,10 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   }
 #pragma unroll
   for (int p = 0; p < SH::NPL; ++p) {
+    lx[p] = 0.f;
+    if (p * SH::NT >= C * L) continue;
     const int idx = tid + p * SH::NT;
-    lx[p] = idx < nv * L ? lg[idx] : 0.f;
+    if (idx < nv * L) lx[p] = lg[idx];
   }
   // wave 0: the chunk's log gates, KPG consecutive tokens per lane
   constexpr int KPG = C <= 64 ? 1 : 2;
@@ -393,7 +400,7 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   const int64_t gam = c / G, cg0 = gam * G;
   const int ci = (int)(c - cg0);
   bool act = false;
-  const E* node = nullptr;
+  int64_t off = 0;                                  // node offset from its base (elements)
   int lev = 0, src = 0;
   int64_t eg = 0;
   if (lane >= 1 && lane <= LOG2G) {
@@ -401,7 +408,7 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
     if ((ci >> (j - 1)) & 1) {
       const int el = ((ci >> j) << j) + (1 << (j - 1)) - 1;   // in-group chunk of the node
       act = true;
-      node = reinterpret_cast<const E*>(a.nodes_in) + (bh * nc + cg0 + el) * D * D;
+      off = (bh * nc + cg0 + el) * D * D;
       src = el + 1;
       lev = LOG2C + j;
     }
@@ -411,31 +418,34 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
     if (gam > 0 && ((gam >> (i - 1)) & 1)) {
       eg = ((gam >> i) << i) + (1ll << (i - 1)) - 1;
       act = true;
-      node = reinterpret_cast<const E*>(a.nodes) + (bh * ng + eg) * D * D;
+      off = (bh * ng + eg) * D * D;
       lev = LOG2C + LOG2G + i;
     }
   }
   const unsigned long long lmask = __ballot(act);
   const int n_lev = __popcll(lmask);
+  // compact the list: lane li receives the lane that holds entry li (lane 63
+  // is never an entry and takes the inactive lanes' writes)
+  const int pos = __popcll(lmask & ((1ull << lane) - 1ull));
+  const int ent = __builtin_amdgcn_ds_permute((act ? pos : 63) << 2, lane);
   const float gx = (lane < ci) ? a.gch[bh * nc + cg0 + lane] : 0.f;
   const double* gp = a.gprefix + bh * (ng + 1);
   const bool grp = act && lane >= 32;
   const double gpe = grp ? gp[eg + 1] : 0.0;
   const double gpg = grp ? gp[gam] : 0.0;
-  auto lane_of = [&](int li) {                      // lane holding list entry li
-    unsigned long long mm = lmask;
-    for (int u = 0; u < li; ++u) mm &= mm - 1ull;
-    return (int)__builtin_ctzll(mm);
-  };
+  // node of entry li: a kernel-argument base plus an offset, so its loads
+  // stay global (not flat) loads
   auto node_of = [&](int li) {
-    const int ln = lane_of(li);
-    const uint64_t pv = reinterpret_cast<uint64_t>(node);
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)pv, ln);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(pv >> 32), ln);
-    return reinterpret_cast<const E*>(((uint64_t)hi << 32) | lo);
+    const int el = __builtin_amdgcn_readlane(ent, li);
+    const uint64_t o64 = (uint64_t)off;
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)o64, el);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(o64 >> 32), el);
+    const int64_t o = (int64_t)(((uint64_t)hi << 32) | lo);
+    return (el >= 32 ? reinterpret_cast<const E*>(a.nodes) : reinterpret_cast<const E*>(a.nodes_in)) + o;
   };
   const int cb0 = w * NCB;
-  Frag nf[SH::NPRE][KSD][NCB];
+  Frag nf[NPRE][KSD][NCB];
+  // node fragments as the A operand: row d_v, k-slice of d_k
   auto load_node = [&](int li, Frag (&dst)[KSD][NCB]) {
     const E* nodeT = node_of(li);
 #pragma unroll
@@ -448,7 +458,7 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   };
   if (SH::EARLY && cb0 < DB) {
 #pragma unroll
-    for (int u = 0; u < SH::NPRE; ++u)
+    for (int u = 0; u < NPRE; ++u)
       if (u < n_lev) load_node(u, nf[u]);
   }
 
@@ -467,12 +477,13 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   }
 #pragma unroll
   for (int p = 0; p < SH::NPL; ++p) {
+    if (p * SH::NT >= C * L) continue;
     const int idx = tid + p * SH::NT;
     if (idx < C * L) lamS[idx] = lx[p];
   }
   if (w == 0) {
-    // in-chunk prefix of log2(a) and its exp2 (the row gate to the chunk start)
-    // (the same arithmetic as chunk_gate_scan)
+    // in-chunk prefix of log2(a) and its exp2 (the row gate to the chunk start),
+    // the same arithmetic as chunk_gate_scan
     float y[KPG];
     if constexpr (KPG == 1) {
       y[0] = wave_incl_scan(lax[0] * kLog2e);
@@ -534,18 +545,21 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
     while ((qb + 1) * (qb + 2) / 2 <= tau) ++qb;
     const int kb = tau - qb * (qb + 1) / 2;
     const int iq = 16 * qb + lr;                   // query of this lane (column of S^T)
+    const int j0 = 16 * kb + 4 * lq;               // its four keys j0 .. j0 + 3
     const float b2q = b2c[iq];
+    const float4 b2k = *reinterpret_cast<const float4*>(b2c + j0);
+    const float bk[4] = {b2k.x, b2k.y, b2k.z, b2k.w};
     float pv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int j = 16 * kb + 4 * lq + i;          // key
-      pv[i] = 0.f;
-      if (j <= iq && iq < nv) {
-        const int lev = fenwick_level_local((unsigned)iq, (unsigned)j);
-        pv[i] = sv[u][i] * __builtin_amdgcn_exp2f(b2q - b2c[j]) * lamS[iq * L + lev];
-      }
+      // computed for every key and then masked: the level stays within
+      // 0..log2 C and the gate exponent past the diagonal is discarded
+      const int j = j0 + i;
+      const int lv = fenwick_level_local((unsigned)iq, (unsigned)j);
+      const float val = sv[u][i] * __builtin_amdgcn_exp2f(b2q - bk[i]) * lamS[iq * L + lv];
+      pv[i] = (j <= iq && iq < nv) ? val : 0.f;
     }
-    E* prow = Ps + iq * lay.ld_p + 16 * kb + 4 * lq;
+    E* prow = Ps + iq * lay.ld_p + j0;
     if constexpr (BF16) {
       *reinterpret_cast<u16x4*>(prow) =
           u16x4{f32_to_bf16(pv[0]), f32_to_bf16(pv[1]), f32_to_bf16(pv[2]), f32_to_bf16(pv[3])};
@@ -555,11 +569,12 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   }
   __syncthreads();
 
-  // ---- phase 2: this wave's output columns for all query rows
+  // ---- phase 2: this wave's output columns for all query rows, transposed:
+  // acc[rb][n][i] = O[16 rb + lr][16 (cb0 + n) + 4 lq + i]
   if (cb0 >= DB) return;
   if (!SH::EARLY) {
 #pragma unroll
-    for (int u = 0; u < SH::NPRE; ++u)
+    for (int u = 0; u < NPRE; ++u)
       if (u < n_lev) load_node(u, nf[u]);
   }
   f32x4 acc[QB][NCB];
@@ -567,21 +582,21 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   for (int rb = 0; rb < QB; ++rb)
 #pragma unroll
     for (int n = 0; n < NCB; ++n) acc[rb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // O = P V over keys 0 .. 16 rb + 15 of each row block
+  // O^T = V^T P^T over keys 0 .. 16 rb + 15 of each row block
 #pragma unroll
   for (int rb = 0; rb < QB; ++rb) {
 #pragma unroll
     for (int s = 0; s < SH::KSC; ++s) {
       if (s * KST > 16 * rb + 15) break;
       const int k0 = s * KST + lq * KPL;
-      Frag pa;
-      if (k0 / 16 <= rb) pa = EL::load(Ps + (16 * rb + lr) * lay.ld_p + k0);
-      else if constexpr (BF16) pa = __builtin_bit_cast(Frag, u16x8{0, 0, 0, 0, 0, 0, 0, 0});
-      else pa = 0.f;
+      Frag pb;
+      if (k0 / 16 <= rb) pb = EL::load(Ps + (16 * rb + lr) * lay.ld_p + k0);
+      else if constexpr (BF16) pb = __builtin_bit_cast(Frag, u16x8{0, 0, 0, 0, 0, 0, 0, 0});
+      else pb = 0.f;
 #pragma unroll
       for (int n = 0; n < NCB; ++n) {
         const auto vf = EL::template load_k<C>(VT + (16 * (cb0 + n) + lr) * lay.ld_t + k0, k0);
-        acc[rb][n] = EL::mma(pa, vf, acc[rb][n]);
+        acc[rb][n] = EL::mma(vf, pb, acc[rb][n]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -590,9 +605,9 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   // ---- occupied levels above the chunk: O += diag(lambda * gate) Q node^T.
   // The row gate exp2(b) and the bucket gate exp2(gate2) are both <= 1.
   auto contract = [&](int li, const Frag (&nfr)[KSD][NCB]) {
-    const int ln = lane_of(li);
-    const float f = __builtin_amdgcn_exp2f(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g2), ln)));
-    const int lv = __builtin_amdgcn_readlane(lev, ln);
+    const int el = __builtin_amdgcn_readlane(ent, li);
+    const float f = __builtin_amdgcn_exp2f(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g2), el)));
+    const int lv = __builtin_amdgcn_readlane(lev, el);
 #pragma unroll
     for (int rb = 0; rb < QB; ++rb) {
       f32x4 tmp[NCB];
@@ -603,15 +618,14 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
         const int k0 = s2 * KST + lq * KPL;
         const auto qf = EL::template load_k<D>(Qs + (16 * rb + lr) * lay.ld_row + k0, k0);
 #pragma unroll
-        for (int n = 0; n < NCB; ++n) tmp[n] = EL::mma(qf, nfr[s2][n], tmp[n]);
+        for (int n = 0; n < NCB; ++n) tmp[n] = EL::mma(nfr[s2][n], qf, tmp[n]);
       }
+      const int r = 16 * rb + lr;                   // this lane's query row
+      const float wgt = lamS[r * L + lv] * e2c[r] * f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rb + 4 * lq + i;
-        const float wgt = lamS[r * L + lv] * e2c[r] * f;
+      for (int n = 0; n < NCB; ++n)
 #pragma unroll
-        for (int n = 0; n < NCB; ++n) acc[rb][n][i] += wgt * tmp[n][i];
-      }
+        for (int i = 0; i < 4; ++i) acc[rb][n][i] += wgt * tmp[n][i];
       // keep the next row block's Q fragments from being hoisted: live ranges
       // stay one row block long
       __builtin_amdgcn_sched_barrier(0);
@@ -619,27 +633,33 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   };
   // ring of NPRE fragment buffers: level li uses buffer li % NPRE and, once
   // multiplied, the buffer takes level li + NPRE
-  for (int base = 0; base < n_lev; base += SH::NPRE) {
+  for (int base = 0; base < n_lev; base += NPRE) {
 #pragma unroll
-    for (int u = 0; u < SH::NPRE; ++u) {
+    for (int u = 0; u < NPRE; ++u) {
       const int li = base + u;
       if (li >= n_lev) break;
       contract(li, nf[u]);
-      if (li + SH::NPRE < n_lev) load_node(li + SH::NPRE, nf[u]);
+      if (li + NPRE < n_lev) load_node(li + NPRE, nf[u]);
     }
   }
 
-  // ---- store
+  // ---- store: four consecutive output columns of one row per lane and block
 #pragma unroll
-  for (int rb = 0; rb < QB; ++rb)
+  for (int rb = 0; rb < QB; ++rb) {
+    const int r = 16 * rb + lr;
+    if (r < nv) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rb + 4 * lq + i;
-      if (r < nv) {
-#pragma unroll
-        for (int n = 0; n < NCB; ++n) og[(int64_t)r * D + 16 * (cb0 + n) + lr] = EL::from_f32(acc[rb][n][i]);
+      for (int n = 0; n < NCB; ++n) {
+        E* o = og + (int64_t)r * D + 16 * (cb0 + n) + 4 * lq;
+        if constexpr (BF16) {
+          *reinterpret_cast<u16x4*>(o) = u16x4{f32_to_bf16(acc[rb][n][0]), f32_to_bf16(acc[rb][n][1]),
+                                               f32_to_bf16(acc[rb][n][2]), f32_to_bf16(acc[rb][n][3])};
+        } else {
+          *reinterpret_cast<float4*>(o) = make_float4(acc[rb][n][0], acc[rb][n][1], acc[rb][n][2], acc[rb][n][3]);
+        }
       }
     }
+  }
 }
 
 // Work item of a block.  Blocks are dealt to the 8 XCDs round-robin (block b
