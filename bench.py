@@ -227,7 +227,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-heads", type=int, default=48)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pmc-summary", default=None)
     ap.add_argument("--rocpd-summary", default=None)

@@ -317,10 +317,10 @@ struct ChunkShape {
   static constexpr int EPV = 16 / (BF16 ? 2 : 4), VPR = D / EPV, NV = C * VPR;
   static constexpr int NPF = (NV + NT - 1) / NT;
   static constexpr int NPL = (C * kMaxLevels + NT - 1) / NT;   // lambda values per thread (bound)
-  static constexpr int NPRE = 2;                              // node fragment buffers per wave
   // small tiles: the first NPRE levels' nodes load with the chunk; larger
   // ones load them at the start of phase 2, where the registers are free
   static constexpr bool EARLY = BF16 && C <= 64 && D <= 64;
+  static constexpr int NPRE = EARLY ? 4 : 2;                  // node fragment buffers per wave
 };
 
 // FULL: the chunk has C rows (every chunk but a ragged last one), so the
