@@ -8,7 +8,7 @@ every input already resident in HBM.  Prints ONE JSON line:
 
   value          tokens/s, a token being one sequence position across all
                  H heads (B*T per step)
-  roofline       for the dominant kernel (the output kernel): algorithmic
+  roofline       for the dominant kernel (fwd_chunk_output): algorithmic
                  bytes per launch / its mean duration from HIP events
                  recorded on the launch stream over the timed steps,
                  against 8 TB/s; `traffic` is the counter-measured HBM
@@ -16,7 +16,9 @@ every input already resident in HBM.  Prints ONE JSON line:
                  taken on the current kernel source, else null
   cpu_baseline   the float64 oracle's Fenwick recurrence timed on the host
                  on a bounded sample of the same workload
-  stages, mfma   per-kernel times and the matrix-core share
+  stages         per kernel (chunk_states, group_tree, chunk_output): mean
+                 time, algorithmic bytes, GB/s and counter traffic
+  mfma           the matrix-core share of the whole forward
   decode         256 decode steps of the decode workload (64 x 16 heads,
                  positions 32768..33023)
 
@@ -27,6 +29,10 @@ Other modes (profiling helpers):
                       counter run sees a kernel of known traffic
   --rocpd-summary F   markdown table of kernel statistics from a rocprofv3
                       results database (.db) or kernel_stats.csv
+  --pmc-profile FETCH_DIR WRITE_DIR
+                      write profiles/fwd_chunk_output_train16k_pmc.json from
+                      a FETCH_SIZE and a WRITE_SIZE run (both taken with
+                      --copy-calibration)
 """
 
 from __future__ import annotations
@@ -49,7 +55,9 @@ BF16_MFMA_PEAK_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
 KERNEL_SOURCES = ["fenwick_tree_hierarchical_amd/csrc/la_fwd_impl.hpp",
                   "fenwick_tree_hierarchical_amd/csrc/la_device.hpp",
                   "fenwick_tree_hierarchical_amd/csrc/la_plan.hpp"]
-PMC_FILE = os.path.join(ROOT, "profiles", "fwd_output_train16k_pmc.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "fwd_chunk_output_train16k_pmc.json")
+# kernel name fragment -> stage name used in the JSON line
+KERNELS = {"fwd_chunk_states": "chunk_states", "fwd_group_tree": "group_tree", "fwd_chunk_output": "chunk_output"}
 
 
 def log(*a):
@@ -64,23 +72,42 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_counts(w, B, H, T, d, C, L, es):
+def algorithmic_counts(w, B, H, T, d, C, L, es, G=8):
     """Work the method itself does (no dense-equivalent inflation).
 
-    Bytes: the essential I/O, q, k, v, out in the layer dtype plus log_a and
-    lambda in float32.  Flops: the dense C x C intra-chunk tiles
-    2 C^2 (d_k + d_v) per chunk, one chunk state 2 C d_k d_v per chunk, and
-    2 C d_k d_v per chunk for each occupied chunk-or-group level
-    (popcount of the chunk index)."""
+    Bytes: the essential I/O -- q, k, v, out in the layer dtype plus log_a
+    and lambda in float32 -- and, per kernel, the state bytes it must move:
+      chunk_states   reads k, v, log_a; writes the bucket node ending at each
+                     chunk inside its group of G chunks (bf16) and each
+                     group's state (fp32)
+      group_tree     reads the group states; writes the bucket node ending at
+                     each group (bf16)
+      chunk_output   reads q, k, v, log_a, lambda and every bucket node once;
+                     writes out
+    Flops: the dense C x C intra-chunk tiles 2 C^2 (d_k + d_v) per chunk, one
+    chunk state 2 C d_k d_v per chunk, and 2 C d_k d_v per chunk for each
+    occupied chunk-or-group level (popcount of the chunk index)."""
     n_chunks = math.ceil(T / C)
+    n_groups = math.ceil(n_chunks / G)
+    BH = B * H
     per_head_token_bytes = 4 * d * es + 4 + 4 * L
-    bytes_total = B * H * T * per_head_token_bytes
+    bytes_io = BH * T * per_head_token_bytes
+    node = d * d * es
+    nodes_in = sum(1 for c in range(n_chunks) if c % G != G - 1 and c + 1 < n_chunks)
+    nodes_grp = max(n_groups - 1, 0)
+    kern = {
+        "chunk_states": BH * (T * (2 * d * es + 4) + nodes_in * node + nodes_grp * d * d * 4 + n_chunks * 4
+                              + n_groups * 4),
+        "group_tree": BH * (nodes_grp * d * d * 4 + n_groups * 4 + nodes_grp * node + (n_groups + 1) * 8),
+        "chunk_output": bytes_io + BH * ((nodes_in + nodes_grp) * node + n_chunks * 4 + (n_groups + 1) * 8),
+    }
     intra = n_chunks * 2 * C * C * (d + d)
     states = n_chunks * 2 * C * d * d
     contr = sum(bin(c).count("1") for c in range(n_chunks)) * 2 * C * d * d
-    flops = B * H * (intra + states + contr)
-    return dict(per_head_token_bytes=per_head_token_bytes, bytes=bytes_total, flops_intra=B * H * intra,
-                flops_states=B * H * states, flops_contractions=B * H * contr, flops=flops)
+    flops = BH * (intra + states + contr)
+    return dict(per_head_token_bytes=per_head_token_bytes, bytes_io=bytes_io, kernel_bytes=kern,
+                node_bytes_per_bh=(nodes_in + nodes_grp) * node, flops_intra=BH * intra,
+                flops_states=BH * states, flops_contractions=BH * contr, flops=flops)
 
 
 def cpu_baseline(w, heads: int):
@@ -108,16 +135,16 @@ def cpu_baseline(w, heads: int):
                       f"({heads}/{w.H} of one sequence = {tokens:.0f} tokens) in {dt:.1f} s, one thread"}
 
 
-def pmc_traffic(src_hash: str, launches_bytes: float):
-    """HBM traffic per output-kernel launch from the committed counter summary,
-    when it was taken on the current kernel source."""
+def pmc_traffic(src_hash: str):
+    """HBM traffic per launch of each forward kernel from the committed
+    counter summary, when it was taken on the current kernel source."""
     if not os.path.exists(PMC_FILE):
         return None, "no counter summary"
     with open(PMC_FILE) as f:
         s = json.load(f)
     if s.get("kernel_source_hash") != src_hash:
         return None, "kernel changed since the counters were taken"
-    return s.get("traffic_bytes_per_launch"), None
+    return s.get("per_kernel_traffic_bytes"), None
 
 
 def bench_decode(la, torch, dev, steps=256):
@@ -196,6 +223,53 @@ def pmc_summary(d: str):
     print(json.dumps(out, indent=1))
 
 
+def _pmc_means(d: str, counter: str):
+    import csv
+    acc = {}
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    acc.setdefault(r.get("Kernel_Name", "?"), []).append(float(r.get("Counter_Value", 0)))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def pmc_profile(fetch_dir: str, write_dir: str, out_path: str):
+    """Write the counter summary bench.py reads: per forward kernel, HBM bytes
+    per launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled
+    by what the same counter reads for a plain device copy of known size (the
+    1 GiB copy that --copy-calibration adds to every step)."""
+    fetch, write = _pmc_means(fetch_dir, "FETCH_SIZE"), _pmc_means(write_dir, "WRITE_SIZE")
+    copy = [k for k in fetch if "copyBuffer" in k]
+    big = max(copy, key=lambda k: fetch[k]) if copy else None
+    if big is None or big not in write:
+        raise SystemExit("no copy kernel in the counter runs: run them with --copy-calibration")
+    gib_kib = float(1 << 20)
+    ff, wf = gib_kib / fetch[big], gib_kib / write[big]
+    per_kib, traffic = {}, {}
+    for frag, stage in KERNELS.items():
+        names = [k for k in fetch if frag in k]
+        if not names:
+            continue
+        n = names[0]
+        per_kib[stage] = {"kernel": n, "FETCH_SIZE": fetch[n], "WRITE_SIZE": write.get(n, 0.0)}
+        traffic[stage] = (fetch[n] * ff + write.get(n, 0.0) * wf) * 1024
+    res = {"workload": "train_16k_bf16 (B=8,H=16,T=16384,d=64,C=64,bf16)",
+           "kernel_source_hash": kernel_source_hash(),
+           "calibration": {"kernel": big, "bytes": "1 GiB read + 1 GiB written",
+                           "fetch_kib": fetch[big], "write_kib": write[big], "fetch_factor": ff, "write_factor": wf},
+           "per_launch_kib": per_kib, "per_kernel_traffic_bytes": traffic,
+           "commands": [
+               "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/prof/fetch "
+               "-o fetch -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-decode --copy-calibration",
+               "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/prof/write "
+               "-o write -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-decode --copy-calibration",
+               "python bench.py --pmc-profile gpurun_out/prof/fetch gpurun_out/prof/write"]}
+    with open(out_path, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+
+
 def rocpd_summary(path: str):
     """Markdown table of per-kernel dispatch statistics from a rocprofv3
     output (SQLite database from the default format, or a kernel_stats.csv)."""
@@ -230,6 +304,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=48)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pmc-summary", default=None)
+    ap.add_argument("--pmc-profile", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None)
     ap.add_argument("--rocpd-summary", default=None)
     args = ap.parse_args()
     if args.rocpd_summary:
@@ -237,6 +312,9 @@ def main():
         return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary)
+        return
+    if args.pmc_profile:
+        pmc_profile(args.pmc_profile[0], args.pmc_profile[1], PMC_FILE)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -256,7 +334,8 @@ def main():
     nws = la.loglinear_fwd_workspace(w.B, w.H, w.T, w.dk, w.dv, w.C, torch.bfloat16)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     n_st = la.loglinear_fwd_num_stages(w.B, w.H, w.T, w.dk, w.dv, w.C, torch.bfloat16)
-    stage_names = (["group_state", "group_tree", "output"] if n_st == 3 else ["output"])
+    stage_names = {3: ["chunk_states", "group_tree", "chunk_output"], 2: ["chunk_states", "chunk_output"],
+                   1: ["chunk_output"]}[n_st]
     copy_src = copy_dst = None
     if args.copy_calibration:
         copy_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -288,10 +367,12 @@ def main():
     tokens = w.B * w.T
     value = tokens / (wall / args.steps)
     cnt = algorithmic_counts(w, w.B, w.H, w.T, w.dk, w.C, w.L, 2)
-    out_ms = stage_ms[-1]
-    achieved = cnt["bytes"] / (out_ms * 1e-3) / 1e9
+    st_ms = dict(zip(stage_names, stage_ms))
     src_hash = kernel_source_hash()
-    traffic, why = pmc_traffic(src_hash, cnt["bytes"])
+    traffic, why = pmc_traffic(src_hash)
+    out_ms = st_ms["chunk_output"]
+    out_bytes = cnt["kernel_bytes"]["chunk_output"]
+    achieved = out_bytes / (out_ms * 1e-3) / 1e9
     fwd_ms = sum(stage_ms)
     result = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -299,12 +380,19 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d_k": w.dk, "d_v": w.dv, "chunk": w.C,
                    "levels": w.L, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "fwd_output", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "alg_bytes_per_launch": cnt["bytes"],
-                     "alg_bytes_per_head_token": cnt["per_head_token_bytes"],
-                     "traffic_note": why, "kernel_source_hash": src_hash},
-        "stages": {n: {"ms": m} for n, m in zip(stage_names, stage_ms)},
+        "roofline": {"bound": "hbm", "kernel": "fwd_chunk_output", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic.get("chunk_output") if traffic else None,
+                     "alg_bytes_per_launch": out_bytes,
+                     "alg_bytes_note": f"{cnt['per_head_token_bytes']} B per head-token of q, k, v, out, log_a, "
+                                       f"lambda plus one read of every bucket node "
+                                       f"({cnt['node_bytes_per_bh']} B per (b,h))",
+                     "mean_launch_ms": out_ms, "traffic_note": why, "kernel_source_hash": src_hash},
+        "stages": {n: {"ms": m, "alg_bytes": cnt["kernel_bytes"][n],
+                       "alg_gbps": cnt["kernel_bytes"][n] / (m * 1e-3) / 1e9,
+                       "frac_hbm": cnt["kernel_bytes"][n] / (m * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                       "traffic_bytes": (traffic or {}).get(n)}
+                   for n, m in st_ms.items()},
         "mfma": {"alg_tflop": cnt["flops"] / 1e12,
                  "achieved_tflops_whole_fwd": cnt["flops"] / (fwd_ms * 1e-3) / 1e12,
                  "frac_of_bf16_peak_whole_fwd": cnt["flops"] / (fwd_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
