@@ -64,11 +64,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def _code_only(text: str) -> str:
+    """C++ source without comments and whitespace: what the compiler sees."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return "".join(text.split())
+
+
+def kernel_source_hash(read=None) -> str:
+    """Hash of the forward kernels' source, comments and whitespace ignored."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(ROOT, p)) as f:
+                text = f.read()
+        else:
+            text = read(p)
+        h.update(_code_only(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -65,8 +65,7 @@ LA_HD constexpr int state_group(int D) {
   }
   return G;
 }
-// fwd_chunk_output: one workgroup per (b,h, chunk); one wave per 16-query
-// block (at least 4 waves).
+// fwd_chunk_output: one workgroup per (b,h, chunk) of max(C/16, 4) waves.
 LA_HD constexpr int output_waves(int C) { return C / 16 > 4 ? C / 16 : 4; }
 
 // LDS carve-up (byte offsets).  Tile rows are padded by 16 bytes so that the

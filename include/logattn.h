@@ -91,15 +91,19 @@ LA_API int loglinear_fwd_workspace(int B, int H, int64_t T, int dk, int dv, int 
  *   q      [B, H, T, dk]  dtype          16-byte aligned
  *   k      [B, H, T, dk]  dtype          16-byte aligned
  *   v      [B, H, T, dv]  dtype          16-byte aligned
- *   log_a  [B, H, T]      float32 (<= 0 in the model; any finite value works)
+ *   log_a  [B, H, T]      float32, <= 0 (gates a = exp(log_a) in (0, 1], as in
+ *                         the model).  The kernels split each decay into
+ *                         factors that are all <= 1 under this condition;
+ *                         positive values may overflow them.
  *   lambda [B, H, T, L]   float32, level index innermost; L >= ceil(log2 T)+1
  *                         (levels >= ceil(log2 T)+1 are never read)
  *   out    [B, H, T, dv]  dtype, written   16-byte aligned
  *
- * Supported: dk == dv in {16, 32, 64, 128}; C in {16, 32, 64, 128} with
- * C <= max(16, dk) * 2 ... see loglinear_fwd_workspace (it rejects the rest
- * with LA_ESHAPE); T >= 0 (T == 0, B == 0 or H == 0 is a no-op); T need not
- * be a multiple of C (the last chunk is partial).  T <= 2^31 - 1.
+ * Supported: dk == dv in {16, 32, 64, 128} and C in {16, 32, 64, 128}, every
+ * combination except float32 with C == dk == 128, whose tiles exceed the
+ * 160 KB of LDS of a workgroup (LA_ESHAPE; loglinear_fwd_workspace answers
+ * the same); T >= 0 (T == 0, B == 0 or H == 0 is a no-op); T need not be a
+ * multiple of C (the last chunk is partial).  T <= 2^31 - 1.
  * workspace: device memory of at least loglinear_fwd_workspace() bytes,
  * 256-byte aligned; its contents on entry do not matter.
  */
