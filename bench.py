@@ -236,7 +236,8 @@ def pmc_summary(d: str):
     print(json.dumps(out, indent=1))
 
 
-def _pmc_means(d: str, counter: str):
+def _pmc_values(d: str, counter: str):
+    """Per kernel name, the counter's value for every dispatch in a run."""
     import csv
     acc = {}
     for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
@@ -244,7 +245,25 @@ def _pmc_means(d: str, counter: str):
             for r in csv.DictReader(f):
                 if r.get("Counter_Name") == counter:
                     acc.setdefault(r.get("Kernel_Name", "?"), []).append(float(r.get("Counter_Value", 0)))
-    return {k: sum(v) / len(v) for k, v in acc.items()}
+    return acc
+
+
+def _pmc_means(d: str, counter: str):
+    return {k: sum(v) / len(v) for k, v in _pmc_values(d, counter).items()}
+
+
+def _copy_calibration(fetch_dir: str, write_dir: str):
+    """FETCH_SIZE and WRITE_SIZE of the 1 GiB device copies (the largest copy
+    dispatches of the run; other copies, e.g. of a decode state, differ)."""
+    fv = _pmc_values(fetch_dir, "FETCH_SIZE").get("__amd_rocclr_copyBuffer", [])
+    wv = _pmc_values(write_dir, "WRITE_SIZE").get("__amd_rocclr_copyBuffer", [])
+    gib_kib = float(1 << 20)
+    w_big = [x for x in wv if abs(x - gib_kib) < 0.01 * gib_kib]
+    if not fv or not w_big:
+        raise SystemExit("no 1 GiB copy in the counter runs: run them with --copy-calibration")
+    f_big = sorted(fv)[-len(w_big):]
+    fk, wk = sum(f_big) / len(f_big), sum(w_big) / len(w_big)
+    return fk, wk, gib_kib / fk, gib_kib / wk
 
 
 def pmc_profile(fetch_dir: str, write_dir: str, out_path: str):
@@ -253,12 +272,8 @@ def pmc_profile(fetch_dir: str, write_dir: str, out_path: str):
     by what the same counter reads for a plain device copy of known size (the
     1 GiB copy that --copy-calibration adds to every step)."""
     fetch, write = _pmc_means(fetch_dir, "FETCH_SIZE"), _pmc_means(write_dir, "WRITE_SIZE")
-    copy = [k for k in fetch if "copyBuffer" in k]
-    big = max(copy, key=lambda k: fetch[k]) if copy else None
-    if big is None or big not in write:
-        raise SystemExit("no copy kernel in the counter runs: run them with --copy-calibration")
-    gib_kib = float(1 << 20)
-    ff, wf = gib_kib / fetch[big], gib_kib / write[big]
+    big = "__amd_rocclr_copyBuffer"
+    fk, wk, ff, wf = _copy_calibration(fetch_dir, write_dir)
     per_kib, traffic = {}, {}
     for frag, stage in KERNELS.items():
         names = [k for k in fetch if frag in k]
@@ -270,7 +285,7 @@ def pmc_profile(fetch_dir: str, write_dir: str, out_path: str):
     res = {"workload": "train_16k_bf16 (B=8,H=16,T=16384,d=64,C=64,bf16)",
            "kernel_source_hash": kernel_source_hash(),
            "calibration": {"kernel": big, "bytes": "1 GiB read + 1 GiB written",
-                           "fetch_kib": fetch[big], "write_kib": write[big], "fetch_factor": ff, "write_factor": wf},
+                           "fetch_kib": fk, "write_kib": wk, "fetch_factor": ff, "write_factor": wf},
            "per_launch_kib": per_kib, "per_kernel_traffic_bytes": traffic,
            "commands": [
                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/prof/fetch "
