@@ -19,8 +19,9 @@ every input already resident in HBM.  Prints ONE JSON line:
   stages         per kernel (chunk_states, group_tree, chunk_output): mean
                  time, algorithmic bytes, GB/s and counter traffic
   mfma           the matrix-core share of the whole forward
-  decode         256 decode steps of the decode workload (64 x 16 heads,
-                 positions 32768..33023)
+  decode         the decode workload (64 x 16 heads): the 32768-token
+                 prefill handing its state to decode (loglinear_fwd_state),
+                 then 256 decode steps, positions 32768..33023
 
 Other modes (profiling helpers):
   --pmc-summary DIR   parse a rocprofv3 --pmc output directory (FETCH_SIZE
@@ -29,6 +30,8 @@ Other modes (profiling helpers):
                       counter run sees a kernel of known traffic
   --rocpd-summary F   markdown table of kernel statistics from a rocprofv3
                       results database (.db) or kernel_stats.csv
+  --trace-summary F   markdown table of a rocprofv3 kernel_trace.csv, one row
+                      per kernel and grid size
   --pmc-profile FETCH_DIR WRITE_DIR
                       write profiles/fwd_chunk_output_train16k_pmc.json from
                       a FETCH_SIZE and a WRITE_SIZE run (both taken with
@@ -91,12 +94,12 @@ def algorithmic_counts(w, B, H, T, d, C, L, es, G=8):
     Bytes: the essential I/O -- q, k, v, out in the layer dtype plus log_a
     and lambda in float32 -- and, per kernel, the state bytes it must move:
       chunk_states   reads k, v, log_a; writes the bucket node ending at each
-                     chunk inside its group of G chunks (bf16) and each
-                     group's state (fp32)
-      group_tree     reads the group states; writes the bucket node ending at
-                     each group (bf16)
-      chunk_output   reads q, k, v, log_a, lambda and every bucket node once;
-                     writes out
+                     full chunk inside its group of G chunks (bf16) and each
+                     full group's state (fp32) and gate total
+      group_tree     reads the full groups' states; writes the bucket node
+                     ending at each of them (bf16) and the gate prefix
+      chunk_output   reads q, k, v, log_a, lambda and every bucket node some
+                     later chunk needs, once; writes out
     Flops: the dense C x C intra-chunk tiles 2 C^2 (d_k + d_v) per chunk, one
     chunk state 2 C d_k d_v per chunk, and 2 C d_k d_v per chunk for each
     occupied chunk-or-group level (popcount of the chunk index)."""
@@ -106,12 +109,15 @@ def algorithmic_counts(w, B, H, T, d, C, L, es, G=8):
     per_head_token_bytes = 4 * d * es + 4 + 4 * L
     bytes_io = BH * T * per_head_token_bytes
     node = d * d * es
-    nodes_in = sum(1 for c in range(n_chunks) if c % G != G - 1 and c + 1 < n_chunks)
-    nodes_grp = max(n_groups - 1, 0)
+    n_full = T // C
+    n_full_groups = n_full // G
+    nodes_w = sum(1 for c in range(n_full) if c % G != G - 1)                  # written
+    nodes_in = sum(1 for c in range(n_chunks) if c % G != G - 1 and c + 1 < n_chunks)   # read
+    nodes_grp = max(n_groups - 1, 0)                                           # read
     kern = {
-        "chunk_states": BH * (T * (2 * d * es + 4) + nodes_in * node + nodes_grp * d * d * 4 + n_chunks * 4
-                              + n_groups * 4),
-        "group_tree": BH * (nodes_grp * d * d * 4 + n_groups * 4 + nodes_grp * node + (n_groups + 1) * 8),
+        "chunk_states": BH * (T * (2 * d * es + 4) + nodes_w * node + n_full_groups * (d * d * 4 + 4)
+                              + n_chunks * 4),
+        "group_tree": BH * (n_full_groups * (d * d * 4 + 4 + node) + (n_full_groups + 1) * 8),
         "chunk_output": bytes_io + BH * ((nodes_in + nodes_grp) * node + n_chunks * 4 + (n_groups + 1) * 8),
     }
     intra = n_chunks * 2 * C * C * (d + d)
@@ -160,27 +166,62 @@ def pmc_traffic(src_hash: str):
     return s.get("per_kernel_traffic_bytes"), None
 
 
-def bench_decode(la, torch, dev, steps=256):
+def bench_decode(la, torch, dev, steps=256, reps=5):
+    """The decode workload: a 32768-token prefill on 64 x 16 heads that hands
+    its final state to decode (loglinear_fwd_state, timed against the plain
+    forward over the same prefix), then 256 decode steps from that state."""
     from fenwick_tree_hierarchical_amd.workloads import WORKLOADS, make_inputs
 
     w = WORKLOADS["decode_32k_bf16"]
     S = 16
-    B, H, d = w.B, w.H, w.dk
-    st = la.loglinear_state_init(B, H, d, d, S, dev)
-    # timing depends only on which levels are occupied: fill the slots with
-    # values of the right scale and start at the workload's first step
-    g = torch.Generator(device=dev)
-    g.manual_seed(w.seed)
-    st.slots.normal_(0, 0.01, generator=g)
-    st.t = w.prefix
-    x = make_inputs(w, device=dev, T=steps, L=S + 1)
+    B, H, d, P = w.B, w.H, w.dk, w.prefix
+    x = make_inputs(w, device=dev, L=S + 1)                  # T = prefix + steps
     a = torch.exp(x["log_a"])
-    per = [(x["q"][:, :, i].contiguous(), x["k"][:, :, i].contiguous(), x["v"][:, :, i].contiguous(),
-            a[:, :, i].contiguous(), x["lam"][:, :, i].contiguous(), torch.empty(B, H, d, dtype=x["q"].dtype,
-                                                                                    device=dev))
-           for i in range(steps)]
-    L = la.lib()
+    pre = {k: v[:, :, :P].contiguous() for k, v in x.items()}
+    pre["log_a"] = torch.log(a[:, :, :P]).contiguous()
+    nws = la.loglinear_fwd_workspace(B, H, P, d, d, w.C, torch.bfloat16)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(pre["v"])
+    st = la.loglinear_state_init(B, H, d, d, S, dev)
     stream = torch.cuda.current_stream(dev)
+
+    def prefill(with_state):
+        if with_state:
+            la.loglinear_fwd_state(pre["q"], pre["k"], pre["v"], pre["log_a"], pre["lam"], st, out=out,
+                                   chunk=w.C, workspace=ws)
+        else:
+            la.loglinear_fwd(pre["q"], pre["k"], pre["v"], pre["log_a"], pre["lam"], out=out, chunk=w.C,
+                             workspace=ws)
+
+    ms = {}
+    for with_state in (False, True, False, True):            # interleaved, twice
+        prefill(with_state)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            prefill(with_state)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.setdefault(with_state, []).append(e0.elapsed_time(e1) / reps)
+    fwd_ms, state_ms = min(ms[False]), min(ms[True])
+    assert st.t == P
+    # the final-state kernel: each occupied bucket's node read once (bfloat16)
+    # and its slot written once (float32), every scale written
+    occ = bin(P).count("1")
+    st_bytes = B * H * (occ * d * d * (2 + 4) + S * 4)
+    handoff = {"workload": f"{w.name} prefill", "prefix": P, "heads": B * H,
+               "fwd_ms": fwd_ms, "fwd_state_ms": state_ms, "final_state_ms": state_ms - fwd_ms,
+               "prefill_tokens_per_s": B * P / (state_ms * 1e-3),
+               "final_state_alg_bytes": st_bytes,
+               "note": "final_state_ms is the difference of the two timed calls (best of two rounds of "
+                       f"{reps}); the kernel alone is in the kernel trace",
+               "replaces_decode_steps": P}
+
+    per = [(x["q"][:, :, P + i].contiguous(), x["k"][:, :, P + i].contiguous(), x["v"][:, :, P + i].contiguous(),
+            a[:, :, P + i].contiguous(), x["lam"][:, :, P + i].contiguous(),
+            torch.empty(B, H, d, dtype=x["q"].dtype, device=dev)) for i in range(steps)]
+    L = la.lib()
     args = [(ctypes_byref(la, st), q.data_ptr(), k.data_ptr(), v.data_ptr(), aa.data_ptr(), lm.data_ptr(),
              o.data_ptr()) for q, k, v, aa, lm, o in per]
     # warm-up on a copy so the timed steps start at the workload's position
@@ -204,14 +245,15 @@ def bench_decode(la, torch, dev, steps=256):
     # plus q, k, v, out, gate, lambda and the slot scales
     slot = d * d * 4
     tot = 0
-    for t in range(w.prefix, w.prefix + steps):
+    for t in range(P, P + steps):
         tot += (bin(t).count("1") + 1) * slot + 4 * d * 2 + 4 + (S + 1) * 4 + 2 * S * 4
     tot *= B * H
     return {"workload": w.name, "steps": steps, "launch": "eager, one launch per step",
-            "tokens_per_s": B * steps / wall, "us_per_step_wall": wall / steps * 1e6,
-            "us_per_step_gpu": gpu_ms / steps * 1e3,
+            "state": "from the prefill hand-off", "tokens_per_s": B * steps / wall,
+            "us_per_step_wall": wall / steps * 1e6, "us_per_step_gpu": gpu_ms / steps * 1e3,
             "achieved_gbps": tot / (gpu_ms * 1e-3) / 1e9, "peak_gbps": HBM_PEAK_GBPS,
-            "frac": tot / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "alg_bytes_per_step": tot / steps}
+            "frac": tot / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "alg_bytes_per_step": tot / steps,
+            "handoff": handoff}
 
 
 def ctypes_byref(la, st):
@@ -288,14 +330,31 @@ def pmc_profile(fetch_dir: str, write_dir: str, out_path: str):
                            "fetch_kib": fk, "write_kib": wk, "fetch_factor": ff, "write_factor": wf},
            "per_launch_kib": per_kib, "per_kernel_traffic_bytes": traffic,
            "commands": [
-               "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/prof/fetch "
+               f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/{fetch_dir} "
                "-o fetch -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-decode --copy-calibration",
-               "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/prof/write "
+               f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/{write_dir} "
                "-o write -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-decode --copy-calibration",
-               "python bench.py --pmc-profile gpurun_out/prof/fetch gpurun_out/prof/write"]}
+               f"python bench.py --pmc-profile {fetch_dir} {write_dir}"]}
     with open(out_path, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res, indent=1))
+
+
+def trace_summary(path: str):
+    """Markdown table of a rocprofv3 kernel_trace.csv grouped by kernel and
+    grid size (one kernel at several shapes gets one row per shape)."""
+    import csv
+    agg = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = (r["Kernel_Name"], int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]),
+                   int(r["Workgroup_Size_X"]))
+            agg.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel | grid (threads) | block | calls | average us | min us | max us |")
+    print("|---|---|---|---|---|---|---|")
+    for (name, grid, block), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        short = name if len(name) < 70 else name[:67] + "..."
+        print(f"| `{short}` | {grid} | {block} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
 
 
 def rocpd_summary(path: str):
@@ -334,9 +393,13 @@ def main():
     ap.add_argument("--pmc-summary", default=None)
     ap.add_argument("--pmc-profile", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None)
     ap.add_argument("--rocpd-summary", default=None)
+    ap.add_argument("--trace-summary", default=None)
     args = ap.parse_args()
     if args.rocpd_summary:
         rocpd_summary(args.rocpd_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary)

@@ -40,6 +40,8 @@ _SIGS = {
     "loglinear_fwd": ([_p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
     "loglinear_fwd_staged": ([_p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _i, _i, _i, _p, _sz,
                               ctypes.POINTER(_p), _i, _p], _i),
+    "loglinear_fwd_state": ([_p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _i, _i, _i, _p, _sz,
+                             ctypes.POINTER(_LaState), _p], _i),
     "loglinear_state_bytes": ([_i, _i, _i, _i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz)], _i),
     "loglinear_state_init": ([ctypes.POINTER(_LaState), _i, _i, _i, _i, _i, _p, _p, _p], _i),
     "loglinear_decode_step": ([ctypes.POINTER(_LaState), _p, _p, _p, _p, _p, _p, _i, _p], _i),
@@ -194,6 +196,17 @@ class LogLinearState:
     def effective_slots(self) -> torch.Tensor:
         """scale * slots: the bucket matrices themselves ([B,H,S,dk,dv])."""
         return self.slots * self.scale[..., None, None]
+
+
+def loglinear_fwd_state(q, k, v, log_a, lam, state: LogLinearState, out=None, chunk: int = 64,
+                        workspace=None):
+    """loglinear_fwd that also leaves in ``state`` the recurrent state after
+    the T tokens (slots of the occupied levels, scales 1, ``state.t = T``), so
+    that ``loglinear_decode_step`` continues at position T.  Returns out."""
+    args, out, _, dev = _fwd_args(q, k, v, log_a, lam, out, chunk, workspace)
+    _dev(q, state.slots, state.scale)
+    _check(lib().loglinear_fwd_state(*args, ctypes.byref(state._st), _stream(dev)), "loglinear_fwd_state")
+    return out
 
 
 def loglinear_state_init(B: int, H: int, dk: int, dv: int, S: int, device) -> LogLinearState:

@@ -11,17 +11,35 @@ using namespace la;
 
 namespace {
 
+// The forward; `st` (nullable) also receives the final recurrent state.
 int fwd_common(const void* q, const void* k, const void* v, const float* log_a, const float* lambda,
                void* out, int B, int H, int64_t T, int dk, int dv, int C, int L, int dtype, void* ws,
-               size_t ws_bytes, void* const* events, int n_events, la_stream_t stream) {
+               size_t ws_bytes, void* const* events, int n_events, la_state* st, la_stream_t stream) {
   FwdPlan p;
   int rc = plan_fwd(B, H, T, dk, dv, C, dtype, L, &p);
   if (rc != kOK) return rc;
   if (events && n_events != p.n_stages + 1) return kEINVAL;
+  if (st) {
+    rc = check_state_shape(st->B, st->H, st->dk, st->dv, st->S);
+    if (rc != kOK) return rc;
+    if (st->B != B || st->H != H || st->dk != dk || st->dv != dv) return kESHAPE;
+    if (bit_length(T) > st->S) return kECAPACITY;
+    if (p.BH > 0) {
+      if (!st->slots || !st->scale) return kEINVAL;
+      if (!aligned(st->slots, 16) || !aligned(st->scale, 4)) return kEALIGN;
+    }
+  }
   if (p.n_stages == 0) {   // empty problem: nothing to read or write
     if (events)
       for (int i = 0; i < n_events; ++i)
         if (hipEventRecord((hipEvent_t)events[i], (hipStream_t)stream) != hipSuccess) return kEHIP;
+    if (st) {
+      if (p.BH > 0) {      // T == 0: the state before any token
+        rc = launch_state_init(st->slots, p.BH * st->S * dk * dv, st->scale, p.BH * st->S, (hipStream_t)stream);
+        if (rc != kOK) return rc;
+      }
+      st->t = T;
+    }
     return kOK;
   }
   if (!q || !k || !v || !log_a || !lambda || !out) return kEINVAL;
@@ -34,16 +52,21 @@ int fwd_common(const void* q, const void* k, const void* v, const float* log_a, 
   char* w = static_cast<char*>(ws);
   FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.log_a = log_a; a.lam = lambda; a.out = out;
-  a.nodes_in = p.n_chunks > 1 ? static_cast<void*>(w + p.off_nodes_in) : nullptr;
-  a.gch = p.n_chunks > 1 ? reinterpret_cast<float*>(w + p.off_gch) : nullptr;
-  a.gstate = p.n_groups > 1 ? reinterpret_cast<float*>(w + p.off_gstate) : nullptr;
-  a.gtot = p.n_groups > 1 ? reinterpret_cast<float*>(w + p.off_gtot) : nullptr;
-  a.gprefix = p.n_groups > 1 ? reinterpret_cast<double*>(w + p.off_gprefix) : nullptr;
-  a.nodes = p.n_groups > 1 ? static_cast<void*>(w + p.off_nodes) : nullptr;
-  a.T = T; a.n_chunks = p.n_chunks; a.n_groups = p.n_groups; a.L = L;
+  a.nodes_in = p.has_chunk_nodes() ? static_cast<void*>(w + p.off_nodes_in) : nullptr;
+  a.gch = p.has_chunk_nodes() ? reinterpret_cast<float*>(w + p.off_gch) : nullptr;
+  a.gstate = p.has_group_nodes() ? reinterpret_cast<float*>(w + p.off_gstate) : nullptr;
+  a.gtot = p.has_group_nodes() ? reinterpret_cast<float*>(w + p.off_gtot) : nullptr;
+  a.gprefix = p.has_group_nodes() ? reinterpret_cast<double*>(w + p.off_gprefix) : nullptr;
+  a.nodes = p.has_group_nodes() ? static_cast<void*>(w + p.off_nodes) : nullptr;
+  a.T = T; a.n_chunks = p.n_chunks; a.n_groups = p.n_groups; a.n_full_groups = p.n_full_groups; a.L = L;
+  a.st_slots = st ? st->slots : nullptr;
+  a.st_scale = st ? st->scale : nullptr;
+  a.st_S = st ? st->S : 0;
   const hipEvent_t* ev = reinterpret_cast<const hipEvent_t*>(events);
   hipStream_t s = (hipStream_t)stream;
-  return dtype == kBF16 ? launch_fwd_bf16(p, a, s, ev) : launch_fwd_f32(p, a, s, ev);
+  rc = dtype == kBF16 ? launch_fwd_bf16(p, a, s, ev) : launch_fwd_f32(p, a, s, ev);
+  if (rc == kOK && st) st->t = T;
+  return rc;
 }
 
 }  // namespace
@@ -91,7 +114,16 @@ LA_API int loglinear_fwd(const void* q, const void* k, const void* v, const floa
                          int C, int L, int dtype, void* workspace, size_t workspace_bytes,
                          la_stream_t stream) {
   return fwd_common(q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, L, dtype, workspace,
-                    workspace_bytes, nullptr, 0, stream);
+                    workspace_bytes, nullptr, 0, nullptr, stream);
+}
+
+LA_API int loglinear_fwd_state(const void* q, const void* k, const void* v, const float* log_a,
+                               const float* lambda, void* out, int B, int H, int64_t T, int dk, int dv,
+                               int C, int L, int dtype, void* workspace, size_t workspace_bytes,
+                               la_state* state, la_stream_t stream) {
+  if (!state) return kEINVAL;
+  return fwd_common(q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, L, dtype, workspace,
+                    workspace_bytes, nullptr, 0, state, stream);
 }
 
 LA_API int loglinear_fwd_staged(const void* q, const void* k, const void* v, const float* log_a,
@@ -103,7 +135,7 @@ LA_API int loglinear_fwd_staged(const void* q, const void* k, const void* v, con
   for (int i = 0; i < n_events; ++i)
     if (!events[i]) return kEINVAL;
   return fwd_common(q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, L, dtype, workspace,
-                    workspace_bytes, events, n_events, stream);
+                    workspace_bytes, events, n_events, nullptr, stream);
 }
 
 LA_API int loglinear_state_bytes(int B, int H, int dk, int dv, int S, size_t* slot_bytes,

@@ -54,7 +54,13 @@ struct FwdArgs {
   int64_t T;
   int64_t n_chunks;
   int64_t n_groups;
+  int64_t n_full_groups;  // groups of G chunks of C tokens each
   int L;
+  // final recurrent state (loglinear_fwd_state): [BH][st_S][D][D] fp32 slots
+  // and [BH][st_S] scales; null when not asked for
+  float* st_slots;
+  float* st_scale;
+  int st_S;
 };
 
 constexpr int cilog2(int x) { return x <= 1 ? 0 : 1 + cilog2(x >> 1); }
@@ -145,7 +151,7 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
     gt += gch[c];
   }
   if (tid < nch) a.gch[bh * nc + c0 + tid] = b2s[tid * C + C - 1];
-  if (tid == 0 && gam + 1 < ng) a.gtot[bh * ng + gam] = gt;
+  if (tid == 0 && (gam + 1) * G * C <= T) a.gtot[bh * ng + gam] = gt;
 
   f32x4 sl[NS][TPW];   // in-group carry: bucket states of levels 1..NS, fp32
   float sc2[NS];       // their lazy log2 gates (from the bucket end to the current chunk start)
@@ -194,8 +200,9 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
 #pragma unroll
     for (int j = 0; j < NS; ++j) fj[j] = j < kk ? __builtin_amdgcn_exp2f(sc2[j] + gc) : 0.f;
     const int64_t cg = c0 + c;
-    const bool write_node = (c != G - 1) && (cg + 1 < nc);
-    const bool write_group = (c == G - 1) && (gam + 1 < ng);
+    // the bucket ending at every full chunk, and every full group's state
+    const bool write_node = (c != G - 1) && ((cg + 1) * C <= T);
+    const bool write_group = (c == G - 1) && ((gam + 1) * G * C <= T);
 #pragma unroll
     for (int h = 0; h < TPW; ++h) {
       const int tix = w + h * NW;
@@ -231,11 +238,13 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
 }
 
 // ---------------------------------------------------------------------------
-// Group tree: per (b,h) and state element, walk the groups with the
+// Group tree: per (b,h) and state element, walk the full groups with the
 // binary-counter carry.  node[e] = A_e + sum_{j<=k} gate * bucket_j where
-// k = trailing ones of e: the bucket of 2^k groups ending at group e.
-// MAXJ bounds the carry levels (bit length of the group count); the launcher
-// picks the smallest instantiation that covers the sequence.
+// k = trailing ones of e: the bucket of 2^k groups ending at group e.  It
+// also writes gprefix[0 .. n_full_groups], the exclusive prefix sums of the
+// group gate totals.  MAXJ bounds the carry levels (bit length of the group
+// count); the launcher picks the smallest instantiation that covers the
+// sequence.
 template <bool BF16, int MAXJ>
 __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
   using EL = Elem<BF16>;
@@ -246,7 +255,7 @@ __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
   const int blk = blockIdx.x % nblk;
   const int elem = blk * 256 + threadIdx.x;
   const bool valid = elem < DD;
-  const int64_t ng = a.n_groups;
+  const int64_t ng = a.n_groups, nfg = a.n_full_groups;
   float slot[MAXJ];
   float sc[MAXJ];
 #pragma unroll
@@ -256,14 +265,14 @@ __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
   const float* gs = a.gstate + bh * ng * DD;
   E* nd = reinterpret_cast<E*>(a.nodes) + bh * ng * DD;
   constexpr int kBatch = 8;   // independent loads issued together, then walked
-  for (int64_t e0 = 0; e0 + 1 < ng; e0 += kBatch) {
+  for (int64_t e0 = 0; e0 < nfg; e0 += kBatch) {
     float Av[kBatch], gv[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int64_t e = e0 + u;
       Av[u] = 0.f;
       gv[u] = 0.f;
-      if (e + 1 < ng) {
+      if (e < nfg) {
         gv[u] = a.gtot[bh * ng + e];
         if (valid) Av[u] = gs[e * DD + elem];
       }
@@ -271,7 +280,7 @@ __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int64_t e = e0 + u;
-      if (e + 1 >= ng) break;
+      if (e >= nfg) break;
       if (writer) a.gprefix[bh * (ng + 1) + e] = pre;
       const float g = gv[u];
       int kk = 0;
@@ -289,9 +298,98 @@ __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
       pre += (double)g;
     }
   }
-  // Consumers read entries 0..ng-1 only (the last group's total is never
-  // formed: no later group needs it).
-  if (writer) a.gprefix[bh * (ng + 1) + ng - 1] = pre;
+  if (writer) a.gprefix[bh * (ng + 1) + nfg] = pre;
+}
+
+// ---------------------------------------------------------------------------
+// fwd_final_state: the recurrent (decode) state after the T tokens, for a
+// decode that continues at position T ("Log-Linear Attention", Italian
+// summary, technical section 2, item 3: the recurrent form keeps one state per
+// occupied level).  One block per (b,h).  Slot i holds level i+1, occupied
+// iff bit i of T is set: the bucket of keys [((T >> i) << i) - 2^i,
+// (T >> i) << i), each key weighted by its gate product up to token T-1, as a
+// (d_k, d_v) float32 matrix with scale 1.  Buckets smaller than a chunk lie in
+// the last, partial chunk and are summed here from k and v; the others are the
+// node the forward built for the bucket's last chunk (levels inside a group)
+// or last group, decayed from its end to token T-1.  Slots of empty levels
+// are left as they are: a decode step never reads them and overwrites a slot
+// whole when its level fills.
+template <bool BF16, int C, int D>
+__global__ __launch_bounds__(256) void fwd_final_state(FwdArgs a) {
+  using EL = Elem<BF16>;
+  using E = typename EL::T;
+  constexpr int G = state_group(D), LOG2C = cilog2(C), LOG2G = cilog2(G);
+  constexpr int DD = D * D, NQ = DD / 4, PER = (NQ + 255) / 256;   // four (d_k, d_v..d_v+3) entries per item
+  __shared__ float wk[C / 2];
+  const int S = a.st_S;
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t T = a.T, nc = a.n_chunks;
+  if (tid < S) a.st_scale[bh * S + tid] = 1.f;
+  for (int i = 0; i < S; ++i) {
+    if (!((T >> i) & 1)) continue;
+    const int64_t s1 = (T >> i) << i, s0 = s1 - (1ll << i);
+    f32x4 acc[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (i < LOG2C) {
+      // keys s0 .. s1-1 of the last chunk, weight exp2(sum_{r=s+1}^{T-1} log2 a_r)
+      const int nk = 1 << i;
+      if (tid < nk) {
+        float g = 0.f;
+        for (int64_t r = s0 + tid + 1; r < T; ++r) g += a.log_a[bh * T + r] * kLog2e;
+        wk[tid] = __builtin_amdgcn_exp2f(g);
+      }
+      __syncthreads();
+      const E* kb = reinterpret_cast<const E*>(a.k) + (bh * T + s0) * D;
+      const E* vb = reinterpret_cast<const E*>(a.v) + (bh * T + s0) * D;
+      for (int j = 0; j < nk; ++j) {
+        const float wj = wk[j];
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+          const int e = 4 * (tid + p * 256);
+          if (e < DD) {
+            const float kw = wj * EL::to_f32(kb[j * D + e / D]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[p][u] += kw * EL::to_f32(vb[j * D + e % D + u]);
+          }
+        }
+      }
+      __syncthreads();                              // wk is read out before the next level
+    } else {
+      // log2 gate from the node's end to token T-1
+      const bool grp = i >= LOG2C + LOG2G;
+      const int64_t ce = s1 / C - 1;                  // last chunk of the bucket
+      double g = 0.0;
+      const E* node;
+      if (grp) {
+        const int64_t e = s1 / ((int64_t)C * G) - 1;  // last group of the bucket
+        const double* gp = a.gprefix + bh * (a.n_groups + 1);
+        g = gp[a.n_full_groups] - gp[e + 1];
+        for (int64_t c = a.n_full_groups * G; c < nc; ++c) g += (double)a.gch[bh * nc + c];
+        node = reinterpret_cast<const E*>(a.nodes) + (bh * a.n_groups + e) * DD;
+      } else {
+        for (int64_t c = ce + 1; c < nc; ++c) g += (double)a.gch[bh * nc + c];
+        node = reinterpret_cast<const E*>(a.nodes_in) + (bh * nc + ce) * DD;
+      }
+      const float f = __builtin_amdgcn_exp2f((float)g);
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int e = 4 * (tid + p * 256);
+        if (e < DD) {
+          const int dk = e / D, dv = e % D;         // nodes are (d_v, d_k)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[p][u] = f * EL::to_f32(node[(dv + u) * D + dk]);
+        }
+      }
+    }
+    float* out = a.st_slots + (bh * S + i) * DD;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = 4 * (tid + p * 256);
+      if (e < DD) *reinterpret_cast<f32x4*>(out + e) = acc[p];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -701,7 +799,8 @@ int launch_fwd_impl(const FwdPlan& p, FwdArgs a, hipStream_t s, hipEvent_t const
     if (ev) ok = ok && hipEventRecord(ev[stage], s) == hipSuccess;
     ++stage;
   };
-  if (p.n_chunks > 1) {
+  const bool final_state = a.st_slots != nullptr;
+  if (p.n_chunks > 1 || (final_state && p.has_chunk_nodes())) {
     constexpr int lds_s = state_lds(C, D, sizeof(E), G).total;
     ok = ok && hipFuncSetAttribute((const void*)fwd_chunk_states<BF16, C, D>,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds_s) == hipSuccess;
@@ -711,7 +810,7 @@ int launch_fwd_impl(const FwdPlan& p, FwdArgs a, hipStream_t s, hipEvent_t const
                        dim3(StateShape<BF16, C, D>::NT), lds_s, s, a);
     ok = ok && hipGetLastError() == hipSuccess;
   }
-  if (p.n_groups > 1) {
+  if (p.n_groups > 1 || (final_state && p.has_group_nodes())) {
     mark();
     const dim3 grid((unsigned)(((D * D + 255) / 256) * p.BH));
     const int levels = bit_length(p.n_groups);        // carry levels the walk can reach
@@ -730,6 +829,10 @@ int launch_fwd_impl(const FwdPlan& p, FwdArgs a, hipStream_t s, hipEvent_t const
   hipLaunchKernelGGL((fwd_chunk_output<BF16, C, D>), dim3((unsigned)(p.n_chunks * p.BH)),
                      dim3(ChunkShape<BF16, C, D>::NT), p.lds_out, s, a);
   ok = ok && hipGetLastError() == hipSuccess;
+  if (final_state) {
+    hipLaunchKernelGGL((fwd_final_state<BF16, C, D>), dim3((unsigned)p.BH), dim3(256), 0, s, a);
+    ok = ok && hipGetLastError() == hipSuccess;
+  }
   if (ev) ok = ok && hipEventRecord(ev[stage], s) == hipSuccess;
   return ok ? kOK : kEHIP;
 }

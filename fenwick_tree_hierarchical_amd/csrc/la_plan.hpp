@@ -123,11 +123,14 @@ LA_HD constexpr OutLds output_lds(int C, int D, int es, int L) {
 struct FwdPlan {
   int B = 0, H = 0, D = 0, C = 0, L = 0, dtype = 0, es = 0;
   int64_t T = 0, BH = 0, n_chunks = 0, n_groups = 0;
+  int64_t n_full_chunks = 0, n_full_groups = 0;   // chunks of C tokens, groups of G such chunks
   int G = 1, log2G = 0, log2C = 0;
   int lds_out = 0, lds_state = 0;
   size_t off_nodes_in = 0, off_gch = 0;
   size_t off_gstate = 0, off_gtot = 0, off_gprefix = 0, off_nodes = 0, ws_bytes = 0;
   int n_stages = 0;   // 0 for an empty problem
+  bool has_chunk_nodes() const { return n_full_chunks >= 1; }
+  bool has_group_nodes() const { return n_full_groups >= 1; }
 };
 
 // Shape/dtype checks and the plan.  L < 0 skips the lambda-level check (used
@@ -158,6 +161,8 @@ inline int plan_fwd(int B, int H, int64_t T, int dk, int dv, int C, int dtype, i
   if (P.lds_state > kLdsLimit || output_lds(C, dk, P.es, kMaxLevels).total > kLdsLimit) return kESHAPE;
   P.n_chunks = (T + C - 1) / C;
   P.n_groups = (P.n_chunks + P.G - 1) / P.G;
+  P.n_full_chunks = T / C;
+  P.n_full_groups = P.n_full_chunks / P.G;
   if (P.n_chunks * P.BH > (int64_t)0x7fffffff) return kESHAPE;
   if (P.BH == 0 || T == 0) {
     P.n_stages = 0;
@@ -166,11 +171,14 @@ inline int plan_fwd(int B, int H, int64_t T, int dk, int dv, int C, int dtype, i
   }
   const size_t DD = (size_t)dk * dv;
   size_t off = 0;
-  if (P.n_chunks > 1) {
+  // chunk nodes exist once there is a full chunk, group nodes once there is a
+  // full group (the forward reads them from the second chunk or group on; the
+  // final state also reads those ending at the last full chunk and group)
+  if (P.has_chunk_nodes()) {
     P.off_nodes_in = off; off = align_up(off + (size_t)P.BH * P.n_chunks * DD * P.es, 256);
     P.off_gch = off;      off = align_up(off + (size_t)P.BH * P.n_chunks * 4, 256);
   }
-  if (P.n_groups > 1) {
+  if (P.has_group_nodes()) {
     P.off_gstate = off;  off = align_up(off + (size_t)P.BH * P.n_groups * DD * 4, 256);
     P.off_gtot = off;    off = align_up(off + (size_t)P.BH * P.n_groups * 4, 256);
     P.off_gprefix = off; off = align_up(off + (size_t)P.BH * (P.n_groups + 1) * 8, 256);

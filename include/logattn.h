@@ -185,6 +185,31 @@ LA_API int loglinear_decode_step(la_state* st, const void* q, const void* k, con
                                  la_stream_t stream);
 
 /*
+ * The forward that also leaves the recurrent (decode) state after the T
+ * tokens in *state, so that loglinear_decode_step continues at position T:
+ * a prefill hand-off (Italian summary, technical section 2, item 3: the
+ * parallel form for training and the recurrent form for decoding compute
+ * the same per-level states).  Slot i receives the bucket of level i+1 when
+ * bit i of T is set -- the keys [((T >> i) << i) - 2^i, (T >> i) << i), each
+ * weighted by its gate product up to token T-1, as a (dk, dv) matrix; the
+ * slots of empty levels are left as they are (loglinear_decode_step never
+ * reads them and overwrites a slot whole when its level fills).  Every scale
+ * becomes 1 and state->t becomes T (on the host, once the work is enqueued).
+ * With T == 0 the whole state is reset as by loglinear_state_init.  Buckets of whole chunks come from the bucket
+ * nodes the forward builds, in the layer dtype (bfloat16 in LA_BF16 mode);
+ * smaller ones are summed in float32 from k and v.
+ *
+ * state: a state of the same B, H, dk, dv (set up by loglinear_state_init
+ * or by a previous call); its slots and scale are overwritten.  state->S
+ * must be at least the bit length of T, else LA_ECAPACITY (nothing runs).
+ * Arguments, workspace and errors otherwise as loglinear_fwd.
+ */
+LA_API int loglinear_fwd_state(const void* q, const void* k, const void* v, const float* log_a,
+                               const float* lambda, void* out, int B, int H, int64_t T, int dk, int dv,
+                               int C, int L, int dtype, void* workspace, size_t workspace_bytes,
+                               la_state* state, la_stream_t stream);
+
+/*
  * Fenwick level table for checking: out[t * T + s] = l(t, s) for s <= t and
  * -1 for s > t, as int8, computed on the device by the same level function
  * the forward kernels use, with the chunk factorisation for chunk size C:

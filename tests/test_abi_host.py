@@ -59,7 +59,9 @@ def test_workspace_query():
     assert ws(1, 1, 64, 16, 16, 0)[0] == OK
     assert ws(1, 1, 100, 16, 16, 0)[0] == OK        # ragged T is accepted
     assert ws(0, 4, 100, 64, 64)[1] == 0             # empty problem needs nothing
-    assert ws(3, 2, 64, 64, 64)[1] == 0              # a single chunk needs nothing
+    assert ws(3, 2, 63, 64, 64)[1] == 0              # a single partial chunk needs nothing
+    # one full chunk: its bucket node (read by the final state) and gate total
+    assert ws(3, 2, 64, 64, 64)[1] == 3 * 2 * 64 * 64 * 2 + 256
     assert ws(1, 1, 64, 16, 16, 7)[0] == EDTYPE
     assert ws(1, 1, 64, 24, 64)[0] == ESHAPE          # unsupported head dim
     assert ws(1, 1, 64, 64, 48)[0] == ESHAPE          # unsupported chunk
@@ -119,6 +121,30 @@ def test_staged_requires_matching_event_count():
     ev0 = (ctypes.c_void_p * 4)(A, None, A, A)
     rc = L.loglinear_fwd_staged(A, A, A, A, A, A, 8, 16, 16384, 64, 64, 64, 15, 1, A, 1 << 34, ev0, 4, None)
     assert rc == EINVAL
+
+
+def fwd_state(st, B=1, H=1, T=64, d=16, C=16, Lv=7, dt=0, q=A, w=A, wb=1 << 30):
+    return L.loglinear_fwd_state(q, A, A, A, A, A, B, H, T, d, d, C, Lv, dt, w, wb,
+                                 ctypes.byref(st) if st is not None else None, None)
+
+
+def test_fwd_state_validation_codes():
+    st = la._LaState(0, 1, 1, 16, 16, 7, A, A)
+    assert fwd_state(None) == EINVAL
+    assert fwd_state(st, q=None) == EINVAL
+    assert fwd_state(la._LaState(0, 1, 2, 16, 16, 7, A, A)) == ESHAPE       # H differs
+    assert fwd_state(la._LaState(0, 1, 1, 32, 32, 7, A, A)) == ESHAPE       # head dim differs
+    assert fwd_state(la._LaState(0, 1, 1, 16, 16, 6, A, A)) == ECAP         # T=64 needs 7 slots
+    assert fwd_state(la._LaState(0, 1, 1, 16, 16, 41, A, A)) == ESHAPE      # beyond the slot limit
+    assert fwd_state(la._LaState(0, 1, 1, 16, 16, 7, A + 4, A)) == EALIGN
+    assert fwd_state(la._LaState(0, 1, 1, 16, 16, 7, None, A)) == EINVAL
+    assert fwd_state(st, T=1024, Lv=11) == ECAP                               # 11 slots needed
+    assert st.t == 0                                  # unchanged on every error
+    # empty batch: only the host position moves to T
+    st0 = la._LaState(0, 0, 1, 16, 16, 7, None, None)
+    assert L.loglinear_fwd_state(None, None, None, None, None, None, 0, 1, 50, 16, 16, 16, 7, 0, None, 0,
+                                 ctypes.byref(st0), None) == OK
+    assert st0.t == 50
 
 
 def test_state_bytes_and_init_validation():
