@@ -59,6 +59,7 @@ int fwd_common(const void* q, const void* k, const void* v, const float* log_a, 
   a.gprefix = p.has_group_nodes() ? reinterpret_cast<double*>(w + p.off_gprefix) : nullptr;
   a.nodes = p.has_group_nodes() ? static_cast<void*>(w + p.off_nodes) : nullptr;
   a.T = T; a.n_chunks = p.n_chunks; a.n_groups = p.n_groups; a.n_full_groups = p.n_full_groups; a.L = L;
+  a.lam_vec4 = (T * L) % 4 == 0 && aligned(lambda, 16);
   a.st_slots = st ? st->slots : nullptr;
   a.st_scale = st ? st->scale : nullptr;
   a.st_S = st ? st->S : 0;

@@ -56,6 +56,7 @@ struct FwdArgs {
   int64_t n_groups;
   int64_t n_full_groups;  // groups of G chunks of C tokens each
   int L;
+  int lam_vec4;           // lambda rows of every full chunk are 16-byte aligned
   // final recurrent state (loglinear_fwd_state): [BH][st_S][D][D] fp32 slots
   // and [BH][st_S] scales; null when not asked for
   float* st_slots;
@@ -415,6 +416,8 @@ struct ChunkShape {
   static constexpr int EPV = 16 / (BF16 ? 2 : 4), VPR = D / EPV, NV = C * VPR;
   static constexpr int NPF = (NV + NT - 1) / NT;
   static constexpr int NPL = (C * kMaxLevels + NT - 1) / NT;   // lambda values per thread (bound)
+  static constexpr int NPL4 = (C * kMaxLevels / 4 + NT - 1) / NT;   // ... as float4 loads
+  static constexpr int NLX = NPL > 4 * NPL4 ? NPL : 4 * NPL4;   // registers for either
   // small tiles: the first NPRE levels' nodes load with the chunk; larger
   // ones load them at the start of phase 2, where the registers are free
   static constexpr bool EARLY = BF16 && C <= 64 && D <= 64;
@@ -442,7 +445,7 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   const OutLds lay = output_lds(C, D, sizeof(E), L);
   E* Qs = reinterpret_cast<E*>(smem + lay.q);
   E* Ks = reinterpret_cast<E*>(smem + lay.k);
-  E* VT = reinterpret_cast<E*>(smem + lay.vt);
+  E* Vs = reinterpret_cast<E*>(smem + lay.v);
   E* Ps = reinterpret_cast<E*>(smem + lay.p);
   float* lamS = reinterpret_cast<float*>(smem + lay.lam);
   float* b2c = reinterpret_cast<float*>(smem + lay.b2);
@@ -464,11 +467,11 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
 
   // ---- loads of this chunk, all issued before the first LDS store
   uint4 qx[SH::NPF], kx[SH::NPF], vx[SH::NPF];
-  float lx[SH::NPL];
+  float lx[SH::NLX];
 #pragma unroll
   for (int p = 0; p < SH::NPF; ++p) {
     const int idx = tid + p * SH::NT;
-    const int cv = idx / C, r = idx % C;          // rows fastest: transposed LDS writes hit one row
+    const int r = idx / SH::VPR, cv = idx % SH::VPR;   // columns fastest: each row read whole
     qx[p] = kx[p] = vx[p] = make_uint4(0, 0, 0, 0);
     if (idx < SH::NV && r < nv) {
       qx[p] = *reinterpret_cast<const uint4*>(qg + r * D + cv * EPV);
@@ -476,12 +479,27 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
       vx[p] = *reinterpret_cast<const uint4*>(vg + r * D + cv * EPV);
     }
   }
+  // lambda rows: 16-byte loads on full chunks when aligned, else one value
+  // per load
+  const bool lam4 = FULL && a.lam_vec4;
 #pragma unroll
-  for (int p = 0; p < SH::NPL; ++p) {
-    lx[p] = 0.f;
-    if (p * SH::NT >= C * L) continue;
-    const int idx = tid + p * SH::NT;
-    if (idx < nv * L) lx[p] = lg[idx];
+  for (int p = 0; p < SH::NLX; ++p) lx[p] = 0.f;
+  if (lam4) {
+#pragma unroll
+    for (int p = 0; p < SH::NPL4; ++p) {
+      const int idx = tid + p * SH::NT;
+      if (4 * idx < C * L) {
+        const float4 f = *reinterpret_cast<const float4*>(lg + 4 * idx);
+        lx[4 * p] = f.x; lx[4 * p + 1] = f.y; lx[4 * p + 2] = f.z; lx[4 * p + 3] = f.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < SH::NPL; ++p) {
+      if (p * SH::NT >= C * L) continue;
+      const int idx = tid + p * SH::NT;
+      if (idx < nv * L) lx[p] = lg[idx];
+    }
   }
   // wave 0: the chunk's log gates, KPG consecutive tokens per lane
   constexpr int KPG = C <= 64 ? 1 : 2;
@@ -560,24 +578,32 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
       if (u < n_lev) load_node(u, nf[u]);
   }
 
-  // ---- LDS stores: Q and K row-major, V^T, lambda rows, gate prefix
+  // ---- LDS stores: Q, K and V row-major, lambda rows, gate prefix
 #pragma unroll
   for (int p = 0; p < SH::NPF; ++p) {
     const int idx = tid + p * SH::NT;
     if (idx < SH::NV) {
-      const int cv = idx / C, r = idx % C;
+      const int r = idx / SH::VPR, cv = idx % SH::VPR;
       *reinterpret_cast<uint4*>(Qs + r * lay.ld_row + cv * EPV) = qx[p];
       *reinterpret_cast<uint4*>(Ks + r * lay.ld_row + cv * EPV) = kx[p];
-      const E* ve = reinterpret_cast<const E*>(&vx[p]);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) VT[(cv * EPV + e) * lay.ld_t + r] = ve[e];
+      uint32_t* vrow = reinterpret_cast<uint32_t*>(Vs + r * lay.ld_v + cv * EPV);   // 4-byte aligned rows
+      vrow[0] = vx[p].x; vrow[1] = vx[p].y; vrow[2] = vx[p].z; vrow[3] = vx[p].w;
     }
   }
+  if (lam4) {
 #pragma unroll
-  for (int p = 0; p < SH::NPL; ++p) {
-    if (p * SH::NT >= C * L) continue;
-    const int idx = tid + p * SH::NT;
-    if (idx < C * L) lamS[idx] = lx[p];
+    for (int p = 0; p < SH::NPL4; ++p) {
+      const int idx = tid + p * SH::NT;
+      if (4 * idx < C * L)
+        *reinterpret_cast<float4*>(lamS + 4 * idx) = make_float4(lx[4 * p], lx[4 * p + 1], lx[4 * p + 2], lx[4 * p + 3]);
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < SH::NPL; ++p) {
+      if (p * SH::NT >= C * L) continue;
+      const int idx = tid + p * SH::NT;
+      if (idx < C * L) lamS[idx] = lx[p];
+    }
   }
   if (w == 0) {
     // in-chunk prefix of log2(a) and its exp2 (the row gate to the chunk start),
@@ -680,6 +706,27 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   for (int rb = 0; rb < QB; ++rb)
 #pragma unroll
     for (int n = 0; n < NCB; ++n) acc[rb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // V^T fragments (row d_v, a k-slice of keys) gathered from row-major V
+  Frag vf[SH::KSC][NCB];
+#pragma unroll
+  for (int s = 0; s < SH::KSC; ++s) {
+    const int k0 = s * KST + lq * KPL;
+#pragma unroll
+    for (int n = 0; n < NCB; ++n) {
+      const int dv = 16 * (cb0 + n) + lr;
+      if constexpr (BF16) {
+        u16x8 f = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (C >= KST || k0 < C) {
+          const unsigned short* vcol = reinterpret_cast<const unsigned short*>(Vs) + dv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = vcol[(k0 + e) * lay.ld_v];
+        }
+        vf[s][n] = __builtin_bit_cast(Frag, f);
+      } else {
+        vf[s][n] = Vs[k0 * lay.ld_v + dv];
+      }
+    }
+  }
   // O^T = V^T P^T over keys 0 .. 16 rb + 15 of each row block
 #pragma unroll
   for (int rb = 0; rb < QB; ++rb) {
@@ -692,10 +739,7 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
       else if constexpr (BF16) pb = __builtin_bit_cast(Frag, u16x8{0, 0, 0, 0, 0, 0, 0, 0});
       else pb = 0.f;
 #pragma unroll
-      for (int n = 0; n < NCB; ++n) {
-        const auto vf = EL::template load_k<C>(VT + (16 * (cb0 + n) + lr) * lay.ld_t + k0, k0);
-        acc[rb][n] = EL::mma(vf, pb, acc[rb][n]);
-      }
+      for (int n = 0; n < NCB; ++n) acc[rb][n] = EL::mma(vf[s][n], pb, acc[rb][n]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }

@@ -96,12 +96,14 @@ LA_HD constexpr StateLds state_lds(int C, int D, int es, int G) {
   return o;
 }
 struct OutLds {
-  int q, k, vt, p, lam, b2, e2, total, ld_row, ld_t, ld_p;
+  int q, k, v, p, lam, b2, e2, total, ld_row, ld_v, ld_p;
 };
 LA_HD constexpr OutLds output_lds(int C, int D, int es, int L) {
   OutLds o{};
   o.ld_row = D + 16 / es;
-  o.ld_t = C + 16 / es;
+  // V stays row-major; its rows are 4 bytes longer than a multiple of 16, so
+  // the eight rows one V^T fragment gathers from fall in different banks
+  o.ld_v = D + 4 / es;
   o.ld_p = C + 16 / es;
   int off = 0;
   o.q = off;    off += (C * o.ld_row * es + 255) / 256 * 256;
@@ -112,7 +114,7 @@ LA_HD constexpr OutLds output_lds(int C, int D, int es, int L) {
     const int kb = C * o.ld_row * es, pb = C * o.ld_p * es;
     off += ((kb > pb ? kb : pb) + 255) / 256 * 256;
   }
-  o.vt = off;   off += (D * o.ld_t * es + 255) / 256 * 256;
+  o.v = off;    off += (C * o.ld_v * es + 255) / 256 * 256;
   o.lam = off;  off += (C * L * 4 + 255) / 256 * 256;
   o.b2 = off;   off += (C * 4 + 255) / 256 * 256;
   o.e2 = off;   off += (C * 4 + 255) / 256 * 256;
