@@ -87,6 +87,12 @@ __device__ __forceinline__ void chunk_gate_scan(const float* la_bh, int64_t base
   }
 }
 
+// Column swizzle of the transposed (token-contiguous) tiles of the state
+// kernel: row n's tokens are XOR-permuted in granules of 8 by its 8-row block,
+// masked to the chunk width.
+template <int C>
+__device__ __forceinline__ int state_swz(int n) { return 8 * ((n >> 3) & (C / 8 - 1)); }
+
 // ---------------------------------------------------------------------------
 // fwd_chunk_states: one workgroup per (b,h, group of G chunks).
 template <bool BF16, int C, int D>
@@ -129,7 +135,7 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
 #pragma unroll
     for (int p = 0; p < SH::NPF; ++p) {
       const int idx = tid + p * SH::NT;
-      const int cv = idx / C, r = idx % C;       // rows fastest: transposed LDS writes hit one row
+      const int r = idx / SH::VPR, cv = idx % SH::VPR;   // columns fastest: each row read whole
       dk[p] = dv[p] = make_uint4(0, 0, 0, 0);
       if (idx < SH::NV && r < nv) {
         const int64_t off = ((int64_t)c * C + r) * D + cv * EPV;
@@ -175,20 +181,25 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
     E* VT = reinterpret_cast<E*>(smem + ((c & 1) ? lay.vt[1] : lay.vt[0]));
     E* KTs = reinterpret_cast<E*>(smem + ((c & 1) ? lay.kts[1] : lay.kts[0]));
     // stage V^T and K^T gated to the chunk end (with one buffer, the previous
-    // chunk's readers must be done first)
+    // chunk's readers must be done first).  A lane holds EPV elements of one
+    // token row; the column (token) of row n is XOR-swizzled in 8-token
+    // granules by swz(n), so the lanes writing the rows of one granule of d
+    // land in different banks, and a fragment read stays one whole granule.
     if (lay.nbuf == 1 && c > 0) __syncthreads();
 #pragma unroll
     for (int p = 0; p < SH::NPF; ++p) {
       const int idx = tid + p * SH::NT;
       if (idx < SH::NV) {
-        const int cv = idx / C, r = idx % C;
+        const int r = idx / SH::VPR, cv = idx % SH::VPR;
         const E* ke = reinterpret_cast<const E*>(&pk[c & 1][p]);
         const E* ve = reinterpret_cast<const E*>(&pv[c & 1][p]);
         const float u = __builtin_amdgcn_exp2f(gc - b2c[r]);
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-          VT[(cv * EPV + e) * lay.ld_t + r] = ve[e];
-          KTs[(cv * EPV + e) * lay.ld_t + r] = EL::from_f32(EL::to_f32(ke[e]) * u);
+          const int n = cv * EPV + e;
+          const int col = r ^ state_swz<C>(n);
+          VT[n * lay.ld_t + col] = ve[e];
+          KTs[n * lay.ld_t + col] = EL::from_f32(EL::to_f32(ke[e]) * u);
         }
       }
     }
@@ -209,23 +220,31 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
       const int tix = w + h * NW;
       if (tix >= SH::HT) continue;
       const int mb = tix / DB, nb = tix % DB;
+      // transposed tile: hh[i] = H[d_v = 16 mb + lr][d_k = 16 nb + 4 lq + i]
       f32x4 hh = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < SH::KSC; ++s) {
         const int k0 = s * KST + lq * KPL;
-        const auto va = EL::template load_k<C>(VT + (16 * mb + lr) * lay.ld_t + k0, k0);
-        const auto kf = EL::template load_k<C>(KTs + (16 * nb + lr) * lay.ld_t + k0, k0);
-        hh = EL::mma(va, kf, hh);
+        const int nv_ = 16 * mb + lr, nk_ = 16 * nb + lr;
+        const auto va = EL::template load_k<C>(VT + nv_ * lay.ld_t + (k0 ^ state_swz<C>(nv_)), k0);
+        const auto kf = EL::template load_k<C>(KTs + nk_ * lay.ld_t + (k0 ^ state_swz<C>(nk_)), k0);
+        hh = EL::mma(kf, va, hh);
       }
       // the bucket ending at this chunk: the chunk plus levels 1..kk
 #pragma unroll
       for (int j = 0; j < NS; ++j)
         if (j < kk) hh += fj[j] * sl[j][h];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * mb + 4 * lq + i, col = 16 * nb + lr;   // (d_v, d_k)
-        if (write_node) nin[(int64_t)c * D * D + row * D + col] = EL::from_f32(hh[i]);
-        if (write_group) a.gstate[(bh * ng + gam) * D * D + row * D + col] = hh[i];
+      {
+        const int row = 16 * mb + lr, col = 16 * nb + 4 * lq;      // (d_v, d_k .. d_k + 3)
+        if (write_node) {
+          E* o = nin + (int64_t)c * D * D + row * D + col;
+          if constexpr (BF16)
+            *reinterpret_cast<u16x4*>(o) = u16x4{f32_to_bf16(hh[0]), f32_to_bf16(hh[1]), f32_to_bf16(hh[2]),
+                                                 f32_to_bf16(hh[3])};
+          else
+            *reinterpret_cast<f32x4*>(o) = hh;
+        }
+        if (write_group) *reinterpret_cast<f32x4*>(a.gstate + (bh * ng + gam) * D * D + row * D + col) = hh;
       }
 #pragma unroll
       for (int j = 0; j < NS; ++j)
