@@ -256,6 +256,51 @@ def bench_decode(la, torch, dev, steps=256, reps=5):
             "handoff": handoff}
 
 
+def bench_decode_large(la, torch, dev, B=256, steps=64):
+    """Decode steps at batch 256 x 16 heads (1 GiB of slots, four times the
+    256 MB MALL), so the slots cannot stay in the last-level cache.  The
+    slots are filled with values of the right scale; the work depends only
+    on which levels are occupied."""
+    from fenwick_tree_hierarchical_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS["decode_32k_bf16"]
+    S, H, d, P = 16, w.H, w.dk, w.prefix
+    st = la.loglinear_state_init(B, H, d, d, S, dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    st.slots.normal_(0, 0.01, generator=g)
+    st.t = P
+    x = make_inputs(w, device=dev, B=B, T=steps, L=S + 1)
+    a = torch.exp(x["log_a"])
+    per = [(x["q"][:, :, i].contiguous(), x["k"][:, :, i].contiguous(), x["v"][:, :, i].contiguous(),
+            a[:, :, i].contiguous(), x["lam"][:, :, i].contiguous(),
+            torch.empty(B, H, d, dtype=x["q"].dtype, device=dev)) for i in range(steps)]
+    L = la.lib()
+    stream = torch.cuda.current_stream(dev)
+    warm = st.clone()
+    for i in range(4):
+        assert L.loglinear_decode_step(ctypes_byref(la, warm), *[t.data_ptr() for t in per[i][:5]],
+                                       per[i][5].data_ptr(), la.LA_BF16, stream.cuda_stream) == 0
+    del warm
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        rc = L.loglinear_decode_step(ctypes_byref(la, st), *[t.data_ptr() for t in per[i][:5]], per[i][5].data_ptr(),
+                                     la.LA_BF16, stream.cuda_stream)
+        if rc:
+            raise RuntimeError(la.loglinear_strerror(rc))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gpu_ms = e0.elapsed_time(e1)
+    slot = d * d * 4
+    tot = sum((bin(t).count("1") + 1) * slot + 4 * d * 2 + 4 + (S + 1) * 4 + 2 * S * 4
+              for t in range(P, P + steps)) * B * H
+    return {"batch": B, "heads": B * H, "steps": steps, "slot_bytes": B * H * S * slot,
+            "us_per_step_gpu": gpu_ms / steps * 1e3, "achieved_gbps": tot / (gpu_ms * 1e-3) / 1e9,
+            "frac": tot / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+
+
 def ctypes_byref(la, st):
     import ctypes
     return ctypes.byref(st._st)
@@ -453,7 +498,10 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    stage_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(n_st)]
+    per_step = [[e[j].elapsed_time(e[j + 1]) for e in evs] for j in range(n_st)]
+    stage_ms = [sum(v) / args.steps for v in per_step]
+    stage_med = [sorted(v)[len(v) // 2] for v in per_step]
+    stage_min = [min(v) for v in per_step]
     ms_per_step = wall / args.steps * 1e3
     tokens = w.B * w.T
     value = tokens / (wall / args.steps)
@@ -479,11 +527,11 @@ def main():
                                        f"lambda plus one read of every bucket node "
                                        f"({cnt['node_bytes_per_bh']} B per (b,h))",
                      "mean_launch_ms": out_ms, "traffic_note": why, "kernel_source_hash": src_hash},
-        "stages": {n: {"ms": m, "alg_bytes": cnt["kernel_bytes"][n],
+        "stages": {n: {"ms": m, "median_ms": stage_med[i], "min_ms": stage_min[i], "alg_bytes": cnt["kernel_bytes"][n],
                        "alg_gbps": cnt["kernel_bytes"][n] / (m * 1e-3) / 1e9,
                        "frac_hbm": cnt["kernel_bytes"][n] / (m * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                        "traffic_bytes": (traffic or {}).get(n)}
-                   for n, m in st_ms.items()},
+                   for i, (n, m) in enumerate(st_ms.items())},
         "mfma": {"alg_tflop": cnt["flops"] / 1e12,
                  "achieved_tflops_whole_fwd": cnt["flops"] / (fwd_ms * 1e-3) / 1e12,
                  "frac_of_bf16_peak_whole_fwd": cnt["flops"] / (fwd_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
@@ -494,6 +542,8 @@ def main():
     if not args.no_decode:
         log("bench: decode 256 steps")
         result["decode"] = bench_decode(la, torch, dev)
+        log("bench: decode at batch 256")
+        result["decode"]["batch_256"] = bench_decode_large(la, torch, dev)
     if not args.no_cpu:
         log(f"bench: oracle CPU baseline on {args.cpu_heads} heads")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
