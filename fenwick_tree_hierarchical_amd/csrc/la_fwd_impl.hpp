@@ -269,45 +269,32 @@ template <bool BF16, int MAXJ>
 __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
   using EL = Elem<BF16>;
   using E = typename EL::T;
-  constexpr int kEl = 2;      // state elements per thread: a launch fits the GPU in one round
   const int DD = D * D;
-  const int nblk = (DD + 256 * kEl - 1) / (256 * kEl);
+  const int nblk = (DD + 255) / 256;
   const int64_t bh = blockIdx.x / nblk;
   const int blk = blockIdx.x % nblk;
-  int elem[kEl];
-  bool valid[kEl];
-#pragma unroll
-  for (int q = 0; q < kEl; ++q) {
-    elem[q] = blk * 256 * kEl + q * 256 + threadIdx.x;
-    valid[q] = elem[q] < DD;
-  }
+  const int elem = blk * 256 + threadIdx.x;
+  const bool valid = elem < DD;
   const int64_t ng = a.n_groups, nfg = a.n_full_groups;
-  float slot[MAXJ][kEl];
-  float sc[MAXJ];             // lazy log2 gates, the same for every element
+  float slot[MAXJ];
+  float sc[MAXJ];
 #pragma unroll
-  for (int j = 0; j < MAXJ; ++j) {
-    sc[j] = 0.f;
-#pragma unroll
-    for (int q = 0; q < kEl; ++q) slot[j][q] = 0.f;
-  }
+  for (int j = 0; j < MAXJ; ++j) { slot[j] = 0.f; sc[j] = 0.f; }
   double pre = 0.0;
   const bool writer = blk == 0 && threadIdx.x == 0;
   const float* gs = a.gstate + bh * ng * DD;
   E* nd = reinterpret_cast<E*>(a.nodes) + bh * ng * DD;
   constexpr int kBatch = 8;   // independent loads issued together, then walked
   for (int64_t e0 = 0; e0 < nfg; e0 += kBatch) {
-    float Av[kBatch][kEl], gv[kBatch];
+    float Av[kBatch], gv[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int64_t e = e0 + u;
+      Av[u] = 0.f;
       gv[u] = 0.f;
-#pragma unroll
-      for (int q = 0; q < kEl; ++q) Av[u][q] = 0.f;
       if (e < nfg) {
         gv[u] = a.gtot[bh * ng + e];
-#pragma unroll
-        for (int q = 0; q < kEl; ++q)
-          if (valid[q]) Av[u][q] = gs[e * DD + elem[q]];
+        if (valid) Av[u] = gs[e * DD + elem];
       }
     }
 #pragma unroll
@@ -318,22 +305,16 @@ __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
       const float g = gv[u];
       int kk = 0;
       for (int64_t x = e; x & 1; x >>= 1) ++kk;
-      float f[MAXJ];
+      float nw = Av[u];
 #pragma unroll
-      for (int j = 0; j < MAXJ; ++j) f[j] = j < kk ? __builtin_amdgcn_exp2f(sc[j] + g) : 0.f;
+      for (int j = 0; j < MAXJ; ++j)
+        if (j < kk) nw += __builtin_amdgcn_exp2f(sc[j] + g) * slot[j];
 #pragma unroll
-      for (int q = 0; q < kEl; ++q) {
-        float nw = Av[u][q];
-#pragma unroll
-        for (int j = 0; j < MAXJ; ++j)
-          if (j < kk) nw += f[j] * slot[j][q];
-#pragma unroll
-        for (int j = 0; j < MAXJ; ++j)
-          if (j == kk) slot[j][q] = nw;
-        if (valid[q]) nd[e * DD + elem[q]] = EL::from_f32(nw);
+      for (int j = 0; j < MAXJ; ++j) {
+        if (j == kk) { slot[j] = nw; sc[j] = 0.f; }
+        else sc[j] += g;
       }
-#pragma unroll
-      for (int j = 0; j < MAXJ; ++j) sc[j] = (j == kk) ? 0.f : sc[j] + g;
+      if (valid) nd[e * DD + elem] = EL::from_f32(nw);
       pre += (double)g;
     }
   }
@@ -894,7 +875,7 @@ int launch_fwd_impl(const FwdPlan& p, FwdArgs a, hipStream_t s, hipEvent_t const
   }
   if (p.n_groups > 1 || (final_state && p.has_group_nodes())) {
     mark();
-    const dim3 grid((unsigned)(((D * D + 511) / 512) * p.BH));    // two state elements per thread
+    const dim3 grid((unsigned)(((D * D + 255) / 256) * p.BH));
     const int levels = bit_length(p.n_groups);        // carry levels the walk can reach
     if (levels <= 8)
       hipLaunchKernelGGL((fwd_group_tree<BF16, 8>), grid, dim3(256), 0, s, a, D);
