@@ -21,6 +21,10 @@ order q, k, v, log_a, lambda, each over its full [B, H, T, ...] shape:
   lambda  = softplus(x), x ~ N(0, 1), per token and level
 q, k, v are then cast to the layer dtype (round to nearest even); log_a and
 lambda stay float32.
+
+The backward pass also takes the gradient of the loss with respect to the
+output, ``make_grad_out``: dout ~ N(0, 1) over [B, H, T, d_v], drawn from its
+own generator seeded with the workload seed + 1000, in the layer dtype.
 """
 
 from __future__ import annotations
@@ -116,3 +120,16 @@ def make_inputs(w: Workload, device="cpu", B=None, H=None, T=None, L=None,
     dt = torch_dtype(w.dtype if dtype is None else dtype)
     return dict(q=q.to(dt).contiguous(), k=k.to(dt).contiguous(), v=v.to(dt).contiguous(),
                 log_a=log_a.contiguous(), lam=lam.contiguous())
+
+
+def make_grad_out(w: Workload, device="cpu", B=None, H=None, T=None, seed: int | None = None,
+                  d: int | None = None, dtype: str | None = None):
+    """Seeded upstream gradient dout [B, H, T, d_v] ~ N(0, 1) in the layer dtype."""
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    T = w.T if T is None else T
+    dv = w.dv if d is None else d
+    g = torch.Generator(device=device)
+    g.manual_seed((w.seed if seed is None else seed) + 1000)
+    dout = torch.randn(B, H, T, dv, device=device, dtype=torch.float32, generator=g)
+    return dout.to(torch_dtype(w.dtype if dtype is None else dtype)).contiguous()

@@ -36,6 +36,7 @@ Modules:
   special  -- special-case references written without the level machinery,
               and a pure-Python brute force for tiny inputs
   metrics  -- relative L2 error
+  backward -- the gradients of the operator (chain rule on the quadratic form)
 
 Pin status (what fixes each function other than itself) is listed in the
 header of each module.  Nothing here is "parity unpinned"; the *choice* of the
@@ -43,4 +44,4 @@ level reading above is an interpretation of the pages, which print no formula
 for it.
 """
 
-from . import levels, forms, special, metrics  # noqa: F401
+from . import levels, forms, special, metrics, backward  # noqa: F401

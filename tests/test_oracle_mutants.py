@@ -14,7 +14,8 @@ import pytest
 import torch
 
 from fenwick_tree_hierarchical_amd.workloads import WORKLOADS, make_inputs
-from oracle import forms, levels, metrics, special
+from fenwick_tree_hierarchical_amd.workloads import make_grad_out
+from oracle import backward, forms, levels, metrics, special
 
 
 def _inputs(T, d=3, variant=None, seed=11):
@@ -210,3 +211,119 @@ def test_mutant_is_caught(name, monkeypatch):
     with np.errstate(all="ignore"):
         fails = pin_battery()
     assert fails, f"mutant {name} passed every pin"
+
+
+# ------------------------------------------------------- gradient mutants
+# The gradient pins of test_oracle_backward.py, run on small inputs through
+# the (patched) ``backward.backward_quadratic``.
+
+def _bwd_inputs(T, d=3, variant=None, seed=21):
+    x = _inputs(T, d=d, variant=variant, seed=seed)
+    x = {k: v.double().numpy() for k, v in x.items()}
+    x["dout"] = make_grad_out(WORKLOADS["tiny_f32"], B=1, H=1, T=T, seed=seed, d=d).double().numpy()
+    return x
+
+
+def bwd_pin_battery():
+    names = ("q", "k", "v", "log_a", "lam")
+    fails = []
+    x = _bwd_inputs(7)
+    g = dict(zip(names, backward.backward_quadratic(x["q"], x["k"], x["v"], x["log_a"], x["lam"], x["dout"])))
+
+    def lossf(y):
+        return backward.loss(_real_quad(y["q"], y["k"], y["v"], y["log_a"], y["lam"]), y["dout"])
+
+    for name in names:
+        fd = np.zeros_like(x[name])
+        for idx in np.ndindex(*x[name].shape):
+            xp = {k: v.copy() for k, v in x.items()}
+            xm = {k: v.copy() for k, v in x.items()}
+            xp[name][idx] += 1e-6
+            xm[name][idx] -= 1e-6
+            fd[idx] = (lossf(xp) - lossf(xm)) / 2e-6
+        if not np.allclose(g[name], fd, rtol=1e-6, atol=1e-8):
+            fails.append("fd_" + name)
+    x = _bwd_inputs(30, variant="const:1.0")
+    g = backward.backward_quadratic(x["q"], x["k"], x["v"], x["log_a"], x["lam"], x["dout"])
+    ref = special.mamba2_backward(x["q"], x["k"], x["v"], x["log_a"], x["dout"])
+    for name, u, r in zip(names, g, ref):
+        if metrics.rel_l2(u, r) > 1e-10:
+            fails.append("mamba2_adjoint_" + name)
+    return fails
+
+
+def test_unpatched_gradients_pass_battery():
+    assert bwd_pin_battery() == []
+
+
+_real_bwd = backward.backward_quadratic
+
+
+def _revcumsum(x):
+    return np.cumsum(x[..., ::-1], axis=-1)[..., ::-1]
+
+
+def _dlambda_of(dlog_a):
+    """dLambda_u recovered from its reverse cumulative sum."""
+    nxt = np.concatenate([dlog_a[..., 1:], np.zeros_like(dlog_a[..., :1])], axis=-1)
+    return dlog_a - nxt
+
+
+def m_bwd_exclusive_gate_sum(*a, **kw):
+    dq, dk, dv, dla, dlam = _real_bwd(*a, **kw)
+    return dq, dk, dv, _revcumsum(_dlambda_of(dla)) - _dlambda_of(dla), dlam
+
+
+def m_bwd_forward_gate_sum(*a, **kw):
+    dq, dk, dv, dla, dlam = _real_bwd(*a, **kw)
+    return dq, dk, dv, np.cumsum(_dlambda_of(dla), axis=-1), dlam
+
+
+def m_bwd_no_column_term(q, k, v, log_a, lam, dout, **kw):
+    dq, dk, dv, dla, dlam = _real_bwd(q, k, v, log_a, lam, dout, **kw)
+    col = np.sum(forms._f64(v) * dv, axis=-1)                  # sum_t A S dP over queries of key u
+    return dq, dk, dv, _revcumsum(_dlambda_of(dla) + col), dlam
+
+
+def m_bwd_lambda_kept_in_dlambda(q, k, v, log_a, lam, dout, **kw):
+    dq, dk, dv, dla, dlam = _real_bwd(q, k, v, log_a, lam, dout, **kw)
+    return dq, dk, dv, dla, dlam * forms._f64(lam)
+
+
+def m_bwd_level_shifted(*a, **kw):
+    dq, dk, dv, dla, dlam = _real_bwd(*a, **kw)
+    return dq, dk, dv, dla, np.roll(dlam, 1, axis=-1)
+
+
+def m_bwd_dk_dv_swapped(*a, **kw):
+    dq, dk, dv, dla, dlam = _real_bwd(*a, **kw)
+    return dq, dv, dk, dla, dlam
+
+
+def m_bwd_no_decay(q, k, v, log_a, lam, dout, **kw):
+    return _real_bwd(q, k, v, np.zeros_like(forms._f64(log_a)), lam, dout, **kw)
+
+
+def m_bwd_key_time_reversed(q, k, v, log_a, lam, dout, **kw):
+    dq, dk, dv, dla, dlam = _real_bwd(q, k, v, log_a, lam, dout, **kw)
+    return dq, dk[..., ::-1, :], dv, dla, dlam
+
+
+BWD_MUTANTS = {
+    "bwd_exclusive_gate_sum": m_bwd_exclusive_gate_sum,
+    "bwd_forward_gate_sum": m_bwd_forward_gate_sum,
+    "bwd_no_column_term": m_bwd_no_column_term,
+    "bwd_lambda_kept_in_dlambda": m_bwd_lambda_kept_in_dlambda,
+    "bwd_level_shifted": m_bwd_level_shifted,
+    "bwd_dk_dv_swapped": m_bwd_dk_dv_swapped,
+    "bwd_no_decay": m_bwd_no_decay,
+    "bwd_key_time_reversed": m_bwd_key_time_reversed,
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_gradient_mutant_is_caught(name, monkeypatch):
+    monkeypatch.setattr(backward, "backward_quadratic", BWD_MUTANTS[name])
+    with np.errstate(all="ignore"):
+        fails = bwd_pin_battery()
+    assert fails, f"gradient mutant {name} passed every pin"
