@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "LogAttnError", "lib", "loglinear_fwd", "loglinear_fwd_workspace", "loglinear_fwd_num_stages",
-    "loglinear_fwd_staged", "LogLinearState", "loglinear_state_init", "loglinear_decode_step",
+    "loglinear_fwd_staged", "loglinear_bwd", "loglinear_bwd_workspace", "LogLinearState", "loglinear_state_init", "loglinear_decode_step",
     "loglinear_level_table", "loglinear_strerror", "LA_F32", "LA_BF16",
 ]
 
@@ -42,6 +42,8 @@ _SIGS = {
                               ctypes.POINTER(_p), _i, _p], _i),
     "loglinear_fwd_state": ([_p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _i, _i, _i, _p, _sz,
                              ctypes.POINTER(_LaState), _p], _i),
+    "loglinear_bwd_workspace": ([_i, _i, _i64, _i, _i, _i, _i, ctypes.POINTER(_sz)], _i),
+    "loglinear_bwd": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
     "loglinear_state_bytes": ([_i, _i, _i, _i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz)], _i),
     "loglinear_state_init": ([ctypes.POINTER(_LaState), _i, _i, _i, _i, _i, _p, _p, _p], _i),
     "loglinear_decode_step": ([ctypes.POINTER(_LaState), _p, _p, _p, _p, _p, _p, _i, _p], _i),
@@ -166,6 +168,48 @@ def loglinear_fwd_staged(q, k, v, log_a, lam, events, out=None, chunk: int = 64,
     arr = (_p * len(events))(*[e.cuda_event for e in events])
     _check(lib().loglinear_fwd_staged(*args, arr, len(events), s.cuda_stream), "loglinear_fwd_staged")
     return out
+
+
+def loglinear_bwd_workspace(B: int, H: int, T: int, dk: int, dv: int, C: int, dtype: torch.dtype) -> int:
+    n = _sz(0)
+    _check(lib().loglinear_bwd_workspace(B, H, T, dk, dv, C, _dtype_code(dtype), ctypes.byref(n)),
+           "loglinear_bwd_workspace")
+    return n.value
+
+
+def loglinear_bwd(q, k, v, log_a, lam, dout, chunk: int = 64, workspace=None, grads=None):
+    """Gradients of a loss with respect to q, k, v, log_a and lam, given
+    dout = dL/dout of the forward.  Returns (dq, dk, dv, dlog_a, dlam): dq,
+    dk, dv in q's dtype, dlog_a [B,H,T] and dlam [B,H,T,L] float32.  ``grads``
+    optionally supplies those five output tensors."""
+    dev = _dev(q, k, v, log_a, lam, dout)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or log_a.shape != (B, H, T) or lam.shape[:3] != (B, H, T):
+        raise ValueError("shape mismatch between q, k, v, log_a and lambda")
+    if dout.shape != v.shape or dout.dtype != q.dtype or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v and dout must share one dtype, dout the shape of v")
+    if log_a.dtype != torch.float32 or lam.dtype != torch.float32:
+        raise TypeError("log_a and lambda must be float32")
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                 torch.empty(B, H, T, dtype=torch.float32, device=dev),
+                 torch.empty(B, H, T, L, dtype=torch.float32, device=dev))
+    gq, gk, gv, gla, glam = grads
+    _dev(q, gq, gk, gv, gla, glam)
+    if (gq.shape, gk.shape, gv.shape, gla.shape, glam.shape) != (q.shape, k.shape, v.shape, log_a.shape, lam.shape):
+        raise ValueError("gradient tensors have the wrong shapes")
+    if gq.dtype != q.dtype or gk.dtype != q.dtype or gv.dtype != q.dtype or gla.dtype != torch.float32 \
+            or glam.dtype != torch.float32:
+        raise TypeError("gradient tensors have the wrong dtypes")
+    nws = loglinear_bwd_workspace(B, H, T, dk, dv, chunk, q.dtype)
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    _check(lib().loglinear_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(dout), _ptr(gq), _ptr(gk),
+                               _ptr(gv), _ptr(gla), _ptr(glam), B, H, T, dk, dv, chunk, L, _dtype_code(q.dtype),
+                               _ptr(workspace), workspace.numel(), _stream(dev)), "loglinear_bwd")
+    return gq, gk, gv, gla, glam
 
 
 class LogLinearState:

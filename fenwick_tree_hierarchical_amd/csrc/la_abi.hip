@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include "../../include/logattn.h"
+#include "la_bwd_impl.hpp"
 #include "la_fwd_impl.hpp"
 #include "la_internal.hpp"
 #include "la_plan.hpp"
@@ -137,6 +138,59 @@ LA_API int loglinear_fwd_staged(const void* q, const void* k, const void* v, con
     if (!events[i]) return kEINVAL;
   return fwd_common(q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, L, dtype, workspace,
                     workspace_bytes, events, n_events, nullptr, stream);
+}
+
+LA_API int loglinear_bwd_workspace(int B, int H, int64_t T, int dk, int dv, int C, int dtype,
+                                   size_t* bytes) {
+  if (!bytes) return kEINVAL;
+  BwdPlan p;
+  int rc = plan_bwd(B, H, T, dk, dv, C, dtype, -1, &p);
+  if (rc != kOK) return rc;
+  *bytes = p.ws_bytes;
+  return kOK;
+}
+
+LA_API int loglinear_bwd(const void* q, const void* k, const void* v, const float* log_a,
+                         const float* lambda, const void* dout, void* grad_q, void* grad_k,
+                         void* grad_v, float* grad_log_a, float* grad_lambda, int B, int H, int64_t T,
+                         int dk, int dv, int C, int L, int dtype, void* workspace,
+                         size_t workspace_bytes, la_stream_t stream) {
+  BwdPlan P;
+  int rc = plan_bwd(B, H, T, dk, dv, C, dtype, L, &P);
+  if (rc != kOK) return rc;
+  const FwdPlan& p = P.f;
+  if (p.BH == 0 || T == 0) return kOK;   // empty problem: nothing to read or write
+  if (!q || !k || !v || !log_a || !lambda || !dout) return kEINVAL;
+  if (!grad_q || !grad_k || !grad_v || !grad_log_a || !grad_lambda) return kEINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(grad_q, 16) ||
+      !aligned(grad_k, 16) || !aligned(grad_v, 16))
+    return kEALIGN;
+  if (!aligned(log_a, 4) || !aligned(lambda, 4) || !aligned(grad_log_a, 4) || !aligned(grad_lambda, 4))
+    return kEALIGN;
+  if (!workspace || workspace_bytes < P.ws_bytes) return kEWORKSPACE;
+  if (!aligned(workspace, 256)) return kEALIGN;
+  char* w = static_cast<char*>(workspace);
+  // forward structure over (k := v, v := k): its nodes are sum gate k v^T
+  FwdArgs fa{};
+  fa.q = nullptr; fa.k = v; fa.v = k; fa.log_a = log_a; fa.lam = lambda; fa.out = nullptr;
+  fa.nodes_in = p.has_chunk_nodes() ? static_cast<void*>(w + p.off_nodes_in) : nullptr;
+  fa.gch = p.has_chunk_nodes() ? reinterpret_cast<float*>(w + p.off_gch) : nullptr;
+  fa.gstate = p.has_group_nodes() ? reinterpret_cast<float*>(w + p.off_gstate) : nullptr;
+  fa.gtot = p.has_group_nodes() ? reinterpret_cast<float*>(w + p.off_gtot) : nullptr;
+  fa.gprefix = p.has_group_nodes() ? reinterpret_cast<double*>(w + p.off_gprefix) : nullptr;
+  fa.nodes = p.has_group_nodes() ? static_cast<void*>(w + p.off_nodes) : nullptr;
+  fa.T = T; fa.n_chunks = p.n_chunks; fa.n_groups = p.n_groups; fa.n_full_groups = p.n_full_groups; fa.L = L;
+  BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.log_a = log_a; a.lam = lambda;
+  a.dq = grad_q; a.dk = grad_k; a.dv = grad_v; a.dlog_a = grad_log_a; a.dlam = grad_lambda;
+  a.nodes_in = fa.nodes_in; a.nodes = fa.nodes; a.gch = fa.gch; a.gprefix = fa.gprefix;
+  a.rnodes_in = p.n_chunks > 1 ? static_cast<void*>(w + P.off_rnodes_in) : nullptr;
+  a.rpart = p.n_groups > 1 ? reinterpret_cast<float*>(w + P.off_rpart) : nullptr;
+  a.rnodes = p.n_groups > 1 ? static_cast<void*>(w + P.off_rnodes) : nullptr;
+  a.dcol = reinterpret_cast<float*>(w + P.off_dcol);
+  a.T = T; a.n_chunks = p.n_chunks; a.n_groups = p.n_groups; a.L = L; a.JG = P.JG;
+  hipStream_t s = (hipStream_t)stream;
+  return dtype == kBF16 ? launch_bwd_bf16(P, fa, a, s) : launch_bwd_f32(P, fa, a, s);
 }
 
 LA_API int loglinear_state_bytes(int B, int H, int dk, int dv, int S, size_t* slot_bytes,

@@ -1,0 +1,880 @@
+// Backward pass of log-linear Mamba-2 attention for gfx950.
+//
+// Training needs the gradients of the operator, those of the level weights
+// lambda included ("Log-Linear Attention", Spanish summary, section 5
+// "Limitaciones", first item).  For a loss with gradient dout with respect to
+// O, with A[t,s] = lambda_t^(l(t,s)) M^S[t,s], S = q.k and dP = dout.v:
+//   dq_t = sum_s A dP k_s        dk_s = sum_t A dP q_t       dv_s = sum_t A S dout_t
+//   dlambda_t^l = sum_{s in bucket l of t} M^S S dP
+//   dlog_a_r = sum_{u >= r} (dout_u . o_u - v_u . dv_u),  dout_u . o_u = sum_l lambda_u^l dlambda_u^l.
+// The chunking is the forward's (chunks of C tokens, groups of G chunks).
+//
+// Query side.  The forward's chunk nodes built over (k := v, v := k), i.e.
+// N = sum gate * k v^T in (d_k, d_v) order, give dq_t = sum_l lambda gate
+// N dout_t and dlambda_t^l = gate q_t . N dout_t, so the forward's state and
+// group-tree kernels run unchanged; bwd_chunk_dq forms per chunk the
+// intra-chunk tiles and one product per occupied level.
+//
+// Key side.  The queries that see key s at level l form one aligned block: the
+// upper half of the level-l block holding s.  Their weight lambda_t^l belongs
+// to the query, so every such block needs a node weighted by its own level:
+//   R = sum_{t in block} lambda_t^l gate(block start .. t) q_t dout_t^T.
+// Unlike the forward's nodes these do not merge along the tree (the weights
+// change with the level).  bwd_rev_states forms the blocks inside a group of G
+// chunks, and each group's share of the larger blocks; bwd_rev_tree adds the
+// shares up; bwd_chunk_dkv forms the intra-chunk tiles and, per level,
+// dk_s += gate(s .. block start) R v_s and dv_s += gate R^T k_s.
+// bwd_gate_grad takes the reverse cumulative sum of the per-token gate terms.
+//
+// Gates are in log2 units as in the forward; every exponent applied is <= 0.
+#pragma once
+
+#include "la_bwd_plan.hpp"
+#include "la_fwd_impl.hpp"
+
+namespace la {
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* log_a;
+  const float* lam;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dlog_a;         // [BH][T]: row terms from bwd_chunk_dq, then the gate gradient
+  float* dlam;           // [BH][T][L]
+  const void* nodes_in;  // query side, forward structure over (v, k): [BH][n_chunks][d_k][d_v]
+  const void* nodes;     // [BH][n_groups][d_k][d_v]
+  const float* gch;      // [BH][n_chunks] log2 gate total of each chunk
+  const double* gprefix; // [BH][n_groups + 1] exclusive prefix sums of the group totals
+  void* rnodes_in;       // key side: block starting at chunk x inside a group, [BH][n_chunks][d_k][d_v]
+  float* rpart;          // [BH][n_groups][JG][d_k][d_v] fp32: a group's share of its group-level blocks
+  void* rnodes;          // block starting at group x, [BH][n_groups][d_k][d_v]
+  float* dcol;           // [BH][T]: v_s . dv_s
+  int64_t T;
+  int64_t n_chunks;
+  int64_t n_groups;
+  int L;
+  int JG;                // group levels with an upper block
+};
+
+template <bool BF16, int C, int D>
+struct BwdShape {
+  using EL = Elem<BF16>;
+  static constexpr int NW = bwd_waves(C), NT = 64 * NW;
+  static constexpr int QB = C / 16, DB = D / 16;
+  static constexpr int KSD = (D + EL::kStep - 1) / EL::kStep;   // k-steps over d
+  static constexpr int KSC = (C + EL::kStep - 1) / EL::kStep;   // k-steps over tokens
+  static constexpr int EPV = 16 / (BF16 ? 2 : 4), VPR = D / EPV, NV = C * VPR;
+  static constexpr int NPF = (NV + NT - 1) / NT;
+  static constexpr int LOG2C = cilog2(C);
+};
+
+// Operand fragment of a transposed tile read from a row-major LDS tile: row
+// `col` of tile^T (a column of the tile), k-slice of rows k0 .. k0 + KPL - 1;
+// zero past `rows`.
+template <bool BF16, int ROWS>
+__device__ __forceinline__ typename Elem<BF16>::Frag gather_col(const typename Elem<BF16>::T* tile, int ld, int k0,
+                                                                int col) {
+  if constexpr (BF16) {
+    u16x8 f = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (ROWS >= Elem<BF16>::kStep || k0 < ROWS) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = tile[(k0 + e) * ld + col];
+    }
+    return __builtin_bit_cast(bf16x8, f);
+  } else {
+    return tile[k0 * ld + col];
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ typename Elem<BF16>::Frag zero_frag() {
+  if constexpr (BF16) return __builtin_bit_cast(bf16x8, u16x8{0, 0, 0, 0, 0, 0, 0, 0});
+  else return 0.f;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store4(typename Elem<BF16>::T* p, f32x4 x) {
+  if constexpr (BF16)
+    *reinterpret_cast<u16x4*>(p) = u16x4{f32_to_bf16(x[0]), f32_to_bf16(x[1]), f32_to_bf16(x[2]), f32_to_bf16(x[3])};
+  else
+    *reinterpret_cast<f32x4*>(p) = x;
+}
+
+// Q, K, V and dout rows of chunk `tc` (nv valid rows) into row-major LDS
+// tiles, zero past the end; lambda rows into lamS.
+template <bool BF16, int C, int D>
+__device__ __forceinline__ void bwd_load_chunk(const BwdArgs& a, unsigned char* smem, const BwdChunkLds& lay,
+                                               int64_t bh, int64_t tc, int nv) {
+  using SH = BwdShape<BF16, C, D>;
+  using E = typename Elem<BF16>::T;
+  const int tid = threadIdx.x;
+  const int64_t T = a.T;
+  const int L = a.L;
+  const void* src[4] = {a.q, a.k, a.v, a.dout};
+  const int dst[4] = {lay.q, lay.k, lay.v, lay.g};
+  uint4 x[4][SH::NPF];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const E* g = reinterpret_cast<const E*>(src[m]) + (bh * T + tc) * D;
+#pragma unroll
+    for (int p = 0; p < SH::NPF; ++p) {
+      const int idx = tid + p * SH::NT;
+      const int r = idx / SH::VPR, cv = idx % SH::VPR;
+      x[m][p] = make_uint4(0, 0, 0, 0);
+      if (idx < SH::NV && r < nv) x[m][p] = *reinterpret_cast<const uint4*>(g + r * D + cv * SH::EPV);
+    }
+  }
+  const float* lg = a.lam + (bh * T + tc) * L;
+  float* lamS = reinterpret_cast<float*>(smem + lay.lam);
+  for (int idx = tid; idx < C * L; idx += SH::NT) lamS[idx] = idx < nv * L ? lg[idx] : 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    E* t = reinterpret_cast<E*>(smem + dst[m]);
+#pragma unroll
+    for (int p = 0; p < SH::NPF; ++p) {
+      const int idx = tid + p * SH::NT;
+      if (idx < SH::NV) {
+        const int r = idx / SH::VPR, cv = idx % SH::VPR;
+        *reinterpret_cast<uint4*>(t + r * lay.ld_row + cv * SH::EPV) = x[m][p];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_chunk_dq: one workgroup per (b,h, chunk); wave w owns query rows
+// 16 w .. 16 w + 15.  Writes dq, the lambda gradients of the chunk's rows and
+// the row terms dout_t . o_t = sum_l lambda_t^l dlambda_t^l (into dlog_a).
+template <bool BF16, int C, int D>
+__global__ __launch_bounds__(64 * bwd_waves(C)) void bwd_chunk_dq(BwdArgs a) {
+  using SH = BwdShape<BF16, C, D>;
+  using EL = Elem<BF16>;
+  using E = typename EL::T;
+  using Frag = typename EL::Frag;
+  constexpr int DB = SH::DB, KSD = SH::KSD, KPL = EL::kPerLane, KST = EL::kStep, LOG2C = SH::LOG2C;
+  constexpr int G = state_group(D), LOG2G = cilog2(G);
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int L = a.L;
+  const BwdChunkLds lay = bwd_chunk_lds(C, D, sizeof(E), L, false);
+  const E* Qs = reinterpret_cast<const E*>(smem + lay.q);
+  const E* Ks = reinterpret_cast<const E*>(smem + lay.k);
+  const E* Vs = reinterpret_cast<const E*>(smem + lay.v);
+  const E* Gs = reinterpret_cast<const E*>(smem + lay.g);
+  E* Ps = reinterpret_cast<E*>(smem + lay.s0);
+  const float* lamS = reinterpret_cast<const float*>(smem + lay.lam);
+  float* dlS = reinterpret_cast<float*>(smem + lay.dl);
+  float* b2c = reinterpret_cast<float*>(smem + lay.b2);
+  float* e2c = reinterpret_cast<float*>(smem + lay.e2);
+
+  const int64_t nc = a.n_chunks, ng = a.n_groups, T = a.T;
+  const int64_t item = xcd_item(blockIdx.x, gridDim.x);
+  const int64_t bh = item / nc, c = item % nc;
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id(), lq = lane >> 4, lr = lane & 15;
+  const int64_t tc = c * C;
+  const int nv = (int)(T - tc < C ? T - tc : C);
+
+  bwd_load_chunk<BF16, C, D>(a, smem, lay, bh, tc, nv);
+  for (int idx = tid; idx < C * L; idx += SH::NT) dlS[idx] = 0.f;
+  if (w == 0) {
+    // in-chunk inclusive prefix of log2(a), and its exp2: the gate from the
+    // chunk start through each row
+    const float x = (lane < C && tc + lane < T) ? a.log_a[bh * T + tc + lane] * kLog2e : 0.f;
+    const float y = wave_incl_scan(x);
+    if (lane < C) {
+      b2c[lane] = y;
+      e2c[lane] = __builtin_amdgcn_exp2f(y);
+    }
+  }
+
+  // occupied levels above the chunk, as in the forward: lanes 1..LOG2G hold
+  // the chunk levels inside the group, lanes 32..62 the group levels
+  const int64_t gam = c / G, cg0 = gam * G;
+  const int ci = (int)(c - cg0);
+  bool act = false;
+  int64_t off = 0;
+  int lev = 0, src = 0;
+  int64_t eg = 0;
+  if (lane >= 1 && lane <= LOG2G) {
+    const int j = lane;
+    if ((ci >> (j - 1)) & 1) {
+      const int el = ((ci >> j) << j) + (1 << (j - 1)) - 1;
+      act = true;
+      off = (bh * nc + cg0 + el) * D * D;
+      src = el + 1;
+      lev = LOG2C + j;
+    }
+  }
+  if (lane >= 32 && lane < 63) {
+    const int i = lane - 31;
+    if (gam > 0 && ((gam >> (i - 1)) & 1)) {
+      eg = ((gam >> i) << i) + (1ll << (i - 1)) - 1;
+      act = true;
+      off = (bh * ng + eg) * D * D;
+      lev = LOG2C + LOG2G + i;
+    }
+  }
+  const unsigned long long lmask = __ballot(act);
+  const int n_lev = __popcll(lmask);
+  const int pos = __popcll(lmask & ((1ull << lane) - 1ull));
+  const int ent = __builtin_amdgcn_ds_permute((act ? pos : 63) << 2, lane);
+  const float gx = (lane < ci) ? a.gch[bh * nc + cg0 + lane] : 0.f;
+  const bool grp = act && lane >= 32;
+  float g2 = 0.f;
+  {
+    const float incl = wave_incl_scan(gx);
+    float S = __shfl_up(incl, 1, 64);
+    if (lane == 0) S = 0.f;
+    const float pre = __shfl(S, ci, 64);
+    const float Se = __shfl(S, src, 64);
+    if (act) {
+      if (grp) {
+        const double* gp = a.gprefix + bh * (ng + 1);
+        g2 = (float)(gp[gam] - gp[eg + 1]) + pre;
+      } else {
+        g2 = pre - Se;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 1: score tiles of row block rb = w against key blocks kb <= rb,
+  // transposed (lane: query row, four keys).  dS = dP * gate * lambda goes to
+  // LDS; the lambda gradients of levels 0..log2 C sum S * dP * gate by level.
+  const int rb = w;
+  const int iq = 16 * rb + lr;
+  float dlr[LOG2C + 1];
+#pragma unroll
+  for (int u = 0; u <= LOG2C; ++u) dlr[u] = 0.f;
+  for (int kb = 0; kb <= rb; ++kb) {
+    f32x4 ss = f32x4{0.f, 0.f, 0.f, 0.f}, sd = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KSD; ++s) {
+      const int k0 = s * KST + lq * KPL;
+      const auto kf = EL::template load_k<D>(Ks + (16 * kb + lr) * lay.ld_row + k0, k0);
+      const auto qf = EL::template load_k<D>(Qs + iq * lay.ld_row + k0, k0);
+      ss = EL::mma(kf, qf, ss);
+      const auto vf = EL::template load_k<D>(Vs + (16 * kb + lr) * lay.ld_row + k0, k0);
+      const auto gf = EL::template load_k<D>(Gs + iq * lay.ld_row + k0, k0);
+      sd = EL::mma(vf, gf, sd);
+    }
+    const int j0 = 16 * kb + 4 * lq;
+    const float b2q = b2c[iq];
+    float dsv[4], ev[4];
+    int lvv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + i;
+      int lv = fenwick_level_local((unsigned)iq, (unsigned)j);
+      lv = lv < L ? lv : L - 1;
+      const float W = __builtin_amdgcn_exp2f(b2q - b2c[j]);
+      const bool ok = j <= iq && iq < nv;
+      dsv[i] = ok ? sd[i] * W * lamS[iq * L + lv] : 0.f;
+      ev[i] = ok ? ss[i] * sd[i] * W : 0.f;
+      lvv[i] = lv;
+    }
+    if (kb == rb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int u = 0; u <= 4 && u <= LOG2C; ++u) dlr[u] += (lvv[i] == u) ? ev[i] : 0.f;
+    } else {
+      // every key of an earlier 16-block is at level 5 + msb(rb ^ kb)
+      const int lk = 5 + (31 - __builtin_clz((unsigned)(rb ^ kb)));
+      const float es = (ev[0] + ev[1]) + (ev[2] + ev[3]);
+#pragma unroll
+      for (int u = 5; u <= LOG2C; ++u) dlr[u] += (lk == u) ? es : 0.f;
+    }
+    if constexpr (BF16)
+      *reinterpret_cast<u16x4*>(Ps + iq * lay.ld_s + j0) =
+          u16x4{f32_to_bf16(dsv[0]), f32_to_bf16(dsv[1]), f32_to_bf16(dsv[2]), f32_to_bf16(dsv[3])};
+    else
+      *reinterpret_cast<float4*>(Ps + iq * lay.ld_s + j0) = make_float4(dsv[0], dsv[1], dsv[2], dsv[3]);
+  }
+#pragma unroll
+  for (int u = 0; u <= LOG2C; ++u) {
+    dlr[u] += __shfl_xor(dlr[u], 16, 64);
+    dlr[u] += __shfl_xor(dlr[u], 32, 64);
+  }
+  if (lq == 0 && iq < nv) {
+#pragma unroll
+    for (int u = 0; u <= LOG2C; ++u)
+      if (u < L) dlS[iq * L + u] = dlr[u];
+  }
+  __syncthreads();
+
+  // ---- phase 2: dq^T = K^T dS^T over keys 0 .. 16 rb + 15 (lane: query row,
+  // four consecutive d_k), then one product dout N^T per occupied level
+  f32x4 acc[DB];
+#pragma unroll
+  for (int n = 0; n < DB; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < SH::KSC; ++s) {
+    if (s * KST > 16 * rb + 15) break;
+    const int k0 = s * KST + lq * KPL;
+    Frag pb = zero_frag<BF16>();
+    if (k0 < C && k0 / 16 <= rb) pb = EL::load(Ps + iq * lay.ld_s + k0);
+#pragma unroll
+    for (int n = 0; n < DB; ++n) {
+      const Frag kt = gather_col<BF16, C>(Ks, lay.ld_row, k0, 16 * n + lr);
+      acc[n] = EL::mma(kt, pb, acc[n]);
+    }
+  }
+  Frag gfr[KSD];
+#pragma unroll
+  for (int s2 = 0; s2 < KSD; ++s2) {
+    const int k0 = s2 * KST + lq * KPL;
+    gfr[s2] = EL::template load_k<D>(Gs + iq * lay.ld_row + k0, k0);
+  }
+  const float e2q = e2c[iq];
+  for (int li = 0; li < n_lev; ++li) {
+    const int el = __builtin_amdgcn_readlane(ent, li);
+    const uint64_t o64 = (uint64_t)off;
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)o64, el);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(o64 >> 32), el);
+    const int64_t o = (int64_t)(((uint64_t)hi << 32) | lo);
+    const E* node = (el >= 32 ? reinterpret_cast<const E*>(a.nodes) : reinterpret_cast<const E*>(a.nodes_in)) + o;
+    const float f = __builtin_amdgcn_exp2f(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g2), el)));
+    const int lv = __builtin_amdgcn_readlane(lev, el);
+    const float wq = e2q * f;
+    const float wl = wq * lamS[iq * L + lv];
+    float dsum = 0.f;
+#pragma unroll
+    for (int n = 0; n < DB; ++n) {
+      f32x4 tmp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < KSD; ++s2) {
+        const int k0 = s2 * KST + lq * KPL;
+        const auto nf = EL::template load_k<D>(node + (16 * n + lr) * D + k0, k0);
+        tmp = EL::mma(nf, gfr[s2], tmp);
+      }
+      const E* qrow = Qs + iq * lay.ld_row + 16 * n + 4 * lq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dsum += tmp[i] * EL::to_f32(qrow[i]);
+        acc[n][i] += wl * tmp[i];
+      }
+    }
+    dsum += __shfl_xor(dsum, 16, 64);
+    dsum += __shfl_xor(dsum, 32, 64);
+    if (lq == 0 && iq < nv) dlS[iq * L + lv] = wq * dsum;
+  }
+  if (iq < nv) {
+    E* o = reinterpret_cast<E*>(a.dq) + (bh * T + tc + iq) * D + 4 * lq;
+#pragma unroll
+    for (int n = 0; n < DB; ++n) store4<BF16>(o + 16 * n, acc[n]);
+  }
+  __syncthreads();
+  // row terms and the lambda gradients of the chunk's rows (levels with an
+  // empty bucket stay zero)
+  if (tid < nv) {
+    float r = 0.f;
+    for (int u = 0; u < L; ++u) r += lamS[tid * L + u] * dlS[tid * L + u];
+    a.dlog_a[bh * T + tc + tid] = r;
+  }
+  float* dl = a.dlam + (bh * T + tc) * L;
+  for (int idx = tid; idx < nv * L; idx += SH::NT) dl[idx] = dlS[idx];
+}
+
+// ---------------------------------------------------------------------------
+// bwd_rev_states: one workgroup per (b,h, group of G chunks).  For every chunk
+// level j: the key-side node of each block inside the group that is the upper
+// half of its level-j block (chunks whose in-group index has bit j-1 set), and,
+// for the group levels whose bit is set in the group index, the group's share
+// of its block (gate measured from the group start).  One level at a time, one
+// chunk at a time: gated Q^T and dout^T staged transposed, then
+// R += dout^T-by-Q products on the matrix cores.
+template <bool BF16, int C, int D>
+__global__ __launch_bounds__(64 * state_waves(D)) void bwd_rev_states(BwdArgs a) {
+  using EL = Elem<BF16>;
+  using E = typename EL::T;
+  constexpr int NW = state_waves(D), NT = 64 * NW, DB = D / 16, HT = DB * DB, TPW = state_tiles_per_wave(D);
+  constexpr int G = state_group(D), LOG2G = cilog2(G), LOG2C = cilog2(C);
+  constexpr int KPL = EL::kPerLane, KST = EL::kStep, KSC = (C + KST - 1) / KST;
+  constexpr int EPV = 16 / (BF16 ? 2 : 4), VPR = D / EPV, NV = C * VPR, NPF = (NV + NT - 1) / NT;
+  constexpr RevLds lay = rev_lds(C, D, sizeof(E), G);
+  extern __shared__ __align__(16) unsigned char smem[];
+  E* QT = reinterpret_cast<E*>(smem + lay.qt);
+  E* GT = reinterpret_cast<E*>(smem + lay.gt);
+  float* b2s = reinterpret_cast<float*>(smem + lay.b2);
+
+  const int64_t ng = a.n_groups, nc = a.n_chunks, T = a.T;
+  const int64_t bh = blockIdx.x / ng, gam = blockIdx.x % ng;
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id(), lq = lane >> 4, lr = lane & 15;
+  const int L = a.L;
+  const int64_t c0 = gam * G;
+  const int nch = (int)(nc - c0 < G ? nc - c0 : G);
+  const int64_t t0 = c0 * C;
+  const float* la_bh = a.log_a + bh * T;
+  for (int c = w; c < nch; c += NW) chunk_gate_scan<C>(la_bh, t0 + (int64_t)c * C, T, b2s + c * C);
+  __syncthreads();
+
+  const E* qb = reinterpret_cast<const E*>(a.q) + (bh * T + t0) * D;
+  const E* gb = reinterpret_cast<const E*>(a.dout) + (bh * T + t0) * D;
+  const float* lb = a.lam + (bh * T + t0) * L;
+  f32x4 acc[TPW];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int h = 0; h < TPW; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // R[d_k][d_v] tiles of this wave to dst (row-major (d_k, d_v))
+  auto flush = [&](auto* dst) {
+#pragma unroll
+    for (int h = 0; h < TPW; ++h) {
+      const int tix = w + h * NW;
+      if (tix >= HT) continue;
+      const int mb = tix / DB, nb = tix % DB;
+      auto* o = dst + (16 * mb + lr) * D + 16 * nb + 4 * lq;
+      if constexpr (sizeof(*o) == 4) *reinterpret_cast<f32x4*>(o) = acc[h];
+      else store4<BF16>(reinterpret_cast<E*>(o), acc[h]);
+    }
+  };
+  const int nlev = LOG2G + a.JG;
+  for (int j = 1; j <= nlev; ++j) {
+    const bool in_group = j <= LOG2G;
+    if (!in_group && !((gam >> (j - LOG2G - 1)) & 1)) continue;
+    const int lvl = LOG2C + j;
+    zero_acc();
+    for (int ci = 0; ci < nch; ++ci) {
+      if (in_group && !((ci >> (j - 1)) & 1)) continue;
+      const int xs = in_group ? ((ci >> (j - 1)) << (j - 1)) : 0;   // block (or group) start
+      float pre = 0.f;                                                 // gate from xs to this chunk
+      for (int u = xs; u < ci; ++u) pre += b2s[u * C + C - 1];
+      const int nvr = (int)(T - t0 - (int64_t)ci * C < C ? T - t0 - (int64_t)ci * C : C);
+      // stage Q^T weighted by lambda of the level and the gate, and dout^T
+      uint4 qx[NPF], gx[NPF];
+      float wr[NPF];
+#pragma unroll
+      for (int p = 0; p < NPF; ++p) {
+        const int idx = tid + p * NT;
+        const int r = idx / VPR, cv = idx % VPR;
+        qx[p] = gx[p] = make_uint4(0, 0, 0, 0);
+        wr[p] = 0.f;
+        if (idx < NV && r < nvr) {
+          const int64_t off = ((int64_t)ci * C + r) * D + cv * EPV;
+          qx[p] = *reinterpret_cast<const uint4*>(qb + off);
+          gx[p] = *reinterpret_cast<const uint4*>(gb + off);
+          wr[p] = lb[((int64_t)ci * C + r) * L + lvl] * __builtin_amdgcn_exp2f(b2s[ci * C + r] + pre);
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < NPF; ++p) {
+        const int idx = tid + p * NT;
+        if (idx < NV) {
+          const int r = idx / VPR, cv = idx % VPR;
+          const E* qe = reinterpret_cast<const E*>(&qx[p]);
+          const E* ge = reinterpret_cast<const E*>(&gx[p]);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            const int n = cv * EPV + e;
+            const int col = r ^ state_swz<C>(n);
+            QT[n * lay.ld_t + col] = EL::from_f32(EL::to_f32(qe[e]) * wr[p]);
+            GT[n * lay.ld_t + col] = ge[e];
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int h = 0; h < TPW; ++h) {
+        const int tix = w + h * NW;
+        if (tix >= HT) continue;
+        const int mb = tix / DB, nb = tix % DB;   // d_k block, d_v block
+#pragma unroll
+        for (int s = 0; s < KSC; ++s) {
+          const int k0 = s * KST + lq * KPL;
+          const int ng_ = 16 * nb + lr, nq_ = 16 * mb + lr;
+          const auto gf = EL::template load_k<C>(GT + ng_ * lay.ld_t + (k0 ^ state_swz<C>(ng_)), k0);
+          const auto qf = EL::template load_k<C>(QT + nq_ * lay.ld_t + (k0 ^ state_swz<C>(nq_)), k0);
+          acc[h] = EL::mma(gf, qf, acc[h]);
+        }
+      }
+      __syncthreads();
+      const bool last = in_group ? ((((ci + 1) & ((1 << (j - 1)) - 1)) == 0) || ci == nch - 1) : ci == nch - 1;
+      if (last) {
+        if (in_group) {
+          flush(reinterpret_cast<E*>(a.rnodes_in) + (bh * nc + c0 + xs) * D * D);
+        } else {
+          flush(a.rpart + ((bh * ng + gam) * a.JG + (j - LOG2G - 1)) * D * D);
+        }
+        zero_acc();
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_rev_tree: the key-side node of every block of groups that is the upper
+// half of its level block: it starts at group x >= 1 and spans 2^ctz(x)
+// groups; the sum of those groups' shares, each carried by the gate from the
+// block start to the group start.
+template <bool BF16>
+__global__ __launch_bounds__(256) void bwd_rev_tree(BwdArgs a, int D) {
+  using EL = Elem<BF16>;
+  using E = typename EL::T;
+  const int DD = D * D;
+  const int nblk = (DD + 255) / 256;
+  const int64_t ng = a.n_groups;
+  const int64_t item = blockIdx.x / nblk;
+  const int64_t bh = item / (ng - 1), x = 1 + item % (ng - 1);
+  const int elem = (int)(blockIdx.x % nblk) * 256 + threadIdx.x;
+  if (elem >= DD) return;
+  const int i = __builtin_ctzll((unsigned long long)x);     // block of 2^i groups, group level i + 1
+  const int64_t end = x + (1ll << i) < ng ? x + (1ll << i) : ng;
+  const double* gp = a.gprefix + bh * (ng + 1);
+  const double base = gp[x];
+  float acc = 0.f;
+  for (int64_t g = x; g < end; ++g)
+    acc += __builtin_amdgcn_exp2f((float)(gp[g] - base)) * a.rpart[((bh * ng + g) * a.JG + i) * DD + elem];
+  reinterpret_cast<E*>(a.rnodes)[(bh * ng + x) * DD + elem] = EL::from_f32(acc);
+}
+
+// ---------------------------------------------------------------------------
+// bwd_chunk_dkv: one workgroup per (b,h, chunk); wave w owns key rows
+// 16 w .. 16 w + 15.  Writes dk, dv and the column terms v_s . dv_s.
+template <bool BF16, int C, int D>
+__global__ __launch_bounds__(64 * bwd_waves(C)) void bwd_chunk_dkv(BwdArgs a) {
+  using SH = BwdShape<BF16, C, D>;
+  using EL = Elem<BF16>;
+  using E = typename EL::T;
+  using Frag = typename EL::Frag;
+  constexpr int DB = SH::DB, KSD = SH::KSD, KPL = EL::kPerLane, KST = EL::kStep, LOG2C = SH::LOG2C;
+  constexpr int G = state_group(D), LOG2G = cilog2(G);
+  constexpr int EPV = SH::EPV, VPR = SH::VPR;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int L = a.L;
+  const BwdChunkLds lay = bwd_chunk_lds(C, D, sizeof(E), L, true);
+  const E* Qs = reinterpret_cast<const E*>(smem + lay.q);
+  const E* Ks = reinterpret_cast<const E*>(smem + lay.k);
+  const E* Vs = reinterpret_cast<const E*>(smem + lay.v);
+  const E* Gs = reinterpret_cast<const E*>(smem + lay.g);
+  E* PT = reinterpret_cast<E*>(smem + lay.s0);
+  E* DST = reinterpret_cast<E*>(smem + lay.s1);
+  E* Rs = reinterpret_cast<E*>(smem + lay.nd);
+  const float* lamS = reinterpret_cast<const float*>(smem + lay.lam);
+  float* b2c = reinterpret_cast<float*>(smem + lay.b2);
+  float* e2c = reinterpret_cast<float*>(smem + lay.e2);
+
+  const int64_t nc = a.n_chunks, ng = a.n_groups, T = a.T;
+  const int64_t item = xcd_item(blockIdx.x, gridDim.x);
+  const int64_t bh = item / nc, c = item % nc;
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id(), lq = lane >> 4, lr = lane & 15;
+  const int64_t tc = c * C;
+  const int nv = (int)(T - tc < C ? T - tc : C);
+
+  bwd_load_chunk<BF16, C, D>(a, smem, lay, bh, tc, nv);
+  if (w == 0) {
+    // in-chunk prefix of log2(a), and the gate from each key to the chunk end
+    const float x = (lane < C && tc + lane < T) ? a.log_a[bh * T + tc + lane] * kLog2e : 0.f;
+    const float y = wave_incl_scan(x);
+    const float tot = __shfl(y, C - 1, 64);
+    if (lane < C) {
+      b2c[lane] = y;
+      e2c[lane] = __builtin_amdgcn_exp2f(tot - y);
+    }
+  }
+
+  // levels whose upper block lies above the chunk: lanes 1..LOG2G, chunk
+  // level j inside the group (bit j-1 of the in-group index clear); lanes
+  // 32..62, group level i (bit i-1 of the group index clear)
+  const int64_t gam = c / G, cg0 = gam * G;
+  const int ci = (int)(c - cg0);
+  bool act = false;
+  int64_t off = 0;
+  int dst_x = 0;
+  int64_t xg = 0;
+  if (lane >= 1 && lane <= LOG2G) {
+    const int j = lane;
+    if (!((ci >> (j - 1)) & 1)) {
+      const int x = ((ci >> j) << j) + (1 << (j - 1));
+      if (cg0 + x < nc) {
+        act = true;
+        off = (bh * nc + cg0 + x) * D * D;
+        dst_x = x;
+      }
+    }
+  }
+  if (lane >= 32 && lane < 63) {
+    const int i = lane - 31;
+    if (!((gam >> (i - 1)) & 1)) {
+      xg = ((gam >> i) << i) + (1ll << (i - 1));
+      if (xg < ng) {
+        act = true;
+        off = (bh * ng + xg) * D * D;
+      }
+    }
+  }
+  const unsigned long long lmask = __ballot(act);
+  const int n_lev = __popcll(lmask);
+  const int pos = __popcll(lmask & ((1ull << lane) - 1ull));
+  const int ent = __builtin_amdgcn_ds_permute((act ? pos : 63) << 2, lane);
+  float g2 = 0.f;                               // log2 gate from the chunk end to the block start
+  if (nc > 1) {
+    const float gx = (lane < G && cg0 + lane < nc) ? a.gch[bh * nc + cg0 + lane] : 0.f;
+    const float incl = wave_incl_scan(gx);
+    float S = __shfl_up(incl, 1, 64);           // S(y): gates of the group's chunks before y
+    if (lane == 0) S = 0.f;
+    const float after = __shfl(S, ci + 1, 64);
+    const float at_x = __shfl(S, dst_x, 64);
+    const float at_end = __shfl(S, G, 64);
+    if (act) {
+      if (lane >= 32) {
+        const double* gp = a.gprefix + bh * (ng + 1);
+        g2 = (at_end - after) + (float)(gp[xg] - gp[gam + 1]);
+      } else {
+        g2 = at_x - after;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 1: transposed tiles of key block kb = w against query blocks
+  // qb >= kb (lane: key row, four queries): P^T = S * gate * lambda and
+  // dS^T = dP * gate * lambda
+  const int kb = w;
+  const int sk = 16 * kb + lr;
+  const float b2k = b2c[sk];
+  for (int qb = kb; qb < SH::QB; ++qb) {
+    f32x4 ss = f32x4{0.f, 0.f, 0.f, 0.f}, sd = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KSD; ++s) {
+      const int k0 = s * KST + lq * KPL;
+      const auto qf = EL::template load_k<D>(Qs + (16 * qb + lr) * lay.ld_row + k0, k0);
+      const auto kf = EL::template load_k<D>(Ks + sk * lay.ld_row + k0, k0);
+      ss = EL::mma(qf, kf, ss);
+      const auto gf = EL::template load_k<D>(Gs + (16 * qb + lr) * lay.ld_row + k0, k0);
+      const auto vf = EL::template load_k<D>(Vs + sk * lay.ld_row + k0, k0);
+      sd = EL::mma(gf, vf, sd);
+    }
+    const int t0 = 16 * qb + 4 * lq;
+    float pv[4], dv_[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + i;
+      int lv = fenwick_level_local((unsigned)t, (unsigned)sk);
+      lv = lv < L ? lv : L - 1;
+      const float W = __builtin_amdgcn_exp2f(b2c[t] - b2k) * lamS[t * L + lv];
+      const bool ok = sk <= t && t < nv;
+      pv[i] = ok ? ss[i] * W : 0.f;
+      dv_[i] = ok ? sd[i] * W : 0.f;
+    }
+    if constexpr (BF16) {
+      *reinterpret_cast<u16x4*>(PT + sk * lay.ld_s + t0) =
+          u16x4{f32_to_bf16(pv[0]), f32_to_bf16(pv[1]), f32_to_bf16(pv[2]), f32_to_bf16(pv[3])};
+      *reinterpret_cast<u16x4*>(DST + sk * lay.ld_s + t0) =
+          u16x4{f32_to_bf16(dv_[0]), f32_to_bf16(dv_[1]), f32_to_bf16(dv_[2]), f32_to_bf16(dv_[3])};
+    } else {
+      *reinterpret_cast<float4*>(PT + sk * lay.ld_s + t0) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+      *reinterpret_cast<float4*>(DST + sk * lay.ld_s + t0) = make_float4(dv_[0], dv_[1], dv_[2], dv_[3]);
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: dk^T = Q^T dS and dv^T = dout^T P over queries from the key
+  // block on (lane: key row, four consecutive columns)
+  f32x4 ak[DB], av[DB];
+#pragma unroll
+  for (int n = 0; n < DB; ++n) ak[n] = av[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < SH::KSC; ++s) {
+    if (s * KST + KST <= 16 * kb) continue;
+    const int k0 = s * KST + lq * KPL;
+    Frag df = zero_frag<BF16>(), pf = zero_frag<BF16>();
+    if (k0 < C && k0 / 16 >= kb) {
+      df = EL::load(DST + sk * lay.ld_s + k0);
+      pf = EL::load(PT + sk * lay.ld_s + k0);
+    }
+#pragma unroll
+    for (int n = 0; n < DB; ++n) {
+      const Frag qt = gather_col<BF16, C>(Qs, lay.ld_row, k0, 16 * n + lr);
+      ak[n] = EL::mma(qt, df, ak[n]);
+      const Frag gt = gather_col<BF16, C>(Gs, lay.ld_row, k0, 16 * n + lr);
+      av[n] = EL::mma(gt, pf, av[n]);
+    }
+  }
+  // ---- key-side nodes: dk += gate R v, dv += gate R^T k per level
+  Frag vfr[KSD], kfr[KSD];
+#pragma unroll
+  for (int s2 = 0; s2 < KSD; ++s2) {
+    const int k0 = s2 * KST + lq * KPL;
+    vfr[s2] = EL::template load_k<D>(Vs + sk * lay.ld_row + k0, k0);
+    kfr[s2] = EL::template load_k<D>(Ks + sk * lay.ld_row + k0, k0);
+  }
+  const float e2k = e2c[sk];
+  for (int li = 0; li < n_lev; ++li) {
+    const int el = __builtin_amdgcn_readlane(ent, li);
+    const uint64_t o64 = (uint64_t)off;
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)o64, el);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(o64 >> 32), el);
+    const int64_t o = (int64_t)(((uint64_t)hi << 32) | lo);
+    const E* node = (el >= 32 ? reinterpret_cast<const E*>(a.rnodes) : reinterpret_cast<const E*>(a.rnodes_in)) + o;
+    const float f = __builtin_amdgcn_exp2f(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g2), el)));
+    __syncthreads();                            // the previous node is no longer read
+    for (int idx = tid; idx < D * VPR; idx += SH::NT) {
+      const int r = idx / VPR, cv = idx % VPR;
+      *reinterpret_cast<uint4*>(Rs + r * lay.ld_nd + cv * EPV) = *reinterpret_cast<const uint4*>(node + r * D + cv * EPV);
+    }
+    __syncthreads();
+    const float wk = f * e2k;
+#pragma unroll
+    for (int n = 0; n < DB; ++n) {
+      f32x4 tk = f32x4{0.f, 0.f, 0.f, 0.f}, tv = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < KSD; ++s2) {
+        const int k0 = s2 * KST + lq * KPL;
+        const auto rf = EL::template load_k<D>(Rs + (16 * n + lr) * lay.ld_nd + k0, k0);   // R row d_k, k-slice d_v
+        tk = EL::mma(rf, vfr[s2], tk);
+        const Frag rt = gather_col<BF16, D>(Rs, lay.ld_nd, k0, 16 * n + lr);              // R^T row d_v, k-slice d_k
+        tv = EL::mma(rt, kfr[s2], tv);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ak[n][i] += wk * tk[i];
+        av[n][i] += wk * tv[i];
+      }
+    }
+  }
+  // column term v_s . dv_s, then the rows of dk and dv
+  float cs = 0.f;
+#pragma unroll
+  for (int n = 0; n < DB; ++n) {
+    const E* vrow = Vs + sk * lay.ld_row + 16 * n + 4 * lq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cs += av[n][i] * EL::to_f32(vrow[i]);
+  }
+  cs += __shfl_xor(cs, 16, 64);
+  cs += __shfl_xor(cs, 32, 64);
+  if (sk < nv) {
+    if (lq == 0) a.dcol[bh * T + tc + sk] = cs;
+    E* ok = reinterpret_cast<E*>(a.dk) + (bh * T + tc + sk) * D + 4 * lq;
+    E* ov = reinterpret_cast<E*>(a.dv) + (bh * T + tc + sk) * D + 4 * lq;
+#pragma unroll
+    for (int n = 0; n < DB; ++n) {
+      store4<BF16>(ok + 16 * n, ak[n]);
+      store4<BF16>(ov + 16 * n, av[n]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_gate_grad: one workgroup per (b,h).  dlog_a_r = sum_{u >= r} (row_u -
+// col_u), tiles of 1024 tokens from the end: float sums inside a tile, a
+// float64 carry across tiles.  (A template only so that every translation
+// unit including this header may instantiate it.)
+template <int TILE_THREADS>
+__global__ __launch_bounds__(TILE_THREADS) void bwd_gate_grad(BwdArgs a) {
+  static_assert(TILE_THREADS == 256, "one float per thread and four tokens each");
+  __shared__ float sh[256];
+  const int64_t bh = blockIdx.x, T = a.T;
+  const int tid = threadIdx.x;
+  float* dl = a.dlog_a + bh * T;
+  const float* dc = a.dcol + bh * T;
+  double carry = 0.0;
+  for (int64_t hi = T; hi > 0; hi -= 1024) {
+    const int64_t lo = hi - 1024 > 0 ? hi - 1024 : 0;
+    float x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = lo + 4 * tid + u;
+      x[u] = i < hi ? dl[i] - dc[i] : 0.f;
+    }
+    float sfx[4];
+    sfx[3] = x[3];
+    sfx[2] = x[2] + sfx[3];
+    sfx[1] = x[1] + sfx[2];
+    sfx[0] = x[0] + sfx[1];
+    sh[tid] = sfx[0];
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      const float y = tid + d < 256 ? sh[tid + d] : 0.f;
+      __syncthreads();
+      sh[tid] += y;
+      __syncthreads();
+    }
+    const float after = sh[tid] - sfx[0];      // tokens of later threads in the tile
+    const float tile = sh[0];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = lo + 4 * tid + u;
+      if (i < hi) dl[i] = (float)(carry + (double)(after + sfx[u]));
+    }
+    carry += (double)tile;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch for one (dtype, C, D) instantiation.  fa carries the
+// forward-structure buffers over (k := v, v := k).
+template <bool BF16, int C, int D>
+int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s) {
+  using E = typename Elem<BF16>::T;
+  const FwdPlan& p = P.f;
+  constexpr int G = state_group(D);
+  if (p.G != G) return kEHIP;
+  bool ok = true;
+  if (p.n_chunks > 1) {
+    constexpr int lds_s = state_lds(C, D, sizeof(E), G).total;
+    ok = ok && hipFuncSetAttribute((const void*)fwd_chunk_states<BF16, C, D>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds_s) == hipSuccess;
+    if (!ok) return kEHIP;
+    hipLaunchKernelGGL((fwd_chunk_states<BF16, C, D>), dim3((unsigned)(p.n_groups * p.BH)),
+                       dim3(StateShape<BF16, C, D>::NT), lds_s, s, fa);
+    ok = ok && hipGetLastError() == hipSuccess;
+  }
+  if (p.n_groups > 1) {
+    const dim3 grid((unsigned)(((D * D + 255) / 256) * p.BH));
+    const int levels = bit_length(p.n_groups);
+    if (levels <= 8)
+      hipLaunchKernelGGL((fwd_group_tree<BF16, 8>), grid, dim3(256), 0, s, fa, D);
+    else if (levels <= 16)
+      hipLaunchKernelGGL((fwd_group_tree<BF16, 16>), grid, dim3(256), 0, s, fa, D);
+    else
+      hipLaunchKernelGGL((fwd_group_tree<BF16, 32>), grid, dim3(256), 0, s, fa, D);
+    ok = ok && hipGetLastError() == hipSuccess;
+  }
+  ok = ok && hipFuncSetAttribute((const void*)bwd_chunk_dq<BF16, C, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 P.lds_dq) == hipSuccess;
+  if (!ok) return kEHIP;
+  hipLaunchKernelGGL((bwd_chunk_dq<BF16, C, D>), dim3((unsigned)(p.n_chunks * p.BH)), dim3(64 * bwd_waves(C)),
+                     P.lds_dq, s, a);
+  ok = ok && hipGetLastError() == hipSuccess;
+  if (p.n_chunks > 1) {
+    ok = ok && hipFuncSetAttribute((const void*)bwd_rev_states<BF16, C, D>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, P.lds_rev) == hipSuccess;
+    if (!ok) return kEHIP;
+    hipLaunchKernelGGL((bwd_rev_states<BF16, C, D>), dim3((unsigned)(p.n_groups * p.BH)),
+                       dim3(64 * state_waves(D)), P.lds_rev, s, a);
+    ok = ok && hipGetLastError() == hipSuccess;
+  }
+  if (p.n_groups > 1) {
+    const int nblk = (D * D + 255) / 256;
+    hipLaunchKernelGGL((bwd_rev_tree<BF16>), dim3((unsigned)(p.BH * (p.n_groups - 1) * nblk)), dim3(256), 0, s, a, D);
+    ok = ok && hipGetLastError() == hipSuccess;
+  }
+  ok = ok && hipFuncSetAttribute((const void*)bwd_chunk_dkv<BF16, C, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 P.lds_dkv) == hipSuccess;
+  if (!ok) return kEHIP;
+  hipLaunchKernelGGL((bwd_chunk_dkv<BF16, C, D>), dim3((unsigned)(p.n_chunks * p.BH)), dim3(64 * bwd_waves(C)),
+                     P.lds_dkv, s, a);
+  ok = ok && hipGetLastError() == hipSuccess;
+  hipLaunchKernelGGL((bwd_gate_grad<256>), dim3((unsigned)p.BH), dim3(256), 0, s, a);
+  ok = ok && hipGetLastError() == hipSuccess;
+  return ok ? kOK : kEHIP;
+}
+
+template <bool BF16>
+int launch_bwd_dtype(const BwdPlan& P, const FwdArgs& fa, const BwdArgs& a, hipStream_t s) {
+#define LA_CASE(CC, DD) \
+  if (P.f.C == CC && P.f.D == DD) return launch_bwd_impl<BF16, CC, DD>(P, fa, a, s);
+  LA_CASE(16, 16) LA_CASE(16, 32) LA_CASE(16, 64) LA_CASE(16, 128)
+  LA_CASE(32, 16) LA_CASE(32, 32) LA_CASE(32, 64) LA_CASE(32, 128)
+  LA_CASE(64, 16) LA_CASE(64, 32) LA_CASE(64, 64) LA_CASE(64, 128)
+#undef LA_CASE
+  return kESHAPE;
+}
+
+}  // namespace la

@@ -1,0 +1,108 @@
+// Host-side plan of the backward pass: shape checks, the workspace carve-up
+// and the LDS carve-up of the backward kernels.  Pure C++17 like la_plan.hpp,
+// which it extends; the kernels include it so that LDS offsets are defined
+// once.
+#pragma once
+
+#include "la_plan.hpp"
+
+namespace la {
+
+// bwd_chunk_dq and bwd_chunk_dkv: one workgroup per (b,h, chunk), one wave per
+// 16-row block of the chunk.
+LA_HD constexpr int bwd_waves(int C) { return C / 16; }
+
+// LDS of the two per-chunk kernels.  Q, K, V and dout tiles are row-major with
+// rows padded by 16 bytes; the score-gradient tiles hold C x C entries
+// (bwd_chunk_dq: dS by query row; bwd_chunk_dkv: P^T and dS^T by key row);
+// lam holds the chunk's lambda rows, dl the lambda gradients being formed,
+// nd one reverse node (bwd_chunk_dkv), b2/e2 gate prefixes.
+struct BwdChunkLds {
+  int q, k, v, g, s0, s1, lam, dl, nd, b2, e2, total, ld_row, ld_s, ld_nd;
+};
+LA_HD constexpr BwdChunkLds bwd_chunk_lds(int C, int D, int es, int L, bool key_side) {
+  BwdChunkLds o{};
+  o.ld_row = D + 16 / es;
+  o.ld_s = C + 16 / es;
+  o.ld_nd = D + 16 / es;
+  const int tile = (C * o.ld_row * es + 255) / 256 * 256;
+  const int stile = (C * o.ld_s * es + 255) / 256 * 256;
+  int off = 0;
+  o.q = off;  off += tile;
+  o.k = off;  off += tile;
+  o.v = off;  off += tile;
+  o.g = off;  off += tile;
+  o.s0 = off; off += stile;
+  o.s1 = off; off += key_side ? stile : 0;
+  o.lam = off; off += (C * L * 4 + 255) / 256 * 256;
+  o.dl = off;  off += key_side ? 0 : (C * L * 4 + 255) / 256 * 256;
+  o.nd = off;  off += key_side ? (D * o.ld_nd * es + 255) / 256 * 256 : 0;
+  o.b2 = off;  off += (C * 4 + 255) / 256 * 256;
+  o.e2 = off;  off += (C * 4 + 255) / 256 * 256;
+  o.total = off;
+  return o;
+}
+
+// bwd_rev_states: one workgroup per (b,h, group of G chunks), the state
+// kernel's wave count; gated Q^T and dout^T of one chunk, the group's gate
+// prefixes and the chunk's token weights.
+struct RevLds {
+  int qt, gt, b2, w, total, ld_t;
+};
+LA_HD constexpr RevLds rev_lds(int C, int D, int es, int G) {
+  RevLds o{};
+  o.ld_t = C + 16 / es;
+  const int tile = (D * o.ld_t * es + 255) / 256 * 256;
+  int off = 0;
+  o.qt = off; off += tile;
+  o.gt = off; off += tile;
+  o.b2 = off; off += (G * C * 4 + 255) / 256 * 256;
+  o.w = off;  off += (C * 4 + 255) / 256 * 256;
+  o.total = off;
+  return o;
+}
+
+struct BwdPlan {
+  FwdPlan f;                 // the forward structure over (k := v, v := k): nodes for dq
+  int JG = 0;                // group levels that have an upper block (bit length of n_groups - 1)
+  int lds_dq = 0, lds_dkv = 0, lds_rev = 0;
+  size_t off_rnodes_in = 0, off_rpart = 0, off_rnodes = 0, off_dcol = 0, ws_bytes = 0;
+};
+
+// Shape checks and the plan of the backward.  The forward's envelope, with
+// chunks of at most 64 tokens; shapes whose tiles exceed the LDS are
+// rejected.  L < 0 skips the level check (workspace query).
+inline int plan_bwd(int B, int H, int64_t T, int dk, int dv, int C, int dtype, int L, BwdPlan* p) {
+  if (!p) return kEINVAL;
+  BwdPlan P;
+  int rc = plan_fwd(B, H, T, dk, dv, C, dtype, L, &P.f);
+  if (rc != kOK) return rc;
+  if (C > 64) return kESHAPE;
+  const FwdPlan& f = P.f;
+  P.lds_dq = bwd_chunk_lds(C, dk, f.es, f.L, false).total;
+  P.lds_dkv = bwd_chunk_lds(C, dk, f.es, f.L, true).total;
+  P.lds_rev = rev_lds(C, dk, f.es, f.G).total;
+  if (bwd_chunk_lds(C, dk, f.es, kMaxLevels, false).total > kLdsLimit ||
+      bwd_chunk_lds(C, dk, f.es, kMaxLevels, true).total > kLdsLimit || P.lds_rev > kLdsLimit)
+    return kESHAPE;
+  if (f.BH == 0 || T == 0) {
+    *p = P;
+    return kOK;
+  }
+  P.JG = f.n_groups > 1 ? bit_length(f.n_groups - 1) : 0;
+  const size_t DD = (size_t)dk * dv;
+  size_t off = f.ws_bytes;
+  if (f.n_chunks > 1) {
+    P.off_rnodes_in = off; off = align_up(off + (size_t)f.BH * f.n_chunks * DD * f.es, 256);
+  }
+  if (f.n_groups > 1) {
+    P.off_rpart = off;  off = align_up(off + (size_t)f.BH * f.n_groups * P.JG * DD * 4, 256);
+    P.off_rnodes = off; off = align_up(off + (size_t)f.BH * f.n_groups * DD * f.es, 256);
+  }
+  P.off_dcol = off; off = align_up(off + (size_t)f.BH * T * 4, 256);
+  P.ws_bytes = off;
+  *p = P;
+  return kOK;
+}
+
+}  // namespace la

@@ -5,16 +5,23 @@
 #include <stdint.h>
 
 #include "../../include/logattn.h"
+#include "la_bwd_plan.hpp"
 #include "la_plan.hpp"
 
 namespace la {
 
 struct FwdArgs;
+struct BwdArgs;
 
 // Forward: enqueue the stages of `p` on stream s; ev (nullable) holds
 // p.n_stages + 1 events recorded around the stages.
 int launch_fwd_bf16(const FwdPlan& p, const FwdArgs& a, hipStream_t s, hipEvent_t const* ev);
 int launch_fwd_f32(const FwdPlan& p, const FwdArgs& a, hipStream_t s, hipEvent_t const* ev);
+
+// Backward: enqueue its kernels on stream s.  fa carries the forward-structure
+// buffers over (k := v, v := k).
+int launch_bwd_bf16(const BwdPlan& p, const FwdArgs& fa, const BwdArgs& a, hipStream_t s);
+int launch_bwd_f32(const BwdPlan& p, const FwdArgs& fa, const BwdArgs& a, hipStream_t s);
 
 int launch_decode(const la_state* st, const void* q, const void* k, const void* v, const float* a,
                   const float* lam, void* out, int dtype, int kstar, hipStream_t s);

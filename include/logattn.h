@@ -209,6 +209,50 @@ LA_API int loglinear_fwd_state(const void* q, const void* k, const void* v, cons
                                int C, int L, int dtype, void* workspace, size_t workspace_bytes,
                                la_state* state, la_stream_t stream);
 
+/* Workspace size for loglinear_bwd (host only); errors as loglinear_bwd. */
+LA_API int loglinear_bwd_workspace(int B, int H, int64_t T, int dk, int dv, int C, int dtype,
+                                   size_t* bytes);
+
+/*
+ * Backward of loglinear_fwd: the gradients of a loss L with respect to q, k,
+ * v, log_a and lambda, given dout = dL/dout.  Training needs them, the level
+ * weights' included ("Log-Linear Attention", Spanish summary, section 5
+ * "Limitaciones", first item: custom kernels for the hierarchical structure
+ * and for the gradients of lambda).  With A[t,s] = lambda[t, l(t,s)] M^S[t,s]:
+ *   grad_q[t]  = sum_{s<=t} A[t,s] (dout_t . v_s) k_s
+ *   grad_k[s]  = sum_{t>=s} A[t,s] (dout_t . v_s) q_t
+ *   grad_v[s]  = sum_{t>=s} A[t,s] (q_t . k_s) dout_t
+ *   grad_lambda[t, l] = sum over the keys s of bucket l of t of
+ *                       M^S[t,s] (q_t . k_s)(dout_t . v_s); 0 for empty
+ *                       buckets and for levels l >= ceil(log2 T) + 1
+ *   grad_log_a[r] = sum_{u>=r} (dout_u . o_u - v_u . grad_v[u])
+ * (the gate of token 0 multiplies nothing, so grad_log_a[0] is 0 up to
+ * rounding).  Computed chunkwise like the forward, without the forward's
+ * output: dout_u . o_u = sum_l lambda[u, l] grad_lambda[u, l].
+ *
+ *   q, k, v, log_a, lambda  as for loglinear_fwd (inputs, not written)
+ *   dout         [B, H, T, dv]  dtype     16-byte aligned
+ *   grad_q       [B, H, T, dk]  dtype     written, 16-byte aligned
+ *   grad_k       [B, H, T, dk]  dtype     written, 16-byte aligned
+ *   grad_v       [B, H, T, dv]  dtype     written, 16-byte aligned
+ *   grad_log_a   [B, H, T]      float32   written
+ *   grad_lambda  [B, H, T, L]   float32   written (every entry)
+ * The outputs must not overlap the inputs or each other.
+ *
+ * Supported: the shapes loglinear_fwd accepts with C in {16, 32, 64} whose
+ * tiles fit the 160 KB of LDS (every bfloat16 shape; float32 with
+ * dk = 128 needs C <= 32); others return LA_ESHAPE, and
+ * loglinear_bwd_workspace answers the same.  The chunk size only changes the
+ * summation order, so a backward may use another C than its forward.
+ * workspace: at least loglinear_bwd_workspace() bytes, 256-byte aligned.
+ * Errors as loglinear_fwd.
+ */
+LA_API int loglinear_bwd(const void* q, const void* k, const void* v, const float* log_a,
+                         const float* lambda, const void* dout, void* grad_q, void* grad_k,
+                         void* grad_v, float* grad_log_a, float* grad_lambda, int B, int H, int64_t T,
+                         int dk, int dv, int C, int L, int dtype, void* workspace,
+                         size_t workspace_bytes, la_stream_t stream);
+
 /*
  * Fenwick level table for checking: out[t * T + s] = l(t, s) for s <= t and
  * -1 for s > t, as int8, computed on the device by the same level function

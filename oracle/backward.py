@@ -22,6 +22,9 @@ where Lambda is the inclusive cumulative sum of log_a, so that
 M^S[t,s] = exp(Lambda_t - Lambda_s) moves with Lambda_t (+) and Lambda_s (-).
 Levels with no key (empty buckets) get a zero lambda gradient.
 
+``backward_sampled`` evaluates the same sums at chosen query and key rows only
+(long sequences); it is pinned to ``backward_quadratic``.
+
 Pins (tests/test_oracle_backward.py): every entry of every gradient against
 central finite differences of the forward oracle (both of its forms) on tiny
 inputs; homogeneity identities (o_t is linear in q_t and in the lambda row of
@@ -82,6 +85,44 @@ def backward_quadratic(q, k, v, log_a, lam, dout, block=1024):
             dlam_u = row_term - col_term
             dlog_a[b, h] = np.cumsum(dlam_u[::-1])[::-1]
     return dq, dk, dv, dlog_a, dlam
+
+
+def backward_sampled(q, k, v, log_a, lam, dout, rows):
+    """The same gradients at sampled positions, for long sequences: dq and
+    dlam at query rows ``rows`` (their row of the pair matrix) and dk and dv
+    at key rows ``rows`` (their column: every query t >= s).  Returns a dict
+    of [B, H, len(rows), ...] arrays.  The gate of a pair is
+    exp(Lambda_t - Lambda_s) with Lambda the inclusive float64 cumulative sum
+    of log_a, as in ``forms.decay_matrix``; the level is ``levels.level``.
+    """
+    q, k, v, log_a, lam, dout = (_f64(x) for x in (q, k, v, log_a, lam, dout))
+    B, H, T, _ = q.shape
+    L = lam.shape[-1]
+    rows = np.asarray(rows, dtype=np.int64)
+    R = len(rows)
+    res = {"dq": np.zeros((B, H, R, q.shape[-1])), "dlam": np.zeros((B, H, R, L)),
+           "dk": np.zeros((B, H, R, k.shape[-1])), "dv": np.zeros((B, H, R, v.shape[-1]))}
+    for b in range(B):
+        for h in range(H):
+            S = q[b, h, rows] @ k[b, h].T
+            dP = dout[b, h, rows] @ v[b, h].T
+            ms = decay_matrix(log_a[b, h], rows=rows)
+            lev = _levels.level_table(T, rows=rows).astype(np.int64)
+            causal = lev >= 0
+            mh = np.take_along_axis(lam[b, h, rows], np.where(causal, lev, 0), axis=1)
+            A = np.where(causal, ms * mh, 0.0)
+            res["dq"][b, h] = (A * dP) @ k[b, h]
+            E = np.where(causal, ms * S * dP, 0.0)
+            for lv in range(L):
+                res["dlam"][b, h, :, lv] = np.where(lev == lv, E, 0.0).sum(axis=1)
+            cum = np.cumsum(log_a[b, h])
+            for i, s in enumerate(rows):
+                t = np.arange(s, T)
+                lv = np.array([_levels.level(int(u), int(s)) for u in t], dtype=np.int64)
+                a_ts = lam[b, h, t, lv] * np.exp(cum[t] - cum[s])
+                res["dk"][b, h, i] = (a_ts * (dout[b, h, t] @ v[b, h, s])) @ q[b, h, t]
+                res["dv"][b, h, i] = (a_ts * (q[b, h, t] @ k[b, h, s])) @ dout[b, h, t]
+    return res
 
 
 def loss(out, dout) -> float:

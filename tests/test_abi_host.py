@@ -194,3 +194,53 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 16, 16)
     with pytest.raises(ValueError):
         la.loglinear_fwd(x, x, x, torch.zeros(1, 1, 16), torch.zeros(1, 1, 16, 5))
+
+
+def bws(B, H, T, d, C, dt=1):
+    n = ctypes.c_size_t(0)
+    rc = L.loglinear_bwd_workspace(B, H, T, d, d, C, dt, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_bwd_workspace_query():
+    rc, n = bws(8, 16, 16384, 64, 64)
+    assert rc == OK
+    fwd_part = ws(8, 16, 16384, 64, 64)[1]
+    # forward structure, key-side chunk nodes (bf16), group shares (fp32,
+    # 5 group levels for 32 groups) and group nodes, column terms
+    BH, nch, ng, DD = 128, 256, 32, 64 * 64
+    need = fwd_part + BH * nch * DD * 2 + BH * ng * 5 * DD * 4 + BH * ng * DD * 2 + BH * 16384 * 4
+    assert need <= n < need * 1.01
+    assert bws(2, 3, 50, 64, 64)[1] == 1280              # one partial chunk: 2*3*50 column terms, 256-aligned
+    assert bws(1, 1, 64, 64, 128)[0] == ESHAPE              # chunks above 64
+    assert bws(1, 1, 1000, 128, 64, 0)[0] == ESHAPE         # float32 tiles of 64 x 128 exceed the LDS
+    assert bws(1, 1, 1000, 128, 32, 0)[0] == OK
+    for d in (16, 32, 64, 128):
+        for C in (16, 32, 64):
+            assert bws(1, 1, 1000, d, C, 1)[0] == OK, (d, C)
+    assert bws(0, 4, 100, 64, 64)[1] == 0
+    assert L.loglinear_bwd_workspace(1, 1, 64, 64, 64, 64, 1, None) == EINVAL
+
+
+def bwd(B=1, H=1, T=64, d=16, C=16, Lv=7, dt=0, w=A, wb=1 << 30, **kw):
+    p = {n: kw.get(n, A) for n in ("q", "k", "v", "la", "lam", "g", "gq", "gk", "gv", "gla", "glam")}
+    return L.loglinear_bwd(p["q"], p["k"], p["v"], p["la"], p["lam"], p["g"], p["gq"], p["gk"], p["gv"], p["gla"],
+                           p["glam"], B, H, T, d, d, C, Lv, dt, w, wb, None)
+
+
+def test_bwd_validation_codes():
+    assert bwd(g=None) == EINVAL
+    assert bwd(glam=None) == EINVAL
+    assert bwd(gq=A + 8) == EALIGN
+    assert bwd(g=A + 8) == EALIGN
+    assert bwd(gla=A + 2) == EALIGN
+    assert bwd(dt=4) == EDTYPE
+    assert bwd(Lv=6) == ESHAPE
+    assert bwd(C=128) == ESHAPE
+    assert bwd(w=None) == EWS
+    assert bwd(wb=16) == EWS
+    assert bwd(w=A + 16) == EALIGN
+    assert bwd(q=None, k=None, v=None, la=None, lam=None, g=None, gq=None, gk=None, gv=None, gla=None, glam=None,
+               B=0) == OK
+    assert bwd(q=None, k=None, v=None, la=None, lam=None, g=None, gq=None, gk=None, gv=None, gla=None, glam=None,
+               T=0, Lv=0) == OK

@@ -1,0 +1,185 @@
+"""Backward parity: the HIP gradients against the float64 oracle (GPU).
+
+Bars (relative L2 over each gradient tensor): 1e-4 for float32 inputs, 2e-2
+for bfloat16 inputs, for dq, dk, dv and dlambda.  The gate gradient is a
+reverse cumulative sum of differences of two terms that cancel over the
+whole sequence (its first entry is exactly zero), so it is held to the same
+bar relative to the reverse cumulative sum of the magnitudes of those terms,
+which sets the scale its rounding errors follow.  As for the forward, every
+shape class also runs with weak or no decay and with lambda one-hot on
+single levels, so that distant levels carry the gradients.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from fenwick_tree_hierarchical_amd.workloads import WORKLOADS, make_grad_out, make_inputs
+from oracle import backward, forms
+from tests.helpers import TOL, heads, need_gpu, rel_l2, say, to_cpu
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dlog_a", "dlam")
+
+
+def gpu_bwd(x, dout, C, dev):
+    import fenwick_tree_hierarchical_amd as la
+    xd = {k: v.to(dev) for k, v in x.items()}
+    g = la.loglinear_bwd(xd["q"], xd["k"], xd["v"], xd["log_a"], xd["lam"], dout.to(dev), chunk=C)
+    torch.cuda.synchronize()
+    return {n: t.float().cpu().numpy() for n, t in zip(NAMES, g)}
+
+
+def gate_scale(x, dout, ref):
+    """Reverse cumulative sum of |dout_u . o_u| + |v_u . dv_u|: the size of
+    the terms whose differences the gate gradient adds up."""
+    o = forms.forward_quadratic(x["q"], x["k"], x["v"], x["log_a"], x["lam"])
+    row = np.abs(np.sum(dout.double().numpy() * o, axis=-1))
+    col = np.abs(np.sum(x["v"].double().numpy() * ref["dv"], axis=-1))
+    return np.cumsum((row + col)[..., ::-1], axis=-1)[..., ::-1]
+
+
+def check(x, dout, C, dtype, dev, label):
+    say(f"bwd {label}: shape={tuple(x['q'].shape)} C={C} dtype={dtype}")
+    got = gpu_bwd(x, dout, C, dev)
+    r = backward.backward_quadratic(x["q"], x["k"], x["v"], x["log_a"], x["lam"], dout)
+    ref = dict(zip(NAMES, r))
+    errs = {}
+    for n in ("dq", "dk", "dv", "dlam"):
+        assert np.all(np.isfinite(got[n])), n
+        errs[n] = rel_l2(got[n], ref[n])
+    scale = gate_scale(x, dout, ref)
+    errs["dlog_a"] = float(np.linalg.norm(got["dlog_a"] - ref["dlog_a"]) / max(np.linalg.norm(scale), 1e-300))
+    say("   " + "  ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= TOL[dtype], f"{label}: {n} error {e:.3e} > {TOL[dtype]}"
+    # levels with an empty bucket get exactly zero
+    T, L = x["lam"].shape[2], x["lam"].shape[3]
+    t = np.arange(T)
+    for lv in range(1, L):
+        empty = ((t >> (lv - 1)) & 1) == 0
+        assert np.all(got["dlam"][:, :, empty, lv] == 0.0), lv
+    return errs
+
+
+def case(T, d, dtype, variant=None, B=1, H=2, seed=0):
+    x = make_inputs(WORKLOADS["small_bf16"], B=B, H=H, T=T, d=d, dtype=dtype, variant=variant, seed=seed)
+    dout = make_grad_out(WORKLOADS["small_bf16"], B=B, H=H, T=T, d=d, dtype=dtype, seed=seed)
+    return x, dout
+
+
+def test_tiny_f32_workload():
+    dev = need_gpu()
+    w = WORKLOADS["tiny_f32"]
+    x = make_inputs(w)
+    check(x, make_grad_out(w), w.C, "f32", dev, "tiny_f32")
+
+
+@pytest.mark.parametrize("variant", [None, "weak_decay", "no_decay"])
+def test_small_bf16_shape(variant):
+    dev = need_gpu()
+    x, dout = case(2048, 64, "bf16", variant, B=1, H=4, seed=1)
+    check(x, dout, 64, "bf16", dev, f"small_bf16 shape {variant}")
+
+
+SHAPES = [(16, 16), (32, 32), (64, 64), (64, 16), (16, 64), (32, 64), (128, 32), (128, 64), (64, 32), (128, 16)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d,C", SHAPES)
+def test_shapes_weak_decay_ragged(d, C, dtype):
+    """Several full groups, a partial group and a ragged last chunk."""
+    dev = need_gpu()
+    if dtype == "f32" and d == 128 and C == 64:
+        pytest.skip("float32 tiles of 64 x 128 exceed LDS in the backward (rejected with LA_ESHAPE)")
+    T = 21 * C + 5
+    x, dout = case(T, d, dtype, "weak_decay", seed=100 + d + C)
+    check(x, dout, C, dtype, dev, f"d={d} C={C} T={T} weak_decay")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("lev", list(range(12)))
+def test_onehot_level_sweep(lev, dtype):
+    """lambda one-hot on level `lev` of T = 2048 with C = 64: levels 0..6 inside
+    a chunk, 7..9 chunk levels inside a group, 10..11 group levels."""
+    dev = need_gpu()
+    x, dout = case(2048, 64, dtype, f"weak_decay+onehot:{lev}", seed=300 + lev)
+    check(x, dout, 64, dtype, dev, f"onehot level {lev}")
+
+
+@pytest.mark.parametrize("T,C", [(1, 16), (2, 16), (15, 16), (17, 16), (100, 64), (1000, 64), (129, 32),
+                                 (64 * 8 * 4, 64), (64 * 8 * 4 + 64, 64)])
+def test_short_ragged_and_power_of_two(T, C):
+    dev = need_gpu()
+    x, dout = case(T, 32, "f32", "weak_decay", B=2, H=3, seed=T)
+    check(x, dout, C, "f32", dev, f"T={T} C={C}")
+
+
+def test_chunk_size_invariance_f32():
+    dev = need_gpu()
+    x, dout = case(1500, 32, "f32", "weak_decay", seed=5)
+    outs = {C: gpu_bwd(x, dout, C, dev) for C in (16, 32, 64)}
+    for C in (32, 64):
+        for n in NAMES:
+            assert rel_l2(outs[C][n], outs[16][n]) <= 2 * TOL["f32"], (C, n)
+
+
+def test_empty_problems():
+    dev = need_gpu()
+    import fenwick_tree_hierarchical_amd as la
+    for B, T in [(0, 64), (1, 0)]:
+        x, dout = case(T, 64, "bf16", B=B, H=2)
+        xd = {k: v.to(dev) for k, v in x.items()}
+        g = la.loglinear_bwd(xd["q"], xd["k"], xd["v"], xd["log_a"], xd["lam"], dout.to(dev), chunk=64)
+        assert g[0].shape == (B, 2, T, 64) and g[4].shape == x["lam"].shape
+
+
+def test_deterministic():
+    dev = need_gpu()
+    x, dout = case(1000, 64, "bf16", "weak_decay", seed=3)
+    a = gpu_bwd(x, dout, 64, dev)
+    b = gpu_bwd(x, dout, 64, dev)
+    for n in NAMES:
+        assert np.array_equal(a[n], b[n]), n
+
+
+# --------------------------------------------------------------- full size
+def test_train_16k_full_size_sampled():
+    """All 128 heads of the training shape: the gradients at sampled query and
+    key rows of three heads against the oracle; on every head, the
+    homogeneity identities q_t . dq_t = sum_l lambda dlambda = dout_t . o_t
+    against the GPU forward, and a first-gate gradient that is zero up to
+    rounding."""
+    dev = need_gpu()
+    import fenwick_tree_hierarchical_amd as la
+    w = WORKLOADS["train_16k_bf16"]
+    say("bwd full size train_16k_bf16: drawing inputs")
+    x = make_inputs(w, device=dev, variant="weak_decay")
+    dout = make_grad_out(w, device=dev)
+    say("bwd full size train_16k_bf16: backward")
+    dq, dk, dv, dla, dlam = la.loglinear_bwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], dout, chunk=w.C)
+    out = la.loglinear_fwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], chunk=w.C)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv, dla, dlam):
+        assert torch.isfinite(t.float()).all().item()
+    row = (dout.float() * out.float()).sum(-1)
+    assert rel_l2((x["q"].float() * dq.float()).sum(-1).cpu().numpy(), row.cpu().numpy()) <= TOL["bf16"]
+    assert rel_l2((x["lam"] * dlam).sum(-1).cpu().numpy(), row.cpu().numpy()) <= TOL["bf16"]
+    # the first gate's gradient sums row - column terms over the whole
+    # sequence and is zero up to rounding: bounded relative to the sum of
+    # their magnitudes, the scale its rounding follows
+    col = (x["v"].float() * dv.float()).sum(-1)
+    scale = (row.abs() + col.abs()).sum(-1)
+    assert bool((dla[..., 0].abs() <= TOL["bf16"] * scale).all())
+    rows = np.array([0, 1, 63, 64, 511, 512, 4095, 4096, 8191, 8192, 12000, 16320, 16383])
+    idx = [(0, 0), (5, 9), (7, 15)]
+    sub = to_cpu(heads(x, idx))
+    dsub = torch.stack([dout[b, h] for b, h in idx])[None].cpu()
+    say("bwd full size train_16k_bf16: oracle at sampled rows")
+    ref = backward.backward_sampled(sub["q"], sub["k"], sub["v"], sub["log_a"], sub["lam"], dsub, rows)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dlam", dlam)):
+        got = torch.stack([t[b, h, rows] for b, h in idx])[None].float().cpu().numpy()
+        err = rel_l2(got, ref[name])
+        say(f"   {name} rel_l2={err:.3e}")
+        assert err <= TOL["bf16"], name

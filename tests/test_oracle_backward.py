@@ -145,3 +145,12 @@ def test_row_blocks_do_not_change_the_result():
     b = backward.backward_quadratic(x["q"], x["k"], x["v"], x["log_a"], x["lam"], x["dout"], block=16)
     for u, w in zip(a, b):
         assert np.allclose(u, w, rtol=1e-12, atol=1e-13)
+
+
+def test_sampled_rows_equal_the_full_gradients():
+    x = _inp(300, H=2, d=4, seed=12)
+    g = _grads(x)
+    rows = np.array([0, 1, 5, 63, 64, 128, 200, 255, 298, 299])
+    smp = backward.backward_sampled(x["q"], x["k"], x["v"], x["log_a"], x["lam"], x["dout"], rows)
+    for name, full in (("dq", g["q"]), ("dk", g["k"]), ("dv", g["v"]), ("dlam", g["lam"])):
+        assert np.allclose(smp[name], full[:, :, rows], rtol=1e-11, atol=1e-13), name
