@@ -1,6 +1,6 @@
 """Benchmark of log-linear Mamba-2 attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-backward]
 
 One step is one forward (``loglinear_fwd``, all of its kernels) over the
 training-shape layer B=8, H=16, T=16384, d_k=d_v=64, C=64 in bfloat16, with
@@ -19,6 +19,9 @@ every input already resident in HBM.  Prints ONE JSON line:
   stages         per kernel (chunk_states, group_tree, chunk_output): mean
                  time, algorithmic bytes, GB/s and counter traffic
   mfma           the matrix-core share of the whole forward
+  backward       the backward (loglinear_bwd) on the same layer with a
+                 seeded upstream gradient: mean time, tokens/s and its ratio
+                 to the forward
   decode         the decode workload (64 x 16 heads): the 32768-token
                  prefill handing its state to decode (loglinear_fwd_state),
                  then 256 decode steps, positions 32768..33023
@@ -301,6 +304,36 @@ def bench_decode_large(la, torch, dev, B=256, steps=64):
             "frac": tot / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
 
+def bench_backward(la, torch, dev, w, x, fwd_ms, reps=10):
+    """The backward (loglinear_bwd, all of its kernels) on the training shape
+    with a seeded upstream gradient, timed with HIP events on the launch
+    stream.  Essential bytes: q, k, v, dout, log_a, lambda read and dq, dk,
+    dv, dlog_a, dlambda written once."""
+    from fenwick_tree_hierarchical_amd.workloads import make_grad_out
+    dout = make_grad_out(w, device=dev)
+    nws = la.loglinear_bwd_workspace(w.B, w.H, w.T, w.dk, w.dv, w.C, torch.bfloat16)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    grads = la.loglinear_bwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], dout, chunk=w.C, workspace=ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(s)
+    for i in range(reps):
+        la.loglinear_bwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], dout, chunk=w.C, workspace=ws, grads=grads)
+        ev[i + 1].record(s)
+    torch.cuda.synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    mean = sum(ms) / reps
+    es = 2
+    per_tok = 7 * w.dk * es + 2 * 4 + 2 * 4 * w.L
+    nbytes = w.B * w.H * w.T * per_tok
+    return {"workload": w.name, "chunk": w.C, "reps": reps, "ms": mean, "median_ms": sorted(ms)[reps // 2],
+            "min_ms": min(ms), "tokens_per_s": w.B * w.T / (mean * 1e-3), "ratio_to_forward": mean / fwd_ms,
+            "essential_bytes": nbytes, "essential_gbps": nbytes / (mean * 1e-3) / 1e9,
+            "essential_bytes_note": f"{per_tok} B per head-token: q, k, v, dout read and dq, dk, dv written "
+                                    f"(bf16), log_a, lambda read and dlog_a, dlambda written (fp32)"}
+
+
 def ctypes_byref(la, st):
     import ctypes
     return ctypes.byref(st._st)
@@ -376,9 +409,9 @@ def pmc_profile(fetch_dir: str, write_dir: str, out_path: str):
            "per_launch_kib": per_kib, "per_kernel_traffic_bytes": traffic,
            "commands": [
                f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/{fetch_dir} "
-               "-o fetch -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-decode --copy-calibration",
+               "-o fetch -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-decode --no-backward --copy-calibration",
                f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/{write_dir} "
-               "-o write -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-decode --copy-calibration",
+               "-o write -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-decode --no-backward --copy-calibration",
                f"python bench.py --pmc-profile {fetch_dir} {write_dir}"]}
     with open(out_path, "w") as f:
         json.dump(res, f, indent=1)
@@ -433,6 +466,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=48)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pmc-summary", default=None)
@@ -539,6 +573,9 @@ def main():
                  "split_tflop": {"intra": cnt["flops_intra"] / 1e12, "states": cnt["flops_states"] / 1e12,
                                  "contractions": cnt["flops_contractions"] / 1e12}},
     }
+    if not args.no_backward:
+        log("bench: backward")
+        result["backward"] = bench_backward(la, torch, dev, w, x, fwd_ms)
     if not args.no_decode:
         log("bench: decode 256 steps")
         result["decode"] = bench_decode(la, torch, dev)

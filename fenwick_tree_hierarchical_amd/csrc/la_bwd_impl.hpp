@@ -53,6 +53,8 @@ struct BwdArgs {
   void* rnodes_in;       // key side: block starting at chunk x inside a group, [BH][n_chunks][d_k][d_v]
   float* rpart;          // [BH][n_groups][JG][d_k][d_v] fp32: a group's share of its group-level blocks
   void* rnodes;          // block starting at group x, [BH][n_groups][d_k][d_v]
+  void* rnodes_in_t;     // the same key-side nodes transposed, (d_v, d_k)
+  void* rnodes_t;
   float* dcol;           // [BH][T]: v_s . dv_s
   int64_t T;
   int64_t n_chunks;
@@ -66,12 +68,23 @@ struct BwdShape {
   using EL = Elem<BF16>;
   static constexpr int NW = bwd_waves(C), NT = 64 * NW;
   static constexpr int QB = C / 16, DB = D / 16;
+  static constexpr int NST = QB * (QB + 1) / 2;                // causal 16 x 16 score tiles
+  static constexpr int KT = (NST + NW - 1) / NW;               // score tiles per wave (max)
+  static constexpr int NCB = DB > NW ? DB / NW : 1;           // output column blocks per wave
+  static constexpr int NWA = DB >= NW ? NW : DB;               // waves that own columns
   static constexpr int KSD = (D + EL::kStep - 1) / EL::kStep;   // k-steps over d
   static constexpr int KSC = (C + EL::kStep - 1) / EL::kStep;   // k-steps over tokens
   static constexpr int EPV = 16 / (BF16 ? 2 : 4), VPR = D / EPV, NV = C * VPR;
   static constexpr int NPF = (NV + NT - 1) / NT;
   static constexpr int LOG2C = cilog2(C);
 };
+
+// Score tile tau of a chunk -> (later block a, earlier block b), b <= a.
+__device__ __forceinline__ void tile_blocks(int tau, int& a, int& b) {
+  a = 0;
+  while ((a + 1) * (a + 2) / 2 <= tau) ++a;
+  b = tau - a * (a + 1) / 2;
+}
 
 // Operand fragment of a transposed tile read from a row-major LDS tile: row
 // `col` of tile^T (a column of the tile), k-slice of rows k0 .. k0 + KPL - 1;
@@ -147,19 +160,35 @@ __device__ __forceinline__ void bwd_load_chunk(const BwdArgs& a, unsigned char* 
 }
 
 // ---------------------------------------------------------------------------
-// bwd_chunk_dq: one workgroup per (b,h, chunk); wave w owns query rows
-// 16 w .. 16 w + 15.  Writes dq, the lambda gradients of the chunk's rows and
-// the row terms dout_t . o_t = sum_l lambda_t^l dlambda_t^l (into dlog_a).
+// bwd_chunk_dq: one workgroup per (b,h, chunk), laid out like the forward's
+// output kernel.  Phase 1 deals the causal 16 x 16 tiles round-robin over the
+// waves: dP = dout V^T and S = Q K^T, masked into dS = dP * gate * lambda
+// (written over the V tile once every wave is past its V reads) and into the
+// lambda gradients of the levels inside the chunk (row sums of S * dP * gate
+// per tile).  Phase 2 gives each wave 16 columns of d_k for all rows:
+// dq = dS K, then per occupied level Z = dout N^T, dq += lambda * gate * Z
+// and the wave's share of the row dot q . Z (the lambda gradient of that
+// level).  Shares are added in a fixed order, so results are deterministic.
+// Also writes the row terms dout_t . o_t = sum_l lambda_t^l dlambda_t^l.
+// bfloat16 tiles up to d = 64 fit four workgroups of four waves per CU in LDS
+// and are held to the registers of four waves per SIMD.
 template <bool BF16, int C, int D>
-__global__ __launch_bounds__(64 * bwd_waves(C)) void bwd_chunk_dq(BwdArgs a) {
+constexpr int dq_min_waves() { return BF16 && D <= 64 ? 4 : 1; }
+
+template <bool BF16, int C, int D>
+__global__ __launch_bounds__(64 * bwd_waves(C)) __attribute__((amdgpu_waves_per_eu(dq_min_waves<BF16, C, D>(), 8)))
+void bwd_chunk_dq(BwdArgs a) {
   using SH = BwdShape<BF16, C, D>;
   using EL = Elem<BF16>;
   using E = typename EL::T;
   using Frag = typename EL::Frag;
-  constexpr int DB = SH::DB, KSD = SH::KSD, KPL = EL::kPerLane, KST = EL::kStep, LOG2C = SH::LOG2C;
+  constexpr int QB = SH::QB, DB = SH::DB, KSD = SH::KSD, KSC = SH::KSC, NCB = SH::NCB, NW = SH::NW, KT = SH::KT;
+  constexpr int KPL = EL::kPerLane, KST = EL::kStep, LOG2C = SH::LOG2C;
   constexpr int G = state_group(D), LOG2G = cilog2(G);
+  constexpr int NPRE = 2;                                      // node fragment buffers
   extern __shared__ __align__(16) unsigned char smem[];
   const int L = a.L;
+  const int NI = L - LOG2C - 1;                                // levels above the chunk
   const BwdChunkLds lay = bwd_chunk_lds(C, D, sizeof(E), L, false);
   const E* Qs = reinterpret_cast<const E*>(smem + lay.q);
   const E* Ks = reinterpret_cast<const E*>(smem + lay.k);
@@ -167,9 +196,11 @@ __global__ __launch_bounds__(64 * bwd_waves(C)) void bwd_chunk_dq(BwdArgs a) {
   const E* Gs = reinterpret_cast<const E*>(smem + lay.g);
   E* Ps = reinterpret_cast<E*>(smem + lay.s0);
   const float* lamS = reinterpret_cast<const float*>(smem + lay.lam);
-  float* dlS = reinterpret_cast<float*>(smem + lay.dl);
+  float* partO = reinterpret_cast<float*>(smem + lay.part);    // [tile][16]: off-diagonal tile row sums
+  float* partD = partO + SH::NST * 16;                         // [row block][16][5]: diagonal tile levels 0..4
+  float* inter = reinterpret_cast<float*>(smem + lay.inter);   // [wave][level - log2 C - 1][row]
+  float* dlS = reinterpret_cast<float*>(smem + lay.dl);        // [row][level]
   float* b2c = reinterpret_cast<float*>(smem + lay.b2);
-  float* e2c = reinterpret_cast<float*>(smem + lay.e2);
 
   const int64_t nc = a.n_chunks, ng = a.n_groups, T = a.T;
   const int64_t item = xcd_item(blockIdx.x, gridDim.x);
@@ -177,19 +208,6 @@ __global__ __launch_bounds__(64 * bwd_waves(C)) void bwd_chunk_dq(BwdArgs a) {
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id(), lq = lane >> 4, lr = lane & 15;
   const int64_t tc = c * C;
   const int nv = (int)(T - tc < C ? T - tc : C);
-
-  bwd_load_chunk<BF16, C, D>(a, smem, lay, bh, tc, nv);
-  for (int idx = tid; idx < C * L; idx += SH::NT) dlS[idx] = 0.f;
-  if (w == 0) {
-    // in-chunk inclusive prefix of log2(a), and its exp2: the gate from the
-    // chunk start through each row
-    const float x = (lane < C && tc + lane < T) ? a.log_a[bh * T + tc + lane] * kLog2e : 0.f;
-    const float y = wave_incl_scan(x);
-    if (lane < C) {
-      b2c[lane] = y;
-      e2c[lane] = __builtin_amdgcn_exp2f(y);
-    }
-  }
 
   // occupied levels above the chunk, as in the forward: lanes 1..LOG2G hold
   // the chunk levels inside the group, lanes 32..62 the group levels
@@ -222,6 +240,39 @@ __global__ __launch_bounds__(64 * bwd_waves(C)) void bwd_chunk_dq(BwdArgs a) {
   const int n_lev = __popcll(lmask);
   const int pos = __popcll(lmask & ((1ull << lane) - 1ull));
   const int ent = __builtin_amdgcn_ds_permute((act ? pos : 63) << 2, lane);
+  // occupied levels as a bit mask (every level is below 32)
+  unsigned occm = 0;
+  for (int li = 0; li < n_lev; ++li)
+    occm |= 1u << __builtin_amdgcn_readlane(lev, __builtin_amdgcn_readlane(ent, li));
+  const int cb0 = w * NCB;
+  const bool owner = cb0 < DB;
+  auto node_of = [&](int li) {
+    const int el = __builtin_amdgcn_readlane(ent, li);
+    const uint64_t o64 = (uint64_t)off;
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)o64, el);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(o64 >> 32), el);
+    const int64_t o = (int64_t)(((uint64_t)hi << 32) | lo);
+    return (el >= 32 ? reinterpret_cast<const E*>(a.nodes) : reinterpret_cast<const E*>(a.nodes_in)) + o;
+  };
+  // node fragments as the A operand: row d_k (this wave's columns), k-slice of d_v
+  auto load_node = [&](int li, Frag (&dst)[KSD][NCB]) {
+    const E* node = node_of(li);
+#pragma unroll
+    for (int s2 = 0; s2 < KSD; ++s2) {
+      const int k0 = s2 * KST + lq * KPL;
+#pragma unroll
+      for (int n = 0; n < NCB; ++n) dst[s2][n] = EL::template load_k<D>(node + (16 * (cb0 + n) + lr) * D + k0, k0);
+    }
+  };
+  bwd_load_chunk<BF16, C, D>(a, smem, lay, bh, tc, nv);
+  if (w == 0) {
+    // in-chunk inclusive prefix of log2(a): its exp2 is the gate from the
+    // chunk start through each row
+    const float x = (lane < C && tc + lane < T) ? a.log_a[bh * T + tc + lane] * kLog2e : 0.f;
+    const float y = wave_incl_scan(x);
+    if (lane < C) b2c[lane] = y;
+  }
+
   const float gx = (lane < ci) ? a.gch[bh * nc + cg0 + lane] : 0.f;
   const bool grp = act && lane >= 32;
   float g2 = 0.f;
@@ -242,26 +293,45 @@ __global__ __launch_bounds__(64 * bwd_waves(C)) void bwd_chunk_dq(BwdArgs a) {
   }
   __syncthreads();
 
-  // ---- phase 1: score tiles of row block rb = w against key blocks kb <= rb,
-  // transposed (lane: query row, four keys).  dS = dP * gate * lambda goes to
-  // LDS; the lambda gradients of levels 0..log2 C sum S * dP * gate by level.
-  const int rb = w;
-  const int iq = 16 * rb + lr;
-  float dlr[LOG2C + 1];
+  // ---- phase 1: transposed score tiles (lane: query row, four keys)
+  f32x4 ssv[KT], sdv[KT];
 #pragma unroll
-  for (int u = 0; u <= LOG2C; ++u) dlr[u] = 0.f;
-  for (int kb = 0; kb <= rb; ++kb) {
-    f32x4 ss = f32x4{0.f, 0.f, 0.f, 0.f}, sd = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < KT; ++u) {
+    ssv[u] = sdv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int tau = w + u * NW;
+    if (tau >= SH::NST) break;
+    int qb, kb;
+    tile_blocks(tau, qb, kb);
+    const int iq = 16 * qb + lr;
 #pragma unroll
     for (int s = 0; s < KSD; ++s) {
       const int k0 = s * KST + lq * KPL;
       const auto kf = EL::template load_k<D>(Ks + (16 * kb + lr) * lay.ld_row + k0, k0);
       const auto qf = EL::template load_k<D>(Qs + iq * lay.ld_row + k0, k0);
-      ss = EL::mma(kf, qf, ss);
+      ssv[u] = EL::mma(kf, qf, ssv[u]);
       const auto vf = EL::template load_k<D>(Vs + (16 * kb + lr) * lay.ld_row + k0, k0);
       const auto gf = EL::template load_k<D>(Gs + iq * lay.ld_row + k0, k0);
-      sd = EL::mma(vf, gf, sd);
+      sdv[u] = EL::mma(vf, gf, sdv[u]);
     }
+  }
+  // the Q entries of this wave's columns, for the row dots of the levels
+  E qv[QB][NCB][4];
+#pragma unroll
+  for (int rb = 0; rb < QB; ++rb)
+#pragma unroll
+    for (int n = 0; n < NCB; ++n) {
+      const E* qrow = Qs + (16 * rb + lr) * lay.ld_row + 16 * ((owner ? cb0 : 0) + n) + 4 * lq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qv[rb][n][i] = qrow[i];
+    }
+  __syncthreads();                                 // Q and V no longer read: row sums and dS go over them
+#pragma unroll
+  for (int u = 0; u < KT; ++u) {
+    const int tau = w + u * NW;
+    if (tau >= SH::NST) break;
+    int qb, kb;
+    tile_blocks(tau, qb, kb);
+    const int iq = 16 * qb + lr;
     const int j0 = 16 * kb + 4 * lq;
     const float b2q = b2c[iq];
     float dsv[4], ev[4];
@@ -273,108 +343,148 @@ __global__ __launch_bounds__(64 * bwd_waves(C)) void bwd_chunk_dq(BwdArgs a) {
       lv = lv < L ? lv : L - 1;
       const float W = __builtin_amdgcn_exp2f(b2q - b2c[j]);
       const bool ok = j <= iq && iq < nv;
-      dsv[i] = ok ? sd[i] * W * lamS[iq * L + lv] : 0.f;
-      ev[i] = ok ? ss[i] * sd[i] * W : 0.f;
+      dsv[i] = ok ? sdv[u][i] * W * lamS[iq * L + lv] : 0.f;
+      ev[i] = ok ? ssv[u][i] * sdv[u][i] * W : 0.f;
       lvv[i] = lv;
-    }
-    if (kb == rb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int u = 0; u <= 4 && u <= LOG2C; ++u) dlr[u] += (lvv[i] == u) ? ev[i] : 0.f;
-    } else {
-      // every key of an earlier 16-block is at level 5 + msb(rb ^ kb)
-      const int lk = 5 + (31 - __builtin_clz((unsigned)(rb ^ kb)));
-      const float es = (ev[0] + ev[1]) + (ev[2] + ev[3]);
-#pragma unroll
-      for (int u = 5; u <= LOG2C; ++u) dlr[u] += (lk == u) ? es : 0.f;
     }
     if constexpr (BF16)
       *reinterpret_cast<u16x4*>(Ps + iq * lay.ld_s + j0) =
           u16x4{f32_to_bf16(dsv[0]), f32_to_bf16(dsv[1]), f32_to_bf16(dsv[2]), f32_to_bf16(dsv[3])};
     else
       *reinterpret_cast<float4*>(Ps + iq * lay.ld_s + j0) = make_float4(dsv[0], dsv[1], dsv[2], dsv[3]);
-  }
+    if (kb == qb) {
+      // inside a 16-block the levels are 0..4
+      float dlr[5];
 #pragma unroll
-  for (int u = 0; u <= LOG2C; ++u) {
-    dlr[u] += __shfl_xor(dlr[u], 16, 64);
-    dlr[u] += __shfl_xor(dlr[u], 32, 64);
-  }
-  if (lq == 0 && iq < nv) {
+      for (int v = 0; v < 5; ++v) {
+        dlr[v] = 0.f;
 #pragma unroll
-    for (int u = 0; u <= LOG2C; ++u)
-      if (u < L) dlS[iq * L + u] = dlr[u];
+        for (int i = 0; i < 4; ++i) dlr[v] += (lvv[i] == v) ? ev[i] : 0.f;
+        dlr[v] += __shfl_xor(dlr[v], 16, 64);
+        dlr[v] += __shfl_xor(dlr[v], 32, 64);
+      }
+      if (lq == 0) {
+#pragma unroll
+        for (int v = 0; v < 5; ++v) partD[(qb * 16 + lr) * 5 + v] = dlr[v];
+      }
+    } else {
+      // every key of an earlier 16-block is at one level, 5 + msb(qb ^ kb)
+      float es = (ev[0] + ev[1]) + (ev[2] + ev[3]);
+      es += __shfl_xor(es, 16, 64);
+      es += __shfl_xor(es, 32, 64);
+      if (lq == 0) partO[tau * 16 + lr] = es;
+    }
   }
   __syncthreads();
 
-  // ---- phase 2: dq^T = K^T dS^T over keys 0 .. 16 rb + 15 (lane: query row,
-  // four consecutive d_k), then one product dout N^T per occupied level
-  f32x4 acc[DB];
+  // ---- phase 2: this wave's columns of d_k for all query rows, transposed
+  // (lane: query row, four consecutive columns)
+  f32x4 acc[QB][NCB];
 #pragma unroll
-  for (int n = 0; n < DB; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < QB; ++rb)
 #pragma unroll
-  for (int s = 0; s < SH::KSC; ++s) {
-    if (s * KST > 16 * rb + 15) break;
-    const int k0 = s * KST + lq * KPL;
-    Frag pb = zero_frag<BF16>();
-    if (k0 < C && k0 / 16 <= rb) pb = EL::load(Ps + iq * lay.ld_s + k0);
+    for (int n = 0; n < NCB; ++n) acc[rb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Frag nf[NPRE][KSD][NCB];                         // the first levels' node fragments load under dq = dS K
+  if (owner) {
 #pragma unroll
-    for (int n = 0; n < DB; ++n) {
-      const Frag kt = gather_col<BF16, C>(Ks, lay.ld_row, k0, 16 * n + lr);
-      acc[n] = EL::mma(kt, pb, acc[n]);
-    }
-  }
-  Frag gfr[KSD];
+    for (int u = 0; u < NPRE; ++u)
+      if (u < n_lev) load_node(u, nf[u]);
+    Frag kt[KSC][NCB];                             // K^T rows (columns of K), k-slices of keys
 #pragma unroll
-  for (int s2 = 0; s2 < KSD; ++s2) {
-    const int k0 = s2 * KST + lq * KPL;
-    gfr[s2] = EL::template load_k<D>(Gs + iq * lay.ld_row + k0, k0);
-  }
-  const float e2q = e2c[iq];
-  for (int li = 0; li < n_lev; ++li) {
-    const int el = __builtin_amdgcn_readlane(ent, li);
-    const uint64_t o64 = (uint64_t)off;
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)o64, el);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(o64 >> 32), el);
-    const int64_t o = (int64_t)(((uint64_t)hi << 32) | lo);
-    const E* node = (el >= 32 ? reinterpret_cast<const E*>(a.nodes) : reinterpret_cast<const E*>(a.nodes_in)) + o;
-    const float f = __builtin_amdgcn_exp2f(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g2), el)));
-    const int lv = __builtin_amdgcn_readlane(lev, el);
-    const float wq = e2q * f;
-    const float wl = wq * lamS[iq * L + lv];
-    float dsum = 0.f;
+    for (int s = 0; s < KSC; ++s)
 #pragma unroll
-    for (int n = 0; n < DB; ++n) {
-      f32x4 tmp = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < NCB; ++n) kt[s][n] = gather_col<BF16, C>(Ks, lay.ld_row, s * KST + lq * KPL, 16 * (cb0 + n) + lr);
 #pragma unroll
-      for (int s2 = 0; s2 < KSD; ++s2) {
-        const int k0 = s2 * KST + lq * KPL;
-        const auto nf = EL::template load_k<D>(node + (16 * n + lr) * D + k0, k0);
-        tmp = EL::mma(nf, gfr[s2], tmp);
-      }
-      const E* qrow = Qs + iq * lay.ld_row + 16 * n + 4 * lq;
+    for (int rb = 0; rb < QB; ++rb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dsum += tmp[i] * EL::to_f32(qrow[i]);
-        acc[n][i] += wl * tmp[i];
+      for (int s = 0; s < KSC; ++s) {
+        if (s * KST > 16 * rb + 15) break;
+        const int k0 = s * KST + lq * KPL;
+        Frag pb = zero_frag<BF16>();
+        if (k0 < C && k0 / 16 <= rb) pb = EL::load(Ps + (16 * rb + lr) * lay.ld_s + k0);
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) acc[rb][n] = EL::mma(kt[s][n], pb, acc[rb][n]);
       }
     }
-    dsum += __shfl_xor(dsum, 16, 64);
-    dsum += __shfl_xor(dsum, 32, 64);
-    if (lq == 0 && iq < nv) dlS[iq * L + lv] = wq * dsum;
   }
-  if (iq < nv) {
-    E* o = reinterpret_cast<E*>(a.dq) + (bh * T + tc + iq) * D + 4 * lq;
+  __syncthreads();                                 // K and dS no longer read: level shares go over them
+  if (owner) {
+    auto contract = [&](int li, const Frag (&nfr)[KSD][NCB]) {
+      const int el = __builtin_amdgcn_readlane(ent, li);
+      const float f = __builtin_amdgcn_exp2f(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g2), el)));
+      const int lv = __builtin_amdgcn_readlane(lev, el);
 #pragma unroll
-    for (int n = 0; n < DB; ++n) store4<BF16>(o + 16 * n, acc[n]);
+      for (int rb = 0; rb < QB; ++rb) {
+        const int r = 16 * rb + lr;
+        f32x4 tmp[NCB];
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) tmp[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < KSD; ++s2) {
+          const int k0 = s2 * KST + lq * KPL;
+          const auto gf = EL::template load_k<D>(Gs + r * lay.ld_row + k0, k0);
+#pragma unroll
+          for (int n = 0; n < NCB; ++n) tmp[n] = EL::mma(nfr[s2][n], gf, tmp[n]);
+        }
+        const float wq = __builtin_amdgcn_exp2f(b2c[r]) * f;
+        const float wl = wq * lamS[r * L + lv];
+        float ds = 0.f;
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ds += tmp[n][i] * EL::to_f32(qv[rb][n][i]);
+            acc[rb][n][i] += wl * tmp[n][i];
+          }
+        }
+        ds += __shfl_xor(ds, 16, 64);
+        ds += __shfl_xor(ds, 32, 64);
+        if (lq == 0) inter[(w * NI + (lv - LOG2C - 1)) * C + r] = wq * ds;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    for (int base = 0; base < n_lev; base += NPRE) {
+#pragma unroll
+      for (int u = 0; u < NPRE; ++u) {
+        const int li = base + u;
+        if (li >= n_lev) break;
+        contract(li, nf[u]);
+        if (li + NPRE < n_lev) load_node(li + NPRE, nf[u]);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < QB; ++rb) {
+      const int r = 16 * rb + lr;
+      if (r < nv) {
+        E* o = reinterpret_cast<E*>(a.dq) + (bh * T + tc + r) * D + 4 * lq;
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) store4<BF16>(o + 16 * (cb0 + n), acc[rb][n]);
+      }
+    }
+  }
+  __syncthreads();                                 // dout no longer read: dl goes over it
+  // lambda gradients of the chunk's rows: levels 0..4 from the diagonal
+  // tiles, 5..log2 C from the earlier tiles of the row block, the rest from
+  // the waves' shares; levels with an empty bucket are zero
+  for (int idx = tid; idx < C * L; idx += SH::NT) {
+    const int r = idx / L, lv = idx % L;
+    const int rb = r >> 4, rr = r & 15;
+    float val = 0.f;
+    if (lv <= 4 && lv <= LOG2C) {
+      val = partD[(rb * 16 + rr) * 5 + lv];
+    } else if (lv <= LOG2C) {
+      for (int kb = 0; kb < rb; ++kb)
+        if (5 + (31 - __builtin_clz((unsigned)(rb ^ kb))) == lv) val += partO[(rb * (rb + 1) / 2 + kb) * 16 + rr];
+    } else if ((occm >> lv) & 1u) {
+      for (int u = 0; u < SH::NWA; ++u) val += inter[(u * NI + (lv - LOG2C - 1)) * C + r];
+    }
+    dlS[idx] = val;
   }
   __syncthreads();
-  // row terms and the lambda gradients of the chunk's rows (levels with an
-  // empty bucket stay zero)
   if (tid < nv) {
-    float r = 0.f;
-    for (int u = 0; u < L; ++u) r += lamS[tid * L + u] * dlS[tid * L + u];
-    a.dlog_a[bh * T + tc + tid] = r;
+    float rt = 0.f;
+    for (int u = 0; u < L; ++u) rt += lamS[tid * L + u] * dlS[tid * L + u];
+    a.dlog_a[bh * T + tc + tid] = rt;
   }
   float* dl = a.dlam + (bh * T + tc) * L;
   for (int idx = tid; idx < nv * L; idx += SH::NT) dl[idx] = dlS[idx];
@@ -416,13 +526,14 @@ __global__ __launch_bounds__(64 * state_waves(D)) void bwd_rev_states(BwdArgs a)
   const E* qb = reinterpret_cast<const E*>(a.q) + (bh * T + t0) * D;
   const E* gb = reinterpret_cast<const E*>(a.dout) + (bh * T + t0) * D;
   const float* lb = a.lam + (bh * T + t0) * L;
-  f32x4 acc[TPW];
+  f32x4 acc[TPW], acct[TPW];       // R and R^T tiles of this wave
   auto zero_acc = [&]() {
 #pragma unroll
-    for (int h = 0; h < TPW; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < TPW; ++h) acc[h] = acct[h] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
-  // R[d_k][d_v] tiles of this wave to dst (row-major (d_k, d_v))
-  auto flush = [&](auto* dst) {
+  // tiles of R (d_k, d_v) to dst and, when dst_t is given, of R^T (d_v, d_k)
+  // to dst_t, both row-major
+  auto flush = [&](auto* dst, E* dst_t) {
 #pragma unroll
     for (int h = 0; h < TPW; ++h) {
       const int tix = w + h * NW;
@@ -431,6 +542,7 @@ __global__ __launch_bounds__(64 * state_waves(D)) void bwd_rev_states(BwdArgs a)
       auto* o = dst + (16 * mb + lr) * D + 16 * nb + 4 * lq;
       if constexpr (sizeof(*o) == 4) *reinterpret_cast<f32x4*>(o) = acc[h];
       else store4<BF16>(reinterpret_cast<E*>(o), acc[h]);
+      if (dst_t) store4<BF16>(dst_t + (16 * nb + lr) * D + 16 * mb + 4 * lq, acct[h]);
     }
   };
   const int nlev = LOG2G + a.JG;
@@ -490,15 +602,17 @@ __global__ __launch_bounds__(64 * state_waves(D)) void bwd_rev_states(BwdArgs a)
           const auto gf = EL::template load_k<C>(GT + ng_ * lay.ld_t + (k0 ^ state_swz<C>(ng_)), k0);
           const auto qf = EL::template load_k<C>(QT + nq_ * lay.ld_t + (k0 ^ state_swz<C>(nq_)), k0);
           acc[h] = EL::mma(gf, qf, acc[h]);
+          acct[h] = EL::mma(qf, gf, acct[h]);
         }
       }
       __syncthreads();
       const bool last = in_group ? ((((ci + 1) & ((1 << (j - 1)) - 1)) == 0) || ci == nch - 1) : ci == nch - 1;
       if (last) {
         if (in_group) {
-          flush(reinterpret_cast<E*>(a.rnodes_in) + (bh * nc + c0 + xs) * D * D);
+          flush(reinterpret_cast<E*>(a.rnodes_in) + (bh * nc + c0 + xs) * D * D,
+                reinterpret_cast<E*>(a.rnodes_in_t) + (bh * nc + c0 + xs) * D * D);
         } else {
-          flush(a.rpart + ((bh * ng + gam) * a.JG + (j - LOG2G - 1)) * D * D);
+          flush(a.rpart + ((bh * ng + gam) * a.JG + (j - LOG2G - 1)) * D * D, static_cast<E*>(nullptr));
         }
         zero_acc();
       }
@@ -510,40 +624,63 @@ __global__ __launch_bounds__(64 * state_waves(D)) void bwd_rev_states(BwdArgs a)
 // bwd_rev_tree: the key-side node of every block of groups that is the upper
 // half of its level block: it starts at group x >= 1 and spans 2^ctz(x)
 // groups; the sum of those groups' shares, each carried by the gate from the
-// block start to the group start.
+// block start to the group start.  One workgroup per node: R is written
+// row-major, then read back from LDS by columns (rows padded by one 4-byte
+// word, so a column read is spread over the banks) and written as R^T.
 template <bool BF16>
 __global__ __launch_bounds__(256) void bwd_rev_tree(BwdArgs a, int D) {
   using EL = Elem<BF16>;
   using E = typename EL::T;
+  extern __shared__ __align__(16) unsigned char smem[];
+  E* tr = reinterpret_cast<E*>(smem);
+  const int ld = D + 4 / (int)sizeof(E);
   const int DD = D * D;
-  const int nblk = (DD + 255) / 256;
   const int64_t ng = a.n_groups;
-  const int64_t item = blockIdx.x / nblk;
-  const int64_t bh = item / (ng - 1), x = 1 + item % (ng - 1);
-  const int elem = (int)(blockIdx.x % nblk) * 256 + threadIdx.x;
-  if (elem >= DD) return;
+  const int64_t bh = blockIdx.x / (ng - 1), x = 1 + blockIdx.x % (ng - 1);
   const int i = __builtin_ctzll((unsigned long long)x);     // block of 2^i groups, group level i + 1
   const int64_t end = x + (1ll << i) < ng ? x + (1ll << i) : ng;
   const double* gp = a.gprefix + bh * (ng + 1);
   const double base = gp[x];
-  float acc = 0.f;
-  for (int64_t g = x; g < end; ++g)
-    acc += __builtin_amdgcn_exp2f((float)(gp[g] - base)) * a.rpart[((bh * ng + g) * a.JG + i) * DD + elem];
-  reinterpret_cast<E*>(a.rnodes)[(bh * ng + x) * DD + elem] = EL::from_f32(acc);
+  E* R = reinterpret_cast<E*>(a.rnodes) + (bh * ng + x) * DD;
+  E* RT = reinterpret_cast<E*>(a.rnodes_t) + (bh * ng + x) * DD;
+  for (int e = threadIdx.x; e < DD; e += 256) {
+    float acc = 0.f;
+    for (int64_t g = x; g < end; ++g)
+      acc += __builtin_amdgcn_exp2f((float)(gp[g] - base)) * a.rpart[((bh * ng + g) * a.JG + i) * DD + e];
+    const E val = EL::from_f32(acc);
+    R[e] = val;
+    tr[(e / D) * ld + e % D] = val;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < DD; e += 256) RT[e] = tr[(e % D) * ld + e / D];
 }
 
 // ---------------------------------------------------------------------------
-// bwd_chunk_dkv: one workgroup per (b,h, chunk); wave w owns key rows
-// 16 w .. 16 w + 15.  Writes dk, dv and the column terms v_s . dv_s.
+// bwd_chunk_dkv: one workgroup per (b,h, chunk), laid out like bwd_chunk_dq
+// with keys in place of queries.  Phase 1 deals the causal tiles over the
+// waves (lane: key row, four queries): dS^T = dP * gate * lambda goes to LDS,
+// P^T = S * gate * lambda stays in registers.  Phase 2 gives each wave 16
+// columns for all key rows: dk = dS^T Q, then P^T is written over dS^T and
+// dv = P^T dout; per level above the chunk, dk += gate R v and dv += gate
+// R^T k with the key-side node R and its transpose.  Also writes the column
+// terms v_s . dv_s (waves' shares added in a fixed order).  Up to d = 64 it
+// is held to the registers of three waves per SIMD (the LDS allows three
+// workgroups of four waves per CU): measured faster than two waves with a
+// deeper node ring; larger tiles would spill.
 template <bool BF16, int C, int D>
-__global__ __launch_bounds__(64 * bwd_waves(C)) void bwd_chunk_dkv(BwdArgs a) {
+constexpr int dkv_min_waves() { return D <= 64 ? 3 : 1; }
+
+template <bool BF16, int C, int D>
+__global__ __launch_bounds__(64 * bwd_waves(C)) __attribute__((amdgpu_waves_per_eu(dkv_min_waves<BF16, C, D>(), 8)))
+void bwd_chunk_dkv(BwdArgs a) {
   using SH = BwdShape<BF16, C, D>;
   using EL = Elem<BF16>;
   using E = typename EL::T;
   using Frag = typename EL::Frag;
-  constexpr int DB = SH::DB, KSD = SH::KSD, KPL = EL::kPerLane, KST = EL::kStep, LOG2C = SH::LOG2C;
+  constexpr int QB = SH::QB, DB = SH::DB, KSD = SH::KSD, KSC = SH::KSC, NCB = SH::NCB, NW = SH::NW, KT = SH::KT;
+  constexpr int KPL = EL::kPerLane, KST = EL::kStep, LOG2C = SH::LOG2C;
   constexpr int G = state_group(D), LOG2G = cilog2(G);
-  constexpr int EPV = SH::EPV, VPR = SH::VPR;
+  constexpr int NPRE = 1;                                      // node fragment buffers
   extern __shared__ __align__(16) unsigned char smem[];
   const int L = a.L;
   const BwdChunkLds lay = bwd_chunk_lds(C, D, sizeof(E), L, true);
@@ -551,10 +688,9 @@ __global__ __launch_bounds__(64 * bwd_waves(C)) void bwd_chunk_dkv(BwdArgs a) {
   const E* Ks = reinterpret_cast<const E*>(smem + lay.k);
   const E* Vs = reinterpret_cast<const E*>(smem + lay.v);
   const E* Gs = reinterpret_cast<const E*>(smem + lay.g);
-  E* PT = reinterpret_cast<E*>(smem + lay.s0);
-  E* DST = reinterpret_cast<E*>(smem + lay.s1);
-  E* Rs = reinterpret_cast<E*>(smem + lay.nd);
+  E* Ss = reinterpret_cast<E*>(smem + lay.s0);                 // dS^T, then P^T
   const float* lamS = reinterpret_cast<const float*>(smem + lay.lam);
+  float* colS = reinterpret_cast<float*>(smem + lay.col);      // [wave][key row]
   float* b2c = reinterpret_cast<float*>(smem + lay.b2);
   float* e2c = reinterpret_cast<float*>(smem + lay.e2);
 
@@ -564,18 +700,6 @@ __global__ __launch_bounds__(64 * bwd_waves(C)) void bwd_chunk_dkv(BwdArgs a) {
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id(), lq = lane >> 4, lr = lane & 15;
   const int64_t tc = c * C;
   const int nv = (int)(T - tc < C ? T - tc : C);
-
-  bwd_load_chunk<BF16, C, D>(a, smem, lay, bh, tc, nv);
-  if (w == 0) {
-    // in-chunk prefix of log2(a), and the gate from each key to the chunk end
-    const float x = (lane < C && tc + lane < T) ? a.log_a[bh * T + tc + lane] * kLog2e : 0.f;
-    const float y = wave_incl_scan(x);
-    const float tot = __shfl(y, C - 1, 64);
-    if (lane < C) {
-      b2c[lane] = y;
-      e2c[lane] = __builtin_amdgcn_exp2f(tot - y);
-    }
-  }
 
   // levels whose upper block lies above the chunk: lanes 1..LOG2G, chunk
   // level j inside the group (bit j-1 of the in-group index clear); lanes
@@ -611,6 +735,50 @@ __global__ __launch_bounds__(64 * bwd_waves(C)) void bwd_chunk_dkv(BwdArgs a) {
   const int n_lev = __popcll(lmask);
   const int pos = __popcll(lmask & ((1ull << lane) - 1ull));
   const int ent = __builtin_amdgcn_ds_permute((act ? pos : 63) << 2, lane);
+  const int cb0 = w * NCB;
+  const bool owner = cb0 < DB;
+  // key-side nodes: R rows (d_k) and R^T rows (d_v) of this wave's columns;
+  // the first levels' fragments load now, under the tile work
+  auto node_off = [&](int li, int& el) {
+    el = __builtin_amdgcn_readlane(ent, li);
+    const uint64_t o64 = (uint64_t)off;
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)o64, el);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(o64 >> 32), el);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+  };
+  auto load_node = [&](int li, Frag (&rf)[KSD][NCB], Frag (&rt)[KSD][NCB]) {
+    int el;
+    const int64_t o = node_off(li, el);
+    const E* R = (el >= 32 ? reinterpret_cast<const E*>(a.rnodes) : reinterpret_cast<const E*>(a.rnodes_in)) + o;
+    const E* RT = (el >= 32 ? reinterpret_cast<const E*>(a.rnodes_t) : reinterpret_cast<const E*>(a.rnodes_in_t)) + o;
+#pragma unroll
+    for (int s2 = 0; s2 < KSD; ++s2) {
+      const int k0 = s2 * KST + lq * KPL;
+#pragma unroll
+      for (int n = 0; n < NCB; ++n) {
+        rf[s2][n] = EL::template load_k<D>(R + (16 * (cb0 + n) + lr) * D + k0, k0);
+        rt[s2][n] = EL::template load_k<D>(RT + (16 * (cb0 + n) + lr) * D + k0, k0);
+      }
+    }
+  };
+  Frag rf[NPRE][KSD][NCB], rt[NPRE][KSD][NCB];
+  if (owner) {
+#pragma unroll
+    for (int u = 0; u < NPRE; ++u)
+      if (u < n_lev) load_node(u, rf[u], rt[u]);
+  }
+  bwd_load_chunk<BF16, C, D>(a, smem, lay, bh, tc, nv);
+  if (w == 0) {
+    // in-chunk prefix of log2(a), and the gate from each key to the chunk end
+    const float x = (lane < C && tc + lane < T) ? a.log_a[bh * T + tc + lane] * kLog2e : 0.f;
+    const float y = wave_incl_scan(x);
+    const float tot = __shfl(y, C - 1, 64);
+    if (lane < C) {
+      b2c[lane] = y;
+      e2c[lane] = __builtin_amdgcn_exp2f(tot - y);
+    }
+  }
+
   float g2 = 0.f;                               // log2 gate from the chunk end to the block start
   if (nc > 1) {
     const float gx = (lane < G && cg0 + lane < nc) ? a.gch[bh * nc + cg0 + lane] : 0.f;
@@ -631,13 +799,18 @@ __global__ __launch_bounds__(64 * bwd_waves(C)) void bwd_chunk_dkv(BwdArgs a) {
   }
   __syncthreads();
 
-  // ---- phase 1: transposed tiles of key block kb = w against query blocks
-  // qb >= kb (lane: key row, four queries): P^T = S * gate * lambda and
-  // dS^T = dP * gate * lambda
-  const int kb = w;
-  const int sk = 16 * kb + lr;
-  const float b2k = b2c[sk];
-  for (int qb = kb; qb < SH::QB; ++qb) {
+  // ---- phase 1: tile tau = (query block qb, key block kb <= qb), lane: key
+  // row sk, queries t0 .. t0 + 3
+  float pT[KT][4];
+#pragma unroll
+  for (int u = 0; u < KT; ++u) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pT[u][i] = 0.f;
+    const int tau = w + u * NW;
+    if (tau >= SH::NST) break;
+    int qb, kb;
+    tile_blocks(tau, qb, kb);
+    const int sk = 16 * kb + lr;
     f32x4 ss = f32x4{0.f, 0.f, 0.f, 0.f}, sd = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KSD; ++s) {
@@ -650,7 +823,8 @@ __global__ __launch_bounds__(64 * bwd_waves(C)) void bwd_chunk_dkv(BwdArgs a) {
       sd = EL::mma(gf, vf, sd);
     }
     const int t0 = 16 * qb + 4 * lq;
-    float pv[4], dv_[4];
+    const float b2k = b2c[sk];
+    float dv_[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = t0 + i;
@@ -658,104 +832,148 @@ __global__ __launch_bounds__(64 * bwd_waves(C)) void bwd_chunk_dkv(BwdArgs a) {
       lv = lv < L ? lv : L - 1;
       const float W = __builtin_amdgcn_exp2f(b2c[t] - b2k) * lamS[t * L + lv];
       const bool ok = sk <= t && t < nv;
-      pv[i] = ok ? ss[i] * W : 0.f;
+      pT[u][i] = ok ? ss[i] * W : 0.f;
       dv_[i] = ok ? sd[i] * W : 0.f;
     }
-    if constexpr (BF16) {
-      *reinterpret_cast<u16x4*>(PT + sk * lay.ld_s + t0) =
-          u16x4{f32_to_bf16(pv[0]), f32_to_bf16(pv[1]), f32_to_bf16(pv[2]), f32_to_bf16(pv[3])};
-      *reinterpret_cast<u16x4*>(DST + sk * lay.ld_s + t0) =
+    if constexpr (BF16)
+      *reinterpret_cast<u16x4*>(Ss + sk * lay.ld_s + t0) =
           u16x4{f32_to_bf16(dv_[0]), f32_to_bf16(dv_[1]), f32_to_bf16(dv_[2]), f32_to_bf16(dv_[3])};
-    } else {
-      *reinterpret_cast<float4*>(PT + sk * lay.ld_s + t0) = make_float4(pv[0], pv[1], pv[2], pv[3]);
-      *reinterpret_cast<float4*>(DST + sk * lay.ld_s + t0) = make_float4(dv_[0], dv_[1], dv_[2], dv_[3]);
-    }
+    else
+      *reinterpret_cast<float4*>(Ss + sk * lay.ld_s + t0) = make_float4(dv_[0], dv_[1], dv_[2], dv_[3]);
   }
   __syncthreads();
 
-  // ---- phase 2: dk^T = Q^T dS and dv^T = dout^T P over queries from the key
-  // block on (lane: key row, four consecutive columns)
-  f32x4 ak[DB], av[DB];
+  // ---- phase 2: this wave's columns for all key rows, transposed (lane: key
+  // row, four consecutive columns); queries from the key's block on
+  f32x4 ak[QB][NCB], av[QB][NCB];
 #pragma unroll
-  for (int n = 0; n < DB; ++n) ak[n] = av[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kb = 0; kb < QB; ++kb)
 #pragma unroll
-  for (int s = 0; s < SH::KSC; ++s) {
-    if (s * KST + KST <= 16 * kb) continue;
-    const int k0 = s * KST + lq * KPL;
-    Frag df = zero_frag<BF16>(), pf = zero_frag<BF16>();
-    if (k0 < C && k0 / 16 >= kb) {
-      df = EL::load(DST + sk * lay.ld_s + k0);
-      pf = EL::load(PT + sk * lay.ld_s + k0);
-    }
+    for (int n = 0; n < NCB; ++n) ak[kb][n] = av[kb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // dk = dS^T Q: Q^T rows (columns of Q) as the A operand
+  if (owner) {
+    Frag ft[KSC][NCB];
 #pragma unroll
-    for (int n = 0; n < DB; ++n) {
-      const Frag qt = gather_col<BF16, C>(Qs, lay.ld_row, k0, 16 * n + lr);
-      ak[n] = EL::mma(qt, df, ak[n]);
-      const Frag gt = gather_col<BF16, C>(Gs, lay.ld_row, k0, 16 * n + lr);
-      av[n] = EL::mma(gt, pf, av[n]);
-    }
-  }
-  // ---- key-side nodes: dk += gate R v, dv += gate R^T k per level
-  Frag vfr[KSD], kfr[KSD];
+    for (int s = 0; s < KSC; ++s)
 #pragma unroll
-  for (int s2 = 0; s2 < KSD; ++s2) {
-    const int k0 = s2 * KST + lq * KPL;
-    vfr[s2] = EL::template load_k<D>(Vs + sk * lay.ld_row + k0, k0);
-    kfr[s2] = EL::template load_k<D>(Ks + sk * lay.ld_row + k0, k0);
-  }
-  const float e2k = e2c[sk];
-  for (int li = 0; li < n_lev; ++li) {
-    const int el = __builtin_amdgcn_readlane(ent, li);
-    const uint64_t o64 = (uint64_t)off;
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)o64, el);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(o64 >> 32), el);
-    const int64_t o = (int64_t)(((uint64_t)hi << 32) | lo);
-    const E* node = (el >= 32 ? reinterpret_cast<const E*>(a.rnodes) : reinterpret_cast<const E*>(a.rnodes_in)) + o;
-    const float f = __builtin_amdgcn_exp2f(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g2), el)));
-    __syncthreads();                            // the previous node is no longer read
-    for (int idx = tid; idx < D * VPR; idx += SH::NT) {
-      const int r = idx / VPR, cv = idx % VPR;
-      *reinterpret_cast<uint4*>(Rs + r * lay.ld_nd + cv * EPV) = *reinterpret_cast<const uint4*>(node + r * D + cv * EPV);
-    }
-    __syncthreads();
-    const float wk = f * e2k;
+      for (int n = 0; n < NCB; ++n) ft[s][n] = gather_col<BF16, C>(Qs, lay.ld_row, s * KST + lq * KPL, 16 * (cb0 + n) + lr);
 #pragma unroll
-    for (int n = 0; n < DB; ++n) {
-      f32x4 tk = f32x4{0.f, 0.f, 0.f, 0.f}, tv = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < QB; ++kb) {
 #pragma unroll
-      for (int s2 = 0; s2 < KSD; ++s2) {
-        const int k0 = s2 * KST + lq * KPL;
-        const auto rf = EL::template load_k<D>(Rs + (16 * n + lr) * lay.ld_nd + k0, k0);   // R row d_k, k-slice d_v
-        tk = EL::mma(rf, vfr[s2], tk);
-        const Frag rt = gather_col<BF16, D>(Rs, lay.ld_nd, k0, 16 * n + lr);              // R^T row d_v, k-slice d_k
-        tv = EL::mma(rt, kfr[s2], tv);
-      }
+      for (int s = 0; s < KSC; ++s) {
+        if (s * KST + KST <= 16 * kb) continue;
+        const int k0 = s * KST + lq * KPL;
+        Frag sf = zero_frag<BF16>();
+        if (k0 < C && k0 / 16 >= kb) sf = EL::load(Ss + (16 * kb + lr) * lay.ld_s + k0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ak[n][i] += wk * tk[i];
-        av[n][i] += wk * tv[i];
+        for (int n = 0; n < NCB; ++n) ak[kb][n] = EL::mma(ft[s][n], sf, ak[kb][n]);
       }
     }
   }
-  // column term v_s . dv_s, then the rows of dk and dv
-  float cs = 0.f;
+  __syncthreads();                                 // dS^T no longer read: P^T goes over it
 #pragma unroll
-  for (int n = 0; n < DB; ++n) {
-    const E* vrow = Vs + sk * lay.ld_row + 16 * n + 4 * lq;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cs += av[n][i] * EL::to_f32(vrow[i]);
+  for (int u = 0; u < KT; ++u) {
+    const int tau = w + u * NW;
+    if (tau >= SH::NST) break;
+    int qb, kb;
+    tile_blocks(tau, qb, kb);
+    const int sk = 16 * kb + lr, t0 = 16 * qb + 4 * lq;
+    if constexpr (BF16)
+      *reinterpret_cast<u16x4*>(Ss + sk * lay.ld_s + t0) =
+          u16x4{f32_to_bf16(pT[u][0]), f32_to_bf16(pT[u][1]), f32_to_bf16(pT[u][2]), f32_to_bf16(pT[u][3])};
+    else
+      *reinterpret_cast<float4*>(Ss + sk * lay.ld_s + t0) = make_float4(pT[u][0], pT[u][1], pT[u][2], pT[u][3]);
   }
-  cs += __shfl_xor(cs, 16, 64);
-  cs += __shfl_xor(cs, 32, 64);
-  if (sk < nv) {
-    if (lq == 0) a.dcol[bh * T + tc + sk] = cs;
-    E* ok = reinterpret_cast<E*>(a.dk) + (bh * T + tc + sk) * D + 4 * lq;
-    E* ov = reinterpret_cast<E*>(a.dv) + (bh * T + tc + sk) * D + 4 * lq;
+  __syncthreads();
+  if (owner) {
+    // dv = P^T dout: dout^T rows as the A operand
+    Frag ft[KSC][NCB];
 #pragma unroll
-    for (int n = 0; n < DB; ++n) {
-      store4<BF16>(ok + 16 * n, ak[n]);
-      store4<BF16>(ov + 16 * n, av[n]);
+    for (int s = 0; s < KSC; ++s)
+#pragma unroll
+      for (int n = 0; n < NCB; ++n) ft[s][n] = gather_col<BF16, C>(Gs, lay.ld_row, s * KST + lq * KPL, 16 * (cb0 + n) + lr);
+#pragma unroll
+    for (int kb = 0; kb < QB; ++kb) {
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) {
+        if (s * KST + KST <= 16 * kb) continue;
+        const int k0 = s * KST + lq * KPL;
+        Frag sf = zero_frag<BF16>();
+        if (k0 < C && k0 / 16 >= kb) sf = EL::load(Ss + (16 * kb + lr) * lay.ld_s + k0);
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) av[kb][n] = EL::mma(ft[s][n], sf, av[kb][n]);
+      }
     }
+    auto contract = [&](int li, const Frag (&rf)[KSD][NCB], const Frag (&rt)[KSD][NCB]) {
+      const int el = __builtin_amdgcn_readlane(ent, li);
+      const float f = __builtin_amdgcn_exp2f(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g2), el)));
+#pragma unroll
+      for (int kb = 0; kb < QB; ++kb) {
+        const int sk = 16 * kb + lr;
+        f32x4 tk[NCB], tv[NCB];
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) tk[n] = tv[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < KSD; ++s2) {
+          const int k0 = s2 * KST + lq * KPL;
+          const auto vf = EL::template load_k<D>(Vs + sk * lay.ld_row + k0, k0);
+          const auto kf = EL::template load_k<D>(Ks + sk * lay.ld_row + k0, k0);
+#pragma unroll
+          for (int n = 0; n < NCB; ++n) {
+            tk[n] = EL::mma(rf[s2][n], vf, tk[n]);
+            tv[n] = EL::mma(rt[s2][n], kf, tv[n]);
+          }
+        }
+        const float wk = f * e2c[sk];
+#pragma unroll
+        for (int n = 0; n < NCB; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ak[kb][n][i] += wk * tk[n][i];
+            av[kb][n][i] += wk * tv[n][i];
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    for (int base = 0; base < n_lev; base += NPRE) {
+#pragma unroll
+      for (int u = 0; u < NPRE; ++u) {
+        const int li = base + u;
+        if (li >= n_lev) break;
+        contract(li, rf[u], rt[u]);
+        if (li + NPRE < n_lev) load_node(li + NPRE, rf[u], rt[u]);
+      }
+    }
+    // this wave's share of v_s . dv_s, then the rows of dk and dv
+#pragma unroll
+    for (int kb = 0; kb < QB; ++kb) {
+      const int sk = 16 * kb + lr;
+      float cs = 0.f;
+#pragma unroll
+      for (int n = 0; n < NCB; ++n) {
+        const E* vrow = Vs + sk * lay.ld_row + 16 * (cb0 + n) + 4 * lq;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cs += av[kb][n][i] * EL::to_f32(vrow[i]);
+      }
+      cs += __shfl_xor(cs, 16, 64);
+      cs += __shfl_xor(cs, 32, 64);
+      if (lq == 0) colS[w * C + sk] = cs;
+      if (sk < nv) {
+        E* ok = reinterpret_cast<E*>(a.dk) + (bh * T + tc + sk) * D + 4 * lq;
+        E* ov = reinterpret_cast<E*>(a.dv) + (bh * T + tc + sk) * D + 4 * lq;
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) {
+          store4<BF16>(ok + 16 * (cb0 + n), ak[kb][n]);
+          store4<BF16>(ov + 16 * (cb0 + n), av[kb][n]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < nv) {
+    float cs = 0.f;
+    for (int u = 0; u < SH::NWA; ++u) cs += colS[u * C + tid];
+    a.dcol[bh * T + tc + tid] = cs;
   }
 }
 
@@ -851,8 +1069,11 @@ int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s) {
     ok = ok && hipGetLastError() == hipSuccess;
   }
   if (p.n_groups > 1) {
-    const int nblk = (D * D + 255) / 256;
-    hipLaunchKernelGGL((bwd_rev_tree<BF16>), dim3((unsigned)(p.BH * (p.n_groups - 1) * nblk)), dim3(256), 0, s, a, D);
+    const int lds_t = D * (D + 4 / (int)sizeof(E)) * (int)sizeof(E);
+    ok = ok && hipFuncSetAttribute((const void*)bwd_rev_tree<BF16>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   lds_t) == hipSuccess;
+    if (!ok) return kEHIP;
+    hipLaunchKernelGGL((bwd_rev_tree<BF16>), dim3((unsigned)(p.BH * (p.n_groups - 1))), dim3(256), lds_t, s, a, D);
     ok = ok && hipGetLastError() == hipSuccess;
   }
   ok = ok && hipFuncSetAttribute((const void*)bwd_chunk_dkv<BF16, C, D>, hipFuncAttributeMaxDynamicSharedMemorySize,

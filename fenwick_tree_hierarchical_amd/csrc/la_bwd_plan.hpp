@@ -8,37 +8,56 @@
 
 namespace la {
 
-// bwd_chunk_dq and bwd_chunk_dkv: one workgroup per (b,h, chunk), one wave per
-// 16-row block of the chunk.
-LA_HD constexpr int bwd_waves(int C) { return C / 16; }
+// bwd_chunk_dq and bwd_chunk_dkv: one workgroup per (b,h, chunk) of the
+// forward output kernel's wave count.
+LA_HD constexpr int bwd_waves(int C) { return output_waves(C); }
 
 // LDS of the two per-chunk kernels.  Q, K, V and dout tiles are row-major with
-// rows padded by 16 bytes; the score-gradient tiles hold C x C entries
-// (bwd_chunk_dq: dS by query row; bwd_chunk_dkv: P^T and dS^T by key row);
-// lam holds the chunk's lambda rows, dl the lambda gradients being formed,
-// nd one reverse node (bwd_chunk_dkv), b2/e2 gate prefixes.
+// rows padded by 16 bytes; lam holds the chunk's lambda rows, b2 the
+// in-chunk gate prefix.
+//  bwd_chunk_dq: once the score tiles are formed, Q and V are dead: dS (by
+//  query row) goes over V and the per-tile row sums of the lambda gradients
+//  inside the chunk (part) over Q; after dq's intra-chunk product each wave's
+//  share of the level gradients above the chunk (inter) goes over K and dS
+//  when it fits; the finished lambda gradients (dl) go over dout.
+//  bwd_chunk_dkv: dS^T and then P^T (by key row) in a region of their own
+//  (s0), each wave's share of v . dv (col), and e2 the gate from each key to
+//  the chunk end.
 struct BwdChunkLds {
-  int q, k, v, g, s0, s1, lam, dl, nd, b2, e2, total, ld_row, ld_s, ld_nd;
+  int q, k, v, g, s0, lam, part, inter, dl, col, b2, e2, total, ld_row, ld_s;
 };
 LA_HD constexpr BwdChunkLds bwd_chunk_lds(int C, int D, int es, int L, bool key_side) {
   BwdChunkLds o{};
+  const int NW = bwd_waves(C);
+  const int log2c = ilog2(C);
   o.ld_row = D + 16 / es;
   o.ld_s = C + 16 / es;
-  o.ld_nd = D + 16 / es;
   const int tile = (C * o.ld_row * es + 255) / 256 * 256;
   const int stile = (C * o.ld_s * es + 255) / 256 * 256;
+  const int vtile = key_side ? tile : (tile > stile ? tile : stile);
   int off = 0;
   o.q = off;  off += tile;
   o.k = off;  off += tile;
-  o.v = off;  off += tile;
+  o.v = off;  off += vtile;
   o.g = off;  off += tile;
-  o.s0 = off; off += stile;
-  o.s1 = off; off += key_side ? stile : 0;
   o.lam = off; off += (C * L * 4 + 255) / 256 * 256;
-  o.dl = off;  off += key_side ? 0 : (C * L * 4 + 255) / 256 * 256;
-  o.nd = off;  off += key_side ? (D * o.ld_nd * es + 255) / 256 * 256 : 0;
   o.b2 = off;  off += (C * 4 + 255) / 256 * 256;
-  o.e2 = off;  off += (C * 4 + 255) / 256 * 256;
+  if (key_side) {
+    o.s0 = off; off += stile;
+    o.col = off; off += (NW * C * 4 + 255) / 256 * 256;
+    o.e2 = off;  off += (C * 4 + 255) / 256 * 256;
+    o.part = o.inter = o.dl = -1;
+  } else {
+    o.s0 = o.v;
+    o.part = o.q;          // fits: at most C/16 (C/16 + 1) / 2 * 64 + C/16 * 320 bytes
+    o.inter = o.k;
+    const int n_inter = L - log2c - 1 > 0 ? L - log2c - 1 : 0;
+    const int inter_b = NW * n_inter * C * 4;
+    if (inter_b > tile + vtile) { o.inter = off; off += (inter_b + 255) / 256 * 256; }
+    o.dl = o.g;
+    if (C * L * 4 > tile) { o.dl = off; off += (C * L * 4 + 255) / 256 * 256; }
+    o.col = o.e2 = -1;
+  }
   o.total = off;
   return o;
 }
@@ -67,6 +86,7 @@ struct BwdPlan {
   int JG = 0;                // group levels that have an upper block (bit length of n_groups - 1)
   int lds_dq = 0, lds_dkv = 0, lds_rev = 0;
   size_t off_rnodes_in = 0, off_rpart = 0, off_rnodes = 0, off_dcol = 0, ws_bytes = 0;
+  size_t off_rnodes_in_t = 0, off_rnodes_t = 0;   // the same nodes transposed, (d_v, d_k)
 };
 
 // Shape checks and the plan of the backward.  The forward's envelope, with
@@ -93,11 +113,13 @@ inline int plan_bwd(int B, int H, int64_t T, int dk, int dv, int C, int dtype, i
   const size_t DD = (size_t)dk * dv;
   size_t off = f.ws_bytes;
   if (f.n_chunks > 1) {
-    P.off_rnodes_in = off; off = align_up(off + (size_t)f.BH * f.n_chunks * DD * f.es, 256);
+    P.off_rnodes_in = off;   off = align_up(off + (size_t)f.BH * f.n_chunks * DD * f.es, 256);
+    P.off_rnodes_in_t = off; off = align_up(off + (size_t)f.BH * f.n_chunks * DD * f.es, 256);
   }
   if (f.n_groups > 1) {
     P.off_rpart = off;  off = align_up(off + (size_t)f.BH * f.n_groups * P.JG * DD * 4, 256);
-    P.off_rnodes = off; off = align_up(off + (size_t)f.BH * f.n_groups * DD * f.es, 256);
+    P.off_rnodes = off;   off = align_up(off + (size_t)f.BH * f.n_groups * DD * f.es, 256);
+    P.off_rnodes_t = off; off = align_up(off + (size_t)f.BH * f.n_groups * DD * f.es, 256);
   }
   P.off_dcol = off; off = align_up(off + (size_t)f.BH * T * 4, 256);
   P.ws_bytes = off;
