@@ -239,10 +239,8 @@ LA_API int loglinear_bwd_workspace(int B, int H, int64_t T, int dk, int dv, int 
  *   grad_lambda  [B, H, T, L]   float32   written (every entry)
  * The outputs must not overlap the inputs or each other.
  *
- * Supported: the shapes loglinear_fwd accepts with C in {16, 32, 64} whose
- * tiles fit the 160 KB of LDS (every bfloat16 shape; float32 with
- * dk = 128 needs C <= 32); others return LA_ESHAPE, and
- * loglinear_bwd_workspace answers the same.  The chunk size only changes the
+ * Supported: the shapes loglinear_fwd accepts with C in {16, 32, 64} (C = 128
+ * returns LA_ESHAPE, and loglinear_bwd_workspace answers the same).  The chunk size only changes the
  * summation order, so a backward may use another C than its forward.
  * workspace: at least loglinear_bwd_workspace() bytes, 256-byte aligned.
  * Errors as loglinear_fwd.

@@ -206,18 +206,18 @@ def test_bwd_workspace_query():
     rc, n = bws(8, 16, 16384, 64, 64)
     assert rc == OK
     fwd_part = ws(8, 16, 16384, 64, 64)[1]
-    # forward structure, key-side chunk nodes (bf16), group shares (fp32,
-    # 5 group levels for 32 groups) and group nodes, column terms
+    # forward structure, key-side chunk nodes (bf16, and transposed), group
+    # shares (fp32, 5 group levels for 32 groups), group nodes (and
+    # transposed), column terms
     BH, nch, ng, DD = 128, 256, 32, 64 * 64
-    need = fwd_part + BH * nch * DD * 2 + BH * ng * 5 * DD * 4 + BH * ng * DD * 2 + BH * 16384 * 4
+    need = fwd_part + 2 * BH * nch * DD * 2 + BH * ng * 5 * DD * 4 + 2 * BH * ng * DD * 2 + BH * 16384 * 4
     assert need <= n < need * 1.01
     assert bws(2, 3, 50, 64, 64)[1] == 1280              # one partial chunk: 2*3*50 column terms, 256-aligned
     assert bws(1, 1, 64, 64, 128)[0] == ESHAPE              # chunks above 64
-    assert bws(1, 1, 1000, 128, 64, 0)[0] == ESHAPE         # float32 tiles of 64 x 128 exceed the LDS
-    assert bws(1, 1, 1000, 128, 32, 0)[0] == OK
-    for d in (16, 32, 64, 128):
-        for C in (16, 32, 64):
-            assert bws(1, 1, 1000, d, C, 1)[0] == OK, (d, C)
+    for dt in (0, 1):
+        for d in (16, 32, 64, 128):
+            for C in (16, 32, 64):
+                assert bws(1, 1, 1000, d, C, dt)[0] == OK, (dt, d, C)
     assert bws(0, 4, 100, 64, 64)[1] == 0
     assert L.loglinear_bwd_workspace(1, 1, 64, 64, 64, 64, 1, None) == EINVAL
 
