@@ -181,3 +181,35 @@ def test_train_16k_full_size_sampled():
         err = rel_l2(got, ref[name])
         say(f"   {name} rel_l2={err:.3e}")
         assert err <= TOL["bf16"], name
+
+
+def test_long_128k_full_size_sampled():
+    """The long-context shape (one batch, 16 heads, T = 131072, d = 128) with
+    chunks of 64 in the backward: weak decay so that the group levels carry
+    the gradients; one head at sampled query and key rows against the oracle,
+    and the homogeneity identity q_t . dq_t = dout_t . o_t on every head."""
+    dev = need_gpu()
+    import fenwick_tree_hierarchical_amd as la
+    w = WORKLOADS["long_128k_bf16"]
+    say("bwd full size long_128k_bf16: drawing inputs")
+    x = make_inputs(w, device=dev, variant="weak_decay")
+    dout = make_grad_out(w, device=dev)
+    say("bwd full size long_128k_bf16: backward (C = 64)")
+    dq, dk, dv, dla, dlam = la.loglinear_bwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], dout, chunk=64)
+    out = la.loglinear_fwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], chunk=w.C)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv, dla, dlam):
+        assert torch.isfinite(t.float()).all().item()
+    row = (dout.float() * out.float()).sum(-1)
+    assert rel_l2((x["q"].float() * dq.float()).sum(-1).cpu().numpy(), row.cpu().numpy()) <= TOL["bf16"]
+    rows = np.array([0, 63, 64, 4095, 4096, 65535, 65536, 98304, 131000, 131071])
+    idx = [(0, 11)]
+    sub = to_cpu(heads(x, idx))
+    dsub = torch.stack([dout[b, h] for b, h in idx])[None].cpu()
+    say("bwd full size long_128k_bf16: oracle at sampled rows")
+    ref = backward.backward_sampled(sub["q"], sub["k"], sub["v"], sub["log_a"], sub["lam"], dsub, rows)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dlam", dlam)):
+        got = torch.stack([t[b, h, rows] for b, h in idx])[None].float().cpu().numpy()
+        err = rel_l2(got, ref[name])
+        say(f"   {name} rel_l2={err:.3e}")
+        assert err <= TOL["bf16"], name
