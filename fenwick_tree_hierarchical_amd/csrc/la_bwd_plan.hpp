@@ -29,7 +29,8 @@ struct BwdChunkLds {
 LA_HD constexpr BwdChunkLds bwd_chunk_lds(int C, int D, int es, int L, bool key_side) {
   BwdChunkLds o{};
   const int NW = bwd_waves(C);
-  const int log2c = ilog2(C);
+  int log2c = 0;
+  for (int c = C; c > 1; c >>= 1) ++log2c;
   o.ld_row = D + 16 / es;
   o.ld_s = C + 16 / es;
   const int tile = (C * o.ld_row * es + 255) / 256 * 256;
