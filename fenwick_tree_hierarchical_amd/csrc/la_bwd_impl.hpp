@@ -624,35 +624,41 @@ __global__ __launch_bounds__(64 * state_waves(D)) void bwd_rev_states(BwdArgs a)
 // bwd_rev_tree: the key-side node of every block of groups that is the upper
 // half of its level block: it starts at group x >= 1 and spans 2^ctz(x)
 // groups; the sum of those groups' shares, each carried by the gate from the
-// block start to the group start.  One workgroup per node: R is written
-// row-major, then read back from LDS by columns (rows padded by one 4-byte
-// word, so a column read is spread over the banks) and written as R^T.
+// block start to the group start.  One workgroup per band of 16 rows of one
+// node: the band is written as rows of R, and through LDS (rows padded by
+// one 4-byte word) as 16-element runs of the columns of R^T.
 template <bool BF16>
 __global__ __launch_bounds__(256) void bwd_rev_tree(BwdArgs a, int D) {
   using EL = Elem<BF16>;
   using E = typename EL::T;
-  extern __shared__ __align__(16) unsigned char smem[];
-  E* tr = reinterpret_cast<E*>(smem);
+  __shared__ E tr[16 * (128 + 4 / sizeof(E))];
   const int ld = D + 4 / (int)sizeof(E);
-  const int DD = D * D;
+  const int DD = D * D, nband = D / 16;
   const int64_t ng = a.n_groups;
-  const int64_t bh = blockIdx.x / (ng - 1), x = 1 + blockIdx.x % (ng - 1);
+  const int64_t node = blockIdx.x / nband;
+  const int band = blockIdx.x % nband;
+  const int64_t bh = node / (ng - 1), x = 1 + node % (ng - 1);
   const int i = __builtin_ctzll((unsigned long long)x);     // block of 2^i groups, group level i + 1
   const int64_t end = x + (1ll << i) < ng ? x + (1ll << i) : ng;
   const double* gp = a.gprefix + bh * (ng + 1);
   const double base = gp[x];
   E* R = reinterpret_cast<E*>(a.rnodes) + (bh * ng + x) * DD;
   E* RT = reinterpret_cast<E*>(a.rnodes_t) + (bh * ng + x) * DD;
-  for (int e = threadIdx.x; e < DD; e += 256) {
+  const int e0 = band * 16 * D;                             // first element of the band
+  for (int e = threadIdx.x; e < 16 * D; e += 256) {
     float acc = 0.f;
     for (int64_t g = x; g < end; ++g)
-      acc += __builtin_amdgcn_exp2f((float)(gp[g] - base)) * a.rpart[((bh * ng + g) * a.JG + i) * DD + e];
+      acc += __builtin_amdgcn_exp2f((float)(gp[g] - base)) * a.rpart[((bh * ng + g) * a.JG + i) * DD + e0 + e];
     const E val = EL::from_f32(acc);
-    R[e] = val;
+    R[e0 + e] = val;
     tr[(e / D) * ld + e % D] = val;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < DD; e += 256) RT[e] = tr[(e % D) * ld + e / D];
+  // R^T row j, columns band*16 .. band*16 + 15
+  for (int e = threadIdx.x; e < 16 * D; e += 256) {
+    const int j = e / 16, r = e % 16;
+    RT[(int64_t)j * D + band * 16 + r] = tr[r * ld + j];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1069,11 +1075,8 @@ int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s) {
     ok = ok && hipGetLastError() == hipSuccess;
   }
   if (p.n_groups > 1) {
-    const int lds_t = D * (D + 4 / (int)sizeof(E)) * (int)sizeof(E);
-    ok = ok && hipFuncSetAttribute((const void*)bwd_rev_tree<BF16>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   lds_t) == hipSuccess;
-    if (!ok) return kEHIP;
-    hipLaunchKernelGGL((bwd_rev_tree<BF16>), dim3((unsigned)(p.BH * (p.n_groups - 1))), dim3(256), lds_t, s, a, D);
+    hipLaunchKernelGGL((bwd_rev_tree<BF16>), dim3((unsigned)(p.BH * (p.n_groups - 1) * (D / 16))), dim3(256), 0, s, a,
+                       D);
     ok = ok && hipGetLastError() == hipSuccess;
   }
   ok = ok && hipFuncSetAttribute((const void*)bwd_chunk_dkv<BF16, C, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
