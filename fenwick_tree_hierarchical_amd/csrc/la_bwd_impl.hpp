@@ -199,7 +199,6 @@ void bwd_chunk_dq(BwdArgs a) {
   float* partO = reinterpret_cast<float*>(smem + lay.part);    // [tile][16]: off-diagonal tile row sums
   float* partD = partO + SH::NST * 16;                         // [row block][16][5]: diagonal tile levels 0..4
   float* inter = reinterpret_cast<float*>(smem + lay.inter);   // [wave][level - log2 C - 1][row]
-  float* dlS = reinterpret_cast<float*>(smem + lay.dl);        // [row][level]
   float* b2c = reinterpret_cast<float*>(smem + lay.b2);
 
   const int64_t nc = a.n_chunks, ng = a.n_groups, T = a.T;
@@ -462,32 +461,39 @@ void bwd_chunk_dq(BwdArgs a) {
       }
     }
   }
-  __syncthreads();                                 // dout no longer read: dl goes over it
+  __syncthreads();
   // lambda gradients of the chunk's rows: levels 0..4 from the diagonal
   // tiles, 5..log2 C from the earlier tiles of the row block, the rest from
-  // the waves' shares; levels with an empty bucket are zero
-  for (int idx = tid; idx < C * L; idx += SH::NT) {
-    const int r = idx / L, lv = idx % L;
+  // the waves' shares; levels with an empty bucket are zero.  Four threads
+  // per row, each with a quarter of the levels: they write their entries
+  // straight out and add up the row term sum_l lambda_t^l dlambda_t^l with
+  // two shuffles.
+  static_assert(SH::NT >= 4 * C, "four threads per row");
+  {
+    const int r = tid >> 2, part = tid & 3;
+    const int per = (L + 3) >> 2;
     const int rb = r >> 4, rr = r & 15;
-    float val = 0.f;
-    if (lv <= 4 && lv <= LOG2C) {
-      val = partD[(rb * 16 + rr) * 5 + lv];
-    } else if (lv <= LOG2C) {
-      for (int kb = 0; kb < rb; ++kb)
-        if (5 + (31 - __builtin_clz((unsigned)(rb ^ kb))) == lv) val += partO[(rb * (rb + 1) / 2 + kb) * 16 + rr];
-    } else if ((occm >> lv) & 1u) {
-      for (int u = 0; u < SH::NWA; ++u) val += inter[(u * NI + (lv - LOG2C - 1)) * C + r];
-    }
-    dlS[idx] = val;
-  }
-  __syncthreads();
-  if (tid < nv) {
     float rt = 0.f;
-    for (int u = 0; u < L; ++u) rt += lamS[tid * L + u] * dlS[tid * L + u];
-    a.dlog_a[bh * T + tc + tid] = rt;
+    float* dl = a.dlam + (bh * T + tc + r) * L;
+    if (r < C) {
+      for (int lv = part * per; lv < L && lv < (part + 1) * per; ++lv) {
+        float val = 0.f;
+        if (lv <= 4 && lv <= LOG2C) {
+          val = partD[(rb * 16 + rr) * 5 + lv];
+        } else if (lv <= LOG2C) {
+          for (int kb = 0; kb < rb; ++kb)
+            if (5 + (31 - __builtin_clz((unsigned)(rb ^ kb))) == lv) val += partO[(rb * (rb + 1) / 2 + kb) * 16 + rr];
+        } else if ((occm >> lv) & 1u) {
+          for (int u = 0; u < SH::NWA; ++u) val += inter[(u * NI + (lv - LOG2C - 1)) * C + r];
+        }
+        rt += lamS[r * L + lv] * val;
+        if (r < nv) dl[lv] = val;
+      }
+    }
+    rt += __shfl_xor(rt, 1, 64);
+    rt += __shfl_xor(rt, 2, 64);
+    if (r < nv && part == 0) a.dlog_a[bh * T + tc + r] = rt;
   }
-  float* dl = a.dlam + (bh * T + tc) * L;
-  for (int idx = tid; idx < nv * L; idx += SH::NT) dl[idx] = dlS[idx];
 }
 
 // ---------------------------------------------------------------------------

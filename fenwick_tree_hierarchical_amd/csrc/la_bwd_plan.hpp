@@ -19,12 +19,12 @@ LA_HD constexpr int bwd_waves(int C) { return output_waves(C); }
 //  query row) goes over V and the per-tile row sums of the lambda gradients
 //  inside the chunk (part) over Q; after dq's intra-chunk product each wave's
 //  share of the level gradients above the chunk (inter) goes over K and dS
-//  when it fits; the finished lambda gradients (dl) go over dout.
+//  when it fits.
 //  bwd_chunk_dkv: dS^T and then P^T (by key row) in a region of their own
 //  (s0), each wave's share of v . dv (col), and e2 the gate from each key to
 //  the chunk end.
 struct BwdChunkLds {
-  int q, k, v, g, s0, lam, part, inter, dl, col, b2, e2, total, ld_row, ld_s;
+  int q, k, v, g, s0, lam, part, inter, col, b2, e2, total, ld_row, ld_s;
 };
 LA_HD constexpr BwdChunkLds bwd_chunk_lds(int C, int D, int es, int L, bool key_side) {
   BwdChunkLds o{};
@@ -47,7 +47,7 @@ LA_HD constexpr BwdChunkLds bwd_chunk_lds(int C, int D, int es, int L, bool key_
     o.s0 = off; off += stile;
     o.col = off; off += (NW * C * 4 + 255) / 256 * 256;
     o.e2 = off;  off += (C * 4 + 255) / 256 * 256;
-    o.part = o.inter = o.dl = -1;
+    o.part = o.inter = -1;
   } else {
     o.s0 = o.v;
     o.part = o.q;          // fits: at most C/16 (C/16 + 1) / 2 * 64 + C/16 * 320 bytes
@@ -55,8 +55,6 @@ LA_HD constexpr BwdChunkLds bwd_chunk_lds(int C, int D, int es, int L, bool key_
     const int n_inter = L - log2c - 1 > 0 ? L - log2c - 1 : 0;
     const int inter_b = NW * n_inter * C * 4;
     if (inter_b > tile + vtile) { o.inter = off; off += (inter_b + 255) / 256 * 256; }
-    o.dl = o.g;
-    if (C * L * 4 > tile) { o.dl = off; off += (C * L * 4 + 255) / 256 * 256; }
     o.col = o.e2 = -1;
   }
   o.total = off;

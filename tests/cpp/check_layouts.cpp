@@ -49,9 +49,6 @@ int main() {
           const int inter_b = NW * ninter * C * 4;
           if (q.inter == q.k) CHECK(inter_b <= q.g - q.k, "shares over K and dS: C=%d D=%d L=%d", C, D, L);
           else CHECK(q.inter >= q.b2 + C * 4 && q.inter + inter_b <= q.total, "own shares region: C=%d D=%d L=%d", C, D, L);
-          if (q.dl == q.g) CHECK(C * L * 4 <= tile, "dl over dout: C=%d D=%d L=%d", C, D, L);
-          else CHECK(q.dl + C * L * 4 <= q.total && disjoint(q.dl, q.dl + C * L * 4, q.inter, q.inter + inter_b),
-                     "own dl region: C=%d D=%d L=%d", C, D, L);
           CHECK(q.g + tile <= q.lam && q.lam + C * L * 4 <= q.b2 && q.b2 + C * 4 <= q.total, "C=%d D=%d L=%d", C, D, L);
           CHECK((q.ld_row * es) % 16 == 0 && (q.ld_s * es) % 16 == 0, "row alignment C=%d D=%d", C, D);
           // backward, key side: every region live at once is disjoint

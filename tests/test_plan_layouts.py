@@ -4,7 +4,7 @@ tests/cpp/check_layouts.cpp includes the plan headers the kernels use and
 checks, for every tile shape, dtype and level count, that each region fits,
 that regions which are live at the same time do not overlap, that the
 overlays (dS over V, the lambda row sums over Q, the level shares over K and
-dS, the finished lambda gradients over dout) fit the tile they reuse, and
+dS) fit the tile they reuse, and
 that the backward workspace regions are ordered, aligned and sized.
 """
 
