@@ -25,6 +25,11 @@ lambda stay float32.
 The backward pass also takes the gradient of the loss with respect to the
 output, ``make_grad_out``: dout ~ N(0, 1) over [B, H, T, d_v], drawn from its
 own generator seeded with the workload seed + 1000, in the layer dtype.
+
+The Gated DeltaNet form also takes a per-token write strength, ``make_beta``:
+beta = sigmoid(x), x ~ N(0, 1) over [B, H, T], float32, from its own generator
+seeded with the workload seed + 2000 (the gated delta rule's beta lies in
+(0, 1)); its keys are the workload's L2-normalised k.
 """
 
 from __future__ import annotations
@@ -133,3 +138,14 @@ def make_grad_out(w: Workload, device="cpu", B=None, H=None, T=None, seed: int |
     g.manual_seed((w.seed if seed is None else seed) + 1000)
     dout = torch.randn(B, H, T, dv, device=device, dtype=torch.float32, generator=g)
     return dout.to(torch_dtype(w.dtype if dtype is None else dtype)).contiguous()
+
+
+def make_beta(w: Workload, device="cpu", B=None, H=None, T=None, seed: int | None = None):
+    """Seeded write strengths beta [B, H, T] = sigmoid(N(0, 1)), float32."""
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    T = w.T if T is None else T
+    g = torch.Generator(device=device)
+    g.manual_seed((w.seed if seed is None else seed) + 2000)
+    x = torch.randn(B, H, T, device=device, dtype=torch.float32, generator=g)
+    return torch.sigmoid(x).contiguous()

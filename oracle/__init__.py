@@ -44,4 +44,4 @@ level reading above is an interpretation of the pages, which print no formula
 for it.
 """
 
-from . import levels, forms, special, metrics, backward  # noqa: F401
+from . import levels, forms, special, metrics, backward, deltanet  # noqa: F401
