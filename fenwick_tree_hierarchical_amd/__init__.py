@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "LogAttnError", "lib", "loglinear_fwd", "loglinear_fwd_workspace", "loglinear_fwd_num_stages",
     "loglinear_fwd_staged", "loglinear_bwd", "loglinear_bwd_workspace", "LogLinearState", "loglinear_state_init", "loglinear_decode_step",
-    "loglinear_level_table", "loglinear_strerror", "LA_F32", "LA_BF16",
+    "loglinear_level_table", "loglinear_strerror", "loglinear_gdn_fwd", "loglinear_gdn_fwd_workspace",
+    "LA_F32", "LA_BF16",
 ]
 
 LA_F32, LA_BF16 = 0, 1
@@ -48,6 +49,8 @@ _SIGS = {
     "loglinear_state_init": ([ctypes.POINTER(_LaState), _i, _i, _i, _i, _i, _p, _p, _p], _i),
     "loglinear_decode_step": ([ctypes.POINTER(_LaState), _p, _p, _p, _p, _p, _p, _i, _p], _i),
     "loglinear_level_table": ([_i64, _i, _p, _p], _i),
+    "loglinear_gdn_fwd_workspace": ([_i, _i, _i64, _i, _i, _i, _i, ctypes.POINTER(_sz)], _i),
+    "loglinear_gdn_fwd": ([_p, _p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
 }
 
 
@@ -167,6 +170,44 @@ def loglinear_fwd_staged(q, k, v, log_a, lam, events, out=None, chunk: int = 64,
             e.record(s)
     arr = (_p * len(events))(*[e.cuda_event for e in events])
     _check(lib().loglinear_fwd_staged(*args, arr, len(events), s.cuda_stream), "loglinear_fwd_staged")
+    return out
+
+
+def loglinear_gdn_fwd_workspace(B: int, H: int, T: int, dk: int, dv: int, C: int, dtype: torch.dtype) -> int:
+    n = _sz(0)
+    _check(lib().loglinear_gdn_fwd_workspace(B, H, T, dk, dv, C, _dtype_code(dtype), ctypes.byref(n)),
+           "loglinear_gdn_fwd_workspace")
+    return n.value
+
+
+def loglinear_gdn_fwd(q, k, v, log_a, beta, lam, out=None, chunk: int = 64, workspace=None):
+    """Log-linear Gated DeltaNet forward for every (batch, head).
+
+    q, k: [B,H,T,dk]; v: [B,H,T,dv] (float32 or bfloat16); log_a, beta:
+    [B,H,T] float32; lam: [B,H,T,L] float32.  Returns out [B,H,T,dv] in q's
+    dtype.
+    """
+    dev = _dev(q, k, v, log_a, beta, lam)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or log_a.shape != (B, H, T) or \
+            beta.shape != (B, H, T) or lam.shape[:3] != (B, H, T):
+        raise ValueError("shape mismatch between q, k, v, log_a, beta and lambda")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if log_a.dtype != torch.float32 or beta.dtype != torch.float32 or lam.dtype != torch.float32:
+        raise TypeError("log_a, beta and lambda must be float32")
+    if out is None:
+        out = torch.empty(B, H, T, dv, dtype=q.dtype, device=dev)
+    _dev(q, out)
+    if out.shape != (B, H, T, dv) or out.dtype != q.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    nws = loglinear_gdn_fwd_workspace(B, H, T, dk, dv, chunk, q.dtype)
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    _check(lib().loglinear_gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta), _ptr(lam), _ptr(out),
+                                   B, H, T, dk, dv, chunk, lam.shape[-1], _dtype_code(q.dtype),
+                                   _ptr(workspace), workspace.numel(), _stream(dev)), "loglinear_gdn_fwd")
     return out
 
 

@@ -5,6 +5,7 @@
 #include "../../include/logattn.h"
 #include "la_bwd_impl.hpp"
 #include "la_fwd_impl.hpp"
+#include "la_gdn_impl.hpp"
 #include "la_internal.hpp"
 #include "la_plan.hpp"
 
@@ -193,6 +194,43 @@ LA_API int loglinear_bwd(const void* q, const void* k, const void* v, const floa
   a.T = T; a.n_chunks = p.n_chunks; a.n_groups = p.n_groups; a.L = L; a.JG = P.JG;
   hipStream_t s = (hipStream_t)stream;
   return dtype == kBF16 ? launch_bwd_bf16(P, fa, a, s) : launch_bwd_f32(P, fa, a, s);
+}
+
+LA_API int loglinear_gdn_fwd_workspace(int B, int H, int64_t T, int dk, int dv, int C, int dtype,
+                                       size_t* bytes) {
+  if (!bytes) return kEINVAL;
+  GdnPlan p;
+  int rc = plan_gdn(B, H, T, dk, dv, C, dtype, -1, &p);
+  if (rc != kOK) return rc;
+  *bytes = p.ws_bytes;
+  return kOK;
+}
+
+LA_API int loglinear_gdn_fwd(const void* q, const void* k, const void* v, const float* log_a,
+                             const float* beta, const float* lambda, void* out, int B, int H, int64_t T,
+                             int dk, int dv, int C, int L, int dtype, void* workspace,
+                             size_t workspace_bytes, la_stream_t stream) {
+  GdnPlan p;
+  int rc = plan_gdn(B, H, T, dk, dv, C, dtype, L, &p);
+  if (rc != kOK) return rc;
+  if (p.BH == 0 || T == 0) return kOK;   // empty problem: nothing to read or write
+  if (!q || !k || !v || !log_a || !beta || !lambda || !out) return kEINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return kEALIGN;
+  if (!aligned(log_a, 4) || !aligned(beta, 4) || !aligned(lambda, 4)) return kEALIGN;
+  if (p.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < p.ws_bytes) return kEWORKSPACE;
+    if (!aligned(workspace, 256)) return kEALIGN;
+  }
+  char* w = static_cast<char*>(workspace);
+  GdnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.log_a = log_a; a.beta = beta; a.lam = lambda; a.out = out;
+  a.pt = p.n_nodes > 0 ? reinterpret_cast<float*>(w + p.off_pt) : nullptr;
+  a.psit = p.n_nodes > 0 ? reinterpret_cast<float*>(w + p.off_psit) : nullptr;
+  a.gn = p.n_nodes > 0 ? reinterpret_cast<float*>(w + p.off_gn) : nullptr;
+  a.T = T; a.n_chunks = p.n_chunks; a.n_full = p.n_full; a.L = L;
+  for (int m = 0; m < kGdnMaxTree; ++m) a.lev_off[m] = p.lev_off[m];
+  hipStream_t s = (hipStream_t)stream;
+  return dtype == kBF16 ? launch_gdn_bf16(p, a, s) : launch_gdn_f32(p, a, s);
 }
 
 LA_API int loglinear_state_bytes(int B, int H, int dk, int dv, int S, size_t* slot_bytes,

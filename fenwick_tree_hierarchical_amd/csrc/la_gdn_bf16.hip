@@ -1,0 +1,7 @@
+// bf16 instantiations of the log-linear Gated DeltaNet forward kernels.
+#include "la_gdn_impl.hpp"
+#include "la_internal.hpp"
+
+namespace la {
+int launch_gdn_bf16(const GdnPlan& p, const GdnArgs& a, hipStream_t s) { return launch_gdn_dtype<true>(p, a, s); }
+}  // namespace la

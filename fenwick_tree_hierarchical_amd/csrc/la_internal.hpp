@@ -6,12 +6,14 @@
 
 #include "../../include/logattn.h"
 #include "la_bwd_plan.hpp"
+#include "la_gdn_plan.hpp"
 #include "la_plan.hpp"
 
 namespace la {
 
 struct FwdArgs;
 struct BwdArgs;
+struct GdnArgs;
 
 // Forward: enqueue the stages of `p` on stream s; ev (nullable) holds
 // p.n_stages + 1 events recorded around the stages.
@@ -22,6 +24,10 @@ int launch_fwd_f32(const FwdPlan& p, const FwdArgs& a, hipStream_t s, hipEvent_t
 // buffers over (k := v, v := k).
 int launch_bwd_bf16(const BwdPlan& p, const FwdArgs& fa, const BwdArgs& a, hipStream_t s);
 int launch_bwd_f32(const BwdPlan& p, const FwdArgs& fa, const BwdArgs& a, hipStream_t s);
+
+// Log-linear Gated DeltaNet forward: enqueue its kernels on stream s.
+int launch_gdn_bf16(const GdnPlan& p, const GdnArgs& a, hipStream_t s);
+int launch_gdn_f32(const GdnPlan& p, const GdnArgs& a, hipStream_t s);
 
 int launch_decode(const la_state* st, const void* q, const void* k, const void* v, const float* a,
                   const float* lam, void* out, int dtype, int kstar, hipStream_t s);

@@ -251,6 +251,43 @@ LA_API int loglinear_bwd(const void* q, const void* k, const void* v, const floa
                          int dk, int dv, int C, int L, int dtype, void* workspace,
                          size_t workspace_bytes, la_stream_t stream);
 
+/* Workspace size for loglinear_gdn_fwd (host only); errors as loglinear_gdn_fwd. */
+LA_API int loglinear_gdn_fwd_workspace(int B, int H, int64_t T, int dk, int dv, int C, int dtype,
+                                       size_t* bytes);
+
+/*
+ * Log-linear Gated DeltaNet forward: the Fenwick-bucket structure laid over
+ * the gated delta rule ("Log-Linear Attention", both summaries, technical
+ * summary section 2, the second of the two variants).  Every bucket state
+ * follows the gated delta rule's transition A_r = a_r (I - beta_r k_r k_r^T),
+ * a_r = exp(log_a[r]), a key enters its bucket as beta_s k_s v_s^T, and the
+ * output is the lambda-weighted sum of the buckets.  Per (b, h):
+ *   out[t] = sum_{s<=t} lambda[t, l(t,s)] beta_s (q_t^T Phi(t,s) k_s) v_s,
+ *   Phi(t,s) = A_t A_{t-1} ... A_{s+1}  (the identity for s = t),
+ * with l(t,s) the Fenwick level of loglinear_fwd.  lambda constant reduces it
+ * to the gated delta rule; with keys that never overlap it is loglinear_fwd
+ * with values beta v.
+ *
+ *   q, k     [B, H, T, dk]  dtype     16-byte aligned; the delta rule
+ *                                     expects unit-norm keys (not checked)
+ *   v, out   [B, H, T, dv]  dtype     16-byte aligned; out is written
+ *   log_a    [B, H, T]      float32   log of the gate (<= 0 expected)
+ *   beta     [B, H, T]      float32   write strength, in [0, 1] expected
+ *   lambda   [B, H, T, L]   float32   L >= ceil(log2 T) + 1
+ *   C        chunk size, 16, 32 or 64; dk = dv in {16, 32, 64}
+ *   workspace at least loglinear_gdn_fwd_workspace() bytes, 256-byte
+ *            aligned (one fp32 state and one fp32 transition per aligned
+ *            block of 2^m full chunks); owned by the caller
+ * Asynchronous on `stream`; every check happens on the host before any
+ * launch, and on error nothing is written.  Errors: LA_EINVAL (null pointer,
+ * negative count), LA_ESHAPE (dims, C, L, size limits), LA_EDTYPE,
+ * LA_EALIGN, LA_EWORKSPACE, LA_EHIP (launch failure).
+ */
+LA_API int loglinear_gdn_fwd(const void* q, const void* k, const void* v, const float* log_a,
+                             const float* beta, const float* lambda, void* out, int B, int H, int64_t T,
+                             int dk, int dv, int C, int L, int dtype, void* workspace,
+                             size_t workspace_bytes, la_stream_t stream);
+
 /*
  * Fenwick level table for checking: out[t * T + s] = l(t, s) for s <= t and
  * -1 for s > t, as int8, computed on the device by the same level function

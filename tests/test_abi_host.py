@@ -244,3 +244,52 @@ def test_bwd_validation_codes():
                B=0) == OK
     assert bwd(q=None, k=None, v=None, la=None, lam=None, g=None, gq=None, gk=None, gv=None, gla=None, glam=None,
                T=0, Lv=0) == OK
+
+
+def gws(B, H, T, d, C, dt=1):
+    n = ctypes.c_size_t(0)
+    rc = L.loglinear_gdn_fwd_workspace(B, H, T, d, d, C, dt, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_gdn_workspace_query():
+    # one fp32 state and one fp32 transition per aligned block of 2^m full
+    # chunks, plus a gate total: 256 + 128 + ... + 1 = 511 blocks per head
+    rc, n = gws(8, 16, 16384, 64, 64)
+    assert rc == OK
+    nodes = 128 * 511
+    need = nodes * 2 * 64 * 64 * 4 + nodes * 4
+    assert need <= n < need + 3 * 256
+    assert gws(1, 1, 63, 64, 64)[1] == 0          # no full chunk: no nodes
+    assert gws(0, 3, 640, 64, 64)[1] == 0          # empty problem
+    assert gws(2, 1, 100, 16, 16)[0] == OK         # ragged T
+    assert gws(1, 1, 64, 128, 64)[0] == ESHAPE     # d = 128 is not supported here
+    assert gws(1, 1, 64, 64, 128)[0] == ESHAPE     # nor C = 128
+    assert gws(1, 1, 64, 16, 16, 3)[0] == EDTYPE
+    assert gws(-1, 1, 64, 16, 16)[0] == EINVAL
+    assert L.loglinear_gdn_fwd_workspace(1, 1, 64, 64, 64, 64, 1, None) == EINVAL
+    for dt in (0, 1):                              # every supported shape fits in LDS
+        for d in (16, 32, 64):
+            for C in (16, 32, 64):
+                assert gws(1, 1, 1000, d, C, dt)[0] == OK, (dt, d, C)
+
+
+def gdn(q=A, k=A, v=A, la_=A, beta=A, lam=A, out=A, B=1, H=1, T=64, d=16, C=16, Lv=7, dt=0, w=A, wb=1 << 30):
+    return L.loglinear_gdn_fwd(q, k, v, la_, beta, lam, out, B, H, T, d, d, C, Lv, dt, w, wb, None)
+
+
+def test_gdn_validation_codes():
+    assert gdn(q=None) == EINVAL
+    assert gdn(beta=None) == EINVAL
+    assert gdn(out=None) == EINVAL
+    assert gdn(k=A + 8) == EALIGN
+    assert gdn(beta=A + 2) == EALIGN
+    assert gdn(dt=4) == EDTYPE
+    assert gdn(Lv=6) == ESHAPE
+    assert gdn(d=128, C=64) == ESHAPE
+    assert gdn(T=-5) == EINVAL
+    assert gdn(T=64, w=None) == EWS                # four full chunks: nodes needed
+    assert gdn(T=64, wb=100) == EWS
+    assert gdn(T=64, w=A + 64) == EALIGN
+    assert gdn(q=None, k=None, v=None, la_=None, beta=None, lam=None, out=None, B=0) == OK
+    assert gdn(q=None, k=None, v=None, la_=None, beta=None, lam=None, out=None, T=0, Lv=0) == OK
