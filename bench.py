@@ -1,6 +1,6 @@
 """Benchmark of log-linear Mamba-2 attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-backward]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-backward] [--no-gdn]
 
 One step is one forward (``loglinear_fwd``, all of its kernels) over the
 training-shape layer B=8, H=16, T=16384, d_k=d_v=64, C=64 in bfloat16, with
@@ -25,6 +25,9 @@ every input already resident in HBM.  Prints ONE JSON line:
   backward       the backward (loglinear_bwd) on the same layer with a
                  seeded upstream gradient: mean time, tokens/s and its ratio
                  to the forward
+  gdn            the log-linear Gated DeltaNet forward (loglinear_gdn_fwd)
+                 on the same layer shape with seeded beta: mean time,
+                 tokens/s, algorithmic TFLOP/s against the bf16 peak
   decode         the decode workload (64 x 16 heads): the 32768-token
                  prefill handing its state to decode (loglinear_fwd_state),
                  then 256 decode steps, positions 32768..33023
@@ -337,6 +340,69 @@ def bench_backward(la, torch, dev, w, x, fwd_ms, reps=10):
                                     f"(bf16), log_a, lambda read and dlog_a, dlambda written (fp32)"}
 
 
+def gdn_counts(B, H, T, d, C, L, es):
+    """Algorithmic work of the log-linear Gated DeltaNet forward, each needed
+    product counted once.  Per chunk: tril(Q K^T), K K^T, the unit-lower
+    solve (about C^3), Ahat = S T (2 C^3), the carried queries Ahat K and the
+    masked tile times V; per full chunk its state K^T U and transition K^T W
+    with U = T (gated beta V), W = T (beta K); per merge of two blocks two
+    d x d x d products; per query chunk one contraction per set bit of its
+    index and one carry of the queries between consecutive set bits.
+    Essential bytes: q, k, v, out in the layer dtype, log_a, beta, lambda."""
+    n_chunks = -(-T // C)
+    n_full = T // C
+    intra = n_chunks * (8 * C * C * d + 2 * C ** 3 + C ** 3)
+    prep = n_full * (4 * C * C * d + 4 * C * d * d)
+    merges = sum(n_full >> m for m in range(1, 40))
+    tree = merges * 4 * d ** 3
+    pc = [bin(c).count("1") for c in range(n_chunks)]
+    levels = sum(p * 2 * C * d * d + max(p - 1, 0) * 2 * C * d * d for p in pc)
+    bh = B * H
+    per_tok = 4 * d * es + 4 + 4 + 4 * L
+    return {"flops": bh * (intra + prep + tree + levels),
+            "split_tflop": {"intra": bh * intra / 1e12, "chunk_nodes": bh * prep / 1e12,
+                            "tree": bh * tree / 1e12, "levels": bh * levels / 1e12},
+            "essential_bytes": bh * T * per_tok, "per_head_token_bytes": per_tok}
+
+
+def bench_gdn(la, torch, dev, w, reps=10, warmup=5):
+    """The log-linear Gated DeltaNet forward (loglinear_gdn_fwd, all of its
+    kernels) on the training shape, beta ~ sigmoid(N(0,1)); HIP events on the
+    launch stream around each call."""
+    from fenwick_tree_hierarchical_amd.workloads import make_beta, make_inputs
+    x = make_inputs(w, device=dev)
+    beta = make_beta(w, device=dev)
+    out = torch.empty_like(x["v"])
+    nws = la.loglinear_gdn_fwd_workspace(w.B, w.H, w.T, w.dk, w.dv, w.C, torch.bfloat16)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+    def call():
+        la.loglinear_gdn_fwd(x["q"], x["k"], x["v"], x["log_a"], beta, x["lam"], out=out, chunk=w.C, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(s)
+    for i in range(reps):
+        call()
+        ev[i + 1].record(s)
+    torch.cuda.synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    mean = sum(ms) / reps
+    cnt = gdn_counts(w.B, w.H, w.T, w.dk, w.C, w.L, 2)
+    tf = cnt["flops"] / (mean * 1e-3) / 1e12
+    return {"workload": w.name, "chunk": w.C, "reps": reps, "ms": mean, "median_ms": sorted(ms)[reps // 2],
+            "min_ms": min(ms), "tokens_per_s": w.B * w.T / (mean * 1e-3), "workspace_bytes": nws,
+            "alg_tflop": cnt["flops"] / 1e12, "split_tflop": cnt["split_tflop"], "achieved_tflops": tf,
+            "frac_of_bf16_peak": tf / BF16_MFMA_PEAK_TFLOPS,
+            "essential_bytes": cnt["essential_bytes"],
+            "essential_gbps": cnt["essential_bytes"] / (mean * 1e-3) / 1e9,
+            "essential_bytes_note": f"{cnt['per_head_token_bytes']} B per head-token: q, k, v, out (bf16), "
+                                    f"log_a, beta, lambda (fp32)"}
+
+
 def ctypes_byref(la, st):
     import ctypes
     return ctypes.byref(st._st)
@@ -471,6 +537,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-gdn", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=48)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pmc-summary", default=None)
@@ -591,6 +658,9 @@ def main():
     if not args.no_backward:
         log("bench: backward")
         result["backward"] = bench_backward(la, torch, dev, w, x, fwd_ms)
+    if not args.no_gdn:
+        log("bench: gated deltanet forward")
+        result["gdn"] = bench_gdn(la, torch, dev, w)
     if not args.no_decode:
         log("bench: decode 256 steps")
         result["decode"] = bench_decode(la, torch, dev)

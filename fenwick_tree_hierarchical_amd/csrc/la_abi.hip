@@ -217,15 +217,14 @@ LA_API int loglinear_gdn_fwd(const void* q, const void* k, const void* v, const 
   if (!q || !k || !v || !log_a || !beta || !lambda || !out) return kEINVAL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return kEALIGN;
   if (!aligned(log_a, 4) || !aligned(beta, 4) || !aligned(lambda, 4)) return kEALIGN;
-  if (p.ws_bytes > 0) {
-    if (!workspace || workspace_bytes < p.ws_bytes) return kEWORKSPACE;
-    if (!aligned(workspace, 256)) return kEALIGN;
-  }
+  if (!workspace || workspace_bytes < p.ws_bytes) return kEWORKSPACE;
+  if (!aligned(workspace, 256)) return kEALIGN;
   char* w = static_cast<char*>(workspace);
   GdnArgs a{};
   a.q = q; a.k = k; a.v = v; a.log_a = log_a; a.beta = beta; a.lam = lambda; a.out = out;
-  a.pt = p.n_nodes > 0 ? reinterpret_cast<float*>(w + p.off_pt) : nullptr;
-  a.psit = p.n_nodes > 0 ? reinterpret_cast<float*>(w + p.off_psit) : nullptr;
+  a.tb = static_cast<void*>(w + p.off_tb);
+  a.pt = p.n_nodes > 0 ? static_cast<void*>(w + p.off_pt) : nullptr;
+  a.psit = p.n_nodes > 0 ? static_cast<void*>(w + p.off_psit) : nullptr;
   a.gn = p.n_nodes > 0 ? reinterpret_cast<float*>(w + p.off_gn) : nullptr;
   a.T = T; a.n_chunks = p.n_chunks; a.n_full = p.n_full; a.L = L;
   for (int m = 0; m < kGdnMaxTree; ++m) a.lev_off[m] = p.lev_off[m];

@@ -21,9 +21,13 @@
 //   O_c += diag(lambda_lev 2^(b_t + G_j)) Q_j P_j,   Q_{j+1} = Q_j Psi_j,
 // with G_j the log2 gates of the blocks between.
 //
-// Kernels (each workgroup 4 waves; all tiles staged in LDS as fp32; in bf16
-// mode every matrix-core operand is rounded to bf16, fp32 accumulation):
-//   gdn_chunk_prep    per full chunk: P_c, Psi_c, g_c (the tree's level 0)
+// Kernels (4 waves per workgroup).  Tiles are staged in LDS in the layer
+// dtype, with transposed copies where an operand is needed along its other
+// axis, so that every matrix-core operand fragment is one contiguous load;
+// the triangular solve and the accumulators are fp32.
+//   gdn_chunk_prep    per chunk: T by a blocked solve, (T diag(beta))^T for
+//                     the output kernel; per full chunk its node P_c, Psi_c,
+//                     g_c (the tree's level 0)
 //   gdn_tree          per block of 2^m chunks: the merge of its two halves
 //   gdn_chunk_output  per chunk: the intra tile, the carried queries and the
 //                     level contractions; writes the output.
@@ -31,6 +35,8 @@
 
 #include "la_device.hpp"
 #include "la_gdn_plan.hpp"
+
+#include <type_traits>
 
 namespace la {
 
@@ -42,8 +48,9 @@ struct GdnArgs {
   const float* beta;
   const float* lam;
   void* out;
-  float* pt;     // [n_nodes][D][D] block states, (d_v, d_k) order
-  float* psit;   // [n_nodes][D][D] block transitions without gates, transposed
+  void* tb;      // [BH][n_chunks][C][C] (T diag(beta))^T, layer dtype
+  void* pt;      // [n_nodes][D][D] block states, (d_v, d_k) order, layer dtype
+  void* psit;    // [n_nodes][D][D] block transitions without gates, transposed
   float* gn;     // [n_nodes] block log2 gate totals
   int64_t T;
   int64_t n_chunks;
@@ -52,45 +59,140 @@ struct GdnArgs {
   int64_t lev_off[kGdnMaxTree];
 };
 
-// acc += A[m0:m0+16, 0:K] * B[0:K, n0:n0+16] on the matrix cores.
-// AKC: A is stored A[m * lda + k] (else A[k * lda + m]);
-// BKC: B is stored B[n * ldb + k] (else B[k * ldb + n]).
+constexpr int gdn_clog2(int x) { return x <= 1 ? 0 : 1 + gdn_clog2(x >> 1); }
+
+// Operand fragments of the bf16 matrix cores: 8 consecutive k, from bf16 or
+// fp32 storage.
+struct GFrag {
+  static __device__ __forceinline__ bf16x8 ld(const bf16_t* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
+  }
+  static __device__ __forceinline__ bf16x8 ld(const float* p) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+    bf16x8 f;
+    f[0] = (__bf16)a[0]; f[1] = (__bf16)a[1]; f[2] = (__bf16)a[2]; f[3] = (__bf16)a[3];
+    f[4] = (__bf16)b[0]; f[5] = (__bf16)b[1]; f[6] = (__bf16)b[2]; f[7] = (__bf16)b[3];
+    return f;
+  }
+  static __device__ __forceinline__ bf16x8 zero() {
+    return __builtin_bit_cast(bf16x8, u16x8{0, 0, 0, 0, 0, 0, 0, 0});
+  }
+};
+
+// acc += A[m0:m0+16, 0:K] B[0:K, n0:n0+16] on the matrix cores, with A stored
+// A[m * lda + k] and B stored B[n * ldb + k] (both contiguous along k).
 // Lane l supplies row/column l % 16 and the k-slice l / 16 of its operands;
 // the result holds, in lane l, rows 4 (l / 16) + i of column l % 16.
-template <bool BF16, bool AKC, bool BKC, int K>
-__device__ __forceinline__ f32x4 mm_tile(const float* A, int lda, const float* B, int ldb, int m0, int n0,
-                                         f32x4 acc) {
+template <bool BF16, int K, typename TA, typename TB>
+__device__ __forceinline__ f32x4 mm_kc(const TA* A, int lda, const TB* B, int ldb, int m0, int n0, f32x4 acc) {
   const int lane = lane_id(), r = lane & 15, kq = lane >> 4;
   if constexpr (BF16) {
 #pragma unroll
     for (int k0 = 0; k0 < K; k0 += 32) {
       const int kk = k0 + 8 * kq;
-      bf16x8 fa, fb;
-      if (kk < K) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          fa[i] = (__bf16)(AKC ? A[(m0 + r) * lda + kk + i] : A[(kk + i) * lda + m0 + r]);
-          fb[i] = (__bf16)(BKC ? B[(n0 + r) * ldb + kk + i] : B[(kk + i) * ldb + n0 + r]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          fa[i] = (__bf16)0.f;
-          fb[i] = (__bf16)0.f;
-        }
+      bf16x8 fa = GFrag::zero(), fb = GFrag::zero();
+      if (K >= 32 || kk < K) {
+        fa = GFrag::ld(A + (m0 + r) * lda + kk);
+        fb = GFrag::ld(B + (n0 + r) * ldb + kk);
       }
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
     }
   } else {
 #pragma unroll
     for (int k0 = 0; k0 < K; k0 += 4) {
-      const int kk = k0 + kq;
-      const float fa = AKC ? A[(m0 + r) * lda + kk] : A[kk * lda + m0 + r];
-      const float fb = BKC ? B[(n0 + r) * ldb + kk] : B[kk * ldb + n0 + r];
+      const float fa = A[(m0 + r) * lda + k0 + kq];
+      const float fb = B[(n0 + r) * ldb + k0 + kq];
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa, fb, acc, 0, 0, 0);
     }
   }
   return acc;
+}
+
+// The B-operand strip of one 16-column tile over all K, held in registers:
+// the waves own fixed column strips of every product (n0 = 16 (wave % (N/16))
+// for N <= 64), so a strip is loaded once and reused for all its row tiles,
+// and one from global memory can be issued long before it is used.
+template <bool BF16, int K> struct BStrip {
+  static constexpr int N = BF16 ? (K + 31) / 32 : K / 4;
+  typename std::conditional<BF16, bf16x8, float>::type f[N];
+};
+template <bool BF16, int K, typename TB>
+__device__ __forceinline__ BStrip<BF16, K> load_strip(const TB* B, int ldb, int n0) {
+  BStrip<BF16, K> b;
+  const int lane = lane_id(), r = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < BStrip<BF16, K>::N; ++s) {
+    if constexpr (BF16) {
+      const int kk = 32 * s + 8 * kq;
+      b.f[s] = (K >= 32 || kk < K) ? GFrag::ld(B + (n0 + r) * ldb + kk) : GFrag::zero();
+    } else {
+      b.f[s] = B[(n0 + r) * ldb + 4 * s + kq];
+    }
+  }
+  return b;
+}
+template <bool BF16, int K, typename TA>
+__device__ __forceinline__ f32x4 mm_strip(const TA* A, int lda, const BStrip<BF16, K>& b, int m0, f32x4 acc) {
+  const int lane = lane_id(), r = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < BStrip<BF16, K>::N; ++s) {
+    if constexpr (BF16) {
+      const int kk = 32 * s + 8 * kq;
+      const bf16x8 fa = (K >= 32 || kk < K) ? GFrag::ld(A + (m0 + r) * lda + kk) : GFrag::zero();
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, b.f[s], acc, 0, 0, 0);
+    } else {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(m0 + r) * lda + 4 * s + kq], b.f[s], acc, 0, 0, 0);
+    }
+  }
+  return acc;
+}
+
+// 16-byte vectors of a C x D row-major tile of global memory, rows at or
+// past `nv` read as zero: every thread issues its loads before any is used.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <int C, int D, int ES> struct TileVec {
+  static constexpr int EPV = 16 / ES, VPR = D / EPV, NV = C * VPR;
+  static constexpr int VPT = (NV + kGdnThreads - 1) / kGdnThreads;
+  u32x4 v[VPT];
+};
+template <int C, int D, typename E>
+__device__ __forceinline__ TileVec<C, D, sizeof(E)> load_tile(const E* p, int nv) {
+  using TV = TileVec<C, D, sizeof(E)>;
+  TV t;
+#pragma unroll
+  for (int u = 0; u < TV::VPT; ++u) {
+    const int e = threadIdx.x + kGdnThreads * u;
+    const int i = e / TV::VPR;
+    t.v[u] = u32x4{0u, 0u, 0u, 0u};
+    if (e < TV::NV && i < nv) t.v[u] = reinterpret_cast<const u32x4*>(p)[e];
+  }
+  return t;
+}
+// 16 bytes of E built from 16 / sizeof(E) floats.
+template <typename E>
+__device__ __forceinline__ u32x4 pack16(const float* x) {
+  u32x4 w;
+  if constexpr (sizeof(E) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (unsigned)Elem<true>::from_f32(x[2 * i]) | ((unsigned)Elem<true>::from_f32(x[2 * i + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = __builtin_bit_cast(unsigned, x[i]);
+  }
+  return w;
+}
+
+// Element k of vector u of a loaded tile.
+template <typename E, int C, int D>
+__device__ __forceinline__ E tile_elem(const TileVec<C, D, sizeof(E)>& t, int u, int k) {
+  if constexpr (sizeof(E) == 2) {
+    const unsigned w = t.v[u][k >> 1];
+    return static_cast<E>((k & 1) ? (w >> 16) : (w & 0xffffu));
+  } else {
+    const unsigned w = t.v[u][k];   // a scalar copy first: a bit cast of the
+    return __builtin_bit_cast(E, w);  // vector element itself read element 0
+  }
 }
 
 // The 16x16 output tiles of an M x N product dealt round-robin to the waves.
@@ -100,34 +202,87 @@ __device__ __forceinline__ void for_tiles(F&& f) {
   for (int t = wave_id(); t < NT; t += kGdnThreads / 64) f((t / TN) * 16, (t % TN) * 16);
 }
 
-constexpr int gdn_clog2(int x) { return x <= 1 ? 0 : 1 + gdn_clog2(x >> 1); }
-
 __device__ __forceinline__ int tile_row0() { return 4 * (lane_id() >> 4); }
 __device__ __forceinline__ int tile_col() { return lane_id() & 15; }
 
-// T^T for T = (I + L)^-1, L[i][m] = beta_i G[i][m] for m < i (unit lower
-// triangular), by forward substitution: lane j solves column j.  One wave.
+template <typename E>
+__device__ __forceinline__ E to_e(float x) { return Elem<sizeof(E) == 2>::from_f32(x); }
+template <typename E>
+__device__ __forceinline__ float from_e(E x) { return Elem<sizeof(E) == 2>::to_f32(x); }
+
+// Four consecutive values of one output column, as one store / load.
+template <typename E>
+__device__ __forceinline__ void store4(E* p, f32x4 v) {
+  if constexpr (sizeof(E) == 2) {
+    *reinterpret_cast<u16x4*>(p) = u16x4{to_e<E>(v[0]), to_e<E>(v[1]), to_e<E>(v[2]), to_e<E>(v[3])};
+  } else {
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+}
+template <typename E>
+__device__ __forceinline__ f32x4 load4(const E* p) {
+  if constexpr (sizeof(E) == 2) {
+    const u16x4 u = *reinterpret_cast<const u16x4*>(p);
+    return f32x4{from_e<E>(u[0]), from_e<E>(u[1]), from_e<E>(u[2]), from_e<E>(u[3])};
+  } else {
+    return *reinterpret_cast<const f32x4*>(p);
+  }
+}
+
+// T = (I + L)^-1 for the unit lower triangular I + L, L[i][m] = beta_i G[i][m]
+// (m < i), row-major into Tm (fp32, zeros above the diagonal), by blocks of
+// 16: the diagonal blocks by forward substitution (lane 16 b + j solves
+// column j of block b), then each block row r from the rows above it,
+// T_rj = -T_rr sum_{k<r} L_rk T_kj.  Called by every thread of the
+// workgroup; returns with the workgroup synchronised.
 template <int C>
-__device__ __forceinline__ void solve_unit_lower(const float* G, int ld, const float* beta, float* Tt) {
-  const int j = lane_id();
-  float x[C];
+__device__ __forceinline__ void solve_blocked(const float* G, const float* beta, float* Tm, float* X) {
+  constexpr int LF = gdn_lde(C, 4), NB = C / 16;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < C * C; e += kGdnThreads) {   // the blocks above the diagonal
+    const int i = e / C, j = e % C;
+    if ((j >> 4) > (i >> 4)) Tm[i * LF + j] = 0.f;
+  }
+  if (tid < 16 * NB) {
+    const int b = tid >> 4, j = tid & 15, o = 16 * b;
+    float x[16];
 #pragma unroll
-  for (int i = 0; i < C; ++i) {
-    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;   // four chains hide the FMA latency
+    for (int i = 0; i < 16; ++i) {
+      float p0 = 0.f, p1 = 0.f;   // two chains hide the FMA latency
 #pragma unroll
-    for (int m = 0; m + 3 < i; m += 4) {
-      p0 = fmaf(G[i * ld + m], x[m], p0);
-      p1 = fmaf(G[i * ld + m + 1], x[m + 1], p1);
-      p2 = fmaf(G[i * ld + m + 2], x[m + 2], p2);
-      p3 = fmaf(G[i * ld + m + 3], x[m + 3], p3);
+      for (int m = 0; m + 1 < i; m += 2) {
+        p0 = fmaf(G[(o + i) * LF + o + m], x[m], p0);
+        p1 = fmaf(G[(o + i) * LF + o + m + 1], x[m + 1], p1);
+      }
+      if (i & 1) p0 = fmaf(G[(o + i) * LF + o + i - 1], x[i - 1], p0);
+      x[i] = (i == j ? 1.f : 0.f) - beta[o + i] * (p0 + p1);
     }
 #pragma unroll
-    for (int m = i & ~3; m < i; ++m) p0 = fmaf(G[i * ld + m], x[m], p0);
-    x[i] = (i == j ? 1.f : 0.f) - beta[i] * ((p0 + p1) + (p2 + p3));
+    for (int i = 0; i < 16; ++i) Tm[(o + i) * LF + o + j] = x[i];
   }
-  if (j < C) {
+  __syncthreads();
 #pragma unroll
-    for (int i = 0; i < C; ++i) Tt[j * ld + i] = x[i];
+  for (int rb = 1; rb < NB; ++rb) {
+    const int o = 16 * rb;   // block row rb; its columns 0 .. o-1 below the diagonal block
+    for (int e = tid; e < 16 * o; e += kGdnThreads) {
+      const int r = e / o, cc = e % o;
+      float p0 = 0.f, p1 = 0.f;
+      int mm = cc;
+      for (; mm + 1 < o; mm += 2) {
+        p0 = fmaf(G[(o + r) * LF + mm], Tm[mm * LF + cc], p0);
+        p1 = fmaf(G[(o + r) * LF + mm + 1], Tm[(mm + 1) * LF + cc], p1);
+      }
+      if (mm < o) p0 = fmaf(G[(o + r) * LF + mm], Tm[mm * LF + cc], p0);
+      X[r * LF + cc] = beta[o + r] * (p0 + p1);
+    }
+    __syncthreads();
+    for (int e = tid; e < 16 * o; e += kGdnThreads) {
+      const int r = e / o, cc = e % o;
+      float p = 0.f;
+      for (int rr = 0; rr <= r; ++rr) p = fmaf(Tm[(o + r) * LF + o + rr], X[rr * LF + cc], p);
+      Tm[(o + r) * LF + cc] = -p;
+    }
+    __syncthreads();
   }
 }
 
@@ -146,73 +301,98 @@ __device__ __forceinline__ void gdn_gate_scan(const float* la, const float* be, 
 }
 
 // ---------------------------------------------------------------------------
-// gdn_chunk_prep: one workgroup per (b,h, full chunk).  Level-0 nodes.
+// gdn_chunk_prep: one workgroup per (b,h, chunk).
 template <bool BF16, int C, int D>
 __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_prep(GdnArgs a) {
   using EL = Elem<BF16>;
   using E = typename EL::T;
-  constexpr int LD = gdn_ld(C, D);
-  constexpr GdnPrepLds LY = gdn_prep_lds(C, D);
+  constexpr int es = sizeof(E);
+  constexpr int LDD = gdn_lde(D, es), LDC = gdn_lde(C, es), LF = gdn_lde(C, 4);
+  constexpr GdnPrepLds LY = gdn_prep_lds(C, D, es);
   extern __shared__ __align__(16) unsigned char smem[];
-  float* Kl = reinterpret_cast<float*>(smem + LY.k);
-  float* Vs = reinterpret_cast<float*>(smem + LY.vs);
-  float* Kb = reinterpret_cast<float*>(smem + LY.kb);
-  float* Gm = reinterpret_cast<float*>(smem + LY.g);
-  float* Tt = reinterpret_cast<float*>(smem + LY.tt);
-  float* Wl = reinterpret_cast<float*>(smem + LY.w);
+  E* Kr = reinterpret_cast<E*>(smem + LY.kr);
+  E* Ut = reinterpret_cast<E*>(smem + LY.kr);     // over K once K K^T is formed
+  E* Kt = reinterpret_cast<E*>(smem + LY.kt);
+  E* Vst = reinterpret_cast<E*>(smem + LY.vst);
+  E* Kbt = reinterpret_cast<E*>(smem + LY.kbt);
+  float* G = reinterpret_cast<float*>(smem + LY.g);
+  E* Wt = reinterpret_cast<E*>(smem + LY.g);      // over K K^T once T is solved
+  float* Tm = reinterpret_cast<float*>(smem + LY.tm);
+  float* X = reinterpret_cast<float*>(smem + LY.x);
   float* b2 = reinterpret_cast<float*>(smem + LY.b2);
   float* bet = reinterpret_cast<float*>(smem + LY.beta);
-  const int64_t nf = a.n_full;
-  const int64_t bh = blockIdx.x / nf, c = blockIdx.x % nf;
+  const int64_t bh = blockIdx.x / a.n_chunks, c = blockIdx.x % a.n_chunks;
   const int64_t t0 = c * C;
+  const int nv = (int)((a.T - t0) < C ? (a.T - t0) : C);
+  const bool full = c < a.n_full;
   const int tid = threadIdx.x;
-  if (wave_id() == 0) gdn_gate_scan<C>(a.log_a + bh * a.T, a.beta + bh * a.T, t0, C, b2, bet);
+  using TV = TileVec<C, D, es>;
+  const TV kt = load_tile<C, D>(static_cast<const E*>(a.k) + (bh * a.T + t0) * D, nv);
+  const TV vt = load_tile<C, D>(static_cast<const E*>(a.v) + (bh * a.T + t0) * D, nv);
+  if (wave_id() == 0) gdn_gate_scan<C>(a.log_a + bh * a.T, a.beta + bh * a.T, t0, nv, b2, bet);
   __syncthreads();
   const float g = b2[C - 1];
-  const E* kp = static_cast<const E*>(a.k) + (bh * a.T + t0) * D;
-  const E* vp = static_cast<const E*>(a.v) + (bh * a.T + t0) * D;
-  for (int e = tid; e < C * D; e += kGdnThreads) {
-    const int i = e / D, j = e % D;
-    const float kv = EL::to_f32(kp[e]), vv = EL::to_f32(vp[e]);
-    Kl[i * LD + j] = kv;
-    Kb[i * LD + j] = bet[i] * kv;
-    Vs[i * LD + j] = bet[i] * exp2f(g - b2[i]) * vv;
+#pragma unroll
+  for (int u = 0; u < TV::VPT; ++u) {
+    const int e = tid + kGdnThreads * u;
+    if (e < TV::NV) {
+      const int i = e / TV::VPR, j0 = (e % TV::VPR) * TV::EPV;
+      *reinterpret_cast<u32x4*>(Kr + i * LDD + j0) = kt.v[u];
+      const float sb = bet[i], sv = bet[i] * exp2f(g - b2[i]);
+#pragma unroll
+      for (int kk = 0; kk < TV::EPV; ++kk) {
+        const E ke = tile_elem<E, C, D>(kt, u, kk);
+        Kt[(j0 + kk) * LDC + i] = ke;
+        Kbt[(j0 + kk) * LDC + i] = to_e<E>(sb * from_e<E>(ke));
+        Vst[(j0 + kk) * LDC + i] = to_e<E>(sv * from_e<E>(tile_elem<E, C, D>(vt, u, kk)));
+      }
+    }
   }
   __syncthreads();
-  // K K^T
+  // K K^T (fp32)
   for_tiles<C, C>([&](int m0, int n0) {
-    const f32x4 acc = mm_tile<BF16, true, true, D>(Kl, LD, Kl, LD, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
+    const f32x4 acc = mm_kc<BF16, D>(Kr, LDD, Kr, LDD, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Gm[(m0 + tile_row0() + i) * LD + n0 + tile_col()] = acc[i];
+    for (int i = 0; i < 4; ++i) G[(m0 + tile_row0() + i) * LF + n0 + tile_col()] = acc[i];
   });
   __syncthreads();
-  if (wave_id() == 0) solve_unit_lower<C>(Gm, LD, bet, Tt);
-  __syncthreads();
-  // U = T Vs (over K K^T) and W = T Kb
-  for_tiles<C, 2 * D>([&](int m0, int n0) {
-    const bool isw = n0 >= D;
-    const int nn = isw ? n0 - D : n0;
-    const f32x4 acc =
-        mm_tile<BF16, false, false, C>(Tt, LD, isw ? Kb : Vs, LD, m0, nn, f32x4{0.f, 0.f, 0.f, 0.f});
-    float* dst = isw ? Wl : Gm;
+  solve_blocked<C>(G, bet, Tm, X);
+  // (T diag(beta))^T for the output kernel
+  E* tb = static_cast<E*>(a.tb) + (bh * a.n_chunks + c) * (C * C);
+  {
+    constexpr int EPV = 16 / es, VR = C / EPV;
+    for (int e = tid; e < C * VR; e += kGdnThreads) {
+      const int s = e / VR, r0 = (e % VR) * EPV;
+      float x[EPV];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[(m0 + tile_row0() + i) * LD + nn + tile_col()] = acc[i];
+      for (int kk = 0; kk < EPV; ++kk) x[kk] = Tm[(r0 + kk) * LF + s] * bet[s];
+      reinterpret_cast<u32x4*>(tb)[e] = pack16<E>(x);
+    }
+  }
+  if (!full) return;
+  // U^T = (gated beta V)^T T^T over K, W^T = (beta K)^T T^T over K K^T
+  for_tiles<D, 2 * C>([&](int m0, int n0) {
+    const bool isw = n0 >= C;
+    const int nn = isw ? n0 - C : n0;
+    const f32x4 acc = mm_kc<BF16, C>(isw ? Kbt : Vst, LDC, Tm, LF, m0, nn, f32x4{0.f, 0.f, 0.f, 0.f});
+    E* dst = isw ? Wt : Ut;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[(m0 + tile_row0() + i) * LDC + nn + tile_col()] = to_e<E>(acc[i]);
   });
   __syncthreads();
   // P_c = K^T U and Psi_c = I - K^T W, stored transposed
-  const int64_t node = a.lev_off[0] + bh * nf + c;
-  float* pt = a.pt + node * (D * D);
-  float* ps = a.psit + node * (D * D);
+  const int64_t node = a.lev_off[0] + bh * a.n_full + c;
+  E* pt = static_cast<E*>(a.pt) + node * (D * D);
+  E* ps = static_cast<E*>(a.psit) + node * (D * D);
   for_tiles<D, 2 * D>([&](int m0, int n0) {
     const bool isw = n0 >= D;
     const int nn = isw ? n0 - D : n0;
-    const f32x4 acc =
-        mm_tile<BF16, false, false, C>(Kl, LD, isw ? Wl : Gm, LD, m0, nn, f32x4{0.f, 0.f, 0.f, 0.f});
+    const f32x4 acc = mm_kc<BF16, C>(Kt, LDC, isw ? Wt : Ut, LDC, m0, nn, f32x4{0.f, 0.f, 0.f, 0.f});
     const int col = nn + tile_col(), row = m0 + tile_row0();
     f32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = isw ? ((row + i == col ? 1.f : 0.f) - acc[i]) : acc[i];
-    *reinterpret_cast<f32x4*>((isw ? ps : pt) + col * D + row) = o;
+    store4<E>((isw ? ps : pt) + col * D + row, o);
   });
   if (tid == 0) a.gn[node] = g;
 }
@@ -222,31 +402,62 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_prep(GdnArgs a) {
 // halves of level m - 1.
 template <bool BF16, int D>
 __global__ __launch_bounds__(kGdnThreads) void gdn_tree(GdnArgs a, int m) {
+  using E = typename Elem<BF16>::T;
+  constexpr int es = sizeof(E), LDD = gdn_lde(D, es), DD = D * D;
+  extern __shared__ __align__(16) unsigned char smem[];
+  E* PsiR = reinterpret_cast<E*>(smem);   // Psi of the right half, row-major
   const int64_t nm = a.n_full >> m, np = a.n_full >> (m - 1);
   const int64_t bh = blockIdx.x / nm, x = blockIdx.x % nm;
   const int64_t iL = a.lev_off[m - 1] + bh * np + 2 * x, iR = iL + 1;
   const int64_t io = a.lev_off[m] + bh * nm + x;
-  constexpr int DD = D * D;
+  const E* pt = static_cast<const E*>(a.pt);
+  const E* ps = static_cast<const E*>(a.psit);
+  using TV = TileVec<D, D, es>;
+  const TV pr = load_tile<D, D>(ps + iR * DD, D);
+  // each wave owns column strips (of P or of Psi): their B operands, taken
+  // from the left half in global memory, are loaded once, before the wait
+  constexpr int TN = D / 16, NJ = 2 * TN, JPW = (NJ + 3) / 4;
+  BStrip<BF16, D> bs[JPW];
+#pragma unroll
+  for (int u = 0; u < JPW; ++u) {
+    const int j = wave_id() + 4 * u;
+    if (j < NJ) bs[u] = load_strip<BF16, D>((j >= TN ? ps : pt) + iL * DD, D, 16 * (j % TN));
+  }
+#pragma unroll
+  for (int u = 0; u < TV::VPT; ++u) {
+    const int e = threadIdx.x + kGdnThreads * u;
+    if (e < TV::NV) {
+      const int i = e / TV::VPR, j0 = (e % TV::VPR) * TV::EPV;
+#pragma unroll
+      for (int kk = 0; kk < TV::EPV; ++kk) PsiR[(j0 + kk) * LDD + i] = tile_elem<E, D, D>(pr, u, kk);
+    }
+  }
   const float gR = a.gn[iR];
   const float sR = exp2f(gR);
-  const float* psR = a.psit + iR * DD;
-  for_tiles<D, 2 * D>([&](int m0, int n0) {
-    const bool isp = n0 >= D;
-    const int nn = isp ? n0 - D : n0;
-    // P = 2^gR Psi_R P_L + P_R ; Psi = Psi_R Psi_L
-    const float* Bop = isp ? a.psit + iL * DD : a.pt + iL * DD;
-    const f32x4 acc = mm_tile<BF16, false, true, D>(psR, D, Bop, D, m0, nn, f32x4{0.f, 0.f, 0.f, 0.f});
-    const int col = nn + tile_col(), row = m0 + tile_row0();
-    f32x4 o;
-    if (isp) {
-      o = acc;
-    } else {
-      const f32x4 pr = *reinterpret_cast<const f32x4*>(a.pt + iR * DD + col * D + row);
+  __syncthreads();
+  E* pto = static_cast<E*>(a.pt) + io * DD;
+  E* pso = static_cast<E*>(a.psit) + io * DD;
+  // P = 2^gR Psi_R P_L + P_R ; Psi = Psi_R Psi_L (both stored transposed)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = fmaf(sR, acc[i], pr[i]);
+  for (int u = 0; u < JPW; ++u) {
+    const int j = wave_id() + 4 * u;
+    if (j < NJ) {
+      const bool isp = j >= TN;
+      const int col = 16 * (j % TN) + tile_col();
+#pragma unroll
+      for (int m0 = 0; m0 < D; m0 += 16) {
+        const f32x4 acc = mm_strip<BF16, D>(PsiR, LDD, bs[u], m0, f32x4{0.f, 0.f, 0.f, 0.f});
+        const int row = m0 + tile_row0();
+        f32x4 o = acc;
+        if (!isp) {
+          const f32x4 r4 = load4<E>(pt + iR * DD + col * D + row);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = fmaf(sR, acc[i], r4[i]);
+        }
+        store4<E>((isp ? pso : pto) + col * D + row, o);
+      }
     }
-    *reinterpret_cast<f32x4*>((isp ? a.psit : a.pt) + io * DD + col * D + row) = o;
-  });
+  }
   if (threadIdx.x == 0) a.gn[io] = a.gn[iL] + gR;
 }
 
@@ -256,15 +467,16 @@ template <bool BF16, int C, int D>
 __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
   using EL = Elem<BF16>;
   using E = typename EL::T;
-  constexpr int LD = gdn_ld(C, D);
-  const GdnOutLds LY = gdn_out_lds(C, D, a.L);
+  constexpr int es = sizeof(E);
+  constexpr int LDD = gdn_lde(D, es), LDC = gdn_lde(C, es);
+  const GdnOutLds LY = gdn_out_lds(C, D, es, a.L);
   extern __shared__ __align__(16) unsigned char smem[];
-  float* Ql = reinterpret_cast<float*>(smem + LY.q);
-  float* Kl = reinterpret_cast<float*>(smem + LY.k);
-  float* Vl = reinterpret_cast<float*>(smem + LY.v);
-  float* Sl = reinterpret_cast<float*>(smem + LY.s);
-  float* Al = reinterpret_cast<float*>(smem + LY.a);
-  float* Tt = reinterpret_cast<float*>(smem + LY.tt);
+  E* Ql = reinterpret_cast<E*>(smem + LY.q);
+  E* Kl = reinterpret_cast<E*>(smem + LY.k);
+  E* Kt = reinterpret_cast<E*>(smem + LY.kt);
+  E* Vt = reinterpret_cast<E*>(smem + LY.vt);
+  E* Sl = reinterpret_cast<E*>(smem + LY.s);
+  E* Al = reinterpret_cast<E*>(smem + LY.a);
   float* lam = reinterpret_cast<float*>(smem + LY.lam);
   float* b2 = reinterpret_cast<float*>(smem + LY.b2);
   float* bet = reinterpret_cast<float*>(smem + LY.beta);
@@ -273,107 +485,155 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
   const int64_t t0 = c * C;
   const int nv = (int)((a.T - t0) < C ? (a.T - t0) : C);
   const int tid = threadIdx.x;
-  if (wave_id() == 0) gdn_gate_scan<C>(a.log_a + bh * a.T, a.beta + bh * a.T, t0, nv, b2, bet);
   const int64_t row0 = bh * a.T + t0;
-  const E* qp = static_cast<const E*>(a.q) + row0 * D;
-  const E* kp = static_cast<const E*>(a.k) + row0 * D;
-  const E* vp = static_cast<const E*>(a.v) + row0 * D;
-  for (int e = tid; e < C * D; e += kGdnThreads) {
-    const int i = e / D, j = e % D;
-    const bool ok = i < nv;
-    Ql[i * LD + j] = ok ? EL::to_f32(qp[e]) : 0.f;
-    Kl[i * LD + j] = ok ? EL::to_f32(kp[e]) : 0.f;
-    Vl[i * LD + j] = ok ? EL::to_f32(vp[e]) : 0.f;
-  }
+  using TV = TileVec<C, D, es>;
+  const TV qv = load_tile<C, D>(static_cast<const E*>(a.q) + row0 * D, nv);
+  const TV kv = load_tile<C, D>(static_cast<const E*>(a.k) + row0 * D, nv);
+  const TV vv = load_tile<C, D>(static_cast<const E*>(a.v) + row0 * D, nv);
+  constexpr int LPT = (C * kMaxLevels + kGdnThreads - 1) / kGdnThreads;
+  float lv[LPT];
   const float* lp = a.lam + row0 * L;
-  for (int e = tid; e < C * L; e += kGdnThreads) lam[e] = e < nv * L ? lp[e] : 0.f;
-  __syncthreads();
-  // tril(Q K^T) and K K^T
-  for_tiles<C, 2 * C>([&](int m0, int n0) {
-    const bool isg = n0 >= C;
-    const int nn = isg ? n0 - C : n0;
-    const float* Aop = isg ? Kl : Ql;
-    const f32x4 acc = mm_tile<BF16, true, true, D>(Aop, LD, Kl, LD, m0, nn, f32x4{0.f, 0.f, 0.f, 0.f});
-    const int col = nn + tile_col(), row = m0 + tile_row0();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (isg) Al[(row + i) * LD + col] = acc[i];
-      else Sl[(row + i) * LD + col] = col <= row + i ? acc[i] : 0.f;
+  for (int u = 0; u < LPT; ++u) {
+    const int e = tid + kGdnThreads * u;
+    lv[u] = e < nv * L ? lp[e] : 0.f;
+  }
+  // the B strips this wave needs from global memory, issued early: the
+  // columns of (T diag(beta))^T for Ahat, and the first bucket node's state
+  // and transition
+  constexpr int TNC = C / 16, TND = D / 16;
+  const int n0c = 16 * (wave_id() % TNC), n0d = 16 * (wave_id() % TND);
+  const E* tbp = static_cast<const E*>(a.tb) + (bh * a.n_chunks + c) * (C * C);
+  const BStrip<BF16, C> tbs = load_strip<BF16, C>(tbp, C, n0c);
+  const E* ptb = static_cast<const E*>(a.pt);
+  const E* psb = static_cast<const E*>(a.psit);
+  const int64_t nf = a.n_full;
+  BStrip<BF16, D> pf{}, sf{};
+  if (c != 0) {
+    const int m = __builtin_ctzll((unsigned long long)c);
+    const int64_t node = a.lev_off[m] + bh * (nf >> m) + (c >> m) - 1;
+    pf = load_strip<BF16, D>(ptb + node * (D * D), D, n0d);
+    if ((c >> (m + 1)) != 0) sf = load_strip<BF16, D>(psb + node * (D * D), D, n0d);
+  }
+  if (wave_id() == 0) gdn_gate_scan<C>(a.log_a + bh * a.T, a.beta + bh * a.T, t0, nv, b2, bet);
+#pragma unroll
+  for (int u = 0; u < TV::VPT; ++u) {
+    const int e = tid + kGdnThreads * u;
+    if (e < TV::NV) {
+      const int i = e / TV::VPR, j0 = (e % TV::VPR) * TV::EPV;
+      *reinterpret_cast<u32x4*>(Ql + i * LDD + j0) = qv.v[u];
+      *reinterpret_cast<u32x4*>(Kl + i * LDD + j0) = kv.v[u];
+#pragma unroll
+      for (int kk = 0; kk < TV::EPV; ++kk) {
+        Kt[(j0 + kk) * LDC + i] = tile_elem<E, C, D>(kv, u, kk);
+        Vt[(j0 + kk) * LDC + i] = tile_elem<E, C, D>(vv, u, kk);
+      }
     }
+  }
+#pragma unroll
+  for (int u = 0; u < LPT; ++u) {
+    const int e = tid + kGdnThreads * u;
+    if (e < C * L) lam[e] = lv[u];
+  }
+  __syncthreads();
+  // tril(Q K^T)
+  const BStrip<BF16, D> ks = load_strip<BF16, D>(Kl, LDD, n0c);
+  for_tiles<C, C>([&](int m0, int n0) {
+    const f32x4 acc = mm_strip<BF16, D>(Ql, LDD, ks, m0, f32x4{0.f, 0.f, 0.f, 0.f});
+    const int col = n0 + tile_col(), row = m0 + tile_row0();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Sl[(row + i) * LDC + col] = to_e<E>(col <= row + i ? acc[i] : 0.f);
   });
   __syncthreads();
-  if (wave_id() == 0) solve_unit_lower<C>(Al, LD, bet, Tt);
-  __syncthreads();
-  // Ahat = tril(Q K^T) T diag(beta), over K K^T
+  // Ahat = tril(Q K^T) T diag(beta)
   for_tiles<C, C>([&](int m0, int n0) {
-    const f32x4 acc = mm_tile<BF16, true, true, C>(Sl, LD, Tt, LD, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
+    const f32x4 acc = mm_strip<BF16, C>(Sl, LDC, tbs, m0, f32x4{0.f, 0.f, 0.f, 0.f});
     const int col = n0 + tile_col(), row = m0 + tile_row0();
-    const float bcol = bet[col];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Al[(row + i) * LD + col] = acc[i] * bcol;
+    for (int i = 0; i < 4; ++i) Al[(row + i) * LDC + col] = to_e<E>(acc[i]);
   });
   __syncthreads();
   // carried queries Q' = Q - Ahat K, in place
+  const BStrip<BF16, C> kts = load_strip<BF16, C>(Kt, LDC, n0d);
   for_tiles<C, D>([&](int m0, int n0) {
-    const f32x4 acc = mm_tile<BF16, true, false, C>(Al, LD, Kl, LD, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
+    const f32x4 acc = mm_strip<BF16, C>(Al, LDC, kts, m0, f32x4{0.f, 0.f, 0.f, 0.f});
     const int col = n0 + tile_col(), row = m0 + tile_row0();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Ql[(row + i) * LD + col] -= acc[i];
+    for (int i = 0; i < 4; ++i) {
+      E& qv = Ql[(row + i) * LDD + col];
+      qv = to_e<E>(from_e<E>(qv) - acc[i]);
+    }
   });
   __syncthreads();
   // the masked intra tile: lambda of the level and the gate ratio
   for (int e = tid; e < C * C; e += kGdnThreads) {
     const int i = e / C, j = e % C;
     float p = 0.f;
-    if (j <= i && i < nv) p = Al[i * LD + j] * lam[i * L + fenwick_level_local((unsigned)i, (unsigned)j)] * exp2f(b2[i] - b2[j]);
-    Al[i * LD + j] = p;
+    if (j <= i && i < nv)
+      p = from_e<E>(Al[i * LDC + j]) * lam[i * L + fenwick_level_local((unsigned)i, (unsigned)j)] *
+          exp2f(b2[i] - b2[j]);
+    Al[i * LDC + j] = to_e<E>(p);
   }
   __syncthreads();
   // O = P V, each wave keeping its output tiles in registers
+  const BStrip<BF16, C> vts = load_strip<BF16, C>(Vt, LDC, n0d);
   constexpr int TN = D / 16, OT = (C / 16) * TN, NW = kGdnThreads / 64, OPW = (OT + NW - 1) / NW;
   f32x4 o[OPW];
 #pragma unroll
   for (int u = 0; u < OPW; ++u) {
     const int t = wave_id() + NW * u;
     o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (t < OT) o[u] = mm_tile<BF16, true, false, C>(Al, LD, Vl, LD, (t / TN) * 16, (t % TN) * 16, o[u]);
+    if (t < OT) o[u] = mm_strip<BF16, C>(Al, LDC, vts, (t / TN) * 16, o[u]);
   }
-  // bucket nodes of the set bits of c, most recent first
+  // bucket nodes of the set bits of c, most recent first; the next node's
+  // strips are loaded while this one is used
   constexpr int log2C = gdn_clog2(C);
-  float* cur = Ql;
-  float* nxt = Sl;
-  float G = 0.f;
-  const int64_t nf = a.n_full;
+  E* cur = Ql;
+  E* nxt = Sl;
+  float Gs = 0.f;
   for (int m = 0; (c >> m) != 0; ++m) {
     if (!((c >> m) & 1)) continue;
     const int64_t node = a.lev_off[m] + bh * (nf >> m) + (c >> m) - 1;
-    const float* P = a.pt + node * (D * D);
     const int lev = log2C + 1 + m;
+    const int64_t up = c >> (m + 1);
+    BStrip<BF16, D> pn{}, sn{};
+    if (up != 0) {
+      const int m2 = m + 1 + __builtin_ctzll((unsigned long long)up);
+      const int64_t node2 = a.lev_off[m2] + bh * (nf >> m2) + (c >> m2) - 1;
+      pn = load_strip<BF16, D>(ptb + node2 * (D * D), D, n0d);
+      if ((c >> (m2 + 1)) != 0) sn = load_strip<BF16, D>(psb + node2 * (D * D), D, n0d);
+    }
 #pragma unroll
     for (int u = 0; u < OPW; ++u) {
       const int t = wave_id() + NW * u;
       if (t < OT) {
-        const int m0 = (t / TN) * 16, n0 = (t % TN) * 16;
-        const f32x4 y = mm_tile<BF16, true, true, D>(cur, LD, P, D, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
+        const int m0 = (t / TN) * 16;
+        const f32x4 y = mm_strip<BF16, D>(cur, LDD, pf, m0, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = m0 + tile_row0() + i;
-          o[u][i] = fmaf(lam[row * L + lev] * exp2f(b2[row] + G), y[i], o[u][i]);
+          o[u][i] = fmaf(lam[row * L + lev] * exp2f(b2[row] + Gs), y[i], o[u][i]);
         }
       }
     }
-    if ((c >> (m + 1)) != 0) {   // an older node follows: carry the queries through this block
-      const float* Ps = a.psit + node * (D * D);
-      for_tiles<C, D>([&](int m0, int n0) {
-        const f32x4 acc = mm_tile<BF16, true, true, D>(cur, LD, Ps, D, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
+    if (up != 0) {   // an older node follows: carry the queries through this block
 #pragma unroll
-        for (int i = 0; i < 4; ++i) nxt[(m0 + tile_row0() + i) * LD + n0 + tile_col()] = acc[i];
-      });
-      G += a.gn[node];
+      for (int u = 0; u < OPW; ++u) {
+        const int t = wave_id() + NW * u;
+        if (t < OT) {
+          const int m0 = (t / TN) * 16;
+          const f32x4 acc = mm_strip<BF16, D>(cur, LDD, sf, m0, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) nxt[(m0 + tile_row0() + i) * LDD + n0d + tile_col()] = to_e<E>(acc[i]);
+        }
+      }
+      Gs += a.gn[node];
       __syncthreads();
-      float* sw = cur;
+      E* sw = cur;
       cur = nxt;
       nxt = sw;
+      pf = pn;
+      sf = sn;
     }
   }
   E* op = static_cast<E*>(a.out) + row0 * D;
@@ -385,7 +645,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = m0 + tile_row0() + i;
-        if (row < nv) op[row * D + n0 + tile_col()] = EL::from_f32(o[u][i]);
+        if (row < nv) op[row * D + n0 + tile_col()] = to_e<E>(o[u][i]);
       }
     }
   }
@@ -394,26 +654,23 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
 // ---------------------------------------------------------------------------
 template <bool BF16, int C, int D>
 int launch_gdn_impl(const GdnPlan& p, const GdnArgs& a, hipStream_t s) {
-  bool ok = true;
-  if (p.n_full >= 1) {
-    ok = ok && hipFuncSetAttribute((const void*)gdn_chunk_prep<BF16, C, D>,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_prep) == hipSuccess;
-    if (!ok) return kEHIP;
-    hipLaunchKernelGGL((gdn_chunk_prep<BF16, C, D>), dim3((unsigned)(p.BH * p.n_full)), dim3(kGdnThreads),
-                       p.lds_prep, s, a);
-    ok = ok && hipGetLastError() == hipSuccess;
-    for (int m = 1; m < p.n_tree && ok; ++m) {
-      hipLaunchKernelGGL((gdn_tree<BF16, D>), dim3((unsigned)(p.BH * (p.n_full >> m))), dim3(kGdnThreads), 0, s,
-                         a, m);
-      ok = ok && hipGetLastError() == hipSuccess;
-    }
+  bool ok = hipFuncSetAttribute((const void*)gdn_chunk_prep<BF16, C, D>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_prep) == hipSuccess;
+  if (!ok) return kEHIP;
+  hipLaunchKernelGGL((gdn_chunk_prep<BF16, C, D>), dim3((unsigned)(p.BH * p.n_chunks)), dim3(kGdnThreads),
+                     p.lds_prep, s, a);
+  ok = hipGetLastError() == hipSuccess;
+  for (int m = 1; m < p.n_tree && ok; ++m) {
+    hipLaunchKernelGGL((gdn_tree<BF16, D>), dim3((unsigned)(p.BH * (p.n_full >> m))), dim3(kGdnThreads),
+                       p.lds_tree, s, a, m);
+    ok = hipGetLastError() == hipSuccess;
   }
   ok = ok && hipFuncSetAttribute((const void*)gdn_chunk_output<BF16, C, D>,
                                  hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_out) == hipSuccess;
   if (!ok) return kEHIP;
   hipLaunchKernelGGL((gdn_chunk_output<BF16, C, D>), dim3((unsigned)(p.BH * p.n_chunks)), dim3(kGdnThreads),
                      p.lds_out, s, a);
-  ok = ok && hipGetLastError() == hipSuccess;
+  ok = hipGetLastError() == hipSuccess;
   return ok ? kOK : kEHIP;
 }
 

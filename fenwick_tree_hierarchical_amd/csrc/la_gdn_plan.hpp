@@ -2,14 +2,18 @@
 // checks, the Fenwick node tree carve-up of the workspace and the LDS
 // carve-up of its kernels.  Pure C++17 (builds into CPU test programs too).
 //
-// Workspace: one node per aligned block of 2^m full chunks (m = 0, 1, ...),
-// level by level; node (m, bh, x) covers chunks [x 2^m, (x+1) 2^m) of head bh
-// and holds
-//   pt   [D][D] fp32  the block's state at its last token, (d_v, d_k) order
-//                     (sum over its keys s of Phi(end, s) beta_s k_s v_s^T)
-//   psit [D][D] fp32  the block's transition without gates, transposed
-//                     (the product of (I - beta_r k_r k_r^T) over its tokens)
-//   gn        fp32    the block's log2 gate total
+// Workspace, all per head bh:
+//   tb   [n_chunks][C][C]  layer dtype  (T diag(beta))^T of every chunk, T
+//                          the inverse of I + strict_tril(diag(beta) K K^T)
+//   one node per aligned block of 2^m full chunks (m = 0, 1, ...), level by
+//   level; node (m, bh, x) covers chunks [x 2^m, (x+1) 2^m) and holds
+//   pt   [D][D]  layer dtype  the block's state at its last token, (d_v, d_k)
+//                             order: sum over its keys s of
+//                             Phi(end, s) beta_s k_s v_s^T, transposed
+//   psit [D][D]  layer dtype  the block's transition without gates,
+//                             transposed (the product of the
+//                             I - beta_r k_r k_r^T over its tokens)
+//   gn           fp32         the block's log2 gate total
 #pragma once
 
 #include "la_plan.hpp"
@@ -19,65 +23,74 @@ namespace la {
 constexpr int kGdnMaxTree = 32;   // tree levels (n_full_chunks < 2^31)
 constexpr int kGdnThreads = 256;  // 4 waves per workgroup in every kernel
 
-// LDS regions are all C x (max(C, D) + 4) floats: a 16-byte row pad keeps
-// the 16 rows an operand fragment reads in different banks.
-LA_HD constexpr int gdn_ld(int C, int D) { return (C > D ? C : D) + 4; }
-LA_HD constexpr int gdn_region_bytes(int C, int D) { return (C * gdn_ld(C, D) * 4 + 255) / 256 * 256; }
+// Row stride (elements) of an LDS tile with `cols` columns of es-byte
+// elements: a 16-byte pad, so rows start 16-byte aligned and the rows one
+// operand fragment reads spread over the banks.
+LA_HD constexpr int gdn_lde(int cols, int es) { return cols + 16 / es; }
+// Bytes of a rows x cols tile, rounded to 256.
+LA_HD constexpr int gdn_tile(int rows, int cols, int es) { return (rows * gdn_lde(cols, es) * es + 255) / 256 * 256; }
+LA_HD constexpr int gdn_max(int a, int b) { return a > b ? a : b; }
 
-// gdn_chunk_prep: K, beta-and-gate scaled V, beta-scaled K, K K^T (then U),
-// T^T and W, plus the gate scan and beta of the chunk.
+// gdn_chunk_prep: K (then U^T), K^T, (gated beta V)^T, (beta K)^T, K K^T
+// (fp32, then W^T), T (fp32), the blocked solve's scratch, gate scan, beta.
 struct GdnPrepLds {
-  int k, vs, kb, g, tt, w, b2, beta, total;
+  int kr, kt, vst, kbt, g, tm, x, b2, beta, total;
 };
-LA_HD constexpr GdnPrepLds gdn_prep_lds(int C, int D) {
+LA_HD constexpr GdnPrepLds gdn_prep_lds(int C, int D, int es) {
   GdnPrepLds o{};
-  const int r = gdn_region_bytes(C, D);
+  const int sq = gdn_max(gdn_tile(C, D, es), gdn_tile(D, C, es));   // K row-major or U^T
+  const int f = gdn_tile(C, C, 4);                                  // fp32 C x C
   const int v = (C * 4 + 255) / 256 * 256;
   int off = 0;
-  o.k = off;  off += r;
-  o.vs = off; off += r;
-  o.kb = off; off += r;
-  o.g = off;  off += r;    // K K^T, then U = T diag(beta gate) V
-  o.tt = off; off += r;
-  o.w = off;  off += r;
-  o.b2 = off; off += v;
+  o.kr = off;  off += sq;
+  o.kt = off;  off += gdn_tile(D, C, es);
+  o.vst = off; off += gdn_tile(D, C, es);
+  o.kbt = off; off += gdn_tile(D, C, es);
+  o.g = off;   off += gdn_max(f, gdn_tile(D, C, es));                // K K^T, then W^T
+  o.tm = off;  off += f;
+  o.x = off;   off += gdn_tile(16, C, 4);
+  o.b2 = off;  off += v;
   o.beta = off; off += v;
   o.total = off;
   return o;
 }
 
-// gdn_chunk_output: Q (then the carried queries), K, V, Q K^T (then the
-// second carried-query buffer), K K^T (then A-hat, then the masked tile),
-// T^T, the chunk's lambda rows, gate scan and beta.
+// gdn_tree: Psi of the right half, row-major.
+LA_HD constexpr int gdn_tree_lds(int D, int es) { return gdn_tile(D, D, es); }
+
+// gdn_chunk_output: Q (then the carried queries), K, K^T, V^T, tril(Q K^T)
+// (then the second carried-query buffer), Ahat (then the masked tile), the
+// chunk's lambda rows, gate scan and beta.  (T diag(beta))^T is read from
+// global memory straight into registers.
 struct GdnOutLds {
-  int q, k, v, s, a, tt, lam, b2, beta, total;
+  int q, k, kt, vt, s, a, lam, b2, beta, total;
 };
-LA_HD constexpr GdnOutLds gdn_out_lds(int C, int D, int L) {
+LA_HD constexpr GdnOutLds gdn_out_lds(int C, int D, int es, int L) {
   GdnOutLds o{};
-  const int r = gdn_region_bytes(C, D);
+  const int cd = gdn_tile(C, D, es), dc = gdn_tile(D, C, es), cc = gdn_tile(C, C, es);
   const int v = (C * 4 + 255) / 256 * 256;
   int off = 0;
-  o.q = off;  off += r;
-  o.k = off;  off += r;
-  o.v = off;  off += r;
-  o.s = off;  off += r;
-  o.a = off;  off += r;
-  o.tt = off; off += r;
+  o.q = off;   off += cd;
+  o.k = off;   off += cd;
+  o.kt = off;  off += dc;
+  o.vt = off;  off += dc;
+  o.s = off;   off += gdn_max(cc, cd);
+  o.a = off;   off += cc;
   o.lam = off; off += (C * L * 4 + 255) / 256 * 256;
-  o.b2 = off; off += v;
+  o.b2 = off;  off += v;
   o.beta = off; off += v;
   o.total = off;
   return o;
 }
 
 struct GdnPlan {
-  int B = 0, H = 0, D = 0, C = 0, L = 0, dtype = 0, log2C = 0;
+  int B = 0, H = 0, D = 0, C = 0, L = 0, dtype = 0, es = 0, log2C = 0;
   int64_t T = 0, BH = 0, n_chunks = 0, n_full = 0;
   int n_tree = 0;                       // levels m with at least one node
   int64_t lev_off[kGdnMaxTree] = {};    // first node of level m
   int64_t n_nodes = 0;
-  size_t off_pt = 0, off_psit = 0, off_gn = 0, ws_bytes = 0;
-  int lds_prep = 0, lds_out = 0;
+  size_t off_tb = 0, off_pt = 0, off_psit = 0, off_gn = 0, ws_bytes = 0;
+  int lds_prep = 0, lds_tree = 0, lds_out = 0;
 };
 
 // Checks and the plan.  L < 0 skips the level-count check (workspace query).
@@ -96,15 +109,17 @@ inline int plan_gdn(int B, int H, int64_t T, int dk, int dv, int C, int dtype, i
   }
   GdnPlan P;
   P.B = B; P.H = H; P.T = T; P.D = dk; P.C = C; P.dtype = dtype;
+  P.es = dtype == kBF16 ? 2 : 4;
   P.L = L < 0 ? kMaxLevels : L;
   P.log2C = ilog2(C);
   P.BH = (int64_t)B * H;
   P.n_chunks = (T + C - 1) / C;
   P.n_full = T / C;
   if (P.n_chunks * P.BH > (int64_t)0x7fffffff) return kESHAPE;
-  P.lds_prep = gdn_prep_lds(C, dk).total;
-  P.lds_out = gdn_out_lds(C, dk, P.L).total;
-  if (P.lds_prep > kLdsLimit || gdn_out_lds(C, dk, kMaxLevels).total > kLdsLimit) return kESHAPE;
+  P.lds_prep = gdn_prep_lds(C, dk, P.es).total;
+  P.lds_tree = gdn_tree_lds(dk, P.es);
+  P.lds_out = gdn_out_lds(C, dk, P.es, P.L).total;
+  if (P.lds_prep > kLdsLimit || gdn_out_lds(C, dk, P.es, kMaxLevels).total > kLdsLimit) return kESHAPE;
   int64_t n = 0;
   P.n_tree = 0;
   for (int m = 0; m < kGdnMaxTree && (P.n_full >> m) >= 1; ++m) {
@@ -115,9 +130,10 @@ inline int plan_gdn(int B, int H, int64_t T, int dk, int dv, int C, int dtype, i
   P.n_nodes = n;
   const size_t DD = (size_t)dk * dv;
   size_t off = 0;
+  P.off_tb = off; off = align_up(off + (size_t)P.BH * P.n_chunks * C * C * P.es, 256);
   if (n > 0) {
-    P.off_pt = off;   off = align_up(off + (size_t)n * DD * 4, 256);
-    P.off_psit = off; off = align_up(off + (size_t)n * DD * 4, 256);
+    P.off_pt = off;   off = align_up(off + (size_t)n * DD * P.es, 256);
+    P.off_psit = off; off = align_up(off + (size_t)n * DD * P.es, 256);
     P.off_gn = off;   off = align_up(off + (size_t)n * 4, 256);
   }
   P.ws_bytes = (P.BH == 0 || T == 0) ? 0 : off;

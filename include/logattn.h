@@ -276,8 +276,9 @@ LA_API int loglinear_gdn_fwd_workspace(int B, int H, int64_t T, int dk, int dv, 
  *   lambda   [B, H, T, L]   float32   L >= ceil(log2 T) + 1
  *   C        chunk size, 16, 32 or 64; dk = dv in {16, 32, 64}
  *   workspace at least loglinear_gdn_fwd_workspace() bytes, 256-byte
- *            aligned (one fp32 state and one fp32 transition per aligned
- *            block of 2^m full chunks); owned by the caller
+ *            aligned, owned by the caller: per chunk a C x C matrix, per
+ *            aligned block of 2^m full chunks a d x d state and a d x d
+ *            transition, all in the layer dtype
  * Asynchronous on `stream`; every check happens on the host before any
  * launch, and on error nothing is written.  Errors: LA_EINVAL (null pointer,
  * negative count), LA_ESHAPE (dims, C, L, size limits), LA_EDTYPE,

@@ -253,14 +253,15 @@ def gws(B, H, T, d, C, dt=1):
 
 
 def test_gdn_workspace_query():
-    # one fp32 state and one fp32 transition per aligned block of 2^m full
-    # chunks, plus a gate total: 256 + 128 + ... + 1 = 511 blocks per head
+    # a C x C matrix per chunk, a state and a transition per aligned block
+    # of 2^m full chunks (256 + 128 + ... + 1 = 511 per head), all bf16,
+    # plus an fp32 gate total per block
     rc, n = gws(8, 16, 16384, 64, 64)
     assert rc == OK
     nodes = 128 * 511
-    need = nodes * 2 * 64 * 64 * 4 + nodes * 4
-    assert need <= n < need + 3 * 256
-    assert gws(1, 1, 63, 64, 64)[1] == 0          # no full chunk: no nodes
+    need = 128 * 256 * 64 * 64 * 2 + nodes * 2 * 64 * 64 * 2 + nodes * 4
+    assert need <= n < need + 4 * 256
+    assert gws(1, 1, 63, 64, 64)[1] == 64 * 64 * 2  # no full chunk: the chunk's matrix only
     assert gws(0, 3, 640, 64, 64)[1] == 0          # empty problem
     assert gws(2, 1, 100, 16, 16)[0] == OK         # ragged T
     assert gws(1, 1, 64, 128, 64)[0] == ESHAPE     # d = 128 is not supported here
@@ -288,7 +289,7 @@ def test_gdn_validation_codes():
     assert gdn(Lv=6) == ESHAPE
     assert gdn(d=128, C=64) == ESHAPE
     assert gdn(T=-5) == EINVAL
-    assert gdn(T=64, w=None) == EWS                # four full chunks: nodes needed
+    assert gdn(T=64, w=None) == EWS                # every non-empty problem needs a workspace
     assert gdn(T=64, wb=100) == EWS
     assert gdn(T=64, w=A + 64) == EALIGN
     assert gdn(q=None, k=None, v=None, la_=None, beta=None, lam=None, out=None, B=0) == OK
