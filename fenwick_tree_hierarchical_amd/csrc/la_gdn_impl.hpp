@@ -21,7 +21,7 @@
 //   O_c += diag(lambda_lev 2^(b_t + G_j)) Q_j P_j,   Q_{j+1} = Q_j Psi_j,
 // with G_j the log2 gates of the blocks between.
 //
-// Kernels (4 waves per workgroup).  Tiles are staged in LDS in the layer
+// Kernels (8 waves per workgroup).  Tiles are staged in LDS in the layer
 // dtype, with transposed copies where an operand is needed along its other
 // axis, so that every matrix-core operand fragment is one contiguous load;
 // the triangular solve and the accumulators are fp32.
@@ -233,7 +233,7 @@ __device__ __forceinline__ f32x4 load4(const E* p) {
 // (m < i), row-major into Tm (fp32, zeros above the diagonal), by blocks of
 // 16: the diagonal blocks by forward substitution (lane 16 b + j solves
 // column j of block b), then each block row r from the rows above it,
-// T_rj = -T_rr sum_{k<r} L_rk T_kj.  Called by every thread of the
+// T_rj = -T_rr sum_{k<r} L_rk T_kj, on the fp32 matrix cores.  Called by every thread of the
 // workgroup; returns with the workgroup synchronised.
 template <int C>
 __device__ __forceinline__ void solve_blocked(const float* G, const float* beta, float* Tm, float* X) {
@@ -261,26 +261,38 @@ __device__ __forceinline__ void solve_blocked(const float* G, const float* beta,
     for (int i = 0; i < 16; ++i) Tm[(o + i) * LF + o + j] = x[i];
   }
   __syncthreads();
+  // block rows on the fp32 matrix cores (lane l supplies A[l % 16][l / 16]
+  // and B[l / 16][l % 16] of each 16 x 16 x 4 step): wave cb forms
+  // X = beta L[rb, cb..rb-1] T[cb..rb-1, cb], then T[rb, cb] = -T[rb, rb] X
+  const int w = wave_id(), lane = lane_id(), r = lane & 15, kq = lane >> 4;
 #pragma unroll
   for (int rb = 1; rb < NB; ++rb) {
-    const int o = 16 * rb;   // block row rb; its columns 0 .. o-1 below the diagonal block
-    for (int e = tid; e < 16 * o; e += kGdnThreads) {
-      const int r = e / o, cc = e % o;
-      float p0 = 0.f, p1 = 0.f;
-      int mm = cc;
-      for (; mm + 1 < o; mm += 2) {
-        p0 = fmaf(G[(o + r) * LF + mm], Tm[mm * LF + cc], p0);
-        p1 = fmaf(G[(o + r) * LF + mm + 1], Tm[(mm + 1) * LF + cc], p1);
+    const int o = 16 * rb;
+    if (w < rb) {
+      const int oc = 16 * w;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const float br = beta[o + r];
+      for (int kb = w; kb < rb; ++kb) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const int k = 16 * kb + 4 * st + kq;
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(G[(o + r) * LF + k] * br, Tm[k * LF + oc + r], acc, 0, 0, 0);
+        }
       }
-      if (mm < o) p0 = fmaf(G[(o + r) * LF + mm], Tm[mm * LF + cc], p0);
-      X[r * LF + cc] = beta[o + r] * (p0 + p1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) X[(4 * kq + i) * LF + oc + r] = acc[i];
     }
     __syncthreads();
-    for (int e = tid; e < 16 * o; e += kGdnThreads) {
-      const int r = e / o, cc = e % o;
-      float p = 0.f;
-      for (int rr = 0; rr <= r; ++rr) p = fmaf(Tm[(o + r) * LF + o + rr], X[rr * LF + cc], p);
-      Tm[(o + r) * LF + cc] = -p;
+    if (w < rb) {
+      const int oc = 16 * w;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int k = 4 * st + kq;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Tm[(o + r) * LF + o + k], X[k * LF + oc + r], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Tm[(o + 4 * kq + i) * LF + oc + r] = -acc[i];
     }
     __syncthreads();
   }
@@ -416,11 +428,11 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree(GdnArgs a, int m) {
   const TV pr = load_tile<D, D>(ps + iR * DD, D);
   // each wave owns column strips (of P or of Psi): their B operands, taken
   // from the left half in global memory, are loaded once, before the wait
-  constexpr int TN = D / 16, NJ = 2 * TN, JPW = (NJ + 3) / 4;
+  constexpr int TN = D / 16, NJ = 2 * TN, NW = kGdnThreads / 64, JPW = (NJ + NW - 1) / NW;
   BStrip<BF16, D> bs[JPW];
 #pragma unroll
   for (int u = 0; u < JPW; ++u) {
-    const int j = wave_id() + 4 * u;
+    const int j = wave_id() + NW * u;
     if (j < NJ) bs[u] = load_strip<BF16, D>((j >= TN ? ps : pt) + iL * DD, D, 16 * (j % TN));
   }
 #pragma unroll
@@ -440,7 +452,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree(GdnArgs a, int m) {
   // P = 2^gR Psi_R P_L + P_R ; Psi = Psi_R Psi_L (both stored transposed)
 #pragma unroll
   for (int u = 0; u < JPW; ++u) {
-    const int j = wave_id() + 4 * u;
+    const int j = wave_id() + NW * u;
     if (j < NJ) {
       const bool isp = j >= TN;
       const int col = 16 * (j % TN) + tile_col();
@@ -586,8 +598,17 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
     if (t < OT) o[u] = mm_strip<BF16, C>(Al, LDC, vts, (t / TN) * 16, o[u]);
   }
   // bucket nodes of the set bits of c, most recent first; the next node's
-  // strips are loaded while this one is used
+  // strips are loaded while this one is used.  Row weights are
+  // lambda * 2^(b_t) * 2^(G): the per-row gate is formed once (both exponents
+  // are <= 0, so the split only moves underflow below 2^-126)
   constexpr int log2C = gdn_clog2(C);
+  float gam[OPW][4];
+#pragma unroll
+  for (int u = 0; u < OPW; ++u) {
+    const int t = wave_id() + NW * u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gam[u][i] = t < OT ? exp2f(b2[(t / TN) * 16 + tile_row0() + i]) : 0.f;
+  }
   E* cur = Ql;
   E* nxt = Sl;
   float Gs = 0.f;
@@ -603,6 +624,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
       pn = load_strip<BF16, D>(ptb + node2 * (D * D), D, n0d);
       if ((c >> (m2 + 1)) != 0) sn = load_strip<BF16, D>(psb + node2 * (D * D), D, n0d);
     }
+    const float sg = exp2f(Gs);
 #pragma unroll
     for (int u = 0; u < OPW; ++u) {
       const int t = wave_id() + NW * u;
@@ -612,7 +634,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = m0 + tile_row0() + i;
-          o[u][i] = fmaf(lam[row * L + lev] * exp2f(b2[row] + Gs), y[i], o[u][i]);
+          o[u][i] = fmaf(lam[row * L + lev] * gam[u][i] * sg, y[i], o[u][i]);
         }
       }
     }

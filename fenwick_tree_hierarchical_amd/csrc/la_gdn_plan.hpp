@@ -21,7 +21,7 @@
 namespace la {
 
 constexpr int kGdnMaxTree = 32;   // tree levels (n_full_chunks < 2^31)
-constexpr int kGdnThreads = 256;  // 4 waves per workgroup in every kernel
+constexpr int kGdnThreads = 512;  // 8 waves per workgroup in every kernel
 
 // Row stride (elements) of an LDS tile with `cols` columns of es-byte
 // elements: a 16-byte pad, so rows start 16-byte aligned and the rows one
