@@ -155,6 +155,13 @@ template <int C, int D, int ES> struct TileVec {
   static constexpr int VPT = (NV + kGdnThreads - 1) / kGdnThreads;
   u32x4 v[VPT];
 };
+// Thread-to-vector map: consecutive threads take consecutive rows of one
+// 16-byte column, so that the transposed LDS copies written from the
+// vectors land in consecutive addresses (no bank conflicts).
+template <int C, int VPR>
+__device__ __forceinline__ int tile_row(int e) { return e % C; }
+template <int C, int VPR>
+__device__ __forceinline__ int tile_vcol(int e) { return e / C; }
 template <int C, int D, typename E>
 __device__ __forceinline__ TileVec<C, D, sizeof(E)> load_tile(const E* p, int nv) {
   using TV = TileVec<C, D, sizeof(E)>;
@@ -162,9 +169,9 @@ __device__ __forceinline__ TileVec<C, D, sizeof(E)> load_tile(const E* p, int nv
 #pragma unroll
   for (int u = 0; u < TV::VPT; ++u) {
     const int e = threadIdx.x + kGdnThreads * u;
-    const int i = e / TV::VPR;
+    const int i = tile_row<C, TV::VPR>(e), vc = tile_vcol<C, TV::VPR>(e);
     t.v[u] = u32x4{0u, 0u, 0u, 0u};
-    if (e < TV::NV && i < nv) t.v[u] = reinterpret_cast<const u32x4*>(p)[e];
+    if (e < TV::NV && i < nv) t.v[u] = reinterpret_cast<const u32x4*>(p)[i * TV::VPR + vc];
   }
   return t;
 }
@@ -348,7 +355,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_prep(GdnArgs a) {
   for (int u = 0; u < TV::VPT; ++u) {
     const int e = tid + kGdnThreads * u;
     if (e < TV::NV) {
-      const int i = e / TV::VPR, j0 = (e % TV::VPR) * TV::EPV;
+      const int i = tile_row<C, TV::VPR>(e), j0 = tile_vcol<C, TV::VPR>(e) * TV::EPV;
       *reinterpret_cast<u32x4*>(Kr + i * LDD + j0) = kt.v[u];
       const float sb = bet[i], sv = bet[i] * exp2f(g - b2[i]);
 #pragma unroll
@@ -439,7 +446,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree(GdnArgs a, int m) {
   for (int u = 0; u < TV::VPT; ++u) {
     const int e = threadIdx.x + kGdnThreads * u;
     if (e < TV::NV) {
-      const int i = e / TV::VPR, j0 = (e % TV::VPR) * TV::EPV;
+      const int i = tile_row<D, TV::VPR>(e), j0 = tile_vcol<D, TV::VPR>(e) * TV::EPV;
 #pragma unroll
       for (int kk = 0; kk < TV::EPV; ++kk) PsiR[(j0 + kk) * LDD + i] = tile_elem<E, D, D>(pr, u, kk);
     }
@@ -489,6 +496,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
   E* Vt = reinterpret_cast<E*>(smem + LY.vt);
   E* Sl = reinterpret_cast<E*>(smem + LY.s);
   E* Al = reinterpret_cast<E*>(smem + LY.a);
+  E* Pl = reinterpret_cast<E*>(smem + LY.k);      // the masked tile, over K once Q K^T is formed
   float* lam = reinterpret_cast<float*>(smem + LY.lam);
   float* b2 = reinterpret_cast<float*>(smem + LY.b2);
   float* bet = reinterpret_cast<float*>(smem + LY.beta);
@@ -520,19 +528,30 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
   const E* ptb = static_cast<const E*>(a.pt);
   const E* psb = static_cast<const E*>(a.psit);
   const int64_t nf = a.n_full;
-  BStrip<BF16, D> pf{}, sf{};
-  if (c != 0) {
-    const int m = __builtin_ctzll((unsigned long long)c);
+  // node strips two levels deep: (pf, sf) for the current set bit of c,
+  // (pn, sn) for the next one
+  auto next_bit = [&](int m) -> int {   // next set bit of c above m, or -1
+    const int64_t up = m < 0 ? c : (c >> (m + 1));
+    return up == 0 ? -1 : (m + 1 + __builtin_ctzll((unsigned long long)up));
+  };
+  auto load_node = [&](int m, BStrip<BF16, D>& P, BStrip<BF16, D>& S) {
     const int64_t node = a.lev_off[m] + bh * (nf >> m) + (c >> m) - 1;
-    pf = load_strip<BF16, D>(ptb + node * (D * D), D, n0d);
-    if ((c >> (m + 1)) != 0) sf = load_strip<BF16, D>(psb + node * (D * D), D, n0d);
+    P = load_strip<BF16, D>(ptb + node * (D * D), D, n0d);
+    if (next_bit(m) >= 0) S = load_strip<BF16, D>(psb + node * (D * D), D, n0d);
+  };
+  BStrip<BF16, D> pf{}, sf{}, pn{}, sn{};
+  const int mfirst = next_bit(-1);
+  if (mfirst >= 0) {
+    load_node(mfirst, pf, sf);
+    const int msec = next_bit(mfirst);
+    if (msec >= 0) load_node(msec, pn, sn);
   }
   if (wave_id() == 0) gdn_gate_scan<C>(a.log_a + bh * a.T, a.beta + bh * a.T, t0, nv, b2, bet);
 #pragma unroll
   for (int u = 0; u < TV::VPT; ++u) {
     const int e = tid + kGdnThreads * u;
     if (e < TV::NV) {
-      const int i = e / TV::VPR, j0 = (e % TV::VPR) * TV::EPV;
+      const int i = tile_row<C, TV::VPR>(e), j0 = tile_vcol<C, TV::VPR>(e) * TV::EPV;
       *reinterpret_cast<u32x4*>(Ql + i * LDD + j0) = qv.v[u];
       *reinterpret_cast<u32x4*>(Kl + i * LDD + j0) = kv.v[u];
 #pragma unroll
@@ -557,12 +576,20 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
     for (int i = 0; i < 4; ++i) Sl[(row + i) * LDC + col] = to_e<E>(col <= row + i ? acc[i] : 0.f);
   });
   __syncthreads();
-  // Ahat = tril(Q K^T) T diag(beta)
+  // Ahat = tril(Q K^T) T diag(beta), and from it the masked intra tile P:
+  // lambda of the level and the gate ratio
   for_tiles<C, C>([&](int m0, int n0) {
     const f32x4 acc = mm_strip<BF16, C>(Sl, LDC, tbs, m0, f32x4{0.f, 0.f, 0.f, 0.f});
     const int col = n0 + tile_col(), row = m0 + tile_row0();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Al[(row + i) * LDC + col] = to_e<E>(acc[i]);
+    for (int i = 0; i < 4; ++i) {
+      const int t = row + i;
+      Al[t * LDC + col] = to_e<E>(acc[i]);
+      float p = 0.f;
+      if (col <= t && t < nv)
+        p = acc[i] * lam[t * L + fenwick_level_local((unsigned)t, (unsigned)col)] * exp2f(b2[t] - b2[col]);
+      Pl[t * LDC + col] = to_e<E>(p);
+    }
   });
   __syncthreads();
   // carried queries Q' = Q - Ahat K, in place
@@ -576,17 +603,6 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
       qv = to_e<E>(from_e<E>(qv) - acc[i]);
     }
   });
-  __syncthreads();
-  // the masked intra tile: lambda of the level and the gate ratio
-  for (int e = tid; e < C * C; e += kGdnThreads) {
-    const int i = e / C, j = e % C;
-    float p = 0.f;
-    if (j <= i && i < nv)
-      p = from_e<E>(Al[i * LDC + j]) * lam[i * L + fenwick_level_local((unsigned)i, (unsigned)j)] *
-          exp2f(b2[i] - b2[j]);
-    Al[i * LDC + j] = to_e<E>(p);
-  }
-  __syncthreads();
   // O = P V, each wave keeping its output tiles in registers
   const BStrip<BF16, C> vts = load_strip<BF16, C>(Vt, LDC, n0d);
   constexpr int TN = D / 16, OT = (C / 16) * TN, NW = kGdnThreads / 64, OPW = (OT + NW - 1) / NW;
@@ -595,8 +611,9 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
   for (int u = 0; u < OPW; ++u) {
     const int t = wave_id() + NW * u;
     o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (t < OT) o[u] = mm_strip<BF16, C>(Al, LDC, vts, (t / TN) * 16, o[u]);
+    if (t < OT) o[u] = mm_strip<BF16, C>(Pl, LDC, vts, (t / TN) * 16, o[u]);
   }
+  __syncthreads();   // the carried queries are complete
   // bucket nodes of the set bits of c, most recent first; the next node's
   // strips are loaded while this one is used.  Row weights are
   // lambda * 2^(b_t) * 2^(G): the per-row gate is formed once (both exponents
@@ -612,18 +629,13 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
   E* cur = Ql;
   E* nxt = Sl;
   float Gs = 0.f;
-  for (int m = 0; (c >> m) != 0; ++m) {
-    if (!((c >> m) & 1)) continue;
+  for (int m = mfirst; m >= 0; m = next_bit(m)) {
     const int64_t node = a.lev_off[m] + bh * (nf >> m) + (c >> m) - 1;
     const int lev = log2C + 1 + m;
     const int64_t up = c >> (m + 1);
-    BStrip<BF16, D> pn{}, sn{};
-    if (up != 0) {
-      const int m2 = m + 1 + __builtin_ctzll((unsigned long long)up);
-      const int64_t node2 = a.lev_off[m2] + bh * (nf >> m2) + (c >> m2) - 1;
-      pn = load_strip<BF16, D>(ptb + node2 * (D * D), D, n0d);
-      if ((c >> (m2 + 1)) != 0) sn = load_strip<BF16, D>(psb + node2 * (D * D), D, n0d);
-    }
+    BStrip<BF16, D> pn2{}, sn2{};
+    const int m3 = next_bit(next_bit(m) < 0 ? 62 : next_bit(m));
+    if (m3 >= 0) load_node(m3, pn2, sn2);
     const float sg = exp2f(Gs);
 #pragma unroll
     for (int u = 0; u < OPW; ++u) {
@@ -656,6 +668,8 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
       nxt = sw;
       pf = pn;
       sf = sn;
+      pn = pn2;
+      sn = sn2;
     }
   }
   E* op = static_cast<E*>(a.out) + row0 * D;

@@ -58,8 +58,8 @@ LA_HD constexpr GdnPrepLds gdn_prep_lds(int C, int D, int es) {
 // gdn_tree: Psi of the right half, row-major.
 LA_HD constexpr int gdn_tree_lds(int D, int es) { return gdn_tile(D, D, es); }
 
-// gdn_chunk_output: Q (then the carried queries), K, K^T, V^T, tril(Q K^T)
-// (then the second carried-query buffer), Ahat (then the masked tile), the
+// gdn_chunk_output: Q (then the carried queries), K (then the masked tile),
+// K^T, V^T, tril(Q K^T) (then the second carried-query buffer), Ahat, the
 // chunk's lambda rows, gate scan and beta.  (T diag(beta))^T is read from
 // global memory straight into registers.
 struct GdnOutLds {
@@ -71,7 +71,7 @@ LA_HD constexpr GdnOutLds gdn_out_lds(int C, int D, int es, int L) {
   const int v = (C * 4 + 255) / 256 * 256;
   int off = 0;
   o.q = off;   off += cd;
-  o.k = off;   off += cd;
+  o.k = off;   off += gdn_max(cd, cc);     // K, then the masked tile
   o.kt = off;  off += dc;
   o.vt = off;  off += dc;
   o.s = off;   off += gdn_max(cc, cd);
