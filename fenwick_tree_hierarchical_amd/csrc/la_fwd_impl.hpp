@@ -277,9 +277,9 @@ __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
   const bool valid = elem < DD;
   const int64_t ng = a.n_groups, nfg = a.n_full_groups;
   float slot[MAXJ];
-  float sc[MAXJ];
+  float fac[MAXJ];    // gate product from the end of slot j's bucket to the current group
 #pragma unroll
-  for (int j = 0; j < MAXJ; ++j) { slot[j] = 0.f; sc[j] = 0.f; }
+  for (int j = 0; j < MAXJ; ++j) { slot[j] = 0.f; fac[j] = 1.f; }
   double pre = 0.0;
   const bool writer = blk == 0 && threadIdx.x == 0;
   const float* gs = a.gstate + bh * ng * DD;
@@ -303,17 +303,18 @@ __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
       if (e >= nfg) break;
       if (writer) a.gprefix[bh * (ng + 1) + e] = pre;
       const float g = gv[u];
+      const float eg = __builtin_amdgcn_exp2f(g);   // one exponential per group, shared by the slots
       int kk = 0;
       for (int64_t x = e; x & 1; x >>= 1) ++kk;
       float nw = Av[u];
 #pragma unroll
-      for (int j = 0; j < MAXJ; ++j)
-        if (j < kk) nw += __builtin_amdgcn_exp2f(sc[j] + g) * slot[j];
-#pragma unroll
       for (int j = 0; j < MAXJ; ++j) {
-        if (j == kk) { slot[j] = nw; sc[j] = 0.f; }
-        else sc[j] += g;
+        fac[j] *= eg;
+        if (j < kk) nw += fac[j] * slot[j];
       }
+#pragma unroll
+      for (int j = 0; j < MAXJ; ++j)
+        if (j == kk) { slot[j] = nw; fac[j] = 1.f; }
       if (valid) nd[e * DD + elem] = EL::from_f32(nw);
       pre += (double)g;
     }
