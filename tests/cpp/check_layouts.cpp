@@ -5,6 +5,7 @@
 #include <initializer_list>
 
 #include "../../fenwick_tree_hierarchical_amd/csrc/la_bwd_plan.hpp"
+#include "../../fenwick_tree_hierarchical_amd/csrc/la_gdn_plan.hpp"
 
 using namespace la;
 
@@ -94,6 +95,64 @@ int main() {
           CHECK(p.ws_bytes >= p.off_dcol + (size_t)f.BH * T * 4, "T=%lld", T);
           // every group level a key-side block can use has a share slot
           if (f.n_groups > 1) CHECK((1LL << (p.JG - 1)) < f.n_groups && (1LL << p.JG) >= f.n_groups, "T=%lld", T);
+        }
+      }
+
+  // Gated DeltaNet: LDS regions in order, 256-byte aligned, each large enough
+  // for every tile placed in it, inside the limit; workspace regions ordered
+  // and sized; the node levels cover every block a query chunk reads.
+  for (int es : {2, 4})
+    for (int C : {16, 32, 64})
+      for (int D : {16, 32, 64}) {
+        const int tCD = gdn_tile(C, D, es), tDC = gdn_tile(D, C, es), tCC = gdn_tile(C, C, es);
+        const int fCC = gdn_tile(C, C, 4);
+        const GdnPrepLds pl = gdn_prep_lds(C, D, es);
+        const int po[] = {pl.kr, pl.kt, pl.vst, pl.kbt, pl.g, pl.tm, pl.x, pl.b2, pl.beta, pl.total};
+        for (int i = 0; i + 1 < 10; ++i) CHECK(po[i] % 256 == 0 && po[i] < po[i + 1], "gdn prep C=%d D=%d es=%d", C, D, es);
+        CHECK(pl.kt - pl.kr >= tCD && pl.kt - pl.kr >= tDC, "gdn prep K/U^T C=%d D=%d es=%d", C, D, es);
+        CHECK(pl.vst - pl.kt >= tDC && pl.kbt - pl.vst >= tDC && pl.g - pl.kbt >= tDC, "gdn prep C=%d D=%d", C, D);
+        CHECK(pl.tm - pl.g >= fCC && pl.tm - pl.g >= tDC, "gdn prep G/W^T C=%d D=%d es=%d", C, D, es);
+        CHECK(pl.x - pl.tm >= fCC && pl.b2 - pl.x >= 16 * gdn_lde(C, 4) * 4, "gdn prep T/X C=%d D=%d", C, D);
+        CHECK(pl.beta - pl.b2 >= C * 4 && pl.total - pl.beta >= C * 4, "gdn prep gates C=%d", C);
+        CHECK(pl.total <= kLdsLimit, "gdn prep LDS %d C=%d D=%d es=%d", pl.total, C, D, es);
+        CHECK(gdn_tree_lds(D, es) >= D * gdn_lde(D, es) * es && gdn_tree_lds(D, es) <= kLdsLimit, "gdn tree D=%d", D);
+        for (int L = 1; L <= kMaxLevels; ++L) {
+          const GdnOutLds ol = gdn_out_lds(C, D, es, L);
+          const int oo[] = {ol.q, ol.k, ol.kt, ol.vt, ol.s, ol.a, ol.lam, ol.b2, ol.beta, ol.total};
+          for (int i = 0; i + 1 < 10; ++i) CHECK(oo[i] % 256 == 0 && oo[i] < oo[i + 1], "gdn out C=%d D=%d L=%d", C, D, L);
+          CHECK(ol.k - ol.q >= tCD, "gdn out Q C=%d D=%d", C, D);
+          CHECK(ol.kt - ol.k >= tCD && ol.kt - ol.k >= tCC, "gdn out K/P C=%d D=%d es=%d", C, D, es);
+          CHECK(ol.vt - ol.kt >= tDC && ol.s - ol.vt >= tDC, "gdn out K^T/V^T C=%d D=%d", C, D);
+          CHECK(ol.a - ol.s >= tCC && ol.a - ol.s >= tCD, "gdn out S/Qb C=%d D=%d es=%d", C, D, es);
+          CHECK(ol.lam - ol.a >= tCC && ol.b2 - ol.lam >= C * L * 4, "gdn out Ahat/lambda C=%d L=%d", C, L);
+          CHECK(ol.total <= kLdsLimit, "gdn out LDS %d C=%d D=%d es=%d L=%d", ol.total, C, D, es, L);
+          ++n;
+        }
+        for (long long T : {1LL, 15LL, 16LL, 100LL, 1000LL, 4097LL, 16384LL}) {
+          GdnPlan p;
+          const int dt = es == 2 ? kBF16 : kF32;
+          if (plan_gdn(2, 3, T, D, D, C, dt, levels_needed(T), &p) != kOK) {
+            CHECK(false, "gdn plan rejected T=%lld C=%d D=%d", T, C, D);
+            continue;
+          }
+          const size_t DD = (size_t)D * D;
+          CHECK(p.off_tb == 0 && p.ws_bytes >= (size_t)p.BH * p.n_chunks * C * C * es, "gdn tb T=%lld", T);
+          if (p.n_nodes > 0) {
+            CHECK(p.off_pt % 256 == 0 && p.off_pt >= (size_t)p.BH * p.n_chunks * C * C * es, "gdn pt T=%lld", T);
+            CHECK(p.off_psit % 256 == 0 && p.off_psit >= p.off_pt + p.n_nodes * DD * es, "gdn psit T=%lld", T);
+            CHECK(p.off_gn % 256 == 0 && p.off_gn >= p.off_psit + p.n_nodes * DD * es, "gdn gn T=%lld", T);
+            CHECK(p.ws_bytes >= p.off_gn + p.n_nodes * 4, "gdn ws T=%lld", T);
+          }
+          // every block (m, x) a query chunk c reads, x = (c >> m) - 1 for a set
+          // bit m of c, lies inside level m of the node array
+          for (long long c = 0; c < p.n_chunks; ++c)
+            for (int m = 0; m < 62 && (c >> m) != 0; ++m)
+              if ((c >> m) & 1) {
+                CHECK(m < p.n_tree && ((c >> m) - 1) < (p.n_full >> m), "gdn node T=%lld c=%lld m=%d", T, c, m);
+                if (m + 1 < p.n_tree)
+                  CHECK(p.lev_off[m] + p.BH * (p.n_full >> m) <= p.lev_off[m + 1], "gdn levels T=%lld", T);
+              }
+          ++n;
         }
       }
   std::printf("ok %d\n", n);

@@ -5,7 +5,10 @@ checks, for every tile shape, dtype and level count, that each region fits,
 that regions which are live at the same time do not overlap, that the
 overlays (dS over V, the lambda row sums over Q, the level shares over K and
 dS) fit the tile they reuse, and
-that the backward workspace regions are ordered, aligned and sized.
+that the backward workspace regions are ordered, aligned and sized, and, for
+the Gated DeltaNet kernels, that every LDS region holds the tiles placed in it,
+the workspace regions are ordered and sized, and every tree node a query chunk
+reads lies inside its level.
 """
 
 import os
