@@ -25,10 +25,11 @@
 // dtype, with transposed copies where an operand is needed along its other
 // axis, so that every matrix-core operand fragment is one contiguous load;
 // the triangular solve and the accumulators are fp32.
-//   gdn_chunk_prep    per chunk: T by a blocked solve, (T diag(beta))^T for
-//                     the output kernel; per full chunk its node P_c, Psi_c,
-//                     g_c (the tree's level 0)
-//   gdn_tree          per block of 2^m chunks: the merge of its two halves
+//   gdn_chunk_prep    per pair of chunks: T by a blocked solve and
+//                     (T diag(beta))^T for the output kernel; the nodes of
+//                     full chunks (P_c, Psi_c, g_c), the even one stored, and
+//                     their merge (the tree's level 1)
+//   gdn_tree          per block of 2^m chunks, m >= 2: the merge of its halves
 //   gdn_chunk_output  per chunk: the intra tile, the carried queries and the
 //                     level contractions; writes the output.
 #pragma once
@@ -320,15 +321,25 @@ __device__ __forceinline__ void gdn_gate_scan(const float* la, const float* be, 
 }
 
 // ---------------------------------------------------------------------------
-// gdn_chunk_prep: one workgroup per (b,h, chunk).
+// gdn_chunk_prep, one chunk: T by the blocked solve, (T diag(beta))^T written
+// for the output kernel, and for a full chunk its node in registers: each
+// wave holds NPW 16x16 tiles of the state (P) and of the transition (S),
+// tile u being (m0, n0) = (16 (t / TN), 16 (t % TN)), t = wave + NW u, rows
+// m0 + 4 (lane / 16) + i of column n0 + lane % 16.  Returns whether the chunk
+// is full; `gout` is its log2 gate total.
+template <int D> struct PrepTiles {
+  static constexpr int TN = D / 16, NT = TN * TN, NW = kGdnThreads / 64, NPW = (NT + NW - 1) / NW;
+};
+
 template <bool BF16, int C, int D>
-__global__ __launch_bounds__(kGdnThreads) void gdn_chunk_prep(GdnArgs a) {
+__device__ __forceinline__ bool gdn_prep_chunk(const GdnArgs& a, unsigned char* smem, int64_t bh, int64_t c,
+                                               f32x4 (&P)[PrepTiles<D>::NPW], f32x4 (&S)[PrepTiles<D>::NPW],
+                                               float& gout) {
   using EL = Elem<BF16>;
   using E = typename EL::T;
   constexpr int es = sizeof(E);
   constexpr int LDD = gdn_lde(D, es), LDC = gdn_lde(C, es), LF = gdn_lde(C, 4);
   constexpr GdnPrepLds LY = gdn_prep_lds(C, D, es);
-  extern __shared__ __align__(16) unsigned char smem[];
   E* Kr = reinterpret_cast<E*>(smem + LY.kr);
   E* Ut = reinterpret_cast<E*>(smem + LY.kr);     // over K once K K^T is formed
   E* Kt = reinterpret_cast<E*>(smem + LY.kt);
@@ -340,7 +351,6 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_prep(GdnArgs a) {
   float* X = reinterpret_cast<float*>(smem + LY.x);
   float* b2 = reinterpret_cast<float*>(smem + LY.b2);
   float* bet = reinterpret_cast<float*>(smem + LY.beta);
-  const int64_t bh = blockIdx.x / a.n_chunks, c = blockIdx.x % a.n_chunks;
   const int64_t t0 = c * C;
   const int nv = (int)((a.T - t0) < C ? (a.T - t0) : C);
   const bool full = c < a.n_full;
@@ -388,7 +398,8 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_prep(GdnArgs a) {
       reinterpret_cast<u32x4*>(tb)[e] = pack16<E>(x);
     }
   }
-  if (!full) return;
+  gout = g;
+  if (!full) return false;
   // U^T = (gated beta V)^T T^T over K, W^T = (beta K)^T T^T over K K^T
   for_tiles<D, 2 * C>([&](int m0, int n0) {
     const bool isw = n0 >= C;
@@ -399,25 +410,113 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_prep(GdnArgs a) {
     for (int i = 0; i < 4; ++i) dst[(m0 + tile_row0() + i) * LDC + nn + tile_col()] = to_e<E>(acc[i]);
   });
   __syncthreads();
-  // P_c = K^T U and Psi_c = I - K^T W, stored transposed
-  const int64_t node = a.lev_off[0] + bh * a.n_full + c;
+  // P_c = K^T U and Psi_c = I - K^T W
+  using PT = PrepTiles<D>;
+#pragma unroll
+  for (int u = 0; u < PT::NPW; ++u) {
+    const int t = wave_id() + PT::NW * u;
+    if (t < PT::NT) {
+      const int m0 = (t / PT::TN) * 16, n0 = (t % PT::TN) * 16;
+      P[u] = mm_kc<BF16, C>(Kt, LDC, Ut, LDC, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
+      const f32x4 acc = mm_kc<BF16, C>(Kt, LDC, Wt, LDC, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
+      const int col = n0 + tile_col(), row = m0 + tile_row0();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[u][i] = (row + i == col ? 1.f : 0.f) - acc[i];
+    }
+  }
+  return true;
+}
+
+// Node tiles held as in gdn_prep_chunk, stored transposed into node `node`.
+template <bool BF16, int D>
+__device__ __forceinline__ void store_node(const GdnArgs& a, int64_t node, const f32x4 (&P)[PrepTiles<D>::NPW],
+                                           const f32x4 (&S)[PrepTiles<D>::NPW]) {
+  using E = typename Elem<BF16>::T;
+  using PT = PrepTiles<D>;
   E* pt = static_cast<E*>(a.pt) + node * (D * D);
   E* ps = static_cast<E*>(a.psit) + node * (D * D);
-  for_tiles<D, 2 * D>([&](int m0, int n0) {
-    const bool isw = n0 >= D;
-    const int nn = isw ? n0 - D : n0;
-    const f32x4 acc = mm_kc<BF16, C>(Kt, LDC, isw ? Wt : Ut, LDC, m0, nn, f32x4{0.f, 0.f, 0.f, 0.f});
-    const int col = nn + tile_col(), row = m0 + tile_row0();
-    f32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = isw ? ((row + i == col ? 1.f : 0.f) - acc[i]) : acc[i];
-    store4<E>((isw ? ps : pt) + col * D + row, o);
-  });
-  if (tid == 0) a.gn[node] = g;
+  for (int u = 0; u < PT::NPW; ++u) {
+    const int t = wave_id() + PT::NW * u;
+    if (t < PT::NT) {
+      const int col = (t % PT::TN) * 16 + tile_col(), row = (t / PT::TN) * 16 + tile_row0();
+      store4<E>(pt + col * D + row, P[u]);
+      store4<E>(ps + col * D + row, S[u]);
+    }
+  }
+}
+
+// gdn_chunk_prep: one workgroup per (b,h, pair of chunks 2x, 2x+1).  The even
+// chunk's level-0 node is stored (query chunk c reads the level-0 node of
+// chunk c - 1 only for odd c); when both chunks are full, their level-1 node
+// P = 2^(g_1) Psi_1 P_0 + P_1, Psi = Psi_1 Psi_0 is formed here from the
+// register tiles, so odd level-0 nodes are never stored and the tree starts
+// at level 2.
+template <bool BF16, int C, int D>
+__global__ __launch_bounds__(kGdnThreads) void gdn_chunk_prep(GdnArgs a) {
+  using E = typename Elem<BF16>::T;
+  using PT = PrepTiles<D>;
+  constexpr int es = sizeof(E), LDD = gdn_lde(D, es), DD = D * D;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int64_t npair = (a.n_chunks + 1) / 2;
+  const int64_t bh = blockIdx.x / npair, x = blockIdx.x % npair;
+  const int64_t c0 = 2 * x, c1 = c0 + 1;
+  f32x4 P0[PT::NPW], S0[PT::NPW], P1[PT::NPW], S1[PT::NPW];
+  float g0 = 0.f, g1 = 0.f;
+  const bool f0 = gdn_prep_chunk<BF16, C, D>(a, smem, bh, c0, P0, S0, g0);
+  if (f0) {
+    const int64_t node = a.lev_off[0] + bh * a.n_full + c0;
+    store_node<BF16, D>(a, node, P0, S0);
+    if (threadIdx.x == 0) a.gn[node] = g0;
+  }
+  if (c1 >= a.n_chunks) return;
+  __syncthreads();   // the second chunk reuses the LDS
+  const bool f1 = gdn_prep_chunk<BF16, C, D>(a, smem, bh, c1, P1, S1, g1);
+  if (!f1) return;   // a full odd chunk implies a full even one
+  __syncthreads();
+  // Psi_1 row-major, P_0 and Psi_0 transposed (rows = d_v), over the dead tiles
+  constexpr int TB = gdn_tile(D, D, es);
+  E* A1 = reinterpret_cast<E*>(smem);
+  E* B0 = reinterpret_cast<E*>(smem + TB);
+  E* C0 = reinterpret_cast<E*>(smem + 2 * TB);
+#pragma unroll
+  for (int u = 0; u < PT::NPW; ++u) {
+    const int t = wave_id() + PT::NW * u;
+    if (t < PT::NT) {
+      const int col = (t % PT::TN) * 16 + tile_col(), row = (t / PT::TN) * 16 + tile_row0();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        A1[(row + i) * LDD + col] = to_e<E>(S1[u][i]);
+        B0[col * LDD + row + i] = to_e<E>(P0[u][i]);
+        C0[col * LDD + row + i] = to_e<E>(S0[u][i]);
+      }
+    }
+  }
+  __syncthreads();
+  const float s1 = exp2f(g1);
+  const int64_t node = a.lev_off[1] + bh * (a.n_full >> 1) + x;
+  E* pt = static_cast<E*>(a.pt) + node * DD;
+  E* ps = static_cast<E*>(a.psit) + node * DD;
+#pragma unroll
+  for (int u = 0; u < PT::NPW; ++u) {
+    const int t = wave_id() + PT::NW * u;
+    if (t < PT::NT) {
+      const int m0 = (t / PT::TN) * 16, n0 = (t % PT::TN) * 16;
+      const int col = n0 + tile_col(), row = m0 + tile_row0();
+      const f32x4 ap = mm_kc<BF16, D>(A1, LDD, B0, LDD, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
+      const f32x4 as = mm_kc<BF16, D>(A1, LDD, C0, LDD, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = fmaf(s1, ap[i], P1[u][i]);
+      store4<E>(pt + col * D + row, o);
+      store4<E>(ps + col * D + row, as);
+    }
+  }
+  if (threadIdx.x == 0) a.gn[node] = g0 + g1;
 }
 
 // ---------------------------------------------------------------------------
-// gdn_tree: one workgroup per block of 2^m chunks (m >= 1), merging the
+// gdn_tree: one workgroup per block of 2^m chunks (m >= 2), merging the
 // halves of level m - 1.
 template <bool BF16, int D>
 __global__ __launch_bounds__(kGdnThreads) void gdn_tree(GdnArgs a, int m) {
@@ -693,10 +792,10 @@ int launch_gdn_impl(const GdnPlan& p, const GdnArgs& a, hipStream_t s) {
   bool ok = hipFuncSetAttribute((const void*)gdn_chunk_prep<BF16, C, D>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_prep) == hipSuccess;
   if (!ok) return kEHIP;
-  hipLaunchKernelGGL((gdn_chunk_prep<BF16, C, D>), dim3((unsigned)(p.BH * p.n_chunks)), dim3(kGdnThreads),
-                     p.lds_prep, s, a);
+  hipLaunchKernelGGL((gdn_chunk_prep<BF16, C, D>), dim3((unsigned)(p.BH * ((p.n_chunks + 1) / 2))),
+                     dim3(kGdnThreads), p.lds_prep, s, a);
   ok = hipGetLastError() == hipSuccess;
-  for (int m = 1; m < p.n_tree && ok; ++m) {
+  for (int m = 2; m < p.n_tree && ok; ++m) {   // level 1 comes from the prep kernel
     hipLaunchKernelGGL((gdn_tree<BF16, D>), dim3((unsigned)(p.BH * (p.n_full >> m))), dim3(kGdnThreads),
                        p.lds_tree, s, a, m);
     ok = hipGetLastError() == hipSuccess;

@@ -5,8 +5,9 @@
 // Workspace, all per head bh:
 //   tb   [n_chunks][C][C]  layer dtype  (T diag(beta))^T of every chunk, T
 //                          the inverse of I + strict_tril(diag(beta) K K^T)
-//   one node per aligned block of 2^m full chunks (m = 0, 1, ...), level by
-//   level; node (m, bh, x) covers chunks [x 2^m, (x+1) 2^m) and holds
+//   one node slot per aligned block of 2^m full chunks (m = 0, 1, ...), level
+//   by level (odd level-0 slots are never written: no reader needs them);
+//   node (m, bh, x) covers chunks [x 2^m, (x+1) 2^m) and holds
 //   pt   [D][D]  layer dtype  the block's state at its last token, (d_v, d_k)
 //                             order: sum over its keys s of
 //                             Phi(end, s) beta_s k_s v_s^T, transposed
@@ -32,7 +33,8 @@ LA_HD constexpr int gdn_tile(int rows, int cols, int es) { return (rows * gdn_ld
 LA_HD constexpr int gdn_max(int a, int b) { return a > b ? a : b; }
 
 // gdn_chunk_prep: K (then U^T), K^T, (gated beta V)^T, (beta K)^T, K K^T
-// (fp32, then W^T), T (fp32), the blocked solve's scratch, gate scan, beta.
+// (fp32, then W^T), T (fp32), the blocked solve's scratch, gate scan, beta;
+// for the merge of a chunk pair, three D x D tiles from offset 0.
 struct GdnPrepLds {
   int kr, kt, vst, kbt, g, tm, x, b2, beta, total;
 };
@@ -51,7 +53,8 @@ LA_HD constexpr GdnPrepLds gdn_prep_lds(int C, int D, int es) {
   o.x = off;   off += gdn_tile(16, C, 4);
   o.b2 = off;  off += v;
   o.beta = off; off += v;
-  o.total = off;
+  // the merge of a chunk pair stages three D x D tiles from offset 0
+  o.total = gdn_max(off, 3 * gdn_tile(D, D, es));
   return o;
 }
 

@@ -115,6 +115,7 @@ int main() {
         CHECK(pl.x - pl.tm >= fCC && pl.b2 - pl.x >= 16 * gdn_lde(C, 4) * 4, "gdn prep T/X C=%d D=%d", C, D);
         CHECK(pl.beta - pl.b2 >= C * 4 && pl.total - pl.beta >= C * 4, "gdn prep gates C=%d", C);
         CHECK(pl.total <= kLdsLimit, "gdn prep LDS %d C=%d D=%d es=%d", pl.total, C, D, es);
+        CHECK(pl.total >= 3 * gdn_tile(D, D, es), "gdn prep merge staging C=%d D=%d es=%d", C, D, es);
         CHECK(gdn_tree_lds(D, es) >= D * gdn_lde(D, es) * es && gdn_tree_lds(D, es) <= kLdsLimit, "gdn tree D=%d", D);
         for (int L = 1; L <= kMaxLevels; ++L) {
           const GdnOutLds ol = gdn_out_lds(C, D, es, L);
