@@ -1056,7 +1056,7 @@ int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s) {
     ok = ok && hipGetLastError() == hipSuccess;
   }
   if (p.n_groups > 1) {
-    const dim3 grid((unsigned)(((D * D + 255) / 256) * p.BH));
+    const dim3 grid((unsigned)(group_tree_blocks(D) * p.BH));
     const int levels = bit_length(p.n_groups);
     if (levels <= 8)
       hipLaunchKernelGGL((fwd_group_tree<BF16, 8>), grid, dim3(256), 0, s, fa, D);

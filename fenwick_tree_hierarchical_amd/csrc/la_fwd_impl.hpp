@@ -258,64 +258,79 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
 }
 
 // ---------------------------------------------------------------------------
-// Group tree: per (b,h) and state element, walk the full groups with the
-// binary-counter carry.  node[e] = A_e + sum_{j<=k} gate * bucket_j where
+// Group tree: per (b,h) and four consecutive state elements, walk the full
+// groups with the binary-counter carry.  node[e] = A_e + sum_{j<=k} gate * bucket_j where
 // k = trailing ones of e: the bucket of 2^k groups ending at group e.  It
 // also writes gprefix[0 .. n_full_groups], the exclusive prefix sums of the
 // group gate totals.  MAXJ bounds the carry levels (bit length of the group
 // count); the launcher picks the smallest instantiation that covers the
 // sequence.
+// Workgroups of 256 threads per (b,h): four state elements per thread.
+LA_HD constexpr int group_tree_blocks(int D) { return (D * D / 4 + 255) / 256; }
+
 template <bool BF16, int MAXJ>
 __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
   using EL = Elem<BF16>;
   using E = typename EL::T;
-  const int DD = D * D;
-  const int nblk = (DD + 255) / 256;
+  constexpr int V = 4;   // consecutive state elements per thread: one 16-byte load per group
+  const int DD = D * D, NQ = DD / V;
+  const int nblk = group_tree_blocks(D);
   const int64_t bh = blockIdx.x / nblk;
   const int blk = blockIdx.x % nblk;
-  const int elem = blk * 256 + threadIdx.x;
-  const bool valid = elem < DD;
+  const int q4 = blk * 256 + threadIdx.x;
+  const bool valid = q4 < NQ;
   const int64_t ng = a.n_groups, nfg = a.n_full_groups;
-  float slot[MAXJ];
+  f32x4 slot[MAXJ];
   float fac[MAXJ];    // gate product from the end of slot j's bucket to the current group
 #pragma unroll
-  for (int j = 0; j < MAXJ; ++j) { slot[j] = 0.f; fac[j] = 1.f; }
+  for (int j = 0; j < MAXJ; ++j) { slot[j] = f32x4{0.f, 0.f, 0.f, 0.f}; fac[j] = 1.f; }
   double pre = 0.0;
   const bool writer = blk == 0 && threadIdx.x == 0;
-  const float* gs = a.gstate + bh * ng * DD;
+  const f32x4* gs = reinterpret_cast<const f32x4*>(a.gstate + bh * ng * DD);
   E* nd = reinterpret_cast<E*>(a.nodes) + bh * ng * DD;
   constexpr int kBatch = 8;   // independent loads issued together, then walked
   for (int64_t e0 = 0; e0 < nfg; e0 += kBatch) {
-    float Av[kBatch], gv[kBatch];
+    f32x4 Av[kBatch];
+    float gv[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int64_t e = e0 + u;
-      Av[u] = 0.f;
+      Av[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       gv[u] = 0.f;
       if (e < nfg) {
         gv[u] = a.gtot[bh * ng + e];
-        if (valid) Av[u] = gs[e * DD + elem];
+        if (valid) Av[u] = gs[e * NQ + q4];
       }
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int64_t e = e0 + u;
-      if (e >= nfg) break;
+      if (e >= nfg) continue;   // (predicated, so the walk unrolls with constant indices)
       if (writer) a.gprefix[bh * (ng + 1) + e] = pre;
       const float g = gv[u];
       const float eg = __builtin_amdgcn_exp2f(g);   // one exponential per group, shared by the slots
       int kk = 0;
       for (int64_t x = e; x & 1; x >>= 1) ++kk;
-      float nw = Av[u];
+      f32x4 nw = Av[u];
 #pragma unroll
       for (int j = 0; j < MAXJ; ++j) {
         fac[j] *= eg;
-        if (j < kk) nw += fac[j] * slot[j];
+        if (j < kk) {
+#pragma unroll
+          for (int i = 0; i < V; ++i) nw[i] = fmaf(fac[j], slot[j][i], nw[i]);
+        }
       }
 #pragma unroll
       for (int j = 0; j < MAXJ; ++j)
         if (j == kk) { slot[j] = nw; fac[j] = 1.f; }
-      if (valid) nd[e * DD + elem] = EL::from_f32(nw);
+      if (valid) {
+        if constexpr (BF16) {
+          *reinterpret_cast<u16x4*>(nd + e * DD + V * q4) =
+              u16x4{EL::from_f32(nw[0]), EL::from_f32(nw[1]), EL::from_f32(nw[2]), EL::from_f32(nw[3])};
+        } else {
+          *reinterpret_cast<f32x4*>(nd + e * DD + V * q4) = nw;
+        }
+      }
       pre += (double)g;
     }
   }
@@ -876,7 +891,7 @@ int launch_fwd_impl(const FwdPlan& p, FwdArgs a, hipStream_t s, hipEvent_t const
   }
   if (p.n_groups > 1 || (final_state && p.has_group_nodes())) {
     mark();
-    const dim3 grid((unsigned)(((D * D + 255) / 256) * p.BH));
+    const dim3 grid((unsigned)(group_tree_blocks(D) * p.BH));
     const int levels = bit_length(p.n_groups);        // carry levels the walk can reach
     if (levels <= 8)
       hipLaunchKernelGGL((fwd_group_tree<BF16, 8>), grid, dim3(256), 0, s, a, D);
