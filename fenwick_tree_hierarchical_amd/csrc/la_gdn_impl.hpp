@@ -21,6 +21,9 @@
 //   O_c += diag(lambda_lev 2^(b_t + G_j)) Q_j P_j,   Q_{j+1} = Q_j Psi_j,
 // with G_j the log2 gates of the blocks between.
 //
+// Gates enter only as 2^x with x <= 0, taken by the hardware exponential
+// (results below 2^-126 flush to zero).
+//
 // Kernels (8 waves per workgroup).  Tiles are staged in LDS in the layer
 // dtype, with transposed copies where an operand is needed along its other
 // axis, so that every matrix-core operand fragment is one contiguous load;
@@ -367,7 +370,7 @@ __device__ __forceinline__ bool gdn_prep_chunk(const GdnArgs& a, unsigned char* 
     if (e < TV::NV) {
       const int i = tile_row<C, TV::VPR>(e), j0 = tile_vcol<C, TV::VPR>(e) * TV::EPV;
       *reinterpret_cast<u32x4*>(Kr + i * LDD + j0) = kt.v[u];
-      const float sb = bet[i], sv = bet[i] * exp2f(g - b2[i]);
+      const float sb = bet[i], sv = bet[i] * __builtin_amdgcn_exp2f(g - b2[i]);
 #pragma unroll
       for (int kk = 0; kk < TV::EPV; ++kk) {
         const E ke = tile_elem<E, C, D>(kt, u, kk);
@@ -493,7 +496,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_prep(GdnArgs a) {
     }
   }
   __syncthreads();
-  const float s1 = exp2f(g1);
+  const float s1 = __builtin_amdgcn_exp2f(g1);
   const int64_t node = a.lev_off[1] + bh * (a.n_full >> 1) + x;
   E* pt = static_cast<E*>(a.pt) + node * DD;
   E* ps = static_cast<E*>(a.psit) + node * DD;
@@ -551,7 +554,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree(GdnArgs a, int m) {
     }
   }
   const float gR = a.gn[iR];
-  const float sR = exp2f(gR);
+  const float sR = __builtin_amdgcn_exp2f(gR);
   __syncthreads();
   E* pto = static_cast<E*>(a.pt) + io * DD;
   E* pso = static_cast<E*>(a.psit) + io * DD;
@@ -686,7 +689,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
       Al[t * LDC + col] = to_e<E>(acc[i]);
       float p = 0.f;
       if (col <= t && t < nv)
-        p = acc[i] * lam[t * L + fenwick_level_local((unsigned)t, (unsigned)col)] * exp2f(b2[t] - b2[col]);
+        p = acc[i] * lam[t * L + fenwick_level_local((unsigned)t, (unsigned)col)] * __builtin_amdgcn_exp2f(b2[t] - b2[col]);
       Pl[t * LDC + col] = to_e<E>(p);
     }
   });
@@ -723,7 +726,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
   for (int u = 0; u < OPW; ++u) {
     const int t = wave_id() + NW * u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) gam[u][i] = t < OT ? exp2f(b2[(t / TN) * 16 + tile_row0() + i]) : 0.f;
+    for (int i = 0; i < 4; ++i) gam[u][i] = t < OT ? __builtin_amdgcn_exp2f(b2[(t / TN) * 16 + tile_row0() + i]) : 0.f;
   }
   E* cur = Ql;
   E* nxt = Sl;
@@ -735,7 +738,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
     BStrip<BF16, D> pn2{}, sn2{};
     const int m3 = next_bit(next_bit(m) < 0 ? 62 : next_bit(m));
     if (m3 >= 0) load_node(m3, pn2, sn2);
-    const float sg = exp2f(Gs);
+    const float sg = __builtin_amdgcn_exp2f(Gs);
 #pragma unroll
     for (int u = 0; u < OPW; ++u) {
       const int t = wave_id() + NW * u;
