@@ -151,12 +151,35 @@ __device__ __forceinline__ f32x4 mm_strip(const TA* A, int lda, const BStrip<BF1
   return acc;
 }
 
+// The B strip of a row-major tile M[s][n] taken along s (B[n][k] = M[k][n],
+// n0 <= n < n0 + 16): scalar reads, once per wave, before M is reused.
+template <bool BF16, int K, typename TB>
+__device__ __forceinline__ BStrip<BF16, K> load_strip_t(const TB* M, int ldm, int n0) {
+  BStrip<BF16, K> b;
+  const int lane = lane_id(), r = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < BStrip<BF16, K>::N; ++s) {
+    if constexpr (BF16) {
+      const int kk = 32 * s + 8 * kq;
+      bf16x8 f = GFrag::zero();
+      if (K >= 32 || kk < K) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = __builtin_bit_cast(__bf16, M[(kk + i) * ldm + n0 + r]);
+      }
+      b.f[s] = f;
+    } else {
+      b.f[s] = M[(4 * s + kq) * ldm + n0 + r];
+    }
+  }
+  return b;
+}
+
 // 16-byte vectors of a C x D row-major tile of global memory, rows at or
 // past `nv` read as zero: every thread issues its loads before any is used.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-template <int C, int D, int ES> struct TileVec {
+template <int C, int D, int ES, int NT = kGdnThreads> struct TileVec {
   static constexpr int EPV = 16 / ES, VPR = D / EPV, NV = C * VPR;
-  static constexpr int VPT = (NV + kGdnThreads - 1) / kGdnThreads;
+  static constexpr int VPT = (NV + NT - 1) / NT;
   u32x4 v[VPT];
 };
 // Thread-to-vector map: consecutive threads take consecutive rows of one
@@ -166,13 +189,13 @@ template <int C, int VPR>
 __device__ __forceinline__ int tile_row(int e) { return e % C; }
 template <int C, int VPR>
 __device__ __forceinline__ int tile_vcol(int e) { return e / C; }
-template <int C, int D, typename E>
-__device__ __forceinline__ TileVec<C, D, sizeof(E)> load_tile(const E* p, int nv) {
-  using TV = TileVec<C, D, sizeof(E)>;
+template <int C, int D, int NT = kGdnThreads, typename E>
+__device__ __forceinline__ TileVec<C, D, sizeof(E), NT> load_tile(const E* p, int nv) {
+  using TV = TileVec<C, D, sizeof(E), NT>;
   TV t;
 #pragma unroll
   for (int u = 0; u < TV::VPT; ++u) {
-    const int e = threadIdx.x + kGdnThreads * u;
+    const int e = threadIdx.x + NT * u;
     const int i = tile_row<C, TV::VPR>(e), vc = tile_vcol<C, TV::VPR>(e);
     t.v[u] = u32x4{0u, 0u, 0u, 0u};
     if (e < TV::NV && i < nv) t.v[u] = reinterpret_cast<const u32x4*>(p)[i * TV::VPR + vc];
@@ -195,8 +218,8 @@ __device__ __forceinline__ u32x4 pack16(const float* x) {
 }
 
 // Element k of vector u of a loaded tile.
-template <typename E, int C, int D>
-__device__ __forceinline__ E tile_elem(const TileVec<C, D, sizeof(E)>& t, int u, int k) {
+template <typename E, int C, int D, int NT = kGdnThreads>
+__device__ __forceinline__ E tile_elem(const TileVec<C, D, sizeof(E), NT>& t, int u, int k) {
   if constexpr (sizeof(E) == 2) {
     const unsigned w = t.v[u][k >> 1];
     return static_cast<E>((k & 1) ? (w >> 16) : (w & 0xffffu));
@@ -583,55 +606,68 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree(GdnArgs a, int m) {
 }
 
 // ---------------------------------------------------------------------------
-// gdn_chunk_output: one workgroup per (b,h, chunk).
+// gdn_chunk_output: one workgroup of four waves per (b,h, chunk).  LDS holds
+// Q (then the carried queries), K (then Ahat), V (then the masked tile P),
+// tril(Q K^T) (then the second carried-query buffer), the chunk's lambda rows
+// in the layer dtype, its gate scan and betas: 38 KB at C = d = 64 in bf16,
+// so four workgroups fit a CU.  Wave w owns the 16-column strip 16 (w % TN)
+// of every product and keeps its B operands in registers: the K and V strips
+// taken along the tokens before those tiles are overwritten, (T diag(beta))^T
+// and the bucket nodes straight from global memory.
+// bf16 tiles fit four workgroups per CU by LDS; the compiler is held to the
+// 128 registers that allow it (no spills).  fp32 tiles are larger and are
+// left unconstrained.
+template <bool BF16>
+constexpr int gdn_out_min_waves() { return BF16 ? 4 : 1; }
+
 template <bool BF16, int C, int D>
-__global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
+__global__ __launch_bounds__(kGdnOutThreads) __attribute__((amdgpu_waves_per_eu(gdn_out_min_waves<BF16>(), 8)))
+void gdn_chunk_output(GdnArgs a) {
   using EL = Elem<BF16>;
   using E = typename EL::T;
+  constexpr int NT = kGdnOutThreads, NW = NT / 64;
   constexpr int es = sizeof(E);
   constexpr int LDD = gdn_lde(D, es), LDC = gdn_lde(C, es);
+  constexpr int TNC = C / 16, TND = D / 16, RB = C / 16;
+  constexpr int OCC = (RB * TNC + NW - 1) / NW, OCD = (RB * TND + NW - 1) / NW;
   const GdnOutLds LY = gdn_out_lds(C, D, es, a.L);
   extern __shared__ __align__(16) unsigned char smem[];
   E* Ql = reinterpret_cast<E*>(smem + LY.q);
   E* Kl = reinterpret_cast<E*>(smem + LY.k);
-  E* Kt = reinterpret_cast<E*>(smem + LY.kt);
-  E* Vt = reinterpret_cast<E*>(smem + LY.vt);
+  E* Al = Kl;                                      // Ahat, over K once its strips are taken
+  E* Vl = reinterpret_cast<E*>(smem + LY.v);
+  E* Pl = Vl;                                      // P, over V once its strip is taken
   E* Sl = reinterpret_cast<E*>(smem + LY.s);
-  E* Al = reinterpret_cast<E*>(smem + LY.a);
-  E* Pl = reinterpret_cast<E*>(smem + LY.k);      // the masked tile, over K once Q K^T is formed
-  float* lam = reinterpret_cast<float*>(smem + LY.lam);
+  E* lam = reinterpret_cast<E*>(smem + LY.lam);
   float* b2 = reinterpret_cast<float*>(smem + LY.b2);
   float* bet = reinterpret_cast<float*>(smem + LY.beta);
   const int L = a.L;
   const int64_t bh = blockIdx.x / a.n_chunks, c = blockIdx.x % a.n_chunks;
   const int64_t t0 = c * C;
   const int nv = (int)((a.T - t0) < C ? (a.T - t0) : C);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = wave_id();
+  const int n0c = 16 * (w % TNC), n0d = 16 * (w % TND);
   const int64_t row0 = bh * a.T + t0;
-  using TV = TileVec<C, D, es>;
-  const TV qv = load_tile<C, D>(static_cast<const E*>(a.q) + row0 * D, nv);
-  const TV kv = load_tile<C, D>(static_cast<const E*>(a.k) + row0 * D, nv);
-  const TV vv = load_tile<C, D>(static_cast<const E*>(a.v) + row0 * D, nv);
-  constexpr int LPT = (C * kMaxLevels + kGdnThreads - 1) / kGdnThreads;
+  using TV = TileVec<C, D, es, NT>;
+  const TV tq = load_tile<C, D, NT>(static_cast<const E*>(a.q) + row0 * D, nv);
+  const TV tk = load_tile<C, D, NT>(static_cast<const E*>(a.k) + row0 * D, nv);
+  const TV tvv = load_tile<C, D, NT>(static_cast<const E*>(a.v) + row0 * D, nv);
+  constexpr int LPT = (C * kMaxLevels + NT - 1) / NT;
   float lv[LPT];
   const float* lp = a.lam + row0 * L;
 #pragma unroll
   for (int u = 0; u < LPT; ++u) {
-    const int e = tid + kGdnThreads * u;
+    const int e = tid + NT * u;
     lv[u] = e < nv * L ? lp[e] : 0.f;
   }
   // the B strips this wave needs from global memory, issued early: the
-  // columns of (T diag(beta))^T for Ahat, and the first bucket node's state
-  // and transition
-  constexpr int TNC = C / 16, TND = D / 16;
-  const int n0c = 16 * (wave_id() % TNC), n0d = 16 * (wave_id() % TND);
+  // columns of (T diag(beta))^T for Ahat, and the first two bucket nodes'
+  // states and transitions
   const E* tbp = static_cast<const E*>(a.tb) + (bh * a.n_chunks + c) * (C * C);
   const BStrip<BF16, C> tbs = load_strip<BF16, C>(tbp, C, n0c);
   const E* ptb = static_cast<const E*>(a.pt);
   const E* psb = static_cast<const E*>(a.psit);
   const int64_t nf = a.n_full;
-  // node strips two levels deep: (pf, sf) for the current set bit of c,
-  // (pn, sn) for the next one
   auto next_bit = [&](int m) -> int {   // next set bit of c above m, or -1
     const int64_t up = m < 0 ? c : (c >> (m + 1));
     return up == 0 ? -1 : (m + 1 + __builtin_ctzll((unsigned long long)up));
@@ -648,85 +684,92 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
     const int msec = next_bit(mfirst);
     if (msec >= 0) load_node(msec, pn, sn);
   }
-  if (wave_id() == 0) gdn_gate_scan<C>(a.log_a + bh * a.T, a.beta + bh * a.T, t0, nv, b2, bet);
+  if (w == 0) gdn_gate_scan<C>(a.log_a + bh * a.T, a.beta + bh * a.T, t0, nv, b2, bet);
 #pragma unroll
   for (int u = 0; u < TV::VPT; ++u) {
-    const int e = tid + kGdnThreads * u;
+    const int e = tid + NT * u;
     if (e < TV::NV) {
       const int i = tile_row<C, TV::VPR>(e), j0 = tile_vcol<C, TV::VPR>(e) * TV::EPV;
-      *reinterpret_cast<u32x4*>(Ql + i * LDD + j0) = qv.v[u];
-      *reinterpret_cast<u32x4*>(Kl + i * LDD + j0) = kv.v[u];
-#pragma unroll
-      for (int kk = 0; kk < TV::EPV; ++kk) {
-        Kt[(j0 + kk) * LDC + i] = tile_elem<E, C, D>(kv, u, kk);
-        Vt[(j0 + kk) * LDC + i] = tile_elem<E, C, D>(vv, u, kk);
-      }
+      *reinterpret_cast<u32x4*>(Ql + i * LDD + j0) = tq.v[u];
+      *reinterpret_cast<u32x4*>(Kl + i * LDD + j0) = tk.v[u];
+      *reinterpret_cast<u32x4*>(Vl + i * LDD + j0) = tvv.v[u];
     }
   }
 #pragma unroll
   for (int u = 0; u < LPT; ++u) {
-    const int e = tid + kGdnThreads * u;
-    if (e < C * L) lam[e] = lv[u];
+    const int e = tid + NT * u;
+    if (e < C * L) lam[e] = to_e<E>(lv[u]);
   }
   __syncthreads();
-  // tril(Q K^T)
+  // the K and V strips, then tril(Q K^T)
   const BStrip<BF16, D> ks = load_strip<BF16, D>(Kl, LDD, n0c);
-  for_tiles<C, C>([&](int m0, int n0) {
-    const f32x4 acc = mm_strip<BF16, D>(Ql, LDD, ks, m0, f32x4{0.f, 0.f, 0.f, 0.f});
-    const int col = n0 + tile_col(), row = m0 + tile_row0();
+  const BStrip<BF16, C> kts = load_strip_t<BF16, C>(Kl, LDD, n0d);
+  const BStrip<BF16, C> vts = load_strip_t<BF16, C>(Vl, LDD, n0d);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Sl[(row + i) * LDC + col] = to_e<E>(col <= row + i ? acc[i] : 0.f);
-  });
+  for (int u = 0; u < OCC; ++u) {
+    const int t = w + NW * u;
+    if (t < RB * TNC) {
+      const int m0 = (t / TNC) * 16;
+      const f32x4 acc = mm_strip<BF16, D>(Ql, LDD, ks, m0, f32x4{0.f, 0.f, 0.f, 0.f});
+      const int col = n0c + tile_col(), row = m0 + tile_row0();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Sl[(row + i) * LDC + col] = to_e<E>(col <= row + i ? acc[i] : 0.f);
+    }
+  }
   __syncthreads();
   // Ahat = tril(Q K^T) T diag(beta), and from it the masked intra tile P:
   // lambda of the level and the gate ratio
-  for_tiles<C, C>([&](int m0, int n0) {
-    const f32x4 acc = mm_strip<BF16, C>(Sl, LDC, tbs, m0, f32x4{0.f, 0.f, 0.f, 0.f});
-    const int col = n0 + tile_col(), row = m0 + tile_row0();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = row + i;
-      Al[t * LDC + col] = to_e<E>(acc[i]);
-      float p = 0.f;
-      if (col <= t && t < nv)
-        p = acc[i] * lam[t * L + fenwick_level_local((unsigned)t, (unsigned)col)] * __builtin_amdgcn_exp2f(b2[t] - b2[col]);
-      Pl[t * LDC + col] = to_e<E>(p);
+  for (int u = 0; u < OCC; ++u) {
+    const int t = w + NW * u;
+    if (t < RB * TNC) {
+      const int m0 = (t / TNC) * 16;
+      const f32x4 acc = mm_strip<BF16, C>(Sl, LDC, tbs, m0, f32x4{0.f, 0.f, 0.f, 0.f});
+      const int col = n0c + tile_col(), row = m0 + tile_row0();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tr = row + i;
+        Al[tr * LDC + col] = to_e<E>(acc[i]);
+        float p = 0.f;
+        if (col <= tr && tr < nv)
+          p = acc[i] * from_e<E>(lam[tr * L + fenwick_level_local((unsigned)tr, (unsigned)col)]) *
+              __builtin_amdgcn_exp2f(b2[tr] - b2[col]);
+        Pl[tr * LDC + col] = to_e<E>(p);
+      }
     }
-  });
+  }
   __syncthreads();
-  // carried queries Q' = Q - Ahat K, in place
-  const BStrip<BF16, C> kts = load_strip<BF16, C>(Kt, LDC, n0d);
-  for_tiles<C, D>([&](int m0, int n0) {
-    const f32x4 acc = mm_strip<BF16, C>(Al, LDC, kts, m0, f32x4{0.f, 0.f, 0.f, 0.f});
-    const int col = n0 + tile_col(), row = m0 + tile_row0();
+  // carried queries Q' = Q - Ahat K (in place) and O = P V in registers
+  f32x4 o[OCD];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      E& qv = Ql[(row + i) * LDD + col];
-      qv = to_e<E>(from_e<E>(qv) - acc[i]);
-    }
-  });
-  // O = P V, each wave keeping its output tiles in registers
-  const BStrip<BF16, C> vts = load_strip<BF16, C>(Vt, LDC, n0d);
-  constexpr int TN = D / 16, OT = (C / 16) * TN, NW = kGdnThreads / 64, OPW = (OT + NW - 1) / NW;
-  f32x4 o[OPW];
-#pragma unroll
-  for (int u = 0; u < OPW; ++u) {
-    const int t = wave_id() + NW * u;
+  for (int u = 0; u < OCD; ++u) {
+    const int t = w + NW * u;
     o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (t < OT) o[u] = mm_strip<BF16, C>(Pl, LDC, vts, (t / TN) * 16, o[u]);
+    if (t < RB * TND) {
+      const int m0 = (t / TND) * 16;
+      const f32x4 acc = mm_strip<BF16, C>(Al, LDC, kts, m0, f32x4{0.f, 0.f, 0.f, 0.f});
+      const int col = n0d + tile_col(), row = m0 + tile_row0();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        E& qe = Ql[(row + i) * LDD + col];
+        qe = to_e<E>(from_e<E>(qe) - acc[i]);
+      }
+      o[u] = mm_strip<BF16, C>(Pl, LDC, vts, m0, o[u]);
+    }
   }
   __syncthreads();   // the carried queries are complete
-  // bucket nodes of the set bits of c, most recent first; the next node's
-  // strips are loaded while this one is used.  Row weights are
+  // bucket nodes of the set bits of c, most recent first; the node two levels
+  // ahead is loaded while this one is used.  Row weights are
   // lambda * 2^(b_t) * 2^(G): the per-row gate is formed once (both exponents
   // are <= 0, so the split only moves underflow below 2^-126)
   constexpr int log2C = gdn_clog2(C);
-  float gam[OPW][4];
+  float gam[OCD][4];
 #pragma unroll
-  for (int u = 0; u < OPW; ++u) {
-    const int t = wave_id() + NW * u;
+  for (int u = 0; u < OCD; ++u) {
+    const int t = w + NW * u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) gam[u][i] = t < OT ? __builtin_amdgcn_exp2f(b2[(t / TN) * 16 + tile_row0() + i]) : 0.f;
+    for (int i = 0; i < 4; ++i)
+      gam[u][i] = t < RB * TND ? __builtin_amdgcn_exp2f(b2[(t / TND) * 16 + tile_row0() + i]) : 0.f;
   }
   E* cur = Ql;
   E* nxt = Sl;
@@ -740,24 +783,24 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
     if (m3 >= 0) load_node(m3, pn2, sn2);
     const float sg = __builtin_amdgcn_exp2f(Gs);
 #pragma unroll
-    for (int u = 0; u < OPW; ++u) {
-      const int t = wave_id() + NW * u;
-      if (t < OT) {
-        const int m0 = (t / TN) * 16;
+    for (int u = 0; u < OCD; ++u) {
+      const int t = w + NW * u;
+      if (t < RB * TND) {
+        const int m0 = (t / TND) * 16;
         const f32x4 y = mm_strip<BF16, D>(cur, LDD, pf, m0, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = m0 + tile_row0() + i;
-          o[u][i] = fmaf(lam[row * L + lev] * gam[u][i] * sg, y[i], o[u][i]);
+          o[u][i] = fmaf(from_e<E>(lam[row * L + lev]) * gam[u][i] * sg, y[i], o[u][i]);
         }
       }
     }
     if (up != 0) {   // an older node follows: carry the queries through this block
 #pragma unroll
-      for (int u = 0; u < OPW; ++u) {
-        const int t = wave_id() + NW * u;
-        if (t < OT) {
-          const int m0 = (t / TN) * 16;
+      for (int u = 0; u < OCD; ++u) {
+        const int t = w + NW * u;
+        if (t < RB * TND) {
+          const int m0 = (t / TND) * 16;
           const f32x4 acc = mm_strip<BF16, D>(cur, LDD, sf, m0, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
           for (int i = 0; i < 4; ++i) nxt[(m0 + tile_row0() + i) * LDD + n0d + tile_col()] = to_e<E>(acc[i]);
@@ -776,14 +819,14 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_chunk_output(GdnArgs a) {
   }
   E* op = static_cast<E*>(a.out) + row0 * D;
 #pragma unroll
-  for (int u = 0; u < OPW; ++u) {
-    const int t = wave_id() + NW * u;
-    if (t < OT) {
-      const int m0 = (t / TN) * 16, n0 = (t % TN) * 16;
+  for (int u = 0; u < OCD; ++u) {
+    const int t = w + NW * u;
+    if (t < RB * TND) {
+      const int m0 = (t / TND) * 16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = m0 + tile_row0() + i;
-        if (row < nv) op[row * D + n0 + tile_col()] = to_e<E>(o[u][i]);
+        if (row < nv) op[row * D + n0d + tile_col()] = to_e<E>(o[u][i]);
       }
     }
   }
@@ -806,7 +849,7 @@ int launch_gdn_impl(const GdnPlan& p, const GdnArgs& a, hipStream_t s) {
   ok = ok && hipFuncSetAttribute((const void*)gdn_chunk_output<BF16, C, D>,
                                  hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_out) == hipSuccess;
   if (!ok) return kEHIP;
-  hipLaunchKernelGGL((gdn_chunk_output<BF16, C, D>), dim3((unsigned)(p.BH * p.n_chunks)), dim3(kGdnThreads),
+  hipLaunchKernelGGL((gdn_chunk_output<BF16, C, D>), dim3((unsigned)(p.BH * p.n_chunks)), dim3(kGdnOutThreads),
                      p.lds_out, s, a);
   ok = hipGetLastError() == hipSuccess;
   return ok ? kOK : kEHIP;

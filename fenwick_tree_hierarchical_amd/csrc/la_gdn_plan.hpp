@@ -22,7 +22,8 @@
 namespace la {
 
 constexpr int kGdnMaxTree = 32;   // tree levels (n_full_chunks < 2^31)
-constexpr int kGdnThreads = 512;  // 8 waves per workgroup in every kernel
+constexpr int kGdnThreads = 512;     // 8 waves per workgroup: prep and tree kernels
+constexpr int kGdnOutThreads = 256;  // 4 waves per workgroup: output kernel
 
 // Row stride (elements) of an LDS tile with `cols` columns of es-byte
 // elements: a 16-byte pad, so rows start 16-byte aligned and the rows one
@@ -61,25 +62,23 @@ LA_HD constexpr GdnPrepLds gdn_prep_lds(int C, int D, int es) {
 // gdn_tree: Psi of the right half, row-major.
 LA_HD constexpr int gdn_tree_lds(int D, int es) { return gdn_tile(D, D, es); }
 
-// gdn_chunk_output: Q (then the carried queries), K (then the masked tile),
-// K^T, V^T, tril(Q K^T) (then the second carried-query buffer), Ahat, the
-// chunk's lambda rows, gate scan and beta.  (T diag(beta))^T is read from
-// global memory straight into registers.
+// gdn_chunk_output (four waves): Q (then the carried queries), K (then
+// Ahat), V (then the masked tile), tril(Q K^T) (then the second carried-query
+// buffer), the chunk's lambda rows in the layer dtype, gate scan and beta.
+// (T diag(beta))^T and the nodes are read from global memory into registers.
 struct GdnOutLds {
-  int q, k, kt, vt, s, a, lam, b2, beta, total;
+  int q, k, v, s, lam, b2, beta, total;
 };
 LA_HD constexpr GdnOutLds gdn_out_lds(int C, int D, int es, int L) {
   GdnOutLds o{};
-  const int cd = gdn_tile(C, D, es), dc = gdn_tile(D, C, es), cc = gdn_tile(C, C, es);
+  const int cd = gdn_tile(C, D, es), cc = gdn_tile(C, C, es), mx = gdn_max(cd, cc);
   const int v = (C * 4 + 255) / 256 * 256;
   int off = 0;
   o.q = off;   off += cd;
-  o.k = off;   off += gdn_max(cd, cc);     // K, then the masked tile
-  o.kt = off;  off += dc;
-  o.vt = off;  off += dc;
-  o.s = off;   off += gdn_max(cc, cd);
-  o.a = off;   off += cc;
-  o.lam = off; off += (C * L * 4 + 255) / 256 * 256;
+  o.k = off;   off += mx;
+  o.v = off;   off += mx;
+  o.s = off;   off += mx;
+  o.lam = off; off += (C * L * es + 255) / 256 * 256;
   o.b2 = off;  off += v;
   o.beta = off; off += v;
   o.total = off;

@@ -119,14 +119,16 @@ int main() {
         CHECK(gdn_tree_lds(D, es) >= D * gdn_lde(D, es) * es && gdn_tree_lds(D, es) <= kLdsLimit, "gdn tree D=%d", D);
         for (int L = 1; L <= kMaxLevels; ++L) {
           const GdnOutLds ol = gdn_out_lds(C, D, es, L);
-          const int oo[] = {ol.q, ol.k, ol.kt, ol.vt, ol.s, ol.a, ol.lam, ol.b2, ol.beta, ol.total};
-          for (int i = 0; i + 1 < 10; ++i) CHECK(oo[i] % 256 == 0 && oo[i] < oo[i + 1], "gdn out C=%d D=%d L=%d", C, D, L);
+          const int oo[] = {ol.q, ol.k, ol.v, ol.s, ol.lam, ol.b2, ol.beta, ol.total};
+          for (int i = 0; i + 1 < 8; ++i) CHECK(oo[i] % 256 == 0 && oo[i] < oo[i + 1], "gdn out C=%d D=%d L=%d", C, D, L);
           CHECK(ol.k - ol.q >= tCD, "gdn out Q C=%d D=%d", C, D);
-          CHECK(ol.kt - ol.k >= tCD && ol.kt - ol.k >= tCC, "gdn out K/P C=%d D=%d es=%d", C, D, es);
-          CHECK(ol.vt - ol.kt >= tDC && ol.s - ol.vt >= tDC, "gdn out K^T/V^T C=%d D=%d", C, D);
-          CHECK(ol.a - ol.s >= tCC && ol.a - ol.s >= tCD, "gdn out S/Qb C=%d D=%d es=%d", C, D, es);
-          CHECK(ol.lam - ol.a >= tCC && ol.b2 - ol.lam >= C * L * 4, "gdn out Ahat/lambda C=%d L=%d", C, L);
+          CHECK(ol.v - ol.k >= tCD && ol.v - ol.k >= tCC, "gdn out K/Ahat C=%d D=%d es=%d", C, D, es);
+          CHECK(ol.s - ol.v >= tCD && ol.s - ol.v >= tCC, "gdn out V/P C=%d D=%d es=%d", C, D, es);
+          CHECK(ol.lam - ol.s >= tCC && ol.lam - ol.s >= tCD, "gdn out S/Qb C=%d D=%d es=%d", C, D, es);
+          CHECK(ol.b2 - ol.lam >= C * L * es, "gdn out lambda C=%d L=%d", C, L);
           CHECK(ol.total <= kLdsLimit, "gdn out LDS %d C=%d D=%d es=%d L=%d", ol.total, C, D, es, L);
+          if (es == 2 && C == 64 && D == 64 && L == 15)
+            CHECK(4 * ol.total <= kLdsLimit, "gdn out: four workgroups per CU at the 16K shape (%d)", ol.total);
           ++n;
         }
         for (long long T : {1LL, 15LL, 16LL, 100LL, 1000LL, 4097LL, 16384LL}) {
