@@ -165,3 +165,16 @@ def test_training_shape_sampled_rows(variant):
     err = rel_l2(sub, ref)
     say(f"   sampled rel_l2={err:.3e}")
     assert err <= TOL["bf16"]
+
+
+def test_extra_levels_are_ignored():
+    """lambda with more levels than ceil(log2 T) + 1: the extra ones are never read."""
+    dev = need_gpu()
+    w = WORKLOADS["tiny_f32"]
+    x = inputs(w, B=1, H=2, T=300, d=16, seed=91, variant="weak_decay")
+    ref = gpu_gdn(x, 16, dev)
+    big = dict(x)
+    pad = torch.randn(1, 2, 300, 11, generator=torch.Generator().manual_seed(5)).abs()
+    big["lam"] = torch.cat([x["lam"], pad], dim=-1).contiguous()     # L = 10 + 11
+    got = gpu_gdn(big, 16, dev)
+    assert np.array_equal(got, ref)
