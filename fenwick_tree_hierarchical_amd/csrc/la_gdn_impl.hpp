@@ -229,6 +229,43 @@ __device__ __forceinline__ E tile_elem(const TileVec<C, D, sizeof(E), NT>& t, in
   }
 }
 
+// Swizzled tile of rows of COLS elements with no padding: the 16-byte
+// granule g of row m is stored at granule g ^ (m mod min(granules, 8)), so
+// the rows an operand fragment reads at one granule fall in different banks.
+template <typename E, int COLS>
+__device__ __forceinline__ int swz(int m, int col) {
+  constexpr int EPG = 16 / (int)sizeof(E), NG = COLS / EPG, GM = (NG < 8 ? NG : 8) - 1;
+  return m * COLS + ((((col / EPG) ^ (m & GM)) * EPG) | (col % EPG));
+}
+
+// mm_kc with either operand in a swizzled [rows][K] tile (ASW / BSW); the
+// other is stored contiguous along k with its leading dimension.
+template <bool BF16, int K, bool ASW, bool BSW, typename TA, typename TB>
+__device__ __forceinline__ f32x4 mm_sw(const TA* A, int lda, const TB* B, int ldb, int m0, int n0, f32x4 acc) {
+  const int lane = lane_id(), r = lane & 15, kq = lane >> 4;
+  if constexpr (BF16) {
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 32) {
+      const int kk = k0 + 8 * kq;
+      bf16x8 fa = GFrag::zero(), fb = GFrag::zero();
+      if (K >= 32 || kk < K) {
+        fa = GFrag::ld(A + (ASW ? swz<TA, K>(m0 + r, kk) : (m0 + r) * lda + kk));
+        fb = GFrag::ld(B + (BSW ? swz<TB, K>(n0 + r, kk) : (n0 + r) * ldb + kk));
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 4) {
+      const int k = k0 + kq;
+      const float fa = A[ASW ? swz<TA, K>(m0 + r, k) : (m0 + r) * lda + k];
+      const float fb = B[BSW ? swz<TB, K>(n0 + r, k) : (n0 + r) * ldb + k];
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa, fb, acc, 0, 0, 0);
+    }
+  }
+  return acc;
+}
+
 // The 16x16 output tiles of an M x N product dealt round-robin to the waves.
 template <int M, int N, typename F>
 __device__ __forceinline__ void for_tiles(F&& f) {
@@ -366,15 +403,17 @@ __device__ __forceinline__ bool gdn_prep_chunk(const GdnArgs& a, unsigned char* 
   constexpr int es = sizeof(E);
   constexpr int LDD = gdn_lde(D, es), LDC = gdn_lde(C, es), LF = gdn_lde(C, 4);
   constexpr GdnPrepLds LY = gdn_prep_lds(C, D, es);
+  // K row-major (padded), then the solve's scratch, then U^T; the token-major
+  // tiles K^T, (gated beta V)^T (then W^T) and (beta K)^T are swizzled
   E* Kr = reinterpret_cast<E*>(smem + LY.kr);
-  E* Ut = reinterpret_cast<E*>(smem + LY.kr);     // over K once K K^T is formed
+  float* X = reinterpret_cast<float*>(smem + LY.kr);
+  E* Ut = reinterpret_cast<E*>(smem + LY.kr);
   E* Kt = reinterpret_cast<E*>(smem + LY.kt);
   E* Vst = reinterpret_cast<E*>(smem + LY.vst);
+  E* Wt = reinterpret_cast<E*>(smem + LY.vst);
   E* Kbt = reinterpret_cast<E*>(smem + LY.kbt);
-  float* G = reinterpret_cast<float*>(smem + LY.g);
-  E* Wt = reinterpret_cast<E*>(smem + LY.g);      // over K K^T once T is solved
-  float* Tm = reinterpret_cast<float*>(smem + LY.tm);
-  float* X = reinterpret_cast<float*>(smem + LY.x);
+  float* G = reinterpret_cast<float*>(smem + LY.g);   // K K^T, then T in place
+  float* Tm = G;
   float* b2 = reinterpret_cast<float*>(smem + LY.b2);
   float* bet = reinterpret_cast<float*>(smem + LY.beta);
   const int64_t t0 = c * C;
@@ -397,9 +436,10 @@ __device__ __forceinline__ bool gdn_prep_chunk(const GdnArgs& a, unsigned char* 
 #pragma unroll
       for (int kk = 0; kk < TV::EPV; ++kk) {
         const E ke = tile_elem<E, C, D>(kt, u, kk);
-        Kt[(j0 + kk) * LDC + i] = ke;
-        Kbt[(j0 + kk) * LDC + i] = to_e<E>(sb * from_e<E>(ke));
-        Vst[(j0 + kk) * LDC + i] = to_e<E>(sv * from_e<E>(tile_elem<E, C, D>(vt, u, kk)));
+        const int at = swz<E, C>(j0 + kk, i);
+        Kt[at] = ke;
+        Kbt[at] = to_e<E>(sb * from_e<E>(ke));
+        Vst[at] = to_e<E>(sv * from_e<E>(tile_elem<E, C, D>(vt, u, kk)));
       }
     }
   }
@@ -411,7 +451,7 @@ __device__ __forceinline__ bool gdn_prep_chunk(const GdnArgs& a, unsigned char* 
     for (int i = 0; i < 4; ++i) G[(m0 + tile_row0() + i) * LF + n0 + tile_col()] = acc[i];
   });
   __syncthreads();
-  solve_blocked<C>(G, bet, Tm, X);
+  solve_blocked<C>(G, bet, Tm, X);   // in place: every entry of G is read before T is written over it
   // (T diag(beta))^T for the output kernel
   E* tb = static_cast<E*>(a.tb) + (bh * a.n_chunks + c) * (C * C);
   {
@@ -426,14 +466,18 @@ __device__ __forceinline__ bool gdn_prep_chunk(const GdnArgs& a, unsigned char* 
   }
   gout = g;
   if (!full) return false;
-  // U^T = (gated beta V)^T T^T over K, W^T = (beta K)^T T^T over K K^T
-  for_tiles<D, 2 * C>([&](int m0, int n0) {
-    const bool isw = n0 >= C;
-    const int nn = isw ? n0 - C : n0;
-    const f32x4 acc = mm_kc<BF16, C>(isw ? Kbt : Vst, LDC, Tm, LF, m0, nn, f32x4{0.f, 0.f, 0.f, 0.f});
-    E* dst = isw ? Wt : Ut;
+  // U^T = (gated beta V)^T T^T over the scratch, then W^T = (beta K)^T T^T
+  // over the (then dead) gated V tile
+  for_tiles<D, C>([&](int m0, int n0) {
+    const f32x4 acc = mm_sw<BF16, C, true, false>(Vst, 0, Tm, LF, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[(m0 + tile_row0() + i) * LDC + nn + tile_col()] = to_e<E>(acc[i]);
+    for (int i = 0; i < 4; ++i) Ut[swz<E, C>(m0 + tile_row0() + i, n0 + tile_col())] = to_e<E>(acc[i]);
+  });
+  __syncthreads();
+  for_tiles<D, C>([&](int m0, int n0) {
+    const f32x4 acc = mm_sw<BF16, C, true, false>(Kbt, 0, Tm, LF, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Wt[swz<E, C>(m0 + tile_row0() + i, n0 + tile_col())] = to_e<E>(acc[i]);
   });
   __syncthreads();
   // P_c = K^T U and Psi_c = I - K^T W
@@ -443,8 +487,8 @@ __device__ __forceinline__ bool gdn_prep_chunk(const GdnArgs& a, unsigned char* 
     const int t = wave_id() + PT::NW * u;
     if (t < PT::NT) {
       const int m0 = (t / PT::TN) * 16, n0 = (t % PT::TN) * 16;
-      P[u] = mm_kc<BF16, C>(Kt, LDC, Ut, LDC, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
-      const f32x4 acc = mm_kc<BF16, C>(Kt, LDC, Wt, LDC, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
+      P[u] = mm_sw<BF16, C, true, true>(Kt, 0, Ut, 0, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
+      const f32x4 acc = mm_sw<BF16, C, true, true>(Kt, 0, Wt, 0, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
       const int col = n0 + tile_col(), row = m0 + tile_row0();
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[u][i] = (row + i == col ? 1.f : 0.f) - acc[i];
@@ -478,8 +522,14 @@ __device__ __forceinline__ void store_node(const GdnArgs& a, int64_t node, const
 // P = 2^(g_1) Psi_1 P_0 + P_1, Psi = Psi_1 Psi_0 is formed here from the
 // register tiles, so odd level-0 nodes are never stored and the tree starts
 // at level 2.
+// bf16 tiles fit three prep workgroups per CU by LDS; the compiler is held
+// to the 80 registers (six waves per SIMD) that allow it.
+template <bool BF16>
+constexpr int gdn_prep_min_waves() { return BF16 ? 6 : 1; }
+
 template <bool BF16, int C, int D>
-__global__ __launch_bounds__(kGdnThreads) void gdn_chunk_prep(GdnArgs a) {
+__global__ __launch_bounds__(kGdnThreads) __attribute__((amdgpu_waves_per_eu(gdn_prep_min_waves<BF16>(), 8)))
+void gdn_chunk_prep(GdnArgs a) {
   using E = typename Elem<BF16>::T;
   using PT = PrepTiles<D>;
   constexpr int es = sizeof(E), LDD = gdn_lde(D, es), DD = D * D;

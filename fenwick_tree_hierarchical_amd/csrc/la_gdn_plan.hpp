@@ -33,28 +33,26 @@ LA_HD constexpr int gdn_lde(int cols, int es) { return cols + 16 / es; }
 LA_HD constexpr int gdn_tile(int rows, int cols, int es) { return (rows * gdn_lde(cols, es) * es + 255) / 256 * 256; }
 LA_HD constexpr int gdn_max(int a, int b) { return a > b ? a : b; }
 
-// gdn_chunk_prep: K (then U^T), K^T, (gated beta V)^T, (beta K)^T, K K^T
-// (fp32, then W^T), T (fp32), the blocked solve's scratch, gate scan, beta;
-// for the merge of a chunk pair, three D x D tiles from offset 0.
+// gdn_chunk_prep: K row-major (then the solve's fp32 scratch, then U^T),
+// K^T, (gated beta V)^T (then W^T) and (beta K)^T as swizzled token-major
+// tiles, K K^T (fp32, then T in place), gate scan and beta; for the merge of
+// a chunk pair, three D x D tiles from offset 0.
 struct GdnPrepLds {
-  int kr, kt, vst, kbt, g, tm, x, b2, beta, total;
+  int kr, kt, vst, kbt, g, b2, beta, total;
 };
 LA_HD constexpr GdnPrepLds gdn_prep_lds(int C, int D, int es) {
   GdnPrepLds o{};
-  const int sq = gdn_max(gdn_tile(C, D, es), gdn_tile(D, C, es));   // K row-major or U^T
+  const int sw = (D * C * es + 255) / 256 * 256;                    // swizzled D x C tile
   const int f = gdn_tile(C, C, 4);                                  // fp32 C x C
   const int v = (C * 4 + 255) / 256 * 256;
   int off = 0;
-  o.kr = off;  off += sq;
-  o.kt = off;  off += gdn_tile(D, C, es);
-  o.vst = off; off += gdn_tile(D, C, es);
-  o.kbt = off; off += gdn_tile(D, C, es);
-  o.g = off;   off += gdn_max(f, gdn_tile(D, C, es));                // K K^T, then W^T
-  o.tm = off;  off += f;
-  o.x = off;   off += gdn_tile(16, C, 4);
+  o.kr = off;  off += gdn_max(gdn_max(gdn_tile(C, D, es), gdn_tile(16, C, 4)), sw);
+  o.kt = off;  off += sw;
+  o.vst = off; off += sw;
+  o.kbt = off; off += sw;
+  o.g = off;   off += f;
   o.b2 = off;  off += v;
   o.beta = off; off += v;
-  // the merge of a chunk pair stages three D x D tiles from offset 0
   o.total = gdn_max(off, 3 * gdn_tile(D, D, es));
   return o;
 }

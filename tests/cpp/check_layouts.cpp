@@ -107,15 +107,19 @@ int main() {
         const int tCD = gdn_tile(C, D, es), tDC = gdn_tile(D, C, es), tCC = gdn_tile(C, C, es);
         const int fCC = gdn_tile(C, C, 4);
         const GdnPrepLds pl = gdn_prep_lds(C, D, es);
-        const int po[] = {pl.kr, pl.kt, pl.vst, pl.kbt, pl.g, pl.tm, pl.x, pl.b2, pl.beta, pl.total};
-        for (int i = 0; i + 1 < 10; ++i) CHECK(po[i] % 256 == 0 && po[i] < po[i + 1], "gdn prep C=%d D=%d es=%d", C, D, es);
-        CHECK(pl.kt - pl.kr >= tCD && pl.kt - pl.kr >= tDC, "gdn prep K/U^T C=%d D=%d es=%d", C, D, es);
-        CHECK(pl.vst - pl.kt >= tDC && pl.kbt - pl.vst >= tDC && pl.g - pl.kbt >= tDC, "gdn prep C=%d D=%d", C, D);
-        CHECK(pl.tm - pl.g >= fCC && pl.tm - pl.g >= tDC, "gdn prep G/W^T C=%d D=%d es=%d", C, D, es);
-        CHECK(pl.x - pl.tm >= fCC && pl.b2 - pl.x >= 16 * gdn_lde(C, 4) * 4, "gdn prep T/X C=%d D=%d", C, D);
+        const int sw = D * C * es;
+        const int po[] = {pl.kr, pl.kt, pl.vst, pl.kbt, pl.g, pl.b2, pl.beta};
+        for (int i = 0; i + 1 < 7; ++i) CHECK(po[i] % 256 == 0 && po[i] < po[i + 1], "gdn prep C=%d D=%d es=%d", C, D, es);
+        CHECK(pl.kt - pl.kr >= tCD && pl.kt - pl.kr >= 16 * gdn_lde(C, 4) * 4 && pl.kt - pl.kr >= sw,
+              "gdn prep K/X/U^T C=%d D=%d es=%d", C, D, es);
+        CHECK(pl.vst - pl.kt >= sw && pl.kbt - pl.vst >= sw && pl.g - pl.kbt >= sw, "gdn prep swizzled C=%d D=%d", C, D);
+        CHECK(pl.b2 - pl.g >= fCC, "gdn prep G/T C=%d", C);
         CHECK(pl.beta - pl.b2 >= C * 4 && pl.total - pl.beta >= C * 4, "gdn prep gates C=%d", C);
         CHECK(pl.total <= kLdsLimit, "gdn prep LDS %d C=%d D=%d es=%d", pl.total, C, D, es);
         CHECK(pl.total >= 3 * gdn_tile(D, D, es), "gdn prep merge staging C=%d D=%d es=%d", C, D, es);
+        if (es == 2 && C == 64 && D == 64)
+          CHECK(3 * pl.total <= kLdsLimit, "gdn prep: three workgroups per CU at the 16K shape (%d)", pl.total);
+        (void)tDC;
         CHECK(gdn_tree_lds(D, es) >= D * gdn_lde(D, es) * es && gdn_tree_lds(D, es) <= kLdsLimit, "gdn tree D=%d", D);
         for (int L = 1; L <= kMaxLevels; ++L) {
           const GdnOutLds ol = gdn_out_lds(C, D, es, L);
