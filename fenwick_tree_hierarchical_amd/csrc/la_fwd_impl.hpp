@@ -309,8 +309,12 @@ __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
       if (writer) a.gprefix[bh * (ng + 1) + e] = pre;
       const float g = gv[u];
       const float eg = __builtin_amdgcn_exp2f(g);   // one exponential per group, shared by the slots
-      int kk = 0;
-      for (int64_t x = e; x & 1; x >>= 1) ++kk;
+      // trailing ones of e: e0 is a multiple of kBatch, so for u < kBatch - 1
+      // they are those of u, a constant of the unrolled loop (the slot
+      // updates below then resolve at compile time); the last group of a
+      // batch continues into the bits of e0 / kBatch
+      const int kk = (u < kBatch - 1) ? __builtin_ctz(~(unsigned)u)
+                                      : cilog2(kBatch) + __builtin_ctzll(~(unsigned long long)(e0 / kBatch));
       f32x4 nw = Av[u];
 #pragma unroll
       for (int j = 0; j < MAXJ; ++j) {
