@@ -1058,7 +1058,9 @@ int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s) {
   if (p.n_groups > 1) {
     const dim3 grid((unsigned)(group_tree_blocks(D) * p.BH));
     const int levels = bit_length(p.n_groups);
-    if (levels <= 8)
+    if (levels <= 6)
+      hipLaunchKernelGGL((fwd_group_tree<BF16, 6>), grid, dim3(256), 0, s, fa, D);
+    else if (levels <= 8)
       hipLaunchKernelGGL((fwd_group_tree<BF16, 8>), grid, dim3(256), 0, s, fa, D);
     else if (levels <= 16)
       hipLaunchKernelGGL((fwd_group_tree<BF16, 16>), grid, dim3(256), 0, s, fa, D);

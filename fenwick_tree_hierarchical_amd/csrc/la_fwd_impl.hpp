@@ -897,7 +897,9 @@ int launch_fwd_impl(const FwdPlan& p, FwdArgs a, hipStream_t s, hipEvent_t const
     mark();
     const dim3 grid((unsigned)(group_tree_blocks(D) * p.BH));
     const int levels = bit_length(p.n_groups);        // carry levels the walk can reach
-    if (levels <= 8)
+    if (levels <= 6)
+      hipLaunchKernelGGL((fwd_group_tree<BF16, 6>), grid, dim3(256), 0, s, a, D);
+    else if (levels <= 8)
       hipLaunchKernelGGL((fwd_group_tree<BF16, 8>), grid, dim3(256), 0, s, a, D);
     else if (levels <= 16)
       hipLaunchKernelGGL((fwd_group_tree<BF16, 16>), grid, dim3(256), 0, s, a, D);
