@@ -258,21 +258,24 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
 }
 
 // ---------------------------------------------------------------------------
-// Group tree: per (b,h) and four consecutive state elements, walk the full
-// groups with the binary-counter carry.  node[e] = A_e + sum_{j<=k} gate * bucket_j where
+// Group tree: per (b,h) and kTreeVec consecutive state elements, walk the
+// full groups with the binary-counter carry.  node[e] = A_e + sum_{j<=k} gate * bucket_j where
 // k = trailing ones of e: the bucket of 2^k groups ending at group e.  It
 // also writes gprefix[0 .. n_full_groups], the exclusive prefix sums of the
 // group gate totals.  MAXJ bounds the carry levels (bit length of the group
 // count); the launcher picks the smallest instantiation that covers the
 // sequence.
 // Workgroups of 256 threads per (b,h): four state elements per thread.
-LA_HD constexpr int group_tree_blocks(int D) { return (D * D / 4 + 255) / 256; }
+constexpr int kTreeVec = 2;   // consecutive state elements per thread of the group tree
+typedef float ftv __attribute__((ext_vector_type(kTreeVec)));
+typedef unsigned short utv __attribute__((ext_vector_type(kTreeVec)));
+LA_HD constexpr int group_tree_blocks(int D) { return (D * D / kTreeVec + 255) / 256; }
 
 template <bool BF16, int MAXJ>
 __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
   using EL = Elem<BF16>;
   using E = typename EL::T;
-  constexpr int V = 4;   // consecutive state elements per thread: one 16-byte load per group
+  constexpr int V = kTreeVec;   // consecutive state elements per thread: one vector load per group
   const int DD = D * D, NQ = DD / V;
   const int nblk = group_tree_blocks(D);
   const int64_t bh = blockIdx.x / nblk;
@@ -280,22 +283,22 @@ __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
   const int q4 = blk * 256 + threadIdx.x;
   const bool valid = q4 < NQ;
   const int64_t ng = a.n_groups, nfg = a.n_full_groups;
-  f32x4 slot[MAXJ];
+  ftv slot[MAXJ];
   float fac[MAXJ];    // gate product from the end of slot j's bucket to the current group
 #pragma unroll
-  for (int j = 0; j < MAXJ; ++j) { slot[j] = f32x4{0.f, 0.f, 0.f, 0.f}; fac[j] = 1.f; }
+  for (int j = 0; j < MAXJ; ++j) { slot[j] = ftv(0.f); fac[j] = 1.f; }
   double pre = 0.0;
   const bool writer = blk == 0 && threadIdx.x == 0;
-  const f32x4* gs = reinterpret_cast<const f32x4*>(a.gstate + bh * ng * DD);
+  const ftv* gs = reinterpret_cast<const ftv*>(a.gstate + bh * ng * DD);
   E* nd = reinterpret_cast<E*>(a.nodes) + bh * ng * DD;
   constexpr int kBatch = 8;   // independent loads issued together, then walked
   for (int64_t e0 = 0; e0 < nfg; e0 += kBatch) {
-    f32x4 Av[kBatch];
+    ftv Av[kBatch];
     float gv[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int64_t e = e0 + u;
-      Av[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      Av[u] = ftv(0.f);
       gv[u] = 0.f;
       if (e < nfg) {
         gv[u] = a.gtot[bh * ng + e];
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
       // batch continues into the bits of e0 / kBatch
       const int kk = (u < kBatch - 1) ? __builtin_ctz(~(unsigned)u)
                                       : cilog2(kBatch) + __builtin_ctzll(~(unsigned long long)(e0 / kBatch));
-      f32x4 nw = Av[u];
+      ftv nw = Av[u];
 #pragma unroll
       for (int j = 0; j < MAXJ; ++j) {
         fac[j] *= eg;
@@ -329,10 +332,12 @@ __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
         if (j == kk) { slot[j] = nw; fac[j] = 1.f; }
       if (valid) {
         if constexpr (BF16) {
-          *reinterpret_cast<u16x4*>(nd + e * DD + V * q4) =
-              u16x4{EL::from_f32(nw[0]), EL::from_f32(nw[1]), EL::from_f32(nw[2]), EL::from_f32(nw[3])};
+          utv o;
+#pragma unroll
+          for (int i = 0; i < V; ++i) o[i] = EL::from_f32(nw[i]);
+          *reinterpret_cast<utv*>(nd + e * DD + V * q4) = o;
         } else {
-          *reinterpret_cast<f32x4*>(nd + e * DD + V * q4) = nw;
+          *reinterpret_cast<ftv*>(nd + e * DD + V * q4) = nw;
         }
       }
       pre += (double)g;
