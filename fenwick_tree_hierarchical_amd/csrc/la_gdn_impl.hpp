@@ -151,6 +151,26 @@ __device__ __forceinline__ f32x4 mm_strip(const TA* A, int lda, const BStrip<BF1
   return acc;
 }
 
+// The same product with the operands swapped (the strip as the A operand, the
+// rows of A as the B operand): lane l then holds row m0 + l % 16 of the
+// result at the four consecutive columns n0 + 4 (l / 16) + i, so a row weight
+// is one value per lane and a row slice is one contiguous store.
+template <bool BF16, int K, typename TA>
+__device__ __forceinline__ f32x4 mm_strip_t(const TA* A, int lda, const BStrip<BF16, K>& b, int m0, f32x4 acc) {
+  const int lane = lane_id(), r = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < BStrip<BF16, K>::N; ++s) {
+    if constexpr (BF16) {
+      const int kk = 32 * s + 8 * kq;
+      const bf16x8 fa = (K >= 32 || kk < K) ? GFrag::ld(A + (m0 + r) * lda + kk) : GFrag::zero();
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b.f[s], fa, acc, 0, 0, 0);
+    } else {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(b.f[s], A[(m0 + r) * lda + 4 * s + kq], acc, 0, 0, 0);
+    }
+  }
+  return acc;
+}
+
 // The B strip of a row-major tile M[s][n] taken along s (B[n][k] = M[k][n],
 // n0 <= n < n0 + 16): scalar reads, once per wave, before M is reused.
 template <bool BF16, int K, typename TB>
@@ -751,19 +771,23 @@ void gdn_chunk_output(GdnArgs a) {
     if (e < C * L) lam[e] = to_e<E>(lv[u]);
   }
   __syncthreads();
-  // the K and V strips, then tril(Q K^T)
+  // the K and V strips, then tril(Q K^T).  Every product from here on is
+  // taken transposed: lane l holds row m0 + l % 16 of the result at the four
+  // consecutive columns 16 (strip) + 4 (l / 16) + i.
   const BStrip<BF16, D> ks = load_strip<BF16, D>(Kl, LDD, n0c);
   const BStrip<BF16, C> kts = load_strip_t<BF16, C>(Kl, LDD, n0d);
   const BStrip<BF16, C> vts = load_strip_t<BF16, C>(Vl, LDD, n0d);
+  const int orow = tile_col(), ocol = n0d + tile_row0(), ccol = n0c + tile_row0();
 #pragma unroll
   for (int u = 0; u < OCC; ++u) {
     const int t = w + NW * u;
     if (t < RB * TNC) {
-      const int m0 = (t / TNC) * 16;
-      const f32x4 acc = mm_strip<BF16, D>(Ql, LDD, ks, m0, f32x4{0.f, 0.f, 0.f, 0.f});
-      const int col = n0c + tile_col(), row = m0 + tile_row0();
+      const int m0 = (t / TNC) * 16, row = m0 + orow;
+      const f32x4 acc = mm_strip_t<BF16, D>(Ql, LDD, ks, m0, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 sv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Sl[(row + i) * LDC + col] = to_e<E>(col <= row + i ? acc[i] : 0.f);
+      for (int i = 0; i < 4; ++i) sv[i] = ccol + i <= row ? acc[i] : 0.f;
+      store4<E>(Sl + row * LDC + ccol, sv);
     }
   }
   __syncthreads();
@@ -773,19 +797,21 @@ void gdn_chunk_output(GdnArgs a) {
   for (int u = 0; u < OCC; ++u) {
     const int t = w + NW * u;
     if (t < RB * TNC) {
-      const int m0 = (t / TNC) * 16;
-      const f32x4 acc = mm_strip<BF16, C>(Sl, LDC, tbs, m0, f32x4{0.f, 0.f, 0.f, 0.f});
-      const int col = n0c + tile_col(), row = m0 + tile_row0();
+      const int m0 = (t / TNC) * 16, tr = m0 + orow;
+      const f32x4 acc = mm_strip_t<BF16, C>(Sl, LDC, tbs, m0, f32x4{0.f, 0.f, 0.f, 0.f});
+      store4<E>(Al + tr * LDC + ccol, acc);
+      const float b2r = b2[tr];
+      const f32x4 b2c = *reinterpret_cast<const f32x4*>(b2 + ccol);
+      f32x4 pv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tr = row + i;
-        Al[tr * LDC + col] = to_e<E>(acc[i]);
-        float p = 0.f;
+        const int col = ccol + i;
+        pv[i] = 0.f;
         if (col <= tr && tr < nv)
-          p = acc[i] * from_e<E>(lam[tr * L + fenwick_level_local((unsigned)tr, (unsigned)col)]) *
-              __builtin_amdgcn_exp2f(b2[tr] - b2[col]);
-        Pl[tr * LDC + col] = to_e<E>(p);
+          pv[i] = acc[i] * from_e<E>(lam[tr * L + fenwick_level_local((unsigned)tr, (unsigned)col)]) *
+                  __builtin_amdgcn_exp2f(b2r - b2c[i]);
       }
+      store4<E>(Pl + tr * LDC + ccol, pv);
     }
   }
   __syncthreads();
@@ -797,14 +823,11 @@ void gdn_chunk_output(GdnArgs a) {
     o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (t < RB * TND) {
       const int m0 = (t / TND) * 16;
-      const f32x4 acc = mm_strip<BF16, C>(Al, LDC, kts, m0, f32x4{0.f, 0.f, 0.f, 0.f});
-      const int col = n0d + tile_col(), row = m0 + tile_row0();
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        E& qe = Ql[(row + i) * LDD + col];
-        qe = to_e<E>(from_e<E>(qe) - acc[i]);
-      }
-      o[u] = mm_strip<BF16, C>(Pl, LDC, vts, m0, o[u]);
+      const f32x4 acc = mm_strip_t<BF16, C>(Al, LDC, kts, m0, f32x4{0.f, 0.f, 0.f, 0.f});
+      E* qe = Ql + (m0 + orow) * LDD + ocol;
+      const f32x4 q4 = load4<E>(qe);
+      store4<E>(qe, f32x4{q4[0] - acc[0], q4[1] - acc[1], q4[2] - acc[2], q4[3] - acc[3]});
+      o[u] = mm_strip_t<BF16, C>(Pl, LDC, vts, m0, o[u]);
     }
   }
   __syncthreads();   // the carried queries are complete
@@ -813,13 +836,11 @@ void gdn_chunk_output(GdnArgs a) {
   // lambda * 2^(b_t) * 2^(G): the per-row gate is formed once (both exponents
   // are <= 0, so the split only moves underflow below 2^-126)
   constexpr int log2C = gdn_clog2(C);
-  float gam[OCD][4];
+  float gam[OCD];
 #pragma unroll
   for (int u = 0; u < OCD; ++u) {
     const int t = w + NW * u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      gam[u][i] = t < RB * TND ? __builtin_amdgcn_exp2f(b2[(t / TND) * 16 + tile_row0() + i]) : 0.f;
+    gam[u] = t < RB * TND ? __builtin_amdgcn_exp2f(b2[(t / TND) * 16 + orow]) : 0.f;
   }
   E* cur = Ql;
   E* nxt = Sl;
@@ -837,12 +858,10 @@ void gdn_chunk_output(GdnArgs a) {
       const int t = w + NW * u;
       if (t < RB * TND) {
         const int m0 = (t / TND) * 16;
-        const f32x4 y = mm_strip<BF16, D>(cur, LDD, pf, m0, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 y = mm_strip_t<BF16, D>(cur, LDD, pf, m0, f32x4{0.f, 0.f, 0.f, 0.f});
+        const float wr = from_e<E>(lam[(m0 + orow) * L + lev]) * gam[u] * sg;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = m0 + tile_row0() + i;
-          o[u][i] = fmaf(from_e<E>(lam[row * L + lev]) * gam[u][i] * sg, y[i], o[u][i]);
-        }
+        for (int i = 0; i < 4; ++i) o[u][i] = fmaf(wr, y[i], o[u][i]);
       }
     }
     if (up != 0) {   // an older node follows: carry the queries through this block
@@ -851,9 +870,7 @@ void gdn_chunk_output(GdnArgs a) {
         const int t = w + NW * u;
         if (t < RB * TND) {
           const int m0 = (t / TND) * 16;
-          const f32x4 acc = mm_strip<BF16, D>(cur, LDD, sf, m0, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int i = 0; i < 4; ++i) nxt[(m0 + tile_row0() + i) * LDD + n0d + tile_col()] = to_e<E>(acc[i]);
+          store4<E>(nxt + (m0 + orow) * LDD + ocol, mm_strip_t<BF16, D>(cur, LDD, sf, m0, f32x4{0.f, 0.f, 0.f, 0.f}));
         }
       }
       Gs += a.gn[node];
@@ -872,12 +889,8 @@ void gdn_chunk_output(GdnArgs a) {
   for (int u = 0; u < OCD; ++u) {
     const int t = w + NW * u;
     if (t < RB * TND) {
-      const int m0 = (t / TND) * 16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = m0 + tile_row0() + i;
-        if (row < nv) op[row * D + n0d + tile_col()] = to_e<E>(o[u][i]);
-      }
+      const int row = (t / TND) * 16 + orow;
+      if (row < nv) store4<E>(op + row * D + ocol, o[u]);
     }
   }
 }
