@@ -86,8 +86,10 @@ struct GFrag {
 // acc += A[m0:m0+16, 0:K] B[0:K, n0:n0+16] on the matrix cores, with A stored
 // A[m * lda + k] and B stored B[n * ldb + k] (both contiguous along k).
 // Lane l supplies row/column l % 16 and the k-slice l / 16 of its operands;
-// the result holds, in lane l, rows 4 (l / 16) + i of column l % 16.
-template <bool BF16, int K, typename TA, typename TB>
+// the result holds, in lane l, rows 4 (l / 16) + i of column l % 16, or with
+// TR (operands swapped on the matrix cores) row l % 16 at the columns
+// 4 (l / 16) + i.
+template <bool BF16, int K, bool TR = false, typename TA, typename TB>
 __device__ __forceinline__ f32x4 mm_kc(const TA* A, int lda, const TB* B, int ldb, int m0, int n0, f32x4 acc) {
   const int lane = lane_id(), r = lane & 15, kq = lane >> 4;
   if constexpr (BF16) {
@@ -99,14 +101,16 @@ __device__ __forceinline__ f32x4 mm_kc(const TA* A, int lda, const TB* B, int ld
         fa = GFrag::ld(A + (m0 + r) * lda + kk);
         fb = GFrag::ld(B + (n0 + r) * ldb + kk);
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
+      acc = TR ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa, acc, 0, 0, 0)
+               : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
     }
   } else {
 #pragma unroll
     for (int k0 = 0; k0 < K; k0 += 4) {
       const float fa = A[(m0 + r) * lda + k0 + kq];
       const float fb = B[(n0 + r) * ldb + k0 + kq];
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa, fb, acc, 0, 0, 0);
+      acc = TR ? __builtin_amdgcn_mfma_f32_16x16x4f32(fb, fa, acc, 0, 0, 0)
+               : __builtin_amdgcn_mfma_f32_16x16x4f32(fa, fb, acc, 0, 0, 0);
     }
   }
   return acc;
@@ -260,7 +264,7 @@ __device__ __forceinline__ int swz(int m, int col) {
 
 // mm_kc with either operand in a swizzled [rows][K] tile (ASW / BSW); the
 // other is stored contiguous along k with its leading dimension.
-template <bool BF16, int K, bool ASW, bool BSW, typename TA, typename TB>
+template <bool BF16, int K, bool ASW, bool BSW, bool TR = false, typename TA, typename TB>
 __device__ __forceinline__ f32x4 mm_sw(const TA* A, int lda, const TB* B, int ldb, int m0, int n0, f32x4 acc) {
   const int lane = lane_id(), r = lane & 15, kq = lane >> 4;
   if constexpr (BF16) {
@@ -272,7 +276,8 @@ __device__ __forceinline__ f32x4 mm_sw(const TA* A, int lda, const TB* B, int ld
         fa = GFrag::ld(A + (ASW ? swz<TA, K>(m0 + r, kk) : (m0 + r) * lda + kk));
         fb = GFrag::ld(B + (BSW ? swz<TB, K>(n0 + r, kk) : (n0 + r) * ldb + kk));
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
+      acc = TR ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa, acc, 0, 0, 0)
+               : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
     }
   } else {
 #pragma unroll
@@ -280,7 +285,8 @@ __device__ __forceinline__ f32x4 mm_sw(const TA* A, int lda, const TB* B, int ld
       const int k = k0 + kq;
       const float fa = A[ASW ? swz<TA, K>(m0 + r, k) : (m0 + r) * lda + k];
       const float fb = B[BSW ? swz<TB, K>(n0 + r, k) : (n0 + r) * ldb + k];
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa, fb, acc, 0, 0, 0);
+      acc = TR ? __builtin_amdgcn_mfma_f32_16x16x4f32(fb, fa, acc, 0, 0, 0)
+               : __builtin_amdgcn_mfma_f32_16x16x4f32(fa, fb, acc, 0, 0, 0);
     }
   }
   return acc;
@@ -353,7 +359,8 @@ __device__ __forceinline__ void solve_blocked(const float* G, const float* beta,
   }
   __syncthreads();
   // block rows on the fp32 matrix cores (lane l supplies A[l % 16][l / 16]
-  // and B[l / 16][l % 16] of each 16 x 16 x 4 step): wave cb forms
+  // and B[l / 16][l % 16] of each 16 x 16 x 4 step, passed swapped so that
+  // lane l receives row l % 16 at the columns 4 (l / 16) + i): wave cb forms
   // X = beta L[rb, cb..rb-1] T[cb..rb-1, cb], then T[rb, cb] = -T[rb, rb] X
   const int w = wave_id(), lane = lane_id(), r = lane & 15, kq = lane >> 4;
 #pragma unroll
@@ -367,11 +374,10 @@ __device__ __forceinline__ void solve_blocked(const float* G, const float* beta,
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           const int k = 16 * kb + 4 * st + kq;
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(G[(o + r) * LF + k] * br, Tm[k * LF + oc + r], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Tm[k * LF + oc + r], G[(o + r) * LF + k] * br, acc, 0, 0, 0);
         }
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) X[(4 * kq + i) * LF + oc + r] = acc[i];
+      *reinterpret_cast<f32x4*>(X + r * LF + oc + 4 * kq) = acc;
     }
     __syncthreads();
     if (w < rb) {
@@ -380,10 +386,9 @@ __device__ __forceinline__ void solve_blocked(const float* G, const float* beta,
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const int k = 4 * st + kq;
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Tm[(o + r) * LF + o + k], X[k * LF + oc + r], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[k * LF + oc + r], Tm[(o + r) * LF + o + k], acc, 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Tm[(o + 4 * kq + i) * LF + oc + r] = -acc[i];
+      *reinterpret_cast<f32x4*>(Tm + (o + r) * LF + oc + 4 * kq) = f32x4{-acc[0], -acc[1], -acc[2], -acc[3]};
     }
     __syncthreads();
   }
@@ -464,11 +469,11 @@ __device__ __forceinline__ bool gdn_prep_chunk(const GdnArgs& a, unsigned char* 
     }
   }
   __syncthreads();
-  // K K^T (fp32)
+  // K K^T (fp32); the products from here to the node tiles are taken with
+  // swapped operands, so a lane writes four consecutive columns of one row
   for_tiles<C, C>([&](int m0, int n0) {
-    const f32x4 acc = mm_kc<BF16, D>(Kr, LDD, Kr, LDD, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-    for (int i = 0; i < 4; ++i) G[(m0 + tile_row0() + i) * LF + n0 + tile_col()] = acc[i];
+    const f32x4 acc = mm_kc<BF16, D, true>(Kr, LDD, Kr, LDD, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
+    *reinterpret_cast<f32x4*>(G + (m0 + tile_col()) * LF + n0 + tile_row0()) = acc;
   });
   __syncthreads();
   solve_blocked<C>(G, bet, Tm, X);   // in place: every entry of G is read before T is written over it
@@ -489,15 +494,13 @@ __device__ __forceinline__ bool gdn_prep_chunk(const GdnArgs& a, unsigned char* 
   // U^T = (gated beta V)^T T^T over the scratch, then W^T = (beta K)^T T^T
   // over the (then dead) gated V tile
   for_tiles<D, C>([&](int m0, int n0) {
-    const f32x4 acc = mm_sw<BF16, C, true, false>(Vst, 0, Tm, LF, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Ut[swz<E, C>(m0 + tile_row0() + i, n0 + tile_col())] = to_e<E>(acc[i]);
+    const f32x4 acc = mm_sw<BF16, C, true, false, true>(Vst, 0, Tm, LF, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
+    store4<E>(Ut + swz<E, C>(m0 + tile_col(), n0 + tile_row0()), acc);
   });
   __syncthreads();
   for_tiles<D, C>([&](int m0, int n0) {
-    const f32x4 acc = mm_sw<BF16, C, true, false>(Kbt, 0, Tm, LF, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Wt[swz<E, C>(m0 + tile_row0() + i, n0 + tile_col())] = to_e<E>(acc[i]);
+    const f32x4 acc = mm_sw<BF16, C, true, false, true>(Kbt, 0, Tm, LF, m0, n0, f32x4{0.f, 0.f, 0.f, 0.f});
+    store4<E>(Wt + swz<E, C>(m0 + tile_col(), n0 + tile_row0()), acc);
   });
   __syncthreads();
   // P_c = K^T U and Psi_c = I - K^T W
@@ -581,11 +584,9 @@ void gdn_chunk_prep(GdnArgs a) {
     if (t < PT::NT) {
       const int col = (t % PT::TN) * 16 + tile_col(), row = (t / PT::TN) * 16 + tile_row0();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        A1[(row + i) * LDD + col] = to_e<E>(S1[u][i]);
-        B0[col * LDD + row + i] = to_e<E>(P0[u][i]);
-        C0[col * LDD + row + i] = to_e<E>(S0[u][i]);
-      }
+      for (int i = 0; i < 4; ++i) A1[(row + i) * LDD + col] = to_e<E>(S1[u][i]);
+      store4<E>(B0 + col * LDD + row, P0[u]);
+      store4<E>(C0 + col * LDD + row, S0[u]);
     }
   }
   __syncthreads();
