@@ -638,6 +638,17 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree(GdnArgs a, int m) {
     const int j = wave_id() + NW * u;
     if (j < NJ) bs[u] = load_strip<BF16, D>((j >= TN ? ps : pt) + iL * DD, D, 16 * (j % TN));
   }
+  // and the state of the right half at this lane's outputs (P strips only)
+  f32x4 pR[JPW][D / 16];
+#pragma unroll
+  for (int u = 0; u < JPW; ++u) {
+    const int j = wave_id() + NW * u;
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb) {
+      pR[u][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (j < TN) pR[u][mb] = load4<E>(pt + iR * DD + (16 * j + tile_col()) * D + 16 * mb + tile_row0());
+    }
+  }
 #pragma unroll
   for (int u = 0; u < TV::VPT; ++u) {
     const int e = threadIdx.x + kGdnThreads * u;
@@ -665,9 +676,8 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree(GdnArgs a, int m) {
         const int row = m0 + tile_row0();
         f32x4 o = acc;
         if (!isp) {
-          const f32x4 r4 = load4<E>(pt + iR * DD + col * D + row);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = fmaf(sR, acc[i], r4[i]);
+          for (int i = 0; i < 4; ++i) o[i] = fmaf(sR, acc[i], pR[u][m0 / 16][i]);
         }
         store4<E>((isp ? pso : pto) + col * D + row, o);
       }
