@@ -158,12 +158,18 @@ __device__ __forceinline__ f32x4 mm_strip(const TA* A, int lda, const BStrip<BF1
 // The same product with the operands swapped (the strip as the A operand, the
 // rows of A as the B operand): lane l then holds row m0 + l % 16 of the
 // result at the four consecutive columns n0 + 4 (l / 16) + i, so a row weight
-// is one value per lane and a row slice is one contiguous store.
+// is one value per lane and a row slice is one contiguous store.  Only the
+// k-steps that overlap [klo, khi) are taken (wave-uniform bounds): the caller
+// guarantees that both operands' other k contribute nothing (triangular
+// factors).
 template <bool BF16, int K, typename TA>
-__device__ __forceinline__ f32x4 mm_strip_t(const TA* A, int lda, const BStrip<BF16, K>& b, int m0, f32x4 acc) {
+__device__ __forceinline__ f32x4 mm_strip_t(const TA* A, int lda, const BStrip<BF16, K>& b, int m0, f32x4 acc,
+                                            int klo = 0, int khi = K) {
   const int lane = lane_id(), r = lane & 15, kq = lane >> 4;
+  constexpr int KS = BF16 ? 32 : 4;
 #pragma unroll
   for (int s = 0; s < BStrip<BF16, K>::N; ++s) {
+    if (KS * s >= khi || KS * (s + 1) <= klo) continue;
     if constexpr (BF16) {
       const int kk = 32 * s + 8 * kq;
       const bf16x8 fa = (K >= 32 || kk < K) ? GFrag::ld(A + (m0 + r) * lda + kk) : GFrag::zero();
@@ -794,7 +800,8 @@ void gdn_chunk_output(GdnArgs a) {
     const int t = w + NW * u;
     if (t < RB * TNC) {
       const int m0 = (t / TNC) * 16, row = m0 + orow;
-      const f32x4 acc = mm_strip_t<BF16, D>(Ql, LDD, ks, m0, f32x4{0.f, 0.f, 0.f, 0.f});
+      const f32x4 acc = n0c > m0 ? f32x4{0.f, 0.f, 0.f, 0.f}   // above the diagonal
+                                 : mm_strip_t<BF16, D>(Ql, LDD, ks, m0, f32x4{0.f, 0.f, 0.f, 0.f});
       f32x4 sv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) sv[i] = ccol + i <= row ? acc[i] : 0.f;
@@ -809,7 +816,9 @@ void gdn_chunk_output(GdnArgs a) {
     const int t = w + NW * u;
     if (t < RB * TNC) {
       const int m0 = (t / TNC) * 16, tr = m0 + orow;
-      const f32x4 acc = mm_strip_t<BF16, C>(Sl, LDC, tbs, m0, f32x4{0.f, 0.f, 0.f, 0.f});
+      // tril(Q K^T) rows m0.. vanish past key m0 + 15 and the columns n0c.. of
+      // the lower triangular T diag(beta) before key n0c
+      const f32x4 acc = mm_strip_t<BF16, C>(Sl, LDC, tbs, m0, f32x4{0.f, 0.f, 0.f, 0.f}, n0c, m0 + 16);
       store4<E>(Al + tr * LDC + ccol, acc);
       const float b2r = b2[tr];
       const f32x4 b2c = *reinterpret_cast<const f32x4*>(b2 + ccol);
@@ -834,11 +843,12 @@ void gdn_chunk_output(GdnArgs a) {
     o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (t < RB * TND) {
       const int m0 = (t / TND) * 16;
-      const f32x4 acc = mm_strip_t<BF16, C>(Al, LDC, kts, m0, f32x4{0.f, 0.f, 0.f, 0.f});
+      // Ahat and P are lower triangular: rows m0.. vanish past key m0 + 15
+      const f32x4 acc = mm_strip_t<BF16, C>(Al, LDC, kts, m0, f32x4{0.f, 0.f, 0.f, 0.f}, 0, m0 + 16);
       E* qe = Ql + (m0 + orow) * LDD + ocol;
       const f32x4 q4 = load4<E>(qe);
       store4<E>(qe, f32x4{q4[0] - acc[0], q4[1] - acc[1], q4[2] - acc[2], q4[3] - acc[3]});
-      o[u] = mm_strip_t<BF16, C>(Pl, LDC, vts, m0, o[u]);
+      o[u] = mm_strip_t<BF16, C>(Pl, LDC, vts, m0, o[u], 0, m0 + 16);
     }
   }
   __syncthreads();   // the carried queries are complete
