@@ -160,3 +160,32 @@ def test_train_16k_full_size_sampled(variant):
 @pytest.mark.parametrize("variant", [None, "weak_decay"])
 def test_long_128k_full_size_sampled(variant):
     full_size_check("long_128k_bf16", variant, [(0, 5)], 128)
+
+
+@pytest.mark.parametrize("variant", ["no_decay", "no_decay+onehot:16", "no_decay+onehot:23"])
+def test_very_long_sequence_deep_group_tree(variant):
+    """T = 2^23 + 37 tokens (d = 16, C = 16, fp32, one head): 65537 groups of
+    eight chunks, so the group tree walks 17 carry levels (its widest slot
+    instantiation) and lambda has 25 levels.  Without decay every bucket
+    matters; lambda one-hot on level 16 or 23 isolates one deep group node
+    (level 23: buckets of 2^22 keys).  Checked at sampled rows, among them
+    rows whose top bits select the deepest buckets."""
+    dev = need_gpu()
+    import fenwick_tree_hierarchical_amd as la
+    w = WORKLOADS["tiny_f32"]
+    T, C = (1 << 23) + 37, 16
+    say(f"fwd very long sequence T={T} variant={variant}: drawing inputs")
+    x = make_inputs(w, device=dev, B=1, H=1, T=T, d=16, dtype="f32", seed=123, variant=variant)
+    assert x["lam"].shape[-1] == 25
+    out = la.loglinear_fwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], chunk=C)
+    torch.cuda.synchronize()
+    rows = np.array([0, 15, 16, 127, 128, (1 << 15) + 9, (1 << 22) - 1, 1 << 22, (1 << 22) + (1 << 21) + 12345,
+                     (1 << 23) - 1, 1 << 23, T - 1])
+    say(f"   oracle at {len(rows)} rows")
+    xs = to_cpu(x)
+    ref = forms.forward_quadratic(xs["q"], xs["k"], xs["v"], xs["log_a"], xs["lam"], rows=rows, block=4)
+    got = out[:, :, rows].float().cpu().numpy()
+    err = rel_l2(got, ref)
+    say(f"   rel_l2={err:.3e}")
+    assert torch.isfinite(out).all().item()
+    assert err <= TOL["f32"]
