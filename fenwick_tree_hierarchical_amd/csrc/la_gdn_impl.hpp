@@ -232,6 +232,25 @@ __device__ __forceinline__ TileVec<C, D, sizeof(E), NT> load_tile(const E* p, in
   }
   return t;
 }
+// The same with the coalesced map (eight consecutive threads read one
+// 128-byte row whole), for tiles that are staged row-major.
+template <int C, int VPR>
+__device__ __forceinline__ int tile_row_c(int e) { return e / VPR; }
+template <int C, int VPR>
+__device__ __forceinline__ int tile_vcol_c(int e) { return e % VPR; }
+template <int C, int D, int NT = kGdnThreads, typename E>
+__device__ __forceinline__ TileVec<C, D, sizeof(E), NT> load_tile_c(const E* p, int nv) {
+  using TV = TileVec<C, D, sizeof(E), NT>;
+  TV t;
+#pragma unroll
+  for (int u = 0; u < TV::VPT; ++u) {
+    const int e = threadIdx.x + NT * u;
+    const int i = tile_row_c<C, TV::VPR>(e), vc = tile_vcol_c<C, TV::VPR>(e);
+    t.v[u] = u32x4{0u, 0u, 0u, 0u};
+    if (e < TV::NV && i < nv) t.v[u] = reinterpret_cast<const u32x4*>(p)[i * TV::VPR + vc];
+  }
+  return t;
+}
 // 16 bytes of E built from 16 / sizeof(E) floats.
 template <typename E>
 __device__ __forceinline__ u32x4 pack16(const float* x) {
@@ -736,9 +755,9 @@ void gdn_chunk_output(GdnArgs a) {
   const int n0c = 16 * (w % TNC), n0d = 16 * (w % TND);
   const int64_t row0 = bh * a.T + t0;
   using TV = TileVec<C, D, es, NT>;
-  const TV tq = load_tile<C, D, NT>(static_cast<const E*>(a.q) + row0 * D, nv);
-  const TV tk = load_tile<C, D, NT>(static_cast<const E*>(a.k) + row0 * D, nv);
-  const TV tvv = load_tile<C, D, NT>(static_cast<const E*>(a.v) + row0 * D, nv);
+  const TV tq = load_tile_c<C, D, NT>(static_cast<const E*>(a.q) + row0 * D, nv);
+  const TV tk = load_tile_c<C, D, NT>(static_cast<const E*>(a.k) + row0 * D, nv);
+  const TV tvv = load_tile_c<C, D, NT>(static_cast<const E*>(a.v) + row0 * D, nv);
   constexpr int LPT = (C * kMaxLevels + NT - 1) / NT;
   float lv[LPT];
   const float* lp = a.lam + row0 * L;
@@ -776,7 +795,7 @@ void gdn_chunk_output(GdnArgs a) {
   for (int u = 0; u < TV::VPT; ++u) {
     const int e = tid + NT * u;
     if (e < TV::NV) {
-      const int i = tile_row<C, TV::VPR>(e), j0 = tile_vcol<C, TV::VPR>(e) * TV::EPV;
+      const int i = tile_row_c<C, TV::VPR>(e), j0 = tile_vcol_c<C, TV::VPR>(e) * TV::EPV;
       *reinterpret_cast<u32x4*>(Ql + i * LDD + j0) = tq.v[u];
       *reinterpret_cast<u32x4*>(Kl + i * LDD + j0) = tk.v[u];
       *reinterpret_cast<u32x4*>(Vl + i * LDD + j0) = tvv.v[u];
