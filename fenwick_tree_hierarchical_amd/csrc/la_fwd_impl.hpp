@@ -788,44 +788,66 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- occupied levels above the chunk: O += diag(lambda * gate) Q node^T.
-  // The row gate exp2(b) and the bucket gate exp2(gate2) are both <= 1.
-  auto contract = [&](int li, const Frag (&nfr)[KSD][NCB]) {
+  // ---- occupied levels above the chunk: O += diag(lambda * gate) Q node^T,
+  // two levels per pass so that each Q fragment is read once for both (the
+  // second level's terms are still added after the first's).  The row gate
+  // exp2(b) and the bucket gate exp2(gate2) are both <= 1.
+  auto level_of = [&](int li, float& f, int& lv) {
     const int el = __builtin_amdgcn_readlane(ent, li);
-    const float f = __builtin_amdgcn_exp2f(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g2), el)));
-    const int lv = __builtin_amdgcn_readlane(lev, el);
+    f = __builtin_amdgcn_exp2f(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g2), el)));
+    lv = __builtin_amdgcn_readlane(lev, el);
+  };
+  auto contract2 = [&](int li, const Frag (&nf0)[KSD][NCB], bool two, const Frag (&nf1)[KSD][NCB]) {
+    float f0, f1 = 0.f;
+    int lv0, lv1 = 0;
+    level_of(li, f0, lv0);
+    if (two) level_of(li + 1, f1, lv1);
 #pragma unroll
     for (int rb = 0; rb < QB; ++rb) {
-      f32x4 tmp[NCB];
+      f32x4 t0[NCB], t1[NCB];
 #pragma unroll
-      for (int n = 0; n < NCB; ++n) tmp[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < NCB; ++n) t0[n] = t1[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s2 = 0; s2 < KSD; ++s2) {
         const int k0 = s2 * KST + lq * KPL;
         const auto qf = EL::template load_k<D>(Qs + (16 * rb + lr) * lay.ld_row + k0, k0);
 #pragma unroll
-        for (int n = 0; n < NCB; ++n) tmp[n] = EL::mma(nfr[s2][n], qf, tmp[n]);
+        for (int n = 0; n < NCB; ++n) {
+          t0[n] = EL::mma(nf0[s2][n], qf, t0[n]);
+          if (two) t1[n] = EL::mma(nf1[s2][n], qf, t1[n]);
+        }
       }
       const int r = 16 * rb + lr;                   // this lane's query row
-      const float wgt = lamS[r * L + lv] * e2c[r] * f;
+      const float e = e2c[r];
+      const float w0 = lamS[r * L + lv0] * e * f0;
 #pragma unroll
       for (int n = 0; n < NCB; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[rb][n][i] += wgt * tmp[n][i];
+        for (int i = 0; i < 4; ++i) acc[rb][n][i] += w0 * t0[n][i];
+      if (two) {
+        const float w1 = lamS[r * L + lv1] * e * f1;
+#pragma unroll
+        for (int n = 0; n < NCB; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[rb][n][i] += w1 * t1[n][i];
+      }
       // keep the next row block's Q fragments from being hoisted: live ranges
       // stay one row block long
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // ring of NPRE fragment buffers: level li uses buffer li % NPRE and, once
-  // multiplied, the buffer takes level li + NPRE
+  // ring of NPRE (even) fragment buffers: level li uses buffer li % NPRE and,
+  // once multiplied, the buffer takes level li + NPRE
+  static_assert(NPRE % 2 == 0, "levels are contracted in pairs");
   for (int base = 0; base < n_lev; base += NPRE) {
 #pragma unroll
-    for (int u = 0; u < NPRE; ++u) {
+    for (int u = 0; u < NPRE; u += 2) {
       const int li = base + u;
       if (li >= n_lev) break;
-      contract(li, nf[u]);
+      const bool two = li + 1 < n_lev;
+      contract2(li, nf[u], two, nf[u + 1]);
       if (li + NPRE < n_lev) load_node(li + NPRE, nf[u]);
+      if (li + 1 + NPRE < n_lev) load_node(li + 1 + NPRE, nf[u + 1]);
     }
   }
 
