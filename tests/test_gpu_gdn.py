@@ -178,3 +178,18 @@ def test_extra_levels_are_ignored():
     big["lam"] = torch.cat([x["lam"], pad], dim=-1).contiguous()     # L = 10 + 11
     got = gpu_gdn(big, 16, dev)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("variant", ["no_decay", "no_decay+onehot:16"])
+def test_deep_chunk_tree(variant):
+    """T = 2^16 + 5 tokens (d = 16, C = 16, fp32, one head): 4096 full chunks,
+    so the chunk tree has levels 0..12 (the tree kernel runs for m = 2..12)
+    and chunk indices carry up to 12 set bits.  Without decay every bucket
+    contributes; lambda one-hot on level 16 isolates the blocks of 2^11
+    chunks.  The whole output against the oracle's recurrence."""
+    dev = need_gpu()
+    w = WORKLOADS["tiny_f32"]
+    T = (1 << 16) + 5
+    x = inputs(w, B=1, H=1, T=T, d=16, dtype="f32", seed=97, variant=variant)
+    assert x["lam"].shape[-1] == 18
+    check(x, 16, "f32", dev, f"deep chunk tree T={T} {variant}")
