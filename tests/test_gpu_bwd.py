@@ -213,3 +213,33 @@ def test_long_128k_full_size_sampled():
         err = rel_l2(got, ref[name])
         say(f"   {name} rel_l2={err:.3e}")
         assert err <= TOL["bf16"], name
+
+
+def test_very_long_sequence_deep_group_trees():
+    """T = 2^23 + 37 tokens (d = 16, C = 16, fp32, one head), no decay: the
+    query-side group tree over 65537 groups (17 carry levels, its widest
+    slot instantiation) and the key-side tree at the same depth.  dq, dk, dv
+    and dlambda at 5 sampled rows against the oracle, and the identity
+    q_t . dq_t = dout_t . o_t on every row."""
+    dev = need_gpu()
+    import fenwick_tree_hierarchical_amd as la
+    w = WORKLOADS["tiny_f32"]
+    T, C = (1 << 23) + 37, 16
+    say(f"bwd very long sequence T={T}: drawing inputs")
+    x = make_inputs(w, device=dev, B=1, H=1, T=T, d=16, dtype="f32", seed=321, variant="no_decay")
+    dout = make_grad_out(w, device=dev, B=1, H=1, T=T, d=16, dtype="f32", seed=322)
+    dq, dk, dv, dla, dlam = la.loglinear_bwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], dout, chunk=C)
+    out = la.loglinear_fwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], chunk=C)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv, dla, dlam):
+        assert torch.isfinite(t).all().item()
+    row = (dout * out).sum(-1)
+    assert rel_l2((x["q"] * dq).sum(-1).cpu().double().numpy(), row.cpu().double().numpy()) <= TOL["f32"]
+    rows = np.array([17, 1 << 22, (1 << 22) + (1 << 21) + 999, (1 << 23) - 1, T - 1])
+    say("   oracle at sampled rows")
+    xs = to_cpu(x)
+    ref = backward.backward_sampled(xs["q"], xs["k"], xs["v"], xs["log_a"], xs["lam"], dout.cpu(), rows)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dlam", dlam)):
+        err = rel_l2(t[:, :, rows].cpu().double().numpy(), ref[name])
+        say(f"   {name} rel_l2={err:.3e}")
+        assert err <= TOL["f32"], name
