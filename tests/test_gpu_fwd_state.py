@@ -147,3 +147,34 @@ def test_decode_32k_handoff_256_steps():
     err_o = rel_l2(got_s, ref[:, :, w.prefix:])
     say(f"   decode vs oracle (2 heads) rel_l2={err_o:.3e}")
     assert err_o <= TOL["bf16"]
+
+
+def test_handoff_after_very_long_prefill():
+    """A prefill of 2^23 + 37 tokens (d = 16, C = 16, fp32, one head, no
+    decay: slots 0, 2, 5 and 23 occupied, the last one a bucket of 2^23
+    keys), then 40 decode steps; they equal the GPU forward over all
+    2^23 + 77 tokens and the oracle at sampled steps."""
+    dev = need_gpu()
+    import fenwick_tree_hierarchical_amd as la
+    from tests.test_gpu_decode import run_decode
+    P, N, C = (1 << 23) + 37, 40, 16
+    T = P + N
+    S = T.bit_length() + 1
+    say(f"hand-off after a {P}-token prefill: drawing inputs")
+    x = make_inputs(WORKLOADS["tiny_f32"], device=dev, B=1, H=1, T=T, L=S + 1, d=16, dtype="f32", seed=55,
+                    variant="no_decay")
+    pre = {k: v[:, :, :P].contiguous() for k, v in x.items()}
+    _, st = gpu_state(pre, S, C, dev)
+    assert st.t == P
+    got, st = run_decode(x, S, dev, st=st, t0=P)
+    assert st.t == T
+    full = la.loglinear_fwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], chunk=C)
+    err_f = rel_l2(got, full[:, :, P:].float().cpu().numpy())
+    say(f"   decode vs GPU forward rel_l2={err_f:.3e}")
+    assert err_f <= TOL["f32"]
+    steps = np.array([0, 1, 7, 26, 39])
+    xs = to_cpu(x)
+    ref = forms.forward_quadratic(xs["q"], xs["k"], xs["v"], xs["log_a"], xs["lam"], rows=P + steps, block=4)
+    err_o = rel_l2(got[:, :, steps], ref)
+    say(f"   decode vs oracle ({len(steps)} steps) rel_l2={err_o:.3e}")
+    assert err_o <= TOL["f32"]
