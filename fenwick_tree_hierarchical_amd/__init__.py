@@ -278,10 +278,6 @@ class LogLinearState:
         c._st = _LaState(st.t, st.B, st.H, st.dk, st.dv, st.S, c.slots.data_ptr(), c.scale.data_ptr())
         return c
 
-    def effective_slots(self) -> torch.Tensor:
-        """scale * slots: the bucket matrices themselves ([B,H,S,dk,dv])."""
-        return self.slots * self.scale[..., None, None]
-
 
 def loglinear_fwd_state(q, k, v, log_a, lam, state: LogLinearState, out=None, chunk: int = 64,
                         workspace=None):
@@ -312,8 +308,13 @@ def loglinear_decode_step(state: LogLinearState, q, k, v, a, lam, out=None):
         raise ValueError("a or lambda shape does not match the state")
     if a.dtype != torch.float32 or lam.dtype != torch.float32:
         raise TypeError("a and lambda must be float32")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
     if out is None:
         out = torch.empty(st.B, st.H, st.dv, dtype=q.dtype, device=dev)
+    _dev(q, out)
+    if out.shape != (st.B, st.H, st.dv) or out.dtype != q.dtype:
+        raise ValueError("out has the wrong shape or dtype")
     _check(lib().loglinear_decode_step(ctypes.byref(st), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(lam),
                                        _ptr(out), _dtype_code(q.dtype), _stream(dev)), "loglinear_decode_step")
     return out

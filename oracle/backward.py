@@ -23,7 +23,10 @@ M^S[t,s] = exp(Lambda_t - Lambda_s) moves with Lambda_t (+) and Lambda_s (-).
 Levels with no key (empty buckets) get a zero lambda gradient.
 
 ``backward_sampled`` evaluates the same sums at chosen query and key rows only
-(long sequences); it is pinned to ``backward_quadratic``.
+(long sequences); it is pinned to ``backward_quadratic``.  ``dlog_a_rows``
+gives the gate gradient at chosen positions of long sequences through the
+forward recurrence (see its docstring); it is pinned to ``backward_quadratic``
+too.
 
 Pins (tests/test_oracle_backward.py): every entry of every gradient against
 central finite differences of the forward oracle (both of its forms) on tiny
@@ -122,6 +125,32 @@ def backward_sampled(q, k, v, log_a, lam, dout, rows):
                 a_ts = lam[b, h, t, lv] * np.exp(cum[t] - cum[s])
                 res["dk"][b, h, i] = (a_ts * (dout[b, h, t] @ v[b, h, s])) @ q[b, h, t]
                 res["dv"][b, h, i] = (a_ts * (q[b, h, t] @ k[b, h, s])) @ dout[b, h, t]
+    return res
+
+
+def dlog_a_rows(q, k, v, log_a, lam, dout, rows):
+    """The gate gradient at positions ``rows`` of long sequences; [B, H, len(rows)].
+
+    Summing dLambda_u = sum_s G[u,s] - sum_t G[t,u] (G = A . S . dP on the
+    pairs s <= t) over u >= r leaves exactly the pairs that straddle r:
+
+        dlog_a_r = sum_{t >= r} sum_{s < r} G[t,s]
+                 = sum_{t >= r} dout_t . o_t^{(<r)},
+
+    where o^{(<r)} is the operator's output with the keys s >= r removed
+    (k_s = 0 there, which zeroes their scores).  That output comes from the
+    token-by-token recurrence (``forms.forward_recurrent``), so a position
+    costs one O(T log T) pass instead of the O(T^2) pair matrix."""
+    from .forms import forward_recurrent
+    q, k, v, log_a, lam, dout = (_f64(x) for x in (q, k, v, log_a, lam, dout))
+    B, H, T, _ = q.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    res = np.zeros((B, H, len(rows)))
+    for i, r in enumerate(rows):
+        kr = k.copy()
+        kr[:, :, r:] = 0.0
+        o, _ = forward_recurrent(q, kr, v, lam, log_a=log_a)
+        res[:, :, i] = np.einsum("bhtd,bhtd->bh", dout[:, :, r:], o[:, :, r:])
     return res
 
 

@@ -154,3 +154,15 @@ def test_sampled_rows_equal_the_full_gradients():
     smp = backward.backward_sampled(x["q"], x["k"], x["v"], x["log_a"], x["lam"], x["dout"], rows)
     for name, full in (("dq", g["q"]), ("dk", g["k"]), ("dv", g["v"]), ("dlam", g["lam"])):
         assert np.allclose(smp[name], full[:, :, rows], rtol=1e-11, atol=1e-13), name
+
+
+@pytest.mark.parametrize("T", [1, 9, 37, 64])
+def test_gate_gradient_rows_equal_the_full_gradient(T):
+    """dlog_a_rows (pairs straddling r, through the recurrence with the later
+    keys removed) equals backward_quadratic's reverse sum at every position."""
+    x = make_inputs(WORKLOADS["small_bf16"], B=1, H=2, T=T, d=8, dtype="f32", variant="weak_decay", seed=40 + T)
+    dout = make_grad_out(WORKLOADS["small_bf16"], B=1, H=2, T=T, d=8, dtype="f32", seed=40 + T)
+    ref = backward.backward_quadratic(x["q"], x["k"], x["v"], x["log_a"], x["lam"], dout)[3]
+    got = backward.dlog_a_rows(x["q"], x["k"], x["v"], x["log_a"], x["lam"], dout, np.arange(T))
+    scale = np.abs(ref).max() + 1e-30
+    assert np.max(np.abs(got - ref)) <= 1e-12 * max(scale, 1.0)
