@@ -465,8 +465,36 @@ struct ChunkShape {
   // small tiles: the first NPRE levels' nodes load with the chunk; larger
   // ones load them at the start of phase 2, where the registers are free
   static constexpr bool EARLY = BF16 && C <= 64 && D <= 64;
-  static constexpr int NPRE = EARLY ? 4 : 2;                  // node fragment buffers per wave
+  static constexpr int NPRE = EARLY && !output_direct(C, D, BF16 ? 2 : 4) ? 4 : 2;   // node fragment buffers per wave
 };
+
+// Direct-load tiles (bfloat16, D = 64 or 128): unpadded rows of 2 D bytes,
+// the 16-byte granule g of row r stored at granule g ^ (r mod 8) of that row,
+// so the 16 rows an operand fragment reads spread over the banks.  The direct
+// global-to-LDS loads write whole 1 KB runs, so the permutation is applied to
+// the global addresses the lanes load.
+template <int D>
+__device__ __forceinline__ int swz_gran(int r, int g) { return r * (2 * D) + ((g ^ (r & 7)) << 4); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposed bfloat16 fragment of a direct-load tile (ds_read_b64_tr_b16: the
+// 16 lanes of a group each read 8 bytes, four consecutive columns of one of
+// four rows, and lane i receives column i of the four rows): lane (lq, lr)
+// receives rows k0 + 8 lq .. + 7 of column c0 + lr, the k-slice of an operand
+// whose rows are the tile's columns.
+template <int D>
+__device__ __forceinline__ bf16x8 swz_tr_frag(const unsigned char* tile, int k0, int c0, int lane) {
+  const int lq = lane >> 4, j = lane & 15;
+  const int g = (c0 >> 3) + ((j & 3) >> 1), o = (j & 1) * 8;
+  const int r0 = k0 + 8 * lq + (j >> 2);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + swz_gran<D>(r0, g) + o));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + swz_gran<D>(r0 + 4, g) + o));
+  return __builtin_bit_cast(bf16x8, u16x8{(unsigned short)lo[0], (unsigned short)lo[1], (unsigned short)lo[2],
+                                          (unsigned short)lo[3], (unsigned short)hi[0], (unsigned short)hi[1],
+                                          (unsigned short)hi[2], (unsigned short)hi[3]});
+}
 
 // FULL: the chunk has C rows (every chunk but a ragged last one), so the
 // row bounds checks fold away.
@@ -495,9 +523,15 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   float* b2c = reinterpret_cast<float*>(smem + lay.b2);
   float* e2c = reinterpret_cast<float*>(smem + lay.e2);
 
+  constexpr bool DIRECT = output_direct(C, D, sizeof(E));
+  const unsigned char* Qt = smem + lay.q;         // direct-load tiles (swizzled rows)
+  const unsigned char* Kt = smem + lay.k;
+  const unsigned char* Vt = smem + lay.v;
+
   const int64_t nc = a.n_chunks, ng = a.n_groups;
-  const int64_t bh = item / nc;
-  const int64_t c = item % nc;
+  // B * H * n_chunks < 2^31 (checked on the host): 32-bit division
+  const int64_t bh = (uint32_t)item / (uint32_t)nc;
+  const int64_t c = (uint32_t)item % (uint32_t)nc;
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id(), lq = lane >> 4, lr = lane & 15;
   const int64_t T = a.T;
   const int64_t tc = c * C;
@@ -512,6 +546,57 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   // ---- loads of this chunk, all issued before the first LDS store
   uint4 qx[SH::NPF], kx[SH::NPF], vx[SH::NPF];
   float lx[SH::NLX];
+  // lambda rows: 16-byte loads on full chunks when aligned, else one value
+  // per load
+  const bool lam4 = FULL && a.lam_vec4;
+  if constexpr (DIRECT) {
+    constexpr int ROWB = 2 * D, GPR = ROWB / 16, RPR = 1024 / ROWB, RUNS = C * ROWB / 1024;
+    if (FULL) {
+      // direct global-to-LDS loads in 1 KB runs: lane l fills granule l mod GPR
+      // of row RPR ri + l / GPR with the logical granule that XORs to it.  The
+      // row's low three bits are (RPR ri + l / GPR) mod 8, so the lane's source
+      // offset inside a run is the same for every run when RPR >= 8 and
+      // alternates with ri when RPR = 4.
+      static_assert((3 * RUNS) % NW == 0, "runs are dealt evenly over the waves");
+      const int lrow = lane / GPR, lg16 = lane % GPR;
+      const unsigned off0 = (unsigned)(lrow * ROWB + ((lg16 ^ (lrow & 7)) << 4));
+      const unsigned off1 = (unsigned)(lrow * ROWB + ((lg16 ^ ((RPR + lrow) & 7)) << 4));
+#pragma unroll
+      for (int k = 0; k < 3 * RUNS / NW; ++k) {
+        const int run = w + k * NW;                  // wave-uniform
+        const int t = run / RUNS, ri = run % RUNS;
+        const E* src = t == 0 ? qg : (t == 1 ? kg : vg);
+        const unsigned o = (RPR >= 8 || (ri & 1) == 0) ? off0 : off1;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char*>(src) + (unsigned)(ri * 1024) + o,
+                                         (__attribute__((address_space(3))) void*)(smem + (t == 0 ? lay.q : t == 1 ? lay.k : lay.v) + ri * 1024),
+                                         16, 0, 0);
+      }
+      const unsigned char* ls = reinterpret_cast<const unsigned char*>(lg);
+      if (lam4) {
+        for (int ri = w; ri * 1024 < C * L * 4; ri += NW) {
+          const unsigned byte = (unsigned)(ri * 1024 + lane * 16);
+          if (byte < (unsigned)(C * L * 4))
+            __builtin_amdgcn_global_load_lds(ls + byte, (__attribute__((address_space(3))) void*)(smem + lay.lam + ri * 1024), 16, 0, 0);
+        }
+      } else {
+        for (int ri = w; ri * 256 < C * L * 4; ri += NW) {
+          const unsigned byte = (unsigned)(ri * 256 + lane * 4);
+          if (byte < (unsigned)(C * L * 4))
+            __builtin_amdgcn_global_load_lds(ls + byte, (__attribute__((address_space(3))) void*)(smem + lay.lam + ri * 256), 4, 0, 0);
+        }
+      }
+    } else {
+      // the partial last chunk: element copies, zeros past the sequence
+      const E* srcs[3] = {qg, kg, vg};
+      for (int i = tid; i < 3 * C * GPR; i += SH::NT) {
+        const int t = i / (C * GPR), rem = i % (C * GPR), r = rem / GPR, g = rem % GPR;
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (r < nv) x = *reinterpret_cast<const uint4*>(srcs[t] + (unsigned)(r * D + g * 8));
+        *reinterpret_cast<uint4*>(smem + (t == 0 ? lay.q : t == 1 ? lay.k : lay.v) + swz_gran<D>(r, g)) = x;
+      }
+      for (int i = tid; i < C * L; i += SH::NT) lamS[i] = i < nv * L ? lg[i] : 0.f;
+    }
+  } else {
 #pragma unroll
   for (int p = 0; p < SH::NPF; ++p) {
     const int idx = tid + p * SH::NT;
@@ -523,9 +608,6 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
       vx[p] = *reinterpret_cast<const uint4*>(vg + r * D + cv * EPV);
     }
   }
-  // lambda rows: 16-byte loads on full chunks when aligned, else one value
-  // per load
-  const bool lam4 = FULL && a.lam_vec4;
 #pragma unroll
   for (int p = 0; p < SH::NLX; ++p) lx[p] = 0.f;
   if (lam4) {
@@ -544,6 +626,7 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
       const int idx = tid + p * SH::NT;
       if (idx < nv * L) lx[p] = lg[idx];
     }
+  }
   }
   // wave 0: the chunk's log gates, KPG consecutive tokens per lane
   constexpr int KPG = C <= 64 ? 1 : 2;
@@ -616,13 +699,14 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
         dst[s2][n] = EL::template load_k<D>(nodeT + (16 * (cb0 + n) + lr) * D + k0, k0);
     }
   };
-  if (SH::EARLY && cb0 < DB) {
+  if (!DIRECT && SH::EARLY && cb0 < DB) {
 #pragma unroll
     for (int u = 0; u < NPRE; ++u)
       if (u < n_lev) load_node(u, nf[u]);
   }
 
   // ---- LDS stores: Q, K and V row-major, lambda rows, gate prefix
+  if constexpr (!DIRECT) {
 #pragma unroll
   for (int p = 0; p < SH::NPF; ++p) {
     const int idx = tid + p * SH::NT;
@@ -648,6 +732,7 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
       const int idx = tid + p * SH::NT;
       if (idx < C * L) lamS[idx] = lx[p];
     }
+  }
   }
   if (w == 0) {
     // in-chunk prefix of log2(a) and its exp2 (the row gate to the chunk start),
@@ -680,7 +765,13 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
     const float Se = __shfl(S, src, 64);
     if (act) g2 = grp ? (float)(gpg - gpe) + pre : pre - Se;
   }
+  if constexpr (DIRECT) __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
   __syncthreads();
+  if (DIRECT && SH::EARLY && cb0 < DB) {
+#pragma unroll
+    for (int u = 0; u < NPRE; ++u)
+      if (u < n_lev) load_node(u, nf[u]);
+  }
 
   // ---- phase 1: masked score tiles P[query][key] (bf16 or fp32).  Every
   // wave first forms its score tiles S^T = K Q^T; once all waves are past
@@ -699,8 +790,14 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
 #pragma unroll
     for (int s = 0; s < KSD; ++s) {
       const int k0 = s * KST + lq * KPL;
-      const auto kf = EL::template load_k<D>(Ks + (16 * kb + lr) * lay.ld_row + k0, k0);
-      const auto qf = EL::template load_k<D>(Qs + iq * lay.ld_row + k0, k0);
+      Frag kf, qf;
+      if constexpr (DIRECT) {
+        kf = __builtin_bit_cast(Frag, *reinterpret_cast<const u16x8*>(Kt + swz_gran<D>(16 * kb + lr, k0 / 8)));
+        qf = __builtin_bit_cast(Frag, *reinterpret_cast<const u16x8*>(Qt + swz_gran<D>(iq, k0 / 8)));
+      } else {
+        kf = EL::template load_k<D>(Ks + (16 * kb + lr) * lay.ld_row + k0, k0);
+        qf = EL::template load_k<D>(Qs + iq * lay.ld_row + k0, k0);
+      }
       sv[u] = EL::mma(kf, qf, sv[u]);
     }
   }
@@ -718,14 +815,25 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
     const float4 b2k = *reinterpret_cast<const float4*>(b2c + j0);
     const float bk[4] = {b2k.x, b2k.y, b2k.z, b2k.w};
     float pv[4];
+    if (kb < qb) {
+      // below the diagonal every pair differs first in the 16-block bits:
+      // one level for the whole tile, no causal mask
+      const float lam_q = lamS[iq * L + 5 + (31 - __builtin_clz((unsigned)(qb ^ kb)))];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // computed for every key and then masked: the level stays within
-      // 0..log2 C and the gate exponent past the diagonal is discarded
-      const int j = j0 + i;
-      const int lv = fenwick_level_local((unsigned)iq, (unsigned)j);
-      const float val = sv[u][i] * __builtin_amdgcn_exp2f(b2q - bk[i]) * lamS[iq * L + lv];
-      pv[i] = (j <= iq && iq < nv) ? val : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const float val = sv[u][i] * __builtin_amdgcn_exp2f(b2q - bk[i]) * lam_q;
+        pv[i] = (FULL || iq < nv) ? val : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // computed for every key and then masked: the level stays within
+        // 0..log2 C and the gate exponent past the diagonal is discarded
+        const int j = j0 + i;
+        const int lv = fenwick_level_local((unsigned)iq, (unsigned)j);
+        const float val = sv[u][i] * __builtin_amdgcn_exp2f(b2q - bk[i]) * lamS[iq * L + lv];
+        pv[i] = (j <= iq && iq < nv) ? val : 0.f;
+      }
     }
     E* prow = Ps + iq * lay.ld_p + j0;
     if constexpr (BF16) {
@@ -758,7 +866,10 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
 #pragma unroll
     for (int n = 0; n < NCB; ++n) {
       const int dv = 16 * (cb0 + n) + lr;
-      if constexpr (BF16) {
+      if constexpr (DIRECT) {
+        // C >= 32 here: every k-slice lies inside the chunk
+        vf[s][n] = swz_tr_frag<D>(Vt, s * KST, 16 * (cb0 + n), lane);
+      } else if constexpr (BF16) {
         u16x8 f = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
         if (C >= KST || k0 < C) {
           const unsigned short* vcol = reinterpret_cast<const unsigned short*>(Vs) + dv;
@@ -810,7 +921,9 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
 #pragma unroll
       for (int s2 = 0; s2 < KSD; ++s2) {
         const int k0 = s2 * KST + lq * KPL;
-        const auto qf = EL::template load_k<D>(Qs + (16 * rb + lr) * lay.ld_row + k0, k0);
+        Frag qf;
+        if constexpr (DIRECT) qf = __builtin_bit_cast(Frag, *reinterpret_cast<const u16x8*>(Qt + swz_gran<D>(16 * rb + lr, k0 / 8)));
+        else qf = EL::template load_k<D>(Qs + (16 * rb + lr) * lay.ld_row + k0, k0);
 #pragma unroll
         for (int n = 0; n < NCB; ++n) {
           t0[n] = EL::mma(nf0[s2][n], qf, t0[n]);
@@ -884,14 +997,14 @@ __device__ __forceinline__ int64_t xcd_item(int64_t b, int64_t n) {
 // waves per SIMD (128) costs no spills -- bf16 tiles up to 64 x 64, those
 // that load the first nodes early -- the compiler is held to it.
 template <bool BF16, int C, int D>
-constexpr int output_min_waves() { return ChunkShape<BF16, C, D>::EARLY ? 4 : 1; }
+constexpr int output_min_waves() { return ChunkShape<BF16, C, D>::EARLY ? (output_direct(C, D, BF16 ? 2 : 4) ? 5 : 4) : 1; }
 
 template <bool BF16, int C, int D>
 __global__ __launch_bounds__(64 * output_waves(C)) __attribute__((amdgpu_waves_per_eu(output_min_waves<BF16, C, D>(), 8)))
 void fwd_chunk_output(FwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t item = xcd_item(blockIdx.x, gridDim.x);
-  const int64_t c = item % a.n_chunks;
+  const int64_t c = (uint32_t)item % (uint32_t)a.n_chunks;
   if ((c + 1) * C <= a.T) chunk_output_body<BF16, C, D, true>(a, smem, item);
   else chunk_output_body<BF16, C, D, false>(a, smem, item);
 }

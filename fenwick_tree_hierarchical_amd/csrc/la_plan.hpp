@@ -95,15 +95,21 @@ LA_HD constexpr StateLds state_lds(int C, int D, int es, int G) {
   o.total = off;
   return o;
 }
+// bfloat16 tiles with 128- or 256-byte rows and C >= 32 arrive by direct global-to-LDS
+// loads into unpadded rows whose 16-byte granules are XOR-permuted by the row
+// index; the other shapes are staged through registers into padded rows.
+LA_HD constexpr bool output_direct(int C, int D, int es) { return es == 2 && C >= 32 && (D == 64 || D == 128); }
 struct OutLds {
   int q, k, v, p, lam, b2, e2, total, ld_row, ld_v, ld_p;
+  bool direct;
 };
 LA_HD constexpr OutLds output_lds(int C, int D, int es, int L) {
   OutLds o{};
-  o.ld_row = D + 16 / es;
-  // V stays row-major; its rows are 4 bytes longer than a multiple of 16, so
-  // the eight rows one V^T fragment gathers from fall in different banks
-  o.ld_v = D + 4 / es;
+  o.direct = output_direct(C, D, es);
+  o.ld_row = o.direct ? D : D + 16 / es;
+  // staged V stays row-major; its rows are 4 bytes longer than a multiple of
+  // 16, so the eight rows one V^T fragment gathers from fall in different banks
+  o.ld_v = o.direct ? D : D + 4 / es;
   o.ld_p = C + 16 / es;
   int off = 0;
   o.q = off;    off += (C * o.ld_row * es + 255) / 256 * 256;
