@@ -17,11 +17,18 @@ every input already resident in HBM.  Prints ONE JSON line:
                  against 8 TB/s; `traffic` is the counter-measured HBM
                  bytes per launch from profiles/ when those counters were
                  taken on the current kernel source, else null
-  cpu_baseline   the float64 oracle's Fenwick recurrence timed on the host
-                 on a bounded sample of the same workload
+  cpu_baseline   the float64 oracle timed on the host cores (worker
+                 processes, one thread each): its recurrence over every
+                 head of the same workload in full, plus the tiny, small and
+                 decode workloads
   stages         per kernel (chunk_states, group_tree, chunk_output): mean
                  time, algorithmic bytes, GB/s and counter traffic
-  mfma           the matrix-core share of the whole forward
+  layer_frac     the layer's essential bytes (q, k, v, out, log_a, lambda)
+                 per timed step against 8 TB/s
+  mfma           the matrix-core share of the whole forward (per timed step)
+  configs        the other forward workloads (tiny fp32, small bf16, the
+                 128K long-context shape): time, tokens/s, per-kernel HBM
+                 fractions and layer_frac
   backward       the backward (loglinear_bwd) on the same layer with a
                  seeded upstream gradient: mean time, tokens/s and its ratio
                  to the forward
@@ -138,29 +145,124 @@ def algorithmic_counts(w, B, H, T, d, C, L, es, G=8):
                 flops_states=BH * states, flops_contractions=BH * contr, flops=flops)
 
 
-def cpu_baseline(w, heads: int):
-    """Time the oracle's token-by-token recurrence on `heads` (b,h) pairs of
-    the workload, full length, on the host."""
-    import torch
-    from fenwick_tree_hierarchical_amd.workloads import make_inputs
-    from oracle import forms
+def host_cores() -> int:
+    """Host cores this process may use, at most 16 (the host share of one GPU)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
+
+def cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:       # pragma: no cover
-        threadpool_limits = None
-    x = make_inputs(w, B=1, H=heads, device="cpu")
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_task(item):
+    """One oracle call in a worker process; returns (seconds, checksum)."""
+    import numpy as np
+    from oracle import forms
+    kind, args = item
     t0 = time.perf_counter()
-    if threadpool_limits:
-        with threadpool_limits(1):
-            forms.forward_recurrent(x["q"], x["k"], x["v"], x["lam"], log_a=x["log_a"])
-    else:
-        forms.forward_recurrent(x["q"], x["k"], x["v"], x["lam"], log_a=x["log_a"])
-    dt = time.perf_counter() - t0
-    tokens = heads * w.T / w.H          # positions across all H heads
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"float64 Fenwick recurrence over {heads} of the {w.B * w.H} heads, full T={w.T} "
-                      f"({heads}/{w.H} of one sequence = {tokens:.0f} tokens) in {dt:.1f} s, one thread"}
+    if kind == "recurrent":
+        q, k, v, la, lam = args
+        out, _ = forms.forward_recurrent(q, k, v, lam, log_a=la)
+    elif kind == "quadratic":
+        q, k, v, la, lam = args
+        out = forms.forward_quadratic(q, k, v, la, lam)
+    else:                                   # "decode": steps from a state at position t0
+        q, k, v, a, lam, t_start, nlev, seed = args
+        BH, steps, d = q.shape
+        st = forms.FenwickState(BH, d, v.shape[-1], nlev, t=t_start)
+        rng = np.random.default_rng(seed)
+        for lv in range(1, nlev + 1):       # the occupied levels of position t_start, values of scale 0.01
+            if (t_start >> (lv - 1)) & 1:
+                st.slots[:, lv] = 0.01 * rng.standard_normal(st.slots[:, lv].shape)
+        out = np.stack([forms.recurrent_step(st, q[:, i], k[:, i], v[:, i], a[:, i], lam[:, i])
+                        for i in range(steps)], axis=1)
+    return time.perf_counter() - t0, float(np.sum(out))
+
+
+def _pool_map(tasks, n):
+    """Run oracle tasks over n spawned worker processes with one BLAS thread
+    each; returns (wall seconds, per-task results)."""
+    import multiprocessing as mp
+    names = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+    saved = {v: os.environ.get(v) for v in names}
+    os.environ.update({v: "1" for v in names})
+    try:
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(min(n, len(tasks))) as pool:
+            import numpy as np
+            warm = tuple(np.zeros(sh, dtype=np.float32) for sh in ((1, 1, 4, 4), (1, 1, 4, 4), (1, 1, 4, 4),
+                                                                   (1, 1, 4), (1, 1, 4, 3)))
+            pool.map(_oracle_task, [("recurrent", warm)] * min(n, len(tasks)))     # workers started and warm
+            t0 = time.perf_counter()
+            res = pool.map(_oracle_task, tasks, chunksize=1)
+            wall = time.perf_counter() - t0
+    finally:
+        for v, val in saved.items():
+            if val is None:
+                os.environ.pop(v, None)
+            else:
+                os.environ[v] = val
+    return wall, res
+
+
+def _head_tasks(x, kind):
+    import numpy as np
+    B, H = x["q"].shape[:2]
+    f = lambda t: t.float().numpy()
+    return [(kind, tuple(f(x[n][b:b + 1, h:h + 1]) for n in ("q", "k", "v", "log_a", "lam")))
+            for b in range(B) for h in range(H)]
+
+
+def cpu_baseline():
+    """The float64 oracle on the host cores, as it stands: its token-by-token
+    recurrence over every head of the training shape (the metric's workload,
+    in full), the tiny and small workloads (recurrence and quadratic form) and
+    the decode workload's 256 steps over all 1024 heads (from a state with
+    the occupancy of position 32768).  Heads are spread over n worker
+    processes, one thread each; wall time from the first task to the last."""
+    import torch
+    from fenwick_tree_hierarchical_amd.workloads import WORKLOADS, make_inputs
+    n = host_cores()
+    res = {"cores": n, "cpu_model": cpu_model(), "threads_per_worker": 1}
+    for name in ("tiny_f32", "small_bf16", "train_16k_bf16"):
+        w = WORKLOADS[name]
+        x = make_inputs(w, device="cpu")
+        entry = {}
+        kinds = ("recurrent", "quadratic") if name != "train_16k_bf16" else ("recurrent",)
+        for kind in kinds:
+            wall, r = _pool_map(_head_tasks(x, kind), n)
+            entry[kind] = {"seconds": wall, "tokens_per_s": w.B * w.T / wall, "heads": w.B * w.H,
+                           "task_seconds": sum(t for t, _ in r)}
+        res[name] = entry
+        del x
+    # decode: 256 steps of all 64 x 16 heads, split into n groups of heads
+    w = WORKLOADS["decode_32k_bf16"]
+    x = make_inputs(w, device="cpu", T=w.steps, L=17)
+    BH = w.B * w.H
+    q, k, v = (x[nm].float().reshape(BH, w.steps, -1).numpy() for nm in ("q", "k", "v"))
+    a = torch.exp(x["log_a"]).reshape(BH, w.steps).double().numpy()
+    lam = x["lam"].reshape(BH, w.steps, -1).double().numpy()
+    parts = [range(i * BH // n, (i + 1) * BH // n) for i in range(n)]
+    tasks = [("decode", (q[p.start:p.stop], k[p.start:p.stop], v[p.start:p.stop], a[p.start:p.stop],
+                         lam[p.start:p.stop], w.prefix, 16, i)) for i, p in enumerate(parts)]
+    wall, r = _pool_map(tasks, n)
+    res["decode_32k_bf16"] = {"recurrent_steps": {"seconds": wall, "tokens_per_s": w.B * w.steps / wall,
+                                                  "heads": BH, "steps": w.steps,
+                                                  "task_seconds": sum(t for t, _ in r)}}
+    main = res["train_16k_bf16"]["recurrent"]
+    return {"value": main["tokens_per_s"], "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"float64 Fenwick recurrence over all {main['heads']} heads of train_16k_bf16 "
+                      f"(B=8, H=16, T=16384, d=64), in full: {main['seconds']:.1f} s wall on {n} worker "
+                      f"processes of one thread ({main['task_seconds']:.0f} CPU-s)",
+            "cpu_model": res["cpu_model"], "configs": {k: v for k, v in res.items() if k not in
+                                                       ("cores", "cpu_model", "threads_per_worker")}}
 
 
 def pmc_traffic(src_hash: str):
@@ -310,7 +412,7 @@ def bench_decode_large(la, torch, dev, B=256, steps=64):
             "frac": tot / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
 
-def bench_backward(la, torch, dev, w, x, fwd_ms, reps=10):
+def bench_backward(la, torch, dev, w, x, reps=10):
     """The backward (loglinear_bwd, all of its kernels) on the training shape
     with a seeded upstream gradient, timed with HIP events on the launch
     stream.  Essential bytes: q, k, v, dout, log_a, lambda read and dq, dk,
@@ -334,7 +436,7 @@ def bench_backward(la, torch, dev, w, x, fwd_ms, reps=10):
     per_tok = 7 * w.dk * es + 2 * 4 + 2 * 4 * w.L
     nbytes = w.B * w.H * w.T * per_tok
     return {"workload": w.name, "chunk": w.C, "reps": reps, "ms": mean, "median_ms": sorted(ms)[reps // 2],
-            "min_ms": min(ms), "tokens_per_s": w.B * w.T / (mean * 1e-3), "ratio_to_forward": mean / fwd_ms,
+            "min_ms": min(ms), "tokens_per_s": w.B * w.T / (mean * 1e-3), "ratio_to_forward": None,
             "essential_bytes": nbytes, "essential_gbps": nbytes / (mean * 1e-3) / 1e9,
             "essential_bytes_note": f"{per_tok} B per head-token: q, k, v, dout read and dq, dk, dv written "
                                     f"(bf16), log_a, lambda read and dlog_a, dlambda written (fp32)"}
@@ -401,6 +503,58 @@ def bench_gdn(la, torch, dev, w, reps=10, warmup=5):
             "essential_gbps": cnt["essential_bytes"] / (mean * 1e-3) / 1e9,
             "essential_bytes_note": f"{cnt['per_head_token_bytes']} B per head-token: q, k, v, out (bf16), "
                                     f"log_a, beta, lambda (fp32)"}
+
+
+def bench_config(la, torch, dev, w, steps=20, warmup=10):
+    """One forward workload (not the metric's): wall time per forward over
+    `steps` calls after `warmup`, then the kernels' durations from HIP events
+    between the stages over as many calls; algorithmic bytes per kernel and
+    the layer's essential bytes against the HBM peak."""
+    from fenwick_tree_hierarchical_amd.workloads import make_inputs, torch_dtype
+    x = make_inputs(w, device=dev)
+    dt = torch_dtype(w.dtype)
+    es = 2 if w.dtype == "bf16" else 4
+    out = torch.empty_like(x["v"])
+    nws = la.loglinear_fwd_workspace(w.B, w.H, w.T, w.dk, w.dv, w.C, dt)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    n_st = la.loglinear_fwd_num_stages(w.B, w.H, w.T, w.dk, w.dv, w.C, dt)
+    names = {3: ["chunk_states", "group_tree", "chunk_output"], 2: ["chunk_states", "chunk_output"],
+             1: ["chunk_output"]}[n_st]
+
+    def call(ev=None):
+        if ev is None:
+            la.loglinear_fwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], out=out, chunk=w.C, workspace=ws)
+        else:
+            la.loglinear_fwd_staged(x["q"], x["k"], x["v"], x["log_a"], x["lam"], ev, out=out, chunk=w.C,
+                                    workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)] for _ in range(steps)]
+    for i in range(steps):
+        call(evs[i])
+    torch.cuda.synchronize()
+    st_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j in range(n_st)]
+    G = 8 if w.dk <= 64 else 4
+    cnt = algorithmic_counts(w, w.B, w.H, w.T, w.dk, w.C, w.L, es, G=G)
+    stages = {}
+    for n, m in zip(names, st_ms):
+        b = cnt["kernel_bytes"][n]
+        stages[n] = {"ms": m, "alg_bytes": b, "alg_gbps": b / (m * 1e-3) / 1e9,
+                     "frac_hbm": b / (m * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    return {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.dk, "chunk": w.C, "dtype": w.dtype,
+            "steps": steps, "warmup": warmup, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
+            "essential_bytes": cnt["bytes_io"],
+            "layer_frac": cnt["bytes_io"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "alg_tflops": cnt["flops"] / (ms * 1e-3) / 1e12,
+            "frac_of_bf16_peak": cnt["flops"] / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS if es == 2 else None,
+            "stages": stages}
 
 
 def ctypes_byref(la, st):
@@ -478,9 +632,9 @@ def pmc_profile(fetch_dir: str, write_dir: str, out_path: str):
            "per_launch_kib": per_kib, "per_kernel_traffic_bytes": traffic,
            "commands": [
                f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/{fetch_dir} "
-               "-o fetch -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-decode --no-backward --no-gdn --copy-calibration",
+               "-o fetch -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-decode --no-backward --no-gdn --no-configs --copy-calibration",
                f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/{write_dir} "
-               "-o write -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-decode --no-backward --no-gdn --copy-calibration",
+               "-o write -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-decode --no-backward --no-gdn --no-configs --copy-calibration",
                f"python bench.py --pmc-profile {fetch_dir} {write_dir}"]}
     with open(out_path, "w") as f:
         json.dump(res, f, indent=1)
@@ -538,7 +692,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-gdn", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=48)
+    ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pmc-summary", default=None)
     ap.add_argument("--pmc-profile", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None)
@@ -590,6 +744,27 @@ def main():
                                     workspace=ws)
         if copy_dst is not None:
             copy_dst.copy_(copy_src)
+
+    # the other GPU legs first, so that the timed forward steps below run on a
+    # GPU that has been busy (clocks up)
+    secondary = {}
+    if not args.no_configs:
+        secondary["configs"] = {}
+        for name in ("tiny_f32", "small_bf16", "long_128k_bf16"):
+            log(f"bench: forward at {name}")
+            secondary["configs"][name] = bench_config(la, torch, dev, WORKLOADS[name])
+    if not args.no_backward:
+        log("bench: backward")
+        secondary["backward"] = bench_backward(la, torch, dev, w, x)
+    if not args.no_gdn:
+        log("bench: gated deltanet forward")
+        secondary["gdn"] = bench_gdn(la, torch, dev, w)
+    if not args.no_decode:
+        log("bench: decode 256 steps")
+        secondary["decode"] = bench_decode(la, torch, dev)
+        log("bench: decode at batch 256")
+        secondary["decode"]["batch_256"] = bench_decode_large(la, torch, dev)
+    torch.cuda.empty_cache()
 
     log(f"bench: warm-up {args.warmup}")
     for _ in range(args.warmup):
@@ -648,27 +823,24 @@ def main():
                        "frac_hbm": cnt["kernel_bytes"][n] / (m * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                        "traffic_bytes": (traffic or {}).get(n)}
                    for i, (n, m) in enumerate(st_ms.items())},
+        "layer_frac": cnt["bytes_io"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "layer_frac_note": f"essential bytes ({cnt['per_head_token_bytes']} B per head-token: q, k, v, out, "
+                           f"log_a, lambda) / ms_per_step / 8 TB/s",
         "mfma": {"alg_tflop": cnt["flops"] / 1e12,
-                 "achieved_tflops_whole_fwd": cnt["flops"] / (fwd_ms * 1e-3) / 1e12,
-                 "frac_of_bf16_peak_whole_fwd": cnt["flops"] / (fwd_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-                 "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+                 "achieved_tflops_whole_fwd": cnt["flops"] / (ms_per_step * 1e-3) / 1e12,
+                 "frac_of_bf16_peak_whole_fwd": cnt["flops"] / (ms_per_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                 "peak_tflops": BF16_MFMA_PEAK_TFLOPS, "time_base": "ms_per_step",
                  "split_tflop": {"intra": cnt["flops_intra"] / 1e12, "states": cnt["flops_states"] / 1e12,
                                  "contractions": cnt["flops_contractions"] / 1e12}},
     }
-    if not args.no_backward:
-        log("bench: backward")
-        result["backward"] = bench_backward(la, torch, dev, w, x, fwd_ms)
-    if not args.no_gdn:
-        log("bench: gated deltanet forward")
-        result["gdn"] = bench_gdn(la, torch, dev, w)
-    if not args.no_decode:
-        log("bench: decode 256 steps")
-        result["decode"] = bench_decode(la, torch, dev)
-        log("bench: decode at batch 256")
-        result["decode"]["batch_256"] = bench_decode_large(la, torch, dev)
+    result.update(secondary)
+    if "backward" in result:
+        result["backward"]["ratio_to_forward"] = result["backward"]["ms"] / ms_per_step
+    result["order"] = ("the other legs (configs, backward, gdn, decode) ran before the warm-up and the "
+                       "timed steps; the CPU baseline after them")
     if not args.no_cpu:
-        log(f"bench: oracle CPU baseline on {args.cpu_heads} heads")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+        log(f"bench: oracle CPU baseline on {host_cores()} host cores")
+        result["cpu_baseline"] = cpu_baseline()
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result))
