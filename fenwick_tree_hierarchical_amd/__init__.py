@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "LogAttnError", "lib", "loglinear_fwd", "loglinear_fwd_workspace", "loglinear_fwd_num_stages",
-    "loglinear_fwd_staged", "loglinear_bwd", "loglinear_bwd_workspace", "LogLinearState", "loglinear_state_init", "loglinear_decode_step",
+    "loglinear_fwd_staged", "loglinear_fwd_noalloc", "loglinear_bwd", "loglinear_bwd_workspace", "LogLinearState", "loglinear_state_init", "loglinear_decode_step",
     "loglinear_level_table", "loglinear_strerror", "loglinear_gdn_fwd", "loglinear_gdn_fwd_workspace",
     "LA_F32", "LA_BF16",
 ]
@@ -41,6 +41,7 @@ _SIGS = {
     "loglinear_fwd": ([_p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
     "loglinear_fwd_staged": ([_p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _i, _i, _i, _p, _sz,
                               ctypes.POINTER(_p), _i, _p], _i),
+    "loglinear_fwd_noalloc": ([_p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _i, _i, _i, _p], _i),
     "loglinear_fwd_state": ([_p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _i, _i, _i, _p, _sz,
                              ctypes.POINTER(_LaState), _p], _i),
     "loglinear_bwd_workspace": ([_i, _i, _i64, _i, _i, _i, _i, ctypes.POINTER(_sz)], _i),
@@ -170,6 +171,27 @@ def loglinear_fwd_staged(q, k, v, log_a, lam, events, out=None, chunk: int = 64,
             e.record(s)
     arr = (_p * len(events))(*[e.cuda_event for e in events])
     _check(lib().loglinear_fwd_staged(*args, arr, len(events), s.cuda_stream), "loglinear_fwd_staged")
+    return out
+
+
+def loglinear_fwd_noalloc(q, k, v, log_a, lam, out, chunk: int = 64):
+    """loglinear_fwd into the caller's ``out`` with the library's fixed
+    per-GPU scratch instead of a workspace (nothing is allocated).  Calls that
+    overlap in time on one GPU share that scratch and must not overlap."""
+    dev = _dev(q, k, v, log_a, lam, out)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or log_a.shape != (B, H, T) or lam.shape[:3] != (B, H, T):
+        raise ValueError("shape mismatch between q, k, v, log_a and lambda")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if log_a.dtype != torch.float32 or lam.dtype != torch.float32:
+        raise TypeError("log_a and lambda must be float32")
+    if out.shape != (B, H, T, dv) or out.dtype != q.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    _check(lib().loglinear_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(out), B, H, T, dk,
+                                       dv, chunk, lam.shape[-1], _dtype_code(q.dtype), _stream(dev)),
+           "loglinear_fwd_noalloc")
     return out
 
 

@@ -2,6 +2,8 @@
 // Every check happens before anything is enqueued; on error nothing runs.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "../../include/logattn.h"
 #include "la_bwd_impl.hpp"
 #include "la_fwd_impl.hpp"
@@ -72,6 +74,31 @@ int fwd_common(const void* q, const void* k, const void* v, const float* log_a, 
   return rc;
 }
 
+// The fixed scratch of loglinear_fwd_noalloc: a device array of the module,
+// present on every GPU the library runs on.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol); it passes the device address hipGetSymbolAddress returns, looked
+// up once per device, with that device current, on the first call there.
+__device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the scratch array on the current device.
+int scratch_on_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return kEHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return kEHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return kOK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -86,6 +113,7 @@ LA_API const char* loglinear_strerror(int code) {
     case LA_EWORKSPACE: return "workspace missing or too small";
     case LA_ECAPACITY: return "decode state has too few slots for this position";
     case LA_EHIP: return "HIP runtime or kernel launch error";
+    case LA_ESCRATCH: return "problem needs more than the fixed scratch of loglinear_fwd_noalloc";
     default: return "unknown status code";
   }
 }
@@ -118,6 +146,22 @@ LA_API int loglinear_fwd(const void* q, const void* k, const void* v, const floa
                          la_stream_t stream) {
   return fwd_common(q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, L, dtype, workspace,
                     workspace_bytes, nullptr, 0, nullptr, stream);
+}
+
+LA_API int loglinear_fwd_noalloc(const void* q, const void* k, const void* v, const float* log_a,
+                                 const float* lambda, void* out, int B, int H, int64_t T, int dk,
+                                 int dv, int C, int L, int dtype, la_stream_t stream) {
+  FwdPlan p;
+  int rc = plan_fwd(B, H, T, dk, dv, C, dtype, L, &p);
+  if (rc != kOK) return rc;
+  if (p.ws_bytes > LA_NOALLOC_SCRATCH_BYTES) return kESCRATCH;
+  void* ws = nullptr;
+  if (p.ws_bytes > 0) {
+    rc = scratch_on_current_device(&ws);
+    if (rc != kOK) return rc;
+  }
+  return fwd_common(q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, L, dtype, ws, LA_NOALLOC_SCRATCH_BYTES,
+                    nullptr, 0, nullptr, stream);
 }
 
 LA_API int loglinear_fwd_state(const void* q, const void* k, const void* v, const float* log_a,

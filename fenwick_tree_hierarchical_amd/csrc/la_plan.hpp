@@ -18,7 +18,7 @@ namespace la {
 enum : int { kF32 = 0, kBF16 = 1 };
 enum : int {
   kOK = 0, kEINVAL = -1, kESHAPE = -2, kEDTYPE = -3, kEALIGN = -4,
-  kEWORKSPACE = -5, kECAPACITY = -6, kEHIP = -7
+  kEWORKSPACE = -5, kECAPACITY = -6, kEHIP = -7, kESCRATCH = -8
 };
 
 constexpr int kMaxLevels = 32;        // lambda levels accepted (T < 2^31 needs <= 32)

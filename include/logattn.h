@@ -26,7 +26,9 @@
  *    and no output is written.
  *  - Pointers are device pointers unless stated otherwise.  The caller
  *    allocates and owns every buffer; the library allocates no device memory
- *    and keeps no global mutable state.
+ *    and keeps no global mutable state, except the fixed scratch array of
+ *    loglinear_fwd_noalloc (one per GPU, held until the process ends) and
+ *    its per-device address.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
  *    stream).  Faults inside kernels surface at the caller's next
  *    synchronisation.  NaN/Inf inputs are not checked; they propagate.
@@ -53,7 +55,9 @@ typedef enum la_status {
   LA_EALIGN = -4,      /* a pointer is not aligned as documented */
   LA_EWORKSPACE = -5,  /* workspace pointer null or smaller than the queried size */
   LA_ECAPACITY = -6,   /* decode state has too few slots for the next merge */
-  LA_EHIP = -7         /* a HIP runtime call or kernel launch failed */
+  LA_EHIP = -7,        /* a HIP runtime call or kernel launch failed */
+  LA_ESCRATCH = -8     /* the problem needs more than the fixed scratch of
+                          loglinear_fwd_noalloc */
 } la_status;
 
 typedef enum la_dtype {
@@ -111,6 +115,25 @@ LA_API int loglinear_fwd(const void* q, const void* k, const void* v, const floa
                          const float* lambda, void* out, int B, int H, int64_t T, int dk, int dv,
                          int C, int L, int dtype, void* workspace, size_t workspace_bytes,
                          la_stream_t stream);
+
+/*
+ * loglinear_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, layouts, results and
+ * errors as loglinear_fwd, except that the workspace is a fixed
+ * LA_NOALLOC_SCRATCH_BYTES array in device memory that the library holds on
+ * every GPU it runs on, from the first call on that GPU until the process
+ * ends; nothing is allocated or freed by this call.  Shapes whose
+ * loglinear_fwd_workspace() exceeds that size return LA_ESCRATCH (in bfloat16
+ * at d = C = 64 it holds up to 186 (b,h) heads of 2048 tokens, 23 of 16384
+ * or 2 of 131072; at d = C = 128, 73, 9 and 1).  All calls on one GPU share
+ * the array: calls that overlap in time on the same GPU (two streams, or
+ * several host threads) race and must be serialised by the caller.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+LA_API int loglinear_fwd_noalloc(const void* q, const void* k, const void* v, const float* log_a,
+                                 const float* lambda, void* out, int B, int H, int64_t T, int dk,
+                                 int dv, int C, int L, int dtype, la_stream_t stream);
 
 /* Number of kernel stages loglinear_fwd enqueues for this shape (host only). */
 LA_API int loglinear_fwd_num_stages(int B, int H, int64_t T, int dk, int dv, int C, int dtype,
