@@ -10,6 +10,7 @@
 #include "la_gdn_impl.hpp"
 #include "la_internal.hpp"
 #include "la_plan.hpp"
+#include "la_validate.hpp"
 
 using namespace la;
 
@@ -24,14 +25,8 @@ int fwd_common(const void* q, const void* k, const void* v, const float* log_a, 
   if (rc != kOK) return rc;
   if (events && n_events != p.n_stages + 1) return kEINVAL;
   if (st) {
-    rc = check_state_shape(st->B, st->H, st->dk, st->dv, st->S);
+    rc = check_fwd_state(p, st);
     if (rc != kOK) return rc;
-    if (st->B != B || st->H != H || st->dk != dk || st->dv != dv) return kESHAPE;
-    if (bit_length(T) > st->S) return kECAPACITY;
-    if (p.BH > 0) {
-      if (!st->slots || !st->scale) return kEINVAL;
-      if (!aligned(st->slots, 16) || !aligned(st->scale, 4)) return kEALIGN;
-    }
   }
   if (p.n_stages == 0) {   // empty problem: nothing to read or write
     if (events)
@@ -46,13 +41,8 @@ int fwd_common(const void* q, const void* k, const void* v, const float* log_a, 
     }
     return kOK;
   }
-  if (!q || !k || !v || !log_a || !lambda || !out) return kEINVAL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return kEALIGN;
-  if (!aligned(log_a, 4) || !aligned(lambda, 4)) return kEALIGN;
-  if (p.ws_bytes > 0) {
-    if (!ws || ws_bytes < p.ws_bytes) return kEWORKSPACE;
-    if (!aligned(ws, 256)) return kEALIGN;
-  }
+  rc = check_fwd_buffers(p, q, k, v, log_a, lambda, out, ws, ws_bytes);
+  if (rc != kOK) return rc;
   char* w = static_cast<char*>(ws);
   FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.log_a = log_a; a.lam = lambda; a.out = out;
@@ -205,15 +195,9 @@ LA_API int loglinear_bwd(const void* q, const void* k, const void* v, const floa
   if (rc != kOK) return rc;
   const FwdPlan& p = P.f;
   if (p.BH == 0 || T == 0) return kOK;   // empty problem: nothing to read or write
-  if (!q || !k || !v || !log_a || !lambda || !dout) return kEINVAL;
-  if (!grad_q || !grad_k || !grad_v || !grad_log_a || !grad_lambda) return kEINVAL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(grad_q, 16) ||
-      !aligned(grad_k, 16) || !aligned(grad_v, 16))
-    return kEALIGN;
-  if (!aligned(log_a, 4) || !aligned(lambda, 4) || !aligned(grad_log_a, 4) || !aligned(grad_lambda, 4))
-    return kEALIGN;
-  if (!workspace || workspace_bytes < P.ws_bytes) return kEWORKSPACE;
-  if (!aligned(workspace, 256)) return kEALIGN;
+  rc = check_bwd_buffers(P, q, k, v, log_a, lambda, dout, grad_q, grad_k, grad_v, grad_log_a, grad_lambda,
+                         workspace, workspace_bytes);
+  if (rc != kOK) return rc;
   char* w = static_cast<char*>(workspace);
   // forward structure over (k := v, v := k): its nodes are sum gate k v^T
   FwdArgs fa{};
@@ -258,11 +242,8 @@ LA_API int loglinear_gdn_fwd(const void* q, const void* k, const void* v, const 
   int rc = plan_gdn(B, H, T, dk, dv, C, dtype, L, &p);
   if (rc != kOK) return rc;
   if (p.BH == 0 || T == 0) return kOK;   // empty problem: nothing to read or write
-  if (!q || !k || !v || !log_a || !beta || !lambda || !out) return kEINVAL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return kEALIGN;
-  if (!aligned(log_a, 4) || !aligned(beta, 4) || !aligned(lambda, 4)) return kEALIGN;
-  if (!workspace || workspace_bytes < p.ws_bytes) return kEWORKSPACE;
-  if (!aligned(workspace, 256)) return kEALIGN;
+  rc = check_gdn_buffers(p, q, k, v, log_a, beta, lambda, out, workspace, workspace_bytes);
+  if (rc != kOK) return rc;
   char* w = static_cast<char*>(workspace);
   GdnArgs a{};
   a.q = q; a.k = k; a.v = v; a.log_a = log_a; a.beta = beta; a.lam = lambda; a.out = out;
@@ -305,20 +286,11 @@ LA_API int loglinear_state_init(la_state* st, int B, int H, int dk, int dv, int 
 LA_API int loglinear_decode_step(la_state* st, const void* q, const void* k, const void* v,
                                  const float* a, const float* lambda, void* out, int dtype,
                                  la_stream_t stream) {
-  if (!st) return kEINVAL;
-  if (dtype != kF32 && dtype != kBF16) return kEDTYPE;
-  int rc = check_state_shape(st->B, st->H, st->dk, st->dv, st->S);
+  int kstar = 0;
+  int rc = check_decode(st, q, k, v, a, lambda, out, dtype, &kstar);
   if (rc != kOK) return rc;
-  if (st->t < 0) return kEINVAL;
-  const int kstar = trailing_ones(st->t);
-  if (kstar + 1 > st->S || bit_length(st->t) > st->S) return kECAPACITY;
   const int64_t BH = (int64_t)st->B * st->H;
   if (BH > 0) {
-    if (!st->slots || !st->scale || !q || !k || !v || !a || !lambda || !out) return kEINVAL;
-    if (!aligned(st->slots, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
-        !aligned(out, 16))
-      return kEALIGN;
-    if (!aligned(st->scale, 4) || !aligned(a, 4) || !aligned(lambda, 4)) return kEALIGN;
     rc = launch_decode(st, q, k, v, a, lambda, out, dtype, kstar, (hipStream_t)stream);
     if (rc != kOK) return rc;
   }

@@ -9,6 +9,7 @@
 // streams only the occupied slots once and writes one merged slot.
 #include "la_device.hpp"
 #include "la_internal.hpp"
+#include "la_levels.hpp"
 #include "la_plan.hpp"
 
 namespace la {
@@ -130,7 +131,11 @@ __global__ void level_table_kernel(int64_t T, int log2C, int8_t* out) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
     const int64_t t = i / T, s = i % T;
-    out[i] = (int8_t)fenwick_level(t, s, log2C);
+    // inside a chunk from the chunk-relative offsets, across chunks through
+    // the output kernel's bucket enumeration (groups of eight chunks)
+    const int64_t ct = t >> log2C, cs = s >> log2C;
+    out[i] = (int8_t)(s > t ? -1 : ct == cs ? fenwick_level(t, s, log2C)
+                                            : enumerated_chunk_level(ct, cs, log2C, ilog2(state_group(64))));
   }
 }
 

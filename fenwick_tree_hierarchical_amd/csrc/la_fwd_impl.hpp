@@ -34,6 +34,7 @@
 #pragma once
 
 #include "la_device.hpp"
+#include "la_levels.hpp"
 #include "la_plan.hpp"
 
 namespace la {
@@ -647,22 +648,22 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   int lev = 0, src = 0;
   int64_t eg = 0;
   if (lane >= 1 && lane <= LOG2G) {
-    const int j = lane;
-    if ((ci >> (j - 1)) & 1) {
-      const int el = ((ci >> j) << j) + (1 << (j - 1)) - 1;   // in-group chunk of the node
+    const BucketRef bk = chunk_level_bucket(c, lane, LOG2C, LOG2G);
+    if (bk.occupied) {
+      const int el = (int)(bk.last - cg0);         // in-group chunk of the node
       act = true;
-      off = (bh * nc + cg0 + el) * D * D;
+      off = (bh * nc + bk.last) * D * D;
       src = el + 1;
-      lev = LOG2C + j;
+      lev = bk.level;
     }
   }
   if (lane >= 32 && lane < 63) {
-    const int i = lane - 31;
-    if (gam > 0 && ((gam >> (i - 1)) & 1)) {
-      eg = ((gam >> i) << i) + (1ll << (i - 1)) - 1;
+    const BucketRef bk = group_level_bucket(c, lane - 31, LOG2C, LOG2G);
+    if (bk.occupied) {
+      eg = bk.last;
       act = true;
       off = (bh * ng + eg) * D * D;
-      lev = LOG2C + LOG2G + i;
+      lev = bk.level;
     }
   }
   const unsigned long long lmask = __ballot(act);

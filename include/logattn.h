@@ -314,10 +314,16 @@ LA_API int loglinear_gdn_fwd(const void* q, const void* k, const void* v, const 
 
 /*
  * Fenwick level table for checking: out[t * T + s] = l(t, s) for s <= t and
- * -1 for s > t, as int8, computed on the device by the same level function
- * the forward kernels use, with the chunk factorisation for chunk size C:
- * inside a chunk the level comes from the bit pattern of the in-chunk
- * offsets, across chunks it is log2(C) + 1 + msb(chunk_t XOR chunk_s).
+ * -1 for s > t, as int8, computed on the device with chunks of C tokens the
+ * way the forward kernels find levels.  Inside a chunk it is the level
+ * function of the in-chunk masks (1 + msb of the offsets' XOR).  Across
+ * chunks it is not a closed form: the table walks the bucket list of the
+ * forward's output kernel (chunk buckets from the set bits of the chunk's
+ * index in its group of 8, group buckets from the set bits of the group
+ * index) and writes the level of the bucket that holds chunk_s, so a
+ * mismatch there shows up in the table.  That enumeration equals
+ * log2(C) + 1 + msb(chunk_t XOR chunk_s) for every group size, which a host
+ * program checks exhaustively.
  *   out  [T, T] int8 device memory; 1 <= T <= 16384; C a power of two
  *        in [1, 2^20].
  */
