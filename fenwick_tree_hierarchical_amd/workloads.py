@@ -149,3 +149,114 @@ def make_beta(w: Workload, device="cpu", B=None, H=None, T=None, seed: int | Non
     g.manual_seed((w.seed if seed is None else seed) + 2000)
     x = torch.randn(B, H, T, device=device, dtype=torch.float32, generator=g)
     return torch.sigmoid(x).contiguous()
+
+
+# --------------------------------------------------------------------------
+# Log-Linear Mamba-2 layer: the operator inside a Mamba-2 block
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class LayerWorkload:
+    """Sizes of one Log-Linear Mamba-2 layer.
+
+    d_model input width; H heads of head dim P (d_inner = H P); N state size
+    (the operator's d_k, with d_v = P); G groups of heads sharing the B and C
+    projections; K taps of the causal conv; C the operator's chunk size; L
+    levels of lambda; eps of the gated RMS norm.
+    """
+    name: str
+    B: int
+    T: int
+    d_model: int
+    H: int
+    P: int
+    N: int
+    G: int
+    K: int
+    C: int
+    L: int
+    dtype: str
+    seed: int
+    eps: float = 1e-5
+
+    @property
+    def d_inner(self) -> int:
+        return self.H * self.P
+
+    @property
+    def conv_dim(self) -> int:
+        return self.H * self.P + 2 * self.G * self.N
+
+    @property
+    def d_in_proj(self) -> int:
+        return 2 * self.H * self.P + 2 * self.G * self.N + self.H + self.H * self.L
+
+
+LAYER_WORKLOADS = {
+    "layer_tiny_f32": LayerWorkload("layer_tiny_f32", 1, 100, 64, 4, 16, 16, 2, 4, 16, 8, "f32", 10),
+    "layer_small_bf16": LayerWorkload("layer_small_bf16", 2, 2048, 256, 4, 64, 64, 1, 4, 64, 12, "bf16", 11),
+    "layer_train_16k_bf16": LayerWorkload("layer_train_16k_bf16", 8, 16384, 512, 16, 64, 64, 1, 4, 64, 15,
+                                          "bf16", 12),
+}
+
+
+def layer_resized(lw: LayerWorkload, **kw) -> LayerWorkload:
+    """``lw`` with some sizes replaced; L follows T unless given."""
+    if "T" in kw and "L" not in kw:
+        kw["L"] = levels_for(kw["T"])
+    return dataclasses.replace(lw, **kw)
+
+
+def make_layer(lw: LayerWorkload, device="cpu", variant: str | None = None, seed: int | None = None):
+    """Seeded input and weights of one layer (Mamba-2's published
+    initialisation, restated):
+
+      u         [B, T, d_model]      ~ N(0, 1)
+      in_proj   [d_in_proj, d_model] ~ U(-1/sqrt(d_model), 1/sqrt(d_model))
+      conv_w    [conv_dim, K]        ~ U(-1/sqrt(K), 1/sqrt(K)), conv_b likewise
+      dt_bias   [H]   softplus^-1(dt0), dt0 = exp(U(log 1e-3, log 1e-1))
+      A_log     [H]   log U(1, 16)
+      D         [H]   1
+      lam_bias  [H, L] 0
+      norm_w    [d_inner] 1
+      out_proj  [d_model, d_inner]   ~ U(-1/sqrt(d_inner), 1/sqrt(d_inner))
+
+    drawn in that order from one generator; u, in_proj, conv_w, conv_b,
+    norm_w and out_proj are then cast to the layer dtype, the rest stay
+    float32.  ``variant``:
+      "lam_one"   the lambda rows of in_proj zeroed and lam_bias set so
+                  that every lambda is 1 (the plain Mamba-2 block)
+      "D0"        D = 0
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(lw.seed if seed is None else seed)
+    f32 = dict(device=device, dtype=torch.float32, generator=g)
+
+    def unif(shape, bound):
+        return (torch.rand(*shape, **f32) * 2.0 - 1.0) * bound
+
+    u = torch.randn(lw.B, lw.T, lw.d_model, **f32)
+    in_proj = unif((lw.d_in_proj, lw.d_model), 1.0 / math.sqrt(lw.d_model))
+    conv_w = unif((lw.conv_dim, lw.K), 1.0 / math.sqrt(lw.K))
+    conv_b = unif((lw.conv_dim,), 1.0 / math.sqrt(lw.K))
+    dt0 = torch.exp(torch.rand(lw.H, **f32) * (math.log(1e-1) - math.log(1e-3)) + math.log(1e-3))
+    dt0 = dt0.clamp(min=1e-4)
+    dt_bias = dt0 + torch.log(-torch.expm1(-dt0))
+    A_log = torch.log(torch.rand(lw.H, **f32) * 15.0 + 1.0)
+    D = torch.ones(lw.H, device=device)
+    lam_bias = torch.zeros(lw.H, lw.L, device=device)
+    norm_w = torch.ones(lw.d_inner, device=device)
+    out_proj = unif((lw.d_model, lw.d_inner), 1.0 / math.sqrt(lw.d_inner))
+    for var in (variant.split("+") if variant else []):
+        if var == "lam_one":
+            in_proj[lw.d_in_proj - lw.H * lw.L:] = 0.0
+            lam_bias = torch.full_like(lam_bias, math.log(math.e - 1.0))
+        elif var == "D0":
+            D = torch.zeros_like(D)
+        else:
+            raise ValueError(f"unknown variant {var!r}")
+    dt = torch_dtype(lw.dtype)
+    return dict(u=u.to(dt).contiguous(), in_proj=in_proj.to(dt).contiguous(), conv_w=conv_w.to(dt).contiguous(),
+                conv_b=conv_b.to(dt).contiguous(), dt_bias=dt_bias.contiguous(), A_log=A_log.contiguous(),
+                D=D.contiguous(), lam_bias=lam_bias.contiguous(), norm_w=norm_w.to(dt).contiguous(),
+                out_proj=out_proj.to(dt).contiguous())

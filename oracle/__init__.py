@@ -37,6 +37,9 @@ Modules:
               and a pure-Python brute force for tiny inputs
   metrics  -- relative L2 error
   backward -- the gradients of the operator (chain rule on the quadratic form)
+  deltanet -- the log-linear Gated DeltaNet form
+  layer    -- the Log-Linear Mamba-2 layer around the operator (projections,
+              causal conv, gates, lambda, D skip, gated norm)
 
 Pin status (what fixes each function other than itself) is listed in the
 header of each module.  Nothing here is "parity unpinned"; the *choice* of the
@@ -44,4 +47,4 @@ level reading above is an interpretation of the pages, which print no formula
 for it.
 """
 
-from . import levels, forms, special, metrics, backward, deltanet  # noqa: F401
+from . import levels, forms, special, metrics, backward, deltanet, layer  # noqa: F401

@@ -1,0 +1,252 @@
+"""Pins of the Log-Linear Mamba-2 layer oracle (CPU only).
+
+``oracle.layer`` has three evaluations written separately: the parallel form
+(whole sequences, array operations), the stepwise decoding form (a rolling
+conv window and the Fenwick-state recurrence, with its own index arithmetic
+and its own softplus and silu formulas), and the stepwise form with the
+textbook Mamba-2 state.  What fixes them besides themselves:
+
+* parallel == stepwise (either operator form, several group counts, ragged
+  T, T = 1);
+* lambda = 1 on every level == the plain Mamba-2 block (a P x N state per
+  head, h = exp(dt A) h + dt x B^T, y = h C + D x): the hierarchical mask
+  collapses to Mamba-2's ([LLA-es] Resumen tecnico section 2, "Variantes",
+  item 1);
+* the causal conv equals numpy.convolve of each channel with its taps;
+* causality: outputs up to t do not move when later inputs change;
+* the gated norm gives unit mean square in every group when eps = 0;
+* planted mistakes (a reversed conv, a dropped bias, v without dt, the D skip
+  dropped, the gate after the norm, the wrong head-to-group map, B and C
+  swapped, ...) each fail at least one of these.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from fenwick_tree_hierarchical_amd.workloads import LAYER_WORKLOADS, layer_resized, make_layer
+from oracle import layer as olayer
+from oracle import metrics
+
+TINY = LAYER_WORKLOADS["layer_tiny_f32"]
+
+
+def _lam_one(w, lw):
+    # lambda = softplus(0 + log(e - 1)) = 1 exactly in float64
+    w = dict(w)
+    w["lam_bias"] = torch.full((lw.H, lw.L), math.log(math.e - 1.0), dtype=torch.float64)
+    return w
+
+
+CASES = [
+    dict(T=37),
+    dict(T=1),
+    dict(T=16, G=1),
+    dict(T=29, G=4),
+    dict(T=23, H=2, G=1, P=8, N=4, K=2),
+    dict(T=19, K=1),
+]
+
+
+@pytest.mark.parametrize("kw", CASES, ids=[str(c) for c in CASES])
+@pytest.mark.parametrize("operator", ["quadratic", "recurrent"])
+def test_parallel_equals_stepwise(kw, operator):
+    lw = layer_resized(TINY, **kw)
+    w = make_layer(lw, seed=3)
+    par = olayer.layer_forward(w["u"], w, lw, operator=operator)
+    step = olayer.layer_forward_stepwise(w["u"], w, lw)
+    assert metrics.rel_l2(par, step) < 1e-12
+
+
+@pytest.mark.parametrize("kw", [dict(T=41), dict(T=26, G=4), dict(T=9, G=1, K=3)])
+@pytest.mark.parametrize("variant", [None, "D0"])
+def test_lambda_one_is_the_plain_mamba2_block(kw, variant):
+    lw = layer_resized(TINY, **kw)
+    w = _lam_one(make_layer(lw, variant="lam_one" + ("+" + variant if variant else ""), seed=5), lw)
+    par = olayer.layer_forward(w["u"], w, lw)
+    ref = olayer.layer_forward_stepwise(w["u"], w, lw, ssm="mamba2")
+    assert metrics.rel_l2(par, ref) < 1e-12
+
+
+def test_lambda_matters():
+    # the same weights with the workload's lambda differ from the plain block
+    lw = layer_resized(TINY, T=41)
+    w = make_layer(lw, variant="D0", seed=5)
+    ref = olayer.layer_forward_stepwise(w["u"], w, lw, ssm="mamba2")
+    assert metrics.rel_l2(olayer.layer_forward(w["u"], w, lw), ref) > 1e-3
+
+
+def test_conv_is_numpy_convolve():
+    rng = np.random.default_rng(0)
+    Bn, T, ch, K = 2, 17, 5, 4
+    x = rng.standard_normal((Bn, T, ch))
+    wts = rng.standard_normal((ch, K))
+    bias = rng.standard_normal(ch)
+    got = olayer.causal_conv(x, wts, bias)
+    for b in range(Bn):
+        for c in range(ch):
+            # out[t] = sum_j w[j] x[t-(K-1)+j]  ==  (x * reversed w)[t] of the full convolution
+            ref = np.convolve(x[b, :, c], wts[c, ::-1])[:T] + bias[c]
+            np.testing.assert_allclose(got[b, :, c], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_causal():
+    lw = layer_resized(TINY, T=30)
+    w = make_layer(lw, seed=7)
+    base = olayer.layer_forward(w["u"], w, lw)
+    u2 = w["u"].clone()
+    u2[:, 17:] = torch.randn(u2[:, 17:].shape, generator=torch.Generator().manual_seed(1))
+    moved = olayer.layer_forward(u2, w, lw)
+    np.testing.assert_array_equal(moved[:, :17], base[:, :17])
+    assert np.abs(moved[:, 17:] - base[:, 17:]).max() > 1e-3
+
+
+def test_gated_norm_unit_mean_square():
+    rng = np.random.default_rng(1)
+    y = rng.standard_normal((2, 5, 12))
+    z = rng.standard_normal((2, 5, 12))
+    for G in (1, 2, 3, 4):
+        g = olayer.gated_rmsnorm(y, z, np.ones(12), G, 0.0)
+        ms = (g.reshape(2, 5, G, 12 // G) ** 2).mean(axis=-1)
+        np.testing.assert_allclose(ms, 1.0, rtol=1e-13)
+        # and the direction of y * silu(z) is kept inside each group
+        raw = (y * z / (1 + np.exp(-z))).reshape(2, 5, G, 12 // G)
+        cos = (raw * g.reshape(2, 5, G, 12 // G)).sum(-1) / np.linalg.norm(raw, axis=-1) / np.linalg.norm(
+            g.reshape(2, 5, G, 12 // G), axis=-1)
+        np.testing.assert_allclose(cos, 1.0, rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# planted mistakes
+# --------------------------------------------------------------------------
+
+def layer_pin_battery():
+    fails = []
+    for kw in (dict(T=37), dict(T=29, G=4)):
+        lw = layer_resized(TINY, **kw)
+        w = make_layer(lw, seed=3)
+        if metrics.rel_l2(olayer.layer_forward(w["u"], w, lw), olayer.layer_forward_stepwise(w["u"], w, lw)) > 1e-10:
+            fails.append(f"parallel_vs_stepwise {kw}")
+        w1 = _lam_one(make_layer(lw, variant="lam_one+D0", seed=5), lw)
+        if metrics.rel_l2(olayer.layer_forward(w1["u"], w1, lw),
+                          olayer.layer_forward_stepwise(w1["u"], w1, lw, ssm="mamba2")) > 1e-10:
+            fails.append(f"mamba2 {kw}")
+    return fails
+
+
+def test_battery_passes_unpatched():
+    assert layer_pin_battery() == []
+
+
+def _conv_reversed(xbc, conv_w, conv_b):
+    return ORIG["causal_conv"](xbc, conv_w[:, ::-1], conv_b)
+
+
+def _conv_no_bias(xbc, conv_w, conv_b):
+    return ORIG["causal_conv"](xbc, conv_w, np.zeros_like(conv_b))
+
+
+def _conv_future(xbc, conv_w, conv_b):
+    # taps over t .. t+K-1 instead of t-K+1 .. t
+    T = xbc.shape[1]
+    K = conv_w.shape[1]
+    pad = np.concatenate([xbc, np.zeros((xbc.shape[0], K - 1, xbc.shape[2]))], axis=1)
+    out = np.broadcast_to(conv_b, xbc.shape).copy()
+    for j in range(K):
+        out += conv_w[:, j] * pad[:, j:j + T, :]
+    return out
+
+
+def _inputs_no_dt_in_v(xbc, dt_raw, lam_raw, w, dims):
+    q, k, v, log_a, lam, x = ORIG["operator_inputs"](xbc, dt_raw, lam_raw, w, dims)
+    return q, k, x.transpose(0, 2, 1, 3), log_a, lam, x
+
+
+def _inputs_no_dt_bias(xbc, dt_raw, lam_raw, w, dims):
+    w2 = dict(w)
+    w2["dt_bias"] = np.zeros(dims.H)
+    return ORIG["operator_inputs"](xbc, dt_raw, lam_raw, w2, dims)
+
+
+def _inputs_bc_swapped(xbc, dt_raw, lam_raw, w, dims):
+    q, k, v, log_a, lam, x = ORIG["operator_inputs"](xbc, dt_raw, lam_raw, w, dims)
+    return k, q, v, log_a, lam, x
+
+
+def _inputs_group_round_robin(xbc, dt_raw, lam_raw, w, dims):
+    q, k, v, log_a, lam, x = ORIG["operator_inputs"](xbc, dt_raw, lam_raw, w, dims)
+    if dims.G in (1, dims.H):
+        return q, k, v, log_a, lam, x
+    # head h reads group h % G instead of h // (H / G)
+    hpg = dims.H // dims.G
+    perm = [(h % dims.G) * hpg for h in range(dims.H)]
+    return q[:, perm], k[:, perm], v, log_a, lam, x
+
+
+def _inputs_lam_no_bias(xbc, dt_raw, lam_raw, w, dims):
+    w2 = dict(w)
+    w2["lam_bias"] = np.zeros((dims.H, dims.L))
+    return ORIG["operator_inputs"](xbc, dt_raw, lam_raw, w2, dims)
+
+
+def _inputs_gate_sign(xbc, dt_raw, lam_raw, w, dims):
+    q, k, v, log_a, lam, x = ORIG["operator_inputs"](xbc, dt_raw, lam_raw, w, dims)
+    return q, k, v, log_a / 2.0, lam, x
+
+
+def _norm_before_gate(y, z, norm_w, G, eps):
+    ones = np.full_like(z, 50.0)          # silu(50) = 50 to double precision
+    n = ORIG["gated_rmsnorm"](y, ones, norm_w, G, eps)
+    return n * z / (1.0 + np.exp(-z))
+
+
+def _norm_gate_without_silu(y, z, norm_w, G, eps):
+    return ORIG["gated_rmsnorm"](y * z / (z / (1.0 + np.exp(-z))), z, norm_w, G, eps)
+
+
+def _norm_one_group(y, z, norm_w, G, eps):
+    return ORIG["gated_rmsnorm"](y, z, norm_w, 1, eps)
+
+
+def _silu_as_sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+ORIG = dict(causal_conv=olayer.causal_conv, operator_inputs=olayer.operator_inputs,
+            gated_rmsnorm=olayer.gated_rmsnorm, _silu=olayer._silu)
+
+MUTANTS = [
+    ("causal_conv", _conv_reversed),
+    ("causal_conv", _conv_no_bias),
+    ("causal_conv", _conv_future),
+    ("operator_inputs", _inputs_no_dt_in_v),
+    ("operator_inputs", _inputs_no_dt_bias),
+    ("operator_inputs", _inputs_bc_swapped),
+    ("operator_inputs", _inputs_group_round_robin),
+    ("operator_inputs", _inputs_lam_no_bias),
+    ("operator_inputs", _inputs_gate_sign),
+    ("gated_rmsnorm", _norm_before_gate),
+    ("gated_rmsnorm", _norm_gate_without_silu),
+    ("gated_rmsnorm", _norm_one_group),
+    ("_silu", _silu_as_sigmoid),
+]
+
+
+@pytest.mark.parametrize("name,fn", MUTANTS, ids=[f.__name__ for _, f in MUTANTS])
+def test_planted_mistake_fails_a_pin(monkeypatch, name, fn):
+    monkeypatch.setattr(olayer, name, fn)
+    assert layer_pin_battery(), f"{fn.__name__} passed every pin"
+
+
+def test_dropped_D_skip_fails_a_pin(monkeypatch):
+    orig = olayer.layer_forward
+
+    def no_skip(u, w, dims, operator="quadratic", return_parts=False):
+        w2 = dict(w)
+        w2["D"] = torch.zeros_like(torch.as_tensor(w["D"]))
+        return orig(u, w2, dims, operator, return_parts)
+
+    monkeypatch.setattr(olayer, "layer_forward", no_skip)
+    assert layer_pin_battery()
