@@ -18,7 +18,7 @@ __all__ = [
     "LogAttnError", "lib", "loglinear_fwd", "loglinear_fwd_workspace", "loglinear_fwd_num_stages",
     "loglinear_fwd_staged", "loglinear_fwd_noalloc", "loglinear_bwd", "loglinear_bwd_workspace", "LogLinearState", "loglinear_state_init", "loglinear_decode_step",
     "loglinear_level_table", "loglinear_strerror", "loglinear_gdn_fwd", "loglinear_gdn_fwd_workspace",
-    "LA_F32", "LA_BF16",
+    "loglinear_mamba2_fwd", "loglinear_mamba2_fwd_workspace", "MAMBA2_WEIGHTS", "LA_F32", "LA_BF16",
 ]
 
 LA_F32, LA_BF16 = 0, 1
@@ -31,6 +31,18 @@ _i, _i64, _p, _sz = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size
 class _LaState(ctypes.Structure):
     _fields_ = [("t", _i64), ("B", _i), ("H", _i), ("dk", _i), ("dv", _i), ("S", _i),
                 ("slots", _p), ("scale", _p)]
+
+
+class _Mamba2Dims(ctypes.Structure):
+    _fields_ = [("B", _i), ("T", _i64), ("d_model", _i), ("H", _i), ("P", _i), ("N", _i), ("G", _i), ("K", _i),
+                ("C", _i), ("L", _i), ("eps", ctypes.c_float), ("dtype", _i)]
+
+
+MAMBA2_WEIGHTS = ("in_proj", "conv_w", "conv_b", "dt_bias", "A_log", "D", "lam_bias", "norm_w", "out_proj")
+
+
+class _Mamba2Weights(ctypes.Structure):
+    _fields_ = [(n, _p) for n in MAMBA2_WEIGHTS]
 
 
 _SIGS = {
@@ -52,6 +64,8 @@ _SIGS = {
     "loglinear_level_table": ([_i64, _i, _p, _p], _i),
     "loglinear_gdn_fwd_workspace": ([_i, _i, _i64, _i, _i, _i, _i, ctypes.POINTER(_sz)], _i),
     "loglinear_gdn_fwd": ([_p, _p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
+    "loglinear_mamba2_fwd_workspace": ([ctypes.POINTER(_Mamba2Dims), ctypes.POINTER(_sz)], _i),
+    "loglinear_mamba2_fwd": ([_p, ctypes.POINTER(_Mamba2Weights), _p, ctypes.POINTER(_Mamba2Dims), _p, _sz, _p], _i),
 }
 
 
@@ -346,4 +360,54 @@ def loglinear_level_table(T: int, C: int, device="cuda") -> torch.Tensor:
     """int8 [T,T] Fenwick level table computed on the device (-1 above the diagonal)."""
     out = torch.empty(T, T, dtype=torch.int8, device=device)
     _check(lib().loglinear_level_table(T, C, _ptr(out), _stream(out.device)), "loglinear_level_table")
+    return out
+
+
+def _mamba2_dims(B, T, d_model, H, P, N, G, K, C, L, eps, dtype) -> _Mamba2Dims:
+    return _Mamba2Dims(B, T, d_model, H, P, N, G, K, C, L, float(eps), _dtype_code(dtype))
+
+
+def loglinear_mamba2_fwd_workspace(B: int, T: int, d_model: int, H: int, P: int, N: int, G: int, K: int, C: int,
+                                   L: int, eps: float, dtype: torch.dtype) -> int:
+    n = _sz(0)
+    d = _mamba2_dims(B, T, d_model, H, P, N, G, K, C, L, eps, dtype)
+    _check(lib().loglinear_mamba2_fwd_workspace(ctypes.byref(d), ctypes.byref(n)), "loglinear_mamba2_fwd_workspace")
+    return n.value
+
+
+def loglinear_mamba2_fwd(u, weights, H: int, P: int, N: int, G: int, C: int = 64, eps: float = 1e-5, out=None,
+                         workspace=None):
+    """Log-Linear Mamba-2 layer forward: u [B, T, d_model] -> [B, T, d_model].
+
+    ``weights`` maps the names in MAMBA2_WEIGHTS to device tensors:
+    in_proj [2HP + 2GN + H + HL, d_model], conv_w [HP + 2GN, K],
+    conv_b [HP + 2GN], norm_w [HP], out_proj [d_model, HP] in u's dtype;
+    dt_bias, A_log, D [H] and lam_bias [H, L] float32.  K and L are read
+    from conv_w and lam_bias.
+    """
+    w = [weights[n] for n in MAMBA2_WEIGHTS]
+    dev = _dev(u, *w)
+    B, T, d_model = u.shape
+    K, L = weights["conv_w"].shape[1], weights["lam_bias"].shape[1]
+    d_inner, conv_dim = H * P, H * P + 2 * G * N
+    shapes = dict(in_proj=(2 * d_inner + 2 * G * N + H + H * L, d_model), conv_w=(conv_dim, K), conv_b=(conv_dim,),
+                  dt_bias=(H,), A_log=(H,), D=(H,), lam_bias=(H, L), norm_w=(d_inner,), out_proj=(d_model, d_inner))
+    for n, shp in shapes.items():
+        if tuple(weights[n].shape) != shp:
+            raise ValueError(f"{n} has shape {tuple(weights[n].shape)}, expected {shp}")
+        want = torch.float32 if n in ("dt_bias", "A_log", "D", "lam_bias") else u.dtype
+        if weights[n].dtype != want:
+            raise TypeError(f"{n} must be {want}")
+    if out is None:
+        out = torch.empty(B, T, d_model, dtype=u.dtype, device=dev)
+    _dev(u, out)
+    if out.shape != (B, T, d_model) or out.dtype != u.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    d = _mamba2_dims(B, T, d_model, H, P, N, G, K, C, L, eps, u.dtype)
+    nws = loglinear_mamba2_fwd_workspace(B, T, d_model, H, P, N, G, K, C, L, eps, u.dtype)
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    wts = _Mamba2Weights(*[_ptr(t) for t in w])
+    _check(lib().loglinear_mamba2_fwd(_ptr(u), ctypes.byref(wts), _ptr(out), ctypes.byref(d), _ptr(workspace),
+                                      workspace.numel(), _stream(dev)), "loglinear_mamba2_fwd")
     return out

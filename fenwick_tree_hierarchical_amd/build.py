@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblogattn.so")
 SOURCES = ["la_abi.hip", "la_fwd_bf16.hip", "la_fwd_f32.hip", "la_bwd_bf16.hip", "la_bwd_f32.hip", "la_decode.hip",
-           "la_gdn_bf16.hip", "la_gdn_f32.hip"]
+           "la_gdn_bf16.hip", "la_gdn_f32.hip", "la_layer_bf16.hip", "la_layer_f32.hip"]
 ARCH = "gfx950"
 
 

@@ -9,12 +9,29 @@
 #include "la_fwd_impl.hpp"
 #include "la_gdn_impl.hpp"
 #include "la_internal.hpp"
+#include "la_layer_impl.hpp"
 #include "la_plan.hpp"
 #include "la_validate.hpp"
 
 using namespace la;
 
 namespace {
+
+// Kernel arguments of a non-empty forward over the workspace `w`.
+FwdArgs fwd_args(const FwdPlan& p, const void* q, const void* k, const void* v, const float* log_a,
+                 const float* lambda, void* out, char* w) {
+  FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.log_a = log_a; a.lam = lambda; a.out = out;
+  a.nodes_in = p.has_chunk_nodes() ? static_cast<void*>(w + p.off_nodes_in) : nullptr;
+  a.gch = p.has_chunk_nodes() ? reinterpret_cast<float*>(w + p.off_gch) : nullptr;
+  a.gstate = p.has_group_nodes() ? reinterpret_cast<float*>(w + p.off_gstate) : nullptr;
+  a.gtot = p.has_group_nodes() ? reinterpret_cast<float*>(w + p.off_gtot) : nullptr;
+  a.gprefix = p.has_group_nodes() ? reinterpret_cast<double*>(w + p.off_gprefix) : nullptr;
+  a.nodes = p.has_group_nodes() ? static_cast<void*>(w + p.off_nodes) : nullptr;
+  a.T = p.T; a.n_chunks = p.n_chunks; a.n_groups = p.n_groups; a.n_full_groups = p.n_full_groups; a.L = p.L;
+  a.lam_vec4 = (p.T * p.L) % 4 == 0 && aligned(lambda, 16);
+  return a;
+}
 
 // The forward; `st` (nullable) also receives the final recurrent state.
 int fwd_common(const void* q, const void* k, const void* v, const float* log_a, const float* lambda,
@@ -43,17 +60,7 @@ int fwd_common(const void* q, const void* k, const void* v, const float* log_a, 
   }
   rc = check_fwd_buffers(p, q, k, v, log_a, lambda, out, ws, ws_bytes);
   if (rc != kOK) return rc;
-  char* w = static_cast<char*>(ws);
-  FwdArgs a{};
-  a.q = q; a.k = k; a.v = v; a.log_a = log_a; a.lam = lambda; a.out = out;
-  a.nodes_in = p.has_chunk_nodes() ? static_cast<void*>(w + p.off_nodes_in) : nullptr;
-  a.gch = p.has_chunk_nodes() ? reinterpret_cast<float*>(w + p.off_gch) : nullptr;
-  a.gstate = p.has_group_nodes() ? reinterpret_cast<float*>(w + p.off_gstate) : nullptr;
-  a.gtot = p.has_group_nodes() ? reinterpret_cast<float*>(w + p.off_gtot) : nullptr;
-  a.gprefix = p.has_group_nodes() ? reinterpret_cast<double*>(w + p.off_gprefix) : nullptr;
-  a.nodes = p.has_group_nodes() ? static_cast<void*>(w + p.off_nodes) : nullptr;
-  a.T = T; a.n_chunks = p.n_chunks; a.n_groups = p.n_groups; a.n_full_groups = p.n_full_groups; a.L = L;
-  a.lam_vec4 = (T * L) % 4 == 0 && aligned(lambda, 16);
+  FwdArgs a = fwd_args(p, q, k, v, log_a, lambda, out, static_cast<char*>(ws));
   a.st_slots = st ? st->slots : nullptr;
   a.st_scale = st ? st->scale : nullptr;
   a.st_S = st ? st->S : 0;
@@ -304,6 +311,61 @@ LA_API int loglinear_level_table(int64_t T, int C, int8_t* out, la_stream_t stre
   if (!is_pow2(C) || C > (1 << 20)) return kESHAPE;
   if (!out) return kEINVAL;
   return launch_level_table(T, ilog2(C), out, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace {
+int plan_layer_dims(const la_mamba2_dims* d, LayerPlan* p) {
+  if (!d) return kEINVAL;
+  return plan_layer(d->B, d->T, d->d_model, d->H, d->P, d->N, d->G, d->K, d->C, d->L, d->eps, d->dtype, p);
+}
+}  // namespace
+
+extern "C" {
+
+LA_API int loglinear_mamba2_fwd_workspace(const la_mamba2_dims* dims, size_t* bytes) {
+  if (!bytes) return kEINVAL;
+  LayerPlan p;
+  const int rc = plan_layer_dims(dims, &p);
+  if (rc != kOK) return rc;
+  *bytes = p.ws_bytes;
+  return kOK;
+}
+
+LA_API int loglinear_mamba2_fwd(const void* u, const la_mamba2_weights* weights, void* out,
+                                const la_mamba2_dims* dims, void* workspace, size_t workspace_bytes,
+                                la_stream_t stream) {
+  LayerPlan p;
+  int rc = plan_layer_dims(dims, &p);
+  if (rc != kOK) return rc;
+  if (p.empty()) return kOK;
+  rc = check_layer_buffers(p, u, weights, out, workspace, workspace_bytes);
+  if (rc != kOK) return rc;
+  char* w = static_cast<char*>(workspace);
+  LayerArgs a{};
+  a.zx = w + p.off_zx;
+  a.conv_w = weights->conv_w; a.conv_b = weights->conv_b;
+  a.dt_bias = weights->dt_bias; a.A_log = weights->A_log; a.D = weights->D; a.lam_bias = weights->lam_bias;
+  a.norm_w = weights->norm_w;
+  a.q = w + p.off_q; a.k = w + p.off_k; a.v = w + p.off_v;
+  a.log_a = reinterpret_cast<float*>(w + p.off_loga);
+  a.lam = reinterpret_cast<float*>(w + p.off_lam);
+  a.o = w + p.off_o;
+  a.y = w + p.off_y;
+  a.T = p.T; a.H = p.H; a.P = p.P; a.N = p.N; a.G = p.G; a.K = p.K; a.L = p.L;
+  a.d_inner = p.d_inner; a.conv_dim = p.conv_dim; a.ld_zx = p.ld_zx;
+  a.col_x = p.col_x; a.col_b = p.col_b; a.col_c = p.col_c; a.col_dt = p.col_dt; a.col_lam = p.col_lam;
+  a.norm_slots = p.norm_slots; a.eps = p.eps;
+  const FwdArgs fa = fwd_args(p.op, a.q, a.k, a.v, a.log_a, a.lam, w + p.off_o, w + p.off_opws);
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf = p.dtype == kBF16;
+  rc = bf ? launch_layer_pre_bf16(p, u, weights->in_proj, a, s) : launch_layer_pre_f32(p, u, weights->in_proj, a, s);
+  if (rc != kOK) return rc;
+  rc = bf ? launch_fwd_bf16(p.op, fa, s, nullptr) : launch_fwd_f32(p.op, fa, s, nullptr);
+  if (rc != kOK) return rc;
+  return bf ? launch_layer_post_bf16(p, weights->out_proj, out, a, s)
+            : launch_layer_post_f32(p, weights->out_proj, out, a, s);
 }
 
 }  // extern "C"

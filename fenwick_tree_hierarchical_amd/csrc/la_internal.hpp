@@ -7,6 +7,7 @@
 #include "../../include/logattn.h"
 #include "la_bwd_plan.hpp"
 #include "la_gdn_plan.hpp"
+#include "la_layer_plan.hpp"
 #include "la_plan.hpp"
 
 namespace la {
@@ -14,6 +15,7 @@ namespace la {
 struct FwdArgs;
 struct BwdArgs;
 struct GdnArgs;
+struct LayerArgs;
 
 // Forward: enqueue the stages of `p` on stream s; ev (nullable) holds
 // p.n_stages + 1 events recorded around the stages.
@@ -28,6 +30,13 @@ int launch_bwd_f32(const BwdPlan& p, const FwdArgs& fa, const BwdArgs& a, hipStr
 // Log-linear Gated DeltaNet forward: enqueue its kernels on stream s.
 int launch_gdn_bf16(const GdnPlan& p, const GdnArgs& a, hipStream_t s);
 int launch_gdn_f32(const GdnPlan& p, const GdnArgs& a, hipStream_t s);
+
+// Log-Linear Mamba-2 layer: the input projection and the operator's inputs
+// (pre), then the gate, norm and output projection (post).
+int launch_layer_pre_bf16(const LayerPlan& p, const void* u, const void* in_proj, const LayerArgs& a, hipStream_t s);
+int launch_layer_pre_f32(const LayerPlan& p, const void* u, const void* in_proj, const LayerArgs& a, hipStream_t s);
+int launch_layer_post_bf16(const LayerPlan& p, const void* out_proj, void* out, const LayerArgs& a, hipStream_t s);
+int launch_layer_post_f32(const LayerPlan& p, const void* out_proj, void* out, const LayerArgs& a, hipStream_t s);
 
 int launch_decode(const la_state* st, const void* q, const void* k, const void* v, const float* a,
                   const float* lam, void* out, int dtype, int kstar, hipStream_t s);

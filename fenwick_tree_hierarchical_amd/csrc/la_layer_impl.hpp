@@ -1,0 +1,481 @@
+// Kernels of the Log-Linear Mamba-2 layer around the operator (gfx950):
+//
+//   gemm_nt          C = A B^T on the matrix cores: the input projection
+//                    (u -> z | x | B | C | dt | lam columns) and the output
+//                    projection
+//   mamba2_prologue  causal depthwise conv + silu of the x | B | C columns,
+//                    softplus gates, and the operator's inputs in its own
+//                    layout: q = C, k = B (per head of each group),
+//                    v = dt x, log_a = dt A, lambda = softplus(. + bias)
+//   mamba2_gate_norm y = o + D x (x recomputed from the conv), times silu(z),
+//                    normalised by the root mean square over each group of
+//                    channels, times the norm weight
+//
+// The layer is Mamba-2's block with its SSM replaced by the log-linear
+// operator ("Log-Linear Attention", Spanish summary, technical section 2,
+// "Variantes", item 1: Mamba-2's selective gate with the hierarchical mask);
+// the block itself (projections, conv, gates, gated norm) follows Mamba-2's
+// published design, since the pages give no layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "la_device.hpp"
+#include "la_layer_plan.hpp"
+
+namespace la {
+
+struct GemmArgs {
+  const void* A;   // [M][lda], rows 16-byte aligned
+  const void* B;   // [N][ldb]
+  void* C;         // [M][ldc]
+  int M, N, K, lda, ldb, ldc;   // K a multiple of the K-slice; ldc a multiple of 4
+  int tiles_n;
+};
+
+constexpr int kGemmStageBytes = 2 * kGemmTile * kGemmKBytes;   // A and B slices of one stage
+constexpr int kGemmLds = 2 * kGemmStageBytes;                    // double buffer
+
+// C[m][n] = sum_k A[m][k] B[n][k], fp32 accumulation, rounded to the element
+// type.  A workgroup of four waves computes a 128 x 128 tile, each wave a
+// 64 x 64 quarter as 4 x 4 matrix-core tiles.  K-slices (128 bytes of every
+// row of the A and B tiles) are double-buffered in LDS: the next slice is
+// loaded into registers while the current one is multiplied, then written
+// to the other buffer.  A slice row's eight 16-byte granules are stored
+// XOR-swizzled by the row's low three bits (granule g of row r at slot
+// g ^ (r & 7)), so the 16 rows one fragment read touches fall in distinct
+// banks.  Rows past M or N are clamped to the last row for loading and never
+// stored.
+template <bool BF16>
+__global__ __launch_bounds__(256, 2) void gemm_nt(GemmArgs g) {
+  using E = Elem<BF16>;
+  using T = typename E::T;
+  constexpr int ES = sizeof(T);
+  constexpr int TILE = kGemmTile, ROWB = kGemmKBytes;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+  // XCD-major tile order: consecutive workgroups are dealt round-robin over the
+  // 8 XCDs, so renumber them so that one XCD sweeps the column tiles of a row
+  // tile while that row tile sits in its L2
+  const int nblk = gridDim.x, per = nblk / 8;
+  int blk = blockIdx.x;
+  if (blk < per * 8) blk = (blk % 8) * per + blk / 8;
+  const int tm = blk / g.tiles_n, tn = blk % g.tiles_n;
+  const int m0 = tm * TILE, n0 = tn * TILE;
+
+  // loads: thread t moves granule t % 8 of rows t / 8 + 32 j (j = 0..3) of
+  // both tiles; eight consecutive threads cover one 128-byte row
+  const int lrow = tid >> 3, lgr = tid & 7;
+  const unsigned char* pa[4];
+  const unsigned char* pb[4];
+  int sw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = lrow + 32 * j;
+    const int ra = min(m0 + r, g.M - 1), rb = min(n0 + r, g.N - 1);
+    pa[j] = static_cast<const unsigned char*>(g.A) + (size_t)ra * g.lda * ES + lgr * 16;
+    pb[j] = static_cast<const unsigned char*>(g.B) + (size_t)rb * g.ldb * ES + lgr * 16;
+    sw[j] = r * ROWB + ((lgr ^ (r & 7)) << 4);
+  }
+  const int nk = g.K * ES / ROWB;
+  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+#define LA_GEMM_GLOAD(kt)                                                   \
+  do {                                                                      \
+    const size_t ko = (size_t)(kt) * ROWB;                                  \
+    ra0 = *reinterpret_cast<const uint4*>(pa[0] + ko);                      \
+    ra1 = *reinterpret_cast<const uint4*>(pa[1] + ko);                      \
+    ra2 = *reinterpret_cast<const uint4*>(pa[2] + ko);                      \
+    ra3 = *reinterpret_cast<const uint4*>(pa[3] + ko);                      \
+    rb0 = *reinterpret_cast<const uint4*>(pb[0] + ko);                      \
+    rb1 = *reinterpret_cast<const uint4*>(pb[1] + ko);                      \
+    rb2 = *reinterpret_cast<const uint4*>(pb[2] + ko);                      \
+    rb3 = *reinterpret_cast<const uint4*>(pb[3] + ko);                      \
+  } while (0)
+#define LA_GEMM_SWRITE(buf)                                                 \
+  do {                                                                      \
+    unsigned char* base = smem + (buf) * kGemmStageBytes;                   \
+    *reinterpret_cast<uint4*>(base + sw[0]) = ra0;                          \
+    *reinterpret_cast<uint4*>(base + sw[1]) = ra1;                          \
+    *reinterpret_cast<uint4*>(base + sw[2]) = ra2;                          \
+    *reinterpret_cast<uint4*>(base + sw[3]) = ra3;                          \
+    *reinterpret_cast<uint4*>(base + TILE * ROWB + sw[0]) = rb0;            \
+    *reinterpret_cast<uint4*>(base + TILE * ROWB + sw[1]) = rb1;            \
+    *reinterpret_cast<uint4*>(base + TILE * ROWB + sw[2]) = rb2;            \
+    *reinterpret_cast<uint4*>(base + TILE * ROWB + sw[3]) = rb3;            \
+  } while (0)
+
+  const int wm = w >> 1, wn = w & 1, fr = lane & 15, fq = lane >> 4;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  LA_GEMM_GLOAD(0);
+  LA_GEMM_SWRITE(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    // the next slice (the last one again on the last step: loaded, never written)
+    LA_GEMM_GLOAD(min(kt + 1, nk - 1));
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the products
+    const unsigned char* As = smem + (kt & 1) * kGemmStageBytes;
+    const unsigned char* Bs = As + TILE * ROWB;
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+      // granule 4 kg + fq of rows ... + fr; (row & 7) == (fr & 7) for every row read
+      const int slot = ((4 * kg + fq) ^ (fr & 7)) << 4;
+      uint4 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(As + (wm * 64 + 16 * i + fr) * ROWB + slot);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const uint4*>(Bs + (wn * 64 + 16 * j + fr) * ROWB + slot);
+      // B as the first operand: lane l then holds C[row l % 16][4 (l / 16) + 0..3]
+      if constexpr (BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = E::mma(__builtin_bit_cast(bf16x8, bf[j]), __builtin_bit_cast(bf16x8, af[i]), acc[i][j]);
+      } else {
+        // fp32: a granule holds 4 consecutive k; k-step c takes element c of
+        // every lane's granule, so the four steps cover the 16 k of the group
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[i][j] = E::mma(__builtin_bit_cast(float, (&bf[j].x)[c]), __builtin_bit_cast(float, (&af[i].x)[c]),
+                                 acc[i][j]);
+      }
+    }
+    // the other buffer was last read before the previous barrier (written
+    // on the last step too, unread, so that the loads above stay unconditional
+    // and are issued before the products)
+    LA_GEMM_SWRITE((kt + 1) & 1);
+    __syncthreads();
+  }
+#undef LA_GEMM_GLOAD
+#undef LA_GEMM_SWRITE
+
+  // store: four consecutive columns per lane and tile
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm * 64 + 16 * i + fr;
+    if (m >= g.M) continue;
+    T* crow = static_cast<T*>(g.C) + (size_t)m * g.ldc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn * 64 + 16 * j + 4 * fq;
+      if (n + 3 < g.N) {
+        if constexpr (BF16) {
+          const unsigned lo = (unsigned)E::from_f32(acc[i][j][0]) | ((unsigned)E::from_f32(acc[i][j][1]) << 16);
+          const unsigned hi = (unsigned)E::from_f32(acc[i][j][2]) | ((unsigned)E::from_f32(acc[i][j][3]) << 16);
+          *reinterpret_cast<uint2*>(crow + n) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<float4*>(crow + n) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < g.N) crow[n + e] = E::from_f32(acc[i][j][e]);
+      }
+    }
+  }
+}
+
+struct LayerArgs {
+  const void* zx;        // [B T][ld_zx] input projection, columns z | x | B | C | dt | lam
+  const void* conv_w;    // [conv_dim][K]
+  const void* conv_b;    // [conv_dim]
+  const float* dt_bias;  // [H]
+  const float* A_log;    // [H]
+  const float* D;        // [H]
+  const float* lam_bias; // [H][L]
+  const void* norm_w;    // [d_inner]
+  void* q;               // [B][H][T][N]
+  void* k;               // [B][H][T][N]
+  void* v;               // [B][H][T][P]
+  float* log_a;          // [B][H][T]
+  float* lam;            // [B][H][T][L]
+  const void* o;         // [B][H][T][P] operator output
+  void* y;               // [B T][d_inner] normalised gated output
+  int64_t T;
+  int H, P, N, G, K, L, d_inner, conv_dim, ld_zx;
+  int col_x, col_b, col_c, col_dt, col_lam;
+  int norm_slots;
+  float eps;
+};
+
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+__device__ __forceinline__ float silu_f(float x) { return x / (1.f + expf(-x)); }
+
+template <bool BF16, int VEC>
+__device__ __forceinline__ void load_vec(const typename Elem<BF16>::T* p, float (&x)[VEC]) {
+  if constexpr (BF16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const unsigned w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __builtin_bit_cast(float, w4[e] << 16);
+      x[2 * e + 1] = __builtin_bit_cast(float, w4[e] & 0xffff0000u);
+    }
+  } else {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+  }
+}
+
+template <bool BF16, int VEC>
+__device__ __forceinline__ void store_vec(typename Elem<BF16>::T* p, const float (&x)[VEC]) {
+  if constexpr (BF16) {
+    unsigned w4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w4[e] = (unsigned)f32_to_bf16(x[2 * e]) | ((unsigned)f32_to_bf16(x[2 * e + 1]) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  }
+}
+
+// Causal conv + silu of one 16-byte granule of conv channels over a run of
+// at most NMAX consecutive tokens of one sequence:
+// out[t] = bias + sum_j w[j] x[t-(K-1)+j], zero before the first token.  A
+// K-tap conv runs as a kMaxConvTaps-tap one whose leading taps are zero.
+// `emit(i, y)` receives token ts + i (i < n).
+template <bool BF16, int VEC, int NMAX, class Emit>
+__device__ __forceinline__ void conv_run(const typename Elem<BF16>::T* zx, int ld_zx, int c0, const void* conv_w,
+                                         const void* conv_b, int K, int64_t ts, int n, Emit emit) {
+  using E = Elem<BF16>;
+  using T = typename E::T;
+  constexpr int KT = kMaxConvTaps;
+  const T* cw = static_cast<const T*>(conv_w);
+  const T* cb = static_cast<const T*>(conv_b);
+  float ta[VEC][KT], bias[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    bias[e] = E::to_f32(cb[c0 + e]);
+#pragma unroll
+    for (int j = 0; j < KT; ++j) ta[e][j] = j >= KT - K ? E::to_f32(cw[(size_t)(c0 + e) * K + j - (KT - K)]) : 0.f;
+  }
+  // the KT - 1 inputs before the run, oldest first
+  float win[KT - 1][VEC];
+#pragma unroll
+  for (int j = 0; j < KT - 1; ++j) {
+    const int64_t t = ts - (KT - 1) + j;
+    if (t >= 0 && j >= KT - K) {
+      load_vec<BF16, VEC>(zx + t * ld_zx, win[j]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) win[j][e] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i) {
+    if (i >= n) break;
+    float cur[VEC];
+    load_vec<BF16, VEC>(zx + (ts + i) * ld_zx, cur);
+    float y[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      float acc = bias[e];
+#pragma unroll
+      for (int j = 0; j < KT - 1; ++j) acc = fmaf(ta[e][j], win[j][e], acc);
+      acc = fmaf(ta[e][KT - 1], cur[e], acc);
+      y[e] = silu_f(acc);
+    }
+#pragma unroll
+    for (int j = 0; j < KT - 2; ++j)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) win[j][e] = win[j + 1][e];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) win[KT - 2][e] = cur[e];
+    emit(i, y);
+  }
+}
+
+// One workgroup per (sequence, 64 tokens): the conv channels in runs of 16
+// tokens per thread, then the gates per (token, head).
+template <bool BF16>
+__global__ __launch_bounds__(256) void mamba2_prologue(LayerArgs a) {
+  using E = Elem<BF16>;
+  using T = typename E::T;
+  constexpr int VEC = 16 / sizeof(T);
+  const int b = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * kPrologueTokens;
+  const int nt = (int)min((int64_t)kPrologueTokens, a.T - t0);
+  const T* zx = static_cast<const T*>(a.zx) + (size_t)b * a.T * a.ld_zx;
+  const int H = a.H, hpg = a.H / a.G;
+  const size_t bh0 = (size_t)b * H;
+
+  // items: x granules, then (B or C granule, head of its group) pairs, each
+  // over runs of kPrologueRun tokens; a B or C granule is convolved once per
+  // head it is copied to (its inputs come from cache after the first)
+  const int XG = a.d_inner / VEC, BCG = 2 * a.G * a.N / VEC;
+  const int per_run = XG + BCG * hpg;
+  const int runs = (nt + kPrologueRun - 1) / kPrologueRun;
+  for (int item = threadIdx.x; item < per_run * runs; item += 256) {
+    const int run = item / per_run, it = item % per_run;
+    const int64_t ts = t0 + run * kPrologueRun;
+    const int n = (int)min((int64_t)kPrologueRun, a.T - ts);
+    if (it < XG) {
+      // x channels: v = dt x for head h
+      const int c0 = it * VEC, h = c0 / a.P, p0 = c0 % a.P;
+      const float dtb = a.dt_bias[h];
+      T* vh = static_cast<T*>(a.v) + ((bh0 + h) * a.T) * a.P + p0;
+      conv_run<BF16, VEC, kPrologueRun>(zx + a.col_x + c0, a.ld_zx, c0, a.conv_w, a.conv_b, a.K, ts, n,
+                                        [&](int i, float (&y)[VEC]) {
+        const int64_t t = ts + i;
+        const float dt = softplus_f(E::to_f32(zx[t * a.ld_zx + a.col_dt + h]) + dtb);
+        float o[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = y[e] * dt;
+        store_vec<BF16, VEC>(vh + t * a.P, o);
+      });
+    } else {
+      // B or C channels of group gi, written for head gi * hpg + hh
+      const int j = it - XG, gr = j / hpg, hh = j % hpg;
+      const int c0 = a.d_inner + gr * VEC;
+      const bool isB = c0 < a.d_inner + a.G * a.N;
+      const int cc = c0 - a.d_inner - (isB ? 0 : a.G * a.N);
+      const int gi = cc / a.N, n0 = cc % a.N;
+      T* dst = static_cast<T*>(isB ? a.k : a.q) + ((bh0 + (size_t)gi * hpg + hh) * a.T) * a.N + n0;
+      conv_run<BF16, VEC, kPrologueRun>(zx + a.col_x + c0, a.ld_zx, c0, a.conv_w, a.conv_b, a.K, ts, n,
+                                        [&](int i, float (&y)[VEC]) { store_vec<BF16, VEC>(dst + (ts + i) * a.N, y); });
+    }
+  }
+
+  // gates: adjacent threads take adjacent tokens of one head
+  for (int item = threadIdx.x; item < nt * H; item += 256) {
+    const int h = item / nt, i = item % nt;
+    const int64_t t = t0 + i;
+    const T* row = zx + t * a.ld_zx;
+    const float dt = softplus_f(E::to_f32(row[a.col_dt + h]) + a.dt_bias[h]);
+    const size_t r = (bh0 + h) * a.T + t;
+    a.log_a[r] = -expf(a.A_log[h]) * dt;
+    float* lr = a.lam + r * a.L;
+    const T* lin = row + a.col_lam + h * a.L;
+    const float* lb = a.lam_bias + h * a.L;
+    for (int l = 0; l < a.L; ++l) lr[l] = softplus_f(E::to_f32(lin[l]) + lb[l]);
+  }
+}
+
+// One workgroup per (sequence, kNormTokens tokens).  Thread (slot s,
+// granule g) rolls the x-channel conv of granule g over TR consecutive tokens
+// (TR = kNormTokens / slots), forms y = o + D x and the gated value
+// y silu(z), and leaves its sum of squares in LDS; each wave then reduces
+// (token, group) pairs, and the threads scale and store.
+template <bool BF16, int TR>
+__global__ __launch_bounds__(256) void mamba2_gate_norm(LayerArgs a) {
+  using E = Elem<BF16>;
+  using T = typename E::T;
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int TOK = kNormTokens, SLOTS = TOK / TR;
+  __shared__ float part[TOK][256];
+  __shared__ float rstd[TOK][256];
+  const int b = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * TOK;
+  const int nt = (int)min((int64_t)TOK, a.T - t0);
+  const T* zx = static_cast<const T*>(a.zx) + (size_t)b * a.T * a.ld_zx;
+  const int DG = a.d_inner / VEC;
+  const int tid = threadIdx.x, g = tid % DG, s = tid / DG;
+  const bool active = tid < SLOTS * DG;
+  const int GG = DG / a.G;   // granules per norm group
+  const int lane = tid & 63, w = tid >> 6;
+
+  float gz[TR][VEC];
+  const int64_t ts = t0 + (int64_t)s * TR;
+  const int n = active ? (int)max((int64_t)0, min((int64_t)TR, a.T - ts)) : 0;
+  if (n > 0) {
+    const int c0 = g * VEC, h = c0 / a.P, p0 = c0 % a.P;
+    const float Dh = a.D[h];
+    const T* oh = static_cast<const T*>(a.o) + (((size_t)b * a.H + h) * a.T) * a.P + p0;
+    conv_run<BF16, VEC, TR>(zx + a.col_x + c0, a.ld_zx, c0, a.conv_w, a.conv_b, a.K, ts, n,
+                            [&](int i, float (&x)[VEC]) {
+      const int64_t t = ts + i;
+      float o[VEC], z[VEC];
+      load_vec<BF16, VEC>(oh + t * a.P, o);
+      load_vec<BF16, VEC>(zx + t * a.ld_zx + c0, z);
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float v = (o[e] + Dh * x[e]) * silu_f(z[e]);
+        ss = fmaf(v, v, ss);
+        gz[i][e] = v;
+      }
+      part[s * TR + i][g] = ss;
+    });
+  }
+  __syncthreads();
+  const float inv = 1.f / (float)(a.d_inner / a.G);
+  for (int pr = w; pr < nt * a.G; pr += 4) {
+    const int r = pr / a.G, gi = pr % a.G;
+    float sum = 0.f;
+    for (int j = lane; j < GG; j += 64) sum += part[r][gi * GG + j];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 64);
+    if (lane == 0) rstd[r][gi] = 1.f / sqrtf(sum * inv + a.eps);
+  }
+  __syncthreads();
+  if (n > 0) {
+    const int c0 = g * VEC, gi = g / GG;
+    float nw[VEC];
+    load_vec<BF16, VEC>(static_cast<const T*>(a.norm_w) + c0, nw);
+    T* yrow = static_cast<T*>(a.y) + ((size_t)b * a.T) * a.d_inner + c0;
+#pragma unroll
+    for (int i = 0; i < TR; ++i) {
+      if (i >= n) break;
+      const float rs = rstd[s * TR + i][gi];
+      float o[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[e] = gz[i][e] * rs * nw[e];
+      store_vec<BF16, VEC>(yrow + (ts + i) * a.d_inner, o);
+    }
+  }
+}
+
+template <bool BF16>
+int launch_gemm(const void* A, const void* B, void* C, int M, int N, int K, int lda, int ldb, int ldc,
+                hipStream_t s) {
+  if (M == 0 || N == 0) return kOK;
+  GemmArgs g{A, B, C, M, N, K, lda, ldb, ldc, (N + kGemmTile - 1) / kGemmTile};
+  const int64_t blocks = (int64_t)((M + kGemmTile - 1) / kGemmTile) * g.tiles_n;
+  if (blocks > 0x7fffffff) return kESHAPE;
+  const int lds = kGemmLds;
+  if (hipFuncSetAttribute((const void*)gemm_nt<BF16>, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+    return kEHIP;
+  hipLaunchKernelGGL((gemm_nt<BF16>), dim3((unsigned)blocks), dim3(256), lds, s, g);
+  return hipGetLastError() == hipSuccess ? kOK : kEHIP;
+}
+
+// Input projection and the operator's inputs.
+template <bool BF16>
+int launch_layer_pre(const LayerPlan& p, const void* u, const void* in_proj, const LayerArgs& a, hipStream_t s) {
+  int rc = launch_gemm<BF16>(u, in_proj, const_cast<void*>(a.zx), (int)p.M, p.d_in_proj, p.d_model, p.d_model,
+                             p.d_model, p.ld_zx, s);
+  if (rc != kOK) return rc;
+  const dim3 grid((unsigned)((p.T + kPrologueTokens - 1) / kPrologueTokens), (unsigned)p.B);
+  hipLaunchKernelGGL((mamba2_prologue<BF16>), grid, dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? kOK : kEHIP;
+}
+
+// Gate, norm and output projection.
+template <bool BF16>
+int launch_layer_post(const LayerPlan& p, const void* out_proj, void* out, const LayerArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((p.T + kNormTokens - 1) / kNormTokens), (unsigned)p.B);
+  switch (kNormTokens / p.norm_slots) {
+    case 1: hipLaunchKernelGGL((mamba2_gate_norm<BF16, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((mamba2_gate_norm<BF16, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((mamba2_gate_norm<BF16, 4>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((mamba2_gate_norm<BF16, 8>), grid, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((mamba2_gate_norm<BF16, 16>), grid, dim3(256), 0, s, a); break;
+    default: return kESHAPE;
+  }
+  if (hipGetLastError() != hipSuccess) return kEHIP;
+  return launch_gemm<BF16>(a.y, out_proj, out, (int)p.M, p.d_model, p.d_inner, p.d_inner, p.d_inner, p.d_model, s);
+}
+
+}  // namespace la

@@ -11,6 +11,7 @@
 #include "../../include/logattn.h"
 #include "la_bwd_plan.hpp"
 #include "la_gdn_plan.hpp"
+#include "la_layer_plan.hpp"
 #include "la_plan.hpp"
 
 namespace la {
@@ -86,6 +87,24 @@ inline int check_decode(const la_state* st, const void* q, const void* k, const 
       return kEALIGN;
     if (!aligned(st->scale, 4) || !aligned(a, 4) || !aligned(lambda, 4)) return kEALIGN;
   }
+  return kOK;
+}
+
+// The input, output, weights and workspace of a non-empty layer forward.
+inline int check_layer_buffers(const LayerPlan& p, const void* u, const la_mamba2_weights* w, const void* out,
+                               const void* ws, size_t ws_bytes) {
+  if (!w) return kEINVAL;
+  if (!u || !out || !w->in_proj || !w->conv_w || !w->conv_b || !w->dt_bias || !w->A_log || !w->D || !w->lam_bias ||
+      !w->norm_w || !w->out_proj)
+    return kEINVAL;
+  if (!aligned(u, 16) || !aligned(out, 16) || !aligned(w->in_proj, 16) || !aligned(w->norm_w, 16) ||
+      !aligned(w->out_proj, 16))
+    return kEALIGN;
+  if (!aligned(w->conv_w, p.es) || !aligned(w->conv_b, p.es)) return kEALIGN;
+  if (!aligned(w->dt_bias, 4) || !aligned(w->A_log, 4) || !aligned(w->D, 4) || !aligned(w->lam_bias, 4))
+    return kEALIGN;
+  if (!ws || ws_bytes < p.ws_bytes) return kEWORKSPACE;
+  if (!aligned(ws, 256)) return kEALIGN;
   return kOK;
 }
 

@@ -313,6 +313,77 @@ LA_API int loglinear_gdn_fwd(const void* q, const void* k, const void* v, const 
                              size_t workspace_bytes, la_stream_t stream);
 
 /*
+ * Log-Linear Mamba-2 layer, forward: the Mamba-2 block with its SSM replaced
+ * by loglinear_fwd (Spanish summary, technical section 2, "Variantes", item
+ * 1: Mamba-2's selective gate combined with the hierarchical mask; the pages
+ * give no layer, so the block follows Mamba-2's published design, with one
+ * more group of projected columns for the level weights).  Per sequence b and
+ * token t, with d_inner = H P and head h in group g = h / (H / G):
+ *   zxbcdt = u W_in^T, columns z [H P] | x [H P] | B [G N] | C [G N] | dt [H]
+ *            | lam [H L]
+ *   x|B|C <- silu(causal depthwise conv over time, K taps, plus bias):
+ *            c[t] = conv_b + sum_{j<K} conv_w[j] xBC[t - (K-1) + j]
+ *   dt_h   = softplus(dt_h + dt_bias_h);  log_a_h = -exp(A_log_h) dt_h
+ *   o      = loglinear_fwd(q = C_g, k = B_g, v = dt_h x_h, log_a,
+ *                          lambda = softplus(lam + lam_bias))
+ *   y      = (o + D_h x_h) silu(z), divided by the root mean square over
+ *            each of G equal channel groups (plus eps), times norm_w
+ *   out    = y W_out^T
+ * The operator runs with d_k = N, d_v = P (so N == P) and chunk size C, on
+ * bfloat16 or float32 tensors as loglinear_fwd; projections accumulate in
+ * fp32 and store the element type; the conv, gates and norm run in fp32.
+ *
+ *   u        [B, T, d_model]       dtype, 16-byte aligned
+ *   out      [B, T, d_model]       dtype, 16-byte aligned; written
+ *   weights (la_mamba2_weights, device pointers, read only):
+ *     in_proj  [d_in_proj, d_model] dtype, 16-byte aligned,
+ *              d_in_proj = 2 H P + 2 G N + H + H L
+ *     conv_w   [H P + 2 G N, K]     dtype;  conv_b [H P + 2 G N] dtype
+ *     dt_bias, A_log, D  [H] float32;  lam_bias [H, L] float32
+ *     norm_w   [H P] dtype, 16-byte aligned
+ *     out_proj [d_model, H P] dtype, 16-byte aligned
+ *   sizes (la_mamba2_dims): d_model and H P multiples of 64 (bfloat16) or
+ *     32 (float32); H P at most 2048 (bfloat16) or 1024 (float32); G
+ *     divides H and H P / G is a multiple of 8; 1 <= K <= 4; P == N with
+ *     (P, C, L) as loglinear_fwd accepts for T tokens; 0 <= eps <= 1
+ *   workspace at least loglinear_mamba2_fwd_workspace() bytes, 256-byte
+ *            aligned, owned by the caller: the projection, the operator's
+ *            inputs and output, and its own workspace
+ * Asynchronous on `stream`; every check happens on the host before any
+ * launch, and on error nothing is written.  Errors: LA_EINVAL (null
+ * pointer, non-positive size, eps out of range), LA_ESHAPE, LA_EDTYPE,
+ * LA_EALIGN, LA_EWORKSPACE, LA_EHIP.  B = 0 or T = 0 writes nothing.
+ */
+typedef struct la_mamba2_dims {
+  int B;          /* sequences */
+  int64_t T;      /* tokens per sequence */
+  int d_model;    /* input and output width */
+  int H, P, N, G; /* heads, head dim, state size, groups of heads sharing B and C */
+  int K;          /* conv taps */
+  int C;          /* operator chunk size */
+  int L;          /* lambda levels */
+  float eps;      /* norm epsilon */
+  int dtype;      /* la_dtype */
+} la_mamba2_dims;
+
+typedef struct la_mamba2_weights {
+  const void* in_proj;
+  const void* conv_w;
+  const void* conv_b;
+  const float* dt_bias;
+  const float* A_log;
+  const float* D;
+  const float* lam_bias;
+  const void* norm_w;
+  const void* out_proj;
+} la_mamba2_weights;
+
+LA_API int loglinear_mamba2_fwd_workspace(const la_mamba2_dims* dims, size_t* bytes);
+LA_API int loglinear_mamba2_fwd(const void* u, const la_mamba2_weights* weights, void* out,
+                                const la_mamba2_dims* dims, void* workspace, size_t workspace_bytes,
+                                la_stream_t stream);
+
+/*
  * Fenwick level table for checking: out[t * T + s] = l(t, s) for s <= t and
  * -1 for s > t, as int8, computed on the device with chunks of C tokens the
  * way the forward kernels find levels.  Inside a chunk it is the level

@@ -28,7 +28,9 @@ Three evaluations, written separately:
 
 * ``layer_forward`` -- the parallel form over whole sequences (numpy array
   operations; the operator by ``forms.forward_quadratic`` or
-  ``forms.forward_recurrent``).  The GPU layer is compared with this one.
+  ``forms.forward_recurrent``), in two halves around the operator,
+  ``layer_operator_inputs`` and ``layer_output``, so that long sequences can
+  run the operator head by head.  The GPU layer is compared with this one.
 * ``layer_forward_stepwise(ssm="fenwick")`` -- the decoding form: one token
   at a time, a rolling window of the last K conv inputs per channel, the
   operator by its Fenwick-state recurrence (``forms.recurrent_step``), its own
@@ -120,7 +122,30 @@ def gated_rmsnorm(y, z, norm_w, G, eps):
     return (gg * r).reshape(Bn, T, d) * norm_w
 
 
-def layer_forward(u, w, dims, operator: str = "quadratic", return_parts: bool = False):
+def layer_operator_inputs(u, w, dims):
+    """The steps before the operator: the input projection, the conv, the
+    gates and lambda.  Returns (q, k, v, log_a, lam, x, z) with q, k, v
+    [B, H, T, .], log_a [B, H, T], lam [B, H, T, L], x [B, T, H, P] (the
+    conv output of the x channels) and z [B, T, H P]."""
+    u = _f64(u)
+    zxbcdt = u @ _f64(w["in_proj"]).T
+    z, xbc, dt_raw, lam_raw = split_projection(zxbcdt, dims)
+    xbc = _silu(causal_conv(xbc, _f64(w["conv_w"]), _f64(w["conv_b"])))
+    q, k, v, log_a, lam, x = operator_inputs(xbc, dt_raw, lam_raw, w, dims)
+    return q, k, v, log_a, lam, x, z
+
+
+def layer_output(o, x, z, w, dims):
+    """The steps after the operator: the D skip, the gated norm and the output
+    projection.  o [B, H, T, P] -> [B, T, d_model]."""
+    o = _f64(o)
+    Bn, H, T, P = o.shape
+    y = o.transpose(0, 2, 1, 3) + _f64(w["D"])[:, None] * x        # [B, T, H, P]
+    g = gated_rmsnorm(y.reshape(Bn, T, H * P), z, _f64(w["norm_w"]), dims.G, dims.eps)
+    return g @ _f64(w["out_proj"]).T
+
+
+def layer_forward(u, w, dims, operator: str = "quadratic"):
     """The layer over whole sequences; u [B, T, d_model] -> [B, T, d_model].
 
     ``w`` maps names to arrays or tensors: in_proj [d_in_proj, d_model],
@@ -129,25 +154,14 @@ def layer_forward(u, w, dims, operator: str = "quadratic", return_parts: bool = 
     the attributes H, P, N, G, L, eps.  ``operator`` picks the operator's
     quadratic or recurrent form.
     """
-    u = _f64(u)
-    Bn, T, _ = u.shape
-    H, P = dims.H, dims.P
-    zxbcdt = u @ _f64(w["in_proj"]).T
-    z, xbc, dt_raw, lam_raw = split_projection(zxbcdt, dims)
-    xbc = _silu(causal_conv(xbc, _f64(w["conv_w"]), _f64(w["conv_b"])))
-    q, k, v, log_a, lam, x = operator_inputs(xbc, dt_raw, lam_raw, w, dims)
+    q, k, v, log_a, lam, x, z = layer_operator_inputs(u, w, dims)
     if operator == "quadratic":
         o = _forms.forward_quadratic(q, k, v, log_a, lam)
     elif operator == "recurrent":
         o, _ = _forms.forward_recurrent(q, k, v, lam, log_a=log_a)
     else:
         raise ValueError(operator)
-    y = o.transpose(0, 2, 1, 3) + _f64(w["D"])[:, None] * x        # [B, T, H, P]
-    g = gated_rmsnorm(y.reshape(Bn, T, H * P), z, _f64(w["norm_w"]), dims.G, dims.eps)
-    out = g @ _f64(w["out_proj"]).T
-    if return_parts:
-        return out, dict(q=q, k=k, v=v, log_a=log_a, lam=lam, o=o, g=g, zxbcdt=zxbcdt)
-    return out
+    return layer_output(o, x, z, w, dims)
 
 
 def layer_forward_stepwise(u, w, dims, ssm: str = "fenwick"):

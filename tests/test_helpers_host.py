@@ -1,6 +1,7 @@
 """Host checks of the parity-test helpers (no GPU)."""
 
 import numpy as np
+import pytest
 
 from fenwick_tree_hierarchical_amd.workloads import WORKLOADS, make_inputs
 from oracle import forms
@@ -30,3 +31,17 @@ def test_parity_sees_one_wrong_row_and_one_wrong_head():
     bad[0, 1] *= 1.1                            # one head 10 % off
     p = parity(bad, ref)
     assert p["whole"] < 5e-2 and p["head"] > 9e-2 and tuple(p["worst_head"]) == (0, 1)
+
+
+def test_a_single_row_head_is_held_to_the_row_bar():
+    from tests.helpers import ROW_FACTOR, assert_parity
+    ref = np.ones((8, 1, 8))
+    got = ref.copy()
+    got[0, 0] *= 1.03                     # 3 % off: above the head bar, below the row bar
+    assert_parity(got, ref, 0.02, "one row", lead=1)
+    ref2 = np.ones((8, 2, 8))
+    got2 = ref2.copy()
+    got2[0] *= 1.03                       # a two-row head 3 % off fails the head bar
+    with pytest.raises(AssertionError):
+        assert_parity(got2, ref2, 0.02, "two rows", lead=1)
+    assert ROW_FACTOR * 0.02 > 0.03

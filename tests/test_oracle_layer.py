@@ -243,10 +243,10 @@ def test_planted_mistake_fails_a_pin(monkeypatch, name, fn):
 def test_dropped_D_skip_fails_a_pin(monkeypatch):
     orig = olayer.layer_forward
 
-    def no_skip(u, w, dims, operator="quadratic", return_parts=False):
+    def no_skip(u, w, dims, operator="quadratic"):
         w2 = dict(w)
         w2["D"] = torch.zeros_like(torch.as_tensor(w["D"]))
-        return orig(u, w2, dims, operator, return_parts)
+        return orig(u, w2, dims, operator)
 
     monkeypatch.setattr(olayer, "layer_forward", no_skip)
     assert layer_pin_battery()
