@@ -348,6 +348,7 @@ LA_API int loglinear_mamba2_fwd(const void* u, const la_mamba2_weights* weights,
   a.conv_w = weights->conv_w; a.conv_b = weights->conv_b;
   a.dt_bias = weights->dt_bias; a.A_log = weights->A_log; a.D = weights->D; a.lam_bias = weights->lam_bias;
   a.norm_w = weights->norm_w;
+  a.taps = reinterpret_cast<float*>(w + p.off_taps);
   a.q = w + p.off_q; a.k = w + p.off_k; a.v = w + p.off_v;
   a.log_a = reinterpret_cast<float*>(w + p.off_loga);
   a.lam = reinterpret_cast<float*>(w + p.off_lam);

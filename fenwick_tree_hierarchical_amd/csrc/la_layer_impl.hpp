@@ -195,6 +195,7 @@ struct LayerArgs {
   const float* D;        // [H]
   const float* lam_bias; // [H][L]
   const void* norm_w;    // [d_inner]
+  float* taps;           // [conv_dim][kMaxConvTaps + 1] fp32: taps right-aligned, then the bias
   void* q;               // [B][H][T][N]
   void* k;               // [B][H][T][N]
   void* v;               // [B][H][T][P]
@@ -210,7 +211,8 @@ struct LayerArgs {
 };
 
 __device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
-__device__ __forceinline__ float silu_f(float x) { return x / (1.f + expf(-x)); }
+// silu with the hardware exponential and reciprocal (a few ulp): x / (1 + e^-x)
+__device__ __forceinline__ float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 template <bool BF16, int VEC>
 __device__ __forceinline__ void load_vec(const typename Elem<BF16>::T* p, float (&x)[VEC]) {
@@ -229,6 +231,21 @@ __device__ __forceinline__ void load_vec(const typename Elem<BF16>::T* p, float 
 }
 
 template <bool BF16, int VEC>
+__device__ __forceinline__ void unpack(const uint4 u, float (&x)[VEC]) {
+  if constexpr (BF16) {
+    const unsigned w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __builtin_bit_cast(float, w4[e] << 16);
+      x[2 * e + 1] = __builtin_bit_cast(float, w4[e] & 0xffff0000u);
+    }
+  } else {
+    x[0] = __builtin_bit_cast(float, u.x); x[1] = __builtin_bit_cast(float, u.y);
+    x[2] = __builtin_bit_cast(float, u.z); x[3] = __builtin_bit_cast(float, u.w);
+  }
+}
+
+template <bool BF16, int VEC>
 __device__ __forceinline__ void store_vec(typename Elem<BF16>::T* p, const float (&x)[VEC]) {
   if constexpr (BF16) {
     unsigned w4[4];
@@ -241,139 +258,159 @@ __device__ __forceinline__ void store_vec(typename Elem<BF16>::T* p, const float
   }
 }
 
-// Causal conv + silu of one 16-byte granule of conv channels over a run of
-// at most NMAX consecutive tokens of one sequence:
-// out[t] = bias + sum_j w[j] x[t-(K-1)+j], zero before the first token.  A
-// K-tap conv runs as a kMaxConvTaps-tap one whose leading taps are zero.
-// `emit(i, y)` receives token ts + i (i < n).
-template <bool BF16, int VEC, int NMAX, class Emit>
-__device__ __forceinline__ void conv_run(const typename Elem<BF16>::T* zx, int ld_zx, int c0, const void* conv_w,
-                                         const void* conv_b, int K, int64_t ts, int n, Emit emit) {
+// The conv taps as fp32, right-aligned in kMaxConvTaps slots (a K-tap conv
+// runs as a kMaxConvTaps-tap one whose leading taps are zero), followed by the
+// bias: one 20-byte row per channel, read by the conv kernels as a float4 and
+// a float.
+template <bool BF16>
+__global__ __launch_bounds__(256) void mamba2_taps(LayerArgs a) {
   using E = Elem<BF16>;
   using T = typename E::T;
-  constexpr int KT = kMaxConvTaps;
-  const T* cw = static_cast<const T*>(conv_w);
-  const T* cb = static_cast<const T*>(conv_b);
-  float ta[VEC][KT], bias[VEC];
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= a.conv_dim) return;
+  const T* cw = static_cast<const T*>(a.conv_w) + (size_t)c * a.K;
+  const int pad = kMaxConvTaps - a.K;
+  float* row = a.taps + (size_t)c * (kMaxConvTaps + 1);
+  for (int j = 0; j < kMaxConvTaps; ++j) row[j] = j >= pad ? E::to_f32(cw[j - pad]) : 0.f;
+  row[kMaxConvTaps] = E::to_f32(static_cast<const T*>(a.conv_b)[c]);
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_taps(const float* taps, int c0, float (&w)[VEC][kMaxConvTaps], float (&bias)[VEC]) {
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    bias[e] = E::to_f32(cb[c0 + e]);
+    const float* r = taps + (size_t)(c0 + e) * (kMaxConvTaps + 1);
 #pragma unroll
-    for (int j = 0; j < KT; ++j) ta[e][j] = j >= KT - K ? E::to_f32(cw[(size_t)(c0 + e) * K + j - (KT - K)]) : 0.f;
-  }
-  // the KT - 1 inputs before the run, oldest first
-  float win[KT - 1][VEC];
-#pragma unroll
-  for (int j = 0; j < KT - 1; ++j) {
-    const int64_t t = ts - (KT - 1) + j;
-    if (t >= 0 && j >= KT - K) {
-      load_vec<BF16, VEC>(zx + t * ld_zx, win[j]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) win[j][e] = 0.f;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < NMAX; ++i) {
-    if (i >= n) break;
-    float cur[VEC];
-    load_vec<BF16, VEC>(zx + (ts + i) * ld_zx, cur);
-    float y[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      float acc = bias[e];
-#pragma unroll
-      for (int j = 0; j < KT - 1; ++j) acc = fmaf(ta[e][j], win[j][e], acc);
-      acc = fmaf(ta[e][KT - 1], cur[e], acc);
-      y[e] = silu_f(acc);
-    }
-#pragma unroll
-    for (int j = 0; j < KT - 2; ++j)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) win[j][e] = win[j + 1][e];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) win[KT - 2][e] = cur[e];
-    emit(i, y);
+    for (int j = 0; j < kMaxConvTaps; ++j) w[e][j] = r[j];
+    bias[e] = r[kMaxConvTaps];
   }
 }
 
-// One workgroup per (sequence, 64 tokens): the conv channels in runs of 16
-// tokens per thread, then the gates per (token, head).
+constexpr int kSlabGranules = 16;   // conv channels per prologue workgroup, in 16-byte granules
+constexpr int kHalo = kMaxConvTaps - 1;
+constexpr int kSlabHeads = 16;      // x heads one slab can touch: 128 channels over heads of P >= 16
+
+// Grid (token tiles of kPrologueTokens, sequences, conv slabs + 1).  A conv
+// slab stages kHalo + 64 rows of its 16 granules of conv input in LDS (rows
+// before the first token are zero), then thread (granule g, block tb) forms
+// the conv + silu of tokens 4 tb .. 4 tb + 3 and stores them where the
+// operator reads them: v = dt x for x channels, q / k for every head of the
+// group for C / B channels.  The last slab writes the gates: lambda of head
+// h as one contiguous [tokens, L] block, and log_a.
 template <bool BF16>
-__global__ __launch_bounds__(256) void mamba2_prologue(LayerArgs a) {
+__global__ __launch_bounds__(256) void mamba2_prologue(LayerArgs a, int n_slabs) {
   using E = Elem<BF16>;
   using T = typename E::T;
-  constexpr int VEC = 16 / sizeof(T);
-  const int b = blockIdx.y;
-  const int64_t t0 = (int64_t)blockIdx.x * kPrologueTokens;
-  const int nt = (int)min((int64_t)kPrologueTokens, a.T - t0);
+  constexpr int VEC = 16 / sizeof(T), TOK = kPrologueTokens, SG = kSlabGranules;
+  __shared__ uint4 xs[TOK + kHalo][SG];
+  __shared__ float dtS[TOK][kSlabHeads];
+  const int b = blockIdx.y, slab = blockIdx.z, tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * TOK;
+  const int nt = (int)min((int64_t)TOK, a.T - t0);
   const T* zx = static_cast<const T*>(a.zx) + (size_t)b * a.T * a.ld_zx;
   const int H = a.H, hpg = a.H / a.G;
   const size_t bh0 = (size_t)b * H;
 
-  // items: x granules, then (B or C granule, head of its group) pairs, each
-  // over runs of kPrologueRun tokens; a B or C granule is convolved once per
-  // head it is copied to (its inputs come from cache after the first)
-  const int XG = a.d_inner / VEC, BCG = 2 * a.G * a.N / VEC;
-  const int per_run = XG + BCG * hpg;
-  const int runs = (nt + kPrologueRun - 1) / kPrologueRun;
-  for (int item = threadIdx.x; item < per_run * runs; item += 256) {
-    const int run = item / per_run, it = item % per_run;
-    const int64_t ts = t0 + run * kPrologueRun;
-    const int n = (int)min((int64_t)kPrologueRun, a.T - ts);
-    if (it < XG) {
-      // x channels: v = dt x for head h
-      const int c0 = it * VEC, h = c0 / a.P, p0 = c0 % a.P;
-      const float dtb = a.dt_bias[h];
-      T* vh = static_cast<T*>(a.v) + ((bh0 + h) * a.T) * a.P + p0;
-      conv_run<BF16, VEC, kPrologueRun>(zx + a.col_x + c0, a.ld_zx, c0, a.conv_w, a.conv_b, a.K, ts, n,
-                                        [&](int i, float (&y)[VEC]) {
-        const int64_t t = ts + i;
-        const float dt = softplus_f(E::to_f32(zx[t * a.ld_zx + a.col_dt + h]) + dtb);
-        float o[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) o[e] = y[e] * dt;
-        store_vec<BF16, VEC>(vh + t * a.P, o);
-      });
-    } else {
-      // B or C channels of group gi, written for head gi * hpg + hh
-      const int j = it - XG, gr = j / hpg, hh = j % hpg;
-      const int c0 = a.d_inner + gr * VEC;
-      const bool isB = c0 < a.d_inner + a.G * a.N;
-      const int cc = c0 - a.d_inner - (isB ? 0 : a.G * a.N);
-      const int gi = cc / a.N, n0 = cc % a.N;
-      T* dst = static_cast<T*>(isB ? a.k : a.q) + ((bh0 + (size_t)gi * hpg + hh) * a.T) * a.N + n0;
-      conv_run<BF16, VEC, kPrologueRun>(zx + a.col_x + c0, a.ld_zx, c0, a.conv_w, a.conv_b, a.K, ts, n,
-                                        [&](int i, float (&y)[VEC]) { store_vec<BF16, VEC>(dst + (ts + i) * a.N, y); });
+  if (slab == n_slabs) {
+    // gates: lambda blocks (coalesced stores, short row gathers), then log_a
+    const int per_head = nt * a.L;
+    for (int j = tid; j < H * per_head; j += 256) {
+      const int h = j / per_head, r = j % per_head, i = r / a.L, l = r % a.L;
+      const float raw = E::to_f32(zx[(t0 + i) * a.ld_zx + a.col_lam + h * a.L + l]);
+      a.lam[((bh0 + h) * a.T + t0) * a.L + r] = softplus_f(raw + a.lam_bias[h * a.L + l]);
     }
+    for (int j = tid; j < H * nt; j += 256) {
+      const int h = j / nt, i = j % nt;
+      const float raw = E::to_f32(zx[(t0 + i) * a.ld_zx + a.col_dt + h]);
+      a.log_a[(bh0 + h) * a.T + t0 + i] = -expf(a.A_log[h]) * softplus_f(raw + a.dt_bias[h]);
+    }
+    return;
   }
 
-  // gates: adjacent threads take adjacent tokens of one head
-  for (int item = threadIdx.x; item < nt * H; item += 256) {
-    const int h = item / nt, i = item % nt;
-    const int64_t t = t0 + i;
-    const T* row = zx + t * a.ld_zx;
-    const float dt = softplus_f(E::to_f32(row[a.col_dt + h]) + a.dt_bias[h]);
-    const size_t r = (bh0 + h) * a.T + t;
-    a.log_a[r] = -expf(a.A_log[h]) * dt;
-    float* lr = a.lam + r * a.L;
-    const T* lin = row + a.col_lam + h * a.L;
-    const float* lb = a.lam_bias + h * a.L;
-    for (int l = 0; l < a.L; ++l) lr[l] = softplus_f(E::to_f32(lin[l]) + lb[l]);
+  const int CG = a.conv_dim / VEC, g0 = slab * SG, ng = min(SG, CG - g0);
+  for (int i = tid; i < (nt + kHalo) * SG; i += 256) {
+    const int r = i / SG, g = i % SG;
+    const int64_t t = t0 - kHalo + r;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (g < ng && t >= 0) x = *reinterpret_cast<const uint4*>(zx + t * a.ld_zx + a.col_x + (g0 + g) * VEC);
+    xs[r][g] = x;
+  }
+  // dt of the x heads this slab touches
+  const int c_lo = g0 * VEC, c_hi = min((g0 + ng) * VEC, a.d_inner);
+  const int h_lo = c_lo / a.P, nh = c_hi > c_lo ? (c_hi - 1) / a.P - h_lo + 1 : 0;
+  for (int j = tid; j < nt * nh; j += 256) {
+    const int i = j / nh, hh = j % nh;
+    dtS[i][hh] = softplus_f(E::to_f32(zx[(t0 + i) * a.ld_zx + a.col_dt + h_lo + hh]) + a.dt_bias[h_lo + hh]);
+  }
+  __syncthreads();
+
+  const int g = tid % SG, tb = tid / SG;
+  if (g >= ng) return;
+  const int c0 = (g0 + g) * VEC;
+  T* dst = nullptr;
+  size_t head_stride = 0;
+  int copies = 1, h = 0;
+  if (c0 < a.d_inner) {
+    h = c0 / a.P;
+    dst = static_cast<T*>(a.v) + ((bh0 + h) * a.T + t0) * a.P + c0 % a.P;
+  } else {
+    const bool isB = c0 < a.d_inner + a.G * a.N;
+    const int cc = c0 - a.d_inner - (isB ? 0 : a.G * a.N);
+    const int gi = cc / a.N;
+    dst = static_cast<T*>(isB ? a.k : a.q) + ((bh0 + (size_t)gi * hpg) * a.T + t0) * a.N + cc % a.N;
+    head_stride = (size_t)a.T * a.N;
+    copies = hpg;
+  }
+  const int row_len = c0 < a.d_inner ? a.P : a.N;
+  float w[VEC][kMaxConvTaps], bias[VEC];
+  load_taps<VEC>(a.taps, c0, w, bias);
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const int i = 4 * tb + ii;
+    if (i >= nt) break;
+    float y[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) y[e] = bias[e];
+#pragma unroll
+    for (int j = 0; j < kMaxConvTaps; ++j) {
+      float xv[VEC];
+      const uint4 u = xs[i + j][g];
+      if constexpr (BF16) {
+        const unsigned w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[2 * e] = __builtin_bit_cast(float, w4[e] << 16);
+          xv[2 * e + 1] = __builtin_bit_cast(float, w4[e] & 0xffff0000u);
+        }
+      } else {
+        xv[0] = __builtin_bit_cast(float, u.x); xv[1] = __builtin_bit_cast(float, u.y);
+        xv[2] = __builtin_bit_cast(float, u.z); xv[3] = __builtin_bit_cast(float, u.w);
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) y[e] = fmaf(w[e][j], xv[e], y[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) y[e] = silu_f(y[e]);
+    if (c0 < a.d_inner) {
+      const float dt = dtS[i][h - h_lo];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) y[e] *= dt;
+    }
+    for (int hh = 0; hh < copies; ++hh) store_vec<BF16, VEC>(dst + hh * head_stride + (size_t)i * row_len, y);
   }
 }
 
 // One workgroup per (sequence, kNormTokens tokens).  Thread (slot s,
-// granule g) rolls the x-channel conv of granule g over TR consecutive tokens
-// (TR = kNormTokens / slots), forms y = o + D x and the gated value
-// y silu(z), and leaves its sum of squares in LDS; each wave then reduces
-// (token, group) pairs, and the threads scale and store.
+// granule g) forms, for TR = kNormTokens / slots consecutive tokens, the
+// x-channel conv + silu of granule g (taps from LDS), y = o + D x and the
+// gated value y silu(z), and leaves its sum of squares in LDS; each wave then
+// reduces (token, group) pairs, and the threads scale and store.
 template <bool BF16, int TR>
 __global__ __launch_bounds__(256) void mamba2_gate_norm(LayerArgs a) {
   using E = Elem<BF16>;
   using T = typename E::T;
   constexpr int VEC = 16 / sizeof(T);
-  constexpr int TOK = kNormTokens, SLOTS = TOK / TR;
+  constexpr int TOK = kNormTokens, SLOTS = TOK / TR, NR = TR + kHalo;
   __shared__ float part[TOK][256];
   __shared__ float rstd[TOK][256];
   const int b = blockIdx.y;
@@ -385,29 +422,58 @@ __global__ __launch_bounds__(256) void mamba2_gate_norm(LayerArgs a) {
   const bool active = tid < SLOTS * DG;
   const int GG = DG / a.G;   // granules per norm group
   const int lane = tid & 63, w = tid >> 6;
-
-  float gz[TR][VEC];
   const int64_t ts = t0 + (int64_t)s * TR;
   const int n = active ? (int)max((int64_t)0, min((int64_t)TR, a.T - ts)) : 0;
+  const int c0 = g * VEC, h = c0 / a.P;
+
+  // this thread's inputs, all loads issued before any use: the conv window
+  // (rows ts - kHalo .. ts + TR - 1, zero before the first token), z and o
+  uint4 xr[NR], zr[TR], orr[TR];
+  const T* oh = static_cast<const T*>(a.o) + (((size_t)b * a.H + h) * a.T) * a.P + c0 % a.P;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int64_t t = ts - kHalo + r;
+    xr[r] = make_uint4(0, 0, 0, 0);
+    if (n > 0 && t >= 0 && t < ts + n) xr[r] = *reinterpret_cast<const uint4*>(zx + t * a.ld_zx + a.col_x + c0);
+  }
+#pragma unroll
+  for (int i = 0; i < TR; ++i) {
+    zr[i] = make_uint4(0, 0, 0, 0);
+    orr[i] = make_uint4(0, 0, 0, 0);
+    if (i < n) {
+      zr[i] = *reinterpret_cast<const uint4*>(zx + (ts + i) * a.ld_zx + c0);
+      orr[i] = *reinterpret_cast<const uint4*>(oh + (ts + i) * a.P);
+    }
+  }
+  float wt[VEC][kMaxConvTaps], bias[VEC];
+  load_taps<VEC>(a.taps, c0, wt, bias);
+
+  float gz[TR][VEC];
   if (n > 0) {
-    const int c0 = g * VEC, h = c0 / a.P, p0 = c0 % a.P;
     const float Dh = a.D[h];
-    const T* oh = static_cast<const T*>(a.o) + (((size_t)b * a.H + h) * a.T) * a.P + p0;
-    conv_run<BF16, VEC, TR>(zx + a.col_x + c0, a.ld_zx, c0, a.conv_w, a.conv_b, a.K, ts, n,
-                            [&](int i, float (&x)[VEC]) {
-      const int64_t t = ts + i;
-      float o[VEC], z[VEC];
-      load_vec<BF16, VEC>(oh + t * a.P, o);
-      load_vec<BF16, VEC>(zx + t * a.ld_zx + c0, z);
+#pragma unroll
+    for (int i = 0; i < TR; ++i) {
+      float x[VEC], o[VEC], z[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) x[e] = bias[e];
+#pragma unroll
+      for (int j = 0; j < kMaxConvTaps; ++j) {
+        float xv[VEC];
+        unpack<BF16, VEC>(xr[i + j], xv);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[e] = fmaf(wt[e][j], xv[e], x[e]);
+      }
+      unpack<BF16, VEC>(orr[i], o);
+      unpack<BF16, VEC>(zr[i], z);
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const float v = (o[e] + Dh * x[e]) * silu_f(z[e]);
+        const float v = (o[e] + Dh * silu_f(x[e])) * silu_f(z[e]);
         ss = fmaf(v, v, ss);
         gz[i][e] = v;
       }
-      part[s * TR + i][g] = ss;
-    });
+      if (i < n) part[s * TR + i][g] = ss;
+    }
   }
   __syncthreads();
   const float inv = 1.f / (float)(a.d_inner / a.G);
@@ -421,7 +487,7 @@ __global__ __launch_bounds__(256) void mamba2_gate_norm(LayerArgs a) {
   }
   __syncthreads();
   if (n > 0) {
-    const int c0 = g * VEC, gi = g / GG;
+    const int gi = g / GG;
     float nw[VEC];
     load_vec<BF16, VEC>(static_cast<const T*>(a.norm_w) + c0, nw);
     T* yrow = static_cast<T*>(a.y) + ((size_t)b * a.T) * a.d_inner + c0;
@@ -457,8 +523,10 @@ int launch_layer_pre(const LayerPlan& p, const void* u, const void* in_proj, con
   int rc = launch_gemm<BF16>(u, in_proj, const_cast<void*>(a.zx), (int)p.M, p.d_in_proj, p.d_model, p.d_model,
                              p.d_model, p.ld_zx, s);
   if (rc != kOK) return rc;
-  const dim3 grid((unsigned)((p.T + kPrologueTokens - 1) / kPrologueTokens), (unsigned)p.B);
-  hipLaunchKernelGGL((mamba2_prologue<BF16>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((mamba2_taps<BF16>), dim3((unsigned)((p.conv_dim + 255) / 256)), dim3(256), 0, s, a);
+  const int n_slabs = (p.conv_dim / p.vec + kSlabGranules - 1) / kSlabGranules;
+  const dim3 grid((unsigned)((p.T + kPrologueTokens - 1) / kPrologueTokens), (unsigned)p.B, (unsigned)(n_slabs + 1));
+  hipLaunchKernelGGL((mamba2_prologue<BF16>), grid, dim3(256), 0, s, a, n_slabs);
   return hipGetLastError() == hipSuccess ? kOK : kEHIP;
 }
 
@@ -466,14 +534,15 @@ int launch_layer_pre(const LayerPlan& p, const void* u, const void* in_proj, con
 template <bool BF16>
 int launch_layer_post(const LayerPlan& p, const void* out_proj, void* out, const LayerArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((p.T + kNormTokens - 1) / kNormTokens), (unsigned)p.B);
+#define LA_GN(TR)                                                          \
+  case TR:                                                                 \
+    hipLaunchKernelGGL((mamba2_gate_norm<BF16, TR>), grid, dim3(256), 0, s, a); \
+    break;
   switch (kNormTokens / p.norm_slots) {
-    case 1: hipLaunchKernelGGL((mamba2_gate_norm<BF16, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((mamba2_gate_norm<BF16, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((mamba2_gate_norm<BF16, 4>), grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((mamba2_gate_norm<BF16, 8>), grid, dim3(256), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((mamba2_gate_norm<BF16, 16>), grid, dim3(256), 0, s, a); break;
+    LA_GN(1) LA_GN(2) LA_GN(4) LA_GN(8) LA_GN(16)
     default: return kESHAPE;
   }
+#undef LA_GN
   if (hipGetLastError() != hipSuccess) return kEHIP;
   return launch_gemm<BF16>(a.y, out_proj, out, (int)p.M, p.d_model, p.d_inner, p.d_inner, p.d_inner, p.d_model, s);
 }

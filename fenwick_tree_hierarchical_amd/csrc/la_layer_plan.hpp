@@ -31,6 +31,7 @@ struct LayerPlan {
   // column offsets inside one row of the input projection
   int col_z = 0, col_x = 0, col_b = 0, col_c = 0, col_dt = 0, col_lam = 0;
   size_t off_zx = 0, off_q = 0, off_k = 0, off_v = 0, off_loga = 0, off_lam = 0, off_o = 0, off_opws = 0;
+  size_t off_taps = 0;  // the conv taps and bias as fp32, [conv_dim][kMaxConvTaps + 1]
   size_t off_y = 0;     // the normalised gated output, over q (dead by then)
   size_t ws_bytes = 0;
   FwdPlan op;           // the operator's plan
@@ -89,6 +90,7 @@ inline int plan_layer(int B, int64_t T, int d_model, int H, int P, int N, int G,
   p.off_lam = off;  off = align_up(off + BHT * L * 4, 256);
   p.off_o = off;    off = align_up(off + BHT * P * p.es, 256);
   p.off_opws = off; off = align_up(off + p.op.ws_bytes, 256);
+  p.off_taps = off; off = align_up(off + (size_t)p.conv_dim * (kMaxConvTaps + 1) * 4, 256);
   p.off_y = p.off_q;   // M * d_inner == B H T N because P == N
   p.ws_bytes = off;
   *out = p;
