@@ -505,6 +505,58 @@ def bench_gdn(la, torch, dev, w, reps=10, warmup=5):
                                     f"log_a, beta, lambda (fp32)"}
 
 
+def layer_counts(lw):
+    """Algorithmic work of one Log-Linear Mamba-2 layer forward: the two
+    projections (2 M K N each), the conv (2 K flops per channel and token) and
+    the operator's products (algorithmic_counts); essential bytes: the input
+    and output activations and the weights, each once."""
+    M = lw.B * lw.T
+    gemm = 2 * M * lw.d_model * lw.d_in_proj + 2 * M * lw.d_inner * lw.d_model
+    conv = 2 * lw.K * M * lw.conv_dim
+    op = algorithmic_counts(None, lw.B, lw.H, lw.T, lw.N, lw.C, lw.L, 2, G=8 if lw.N <= 64 else 4)["flops"]
+    es = 2 if lw.dtype == "bf16" else 4
+    weights = (lw.d_in_proj * lw.d_model + lw.conv_dim * (lw.K + 1) + lw.d_inner + lw.d_model * lw.d_inner) * es \
+        + (3 * lw.H + lw.H * lw.L) * 4
+    return {"flops": gemm + conv + op, "split_tflop": {"projections": gemm / 1e12, "conv": conv / 1e12,
+                                                       "operator": op / 1e12},
+            "essential_bytes": 2 * M * lw.d_model * es + weights}
+
+
+def bench_layer(la, torch, dev, lw, reps=10, warmup=5):
+    """The Log-Linear Mamba-2 layer forward (loglinear_mamba2_fwd: projections,
+    conv and gates, the operator, gate and norm) on its training shape; HIP
+    events on the launch stream around each call."""
+    from fenwick_tree_hierarchical_amd.workloads import make_layer
+    w = {k: v.to(dev) for k, v in make_layer(lw).items()}
+    out = torch.empty_like(w["u"])
+    nws = la.loglinear_mamba2_fwd_workspace(lw.B, lw.T, lw.d_model, lw.H, lw.P, lw.N, lw.G, lw.K, lw.C, lw.L,
+                                            lw.eps, w["u"].dtype)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+    def call():
+        la.loglinear_mamba2_fwd(w["u"], w, lw.H, lw.P, lw.N, lw.G, C=lw.C, eps=lw.eps, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(s)
+    for i in range(reps):
+        call()
+        ev[i + 1].record(s)
+    torch.cuda.synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    mean = sum(ms) / reps
+    cnt = layer_counts(lw)
+    tf = cnt["flops"] / (mean * 1e-3) / 1e12
+    return {"workload": lw.name, "B": lw.B, "T": lw.T, "d_model": lw.d_model, "H": lw.H, "P": lw.P, "N": lw.N,
+            "G": lw.G, "K": lw.K, "chunk": lw.C, "reps": reps, "ms": mean, "median_ms": sorted(ms)[reps // 2],
+            "min_ms": min(ms), "tokens_per_s": lw.B * lw.T / (mean * 1e-3), "workspace_bytes": nws,
+            "alg_tflop": cnt["flops"] / 1e12, "split_tflop": cnt["split_tflop"], "achieved_tflops": tf,
+            "frac_of_bf16_peak": tf / BF16_MFMA_PEAK_TFLOPS, "essential_bytes": cnt["essential_bytes"]}
+
+
 def bench_config(la, torch, dev, w, steps=20, warmup=10):
     """One forward workload (not the metric's): wall time per forward over
     `steps` calls after `warmup`, then the kernels' durations from HIP events
@@ -693,6 +745,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-gdn", action="store_true")
     ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pmc-summary", default=None)
     ap.add_argument("--pmc-profile", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None)
@@ -759,6 +812,11 @@ def main():
     if not args.no_gdn:
         log("bench: gated deltanet forward")
         secondary["gdn"] = bench_gdn(la, torch, dev, w)
+    if not args.no_layer:
+        from fenwick_tree_hierarchical_amd.workloads import LAYER_WORKLOADS
+        log("bench: log-linear mamba-2 layer")
+        secondary["layer"] = bench_layer(la, torch, dev, LAYER_WORKLOADS["layer_train_16k_bf16"])
+        torch.cuda.empty_cache()
     if not args.no_decode:
         log("bench: decode 256 steps")
         secondary["decode"] = bench_decode(la, torch, dev)
@@ -836,7 +894,7 @@ def main():
     result.update(secondary)
     if "backward" in result:
         result["backward"]["ratio_to_forward"] = result["backward"]["ms"] / ms_per_step
-    result["order"] = ("the other legs (configs, backward, gdn, decode) ran before the warm-up and the "
+    result["order"] = ("the other legs (configs, backward, gdn, layer, decode) ran before the warm-up and the "
                        "timed steps; the CPU baseline after them")
     if not args.no_cpu:
         log(f"bench: oracle CPU baseline on {host_cores()} host cores")
