@@ -798,9 +798,16 @@ def main():
         if copy_dst is not None:
             copy_dst.copy_(copy_src)
 
-    # the other GPU legs first, so that the timed forward steps below run on a
-    # GPU that has been busy (clocks up)
+    # the other GPU legs first, the light decode legs early and the heavy ones
+    # last, so that the timed forward steps below run on a GPU that has just
+    # been under full load (after a run of light kernels the clocks take a few
+    # dozen forwards to come back up)
     secondary = {}
+    if not args.no_decode:
+        log("bench: decode 256 steps")
+        secondary["decode"] = bench_decode(la, torch, dev)
+        log("bench: decode at batch 256")
+        secondary["decode"]["batch_256"] = bench_decode_large(la, torch, dev)
     if not args.no_configs:
         secondary["configs"] = {}
         for name in ("tiny_f32", "small_bf16", "long_128k_bf16"):
@@ -816,12 +823,6 @@ def main():
         from fenwick_tree_hierarchical_amd.workloads import LAYER_WORKLOADS
         log("bench: log-linear mamba-2 layer")
         secondary["layer"] = bench_layer(la, torch, dev, LAYER_WORKLOADS["layer_train_16k_bf16"])
-        torch.cuda.empty_cache()
-    if not args.no_decode:
-        log("bench: decode 256 steps")
-        secondary["decode"] = bench_decode(la, torch, dev)
-        log("bench: decode at batch 256")
-        secondary["decode"]["batch_256"] = bench_decode_large(la, torch, dev)
     torch.cuda.empty_cache()
 
     log(f"bench: warm-up {args.warmup}")
@@ -894,7 +895,7 @@ def main():
     result.update(secondary)
     if "backward" in result:
         result["backward"]["ratio_to_forward"] = result["backward"]["ms"] / ms_per_step
-    result["order"] = ("the other legs (configs, backward, gdn, layer, decode) ran before the warm-up and the "
+    result["order"] = ("the other legs (decode, configs, backward, gdn, layer) ran before the warm-up and the "
                        "timed steps; the CPU baseline after them")
     if not args.no_cpu:
         log(f"bench: oracle CPU baseline on {host_cores()} host cores")

@@ -292,58 +292,69 @@ __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
   const bool writer = blk == 0 && threadIdx.x == 0;
   const ftv* gs = reinterpret_cast<const ftv*>(a.gstate + bh * ng * DD);
   E* nd = reinterpret_cast<E*>(a.nodes) + bh * ng * DD;
-  constexpr int kBatch = 8;   // independent loads issued together, then walked
-  for (int64_t e0 = 0; e0 < nfg; e0 += kBatch) {
-    ftv Av[kBatch];
-    float gv[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int64_t e = e0 + u;
-      Av[u] = ftv(0.f);
-      gv[u] = 0.f;
-      if (e < nfg) {
-        gv[u] = a.gtot[bh * ng + e];
-        if (valid) Av[u] = gs[e * NQ + q4];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int64_t e = e0 + u;
-      if (e >= nfg) continue;   // (predicated, so the walk unrolls with constant indices)
-      if (writer) a.gprefix[bh * (ng + 1) + e] = pre;
-      const float g = gv[u];
-      const float eg = __builtin_amdgcn_exp2f(g);   // one exponential per group, shared by the slots
-      // trailing ones of e: e0 is a multiple of kBatch, so for u < kBatch - 1
-      // they are those of u, a constant of the unrolled loop (the slot
-      // updates below then resolve at compile time); the last group of a
-      // batch continues into the bits of e0 / kBatch
-      const int kk = (u < kBatch - 1) ? __builtin_ctz(~(unsigned)u)
-                                      : cilog2(kBatch) + __builtin_ctzll(~(unsigned long long)(e0 / kBatch));
-      ftv nw = Av[u];
-#pragma unroll
-      for (int j = 0; j < MAXJ; ++j) {
-        fac[j] *= eg;
-        if (j < kk) {
-#pragma unroll
-          for (int i = 0; i < V; ++i) nw[i] = fmaf(fac[j], slot[j][i], nw[i]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < MAXJ; ++j)
-        if (j == kk) { slot[j] = nw; fac[j] = 1.f; }
-      if (valid) {
-        if constexpr (BF16) {
-          utv o;
-#pragma unroll
-          for (int i = 0; i < V; ++i) o[i] = EL::from_f32(nw[i]);
-          *reinterpret_cast<utv*>(nd + e * DD + V * q4) = o;
-        } else {
-          *reinterpret_cast<ftv*>(nd + e * DD + V * q4) = nw;
-        }
-      }
-      pre += (double)g;
-    }
+  // groups are walked in batches of kBatch; the loads of the next batch are
+  // issued before the current one is walked (two register buffers, the batch
+  // loop unrolled by two so that both buffers keep constant indices; macros
+  // rather than lambdas, which would send the arrays to scratch memory)
+  constexpr int kBatch = 8;
+  ftv A0[kBatch], A1[kBatch];
+  float g0[kBatch], g1[kBatch];
+#define LA_TREE_LOAD(E0, Av, gv)                          \
+  do {                                                    \
+    _Pragma("unroll") for (int u = 0; u < kBatch; ++u) {  \
+      const int64_t e = (E0) + u;                         \
+      Av[u] = ftv(0.f);                                   \
+      gv[u] = 0.f;                                        \
+      if (e < nfg) {                                      \
+        gv[u] = a.gtot[bh * ng + e];                      \
+        if (valid) Av[u] = gs[e * NQ + q4];               \
+      }                                                   \
+    }                                                     \
+  } while (0)
+  // node[e] = A_e + sum over the k = trailing-ones(e) lower slots, decayed
+  // to e; e0 is a multiple of kBatch, so for u < kBatch - 1 the trailing ones
+  // are those of u (a constant of the unrolled loop: the slot updates resolve
+  // at compile time); the last group of a batch continues into e0 / kBatch
+#define LA_TREE_WALK(E0, Av, gv)                                                                         \
+  do {                                                                                                   \
+    _Pragma("unroll") for (int u = 0; u < kBatch; ++u) {                                                 \
+      const int64_t e = (E0) + u;                                                                        \
+      if (e >= nfg) continue;                                                                            \
+      if (writer) a.gprefix[bh * (ng + 1) + e] = pre;                                                    \
+      const float g = gv[u];                                                                             \
+      const float eg = __builtin_amdgcn_exp2f(g);                                                        \
+      const int kk = (u < kBatch - 1) ? __builtin_ctz(~(unsigned)u)                                      \
+                                      : cilog2(kBatch) + __builtin_ctzll(~(unsigned long long)((E0) / kBatch)); \
+      ftv nw = Av[u];                                                                                    \
+      _Pragma("unroll") for (int j = 0; j < MAXJ; ++j) {                                                 \
+        fac[j] *= eg;                                                                                    \
+        if (j < kk) {                                                                                    \
+          _Pragma("unroll") for (int i = 0; i < V; ++i) nw[i] = fmaf(fac[j], slot[j][i], nw[i]);        \
+        }                                                                                                \
+      }                                                                                                  \
+      _Pragma("unroll") for (int j = 0; j < MAXJ; ++j) if (j == kk) { slot[j] = nw; fac[j] = 1.f; }    \
+      if (valid) {                                                                                       \
+        if constexpr (BF16) {                                                                            \
+          utv o;                                                                                         \
+          _Pragma("unroll") for (int i = 0; i < V; ++i) o[i] = EL::from_f32(nw[i]);                      \
+          *reinterpret_cast<utv*>(nd + e * DD + V * q4) = o;                                             \
+        } else {                                                                                         \
+          *reinterpret_cast<ftv*>(nd + e * DD + V * q4) = nw;                                            \
+        }                                                                                                \
+      }                                                                                                  \
+      pre += (double)g;                                                                                  \
+    }                                                                                                    \
+  } while (0)
+  if (nfg > 0) LA_TREE_LOAD(0, A0, g0);
+  for (int64_t e0 = 0; e0 < nfg; e0 += 2 * kBatch) {
+    if (e0 + kBatch < nfg) LA_TREE_LOAD(e0 + kBatch, A1, g1);
+    LA_TREE_WALK(e0, A0, g0);
+    if (e0 + kBatch >= nfg) break;
+    if (e0 + 2 * kBatch < nfg) LA_TREE_LOAD(e0 + 2 * kBatch, A0, g0);
+    LA_TREE_WALK(e0 + kBatch, A1, g1);
   }
+#undef LA_TREE_LOAD
+#undef LA_TREE_WALK
   if (writer) a.gprefix[bh * (ng + 1) + nfg] = pre;
 }
 
