@@ -684,9 +684,9 @@ def pmc_profile(fetch_dir: str, write_dir: str, out_path: str):
            "per_launch_kib": per_kib, "per_kernel_traffic_bytes": traffic,
            "commands": [
                f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/{fetch_dir} "
-               "-o fetch -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-decode --no-backward --no-gdn --no-configs --copy-calibration",
+               "-o fetch -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-decode --no-backward --no-gdn --no-configs --no-layer --copy-calibration",
                f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/{write_dir} "
-               "-o write -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-decode --no-backward --no-gdn --no-configs --copy-calibration",
+               "-o write -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-decode --no-backward --no-gdn --no-configs --no-layer --copy-calibration",
                f"python bench.py --pmc-profile {fetch_dir} {write_dir}"]}
     with open(out_path, "w") as f:
         json.dump(res, f, indent=1)
