@@ -798,21 +798,16 @@ def main():
         if copy_dst is not None:
             copy_dst.copy_(copy_src)
 
-    # the other GPU legs first, the light decode legs early and the heavy ones
-    # last, so that the timed forward steps below run on a GPU that has just
-    # been under full load (after a run of light kernels the clocks take a few
-    # dozen forwards to come back up)
+    # the other GPU legs first: the light decode legs early, the other forward
+    # shapes last, so that the timed forward steps below follow forwards (each
+    # kind of load brings its own clock transient over the first dozens of
+    # launches; after forwards of the other shapes the 16K forward starts settled)
     secondary = {}
     if not args.no_decode:
         log("bench: decode 256 steps")
         secondary["decode"] = bench_decode(la, torch, dev)
         log("bench: decode at batch 256")
         secondary["decode"]["batch_256"] = bench_decode_large(la, torch, dev)
-    if not args.no_configs:
-        secondary["configs"] = {}
-        for name in ("tiny_f32", "small_bf16", "long_128k_bf16"):
-            log(f"bench: forward at {name}")
-            secondary["configs"][name] = bench_config(la, torch, dev, WORKLOADS[name])
     if not args.no_backward:
         log("bench: backward")
         secondary["backward"] = bench_backward(la, torch, dev, w, x)
@@ -823,6 +818,12 @@ def main():
         from fenwick_tree_hierarchical_amd.workloads import LAYER_WORKLOADS
         log("bench: log-linear mamba-2 layer")
         secondary["layer"] = bench_layer(la, torch, dev, LAYER_WORKLOADS["layer_train_16k_bf16"])
+        torch.cuda.empty_cache()
+    if not args.no_configs:
+        secondary["configs"] = {}
+        for name in ("tiny_f32", "small_bf16", "long_128k_bf16"):
+            log(f"bench: forward at {name}")
+            secondary["configs"][name] = bench_config(la, torch, dev, WORKLOADS[name])
     torch.cuda.empty_cache()
 
     log(f"bench: warm-up {args.warmup}")
@@ -895,7 +896,7 @@ def main():
     result.update(secondary)
     if "backward" in result:
         result["backward"]["ratio_to_forward"] = result["backward"]["ms"] / ms_per_step
-    result["order"] = ("the other legs (decode, configs, backward, gdn, layer) ran before the warm-up and the "
+    result["order"] = ("the other legs (decode, backward, gdn, layer, configs) ran before the warm-up and the "
                        "timed steps; the CPU baseline after them")
     if not args.no_cpu:
         log(f"bench: oracle CPU baseline on {host_cores()} host cores")
