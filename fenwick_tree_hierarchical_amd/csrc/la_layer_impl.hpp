@@ -30,29 +30,44 @@ struct GemmArgs {
   const void* A;   // [M][lda], rows 16-byte aligned
   const void* B;   // [N][ldb]
   void* C;         // [M][ldc]
-  int M, N, K, lda, ldb, ldc;   // K a multiple of the K-slice; ldc a multiple of 4
-  int tiles_n;
+  int M, N, K, lda, ldb, ldc;   // K a multiple of two K-slices; ldc a multiple of 4
+  int tiles_n, tiles;           // column tiles, all tiles
 };
 
-constexpr int kGemmStageBytes = 2 * kGemmTile * kGemmKBytes;   // A and B slices of one stage
-constexpr int kGemmLds = 2 * kGemmStageBytes;                    // double buffer
+constexpr int kGemmTM = kGemmTile;                               // rows of a workgroup tile
+constexpr int kGemmTN = kGemmTile;                               // columns of a workgroup tile
+constexpr int kGemmStageBytes = (kGemmTM + kGemmTN) * kGemmKBytes; // A and B slices of one stage
+// LDS of a workgroup: the double buffer, which the epilogue reuses to stage
+// one 32-row block of every wave's results (rows padded by 8 bytes; fp32
+// blocks are larger than the buffers)
+constexpr int kGemmStage32 = 4 * 32 * (128 * 4 + 8);
+constexpr int kGemmLds = 2 * kGemmStageBytes > kGemmStage32 ? 2 * kGemmStageBytes : kGemmStage32;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // C[m][n] = sum_k A[m][k] B[n][k], fp32 accumulation, rounded to the element
-// type.  A workgroup of four waves computes a 128 x 128 tile, each wave a
-// 64 x 64 quarter as 4 x 4 matrix-core tiles.  K-slices (128 bytes of every
-// row of the A and B tiles) are double-buffered in LDS: the next slice is
-// loaded into registers while the current one is multiplied, then written
-// to the other buffer.  A slice row's eight 16-byte granules are stored
-// XOR-swizzled by the row's low three bits (granule g of row r at slot
-// g ^ (r & 7)), so the 16 rows one fragment read touches fall in distinct
-// banks.  Rows past M or N are clamped to the last row for loading and never
-// stored.
+// type.  A workgroup of four waves computes a 256 x 256 tile, each wave a
+// 128 x 128 quarter as 4 x 4 tiles of 32 x 32 on the matrix cores
+// (v_mfma_f32_32x32x16_bf16; fp32: v_mfma_f32_32x32x2f32, four k-steps per
+// 16-byte granule, element c of every lane's granule feeding step c), its 256
+// accumulators per lane in the accumulation registers, one wave per SIMD.
+// The large wave tile keeps the LDS traffic per multiply-add low enough for
+// the matrix cores: 512 bytes of fragments per k for 16384 MACs (a 64 x 64
+// tile needs twice that per MAC, which the LDS cannot feed).  K-slices
+// (kGemmKBytes bytes of every row of the A and B tiles) are double-buffered in
+// LDS and run two slices ahead in registers: slice kt + 2 is loaded while
+// slice kt is multiplied and slice kt + 1, loaded one step earlier, waits to be
+// written to the free buffer.  A slice row's four 16-byte granules are stored
+// XOR-swizzled (granule g of row r at slot g ^ ((r >> 2) & 3)), so the eight
+// rows one LDS cycle of a fragment read serves fall in distinct banks.  Rows
+// past M or N are clamped to the last row for loading and never stored.
 template <bool BF16>
-__global__ __launch_bounds__(256, 2) void gemm_nt(GemmArgs g) {
+__global__ __launch_bounds__(256, 1) void gemm_nt(GemmArgs g) {
   using E = Elem<BF16>;
   using T = typename E::T;
   constexpr int ES = sizeof(T);
-  constexpr int TILE = kGemmTile, ROWB = kGemmKBytes;
+  constexpr int TM = kGemmTM, TN = kGemmTN, ROWB = kGemmKBytes, GPR = ROWB / 16;
+  static_assert(GPR == 4 && TM == 256 && TN == 256, "256 x 256 tiles of four-granule slice rows");
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
@@ -62,127 +77,188 @@ __global__ __launch_bounds__(256, 2) void gemm_nt(GemmArgs g) {
   const int nblk = gridDim.x, per = nblk / 8;
   int blk = blockIdx.x;
   if (blk < per * 8) blk = (blk % 8) * per + blk / 8;
-  const int tm = blk / g.tiles_n, tn = blk % g.tiles_n;
-  const int m0 = tm * TILE, n0 = tn * TILE;
+  const int m0 = (blk / g.tiles_n) * TM, n0 = (blk % g.tiles_n) * TN;
 
-  // loads: thread t moves granule t % 8 of rows t / 8 + 32 j (j = 0..3) of
-  // both tiles; eight consecutive threads cover one 128-byte row
-  const int lrow = tid >> 3, lgr = tid & 7;
+  // loads: thread t moves granule t % 4 of rows t / 4 + 64 j (j < 4) of both
+  // tiles; four consecutive threads cover one 64-byte slice row
+  const int lrow = tid >> 2, lgr = tid & 3;
   const unsigned char* pa[4];
   const unsigned char* pb[4];
   int sw[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int r = lrow + 32 * j;
-    const int ra = min(m0 + r, g.M - 1), rb = min(n0 + r, g.N - 1);
-    pa[j] = static_cast<const unsigned char*>(g.A) + (size_t)ra * g.lda * ES + lgr * 16;
-    pb[j] = static_cast<const unsigned char*>(g.B) + (size_t)rb * g.ldb * ES + lgr * 16;
-    sw[j] = r * ROWB + ((lgr ^ (r & 7)) << 4);
+    const int r = lrow + 64 * j;
+    pa[j] = static_cast<const unsigned char*>(g.A) + (size_t)min(m0 + r, g.M - 1) * g.lda * ES + lgr * 16;
+    pb[j] = static_cast<const unsigned char*>(g.B) + (size_t)min(n0 + r, g.N - 1) * g.ldb * ES + lgr * 16;
+    sw[j] = r * ROWB + ((lgr ^ ((r >> 2) & 3)) << 4);
   }
-  const int nk = g.K * ES / ROWB;
-  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-#define LA_GEMM_GLOAD(kt)                                                   \
+  const int nk = g.K * ES / ROWB;   // even
+  // four register sets of eight granules, named (an array here would live in
+  // scratch memory: it is promoted to registers before the loops unroll)
+  uint4 a0, a1, a2, a3, a4, a5, a6, a7, b0, b1, b2, b3, b4, b5, b6, b7;
+  uint4 c0, c1, c2, c3, c4, c5, c6, c7, d0, d1, d2, d3, d4, d5, d6, d7;
+#define LA_GEMM_GLOAD(x0, x1, x2, x3, y0, y1, y2, y3, kt)                  \
   do {                                                                      \
-    const size_t ko = (size_t)(kt) * ROWB;                                  \
-    ra0 = *reinterpret_cast<const uint4*>(pa[0] + ko);                      \
-    ra1 = *reinterpret_cast<const uint4*>(pa[1] + ko);                      \
-    ra2 = *reinterpret_cast<const uint4*>(pa[2] + ko);                      \
-    ra3 = *reinterpret_cast<const uint4*>(pa[3] + ko);                      \
-    rb0 = *reinterpret_cast<const uint4*>(pb[0] + ko);                      \
-    rb1 = *reinterpret_cast<const uint4*>(pb[1] + ko);                      \
-    rb2 = *reinterpret_cast<const uint4*>(pb[2] + ko);                      \
-    rb3 = *reinterpret_cast<const uint4*>(pb[3] + ko);                      \
+    const size_t ko = (size_t)min(kt, nk - 1) * ROWB;                       \
+    x0 = *reinterpret_cast<const uint4*>(pa[0] + ko);                       \
+    x1 = *reinterpret_cast<const uint4*>(pa[1] + ko);                       \
+    x2 = *reinterpret_cast<const uint4*>(pa[2] + ko);                       \
+    x3 = *reinterpret_cast<const uint4*>(pa[3] + ko);                       \
+    y0 = *reinterpret_cast<const uint4*>(pb[0] + ko);                       \
+    y1 = *reinterpret_cast<const uint4*>(pb[1] + ko);                       \
+    y2 = *reinterpret_cast<const uint4*>(pb[2] + ko);                       \
+    y3 = *reinterpret_cast<const uint4*>(pb[3] + ko);                       \
   } while (0)
-#define LA_GEMM_SWRITE(buf)                                                 \
+#define LA_GEMM_SWRITE(x0, x1, x2, x3, y0, y1, y2, y3, buf)                 \
   do {                                                                      \
     unsigned char* base = smem + (buf) * kGemmStageBytes;                   \
-    *reinterpret_cast<uint4*>(base + sw[0]) = ra0;                          \
-    *reinterpret_cast<uint4*>(base + sw[1]) = ra1;                          \
-    *reinterpret_cast<uint4*>(base + sw[2]) = ra2;                          \
-    *reinterpret_cast<uint4*>(base + sw[3]) = ra3;                          \
-    *reinterpret_cast<uint4*>(base + TILE * ROWB + sw[0]) = rb0;            \
-    *reinterpret_cast<uint4*>(base + TILE * ROWB + sw[1]) = rb1;            \
-    *reinterpret_cast<uint4*>(base + TILE * ROWB + sw[2]) = rb2;            \
-    *reinterpret_cast<uint4*>(base + TILE * ROWB + sw[3]) = rb3;            \
+    *reinterpret_cast<uint4*>(base + sw[0]) = x0;                           \
+    *reinterpret_cast<uint4*>(base + sw[1]) = x1;                           \
+    *reinterpret_cast<uint4*>(base + sw[2]) = x2;                           \
+    *reinterpret_cast<uint4*>(base + sw[3]) = x3;                           \
+    *reinterpret_cast<uint4*>(base + TM * ROWB + sw[0]) = y0;               \
+    *reinterpret_cast<uint4*>(base + TM * ROWB + sw[1]) = y1;               \
+    *reinterpret_cast<uint4*>(base + TM * ROWB + sw[2]) = y2;               \
+    *reinterpret_cast<uint4*>(base + TM * ROWB + sw[3]) = y3;               \
   } while (0)
 
-  const int wm = w >> 1, wn = w & 1, fr = lane & 15, fq = lane >> 4;
-  f32x4 acc[4][4];
+  const int wm = w >> 1, wn = w & 1, fr = lane & 31, fq = lane >> 5;
+  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  LA_GEMM_GLOAD(0);
-  LA_GEMM_SWRITE(0);
+  // the products of the slice in LDS buffer `buf`; B is the first operand, so
+  // lane l then holds, for element e, C row 32 i + l % 32 at column
+  // 32 j + 8 (e / 4) + 4 (l / 32) + e % 4
+#define LA_GEMM_FRAGS(af, bf, As, Bs, ks)                                                                  \
+  do {                                                                                                     \
+    const int slot = ((2 * (ks) + fq) ^ ((fr >> 2) & 3)) << 4;                                             \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                          \
+      af[i] = *reinterpret_cast<const uint4*>(As + (wm * 128 + 32 * i + fr) * ROWB + slot);                \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                          \
+      bf[j] = *reinterpret_cast<const uint4*>(Bs + (wn * 128 + 32 * j + fr) * ROWB + slot);                \
+  } while (0)
+#define LA_GEMM_STEP(af, bf)                                                                               \
+  do {                                                                                                     \
+    if constexpr (BF16) {                                                                                  \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                        \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                      \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bf[j]),           \
+                                                              __builtin_bit_cast(bf16x8, af[i]),           \
+                                                              acc[i][j], 0, 0, 0);                         \
+    } else {                                                                                               \
+      _Pragma("unroll") for (int c = 0; c < 4; ++c)                                                        \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                      \
+          _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                    \
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, (&bf[j].x)[c]),     \
+                                                             __builtin_bit_cast(float, (&af[i].x)[c]),     \
+                                                             acc[i][j], 0, 0, 0);                          \
+    }                                                                                                      \
+  } while (0)
+  // the two k-steps of the slice in LDS buffer `buf`: the second step's
+  // fragments are read while the first step's products run
+#define LA_GEMM_MMA(buf)                                                                                   \
+  do {                                                                                                     \
+    const unsigned char* As = smem + (buf) * kGemmStageBytes;                                              \
+    const unsigned char* Bs = As + TM * ROWB;                                                              \
+    uint4 af0[4], bf0[4], af1[4], bf1[4];                                                                  \
+    LA_GEMM_FRAGS(af0, bf0, As, Bs, 0);                                                                    \
+    LA_GEMM_FRAGS(af1, bf1, As, Bs, 1);                                                                    \
+    LA_GEMM_STEP(af0, bf0);                                                                                \
+    LA_GEMM_STEP(af1, bf1);                                                                                \
+  } while (0)
+
+  // Slice s is in register set s % 4 from four slices before it is
+  // multiplied; it is written to LDS buffer s % 2 at the end of step s - 1,
+  // multiplied in step s, and its register set then takes slice s + 4.  Every
+  // buffer written was last read before the preceding barrier.  Loads past the
+  // last slice fetch the last one again; their products are skipped.
+#define LA_GEMM_HALF(S, X, Y)                                                                  \
+  do {                                                                                         \
+    LA_GEMM_GLOAD(X##0, X##1, X##2, X##3, X##4, X##5, X##6, X##7, (S) + 4);                    \
+    __builtin_amdgcn_sched_barrier(0);   /* keep the loads ahead of the products */            \
+    if ((S) < nk) LA_GEMM_MMA((S) & 1);                                                        \
+    LA_GEMM_SWRITE(Y##0, Y##1, Y##2, Y##3, Y##4, Y##5, Y##6, Y##7, ((S) + 1) & 1);             \
+    __syncthreads();                                                                           \
+  } while (0)
+  LA_GEMM_GLOAD(a0, a1, a2, a3, a4, a5, a6, a7, 0);
+  LA_GEMM_GLOAD(b0, b1, b2, b3, b4, b5, b6, b7, 1);
+  LA_GEMM_GLOAD(c0, c1, c2, c3, c4, c5, c6, c7, 2);
+  LA_GEMM_GLOAD(d0, d1, d2, d3, d4, d5, d6, d7, 3);
+  LA_GEMM_SWRITE(a0, a1, a2, a3, a4, a5, a6, a7, 0);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    // the next slice (the last one again on the last step: loaded, never written)
-    LA_GEMM_GLOAD(min(kt + 1, nk - 1));
-    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the products
-    const unsigned char* As = smem + (kt & 1) * kGemmStageBytes;
-    const unsigned char* Bs = As + TILE * ROWB;
-#pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {
-      // granule 4 kg + fq of rows ... + fr; (row & 7) == (fr & 7) for every row read
-      const int slot = ((4 * kg + fq) ^ (fr & 7)) << 4;
-      uint4 af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(As + (wm * 64 + 16 * i + fr) * ROWB + slot);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const uint4*>(Bs + (wn * 64 + 16 * j + fr) * ROWB + slot);
-      // B as the first operand: lane l then holds C[row l % 16][4 (l / 16) + 0..3]
-      if constexpr (BF16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = E::mma(__builtin_bit_cast(bf16x8, bf[j]), __builtin_bit_cast(bf16x8, af[i]), acc[i][j]);
-      } else {
-        // fp32: a granule holds 4 consecutive k; k-step c takes element c of
-        // every lane's granule, so the four steps cover the 16 k of the group
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc[i][j] = E::mma(__builtin_bit_cast(float, (&bf[j].x)[c]), __builtin_bit_cast(float, (&af[i].x)[c]),
-                                 acc[i][j]);
-      }
-    }
-    // the other buffer was last read before the previous barrier (written
-    // on the last step too, unread, so that the loads above stay unconditional
-    // and are issued before the products)
-    LA_GEMM_SWRITE((kt + 1) & 1);
-    __syncthreads();
+  for (int kt = 0; kt < nk; kt += 4) {
+    LA_GEMM_HALF(kt, a, b);
+    LA_GEMM_HALF(kt + 1, b, c);
+    LA_GEMM_HALF(kt + 2, c, d);
+    LA_GEMM_HALF(kt + 3, d, a);
   }
+#undef LA_GEMM_HALF
 #undef LA_GEMM_GLOAD
 #undef LA_GEMM_SWRITE
+#undef LA_GEMM_MMA
+#undef LA_GEMM_FRAGS
+#undef LA_GEMM_STEP
 
-  // store: four consecutive columns per lane and tile
+  // store through LDS, so that every global store is a whole 256-byte row
+  // segment (a lane's own results are four columns of one row: stored
+  // directly, a row would take many partial-line writes): per block i of 32
+  // rows, each wave writes its 32 x 128 results to LDS (rows padded to an
+  // 8-byte offset mod 256, so the 32 rows of one store instruction hit
+  // distinct banks), then reads 16-byte pieces back along the rows
+  constexpr int SROW = 128 * ES + 8;                 // padded LDS row of a wave's block
+  unsigned char* st = smem + w * 32 * SROW;
+  const int lr = lane >> 4, lc = lane & 15;          // read-back: 4 rows x 16 pieces per instruction
+  constexpr int PPR = 128 * ES / 16;                 // 16-byte pieces per row of the block
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 64 + 16 * i + fr;
-    if (m >= g.M) continue;
-    T* crow = static_cast<T*>(g.C) + (size_t)m * g.ldc;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 64 + 16 * j + 4 * fq;
-      if (n + 3 < g.N) {
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int c = 32 * j + 8 * e4 + 4 * fq;
+        const float v0 = acc[i][j][4 * e4], v1 = acc[i][j][4 * e4 + 1], v2 = acc[i][j][4 * e4 + 2],
+                    v3 = acc[i][j][4 * e4 + 3];
         if constexpr (BF16) {
-          const unsigned lo = (unsigned)E::from_f32(acc[i][j][0]) | ((unsigned)E::from_f32(acc[i][j][1]) << 16);
-          const unsigned hi = (unsigned)E::from_f32(acc[i][j][2]) | ((unsigned)E::from_f32(acc[i][j][3]) << 16);
-          *reinterpret_cast<uint2*>(crow + n) = make_uint2(lo, hi);
+          const unsigned lo = (unsigned)E::from_f32(v0) | ((unsigned)E::from_f32(v1) << 16);
+          const unsigned hi = (unsigned)E::from_f32(v2) | ((unsigned)E::from_f32(v3) << 16);
+          *reinterpret_cast<uint2*>(st + fr * SROW + c * ES) = make_uint2(lo, hi);
         } else {
-          *reinterpret_cast<float4*>(crow + n) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+          *reinterpret_cast<float2*>(st + fr * SROW + c * ES) = make_float2(v0, v1);
+          *reinterpret_cast<float2*>(st + fr * SROW + c * ES + 8) = make_float2(v2, v3);
         }
-      } else {
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // this wave's LDS writes done (lgkmcnt 0)
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < g.N) crow[n + e] = E::from_f32(acc[i][j][e]);
+    for (int rr = 0; rr < 32; rr += 4) {
+      // lane 16 r' + p reads piece p (+ 16 per round) of row rr + r'
+      const int row = rr + lr;
+      const int m = m0 + wm * 128 + 32 * i + row;
+#pragma unroll
+      for (int p0 = 0; p0 < PPR; p0 += 16) {
+        const int p = p0 + lc;
+        const int n = n0 + wn * 128 + p * (16 / ES);
+        const uint4 v = *reinterpret_cast<const uint4*>(st + row * SROW + p * 16);
+        if (m < g.M) {
+          T* dst = static_cast<T*>(g.C) + (size_t)m * g.ldc + n;
+          if (n + 16 / ES <= g.N) {
+            *reinterpret_cast<uint4*>(dst) = v;
+          } else {
+            const T* vv = reinterpret_cast<const T*>(&v);
+#pragma unroll
+            for (int e = 0; e < 16 / ES; ++e)
+              if (n + e < g.N) dst[e] = vv[e];
+          }
+        }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // reads done before the next block overwrites
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -507,13 +583,15 @@ template <bool BF16>
 int launch_gemm(const void* A, const void* B, void* C, int M, int N, int K, int lda, int ldb, int ldc,
                 hipStream_t s) {
   if (M == 0 || N == 0) return kOK;
-  GemmArgs g{A, B, C, M, N, K, lda, ldb, ldc, (N + kGemmTile - 1) / kGemmTile};
-  const int64_t blocks = (int64_t)((M + kGemmTile - 1) / kGemmTile) * g.tiles_n;
-  if (blocks > 0x7fffffff) return kESHAPE;
+  const int64_t tiles_n = (N + kGemmTN - 1) / kGemmTN, tiles = (int64_t)((M + kGemmTM - 1) / kGemmTM) * tiles_n;
+  if (tiles > 0x7fffffff) return kESHAPE;
+  if ((int64_t)K * (BF16 ? 2 : 4) % (2 * kGemmKBytes) != 0) return kESHAPE;   // slices come in pairs
+  if (ldc % (16 / (BF16 ? 2 : 4)) != 0) return kESHAPE;                          // 16-byte row pieces
+  GemmArgs g{A, B, C, M, N, K, lda, ldb, ldc, (int)tiles_n, (int)tiles};
   const int lds = kGemmLds;
   if (hipFuncSetAttribute((const void*)gemm_nt<BF16>, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
     return kEHIP;
-  hipLaunchKernelGGL((gemm_nt<BF16>), dim3((unsigned)blocks), dim3(256), lds, s, g);
+  hipLaunchKernelGGL((gemm_nt<BF16>), dim3((unsigned)tiles), dim3(256), lds, s, g);
   return hipGetLastError() == hipSuccess ? kOK : kEHIP;
 }
 

@@ -14,8 +14,8 @@
 namespace la {
 
 // Kernel geometry shared by the planner and the kernels.
-constexpr int kGemmTile = 128;     // output tile of the projection GEMM (rows and columns)
-constexpr int kGemmKBytes = 128;   // bytes of one row of a K-slice of the GEMM
+constexpr int kGemmTile = 256;     // output tile of the projection GEMM (rows and columns)
+constexpr int kGemmKBytes = 64;    // bytes of one row of a K-slice of the GEMM
 constexpr int kPrologueTokens = 64;  // tokens per workgroup of the conv/gate kernel
 constexpr int kPrologueRun = 16;     // tokens one thread rolls the conv window over
 constexpr int kNormTokens = 16;      // tokens per workgroup of the gate/norm kernel
