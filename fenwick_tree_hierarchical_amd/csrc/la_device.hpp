@@ -101,6 +101,10 @@ __device__ __forceinline__ float wave_incl_scan(float x) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// The wave's index in its workgroup, as a wave-uniform (scalar) value: the
+// compiler cannot tell that threadIdx.x / 64 is the same in every lane, and
+// would otherwise keep it, and everything derived from it (tile indices,
+// branches), in vector registers.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 }  // namespace la
