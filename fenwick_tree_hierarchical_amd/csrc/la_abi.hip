@@ -226,7 +226,7 @@ LA_API int loglinear_bwd(const void* q, const void* k, const void* v, const floa
   a.rnodes_in_t = p.n_chunks > 1 ? static_cast<void*>(w + P.off_rnodes_in_t) : nullptr;
   a.rnodes_t = p.n_groups > 1 ? static_cast<void*>(w + P.off_rnodes_t) : nullptr;
   a.dcol = reinterpret_cast<float*>(w + P.off_dcol);
-  a.T = T; a.n_chunks = p.n_chunks; a.n_groups = p.n_groups; a.L = L; a.JG = P.JG;
+  a.T = T; a.n_chunks = p.n_chunks; a.n_groups = p.n_groups; a.L = L; a.JG = P.JG; a.rhalves = P.rhalves;
   hipStream_t s = (hipStream_t)stream;
   return dtype == kBF16 ? launch_bwd_bf16(P, fa, a, s) : launch_bwd_f32(P, fa, a, s);
 }

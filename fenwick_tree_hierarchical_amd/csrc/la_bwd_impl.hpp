@@ -51,7 +51,7 @@ struct BwdArgs {
   const float* gch;      // [BH][n_chunks] log2 gate total of each chunk
   const double* gprefix; // [BH][n_groups + 1] exclusive prefix sums of the group totals
   void* rnodes_in;       // key side: block starting at chunk x inside a group, [BH][n_chunks][d_k][d_v]
-  float* rpart;          // [BH][n_groups][JG][d_k][d_v] fp32: a group's share of its group-level blocks
+  float* rpart;          // [BH][n_groups][rhalves][JG][d_k][d_v] fp32: a group's share of its group-level blocks
   void* rnodes;          // block starting at group x, [BH][n_groups][d_k][d_v]
   void* rnodes_in_t;     // the same key-side nodes transposed, (d_v, d_k)
   void* rnodes_t;
@@ -61,6 +61,7 @@ struct BwdArgs {
   int64_t n_groups;
   int L;
   int JG;                // group levels with an upper block
+  int rhalves;           // shares per group and level in rpart: 1, or 2 (one per half group)
 };
 
 template <bool BF16, int C, int D>
@@ -627,6 +628,197 @@ __global__ __launch_bounds__(64 * state_waves(D)) void bwd_rev_states(BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// bwd_rev_states_staged: the key-side nodes of bwd_rev_states with every q and
+// dout row read from memory once, for bfloat16 shapes whose half groups fit
+// twice per CU.  One workgroup per half group (G / 2 chunks).  The half's rows
+// are loaded up front (direct global-to-LDS loads into swizzled row-major
+// tiles); then, one level at a time, the level's token weights (lambda of the
+// level times the gate from the block start) go to LDS and each chunk of the
+// level's upper halves adds its products, both operands read as transposed
+// fragments (tokens along k) and the weights applied to the Q fragment in
+// registers, with the rounding of bwd_rev_states.  Blocks of the in-group
+// levels below the top one lie inside a half; the top in-group level's upper
+// half is the second half.  For the group levels each half writes its own
+// share (gate from the group start) and bwd_rev_tree adds the two.  A wave's
+// tiles share their d_k block, so one weighted Q fragment serves all of them.
+template <int C, int D>
+__global__ __launch_bounds__(64 * state_waves(D)) void bwd_rev_states_staged(BwdArgs a) {
+  using EL = Elem<true>;
+  using Frag = typename EL::Frag;
+  constexpr int NW = state_waves(D), NT = 64 * NW, DB = D / 16, HT = DB * DB, TPW = state_tiles_per_wave(D);
+  constexpr int G = state_group(D), GH = G / 2, LOG2G = cilog2(G), LOG2C = cilog2(C);
+  constexpr int KST = EL::kStep, KSC = C / KST;
+  constexpr int ROWB = 2 * D;                      // bytes per token row
+  constexpr RevStagedLds lay = rev_staged_lds(C, D, G);
+  static_assert(C % KST == 0 && D >= 64 && GH >= 1 && TPW * NW == HT, "staged rev-states shape");
+  static_assert(NW % DB == 0, "a wave's tiles share one d_k block");
+  static_assert(GH * C <= NT && G <= NW, "one token row per thread, one gate scan per wave");
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* Qt = smem + lay.q;
+  unsigned char* Gt = smem + lay.g;
+  float* b2s = reinterpret_cast<float*>(smem + lay.b2);   // gate prefixes of every chunk of the group
+  float* wts = reinterpret_cast<float*>(smem + lay.w);    // two buffers of GH * C token weights
+
+  const int64_t ng = a.n_groups, nc = a.n_chunks, T = a.T;
+  const int64_t gidx = blockIdx.x >> 1;
+  const int half = blockIdx.x & 1;
+  const int64_t bh = gidx / ng, gam = gidx % ng;
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id(), lq = lane >> 4;
+  const int L = a.L, JG = a.JG;
+  const int64_t cg0 = gam * G;                                  // the group's first chunk
+  const int nchg = (int)(nc - cg0 < G ? nc - cg0 : G);          // chunks in the group
+  const int h0 = half * GH;                                     // in-group index of this half's first chunk
+  const int nch = nchg - h0 < GH ? nchg - h0 : GH;              // chunks in this half (<= 0: none)
+  const int nlev = LOG2G + JG;
+  // this half's share of group level j
+  auto share = [&](int j) { return a.rpart + (((bh * ng + gam) * 2 + half) * JG + (j - LOG2G - 1)) * D * D; };
+  if (nch <= 0) {
+    // the group ends inside its first half: this half's shares are zero
+    for (int j = LOG2G + 1; j <= nlev; ++j) {
+      if (!((gam >> (j - LOG2G - 1)) & 1)) continue;
+      f32x4* P = reinterpret_cast<f32x4*>(share(j));
+      for (int i = tid; i < D * D / 4; i += NT) P[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
+  const int64_t t0 = (cg0 + h0) * C;
+  const int nrow = (int)(T - t0 < (int64_t)nch * C ? T - t0 : (int64_t)nch * C);   // rows inside the sequence
+  const unsigned char* qsrc = reinterpret_cast<const unsigned char*>(a.q) + (bh * T + t0) * ROWB;
+  const unsigned char* gsrc = reinterpret_cast<const unsigned char*>(a.dout) + (bh * T + t0) * ROWB;
+
+  // ---- this half's q and dout rows into LDS
+  if (nrow == GH * C) {
+    // 1 KB runs: lane l fills granule l mod GPR of row RPR ri + l / GPR with
+    // the logical granule that XORs to it (as in the forward's output kernel)
+    constexpr int GPR = ROWB / 16, RPR = 1024 / ROWB, RUNS = GH * C * ROWB / 1024;
+    static_assert((2 * RUNS) % NW == 0, "runs are dealt evenly over the waves");
+    const int lrow = lane / GPR, lg16 = lane % GPR;
+    const unsigned off0 = (unsigned)(lrow * ROWB + ((lg16 ^ (lrow & 7)) << 4));
+    const unsigned off1 = (unsigned)(lrow * ROWB + ((lg16 ^ ((RPR + lrow) & 7)) << 4));
+#pragma unroll
+    for (int k = 0; k < 2 * RUNS / NW; ++k) {
+      const int run = w + k * NW;                  // wave-uniform
+      const int t = run / RUNS, ri = run % RUNS;
+      const unsigned o = (RPR >= 8 || (ri & 1) == 0) ? off0 : off1;
+      __builtin_amdgcn_global_load_lds((t == 0 ? qsrc : gsrc) + (unsigned)(ri * 1024) + o,
+                                       (__attribute__((address_space(3))) void*)((t == 0 ? Qt : Gt) + ri * 1024),
+                                       16, 0, 0);
+    }
+  } else {
+    // a half that reaches the end of the sequence: granule copies, zeros past it
+    constexpr int GPR = ROWB / 16;
+    const int per = nch * C * GPR;
+    for (int i = tid; i < 2 * per; i += NT) {
+      const int t = i / per, rem = i % per, r = rem / GPR, g = rem % GPR;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (r < nrow) x = *reinterpret_cast<const uint4*>((t == 0 ? qsrc : gsrc) + (size_t)r * ROWB + g * 16);
+      *reinterpret_cast<uint4*>((t == 0 ? Qt : Gt) + swz_gran<D>(r, g)) = x;
+    }
+  }
+  // levels with work in this half (wave-uniform): the in-group levels (the
+  // top one only in the second half) and the group levels whose bit is set in
+  // the group index
+  auto next_level = [&](int j) {
+    ++j;
+    if (j == LOG2G && half == 0) ++j;
+    while (j <= nlev && j > LOG2G && !((gam >> (j - LOG2G - 1)) & 1)) ++j;
+    return j;
+  };
+  // one token row per thread; its lambda of the first level is loaded now,
+  // that of each next level while the current level's products run
+  const int row = tid;
+  const bool has_row = row < nrow;
+  const float* lrow = a.lam + (bh * T + t0 + row) * L + LOG2C;
+  int j = next_level(0);
+  float lam_cur = (j <= nlev && has_row) ? lrow[j] : 0.f;
+
+  const float* la_bh = a.log_a + bh * T;
+  if (w < nchg) chunk_gate_scan<C>(la_bh, (cg0 + w) * C, T, b2s + w * C);
+  __builtin_amdgcn_s_waitcnt(0);                   // this wave's direct loads have landed
+  __syncthreads();
+
+  // this wave's tiles: one d_k block mb, d_v blocks nb(h)
+  const int mb = w % DB;
+  f32x4 acc[TPW], acct[TPW];
+#pragma unroll
+  for (int h = 0; h < TPW; ++h) acc[h] = acct[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int buf = 0;
+  while (j <= nlev) {
+    const bool in_group = j <= LOG2G;
+    const int jn = next_level(j);
+    float* W = wts + buf * (GH * C);
+    buf ^= 1;
+    if (row < nch * C) {
+      const int cig = h0 + row / C;                // in-group chunk of the row
+      float wv = 0.f;
+      if (!in_group || ((cig >> (j - 1)) & 1)) {
+        const int xs = in_group ? ((cig >> (j - 1)) << (j - 1)) : 0;   // block (or group) start
+        float pre = 0.f;                                                 // gate from xs to the chunk
+        for (int u = xs; u < cig; ++u) pre += b2s[u * C + C - 1];
+        if (has_row) wv = lam_cur * __builtin_amdgcn_exp2f(b2s[h0 * C + row] + pre);
+      }
+      W[row] = wv;
+    }
+    __syncthreads();   // W is complete; the other buffer is free once every wave is past this point
+    const float lam_nx = (jn <= nlev && has_row) ? lrow[jn] : 0.f;
+    for (int ci = 0; ci < nch; ++ci) {
+      const int cig = h0 + ci;
+      if (in_group && !((cig >> (j - 1)) & 1)) continue;
+      const unsigned char* qc = Qt + ci * C * ROWB;
+      const unsigned char* gc = Gt + ci * C * ROWB;
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) {
+        const float* wr = W + ci * C + s * KST + 8 * lq;   // this lane's eight tokens
+        const float4 w0 = *reinterpret_cast<const float4*>(wr);
+        const float4 w1 = *reinterpret_cast<const float4*>(wr + 4);
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        i16x4 lo, hi;
+        swz_tr_halves<D>(qc, s * KST, 16 * mb, lane, lo, hi);
+        const bf16_t qv[8] = {(bf16_t)lo[0], (bf16_t)lo[1], (bf16_t)lo[2], (bf16_t)lo[3],
+                              (bf16_t)hi[0], (bf16_t)hi[1], (bf16_t)hi[2], (bf16_t)hi[3]};
+        u16x8 qw;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qw[e] = EL::from_f32(EL::to_f32(qv[e]) * wv[e]);
+        const Frag qf = __builtin_bit_cast(Frag, qw);
+#pragma unroll
+        for (int h = 0; h < TPW; ++h) {
+          const int nb = (w + h * NW) / DB;
+          const Frag gf = swz_tr_frag<D>(gc, s * KST, 16 * nb, lane);
+          acc[h] = EL::mma(gf, qf, acc[h]);
+          if (in_group) acct[h] = EL::mma(qf, gf, acct[h]);   // group shares are stored one way only
+        }
+      }
+      const bool last = in_group ? ((((cig + 1) & ((1 << (j - 1)) - 1)) == 0) || cig == nchg - 1) : ci == nch - 1;
+      if (last) {
+        const int lr = lane & 15;
+        if (in_group) {
+          const int xs = (cig >> (j - 1)) << (j - 1);
+          bf16_t* R = reinterpret_cast<bf16_t*>(a.rnodes_in) + (bh * nc + cg0 + xs) * D * D;
+          bf16_t* RT = reinterpret_cast<bf16_t*>(a.rnodes_in_t) + (bh * nc + cg0 + xs) * D * D;
+#pragma unroll
+          for (int h = 0; h < TPW; ++h) {
+            const int nb = (w + h * NW) / DB;
+            store4<true>(R + (16 * mb + lr) * D + 16 * nb + 4 * lq, acc[h]);
+            store4<true>(RT + (16 * nb + lr) * D + 16 * mb + 4 * lq, acct[h]);
+          }
+        } else {
+          float* P = share(j);
+#pragma unroll
+          for (int h = 0; h < TPW; ++h) {
+            const int nb = (w + h * NW) / DB;
+            *reinterpret_cast<f32x4*>(P + (16 * mb + lr) * D + 16 * nb + 4 * lq) = acc[h];
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < TPW; ++h) acc[h] = acct[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    lam_cur = lam_nx;
+    j = jn;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // bwd_rev_tree: the key-side node of every block of groups that is the upper
 // half of its level block: it starts at group x >= 1 and spans 2^ctz(x)
 // groups; the sum of those groups' shares, each carried by the gate from the
@@ -651,10 +843,15 @@ __global__ __launch_bounds__(256) void bwd_rev_tree(BwdArgs a, int D) {
   E* R = reinterpret_cast<E*>(a.rnodes) + (bh * ng + x) * DD;
   E* RT = reinterpret_cast<E*>(a.rnodes_t) + (bh * ng + x) * DD;
   const int e0 = band * 16 * D;                             // first element of the band
+  const int RH = a.rhalves;
   for (int e = threadIdx.x; e < 16 * D; e += 256) {
     float acc = 0.f;
-    for (int64_t g = x; g < end; ++g)
-      acc += __builtin_amdgcn_exp2f((float)(gp[g] - base)) * a.rpart[((bh * ng + g) * a.JG + i) * DD + e0 + e];
+    for (int64_t g = x; g < end; ++g) {
+      const float* sh = a.rpart + ((bh * ng + g) * RH * a.JG + i) * DD + e0 + e;
+      // the group's share, or the sum of its two halves' shares
+      const float v = RH == 2 ? sh[0] + sh[(size_t)a.JG * DD] : sh[0];
+      acc += __builtin_amdgcn_exp2f((float)(gp[g] - base)) * v;
+    }
     const E val = EL::from_f32(acc);
     R[e0 + e] = val;
     tr[(e / D) * ld + e % D] = val;
@@ -1075,11 +1272,20 @@ int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s) {
                      P.lds_dq, s, a);
   ok = ok && hipGetLastError() == hipSuccess;
   if (p.n_chunks > 1) {
-    ok = ok && hipFuncSetAttribute((const void*)bwd_rev_states<BF16, C, D>,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, P.lds_rev) == hipSuccess;
-    if (!ok) return kEHIP;
-    hipLaunchKernelGGL((bwd_rev_states<BF16, C, D>), dim3((unsigned)(p.n_groups * p.BH)),
-                       dim3(64 * state_waves(D)), P.lds_rev, s, a);
+    if constexpr (rev_staged_fits(BF16, C, D, G)) {
+      constexpr int lds = rev_staged_lds(C, D, G).total;
+      ok = ok && hipFuncSetAttribute((const void*)bwd_rev_states_staged<C, D>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess;
+      if (!ok) return kEHIP;
+      hipLaunchKernelGGL((bwd_rev_states_staged<C, D>), dim3((unsigned)(2 * p.n_groups * p.BH)),
+                         dim3(64 * state_waves(D)), lds, s, a);
+    } else {
+      ok = ok && hipFuncSetAttribute((const void*)bwd_rev_states<BF16, C, D>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, P.lds_rev) == hipSuccess;
+      if (!ok) return kEHIP;
+      hipLaunchKernelGGL((bwd_rev_states<BF16, C, D>), dim3((unsigned)(p.n_groups * p.BH)),
+                         dim3(64 * state_waves(D)), P.lds_rev, s, a);
+    }
     ok = ok && hipGetLastError() == hipSuccess;
   }
   if (p.n_groups > 1) {

@@ -80,9 +80,31 @@ LA_HD constexpr RevLds rev_lds(int C, int D, int es, int G) {
   return o;
 }
 
+// bwd_rev_states_staged: one workgroup per half group (G / 2 chunks): the
+// half's q and dout rows (bf16, swizzled row-major tiles), the gate prefixes
+// of the whole group and two buffers of token weights.  Used where it fits
+// twice per CU (d >= 64 for the swizzle, C >= 32 for the token k-step).
+struct RevStagedLds {
+  int q, g, b2, w, total;
+};
+LA_HD constexpr RevStagedLds rev_staged_lds(int C, int D, int G) {
+  RevStagedLds o{};
+  const int rows = (G / 2) * C * 2 * D;
+  o.q = 0;
+  o.g = rows;
+  o.b2 = 2 * rows;
+  o.w = o.b2 + G * C * 4;
+  o.total = o.w + 2 * (G / 2) * C * 4;
+  return o;
+}
+LA_HD constexpr bool rev_staged_fits(bool bf16, int C, int D, int G) {
+  return bf16 && D >= 64 && C >= 32 && G >= 2 && 2 * rev_staged_lds(C, D, G).total <= kLdsLimit;
+}
+
 struct BwdPlan {
   FwdPlan f;                 // the forward structure over (k := v, v := k): nodes for dq
   int JG = 0;                // group levels that have an upper block (bit length of n_groups - 1)
+  int rhalves = 1;           // partial shares per group and level: 2 where the staged key-side kernel runs
   int lds_dq = 0, lds_dkv = 0, lds_rev = 0;
   size_t off_rnodes_in = 0, off_rpart = 0, off_rnodes = 0, off_dcol = 0, ws_bytes = 0;
   size_t off_rnodes_in_t = 0, off_rnodes_t = 0;   // the same nodes transposed, (d_v, d_k)
@@ -109,6 +131,7 @@ inline int plan_bwd(int B, int H, int64_t T, int dk, int dv, int C, int dtype, i
     return kOK;
   }
   P.JG = f.n_groups > 1 ? bit_length(f.n_groups - 1) : 0;
+  P.rhalves = rev_staged_fits(f.es == 2, C, dk, f.G) ? 2 : 1;
   const size_t DD = (size_t)dk * dv;
   size_t off = f.ws_bytes;
   if (f.n_chunks > 1) {
@@ -116,7 +139,7 @@ inline int plan_bwd(int B, int H, int64_t T, int dk, int dv, int C, int dtype, i
     P.off_rnodes_in_t = off; off = align_up(off + (size_t)f.BH * f.n_chunks * DD * f.es, 256);
   }
   if (f.n_groups > 1) {
-    P.off_rpart = off;  off = align_up(off + (size_t)f.BH * f.n_groups * P.JG * DD * 4, 256);
+    P.off_rpart = off;  off = align_up(off + (size_t)f.BH * f.n_groups * P.rhalves * P.JG * DD * 4, 256);
     P.off_rnodes = off;   off = align_up(off + (size_t)f.BH * f.n_groups * DD * f.es, 256);
     P.off_rnodes_t = off; off = align_up(off + (size_t)f.BH * f.n_groups * DD * f.es, 256);
   }

@@ -496,13 +496,23 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // four rows, and lane i receives column i of the four rows): lane (lq, lr)
 // receives rows k0 + 8 lq .. + 7 of column c0 + lr, the k-slice of an operand
 // whose rows are the tile's columns.
+// The two halves: lo holds rows k0 + 8 lq .. + 3, hi rows k0 + 8 lq + 4 .. + 7.
+// Code that works on the elements takes them from the halves: extracting
+// elements after a bit-cast round trip through bf16x8 was compiled as if
+// every element were element 0.
 template <int D>
-__device__ __forceinline__ bf16x8 swz_tr_frag(const unsigned char* tile, int k0, int c0, int lane) {
+__device__ __forceinline__ void swz_tr_halves(const unsigned char* tile, int k0, int c0, int lane, i16x4& lo,
+                                              i16x4& hi) {
   const int lq = lane >> 4, j = lane & 15;
   const int g = (c0 >> 3) + ((j & 3) >> 1), o = (j & 1) * 8;
   const int r0 = k0 + 8 * lq + (j >> 2);
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + swz_gran<D>(r0, g) + o));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + swz_gran<D>(r0 + 4, g) + o));
+  lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + swz_gran<D>(r0, g) + o));
+  hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + swz_gran<D>(r0 + 4, g) + o));
+}
+template <int D>
+__device__ __forceinline__ bf16x8 swz_tr_frag(const unsigned char* tile, int k0, int c0, int lane) {
+  i16x4 lo, hi;
+  swz_tr_halves<D>(tile, k0, c0, lane, lo, hi);
   return __builtin_bit_cast(bf16x8, u16x8{(unsigned short)lo[0], (unsigned short)lo[1], (unsigned short)lo[2],
                                           (unsigned short)lo[3], (unsigned short)hi[0], (unsigned short)hi[1],
                                           (unsigned short)hi[2], (unsigned short)hi[3]});

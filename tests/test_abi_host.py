@@ -207,11 +207,16 @@ def test_bwd_workspace_query():
     assert rc == OK
     fwd_part = ws(8, 16, 16384, 64, 64)[1]
     # forward structure, key-side chunk nodes (bf16, and transposed), group
-    # shares (fp32, 5 group levels for 32 groups), group nodes (and
-    # transposed), column terms
+    # shares (fp32, 5 group levels for 32 groups; in bf16 one per half group),
+    # group nodes (and transposed), column terms
     BH, nch, ng, DD = 128, 256, 32, 64 * 64
-    need = fwd_part + 2 * BH * nch * DD * 2 + BH * ng * 5 * DD * 4 + 2 * BH * ng * DD * 2 + BH * 16384 * 4
+    need = fwd_part + 2 * BH * nch * DD * 2 + 2 * BH * ng * 5 * DD * 4 + 2 * BH * ng * DD * 2 + BH * 16384 * 4
     assert need <= n < need * 1.01
+    # fp32: one share per group and level
+    rc, n32 = bws(8, 16, 16384, 64, 64, 0)
+    need32 = ws(8, 16, 16384, 64, 64, 0)[1] + 2 * BH * nch * DD * 4 + BH * ng * 5 * DD * 4 + 2 * BH * ng * DD * 4 \
+        + BH * 16384 * 4
+    assert rc == OK and need32 <= n32 < need32 * 1.01
     assert bws(2, 3, 50, 64, 64)[1] == 1280              # one partial chunk: 2*3*50 column terms, 256-aligned
     assert bws(1, 1, 64, 64, 128)[0] == ESHAPE              # chunks above 64
     for dt in (0, 1):
