@@ -120,24 +120,25 @@ __device__ __forceinline__ void store4(typename Elem<BF16>::T* p, f32x4 x) {
 }
 
 // Q, K, V and dout rows of chunk `tc` (nv valid rows) into row-major LDS
-// tiles, zero past the end; lambda rows into lamS.
-template <bool BF16, int C, int D>
-__device__ __forceinline__ void bwd_load_chunk(const BwdArgs& a, unsigned char* smem, const BwdChunkLds& lay,
+// tiles, zero past the end; lambda rows into lamS.  NT threads take part.
+template <bool BF16, int C, int D, int NT = BwdShape<BF16, C, D>::NT, typename Lay>
+__device__ __forceinline__ void bwd_load_chunk(const BwdArgs& a, unsigned char* smem, const Lay& lay,
                                                int64_t bh, int64_t tc, int nv) {
   using SH = BwdShape<BF16, C, D>;
   using E = typename Elem<BF16>::T;
+  constexpr int NPF = (SH::NV + NT - 1) / NT;
   const int tid = threadIdx.x;
   const int64_t T = a.T;
   const int L = a.L;
   const void* src[4] = {a.q, a.k, a.v, a.dout};
   const int dst[4] = {lay.q, lay.k, lay.v, lay.g};
-  uint4 x[4][SH::NPF];
+  uint4 x[4][NPF];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const E* g = reinterpret_cast<const E*>(src[m]) + (bh * T + tc) * D;
 #pragma unroll
-    for (int p = 0; p < SH::NPF; ++p) {
-      const int idx = tid + p * SH::NT;
+    for (int p = 0; p < NPF; ++p) {
+      const int idx = tid + p * NT;
       const int r = idx / SH::VPR, cv = idx % SH::VPR;
       x[m][p] = make_uint4(0, 0, 0, 0);
       if (idx < SH::NV && r < nv) x[m][p] = *reinterpret_cast<const uint4*>(g + r * D + cv * SH::EPV);
@@ -145,13 +146,13 @@ __device__ __forceinline__ void bwd_load_chunk(const BwdArgs& a, unsigned char* 
   }
   const float* lg = a.lam + (bh * T + tc) * L;
   float* lamS = reinterpret_cast<float*>(smem + lay.lam);
-  for (int idx = tid; idx < C * L; idx += SH::NT) lamS[idx] = idx < nv * L ? lg[idx] : 0.f;
+  for (int idx = tid; idx < C * L; idx += NT) lamS[idx] = idx < nv * L ? lg[idx] : 0.f;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     E* t = reinterpret_cast<E*>(smem + dst[m]);
 #pragma unroll
-    for (int p = 0; p < SH::NPF; ++p) {
-      const int idx = tid + p * SH::NT;
+    for (int p = 0; p < NPF; ++p) {
+      const int idx = tid + p * NT;
       if (idx < SH::NV) {
         const int r = idx / SH::VPR, cv = idx % SH::VPR;
         *reinterpret_cast<uint4*>(t + r * lay.ld_row + cv * SH::EPV) = x[m][p];
@@ -1187,6 +1188,536 @@ void bwd_chunk_dkv(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bwd_chunk_fused: bwd_chunk_dq and bwd_chunk_dkv in one workgroup of twice
+// their waves, for the bf16 shapes where two such workgroups fit per CU.  The
+// chunk is loaded once and its causal score tiles are formed once, in both
+// orientations: dS by query row (for dq), dS^T and P^T by key row (for dk and
+// dv), and the in-chunk shares of the lambda gradients.  Then the first half
+// of the waves runs the query side (dq = dS K and the levels of the forward
+// structure over (v, k)) while the second half runs the key side (dk = dS^T Q,
+// dv = P^T dout and the key-side nodes).  Each side's arithmetic is that of
+// its own kernel, so the results are the same bits; the key-side nodes must
+// be complete when it starts.
+template <bool BF16, int C, int D>
+__global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a) {
+  using SH = BwdShape<BF16, C, D>;
+  using EL = Elem<BF16>;
+  using E = typename EL::T;
+  using Frag = typename EL::Frag;
+  constexpr int QB = SH::QB, DB = SH::DB, KSD = SH::KSD, KSC = SH::KSC, NCB = SH::NCB, NW = SH::NW;
+  constexpr int KPL = EL::kPerLane, KST = EL::kStep, LOG2C = SH::LOG2C;
+  constexpr int NW2 = 2 * NW, NT2 = 64 * NW2;
+  constexpr int KT2 = (SH::NST + NW2 - 1) / NW2;              // score tiles per wave (max)
+  constexpr int G = state_group(D), LOG2G = cilog2(G);
+  static_assert(64 * NW >= 4 * C, "four query-side threads per row");
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int L = a.L;
+  const int NI = L - LOG2C - 1;                                // levels above the chunk
+  const BwdFusedLds lay = bwd_fused_lds(C, D, sizeof(E), L);
+  const E* Qs = reinterpret_cast<const E*>(smem + lay.q);
+  const E* Ks = reinterpret_cast<const E*>(smem + lay.k);
+  const E* Vs = reinterpret_cast<const E*>(smem + lay.v);
+  const E* Gs = reinterpret_cast<const E*>(smem + lay.g);
+  E* S0 = reinterpret_cast<E*>(smem + lay.s0);                 // dS by query row
+  E* S1 = reinterpret_cast<E*>(smem + lay.s1);                 // dS^T by key row
+  E* S2 = reinterpret_cast<E*>(smem + lay.s2);                 // P^T by key row
+  const float* lamS = reinterpret_cast<const float*>(smem + lay.lam);
+  float* partO = reinterpret_cast<float*>(smem + lay.part);    // [tile][16]: off-diagonal tile row sums
+  float* partD = partO + SH::NST * 16;                         // [row block][16][5]: diagonal tile levels 0..4
+  float* inter = reinterpret_cast<float*>(smem + lay.inter);   // [wave][level - log2 C - 1][row]
+  float* colS = reinterpret_cast<float*>(smem + lay.col);      // [wave][key row]
+  float* b2c = reinterpret_cast<float*>(smem + lay.b2);
+  float* e2c = reinterpret_cast<float*>(smem + lay.e2);
+
+  const int64_t nc = a.n_chunks, ng = a.n_groups, T = a.T;
+  const int64_t item = xcd_item(blockIdx.x, gridDim.x);
+  const int64_t bh = item / nc, c = item % nc;
+  const int tid = threadIdx.x, lane = lane_id(), wg = wave_id(), lq = lane >> 4, lr = lane & 15;
+  const bool qside = wg < NW;                                  // wave-uniform
+  const int w = qside ? wg : wg - NW;                          // wave index within its side
+  const int64_t tc = c * C;
+  const int nv = (int)(T - tc < C ? T - tc : C);
+  const int64_t gam = c / G, cg0 = gam * G;
+  const int ci = (int)(c - cg0);
+
+  bwd_load_chunk<BF16, C, D, NT2>(a, smem, lay, bh, tc, nv);
+  if (wg == 0) {
+    // in-chunk inclusive prefix of log2(a), and the gate from each key to the
+    // chunk end
+    const float x = (lane < C && tc + lane < T) ? a.log_a[bh * T + tc + lane] * kLog2e : 0.f;
+    const float y = wave_incl_scan(x);
+    const float tot = __shfl(y, C - 1, 64);
+    if (lane < C) {
+      b2c[lane] = y;
+      e2c[lane] = __builtin_amdgcn_exp2f(tot - y);
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 1: tile tau = (query block qb, key block kb <= qb), S and dP
+  // with a lane per query (four keys) and with a lane per key (four queries)
+#pragma unroll
+  for (int u = 0; u < KT2; ++u) {
+    const int tau = wg + u * NW2;
+    if (tau >= SH::NST) break;
+    int qb, kb;
+    tile_blocks(tau, qb, kb);
+    f32x4 sq = f32x4{0.f, 0.f, 0.f, 0.f}, dpq = sq, sk = sq, dpk = sq;
+#pragma unroll
+    for (int s = 0; s < KSD; ++s) {
+      const int k0 = s * KST + lq * KPL;
+      const auto kf = EL::template load_k<D>(Ks + (16 * kb + lr) * lay.ld_row + k0, k0);
+      const auto qf = EL::template load_k<D>(Qs + (16 * qb + lr) * lay.ld_row + k0, k0);
+      const auto vf = EL::template load_k<D>(Vs + (16 * kb + lr) * lay.ld_row + k0, k0);
+      const auto gf = EL::template load_k<D>(Gs + (16 * qb + lr) * lay.ld_row + k0, k0);
+      sq = EL::mma(kf, qf, sq);
+      dpq = EL::mma(vf, gf, dpq);
+      sk = EL::mma(qf, kf, sk);
+      dpk = EL::mma(gf, vf, dpk);
+    }
+    {
+      // query side: dS rows and the in-chunk lambda gradient shares
+      const int iq = 16 * qb + lr;
+      const int j0 = 16 * kb + 4 * lq;
+      const float b2q = b2c[iq];
+      float dsv[4], ev[4];
+      int lvv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + i;
+        int lv = fenwick_level_local((unsigned)iq, (unsigned)j);
+        lv = lv < L ? lv : L - 1;
+        const float W = __builtin_amdgcn_exp2f(b2q - b2c[j]);
+        const bool ok = j <= iq && iq < nv;
+        dsv[i] = ok ? dpq[i] * W * lamS[iq * L + lv] : 0.f;
+        ev[i] = ok ? sq[i] * dpq[i] * W : 0.f;
+        lvv[i] = lv;
+      }
+      *reinterpret_cast<u16x4*>(S0 + iq * lay.ld_s + j0) =
+          u16x4{f32_to_bf16(dsv[0]), f32_to_bf16(dsv[1]), f32_to_bf16(dsv[2]), f32_to_bf16(dsv[3])};
+      if (kb == qb) {
+        // inside a 16-block the levels are 0..4
+        float dlr[5];
+#pragma unroll
+        for (int v = 0; v < 5; ++v) {
+          dlr[v] = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dlr[v] += (lvv[i] == v) ? ev[i] : 0.f;
+          dlr[v] += __shfl_xor(dlr[v], 16, 64);
+          dlr[v] += __shfl_xor(dlr[v], 32, 64);
+        }
+        if (lq == 0) {
+#pragma unroll
+          for (int v = 0; v < 5; ++v) partD[(qb * 16 + lr) * 5 + v] = dlr[v];
+        }
+      } else {
+        // every key of an earlier 16-block is at one level, 5 + msb(qb ^ kb)
+        float es = (ev[0] + ev[1]) + (ev[2] + ev[3]);
+        es += __shfl_xor(es, 16, 64);
+        es += __shfl_xor(es, 32, 64);
+        if (lq == 0) partO[tau * 16 + lr] = es;
+      }
+    }
+    {
+      // key side: dS^T and P^T rows
+      const int skr = 16 * kb + lr, t0 = 16 * qb + 4 * lq;
+      const float b2k = b2c[skr];
+      float pv[4], dv_[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + i;
+        int lv = fenwick_level_local((unsigned)t, (unsigned)skr);
+        lv = lv < L ? lv : L - 1;
+        const float W = __builtin_amdgcn_exp2f(b2c[t] - b2k) * lamS[t * L + lv];
+        const bool ok = skr <= t && t < nv;
+        pv[i] = ok ? sk[i] * W : 0.f;
+        dv_[i] = ok ? dpk[i] * W : 0.f;
+      }
+      *reinterpret_cast<u16x4*>(S1 + skr * lay.ld_s + t0) =
+          u16x4{f32_to_bf16(dv_[0]), f32_to_bf16(dv_[1]), f32_to_bf16(dv_[2]), f32_to_bf16(dv_[3])};
+      *reinterpret_cast<u16x4*>(S2 + skr * lay.ld_s + t0) =
+          u16x4{f32_to_bf16(pv[0]), f32_to_bf16(pv[1]), f32_to_bf16(pv[2]), f32_to_bf16(pv[3])};
+    }
+  }
+  __syncthreads();
+
+  const int cb0 = w * NCB;
+  const bool owner = cb0 < DB;
+  unsigned occm = 0;                               // query side: occupied levels as a bit mask
+  if (qside) {
+    // ---- query side: occupied levels above the chunk, as in the forward
+    bool act = false;
+    int64_t off = 0;
+    int lev = 0, src = 0;
+    int64_t eg = 0;
+    if (lane >= 1 && lane <= LOG2G) {
+      const int j = lane;
+      if ((ci >> (j - 1)) & 1) {
+        const int el = ((ci >> j) << j) + (1 << (j - 1)) - 1;
+        act = true;
+        off = (bh * nc + cg0 + el) * D * D;
+        src = el + 1;
+        lev = LOG2C + j;
+      }
+    }
+    if (lane >= 32 && lane < 63) {
+      const int i = lane - 31;
+      if (gam > 0 && ((gam >> (i - 1)) & 1)) {
+        eg = ((gam >> i) << i) + (1ll << (i - 1)) - 1;
+        act = true;
+        off = (bh * ng + eg) * D * D;
+        lev = LOG2C + LOG2G + i;
+      }
+    }
+    const unsigned long long lmask = __ballot(act);
+    const int n_lev = __popcll(lmask);
+    const int pos = __popcll(lmask & ((1ull << lane) - 1ull));
+    const int ent = __builtin_amdgcn_ds_permute((act ? pos : 63) << 2, lane);
+    for (int li = 0; li < n_lev; ++li)
+      occm |= 1u << __builtin_amdgcn_readlane(lev, __builtin_amdgcn_readlane(ent, li));
+    auto node_of = [&](int li) {
+      const int el = __builtin_amdgcn_readlane(ent, li);
+      const uint64_t o64 = (uint64_t)off;
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)o64, el);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(o64 >> 32), el);
+      const int64_t o = (int64_t)(((uint64_t)hi << 32) | lo);
+      return (el >= 32 ? reinterpret_cast<const E*>(a.nodes) : reinterpret_cast<const E*>(a.nodes_in)) + o;
+    };
+    constexpr int NPRE = 2;
+    auto load_node = [&](int li, Frag (&dst)[KSD][NCB]) {
+      const E* node = node_of(li);
+#pragma unroll
+      for (int s2 = 0; s2 < KSD; ++s2) {
+        const int k0 = s2 * KST + lq * KPL;
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) dst[s2][n] = EL::template load_k<D>(node + (16 * (cb0 + n) + lr) * D + k0, k0);
+      }
+    };
+    const float gx = (lane < ci) ? a.gch[bh * nc + cg0 + lane] : 0.f;
+    const bool grp = act && lane >= 32;
+    float g2 = 0.f;
+    {
+      const float incl = wave_incl_scan(gx);
+      float S = __shfl_up(incl, 1, 64);
+      if (lane == 0) S = 0.f;
+      const float pre = __shfl(S, ci, 64);
+      const float Se = __shfl(S, src, 64);
+      if (act) {
+        if (grp) {
+          const double* gp = a.gprefix + bh * (ng + 1);
+          g2 = (float)(gp[gam] - gp[eg + 1]) + pre;
+        } else {
+          g2 = pre - Se;
+        }
+      }
+    }
+    if (owner) {
+      Frag nf[NPRE][KSD][NCB];
+#pragma unroll
+      for (int u = 0; u < NPRE; ++u)
+        if (u < n_lev) load_node(u, nf[u]);
+      f32x4 acc[QB][NCB];
+#pragma unroll
+      for (int rb = 0; rb < QB; ++rb)
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) acc[rb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      {
+        Frag kt[KSC][NCB];                         // K^T rows (columns of K), k-slices of keys
+#pragma unroll
+        for (int s = 0; s < KSC; ++s)
+#pragma unroll
+          for (int n = 0; n < NCB; ++n)
+            kt[s][n] = gather_col<BF16, C>(Ks, lay.ld_row, s * KST + lq * KPL, 16 * (cb0 + n) + lr);
+#pragma unroll
+        for (int rb = 0; rb < QB; ++rb) {
+#pragma unroll
+          for (int s = 0; s < KSC; ++s) {
+            if (s * KST > 16 * rb + 15) break;
+            const int k0 = s * KST + lq * KPL;
+            Frag pb = zero_frag<BF16>();
+            if (k0 < C && k0 / 16 <= rb) pb = EL::load(S0 + (16 * rb + lr) * lay.ld_s + k0);
+#pragma unroll
+            for (int n = 0; n < NCB; ++n) acc[rb][n] = EL::mma(kt[s][n], pb, acc[rb][n]);
+          }
+        }
+      }
+      // the Q entries of this wave's columns, for the row dots of the levels
+      E qv[QB][NCB][4];
+#pragma unroll
+      for (int rb = 0; rb < QB; ++rb)
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) {
+          const E* qrow = Qs + (16 * rb + lr) * lay.ld_row + 16 * (cb0 + n) + 4 * lq;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) qv[rb][n][i] = qrow[i];
+        }
+      auto contract = [&](int li, const Frag (&nfr)[KSD][NCB]) {
+        const int el = __builtin_amdgcn_readlane(ent, li);
+        const float f = __builtin_amdgcn_exp2f(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g2), el)));
+        const int lv = __builtin_amdgcn_readlane(lev, el);
+#pragma unroll
+        for (int rb = 0; rb < QB; ++rb) {
+          const int r = 16 * rb + lr;
+          f32x4 tmp[NCB];
+#pragma unroll
+          for (int n = 0; n < NCB; ++n) tmp[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s2 = 0; s2 < KSD; ++s2) {
+            const int k0 = s2 * KST + lq * KPL;
+            const auto gf = EL::template load_k<D>(Gs + r * lay.ld_row + k0, k0);
+#pragma unroll
+            for (int n = 0; n < NCB; ++n) tmp[n] = EL::mma(nfr[s2][n], gf, tmp[n]);
+          }
+          const float wq = __builtin_amdgcn_exp2f(b2c[r]) * f;
+          const float wl = wq * lamS[r * L + lv];
+          float ds = 0.f;
+#pragma unroll
+          for (int n = 0; n < NCB; ++n) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              ds += tmp[n][i] * EL::to_f32(qv[rb][n][i]);
+              acc[rb][n][i] += wl * tmp[n][i];
+            }
+          }
+          ds += __shfl_xor(ds, 16, 64);
+          ds += __shfl_xor(ds, 32, 64);
+          if (lq == 0) inter[(w * NI + (lv - LOG2C - 1)) * C + r] = wq * ds;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      for (int base = 0; base < n_lev; base += NPRE) {
+#pragma unroll
+        for (int u = 0; u < NPRE; ++u) {
+          const int li = base + u;
+          if (li >= n_lev) break;
+          contract(li, nf[u]);
+          if (li + NPRE < n_lev) load_node(li + NPRE, nf[u]);
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < QB; ++rb) {
+        const int r = 16 * rb + lr;
+        if (r < nv) {
+          E* o = reinterpret_cast<E*>(a.dq) + (bh * T + tc + r) * D + 4 * lq;
+#pragma unroll
+          for (int n = 0; n < NCB; ++n) store4<BF16>(o + 16 * (cb0 + n), acc[rb][n]);
+        }
+      }
+    }
+  } else {
+    // ---- key side: levels whose upper block lies above the chunk
+    bool act = false;
+    int64_t off = 0;
+    int dst_x = 0;
+    int64_t xg = 0;
+    if (lane >= 1 && lane <= LOG2G) {
+      const int j = lane;
+      if (!((ci >> (j - 1)) & 1)) {
+        const int x = ((ci >> j) << j) + (1 << (j - 1));
+        if (cg0 + x < nc) {
+          act = true;
+          off = (bh * nc + cg0 + x) * D * D;
+          dst_x = x;
+        }
+      }
+    }
+    if (lane >= 32 && lane < 63) {
+      const int i = lane - 31;
+      if (!((gam >> (i - 1)) & 1)) {
+        xg = ((gam >> i) << i) + (1ll << (i - 1));
+        if (xg < ng) {
+          act = true;
+          off = (bh * ng + xg) * D * D;
+        }
+      }
+    }
+    const unsigned long long lmask = __ballot(act);
+    const int n_lev = __popcll(lmask);
+    const int pos = __popcll(lmask & ((1ull << lane) - 1ull));
+    const int ent = __builtin_amdgcn_ds_permute((act ? pos : 63) << 2, lane);
+    auto node_off = [&](int li, int& el) {
+      el = __builtin_amdgcn_readlane(ent, li);
+      const uint64_t o64 = (uint64_t)off;
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)o64, el);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(o64 >> 32), el);
+      return (int64_t)(((uint64_t)hi << 32) | lo);
+    };
+    auto load_node = [&](int li, Frag (&rf)[KSD][NCB], Frag (&rt)[KSD][NCB]) {
+      int el;
+      const int64_t o = node_off(li, el);
+      const E* R = (el >= 32 ? reinterpret_cast<const E*>(a.rnodes) : reinterpret_cast<const E*>(a.rnodes_in)) + o;
+      const E* RT = (el >= 32 ? reinterpret_cast<const E*>(a.rnodes_t) : reinterpret_cast<const E*>(a.rnodes_in_t)) + o;
+#pragma unroll
+      for (int s2 = 0; s2 < KSD; ++s2) {
+        const int k0 = s2 * KST + lq * KPL;
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) {
+          rf[s2][n] = EL::template load_k<D>(R + (16 * (cb0 + n) + lr) * D + k0, k0);
+          rt[s2][n] = EL::template load_k<D>(RT + (16 * (cb0 + n) + lr) * D + k0, k0);
+        }
+      }
+    };
+    float g2 = 0.f;                               // log2 gate from the chunk end to the block start
+    if (nc > 1) {
+      const float gx = (lane < G && cg0 + lane < nc) ? a.gch[bh * nc + cg0 + lane] : 0.f;
+      const float incl = wave_incl_scan(gx);
+      float S = __shfl_up(incl, 1, 64);           // S(y): gates of the group's chunks before y
+      if (lane == 0) S = 0.f;
+      const float after = __shfl(S, ci + 1, 64);
+      const float at_x = __shfl(S, dst_x, 64);
+      const float at_end = __shfl(S, G, 64);
+      if (act) {
+        if (lane >= 32) {
+          const double* gp = a.gprefix + bh * (ng + 1);
+          g2 = (at_end - after) + (float)(gp[xg] - gp[gam + 1]);
+        } else {
+          g2 = at_x - after;
+        }
+      }
+    }
+    if (owner) {
+      constexpr int NPRE = 1;
+      Frag rf[NPRE][KSD][NCB], rt[NPRE][KSD][NCB];
+#pragma unroll
+      for (int u = 0; u < NPRE; ++u)
+        if (u < n_lev) load_node(u, rf[u], rt[u]);
+      f32x4 ak[QB][NCB], av[QB][NCB];
+#pragma unroll
+      for (int kb = 0; kb < QB; ++kb)
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) ak[kb][n] = av[kb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // dk = dS^T Q and dv = P^T dout: columns of Q and of dout as the A operand
+#pragma unroll
+      for (int side = 0; side < 2; ++side) {
+        const E* X = side == 0 ? Qs : Gs;
+        const E* SS = side == 0 ? S1 : S2;
+        Frag ft[KSC][NCB];
+#pragma unroll
+        for (int s = 0; s < KSC; ++s)
+#pragma unroll
+          for (int n = 0; n < NCB; ++n)
+            ft[s][n] = gather_col<BF16, C>(X, lay.ld_row, s * KST + lq * KPL, 16 * (cb0 + n) + lr);
+#pragma unroll
+        for (int kb = 0; kb < QB; ++kb) {
+#pragma unroll
+          for (int s = 0; s < KSC; ++s) {
+            if (s * KST + KST <= 16 * kb) continue;
+            const int k0 = s * KST + lq * KPL;
+            Frag sf = zero_frag<BF16>();
+            if (k0 < C && k0 / 16 >= kb) sf = EL::load(SS + (16 * kb + lr) * lay.ld_s + k0);
+#pragma unroll
+            for (int n = 0; n < NCB; ++n) {
+              if (side == 0) ak[kb][n] = EL::mma(ft[s][n], sf, ak[kb][n]);
+              else av[kb][n] = EL::mma(ft[s][n], sf, av[kb][n]);
+            }
+          }
+        }
+      }
+      auto contract = [&](int li, const Frag (&rfr)[KSD][NCB], const Frag (&rtr)[KSD][NCB]) {
+        const int el = __builtin_amdgcn_readlane(ent, li);
+        const float f = __builtin_amdgcn_exp2f(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g2), el)));
+#pragma unroll
+        for (int kb = 0; kb < QB; ++kb) {
+          const int skr = 16 * kb + lr;
+          f32x4 tk[NCB], tv[NCB];
+#pragma unroll
+          for (int n = 0; n < NCB; ++n) tk[n] = tv[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s2 = 0; s2 < KSD; ++s2) {
+            const int k0 = s2 * KST + lq * KPL;
+            const auto vf = EL::template load_k<D>(Vs + skr * lay.ld_row + k0, k0);
+            const auto kf = EL::template load_k<D>(Ks + skr * lay.ld_row + k0, k0);
+#pragma unroll
+            for (int n = 0; n < NCB; ++n) {
+              tk[n] = EL::mma(rfr[s2][n], vf, tk[n]);
+              tv[n] = EL::mma(rtr[s2][n], kf, tv[n]);
+            }
+          }
+          const float wk = f * e2c[skr];
+#pragma unroll
+          for (int n = 0; n < NCB; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              ak[kb][n][i] += wk * tk[n][i];
+              av[kb][n][i] += wk * tv[n][i];
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      for (int base = 0; base < n_lev; base += NPRE) {
+#pragma unroll
+        for (int u = 0; u < NPRE; ++u) {
+          const int li = base + u;
+          if (li >= n_lev) break;
+          contract(li, rf[u], rt[u]);
+          if (li + NPRE < n_lev) load_node(li + NPRE, rf[u], rt[u]);
+        }
+      }
+      // this wave's share of v_s . dv_s, then the rows of dk and dv
+#pragma unroll
+      for (int kb = 0; kb < QB; ++kb) {
+        const int skr = 16 * kb + lr;
+        float cs = 0.f;
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) {
+          const E* vrow = Vs + skr * lay.ld_row + 16 * (cb0 + n) + 4 * lq;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) cs += av[kb][n][i] * EL::to_f32(vrow[i]);
+        }
+        cs += __shfl_xor(cs, 16, 64);
+        cs += __shfl_xor(cs, 32, 64);
+        if (lq == 0) colS[w * C + skr] = cs;
+        if (skr < nv) {
+          E* okr = reinterpret_cast<E*>(a.dk) + (bh * T + tc + skr) * D + 4 * lq;
+          E* ovr = reinterpret_cast<E*>(a.dv) + (bh * T + tc + skr) * D + 4 * lq;
+#pragma unroll
+          for (int n = 0; n < NCB; ++n) {
+            store4<BF16>(okr + 16 * (cb0 + n), ak[kb][n]);
+            store4<BF16>(ovr + 16 * (cb0 + n), av[kb][n]);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (qside) {
+    // lambda gradients of the chunk's rows (as in bwd_chunk_dq): levels 0..4
+    // from the diagonal tiles, 5..log2 C from the earlier tiles of the row
+    // block, the rest from the query-side waves' shares; four threads per row
+    const int r = tid >> 2, part = tid & 3;
+    const int per = (L + 3) >> 2;
+    const int rb = r >> 4, rr = r & 15;
+    float rt = 0.f;
+    float* dl = a.dlam + (bh * T + tc + r) * L;
+    if (r < C) {
+      for (int lv = part * per; lv < L && lv < (part + 1) * per; ++lv) {
+        float val = 0.f;
+        if (lv <= 4 && lv <= LOG2C) {
+          val = partD[(rb * 16 + rr) * 5 + lv];
+        } else if (lv <= LOG2C) {
+          for (int kb = 0; kb < rb; ++kb)
+            if (5 + (31 - __builtin_clz((unsigned)(rb ^ kb))) == lv) val += partO[(rb * (rb + 1) / 2 + kb) * 16 + rr];
+        } else if ((occm >> lv) & 1u) {
+          for (int u = 0; u < SH::NWA; ++u) val += inter[(u * NI + (lv - LOG2C - 1)) * C + r];
+        }
+        rt += lamS[r * L + lv] * val;
+        if (r < nv) dl[lv] = val;
+      }
+    }
+    rt += __shfl_xor(rt, 1, 64);
+    rt += __shfl_xor(rt, 2, 64);
+    if (r < nv && part == 0) a.dlog_a[bh * T + tc + r] = rt;
+  } else {
+    const int t = tid - 64 * NW;
+    if (t < nv) {
+      float cs = 0.f;
+      for (int u = 0; u < SH::NWA; ++u) cs += colS[u * C + t];
+      a.dcol[bh * T + tc + t] = cs;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // bwd_gate_grad: one workgroup per (b,h).  dlog_a_r = sum_{u >= r} (row_u -
 // col_u), tiles of 1024 tokens from the end: float sums inside a tile, a
 // float64 carry across tiles.  (A template only so that every translation
@@ -1265,12 +1796,18 @@ int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s) {
       hipLaunchKernelGGL((fwd_group_tree<BF16, 32>), grid, dim3(256), 0, s, fa, D);
     ok = ok && hipGetLastError() == hipSuccess;
   }
-  ok = ok && hipFuncSetAttribute((const void*)bwd_chunk_dq<BF16, C, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 P.lds_dq) == hipSuccess;
-  if (!ok) return kEHIP;
-  hipLaunchKernelGGL((bwd_chunk_dq<BF16, C, D>), dim3((unsigned)(p.n_chunks * p.BH)), dim3(64 * bwd_waves(C)),
-                     P.lds_dq, s, a);
-  ok = ok && hipGetLastError() == hipSuccess;
+  // the fused per-chunk kernel needs the key-side nodes first; the query-side
+  // kernel of the split pair does not
+  constexpr bool kFusedShape = bwd_fused_shape(BF16, C, D);
+  const bool fused = kFusedShape && P.lds_fused > 0;
+  if (!fused) {
+    ok = ok && hipFuncSetAttribute((const void*)bwd_chunk_dq<BF16, C, D>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, P.lds_dq) == hipSuccess;
+    if (!ok) return kEHIP;
+    hipLaunchKernelGGL((bwd_chunk_dq<BF16, C, D>), dim3((unsigned)(p.n_chunks * p.BH)), dim3(64 * bwd_waves(C)),
+                       P.lds_dq, s, a);
+    ok = ok && hipGetLastError() == hipSuccess;
+  }
   if (p.n_chunks > 1) {
     if constexpr (rev_staged_fits(BF16, C, D, G)) {
       constexpr int lds = rev_staged_lds(C, D, G).total;
@@ -1293,12 +1830,24 @@ int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s) {
                        D);
     ok = ok && hipGetLastError() == hipSuccess;
   }
-  ok = ok && hipFuncSetAttribute((const void*)bwd_chunk_dkv<BF16, C, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 P.lds_dkv) == hipSuccess;
-  if (!ok) return kEHIP;
-  hipLaunchKernelGGL((bwd_chunk_dkv<BF16, C, D>), dim3((unsigned)(p.n_chunks * p.BH)), dim3(64 * bwd_waves(C)),
-                     P.lds_dkv, s, a);
-  ok = ok && hipGetLastError() == hipSuccess;
+  if constexpr (kFusedShape) {
+    if (fused) {
+      ok = ok && hipFuncSetAttribute((const void*)bwd_chunk_fused<BF16, C, D>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, P.lds_fused) == hipSuccess;
+      if (!ok) return kEHIP;
+      hipLaunchKernelGGL((bwd_chunk_fused<BF16, C, D>), dim3((unsigned)(p.n_chunks * p.BH)),
+                         dim3(128 * bwd_waves(C)), P.lds_fused, s, a);
+      ok = ok && hipGetLastError() == hipSuccess;
+    }
+  }
+  if (!fused) {
+    ok = ok && hipFuncSetAttribute((const void*)bwd_chunk_dkv<BF16, C, D>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, P.lds_dkv) == hipSuccess;
+    if (!ok) return kEHIP;
+    hipLaunchKernelGGL((bwd_chunk_dkv<BF16, C, D>), dim3((unsigned)(p.n_chunks * p.BH)), dim3(64 * bwd_waves(C)),
+                       P.lds_dkv, s, a);
+    ok = ok && hipGetLastError() == hipSuccess;
+  }
   hipLaunchKernelGGL((bwd_gate_grad<256>), dim3((unsigned)p.BH), dim3(256), 0, s, a);
   ok = ok && hipGetLastError() == hipSuccess;
   return ok ? kOK : kEHIP;

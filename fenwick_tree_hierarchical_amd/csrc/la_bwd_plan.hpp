@@ -61,6 +61,47 @@ LA_HD constexpr BwdChunkLds bwd_chunk_lds(int C, int D, int es, int L, bool key_
   return o;
 }
 
+// bwd_chunk_fused: both per-chunk kernels in one workgroup of twice the
+// waves (the first half the query side, the second the key side), for the
+// bf16 shapes where two such workgroups fit per CU.  Every buffer has a region
+// of its own: the tiles, dS by query row (s0), dS^T and P^T by key row (s1,
+// s2), lambda rows, the in-chunk and level shares of the lambda gradients
+// (part, inter), the key side's shares of v . dv (col), the gate prefix (b2)
+// and the gate from each key to the chunk end (e2).
+struct BwdFusedLds {
+  int q, k, v, g, s0, s1, s2, lam, part, inter, col, b2, e2, total, ld_row, ld_s;
+};
+LA_HD constexpr BwdFusedLds bwd_fused_lds(int C, int D, int es, int L) {
+  BwdFusedLds o{};
+  const int NW = bwd_waves(C);
+  int log2c = 0;
+  for (int c = C; c > 1; c >>= 1) ++log2c;
+  o.ld_row = D + 16 / es;
+  o.ld_s = C + 16 / es;
+  const int tile = (C * o.ld_row * es + 255) / 256 * 256;
+  const int stile = (C * o.ld_s * es + 255) / 256 * 256;
+  const int QB = C / 16, NST = QB * (QB + 1) / 2;
+  const int n_inter = L - log2c - 1 > 0 ? L - log2c - 1 : 0;
+  int off = 0;
+  o.q = off;  off += tile;
+  o.k = off;  off += tile;
+  o.v = off;  off += tile;
+  o.g = off;  off += tile;
+  o.s0 = off; off += stile;
+  o.s1 = off; off += stile;
+  o.s2 = off; off += stile;
+  o.lam = off;   off += (C * L * 4 + 255) / 256 * 256;
+  o.part = off;  off += ((NST * 16 + QB * 16 * 5) * 4 + 255) / 256 * 256;
+  o.inter = off; off += (NW * n_inter * C * 4 + 255) / 256 * 256;
+  o.col = off;   off += (NW * C * 4 + 255) / 256 * 256;
+  o.b2 = off;    off += (C * 4 + 255) / 256 * 256;
+  o.e2 = off;    off += (C * 4 + 255) / 256 * 256;
+  o.total = off;
+  return o;
+}
+// The fused kernel's shapes: bf16, 32 <= C (four waves per side), d <= 64.
+LA_HD constexpr bool bwd_fused_shape(bool bf16, int C, int D) { return bf16 && C >= 32 && C <= 64 && D <= 64; }
+
 // bwd_rev_states: one workgroup per (b,h, group of G chunks), the state
 // kernel's wave count; gated Q^T and dout^T of one chunk, the group's gate
 // prefixes and the chunk's token weights.
@@ -106,6 +147,7 @@ struct BwdPlan {
   int JG = 0;                // group levels that have an upper block (bit length of n_groups - 1)
   int rhalves = 1;           // partial shares per group and level: 2 where the staged key-side kernel runs
   int lds_dq = 0, lds_dkv = 0, lds_rev = 0;
+  int lds_fused = 0;         // > 0: the fused per-chunk kernel runs (two workgroups fit per CU)
   size_t off_rnodes_in = 0, off_rpart = 0, off_rnodes = 0, off_dcol = 0, ws_bytes = 0;
   size_t off_rnodes_in_t = 0, off_rnodes_t = 0;   // the same nodes transposed, (d_v, d_k)
 };
@@ -126,6 +168,8 @@ inline int plan_bwd(int B, int H, int64_t T, int dk, int dv, int C, int dtype, i
   if (bwd_chunk_lds(C, dk, f.es, kMaxLevels, false).total > kLdsLimit ||
       bwd_chunk_lds(C, dk, f.es, kMaxLevels, true).total > kLdsLimit || P.lds_rev > kLdsLimit)
     return kESHAPE;
+  if (bwd_fused_shape(f.es == 2, C, dk) && 2 * bwd_fused_lds(C, dk, f.es, f.L).total <= kLdsLimit)
+    P.lds_fused = bwd_fused_lds(C, dk, f.es, f.L).total;
   if (f.BH == 0 || T == 0) {
     *p = P;
     return kOK;
