@@ -845,17 +845,34 @@ __global__ __launch_bounds__(256) void bwd_rev_tree(BwdArgs a, int D) {
   E* RT = reinterpret_cast<E*>(a.rnodes_t) + (bh * ng + x) * DD;
   const int e0 = band * 16 * D;                             // first element of the band
   const int RH = a.rhalves;
-  for (int e = threadIdx.x; e < 16 * D; e += 256) {
-    float acc = 0.f;
-    for (int64_t g = x; g < end; ++g) {
-      const float* sh = a.rpart + ((bh * ng + g) * RH * a.JG + i) * DD + e0 + e;
-      // the group's share, or the sum of its two halves' shares
-      const float v = RH == 2 ? sh[0] + sh[(size_t)a.JG * DD] : sh[0];
-      acc += __builtin_amdgcn_exp2f((float)(gp[g] - base)) * v;
+  const size_t hstride = (size_t)a.JG * DD;                 // from a group's first half share to its second
+  // four consecutive elements per thread; the shares are loaded four groups
+  // at a time, ahead of their weighted adds, which stay in group order
+  for (int e4 = threadIdx.x; e4 < 4 * D; e4 += 256) {
+    const int e = 4 * e4;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int64_t g0 = x; g0 < end; g0 += 4) {
+      f32x4 v[4];
+      float wg[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        wg[u] = 0.f;
+        if (g0 + u < end) {
+          const float* sh = a.rpart + ((bh * ng + g0 + u) * RH * a.JG + i) * DD + e0 + e;
+          // the group's share, or the sum of its two halves' shares
+          const f32x4 s0 = *reinterpret_cast<const f32x4*>(sh);
+          v[u] = RH == 2 ? s0 + *reinterpret_cast<const f32x4*>(sh + hstride) : s0;
+          wg[u] = __builtin_amdgcn_exp2f((float)(gp[g0 + u] - base));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (g0 + u < end) acc += wg[u] * v[u];
     }
-    const E val = EL::from_f32(acc);
-    R[e0 + e] = val;
-    tr[(e / D) * ld + e % D] = val;
+    store4<BF16>(R + e0 + e, acc);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) tr[((e + k) / D) * ld + (e + k) % D] = EL::from_f32(acc[k]);
   }
   __syncthreads();
   // R^T row j, columns band*16 .. band*16 + 15
