@@ -1804,13 +1804,13 @@ int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s) {
     const dim3 grid((unsigned)(group_tree_blocks(D) * p.BH));
     const int levels = bit_length(p.n_groups);
     if (levels <= 6)
-      hipLaunchKernelGGL((fwd_group_tree<BF16, 6>), grid, dim3(256), 0, s, fa, D);
+      hipLaunchKernelGGL((fwd_group_tree<BF16, 6>), grid, dim3(kTreeThreads), 0, s, fa, D);
     else if (levels <= 8)
-      hipLaunchKernelGGL((fwd_group_tree<BF16, 8>), grid, dim3(256), 0, s, fa, D);
+      hipLaunchKernelGGL((fwd_group_tree<BF16, 8>), grid, dim3(kTreeThreads), 0, s, fa, D);
     else if (levels <= 16)
-      hipLaunchKernelGGL((fwd_group_tree<BF16, 16>), grid, dim3(256), 0, s, fa, D);
+      hipLaunchKernelGGL((fwd_group_tree<BF16, 16>), grid, dim3(kTreeThreads), 0, s, fa, D);
     else
-      hipLaunchKernelGGL((fwd_group_tree<BF16, 32>), grid, dim3(256), 0, s, fa, D);
+      hipLaunchKernelGGL((fwd_group_tree<BF16, 32>), grid, dim3(kTreeThreads), 0, s, fa, D);
     ok = ok && hipGetLastError() == hipSuccess;
   }
   // the fused per-chunk kernel needs the key-side nodes first; the query-side

@@ -266,14 +266,16 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
 // group gate totals.  MAXJ bounds the carry levels (bit length of the group
 // count); the launcher picks the smallest instantiation that covers the
 // sequence.
-// Workgroups of 256 threads per (b,h): four state elements per thread.
-constexpr int kTreeVec = 2;   // consecutive state elements per thread of the group tree
+// Workgroups of kTreeThreads threads per (b,h), kTreeVec consecutive state
+// elements (one 16-byte load per group) per thread.
+constexpr int kTreeVec = 4;   // consecutive state elements per thread of the group tree
+constexpr int kTreeThreads = 256;
 typedef float ftv __attribute__((ext_vector_type(kTreeVec)));
 typedef unsigned short utv __attribute__((ext_vector_type(kTreeVec)));
-LA_HD constexpr int group_tree_blocks(int D) { return (D * D / kTreeVec + 255) / 256; }
+LA_HD constexpr int group_tree_blocks(int D) { return (D * D / kTreeVec + kTreeThreads - 1) / kTreeThreads; }
 
 template <bool BF16, int MAXJ>
-__global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
+__global__ __launch_bounds__(kTreeThreads) void fwd_group_tree(FwdArgs a, int D) {
   using EL = Elem<BF16>;
   using E = typename EL::T;
   constexpr int V = kTreeVec;   // consecutive state elements per thread: one vector load per group
@@ -281,7 +283,7 @@ __global__ __launch_bounds__(256) void fwd_group_tree(FwdArgs a, int D) {
   const int nblk = group_tree_blocks(D);
   const int64_t bh = blockIdx.x / nblk;
   const int blk = blockIdx.x % nblk;
-  const int q4 = blk * 256 + threadIdx.x;
+  const int q4 = blk * kTreeThreads + threadIdx.x;
   const bool valid = q4 < NQ;
   const int64_t ng = a.n_groups, nfg = a.n_full_groups;
   ftv slot[MAXJ];
@@ -1060,13 +1062,13 @@ int launch_fwd_impl(const FwdPlan& p, FwdArgs a, hipStream_t s, hipEvent_t const
     const dim3 grid((unsigned)(group_tree_blocks(D) * p.BH));
     const int levels = bit_length(p.n_groups);        // carry levels the walk can reach
     if (levels <= 6)
-      hipLaunchKernelGGL((fwd_group_tree<BF16, 6>), grid, dim3(256), 0, s, a, D);
+      hipLaunchKernelGGL((fwd_group_tree<BF16, 6>), grid, dim3(kTreeThreads), 0, s, a, D);
     else if (levels <= 8)
-      hipLaunchKernelGGL((fwd_group_tree<BF16, 8>), grid, dim3(256), 0, s, a, D);
+      hipLaunchKernelGGL((fwd_group_tree<BF16, 8>), grid, dim3(kTreeThreads), 0, s, a, D);
     else if (levels <= 16)
-      hipLaunchKernelGGL((fwd_group_tree<BF16, 16>), grid, dim3(256), 0, s, a, D);
+      hipLaunchKernelGGL((fwd_group_tree<BF16, 16>), grid, dim3(kTreeThreads), 0, s, a, D);
     else
-      hipLaunchKernelGGL((fwd_group_tree<BF16, 32>), grid, dim3(256), 0, s, a, D);
+      hipLaunchKernelGGL((fwd_group_tree<BF16, 32>), grid, dim3(kTreeThreads), 0, s, a, D);
     ok = ok && hipGetLastError() == hipSuccess;
   }
   ok = ok && hipFuncSetAttribute((const void*)fwd_chunk_output<BF16, C, D>,
