@@ -358,7 +358,8 @@ LA_API int loglinear_mamba2_fwd(const void* u, const la_mamba2_weights* weights,
   a.d_inner = p.d_inner; a.conv_dim = p.conv_dim; a.ld_zx = p.ld_zx;
   a.col_x = p.col_x; a.col_b = p.col_b; a.col_c = p.col_c; a.col_dt = p.col_dt; a.col_lam = p.col_lam;
   a.norm_slots = p.norm_slots; a.eps = p.eps;
-  const FwdArgs fa = fwd_args(p.op, a.q, a.k, a.v, a.log_a, a.lam, w + p.off_o, w + p.off_opws);
+  FwdArgs fa = fwd_args(p.op, a.q, a.k, a.v, a.log_a, a.lam, w + p.off_o, w + p.off_opws);
+  fa.qk_div = p.H / p.G;   // q and k are stored once per group of heads
   hipStream_t s = (hipStream_t)stream;
   const bool bf = p.dtype == kBF16;
   rc = bf ? launch_layer_pre_bf16(p, u, weights->in_proj, a, s) : launch_layer_pre_f32(p, u, weights->in_proj, a, s);

@@ -58,6 +58,10 @@ struct FwdArgs {
   int64_t n_full_groups;  // groups of G chunks of C tokens each
   int L;
   int lam_vec4;           // lambda rows of every full chunk are 16-byte aligned
+  // heads per q/k head group: q and k are [B][H / qk_div][T][d] and head h
+  // reads group h / qk_div (a layer whose heads share B and C); 0 or 1: one
+  // q and k per head
+  int qk_div;
   // final recurrent state (loglinear_fwd_state): [BH][st_S][D][D] fp32 slots
   // and [BH][st_S] scales; null when not asked for
   float* st_slots;
@@ -128,7 +132,8 @@ __global__ __launch_bounds__(64 * state_waves(D)) void fwd_chunk_states(FwdArgs 
   const int nch = (int)(nc - c0 < G ? nc - c0 : G);
   const int64_t t0 = c0 * C;
   const float* la_bh = a.log_a + bh * T;
-  const E* kb = reinterpret_cast<const E*>(a.k) + (bh * T + t0) * D;
+  const int64_t kbh = a.qk_div > 1 ? bh / a.qk_div : bh;   // k's head (group)
+  const E* kb = reinterpret_cast<const E*>(a.k) + (kbh * T + t0) * D;
   const E* vb = reinterpret_cast<const E*>(a.v) + (bh * T + t0) * D;
   uint4 pk[2][SH::NPF], pv[2][SH::NPF];
   auto prefetch = [&](int c, uint4 (&dk)[SH::NPF], uint4 (&dv)[SH::NPF]) {
@@ -400,7 +405,7 @@ __global__ __launch_bounds__(256) void fwd_final_state(FwdArgs a) {
         wk[tid] = __builtin_amdgcn_exp2f(g);
       }
       __syncthreads();
-      const E* kb = reinterpret_cast<const E*>(a.k) + (bh * T + s0) * D;
+      const E* kb = reinterpret_cast<const E*>(a.k) + ((a.qk_div > 1 ? bh / a.qk_div : bh) * T + s0) * D;
       const E* vb = reinterpret_cast<const E*>(a.v) + (bh * T + s0) * D;
       for (int j = 0; j < nk; ++j) {
         const float wj = wk[j];
@@ -561,8 +566,9 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   const int64_t tc = c * C;
   const int nv = FULL ? C : (int)(T - tc < C ? T - tc : C);
 
-  const E* qg = reinterpret_cast<const E*>(a.q) + (bh * T + tc) * D;
-  const E* kg = reinterpret_cast<const E*>(a.k) + (bh * T + tc) * D;
+  const int64_t qkbh = a.qk_div > 1 ? bh / a.qk_div : bh;  // q's and k's head (group)
+  const E* qg = reinterpret_cast<const E*>(a.q) + (qkbh * T + tc) * D;
+  const E* kg = reinterpret_cast<const E*>(a.k) + (qkbh * T + tc) * D;
   const E* vg = reinterpret_cast<const E*>(a.v) + (bh * T + tc) * D;
   E* og = reinterpret_cast<E*>(a.out) + (bh * T + tc) * D;
   const float* lg = a.lam + (bh * T + tc) * L;

@@ -370,8 +370,8 @@ constexpr int kSlabHeads = 16;      // x heads one slab can touch: 128 channels 
 // slab stages kHalo + 64 rows of its 16 granules of conv input in LDS (rows
 // before the first token are zero), then thread (granule g, block tb) forms
 // the conv + silu of tokens 4 tb .. 4 tb + 3 and stores them where the
-// operator reads them: v = dt x for x channels, q / k for every head of the
-// group for C / B channels.  The last slab writes the gates: lambda of head
+// operator reads them: v = dt x for x channels, q / k of the group (read by
+// all of its heads) for C / B channels.  The last slab writes the gates: lambda of head
 // h as one contiguous [tokens, L] block, and log_a.
 template <bool BF16>
 __global__ __launch_bounds__(256) void mamba2_prologue(LayerArgs a, int n_slabs) {
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(256) void mamba2_prologue(LayerArgs a, int n_slabs)
   const int64_t t0 = (int64_t)blockIdx.x * TOK;
   const int nt = (int)min((int64_t)TOK, a.T - t0);
   const T* zx = static_cast<const T*>(a.zx) + (size_t)b * a.T * a.ld_zx;
-  const int H = a.H, hpg = a.H / a.G;
+  const int H = a.H;
   const size_t bh0 = (size_t)b * H;
 
   if (slab == n_slabs) {
@@ -424,8 +424,7 @@ __global__ __launch_bounds__(256) void mamba2_prologue(LayerArgs a, int n_slabs)
   if (g >= ng) return;
   const int c0 = (g0 + g) * VEC;
   T* dst = nullptr;
-  size_t head_stride = 0;
-  int copies = 1, h = 0;
+  int h = 0;
   if (c0 < a.d_inner) {
     h = c0 / a.P;
     dst = static_cast<T*>(a.v) + ((bh0 + h) * a.T + t0) * a.P + c0 % a.P;
@@ -433,9 +432,7 @@ __global__ __launch_bounds__(256) void mamba2_prologue(LayerArgs a, int n_slabs)
     const bool isB = c0 < a.d_inner + a.G * a.N;
     const int cc = c0 - a.d_inner - (isB ? 0 : a.G * a.N);
     const int gi = cc / a.N;
-    dst = static_cast<T*>(isB ? a.k : a.q) + ((bh0 + (size_t)gi * hpg) * a.T + t0) * a.N + cc % a.N;
-    head_stride = (size_t)a.T * a.N;
-    copies = hpg;
+    dst = static_cast<T*>(isB ? a.k : a.q) + (((size_t)b * a.G + gi) * a.T + t0) * a.N + cc % a.N;
   }
   const int row_len = c0 < a.d_inner ? a.P : a.N;
   float w[VEC][kMaxConvTaps], bias[VEC];
@@ -472,7 +469,7 @@ __global__ __launch_bounds__(256) void mamba2_prologue(LayerArgs a, int n_slabs)
 #pragma unroll
       for (int e = 0; e < VEC; ++e) y[e] *= dt;
     }
-    for (int hh = 0; hh < copies; ++hh) store_vec<BF16, VEC>(dst + hh * head_stride + (size_t)i * row_len, y);
+    store_vec<BF16, VEC>(dst + (size_t)i * row_len, y);
   }
 }
 

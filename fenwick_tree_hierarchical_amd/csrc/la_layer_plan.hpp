@@ -32,7 +32,7 @@ struct LayerPlan {
   int col_z = 0, col_x = 0, col_b = 0, col_c = 0, col_dt = 0, col_lam = 0;
   size_t off_zx = 0, off_q = 0, off_k = 0, off_v = 0, off_loga = 0, off_lam = 0, off_o = 0, off_opws = 0;
   size_t off_taps = 0;  // the conv taps and bias as fp32, [conv_dim][kMaxConvTaps + 1]
-  size_t off_y = 0;     // the normalised gated output, over q (dead by then)
+  size_t off_y = 0;     // the normalised gated output, over v (dead by then)
   size_t ws_bytes = 0;
   FwdPlan op;           // the operator's plan
   bool empty() const { return M == 0; }
@@ -80,18 +80,19 @@ inline int plan_layer(int B, int64_t T, int d_model, int H, int P, int N, int G,
     *out = p;
     return kOK;
   }
-  const size_t M = (size_t)p.M, BHT = (size_t)B * H * (size_t)T;
+  const size_t M = (size_t)p.M, BHT = (size_t)B * H * (size_t)T, BGT = (size_t)B * G * (size_t)T;
   size_t off = 0;
   p.off_zx = off;   off = align_up(off + M * p.ld_zx * p.es, 256);
-  p.off_q = off;    off = align_up(off + BHT * N * p.es, 256);
-  p.off_k = off;    off = align_up(off + BHT * N * p.es, 256);
+  // q = C and k = B once per group of heads: the operator reads group h / (H / G)
+  p.off_q = off;    off = align_up(off + BGT * N * p.es, 256);
+  p.off_k = off;    off = align_up(off + BGT * N * p.es, 256);
   p.off_v = off;    off = align_up(off + BHT * P * p.es, 256);
   p.off_loga = off; off = align_up(off + BHT * 4, 256);
   p.off_lam = off;  off = align_up(off + BHT * L * 4, 256);
   p.off_o = off;    off = align_up(off + BHT * P * p.es, 256);
   p.off_opws = off; off = align_up(off + p.op.ws_bytes, 256);
   p.off_taps = off; off = align_up(off + (size_t)p.conv_dim * (kMaxConvTaps + 1) * 4, 256);
-  p.off_y = p.off_q;   // M * d_inner == B H T N because P == N
+  p.off_y = p.off_v;   // M * d_inner == B H T P
   p.ws_bytes = off;
   *out = p;
   return kOK;

@@ -330,7 +330,8 @@ LA_API int loglinear_gdn_fwd(const void* q, const void* k, const void* v, const 
  *            each of G equal channel groups (plus eps), times norm_w
  *   out    = y W_out^T
  * The operator runs with d_k = N, d_v = P (so N == P) and chunk size C, on
- * bfloat16 or float32 tensors as loglinear_fwd; projections accumulate in
+ * bfloat16 or float32 tensors as loglinear_fwd, with q and k held once per
+ * group of heads (every head of group g reads C_g and B_g); projections accumulate in
  * fp32 and store the element type; the conv, gates and norm run in fp32.
  *
  *   u        [B, T, d_model]       dtype, 16-byte aligned
