@@ -223,8 +223,8 @@ LA_API int loglinear_bwd(const void* q, const void* k, const void* v, const floa
   a.rnodes_in = p.n_chunks > 1 ? static_cast<void*>(w + P.off_rnodes_in) : nullptr;
   a.rpart = p.n_groups > 1 ? reinterpret_cast<float*>(w + P.off_rpart) : nullptr;
   a.rnodes = p.n_groups > 1 ? static_cast<void*>(w + P.off_rnodes) : nullptr;
-  a.rnodes_in_t = p.n_chunks > 1 ? static_cast<void*>(w + P.off_rnodes_in_t) : nullptr;
-  a.rnodes_t = p.n_groups > 1 ? static_cast<void*>(w + P.off_rnodes_t) : nullptr;
+  a.rnodes_in_t = p.n_chunks > 1 && P.off_rnodes_in_t ? static_cast<void*>(w + P.off_rnodes_in_t) : nullptr;
+  a.rnodes_t = p.n_groups > 1 && P.off_rnodes_t ? static_cast<void*>(w + P.off_rnodes_t) : nullptr;
   a.dcol = reinterpret_cast<float*>(w + P.off_dcol);
   a.T = T; a.n_chunks = p.n_chunks; a.n_groups = p.n_groups; a.L = L; a.JG = P.JG; a.rhalves = P.rhalves;
   hipStream_t s = (hipStream_t)stream;

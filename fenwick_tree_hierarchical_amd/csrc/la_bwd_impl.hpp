@@ -53,8 +53,8 @@ struct BwdArgs {
   void* rnodes_in;       // key side: block starting at chunk x inside a group, [BH][n_chunks][d_k][d_v]
   float* rpart;          // [BH][n_groups][rhalves][JG][d_k][d_v] fp32: a group's share of its group-level blocks
   void* rnodes;          // block starting at group x, [BH][n_groups][d_k][d_v]
-  void* rnodes_in_t;     // the same key-side nodes transposed, (d_v, d_k)
-  void* rnodes_t;
+  void* rnodes_in_t;     // the same key-side nodes transposed, (d_v, d_k), for the split key-side
+  void* rnodes_t;        // kernel; null where the fused kernel runs (it gathers them from R)
   float* dcol;           // [BH][T]: v_s . dv_s
   int64_t T;
   int64_t n_chunks;
@@ -102,6 +102,27 @@ __device__ __forceinline__ typename Elem<BF16>::Frag gather_col(const typename E
     return __builtin_bit_cast(bf16x8, f);
   } else {
     return tile[k0 * ld + col];
+  }
+}
+
+// The same fragment of a transposed D x D node from its row-major copy in
+// global memory (row `col` of node^T, k-slice k0 ..): unsigned byte offsets
+// from the node's (wave-uniform) base, so the loads take a scalar base.
+template <bool BF16, int D>
+__device__ __forceinline__ typename Elem<BF16>::Frag gather_node_col(const typename Elem<BF16>::T* node, int k0,
+                                                                     int col) {
+  using E = typename Elem<BF16>::T;
+  const unsigned char* b = reinterpret_cast<const unsigned char*>(node);
+  const unsigned o = (unsigned)((k0 * D + col) * (int)sizeof(E));
+  if constexpr (BF16) {
+    u16x8 f = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (D >= Elem<BF16>::kStep || k0 < D) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = *reinterpret_cast<const unsigned short*>(b + o + (unsigned)(e * D * 2));
+    }
+    return __builtin_bit_cast(bf16x8, f);
+  } else {
+    return *reinterpret_cast<const float*>(b + o);
   }
 }
 
@@ -554,6 +575,7 @@ __global__ __launch_bounds__(64 * state_waves(D)) void bwd_rev_states(BwdArgs a)
     }
   };
   const int nlev = LOG2G + a.JG;
+  const bool keep_t = a.rnodes_in_t != nullptr;   // R^T kept for the split key-side kernel
   for (int j = 1; j <= nlev; ++j) {
     const bool in_group = j <= LOG2G;
     if (!in_group && !((gam >> (j - LOG2G - 1)) & 1)) continue;
@@ -610,7 +632,7 @@ __global__ __launch_bounds__(64 * state_waves(D)) void bwd_rev_states(BwdArgs a)
           const auto gf = EL::template load_k<C>(GT + ng_ * lay.ld_t + (k0 ^ state_swz<C>(ng_)), k0);
           const auto qf = EL::template load_k<C>(QT + nq_ * lay.ld_t + (k0 ^ state_swz<C>(nq_)), k0);
           acc[h] = EL::mma(gf, qf, acc[h]);
-          acct[h] = EL::mma(qf, gf, acct[h]);
+          if (keep_t) acct[h] = EL::mma(qf, gf, acct[h]);
         }
       }
       __syncthreads();
@@ -618,7 +640,7 @@ __global__ __launch_bounds__(64 * state_waves(D)) void bwd_rev_states(BwdArgs a)
       if (last) {
         if (in_group) {
           flush(reinterpret_cast<E*>(a.rnodes_in) + (bh * nc + c0 + xs) * D * D,
-                reinterpret_cast<E*>(a.rnodes_in_t) + (bh * nc + c0 + xs) * D * D);
+                keep_t ? reinterpret_cast<E*>(a.rnodes_in_t) + (bh * nc + c0 + xs) * D * D : static_cast<E*>(nullptr));
         } else {
           flush(a.rpart + ((bh * ng + gam) * a.JG + (j - LOG2G - 1)) * D * D, static_cast<E*>(nullptr));
         }
@@ -740,6 +762,7 @@ __global__ __launch_bounds__(64 * state_waves(D)) void bwd_rev_states_staged(Bwd
 
   // this wave's tiles: one d_k block mb, d_v blocks nb(h)
   const int mb = w % DB;
+  const bool keep_t = a.rnodes_in_t != nullptr;    // R^T kept for the split key-side kernel
   f32x4 acc[TPW], acct[TPW];
 #pragma unroll
   for (int h = 0; h < TPW; ++h) acc[h] = acct[h] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -786,7 +809,7 @@ __global__ __launch_bounds__(64 * state_waves(D)) void bwd_rev_states_staged(Bwd
           const int nb = (w + h * NW) / DB;
           const Frag gf = swz_tr_frag<D>(gc, s * KST, 16 * nb, lane);
           acc[h] = EL::mma(gf, qf, acc[h]);
-          if (in_group) acct[h] = EL::mma(qf, gf, acct[h]);   // group shares are stored one way only
+          if (in_group && keep_t) acct[h] = EL::mma(qf, gf, acct[h]);   // group shares are stored one way only
         }
       }
       const bool last = in_group ? ((((cig + 1) & ((1 << (j - 1)) - 1)) == 0) || cig == nchg - 1) : ci == nch - 1;
@@ -795,12 +818,14 @@ __global__ __launch_bounds__(64 * state_waves(D)) void bwd_rev_states_staged(Bwd
         if (in_group) {
           const int xs = (cig >> (j - 1)) << (j - 1);
           bf16_t* R = reinterpret_cast<bf16_t*>(a.rnodes_in) + (bh * nc + cg0 + xs) * D * D;
-          bf16_t* RT = reinterpret_cast<bf16_t*>(a.rnodes_in_t) + (bh * nc + cg0 + xs) * D * D;
 #pragma unroll
           for (int h = 0; h < TPW; ++h) {
             const int nb = (w + h * NW) / DB;
             store4<true>(R + (16 * mb + lr) * D + 16 * nb + 4 * lq, acc[h]);
-            store4<true>(RT + (16 * nb + lr) * D + 16 * mb + 4 * lq, acct[h]);
+            if (keep_t) {
+              bf16_t* RT = reinterpret_cast<bf16_t*>(a.rnodes_in_t) + (bh * nc + cg0 + xs) * D * D;
+              store4<true>(RT + (16 * nb + lr) * D + 16 * mb + 4 * lq, acct[h]);
+            }
           }
         } else {
           float* P = share(j);
@@ -820,12 +845,258 @@ __global__ __launch_bounds__(64 * state_waves(D)) void bwd_rev_states_staged(Bwd
 }
 
 // ---------------------------------------------------------------------------
+// bwd_rev_states_cm: the nodes and shares of bwd_rev_states_staged (d = 64),
+// walking the half's chunks once instead of once per level.  A k-step's Q and
+// dout fragments are read from LDS once and serve every level the chunk takes
+// part in: each in-group level has its own R accumulators (R^T, where it is
+// kept, is stored from them), and up to kRevGroupSlots group levels one share
+// accumulator each (further group levels take another pass over the chunks).  A pass first writes the token weights
+// of all its levels to one table.  Each level adds its products in the order
+// of the level-by-level walk, from the same weights, so the results are the
+// same bits.
+template <int C, int D>
+__global__ __launch_bounds__(64 * state_waves(D)) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void bwd_rev_states_cm(BwdArgs a) {
+  using EL = Elem<true>;
+  using Frag = typename EL::Frag;
+  constexpr int NW = state_waves(D), NT = 64 * NW, DB = D / 16, HT = DB * DB, TPW = state_tiles_per_wave(D);
+  constexpr int G = state_group(D), GH = G / 2, LOG2G = cilog2(G), LOG2C = cilog2(C);
+  constexpr int KST = EL::kStep, KSC = C / KST;
+  constexpr int ROWB = 2 * D;                      // bytes per token row
+  constexpr int GS = kRevGroupSlots, NS = LOG2G + GS;   // weight slots: in-group levels, then group levels
+  constexpr int HR = GH * C;                       // token rows of a half
+  constexpr int KI = (NS * HR + NT - 1) / NT;      // weight-table entries per thread
+  constexpr RevStagedLds lay = rev_cm_lds(C, D, G);
+  static_assert(C % KST == 0 && D == 64 && GH >= 1 && TPW * NW == HT, "chunk-major rev-states shape");
+  static_assert(NW % DB == 0, "a wave's tiles share one d_k block");
+  static_assert(G <= NW, "one gate scan per wave");
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* Qt = smem + lay.q;
+  unsigned char* Gt = smem + lay.g;
+  float* b2s = reinterpret_cast<float*>(smem + lay.b2);   // gate prefixes of every chunk of the group
+  float* wts = reinterpret_cast<float*>(smem + lay.w);    // [NS][HR] token weights of the pass's levels
+
+  const int64_t ng = a.n_groups, nc = a.n_chunks, T = a.T;
+  const int64_t gidx = blockIdx.x >> 1;
+  const int half = blockIdx.x & 1;
+  const int64_t bh = gidx / ng, gam = gidx % ng;
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id(), lq = lane >> 4;
+  const int L = a.L, JG = a.JG;
+  const int64_t cg0 = gam * G;                                  // the group's first chunk
+  const int nchg = (int)(nc - cg0 < G ? nc - cg0 : G);          // chunks in the group
+  const int h0 = half * GH;                                     // in-group index of this half's first chunk
+  const int nch = nchg - h0 < GH ? nchg - h0 : GH;              // chunks in this half (<= 0: none)
+  // this half's share of group level j
+  auto share = [&](int j) { return a.rpart + (((bh * ng + gam) * 2 + half) * JG + (j - LOG2G - 1)) * D * D; };
+  if (nch <= 0) {
+    // the group ends inside its first half: this half's shares are zero
+    for (int j = LOG2G + 1; j <= LOG2G + JG; ++j) {
+      if (!((gam >> (j - LOG2G - 1)) & 1)) continue;
+      f32x4* P = reinterpret_cast<f32x4*>(share(j));
+      for (int i = tid; i < D * D / 4; i += NT) P[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
+  const int64_t t0 = (cg0 + h0) * C;
+  const int nrow = (int)(T - t0 < (int64_t)nch * C ? T - t0 : (int64_t)nch * C);   // rows inside the sequence
+  const unsigned char* qsrc = reinterpret_cast<const unsigned char*>(a.q) + (bh * T + t0) * ROWB;
+  const unsigned char* gsrc = reinterpret_cast<const unsigned char*>(a.dout) + (bh * T + t0) * ROWB;
+
+  // ---- this half's q and dout rows into LDS
+  if (nrow == HR) {
+    // 1 KB runs: lane l fills granule l mod GPR of row RPR ri + l / GPR with
+    // the logical granule that XORs to it
+    constexpr int GPR = ROWB / 16, RPR = 1024 / ROWB, RUNS = HR * ROWB / 1024;
+    static_assert((2 * RUNS) % NW == 0, "runs are dealt evenly over the waves");
+    const int lrow = lane / GPR, lg16 = lane % GPR;
+    const unsigned off0 = (unsigned)(lrow * ROWB + ((lg16 ^ (lrow & 7)) << 4));
+    const unsigned off1 = (unsigned)(lrow * ROWB + ((lg16 ^ ((RPR + lrow) & 7)) << 4));
+#pragma unroll
+    for (int k = 0; k < 2 * RUNS / NW; ++k) {
+      const int run = w + k * NW;                  // wave-uniform
+      const int t = run / RUNS, ri = run % RUNS;
+      const unsigned o = (RPR >= 8 || (ri & 1) == 0) ? off0 : off1;
+      __builtin_amdgcn_global_load_lds((t == 0 ? qsrc : gsrc) + (unsigned)(ri * 1024) + o,
+                                       (__attribute__((address_space(3))) void*)((t == 0 ? Qt : Gt) + ri * 1024),
+                                       16, 0, 0);
+    }
+  } else {
+    // a half that reaches the end of the sequence: granule copies, zeros past it
+    constexpr int GPR = ROWB / 16;
+    const int per = nch * C * GPR;
+    for (int i = tid; i < 2 * per; i += NT) {
+      const int t = i / per, rem = i % per, r = rem / GPR, g = rem % GPR;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (r < nrow) x = *reinterpret_cast<const uint4*>((t == 0 ? qsrc : gsrc) + (size_t)r * ROWB + g * 16);
+      *reinterpret_cast<uint4*>((t == 0 ? Qt : Gt) + swz_gran<D>(r, g)) = x;
+    }
+  }
+
+  // the group levels with work (the set bits of the group index), GS per pass
+  const int ngl = __popcll((unsigned long long)gam);
+  const int npass = ngl > GS ? (ngl + GS - 1) / GS : 1;
+  unsigned long long gbits = (unsigned long long)gam;          // the set bits not yet walked
+  int gl[GS];                                                  // this pass's group levels (0: none)
+  auto take_levels = [&]() {
+#pragma unroll
+    for (int g = 0; g < GS; ++g) {
+      gl[g] = gbits ? LOG2G + 1 + __builtin_ctzll(gbits) : 0;
+      gbits &= gbits - 1;
+    }
+  };
+  take_levels();
+  // level of weight slot sl in this pass (0: no level)
+  auto slot_level = [&](int sl, int pass) {
+    int j = 0;
+#pragma unroll
+    for (int g = 0; g < GS; ++g)
+      if (sl == LOG2G + g) j = gl[g];
+    return sl < LOG2G ? (pass == 0 ? sl + 1 : 0) : j;
+  };
+  // lambda of each of this thread's table entries, loaded with the rows
+  const float* lbase = a.lam + (bh * T + t0) * L + LOG2C;
+  float lamv[KI];
+  auto load_lambda = [&](int pass) {
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+      const int i = tid + k * NT, sl = i / HR, row = i % HR;
+      const int j = i < NS * HR ? slot_level(sl, pass) : 0;
+      lamv[k] = (j > 0 && row < nrow) ? lbase[(int64_t)row * L + j] : 0.f;
+    }
+  };
+  load_lambda(0);
+
+  const float* la_bh = a.log_a + bh * T;
+  if (w < nchg) chunk_gate_scan<C>(la_bh, (cg0 + w) * C, T, b2s + w * C);
+  __builtin_amdgcn_s_waitcnt(0);                   // this wave's direct loads have landed
+  __syncthreads();
+
+  // this wave's tiles: one d_k block mb, d_v blocks nb(h)
+  const int mb = w % DB;
+  const bool keep_t = a.rnodes_in_t != nullptr;    // R^T kept for the split key-side kernel
+  for (int pass = 0; pass < npass; ++pass) {
+    if (pass > 0) {
+      __syncthreads();                             // every wave is done with the last pass's table
+      take_levels();
+      load_lambda(pass);
+    }
+    // token weights: lambda of the level times the gate from the block (or
+    // group) start, zero outside the level's chunks and past the sequence
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+      const int i = tid + k * NT, sl = i / HR, row = i % HR;
+      if (i >= NS * HR || row >= nch * C) continue;
+      const int j = slot_level(sl, pass);
+      float wv = 0.f;
+      if (j > 0) {
+        const bool in_group = j <= LOG2G;
+        const int cig = h0 + row / C;
+        if (!in_group || ((cig >> (j - 1)) & 1)) {
+          const int xs = in_group ? ((cig >> (j - 1)) << (j - 1)) : 0;
+          float pre = 0.f;
+          for (int u = xs; u < cig; ++u) pre += b2s[u * C + C - 1];
+          if (row < nrow) wv = lamv[k] * __builtin_amdgcn_exp2f(b2s[h0 * C + row] + pre);
+        }
+      }
+      wts[i] = wv;
+    }
+    __syncthreads();
+
+    f32x4 ai[LOG2G][TPW], ag[GS][TPW];
+#pragma unroll
+    for (int h = 0; h < TPW; ++h) {
+#pragma unroll
+      for (int l = 0; l < LOG2G; ++l) ai[l][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int g = 0; g < GS; ++g) ag[g][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int ci = 0; ci < nch; ++ci) {
+      const int cig = h0 + ci;
+      const unsigned char* qc = Qt + ci * C * ROWB;
+      const unsigned char* gc = Gt + ci * C * ROWB;
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) {
+        i16x4 lo, hi;
+        swz_tr_halves<D>(qc, s * KST, 16 * mb, lane, lo, hi);
+        const bf16_t qv[8] = {(bf16_t)lo[0], (bf16_t)lo[1], (bf16_t)lo[2], (bf16_t)lo[3],
+                              (bf16_t)hi[0], (bf16_t)hi[1], (bf16_t)hi[2], (bf16_t)hi[3]};
+        Frag gf[TPW];
+#pragma unroll
+        for (int h = 0; h < TPW; ++h) gf[h] = swz_tr_frag<D>(gc, s * KST, 16 * ((w + h * NW) / DB), lane);
+        // the Q fragment weighted by slot sl's weights of this lane's eight tokens
+        auto weighted = [&](int sl) {
+          const float* wr = wts + sl * HR + ci * C + s * KST + 8 * lq;
+          const float4 w0 = *reinterpret_cast<const float4*>(wr);
+          const float4 w1 = *reinterpret_cast<const float4*>(wr + 4);
+          const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+          u16x8 qw;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qw[e] = EL::from_f32(EL::to_f32(qv[e]) * wv[e]);
+          return __builtin_bit_cast(Frag, qw);
+        };
+        if (pass == 0) {
+#pragma unroll
+          for (int l = 0; l < LOG2G; ++l) {
+            if (!((cig >> l) & 1)) continue;
+            const Frag qf = weighted(l);
+#pragma unroll
+            for (int h = 0; h < TPW; ++h) ai[l][h] = EL::mma(gf[h], qf, ai[l][h]);
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < GS; ++g) {
+          if (!gl[g]) continue;
+          const Frag qf = weighted(LOG2G + g);
+#pragma unroll
+          for (int h = 0; h < TPW; ++h) ag[g][h] = EL::mma(gf[h], qf, ag[g][h]);
+        }
+      }
+      const int lr = lane & 15;
+      if (pass == 0) {
+        // in-group blocks that end with this chunk
+#pragma unroll
+        for (int l = 0; l < LOG2G; ++l) {
+          if (!((cig >> l) & 1)) continue;
+          if (!((((cig + 1) & ((1 << l) - 1)) == 0) || cig == nchg - 1)) continue;
+          const int xs = (cig >> l) << l;
+          bf16_t* R = reinterpret_cast<bf16_t*>(a.rnodes_in) + (bh * nc + cg0 + xs) * D * D;
+#pragma unroll
+          for (int h = 0; h < TPW; ++h) {
+            const int nb = (w + h * NW) / DB;
+            store4<true>(R + (16 * mb + lr) * D + 16 * nb + 4 * lq, ai[l][h]);
+            // R^T: element i of the lane's four is row 16 nb + 4 lq + i, column 16 mb + lr
+            if (keep_t) {
+              bf16_t* RT = reinterpret_cast<bf16_t*>(a.rnodes_in_t) + (bh * nc + cg0 + xs) * D * D;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) RT[(16 * nb + 4 * lq + i) * D + 16 * mb + lr] = f32_to_bf16(ai[l][h][i]);
+            }
+            ai[l][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+      }
+    }
+    // this half's shares of the pass's group levels
+    const int lr = lane & 15;
+#pragma unroll
+    for (int g = 0; g < GS; ++g) {
+      if (!gl[g]) continue;
+      float* P = share(gl[g]);
+#pragma unroll
+      for (int h = 0; h < TPW; ++h) {
+        const int nb = (w + h * NW) / DB;
+        *reinterpret_cast<f32x4*>(P + (16 * mb + lr) * D + 16 * nb + 4 * lq) = ag[g][h];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // bwd_rev_tree: the key-side node of every block of groups that is the upper
 // half of its level block: it starts at group x >= 1 and spans 2^ctz(x)
 // groups; the sum of those groups' shares, each carried by the gate from the
 // block start to the group start.  One workgroup per band of 16 rows of one
-// node: the band is written as rows of R, and through LDS (rows padded by
-// one 4-byte word) as 16-element runs of the columns of R^T.
+// node: the band is written as rows of R and, where R^T is kept, through LDS
+// (rows padded by one 4-byte word) as 16-element runs of the columns of R^T.
 template <bool BF16>
 __global__ __launch_bounds__(256) void bwd_rev_tree(BwdArgs a, int D) {
   using EL = Elem<BF16>;
@@ -842,7 +1113,6 @@ __global__ __launch_bounds__(256) void bwd_rev_tree(BwdArgs a, int D) {
   const double* gp = a.gprefix + bh * (ng + 1);
   const double base = gp[x];
   E* R = reinterpret_cast<E*>(a.rnodes) + (bh * ng + x) * DD;
-  E* RT = reinterpret_cast<E*>(a.rnodes_t) + (bh * ng + x) * DD;
   const int e0 = band * 16 * D;                             // first element of the band
   const int RH = a.rhalves;
   const size_t hstride = (size_t)a.JG * DD;                 // from a group's first half share to its second
@@ -874,8 +1144,10 @@ __global__ __launch_bounds__(256) void bwd_rev_tree(BwdArgs a, int D) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) tr[((e + k) / D) * ld + (e + k) % D] = EL::from_f32(acc[k]);
   }
+  if (!a.rnodes_t) return;                                  // workgroup-uniform
   __syncthreads();
   // R^T row j, columns band*16 .. band*16 + 15
+  E* RT = reinterpret_cast<E*>(a.rnodes_t) + (bh * ng + x) * DD;
   for (int e = threadIdx.x; e < 16 * D; e += 256) {
     const int j = e / 16, r = e % 16;
     RT[(int64_t)j * D + band * 16 + r] = tr[r * ld + j];
@@ -1559,19 +1831,27 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
       const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(o64 >> 32), el);
       return (int64_t)(((uint64_t)hi << 32) | lo);
     };
-    auto load_node = [&](int li, Frag (&rf)[KSD][NCB], Frag (&rt)[KSD][NCB]) {
+    // node of entry li; its rows (d_k) of this wave's columns as fragments,
+    // and the rows of R^T (d_v) gathered from the columns of R
+    auto node_ptr = [&](int li) {
       int el;
       const int64_t o = node_off(li, el);
-      const E* R = (el >= 32 ? reinterpret_cast<const E*>(a.rnodes) : reinterpret_cast<const E*>(a.rnodes_in)) + o;
-      const E* RT = (el >= 32 ? reinterpret_cast<const E*>(a.rnodes_t) : reinterpret_cast<const E*>(a.rnodes_in_t)) + o;
+      return (el >= 32 ? reinterpret_cast<const E*>(a.rnodes) : reinterpret_cast<const E*>(a.rnodes_in)) + o;
+    };
+    auto load_rows = [&](const E* R, Frag (&rf)[KSD][NCB]) {
 #pragma unroll
       for (int s2 = 0; s2 < KSD; ++s2) {
         const int k0 = s2 * KST + lq * KPL;
 #pragma unroll
-        for (int n = 0; n < NCB; ++n) {
-          rf[s2][n] = EL::template load_k<D>(R + (16 * (cb0 + n) + lr) * D + k0, k0);
-          rt[s2][n] = EL::template load_k<D>(RT + (16 * (cb0 + n) + lr) * D + k0, k0);
-        }
+        for (int n = 0; n < NCB; ++n) rf[s2][n] = EL::template load_k<D>(R + (16 * (cb0 + n) + lr) * D + k0, k0);
+      }
+    };
+    auto gather_cols = [&](const E* R, Frag (&rt)[KSD][NCB]) {
+#pragma unroll
+      for (int s2 = 0; s2 < KSD; ++s2) {
+        const int k0 = s2 * KST + lq * KPL;
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) rt[s2][n] = gather_node_col<BF16, D>(R, k0, 16 * (cb0 + n) + lr);
       }
     };
     float g2 = 0.f;                               // log2 gate from the chunk end to the block start
@@ -1593,11 +1873,8 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
       }
     }
     if (owner) {
-      constexpr int NPRE = 1;
-      Frag rf[NPRE][KSD][NCB], rt[NPRE][KSD][NCB];
-#pragma unroll
-      for (int u = 0; u < NPRE; ++u)
-        if (u < n_lev) load_node(u, rf[u], rt[u]);
+      Frag rf[KSD][NCB];                         // rows of the next level's node, loaded ahead
+      if (n_lev > 0) load_rows(node_ptr(0), rf);
       f32x4 ak[QB][NCB], av[QB][NCB];
 #pragma unroll
       for (int kb = 0; kb < QB; ++kb)
@@ -1630,44 +1907,55 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
           }
         }
       }
-      auto contract = [&](int li, const Frag (&rfr)[KSD][NCB], const Frag (&rtr)[KSD][NCB]) {
+      // per level: dk += gate R v over all row blocks (the R^T gathers of the
+      // level in flight), the next level's rows loaded, then dv += gate R^T k;
+      // each accumulator takes its terms in the order of the split kernel
+      for (int li = 0; li < n_lev; ++li) {
+        const E* R = node_ptr(li);
+        Frag rt[KSD][NCB];
+        gather_cols(R, rt);
         const int el = __builtin_amdgcn_readlane(ent, li);
         const float f = __builtin_amdgcn_exp2f(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g2), el)));
 #pragma unroll
         for (int kb = 0; kb < QB; ++kb) {
           const int skr = 16 * kb + lr;
-          f32x4 tk[NCB], tv[NCB];
+          f32x4 tk[NCB];
 #pragma unroll
-          for (int n = 0; n < NCB; ++n) tk[n] = tv[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int n = 0; n < NCB; ++n) tk[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s2 = 0; s2 < KSD; ++s2) {
             const int k0 = s2 * KST + lq * KPL;
             const auto vf = EL::template load_k<D>(Vs + skr * lay.ld_row + k0, k0);
-            const auto kf = EL::template load_k<D>(Ks + skr * lay.ld_row + k0, k0);
 #pragma unroll
-            for (int n = 0; n < NCB; ++n) {
-              tk[n] = EL::mma(rfr[s2][n], vf, tk[n]);
-              tv[n] = EL::mma(rtr[s2][n], kf, tv[n]);
-            }
+            for (int n = 0; n < NCB; ++n) tk[n] = EL::mma(rf[s2][n], vf, tk[n]);
           }
           const float wk = f * e2c[skr];
 #pragma unroll
           for (int n = 0; n < NCB; ++n)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              ak[kb][n][i] += wk * tk[n][i];
-              av[kb][n][i] += wk * tv[n][i];
-            }
+            for (int i = 0; i < 4; ++i) ak[kb][n][i] += wk * tk[n][i];
           __builtin_amdgcn_sched_barrier(0);
         }
-      };
-      for (int base = 0; base < n_lev; base += NPRE) {
+        if (li + 1 < n_lev) load_rows(node_ptr(li + 1), rf);
 #pragma unroll
-        for (int u = 0; u < NPRE; ++u) {
-          const int li = base + u;
-          if (li >= n_lev) break;
-          contract(li, rf[u], rt[u]);
-          if (li + NPRE < n_lev) load_node(li + NPRE, rf[u], rt[u]);
+        for (int kb = 0; kb < QB; ++kb) {
+          const int skr = 16 * kb + lr;
+          f32x4 tv[NCB];
+#pragma unroll
+          for (int n = 0; n < NCB; ++n) tv[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s2 = 0; s2 < KSD; ++s2) {
+            const int k0 = s2 * KST + lq * KPL;
+            const auto kf = EL::template load_k<D>(Ks + skr * lay.ld_row + k0, k0);
+#pragma unroll
+            for (int n = 0; n < NCB; ++n) tv[n] = EL::mma(rt[s2][n], kf, tv[n]);
+          }
+          const float wk = f * e2c[skr];
+#pragma unroll
+          for (int n = 0; n < NCB; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) av[kb][n][i] += wk * tv[n][i];
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       // this wave's share of v_s . dv_s, then the rows of dk and dv
@@ -1826,7 +2114,14 @@ int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s) {
     ok = ok && hipGetLastError() == hipSuccess;
   }
   if (p.n_chunks > 1) {
-    if constexpr (rev_staged_fits(BF16, C, D, G)) {
+    if constexpr (rev_cm_fits(BF16, C, D, G)) {
+      constexpr int lds = rev_cm_lds(C, D, G).total;
+      ok = ok && hipFuncSetAttribute((const void*)bwd_rev_states_cm<C, D>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess;
+      if (!ok) return kEHIP;
+      hipLaunchKernelGGL((bwd_rev_states_cm<C, D>), dim3((unsigned)(2 * p.n_groups * p.BH)),
+                         dim3(64 * state_waves(D)), lds, s, a);
+    } else if constexpr (rev_staged_fits(BF16, C, D, G)) {
       constexpr int lds = rev_staged_lds(C, D, G).total;
       ok = ok && hipFuncSetAttribute((const void*)bwd_rev_states_staged<C, D>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess;

@@ -141,6 +141,19 @@ LA_HD constexpr RevStagedLds rev_staged_lds(int C, int D, int G) {
 LA_HD constexpr bool rev_staged_fits(bool bf16, int C, int D, int G) {
   return bf16 && D >= 64 && C >= 32 && G >= 2 && 2 * rev_staged_lds(C, D, G).total <= kLdsLimit;
 }
+// The chunk-major walk of the same kernel (d = 64): the weight buffers become
+// one table of the in-group levels and kRevGroupSlots group levels.
+constexpr int kRevGroupSlots = 3;
+LA_HD constexpr RevStagedLds rev_cm_lds(int C, int D, int G) {
+  RevStagedLds o = rev_staged_lds(C, D, G);
+  int log2g = 0;
+  for (int g = G; g > 1; g >>= 1) ++log2g;
+  o.total = o.w + (log2g + kRevGroupSlots) * (G / 2) * C * 4;
+  return o;
+}
+LA_HD constexpr bool rev_cm_fits(bool bf16, int C, int D, int G) {
+  return rev_staged_fits(bf16, C, D, G) && D == 64 && 2 * rev_cm_lds(C, D, G).total <= kLdsLimit;
+}
 
 struct BwdPlan {
   FwdPlan f;                 // the forward structure over (k := v, v := k): nodes for dq
@@ -149,7 +162,9 @@ struct BwdPlan {
   int lds_dq = 0, lds_dkv = 0, lds_rev = 0;
   int lds_fused = 0;         // > 0: the fused per-chunk kernel runs (two workgroups fit per CU)
   size_t off_rnodes_in = 0, off_rpart = 0, off_rnodes = 0, off_dcol = 0, ws_bytes = 0;
-  size_t off_rnodes_in_t = 0, off_rnodes_t = 0;   // the same nodes transposed, (d_v, d_k)
+  // the same nodes transposed, (d_v, d_k), for the split key-side kernel
+  // (the fused kernel gathers them from the columns of R); 0: not kept
+  size_t off_rnodes_in_t = 0, off_rnodes_t = 0;
 };
 
 // Shape checks and the plan of the backward.  The forward's envelope, with
@@ -180,12 +195,16 @@ inline int plan_bwd(int B, int H, int64_t T, int dk, int dv, int C, int dtype, i
   size_t off = f.ws_bytes;
   if (f.n_chunks > 1) {
     P.off_rnodes_in = off;   off = align_up(off + (size_t)f.BH * f.n_chunks * DD * f.es, 256);
-    P.off_rnodes_in_t = off; off = align_up(off + (size_t)f.BH * f.n_chunks * DD * f.es, 256);
+    if (!P.lds_fused) {
+      P.off_rnodes_in_t = off; off = align_up(off + (size_t)f.BH * f.n_chunks * DD * f.es, 256);
+    }
   }
   if (f.n_groups > 1) {
     P.off_rpart = off;  off = align_up(off + (size_t)f.BH * f.n_groups * P.rhalves * P.JG * DD * 4, 256);
     P.off_rnodes = off;   off = align_up(off + (size_t)f.BH * f.n_groups * DD * f.es, 256);
-    P.off_rnodes_t = off; off = align_up(off + (size_t)f.BH * f.n_groups * DD * f.es, 256);
+    if (!P.lds_fused) {
+      P.off_rnodes_t = off; off = align_up(off + (size_t)f.BH * f.n_groups * DD * f.es, 256);
+    }
   }
   P.off_dcol = off; off = align_up(off + (size_t)f.BH * T * 4, 256);
   P.ws_bytes = off;

@@ -72,6 +72,23 @@ int main() {
         CHECK(r.qt + D * r.ld_t * es <= r.gt && r.gt + D * r.ld_t * es <= r.b2 && r.b2 + G * C * 4 <= r.w &&
                   r.w + C * 4 <= r.total,
               "rev C=%d D=%d es=%d", C, D, es);
+        // the staged and chunk-major key-side kernels: both row tiles, the gate
+        // prefixes and the weights in order, two workgroups per CU where used
+        if (es == 2 && rev_staged_fits(true, C, D, G)) {
+          const RevStagedLds st = rev_staged_lds(C, D, G);
+          const int rows = (G / 2) * C * 2 * D;
+          CHECK(st.q == 0 && st.g == rows && st.b2 == 2 * rows && st.w == st.b2 + G * C * 4 &&
+                    st.total == st.w + 2 * (G / 2) * C * 4 && 2 * st.total <= kLdsLimit,
+                "staged rev C=%d D=%d", C, D);
+          if (rev_cm_fits(true, C, D, G)) {
+            int log2g = 0;
+            for (int g = G; g > 1; g >>= 1) ++log2g;
+            const RevStagedLds cm = rev_cm_lds(C, D, G);
+            CHECK(cm.q == st.q && cm.g == st.g && cm.b2 == st.b2 && cm.w == st.w &&
+                      cm.total == cm.w + (log2g + kRevGroupSlots) * (G / 2) * C * 4 && 2 * cm.total <= kLdsLimit,
+                  "chunk-major rev C=%d D=%d", C, D);
+          }
+        }
         for (long long T : {1LL, 15LL, 64LL, 1000LL, 4097LL, 16384LL, 131072LL}) {
           BwdPlan p;
           const int dt = es == 2 ? kBF16 : kF32;
@@ -80,17 +97,33 @@ int main() {
           const FwdPlan& f = p.f;
           const size_t DD = (size_t)D * D;
           size_t prev = f.ws_bytes;
+          // the transposed nodes are kept only for the split key-side kernel
+          const bool keep_t = p.lds_fused == 0;
+          CHECK(p.rhalves == (rev_staged_fits(es == 2, C, D, f.G) ? 2 : 1), "T=%lld C=%d D=%d", T, C, D);
           if (f.n_chunks > 1) {
             CHECK(p.off_rnodes_in == prev && p.off_rnodes_in % 256 == 0, "T=%lld C=%d D=%d", T, C, D);
-            CHECK(p.off_rnodes_in_t >= p.off_rnodes_in + f.BH * f.n_chunks * DD * f.es, "T=%lld", T);
-            prev = p.off_rnodes_in_t + f.BH * f.n_chunks * DD * f.es;
+            prev = p.off_rnodes_in + f.BH * f.n_chunks * DD * f.es;
+            if (keep_t) {
+              CHECK(p.off_rnodes_in_t >= prev && p.off_rnodes_in_t % 256 == 0, "T=%lld", T);
+              prev = p.off_rnodes_in_t + f.BH * f.n_chunks * DD * f.es;
+            } else {
+              CHECK(p.off_rnodes_in_t == 0, "T=%lld C=%d D=%d", T, C, D);
+            }
           }
           if (f.n_groups > 1) {
             CHECK(p.JG == bit_length(f.n_groups - 1) && p.off_rpart >= prev, "T=%lld", T);
-            CHECK(p.off_rnodes >= p.off_rpart + f.BH * f.n_groups * p.JG * DD * 4, "T=%lld", T);
-            CHECK(p.off_rnodes_t >= p.off_rnodes + f.BH * f.n_groups * DD * f.es, "T=%lld", T);
-            prev = p.off_rnodes_t + f.BH * f.n_groups * DD * f.es;
+            CHECK(p.off_rnodes >= p.off_rpart + f.BH * f.n_groups * p.rhalves * p.JG * DD * 4, "T=%lld", T);
+            prev = p.off_rnodes + f.BH * f.n_groups * DD * f.es;
+            if (keep_t) {
+              CHECK(p.off_rnodes_t >= prev && p.off_rnodes_t % 256 == 0, "T=%lld", T);
+              prev = p.off_rnodes_t + f.BH * f.n_groups * DD * f.es;
+            } else {
+              CHECK(p.off_rnodes_t == 0, "T=%lld C=%d D=%d", T, C, D);
+            }
           }
+          // the workspace query (L unknown: planned for the most levels) covers this plan
+          BwdPlan q;
+          CHECK(plan_bwd(2, 3, T, D, D, C, dt, -1, &q) == kOK && q.ws_bytes >= p.ws_bytes, "T=%lld C=%d D=%d", T, C, D);
           CHECK(p.off_dcol >= prev && p.off_dcol % 256 == 0, "T=%lld", T);
           CHECK(p.ws_bytes >= p.off_dcol + (size_t)f.BH * T * 4, "T=%lld", T);
           // every group level a key-side block can use has a share slot

@@ -141,6 +141,34 @@ def test_deterministic():
         assert np.array_equal(a[n], b[n]), n
 
 
+@pytest.mark.parametrize("d", [64, 32])
+def test_split_key_side_matches_fused(d):
+    """Lambda with levels no key reaches (L = 32, the most accepted) makes the
+    fused per-chunk kernel's LDS plan too large at C = 64, so the same problem
+    runs through the split pair, whose key side reads the transposed nodes the
+    key-side node kernels keep for it (the fused kernel gathers them from the
+    columns of R).  dq, dk, dv and the used levels of dlambda are the same bits
+    as the fused run, the extra levels' gradients are zero, d log_a agrees to
+    rounding (its row terms add the levels in other groups), and the run
+    matches the oracle."""
+    dev = need_gpu()
+    T, C = 4096 + 64 * 5 + 11, 64
+    x, dout = case(T, d, "bf16", "weak_decay", seed=5)
+    L0 = x["lam"].shape[-1]
+    a = gpu_bwd(x, dout, C, dev)
+    g = torch.Generator().manual_seed(6)
+    extra = torch.rand(*x["lam"].shape[:-1], 32 - L0, generator=g, dtype=x["lam"].dtype) + 0.5
+    x32 = dict(x, lam=torch.cat([x["lam"], extra], dim=-1).contiguous())
+    b = gpu_bwd(x32, dout, C, dev)
+    for n in ("dq", "dk", "dv"):
+        assert np.array_equal(a[n], b[n]), n
+    assert np.array_equal(a["dlam"], b["dlam"][..., :L0])
+    assert np.all(b["dlam"][..., L0:] == 0.0)
+    scale = np.abs(a["dlog_a"]).max()
+    assert np.allclose(a["dlog_a"], b["dlog_a"], rtol=1e-5, atol=1e-6 * scale)
+    check(x32, dout, C, "bf16", dev, f"split key side d={d} L=32")
+
+
 # --------------------------------------------------------------- full size
 def test_train_16k_full_size_sampled():
     """All 128 heads of the training shape: the gradients at sampled query and
