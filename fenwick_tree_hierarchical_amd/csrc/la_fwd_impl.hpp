@@ -532,7 +532,11 @@ __device__ __forceinline__ bf16x8 swz_tr_frag(const unsigned char* tile, int k0,
 // (V^T P^T and node Q^T) a lane holds one query row and four consecutive
 // output columns, so each row weight is one value per lane and each output
 // row slice is one contiguous store.
-template <bool BF16, int C, int D, bool FULL>
+//
+// VL (late V): the level contractions run before P V, and V is loaded into
+// the Q tile once every wave is past its Q reads, so the tiles take one 32 KB
+// buffer less (C = d = 128, where that lets two workgroups share a CU).
+template <bool BF16, int C, int D, bool FULL, bool VL = false>
 __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned char* smem, int64_t item) {
   using SH = ChunkShape<BF16, C, D>;
   using EL = Elem<BF16>;
@@ -543,7 +547,7 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   constexpr int G = state_group(D);
   constexpr int LOG2C = cilog2(C), LOG2G = cilog2(G);
   const int L = a.L;
-  const OutLds lay = output_lds(C, D, sizeof(E), L);
+  const OutLds lay = VL ? output_lds_vlate(C, D, sizeof(E), L) : output_lds(C, D, sizeof(E), L);
   E* Qs = reinterpret_cast<E*>(smem + lay.q);
   E* Ks = reinterpret_cast<E*>(smem + lay.k);
   E* Vs = reinterpret_cast<E*>(smem + lay.v);
@@ -553,6 +557,8 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   float* e2c = reinterpret_cast<float*>(smem + lay.e2);
 
   constexpr bool DIRECT = output_direct(C, D, sizeof(E));
+  static_assert(!VL || (DIRECT && NW * NCB == DB), "late V: direct tiles, every wave owns output columns");
+  constexpr int NTL = VL ? 2 : 3;                  // tiles loaded with the chunk: Q, K (and V)
   const unsigned char* Qt = smem + lay.q;         // direct-load tiles (swizzled rows)
   const unsigned char* Kt = smem + lay.k;
   const unsigned char* Vt = smem + lay.v;
@@ -587,12 +593,12 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
       // row's low three bits are (RPR ri + l / GPR) mod 8, so the lane's source
       // offset inside a run is the same for every run when RPR >= 8 and
       // alternates with ri when RPR = 4.
-      static_assert((3 * RUNS) % NW == 0, "runs are dealt evenly over the waves");
+      static_assert((NTL * RUNS) % NW == 0, "runs are dealt evenly over the waves");
       const int lrow = lane / GPR, lg16 = lane % GPR;
       const unsigned off0 = (unsigned)(lrow * ROWB + ((lg16 ^ (lrow & 7)) << 4));
       const unsigned off1 = (unsigned)(lrow * ROWB + ((lg16 ^ ((RPR + lrow) & 7)) << 4));
 #pragma unroll
-      for (int k = 0; k < 3 * RUNS / NW; ++k) {
+      for (int k = 0; k < NTL * RUNS / NW; ++k) {
         const int run = w + k * NW;                  // wave-uniform
         const int t = run / RUNS, ri = run % RUNS;
         const E* src = t == 0 ? qg : (t == 1 ? kg : vg);
@@ -618,7 +624,7 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
     } else {
       // the partial last chunk: element copies, zeros past the sequence
       const E* srcs[3] = {qg, kg, vg};
-      for (int i = tid; i < 3 * C * GPR; i += SH::NT) {
+      for (int i = tid; i < NTL * C * GPR; i += SH::NT) {
         const int t = i / (C * GPR), rem = i % (C * GPR), r = rem / GPR, g = rem % GPR;
         uint4 x = make_uint4(0, 0, 0, 0);
         if (r < nv) x = *reinterpret_cast<const uint4*>(srcs[t] + (unsigned)(r * D + g * 8));
@@ -888,6 +894,7 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
   for (int rb = 0; rb < QB; ++rb)
 #pragma unroll
     for (int n = 0; n < NCB; ++n) acc[rb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (!VL) {
   // V^T fragments (row d_v, a k-slice of keys) gathered from row-major V
   Frag vf[SH::KSC][NCB];
 #pragma unroll
@@ -927,6 +934,7 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
       for (int n = 0; n < NCB; ++n) acc[rb][n] = EL::mma(vf[s][n], pb, acc[rb][n]);
     }
     __builtin_amdgcn_sched_barrier(0);
+  }
   }
 
   // ---- occupied levels above the chunk: O += diag(lambda * gate) Q node^T,
@@ -994,6 +1002,76 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
     }
   }
 
+  if constexpr (VL) {
+    // ---- V into the Q tile, then O^T += V^T P^T
+    __syncthreads();                               // every wave is past its Q reads
+    if (FULL) {
+      constexpr int ROWB = 2 * D, GPR = ROWB / 16, RPR = 1024 / ROWB, RUNS = C * ROWB / 1024;
+      static_assert(RUNS % NW == 0, "runs are dealt evenly over the waves");
+      const int lrow = lane / GPR, lg16 = lane % GPR;
+      const unsigned off0 = (unsigned)(lrow * ROWB + ((lg16 ^ (lrow & 7)) << 4));
+      const unsigned off1 = (unsigned)(lrow * ROWB + ((lg16 ^ ((RPR + lrow) & 7)) << 4));
+#pragma unroll
+      for (int k = 0; k < RUNS / NW; ++k) {
+        const int ri = w + k * NW;                 // wave-uniform
+        const unsigned o = (RPR >= 8 || (ri & 1) == 0) ? off0 : off1;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char*>(vg) + (unsigned)(ri * 1024) + o,
+                                         (__attribute__((address_space(3))) void*)(smem + lay.v + ri * 1024),
+                                         16, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0);               // this wave's direct loads have landed
+    } else {
+      constexpr int GPR = 2 * D / 16;
+      for (int i = tid; i < C * GPR; i += SH::NT) {
+        const int r = i / GPR, g = i % GPR;
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (r < nv) x = *reinterpret_cast<const uint4*>(vg + (unsigned)(r * D + g * 8));
+        *reinterpret_cast<uint4*>(smem + lay.v + swz_gran<D>(r, g)) = x;
+      }
+    }
+    __syncthreads();
+    // V^T fragments (row d_v, a k-slice of keys) gathered from row-major V
+    Frag vf[SH::KSC][NCB];
+  #pragma unroll
+    for (int s = 0; s < SH::KSC; ++s) {
+      const int k0 = s * KST + lq * KPL;
+  #pragma unroll
+      for (int n = 0; n < NCB; ++n) {
+        const int dv = 16 * (cb0 + n) + lr;
+        if constexpr (DIRECT) {
+          // C >= 32 here: every k-slice lies inside the chunk
+          vf[s][n] = swz_tr_frag<D>(Vt, s * KST, 16 * (cb0 + n), lane);
+        } else if constexpr (BF16) {
+          u16x8 f = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+          if (C >= KST || k0 < C) {
+            const unsigned short* vcol = reinterpret_cast<const unsigned short*>(Vs) + dv;
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = vcol[(k0 + e) * lay.ld_v];
+          }
+          vf[s][n] = __builtin_bit_cast(Frag, f);
+        } else {
+          vf[s][n] = Vs[k0 * lay.ld_v + dv];
+        }
+      }
+    }
+    // O^T = V^T P^T over keys 0 .. 16 rb + 15 of each row block
+  #pragma unroll
+    for (int rb = 0; rb < QB; ++rb) {
+  #pragma unroll
+      for (int s = 0; s < SH::KSC; ++s) {
+        if (s * KST > 16 * rb + 15) break;
+        const int k0 = s * KST + lq * KPL;
+        Frag pb;
+        if (k0 / 16 <= rb) pb = EL::load(Ps + (16 * rb + lr) * lay.ld_p + k0);
+        else if constexpr (BF16) pb = __builtin_bit_cast(Frag, u16x8{0, 0, 0, 0, 0, 0, 0, 0});
+        else pb = 0.f;
+  #pragma unroll
+        for (int n = 0; n < NCB; ++n) acc[rb][n] = EL::mma(vf[s][n], pb, acc[rb][n]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
   // ---- store: four consecutive output columns of one row per lane and block
 #pragma unroll
   for (int rb = 0; rb < QB; ++rb) {
@@ -1039,6 +1117,18 @@ void fwd_chunk_output(FwdArgs a) {
   else chunk_output_body<BF16, C, D, false>(a, smem, item);
 }
 
+// The late-V output kernel (bfloat16, C = d = 128): two workgroups per CU,
+// so the register budget of four waves per SIMD.
+template <bool BF16, int C, int D>
+__global__ __launch_bounds__(64 * output_waves(C)) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void fwd_chunk_output_vlate(FwdArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int64_t item = xcd_item(blockIdx.x, gridDim.x);
+  const int64_t c = (uint32_t)item % (uint32_t)a.n_chunks;
+  if ((c + 1) * C <= a.T) chunk_output_body<BF16, C, D, true, true>(a, smem, item);
+  else chunk_output_body<BF16, C, D, false, true>(a, smem, item);
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launch of the stages for one (dtype, C, D) instantiation.
 template <bool BF16, int C, int D>
@@ -1077,13 +1167,28 @@ int launch_fwd_impl(const FwdPlan& p, FwdArgs a, hipStream_t s, hipEvent_t const
       hipLaunchKernelGGL((fwd_group_tree<BF16, 32>), grid, dim3(kTreeThreads), 0, s, a, D);
     ok = ok && hipGetLastError() == hipSuccess;
   }
-  ok = ok && hipFuncSetAttribute((const void*)fwd_chunk_output<BF16, C, D>,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_out) == hipSuccess;
-  if (!ok) return kEHIP;
-  mark();
-  hipLaunchKernelGGL((fwd_chunk_output<BF16, C, D>), dim3((unsigned)(p.n_chunks * p.BH)),
-                     dim3(ChunkShape<BF16, C, D>::NT), p.lds_out, s, a);
-  ok = ok && hipGetLastError() == hipSuccess;
+  bool launched = false;
+  if constexpr (output_vlate_shape(C, D, sizeof(E))) {
+    if (p.lds_out_vlate > 0) {
+      ok = ok && hipFuncSetAttribute((const void*)fwd_chunk_output_vlate<BF16, C, D>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_out_vlate) == hipSuccess;
+      if (!ok) return kEHIP;
+      mark();
+      hipLaunchKernelGGL((fwd_chunk_output_vlate<BF16, C, D>), dim3((unsigned)(p.n_chunks * p.BH)),
+                         dim3(ChunkShape<BF16, C, D>::NT), p.lds_out_vlate, s, a);
+      ok = ok && hipGetLastError() == hipSuccess;
+      launched = true;
+    }
+  }
+  if (!launched) {
+    ok = ok && hipFuncSetAttribute((const void*)fwd_chunk_output<BF16, C, D>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_out) == hipSuccess;
+    if (!ok) return kEHIP;
+    mark();
+    hipLaunchKernelGGL((fwd_chunk_output<BF16, C, D>), dim3((unsigned)(p.n_chunks * p.BH)),
+                       dim3(ChunkShape<BF16, C, D>::NT), p.lds_out, s, a);
+    ok = ok && hipGetLastError() == hipSuccess;
+  }
   if (final_state) {
     hipLaunchKernelGGL((fwd_final_state<BF16, C, D>), dim3((unsigned)p.BH), dim3(256), 0, s, a);
     ok = ok && hipGetLastError() == hipSuccess;

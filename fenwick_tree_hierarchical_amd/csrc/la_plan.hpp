@@ -127,6 +127,20 @@ LA_HD constexpr OutLds output_lds(int C, int D, int es, int L) {
   o.total = off;
   return o;
 }
+// The late-V variant of the output kernel (bfloat16, C = d = 128): the level
+// contractions run before P V, so V is loaded into the Q tile once Q is dead
+// and the workgroup needs one 32 KB tile less.
+LA_HD constexpr bool output_vlate_shape(int C, int D, int es) { return es == 2 && C == 128 && D == 128; }
+LA_HD constexpr OutLds output_lds_vlate(int C, int D, int es, int L) {
+  OutLds o = output_lds(C, D, es, L);
+  const int vbytes = (C * o.ld_v * es + 255) / 256 * 256;
+  o.lam -= vbytes;
+  o.b2 -= vbytes;
+  o.e2 -= vbytes;
+  o.total -= vbytes;
+  o.v = o.q;
+  return o;
+}
 
 struct FwdPlan {
   int B = 0, H = 0, D = 0, C = 0, L = 0, dtype = 0, es = 0;
@@ -134,6 +148,7 @@ struct FwdPlan {
   int64_t n_full_chunks = 0, n_full_groups = 0;   // chunks of C tokens, groups of G such chunks
   int G = 1, log2G = 0, log2C = 0;
   int lds_out = 0, lds_state = 0;
+  int lds_out_vlate = 0;   // > 0: the late-V output kernel runs (two workgroups fit per CU)
   size_t off_nodes_in = 0, off_gch = 0;
   size_t off_gstate = 0, off_gtot = 0, off_gprefix = 0, off_nodes = 0, ws_bytes = 0;
   int n_stages = 0;   // 0 for an empty problem
@@ -166,6 +181,8 @@ inline int plan_fwd(int B, int H, int64_t T, int dk, int dv, int C, int dtype, i
   P.log2G = ilog2(P.G);
   P.lds_state = state_lds(C, dk, P.es, P.G).total;
   P.lds_out = output_lds(C, dk, P.es, P.L).total;
+  if (output_vlate_shape(C, dk, P.es) && 2 * output_lds_vlate(C, dk, P.es, P.L).total <= kLdsLimit)
+    P.lds_out_vlate = output_lds_vlate(C, dk, P.es, P.L).total;
   if (P.lds_state > kLdsLimit || output_lds(C, dk, P.es, kMaxLevels).total > kLdsLimit) return kESHAPE;
   P.n_chunks = (T + C - 1) / C;
   P.n_groups = (P.n_chunks + P.G - 1) / P.G;

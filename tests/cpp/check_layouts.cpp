@@ -37,6 +37,20 @@ int main() {
           CHECK(o.k + kp <= o.v && o.v + C * o.ld_v * es <= o.lam, "C=%d D=%d es=%d L=%d", C, D, es, L);
           CHECK(o.lam + C * L * 4 <= o.b2 && o.b2 + C * 4 <= o.e2 && o.e2 + C * 4 <= o.total, "C=%d D=%d", C, D);
           CHECK((o.ld_row * es) % 16 == 0 && (o.ld_p * es) % 16 == 0, "row alignment C=%d D=%d es=%d", C, D, es);
+          // the late-V variant: V shares the Q tile, the rest back to back after
+          // K|P; the plan picks it exactly where two workgroups fit per CU
+          if (output_vlate_shape(C, D, es)) {
+            const OutLds v = output_lds_vlate(C, D, es, L);
+            CHECK(v.q == 0 && v.v == v.q && v.k == o.k && v.p == o.p && v.ld_v == o.ld_v, "late V C=%d D=%d L=%d", C, D, L);
+            CHECK(C * v.ld_v * es <= v.k && v.k + kp <= v.lam, "late V C=%d D=%d L=%d", C, D, L);
+            CHECK(v.lam + C * L * 4 <= v.b2 && v.b2 + C * 4 <= v.e2 && v.e2 + C * 4 <= v.total, "late V L=%d", L);
+            FwdPlan fp;
+            CHECK(plan_fwd(1, 2, 1000, D, D, C, es == 2 ? kBF16 : kF32, L >= levels_needed(1000) ? L : -1, &fp) == kOK,
+                  "late V plan L=%d", L);
+            if (L >= levels_needed(1000))
+              CHECK((fp.lds_out_vlate > 0) == (2 * v.total <= kLdsLimit) && (fp.lds_out_vlate == 0 || fp.lds_out_vlate == v.total),
+                    "late V choice L=%d", L);
+          }
           if (C > 64) continue;
           // backward, query side
           const BwdChunkLds q = bwd_chunk_lds(C, D, es, L, false);

@@ -69,6 +69,30 @@ def test_shapes_weak_decay_ragged(d, C, dtype):
 
 
 @pytest.mark.parametrize("variant", ["weak_decay", "no_decay"])
+def test_d128_c128_both_output_kernels(variant):
+    """bfloat16 at C = d = 128 has two output kernels: the late-V one (P V
+    after the level contractions, V loaded into the dead Q tile; two
+    workgroups per CU) while the lambda rows fit beside it (L <= 26), else the
+    one with all three tiles resident.  Lambda padded with levels no key
+    reaches (L = 32) runs the second on the same problem: both match the
+    oracle, and each other to the rounding of their summation orders."""
+    dev = need_gpu()
+    T, C = 37 * 128 + 77, 128
+    x = make_inputs(WORKLOADS["small_bf16"], B=1, H=2, T=T, d=128, dtype="bf16", variant=variant, seed=41)
+    L0 = x["lam"].shape[-1]
+    g = torch.Generator().manual_seed(42)
+    extra = torch.rand(*x["lam"].shape[:-1], 32 - L0, generator=g, dtype=x["lam"].dtype) + 0.5
+    x32 = dict(x, lam=torch.cat([x["lam"], extra], dim=-1).contiguous())
+    a = gpu_fwd(x, C, dev)
+    b = gpu_fwd(x32, C, dev)
+    ref = oracle_fwd(x)
+    assert np.all(np.isfinite(a)) and np.all(np.isfinite(b))
+    assert_parity(a, ref, TOL["bf16"], f"late V {variant}")
+    assert_parity(b, ref, TOL["bf16"], f"all tiles resident {variant}")
+    assert_parity(a, b, 1e-2, f"the two kernels {variant}")
+
+
+@pytest.mark.parametrize("variant", ["weak_decay", "no_decay"])
 def test_small_bf16_coverage_variants(variant):
     dev = need_gpu()
     w = WORKLOADS["small_bf16"]
