@@ -12,8 +12,11 @@ every input already resident in HBM.  Prints ONE JSON line:
                  bytes per launch / its mean duration from HIP events
                  recorded on the launch stream around each kernel, over a
                  second pass of as many steps right after the timed ones
-                 (the events cost about 30 us per step, so the timed steps
-                 run without them; `ms_per_step_staged` is that pass),
+                 (the timed steps run without events; `ms_per_step_staged`
+                 is that pass).  The events are timing-only ones created
+                 with hipEventDisableSystemFence, so recording one writes
+                 back and invalidates no caches (`stage_events` says which
+                 kind ran),
                  against 8 TB/s; `traffic` is the counter-measured HBM
                  bytes per launch from profiles/ when those counters were
                  taken on the current kernel source, else null
@@ -81,6 +84,51 @@ KERNELS = {"fwd_chunk_states": "chunk_states", "fwd_group_tree": "group_tree", "
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+class TimingEvent:
+    """A HIP event used only to time the kernels between two records,
+    created with hipEventDisableSystemFence: its record performs no
+    system-scope cache writeback and invalidation, which would otherwise add
+    to the span it measures and leave the next kernel with cold caches.  It
+    is read only after a device synchronize.  Exposes the two members the
+    staged entry point and the bench use (`cuda_event`, `elapsed_time`)."""
+    FLAGS = 0x20000000      # hipEventDisableSystemFence
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if TimingEvent._hip is None:
+            TimingEvent._hip = ctypes.CDLL("libamdhip64.so")
+        h = ctypes.c_void_p()
+        rc = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(h), ctypes.c_uint(self.FLAGS))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.cuda_event = h.value
+
+    def elapsed_time(self, end) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        rc = TimingEvent._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.cuda_event),
+                                                  ctypes.c_void_p(end.cuda_event))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        h = getattr(self, "cuda_event", None)
+        if TimingEvent._hip is not None and h:
+            import ctypes
+            TimingEvent._hip.hipEventDestroy(ctypes.c_void_p(h))
+
+
+def stage_events(torch, n: int):
+    """n timing events for the staged steps, and their kind: fence-free HIP
+    events, or torch's when the HIP runtime library cannot be opened."""
+    try:
+        return [TimingEvent() for _ in range(n)], "hip, hipEventDisableSystemFence"
+    except (OSError, AttributeError, RuntimeError):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)], "torch.cuda.Event"
 
 
 def _code_only(text: str) -> str:
@@ -588,7 +636,8 @@ def bench_config(la, torch, dev, w, steps=20, warmup=10):
         call()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / steps * 1e3
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)] for _ in range(steps)]
+    flat, ev_kind = stage_events(torch, steps * (n_st + 1))
+    evs = [flat[i * (n_st + 1):(i + 1) * (n_st + 1)] for i in range(steps)]
     for i in range(steps):
         call(evs[i])
     torch.cuda.synchronize()
@@ -606,7 +655,7 @@ def bench_config(la, torch, dev, w, steps=20, warmup=10):
             "layer_frac": cnt["bytes_io"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "alg_tflops": cnt["flops"] / (ms * 1e-3) / 1e12,
             "frac_of_bf16_peak": cnt["flops"] / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS if es == 2 else None,
-            "stages": stages}
+            "stages": stages, "stage_events": ev_kind}
 
 
 def ctypes_byref(la, st):
@@ -837,11 +886,12 @@ def main():
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # kernel durations: as many steps again, with HIP events recorded on the
-    # launch stream between the kernels (the events cost about 30 us per
-    # step, so the timed steps above run without them)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)] for _ in range(args.steps)]
-    log(f"bench: {args.steps} staged steps for the kernel durations")
+    # kernel durations: as many steps again, with timing-only HIP events
+    # recorded on the launch stream between the kernels (the timed steps
+    # above run without them)
+    flat, ev_kind = stage_events(torch, args.steps * (n_st + 1))
+    evs = [flat[i * (n_st + 1):(i + 1) * (n_st + 1)] for i in range(args.steps)]
+    log(f"bench: {args.steps} staged steps for the kernel durations ({ev_kind} events)")
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for i in range(args.steps):
@@ -866,6 +916,7 @@ def main():
     result = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "ms_per_step_staged": wall_staged / args.steps * 1e3,
+        "stage_events": ev_kind,
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d_k": w.dk, "d_v": w.dv, "chunk": w.C,
