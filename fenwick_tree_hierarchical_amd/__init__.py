@@ -58,6 +58,8 @@ _SIGS = {
                              ctypes.POINTER(_LaState), _p], _i),
     "loglinear_bwd_workspace": ([_i, _i, _i64, _i, _i, _i, _i, ctypes.POINTER(_sz)], _i),
     "loglinear_bwd": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
+    "loglinear_bwd_from_fwd": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _i, _i, _i, _p, _sz,
+                                _p, _sz, _p], _i),
     "loglinear_state_bytes": ([_i, _i, _i, _i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz)], _i),
     "loglinear_state_init": ([ctypes.POINTER(_LaState), _i, _i, _i, _i, _i, _p, _p, _p], _i),
     "loglinear_decode_step": ([ctypes.POINTER(_LaState), _p, _p, _p, _p, _p, _p, _i, _p], _i),
@@ -254,11 +256,14 @@ def loglinear_bwd_workspace(B: int, H: int, T: int, dk: int, dv: int, C: int, dt
     return n.value
 
 
-def loglinear_bwd(q, k, v, log_a, lam, dout, chunk: int = 64, workspace=None, grads=None):
+def loglinear_bwd(q, k, v, log_a, lam, dout, chunk: int = 64, workspace=None, grads=None, fwd_workspace=None):
     """Gradients of a loss with respect to q, k, v, log_a and lam, given
     dout = dL/dout of the forward.  Returns (dq, dk, dv, dlog_a, dlam): dq,
     dk, dv in q's dtype, dlog_a [B,H,T] and dlam [B,H,T,L] float32.  ``grads``
-    optionally supplies those five output tensors."""
+    optionally supplies those five output tensors.  ``fwd_workspace``: the
+    workspace of the loglinear_fwd call on these inputs (same chunk), kept
+    unchanged since; the backward then reuses its bucket structure
+    (loglinear_bwd_from_fwd)."""
     dev = _dev(q, k, v, log_a, lam, dout)
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -283,9 +288,20 @@ def loglinear_bwd(q, k, v, log_a, lam, dout, chunk: int = 64, workspace=None, gr
     nws = loglinear_bwd_workspace(B, H, T, dk, dv, chunk, q.dtype)
     if workspace is None or workspace.numel() < nws:
         workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
-    _check(lib().loglinear_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(dout), _ptr(gq), _ptr(gk),
-                               _ptr(gv), _ptr(gla), _ptr(glam), B, H, T, dk, dv, chunk, L, _dtype_code(q.dtype),
-                               _ptr(workspace), workspace.numel(), _stream(dev)), "loglinear_bwd")
+    if fwd_workspace is None:
+        _check(lib().loglinear_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(dout), _ptr(gq),
+                                   _ptr(gk), _ptr(gv), _ptr(gla), _ptr(glam), B, H, T, dk, dv, chunk, L,
+                                   _dtype_code(q.dtype), _ptr(workspace), workspace.numel(), _stream(dev)),
+               "loglinear_bwd")
+    else:
+        _dev(q, fwd_workspace)
+        if fwd_workspace.dtype != torch.uint8 or not fwd_workspace.is_contiguous():
+            raise TypeError("fwd_workspace must be a contiguous uint8 tensor")
+        _check(lib().loglinear_bwd_from_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(dout), _ptr(gq),
+                                            _ptr(gk), _ptr(gv), _ptr(gla), _ptr(glam), B, H, T, dk, dv, chunk, L,
+                                            _dtype_code(q.dtype), _ptr(fwd_workspace), fwd_workspace.numel(),
+                                            _ptr(workspace), workspace.numel(), _stream(dev)),
+               "loglinear_bwd_from_fwd")
     return gq, gk, gv, gla, glam
 
 

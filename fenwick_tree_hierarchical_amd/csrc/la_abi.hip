@@ -192,11 +192,13 @@ LA_API int loglinear_bwd_workspace(int B, int H, int64_t T, int dk, int dv, int 
   return kOK;
 }
 
-LA_API int loglinear_bwd(const void* q, const void* k, const void* v, const float* log_a,
-                         const float* lambda, const void* dout, void* grad_q, void* grad_k,
-                         void* grad_v, float* grad_log_a, float* grad_lambda, int B, int H, int64_t T,
-                         int dk, int dv, int C, int L, int dtype, void* workspace,
-                         size_t workspace_bytes, la_stream_t stream) {
+// The backward; with fwd_ws, the query side reads the nodes and gates of the
+// caller's forward (its workspace) where the fused per-chunk kernel runs.
+static int bwd_common(const void* q, const void* k, const void* v, const float* log_a, const float* lambda,
+                      const void* dout, void* grad_q, void* grad_k, void* grad_v, float* grad_log_a,
+                      float* grad_lambda, int B, int H, int64_t T, int dk, int dv, int C, int L, int dtype,
+                      void* workspace, size_t workspace_bytes, const void* fwd_ws, size_t fwd_ws_bytes, bool from_fwd,
+                      la_stream_t stream) {
   BwdPlan P;
   int rc = plan_bwd(B, H, T, dk, dv, C, dtype, L, &P);
   if (rc != kOK) return rc;
@@ -205,16 +207,25 @@ LA_API int loglinear_bwd(const void* q, const void* k, const void* v, const floa
   rc = check_bwd_buffers(P, q, k, v, log_a, lambda, dout, grad_q, grad_k, grad_v, grad_log_a, grad_lambda,
                          workspace, workspace_bytes);
   if (rc != kOK) return rc;
+  if (from_fwd) {
+    rc = check_saved_fwd(p, fwd_ws, fwd_ws_bytes);
+    if (rc != kOK) return rc;
+  }
+  // the forward's nodes serve where the fused per-chunk kernel runs; elsewhere
+  // the forward structure is built in this call's own workspace
+  const bool saved = from_fwd && bwd_fused_shape(dtype == kBF16, C, dk) && P.lds_fused > 0;
   char* w = static_cast<char*>(workspace);
-  // forward structure over (k := v, v := k): its nodes are sum gate k v^T
+  char* n = saved ? static_cast<char*>(const_cast<void*>(fwd_ws)) : w;
+  // forward structure over (k := v, v := k): its nodes are sum gate k v^T (the
+  // forward's own nodes, over (k, v), are their transposes)
   FwdArgs fa{};
   fa.q = nullptr; fa.k = v; fa.v = k; fa.log_a = log_a; fa.lam = lambda; fa.out = nullptr;
-  fa.nodes_in = p.has_chunk_nodes() ? static_cast<void*>(w + p.off_nodes_in) : nullptr;
-  fa.gch = p.has_chunk_nodes() ? reinterpret_cast<float*>(w + p.off_gch) : nullptr;
-  fa.gstate = p.has_group_nodes() ? reinterpret_cast<float*>(w + p.off_gstate) : nullptr;
-  fa.gtot = p.has_group_nodes() ? reinterpret_cast<float*>(w + p.off_gtot) : nullptr;
-  fa.gprefix = p.has_group_nodes() ? reinterpret_cast<double*>(w + p.off_gprefix) : nullptr;
-  fa.nodes = p.has_group_nodes() ? static_cast<void*>(w + p.off_nodes) : nullptr;
+  fa.nodes_in = p.has_chunk_nodes() ? static_cast<void*>(n + p.off_nodes_in) : nullptr;
+  fa.gch = p.has_chunk_nodes() ? reinterpret_cast<float*>(n + p.off_gch) : nullptr;
+  fa.gstate = p.has_group_nodes() ? reinterpret_cast<float*>(n + p.off_gstate) : nullptr;
+  fa.gtot = p.has_group_nodes() ? reinterpret_cast<float*>(n + p.off_gtot) : nullptr;
+  fa.gprefix = p.has_group_nodes() ? reinterpret_cast<double*>(n + p.off_gprefix) : nullptr;
+  fa.nodes = p.has_group_nodes() ? static_cast<void*>(n + p.off_nodes) : nullptr;
   fa.T = T; fa.n_chunks = p.n_chunks; fa.n_groups = p.n_groups; fa.n_full_groups = p.n_full_groups; fa.L = L;
   BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.log_a = log_a; a.lam = lambda;
@@ -228,7 +239,26 @@ LA_API int loglinear_bwd(const void* q, const void* k, const void* v, const floa
   a.dcol = reinterpret_cast<float*>(w + P.off_dcol);
   a.T = T; a.n_chunks = p.n_chunks; a.n_groups = p.n_groups; a.L = L; a.JG = P.JG; a.rhalves = P.rhalves;
   hipStream_t s = (hipStream_t)stream;
-  return dtype == kBF16 ? launch_bwd_bf16(P, fa, a, s) : launch_bwd_f32(P, fa, a, s);
+  return dtype == kBF16 ? launch_bwd_bf16(P, fa, a, s, saved) : launch_bwd_f32(P, fa, a, s, saved);
+}
+
+LA_API int loglinear_bwd(const void* q, const void* k, const void* v, const float* log_a,
+                         const float* lambda, const void* dout, void* grad_q, void* grad_k,
+                         void* grad_v, float* grad_log_a, float* grad_lambda, int B, int H, int64_t T,
+                         int dk, int dv, int C, int L, int dtype, void* workspace,
+                         size_t workspace_bytes, la_stream_t stream) {
+  return bwd_common(q, k, v, log_a, lambda, dout, grad_q, grad_k, grad_v, grad_log_a, grad_lambda, B, H, T, dk,
+                    dv, C, L, dtype, workspace, workspace_bytes, nullptr, 0, false, stream);
+}
+
+LA_API int loglinear_bwd_from_fwd(const void* q, const void* k, const void* v, const float* log_a,
+                                  const float* lambda, const void* dout, void* grad_q, void* grad_k,
+                                  void* grad_v, float* grad_log_a, float* grad_lambda, int B, int H, int64_t T,
+                                  int dk, int dv, int C, int L, int dtype, const void* fwd_workspace,
+                                  size_t fwd_workspace_bytes, void* workspace, size_t workspace_bytes,
+                                  la_stream_t stream) {
+  return bwd_common(q, k, v, log_a, lambda, dout, grad_q, grad_k, grad_v, grad_log_a, grad_lambda, B, H, T, dk,
+                    dv, C, L, dtype, workspace, workspace_bytes, fwd_workspace, fwd_workspace_bytes, true, stream);
 }
 
 LA_API int loglinear_gdn_fwd_workspace(int B, int H, int64_t T, int dk, int dv, int C, int dtype,

@@ -3,7 +3,7 @@
 #include "la_internal.hpp"
 
 namespace la {
-int launch_bwd_f32(const BwdPlan& p, const FwdArgs& fa, const BwdArgs& a, hipStream_t s) {
-  return launch_bwd_dtype<false>(p, fa, a, s);
+int launch_bwd_f32(const BwdPlan& p, const FwdArgs& fa, const BwdArgs& a, hipStream_t s, bool saved) {
+  return launch_bwd_dtype<false>(p, fa, a, s, saved);
 }
 }  // namespace la

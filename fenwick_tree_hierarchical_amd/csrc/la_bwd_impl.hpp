@@ -1487,7 +1487,12 @@ void bwd_chunk_dkv(BwdArgs a) {
 // dv = P^T dout and the key-side nodes).  Each side's arithmetic is that of
 // its own kernel, so the results are the same bits; the key-side nodes must
 // be complete when it starts.
-template <bool BF16, int C, int D>
+//
+// NT: the query-side nodes are the forward's own (saved by the caller's
+// forward pass over (k, v)), which hold the transposes of the nodes over
+// (v, k): their fragments are gathered from the columns, as the key side's
+// R^T fragments are.
+template <bool BF16, int C, int D, bool NT = false>
 __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a) {
   using SH = BwdShape<BF16, C, D>;
   using EL = Elem<BF16>;
@@ -1679,7 +1684,10 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
       for (int s2 = 0; s2 < KSD; ++s2) {
         const int k0 = s2 * KST + lq * KPL;
 #pragma unroll
-        for (int n = 0; n < NCB; ++n) dst[s2][n] = EL::template load_k<D>(node + (16 * (cb0 + n) + lr) * D + k0, k0);
+        for (int n = 0; n < NCB; ++n) {
+          if constexpr (NT) dst[s2][n] = gather_node_col<BF16, D>(node, k0, 16 * (cb0 + n) + lr);
+          else dst[s2][n] = EL::template load_k<D>(node + (16 * (cb0 + n) + lr) * D + k0, k0);
+        }
       }
     };
     const float gx = (lane < ci) ? a.gch[bh * nc + cg0 + lane] : 0.f;
@@ -1702,8 +1710,10 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
     }
     if (owner) {
       Frag nf[NPRE][KSD][NCB];
+      // row loads: a ring of NPRE nodes ahead; gathers (the forward's nodes)
+      // take twice the registers in flight, so one node ahead
 #pragma unroll
-      for (int u = 0; u < NPRE; ++u)
+      for (int u = 0; u < (NT ? 1 : NPRE); ++u)
         if (u < n_lev) load_node(u, nf[u]);
       f32x4 acc[QB][NCB];
 #pragma unroll
@@ -1774,13 +1784,24 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
           __builtin_amdgcn_sched_barrier(0);
         }
       };
-      for (int base = 0; base < n_lev; base += NPRE) {
+      if constexpr (NT) {
+        static_assert(NPRE == 2, "two buffers: the node in use and the next one");
+        for (int base = 0; base < n_lev; base += 2) {
+          if (base + 1 < n_lev) load_node(base + 1, nf[1]);   // gathered while this level is contracted
+          contract(base, nf[0]);
+          if (base + 1 >= n_lev) break;
+          if (base + 2 < n_lev) load_node(base + 2, nf[0]);
+          contract(base + 1, nf[1]);
+        }
+      } else {
+        for (int base = 0; base < n_lev; base += NPRE) {
 #pragma unroll
-        for (int u = 0; u < NPRE; ++u) {
-          const int li = base + u;
-          if (li >= n_lev) break;
-          contract(li, nf[u]);
-          if (li + NPRE < n_lev) load_node(li + NPRE, nf[u]);
+          for (int u = 0; u < NPRE; ++u) {
+            const int li = base + u;
+            if (li >= n_lev) break;
+            contract(li, nf[u]);
+            if (li + NPRE < n_lev) load_node(li + NPRE, nf[u]);
+          }
         }
       }
 #pragma unroll
@@ -2072,14 +2093,20 @@ __global__ __launch_bounds__(TILE_THREADS) void bwd_gate_grad(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Host-side launch for one (dtype, C, D) instantiation.  fa carries the
 // forward-structure buffers over (k := v, v := k).
+// saved: the query-side nodes and gates are those of the caller's forward
+// pass (fa and a point at its workspace), so the forward structure is not
+// built again; only where the fused per-chunk kernel runs.
 template <bool BF16, int C, int D>
-int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s) {
+int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s, bool saved) {
   using E = typename Elem<BF16>::T;
   const FwdPlan& p = P.f;
   constexpr int G = state_group(D);
   if (p.G != G) return kEHIP;
+  constexpr bool kFusedShape = bwd_fused_shape(BF16, C, D);
+  const bool fused = kFusedShape && P.lds_fused > 0;
+  if (saved && !fused) return kEINVAL;
   bool ok = true;
-  if (p.n_chunks > 1) {
+  if (p.n_chunks > 1 && !saved) {
     constexpr int lds_s = state_lds(C, D, sizeof(E), G).total;
     ok = ok && hipFuncSetAttribute((const void*)fwd_chunk_states<BF16, C, D>,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds_s) == hipSuccess;
@@ -2088,7 +2115,7 @@ int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s) {
                        dim3(StateShape<BF16, C, D>::NT), lds_s, s, fa);
     ok = ok && hipGetLastError() == hipSuccess;
   }
-  if (p.n_groups > 1) {
+  if (p.n_groups > 1 && !saved) {
     const dim3 grid((unsigned)(group_tree_blocks(D) * p.BH));
     const int levels = bit_length(p.n_groups);
     if (levels <= 6)
@@ -2103,8 +2130,6 @@ int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s) {
   }
   // the fused per-chunk kernel needs the key-side nodes first; the query-side
   // kernel of the split pair does not
-  constexpr bool kFusedShape = bwd_fused_shape(BF16, C, D);
-  const bool fused = kFusedShape && P.lds_fused > 0;
   if (!fused) {
     ok = ok && hipFuncSetAttribute((const void*)bwd_chunk_dq<BF16, C, D>,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, P.lds_dq) == hipSuccess;
@@ -2143,7 +2168,14 @@ int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s) {
     ok = ok && hipGetLastError() == hipSuccess;
   }
   if constexpr (kFusedShape) {
-    if (fused) {
+    if (fused && saved) {
+      ok = ok && hipFuncSetAttribute((const void*)bwd_chunk_fused<BF16, C, D, true>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, P.lds_fused) == hipSuccess;
+      if (!ok) return kEHIP;
+      hipLaunchKernelGGL((bwd_chunk_fused<BF16, C, D, true>), dim3((unsigned)(p.n_chunks * p.BH)),
+                         dim3(128 * bwd_waves(C)), P.lds_fused, s, a);
+      ok = ok && hipGetLastError() == hipSuccess;
+    } else if (fused) {
       ok = ok && hipFuncSetAttribute((const void*)bwd_chunk_fused<BF16, C, D>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, P.lds_fused) == hipSuccess;
       if (!ok) return kEHIP;
@@ -2166,9 +2198,9 @@ int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s) {
 }
 
 template <bool BF16>
-int launch_bwd_dtype(const BwdPlan& P, const FwdArgs& fa, const BwdArgs& a, hipStream_t s) {
+int launch_bwd_dtype(const BwdPlan& P, const FwdArgs& fa, const BwdArgs& a, hipStream_t s, bool saved) {
 #define LA_CASE(CC, DD) \
-  if (P.f.C == CC && P.f.D == DD) return launch_bwd_impl<BF16, CC, DD>(P, fa, a, s);
+  if (P.f.C == CC && P.f.D == DD) return launch_bwd_impl<BF16, CC, DD>(P, fa, a, s, saved);
   LA_CASE(16, 16) LA_CASE(16, 32) LA_CASE(16, 64) LA_CASE(16, 128)
   LA_CASE(32, 16) LA_CASE(32, 32) LA_CASE(32, 64) LA_CASE(32, 128)
   LA_CASE(64, 16) LA_CASE(64, 32) LA_CASE(64, 64) LA_CASE(64, 128)

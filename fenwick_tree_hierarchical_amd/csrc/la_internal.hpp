@@ -24,8 +24,8 @@ int launch_fwd_f32(const FwdPlan& p, const FwdArgs& a, hipStream_t s, hipEvent_t
 
 // Backward: enqueue its kernels on stream s.  fa carries the forward-structure
 // buffers over (k := v, v := k).
-int launch_bwd_bf16(const BwdPlan& p, const FwdArgs& fa, const BwdArgs& a, hipStream_t s);
-int launch_bwd_f32(const BwdPlan& p, const FwdArgs& fa, const BwdArgs& a, hipStream_t s);
+int launch_bwd_bf16(const BwdPlan& p, const FwdArgs& fa, const BwdArgs& a, hipStream_t s, bool saved);
+int launch_bwd_f32(const BwdPlan& p, const FwdArgs& fa, const BwdArgs& a, hipStream_t s, bool saved);
 
 // Log-linear Gated DeltaNet forward: enqueue its kernels on stream s.
 int launch_gdn_bf16(const GdnPlan& p, const GdnArgs& a, hipStream_t s);

@@ -57,6 +57,16 @@ inline int check_bwd_buffers(const BwdPlan& P, const void* q, const void* k, con
   return kOK;
 }
 
+// The workspace of the forward whose nodes a backward reuses (the forward's
+// plan: the same shapes, dtype, chunk and levels).
+inline int check_saved_fwd(const FwdPlan& p, const void* fwd_ws, size_t fwd_ws_bytes) {
+  if (p.ws_bytes > 0) {
+    if (!fwd_ws || fwd_ws_bytes < p.ws_bytes) return kEWORKSPACE;
+    if (!aligned(fwd_ws, 256)) return kEALIGN;
+  }
+  return kOK;
+}
+
 // The tensors and workspace of a non-empty Gated DeltaNet forward.
 inline int check_gdn_buffers(const GdnPlan& p, const void* q, const void* k, const void* v, const float* log_a,
                              const float* beta, const float* lambda, const void* out, const void* ws,

@@ -274,6 +274,39 @@ LA_API int loglinear_bwd(const void* q, const void* k, const void* v, const floa
                          int dk, int dv, int C, int L, int dtype, void* workspace,
                          size_t workspace_bytes, la_stream_t stream);
 
+/*
+ * loglinear_bwd reusing the forward pass's bucket structure (the same
+ * gradients, "Log-Linear Attention", Spanish summary, section 5 on the level
+ * weights' gradients).  The query side of the backward needs, for every
+ * bucket, the sum of gate * k_s v_s^T over its keys: exactly the transposes
+ * of the nodes the forward builds over (k, v).  So a training step that keeps
+ * its forward's workspace can hand it over, and the backward skips building
+ * that structure again.
+ *
+ *   fwd_workspace        the workspace of an earlier loglinear_fwd call on the
+ *                        same q, k, v, log_a and lambda (same B, H, T, dk, dv,
+ *                        C, L and dtype), not written since; read only.
+ *                        At least loglinear_fwd_workspace() bytes, 256-byte
+ *                        aligned (may be null when that size is 0).
+ *   everything else      as for loglinear_bwd; workspace is this call's own
+ *                        (loglinear_bwd_workspace() bytes).
+ *
+ * The forward's structure is used where the fused per-chunk kernel runs
+ * (bfloat16, C in {32, 64}, dk <= 64, lambda rows that fit: L <= 17 at
+ * C = dk = 64); elsewhere it is not read and the call is loglinear_bwd.  The
+ * gradients agree with loglinear_bwd to the rounding of the two structures'
+ * bfloat16 nodes (each gates its own operand).  A workspace that does not
+ * hold that forward's nodes gives wrong gradients, not an error: the library
+ * cannot tell.  Errors as loglinear_bwd; LA_EWORKSPACE / LA_EALIGN for
+ * fwd_workspace.
+ */
+LA_API int loglinear_bwd_from_fwd(const void* q, const void* k, const void* v, const float* log_a,
+                                  const float* lambda, const void* dout, void* grad_q, void* grad_k,
+                                  void* grad_v, float* grad_log_a, float* grad_lambda, int B, int H, int64_t T,
+                                  int dk, int dv, int C, int L, int dtype, const void* fwd_workspace,
+                                  size_t fwd_workspace_bytes, void* workspace, size_t workspace_bytes,
+                                  la_stream_t stream);
+
 /* Workspace size for loglinear_gdn_fwd (host only); errors as loglinear_gdn_fwd. */
 LA_API int loglinear_gdn_fwd_workspace(int B, int H, int64_t T, int dk, int dv, int C, int dtype,
                                        size_t* bytes);

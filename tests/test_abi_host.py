@@ -251,6 +251,28 @@ def test_bwd_validation_codes():
                T=0, Lv=0) == OK
 
 
+def bwd_ff(B=1, H=1, T=64, d=16, C=16, Lv=7, dt=0, w=A, wb=1 << 30, fw=A, fwb=1 << 30, **kw):
+    p = {n: kw.get(n, A) for n in ("q", "k", "v", "la", "lam", "g", "gq", "gk", "gv", "gla", "glam")}
+    return L.loglinear_bwd_from_fwd(p["q"], p["k"], p["v"], p["la"], p["lam"], p["g"], p["gq"], p["gk"], p["gv"],
+                                    p["gla"], p["glam"], B, H, T, d, d, C, Lv, dt, fw, fwb, w, wb, None)
+
+
+def test_bwd_from_fwd_validation_codes():
+    """The backward reusing a forward's workspace: the backward's own checks
+    first, then the forward workspace's size (that forward's plan) and
+    alignment; empty problems succeed without reading anything."""
+    fn = ctypes.c_size_t(0)
+    assert L.loglinear_fwd_workspace(1, 1, 64, 16, 16, 16, 0, ctypes.byref(fn)) == OK and fn.value > 0
+    assert bwd_ff(g=None) == EINVAL
+    assert bwd_ff(w=None) == EWS
+    assert bwd_ff(fw=None) == EWS
+    assert bwd_ff(fwb=fn.value - 1) == EWS
+    assert bwd_ff(fw=A + 16) == EALIGN
+    assert bwd_ff(Lv=6) == ESHAPE
+    assert bwd_ff(q=None, k=None, v=None, la=None, lam=None, g=None, gq=None, gk=None, gv=None, gla=None, glam=None,
+                  fw=None, fwb=0, B=0) == OK
+
+
 def gws(B, H, T, d, C, dt=1):
     n = ctypes.c_size_t(0)
     rc = L.loglinear_gdn_fwd_workspace(B, H, T, d, d, C, dt, ctypes.byref(n))

@@ -169,6 +169,45 @@ def test_split_key_side_matches_fused(d):
     check(x32, dout, C, "bf16", dev, f"split key side d={d} L=32")
 
 
+@pytest.mark.parametrize("d, C", [(64, 64), (64, 32), (32, 64), (16, 32), (128, 64)])
+def test_backward_from_forward_workspace(d, C):
+    """loglinear_bwd_from_fwd: the backward reading the forward's bucket
+    nodes (their transposes serve the query side) instead of building the
+    structure over (v, k).  dk and dv come from the key side alone, so they
+    are the plain backward's bits; dq, dlambda and dlog_a go through the
+    forward's nodes (rounded with the other operand gated) and match the
+    oracle.  At d = 128 the fused kernel does not run and the call is the
+    plain backward, bit for bit."""
+    dev = need_gpu()
+    import fenwick_tree_hierarchical_amd as la
+    x, dout = case(4096 + 64 * 5 + 11, d, "bf16", "weak_decay", seed=8)
+    label = f"from fwd d={d} C={C}"
+    say(f"bwd {label}: shape={tuple(x['q'].shape)}")
+    plain = gpu_bwd(x, dout, C, dev)
+    xd = {k: v.to(dev) for k, v in x.items()}
+    B, H, T, _ = x["q"].shape
+    fws = torch.empty(max(la.loglinear_fwd_workspace(B, H, T, d, d, C, torch.bfloat16), 1), dtype=torch.uint8,
+                      device=dev)
+    la.loglinear_fwd(xd["q"], xd["k"], xd["v"], xd["log_a"], xd["lam"], chunk=C, workspace=fws)
+    g = la.loglinear_bwd(xd["q"], xd["k"], xd["v"], xd["log_a"], xd["lam"], dout.to(dev), chunk=C,
+                         fwd_workspace=fws)
+    torch.cuda.synchronize()
+    got = {n: t.float().cpu().numpy() for n, t in zip(NAMES, g)}
+    for n in ("dk", "dv"):
+        assert np.array_equal(got[n], plain[n]), n
+    if d == 128:
+        for n in NAMES:
+            assert np.array_equal(got[n], plain[n]), n
+    r = backward.backward_quadratic(x["q"], x["k"], x["v"], x["log_a"], x["lam"], dout)
+    ref = dict(zip(NAMES, r))
+    for n in ("dq", "dlam"):
+        assert np.all(np.isfinite(got[n])), n
+        assert_parity(got[n], ref[n], TOL["bf16"], f"{label} {n}")
+        assert_parity(got[n], plain[n], TOL["bf16"], f"{label} {n} against the plain backward")
+    assert_scaled(got["dlog_a"][..., None], ref["dlog_a"][..., None], gate_scale(x, dout, ref)[..., None],
+                  TOL["bf16"], f"{label} dlog_a")
+
+
 # --------------------------------------------------------------- full size
 def test_train_16k_full_size_sampled():
     """All 128 heads of the training shape: the gradients at sampled query and
