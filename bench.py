@@ -34,7 +34,8 @@ every input already resident in HBM.  Prints ONE JSON line:
                  fractions and layer_frac
   backward       the backward (loglinear_bwd) on the same layer with a
                  seeded upstream gradient: mean time, tokens/s and its ratio
-                 to the forward
+                 to the forward; `from_forward` the same backward handed the
+                 forward's workspace (loglinear_bwd_from_fwd)
   gdn            the log-linear Gated DeltaNet forward (loglinear_gdn_fwd)
                  on the same layer shape with seeded beta: mean time,
                  tokens/s, algorithmic TFLOP/s against the bf16 peak
@@ -463,23 +464,38 @@ def bench_decode_large(la, torch, dev, B=256, steps=64):
 def bench_backward(la, torch, dev, w, x, reps=10):
     """The backward (loglinear_bwd, all of its kernels) on the training shape
     with a seeded upstream gradient, timed with HIP events on the launch
-    stream.  Essential bytes: q, k, v, dout, log_a, lambda read and dq, dk,
-    dv, dlog_a, dlambda written once."""
+    stream; then the same backward handed the forward's workspace
+    (loglinear_bwd_from_fwd: the forward's bucket nodes serve its query side,
+    as in a training step that keeps them).  Essential bytes: q, k, v, dout,
+    log_a, lambda read and dq, dk, dv, dlog_a, dlambda written once."""
     from fenwick_tree_hierarchical_amd.workloads import make_grad_out
     dout = make_grad_out(w, device=dev)
     nws = la.loglinear_bwd_workspace(w.B, w.H, w.T, w.dk, w.dv, w.C, torch.bfloat16)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(la.loglinear_fwd_workspace(w.B, w.H, w.T, w.dk, w.dv, w.C, torch.bfloat16), 1),
+                      dtype=torch.uint8, device=dev)
+    la.loglinear_fwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], chunk=w.C, workspace=fws)
     grads = la.loglinear_bwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], dout, chunk=w.C, workspace=ws)
     torch.cuda.synchronize()
     s = torch.cuda.current_stream(dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    ev[0].record(s)
-    for i in range(reps):
-        la.loglinear_bwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], dout, chunk=w.C, workspace=ws, grads=grads)
-        ev[i + 1].record(s)
-    torch.cuda.synchronize()
-    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+
+    def timed(kw):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        la.loglinear_bwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], dout, chunk=w.C, workspace=ws, grads=grads,
+                         **kw)
+        torch.cuda.synchronize()
+        ev[0].record(s)
+        for i in range(reps):
+            la.loglinear_bwd(x["q"], x["k"], x["v"], x["log_a"], x["lam"], dout, chunk=w.C, workspace=ws,
+                             grads=grads, **kw)
+            ev[i + 1].record(s)
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+
+    ms = timed({})
+    ms_ff = timed({"fwd_workspace": fws})
     mean = sum(ms) / reps
+    mean_ff = sum(ms_ff) / reps
     es = 2
     per_tok = 7 * w.dk * es + 2 * 4 + 2 * 4 * w.L
     nbytes = w.B * w.H * w.T * per_tok
@@ -487,7 +503,11 @@ def bench_backward(la, torch, dev, w, x, reps=10):
             "min_ms": min(ms), "tokens_per_s": w.B * w.T / (mean * 1e-3), "ratio_to_forward": None,
             "essential_bytes": nbytes, "essential_gbps": nbytes / (mean * 1e-3) / 1e9,
             "essential_bytes_note": f"{per_tok} B per head-token: q, k, v, dout read and dq, dk, dv written "
-                                    f"(bf16), log_a, lambda read and dlog_a, dlambda written (fp32)"}
+                                    f"(bf16), log_a, lambda read and dlog_a, dlambda written (fp32)",
+            "from_forward": {"ms": mean_ff, "median_ms": sorted(ms_ff)[reps // 2], "min_ms": min(ms_ff),
+                             "tokens_per_s": w.B * w.T / (mean_ff * 1e-3), "ratio_to_forward": None,
+                             "note": "loglinear_bwd_from_fwd: the forward's workspace handed over, its bucket "
+                                     "nodes serve the query side (no state and tree kernels over (v, k))"}}
 
 
 def gdn_counts(B, H, T, d, C, L, es):
@@ -947,6 +967,7 @@ def main():
     result.update(secondary)
     if "backward" in result:
         result["backward"]["ratio_to_forward"] = result["backward"]["ms"] / ms_per_step
+        result["backward"]["from_forward"]["ratio_to_forward"] = result["backward"]["from_forward"]["ms"] / ms_per_step
     result["order"] = ("the other legs (decode, backward, gdn, layer, configs) ran before the warm-up and the "
                        "timed steps; the CPU baseline after them")
     if not args.no_cpu:
