@@ -2044,49 +2044,73 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// bwd_gate_grad: one workgroup per (b,h).  dlog_a_r = sum_{u >= r} (row_u -
-// col_u), tiles of 1024 tokens from the end: float sums inside a tile, a
-// float64 carry across tiles.  (A template only so that every translation
-// unit including this header may instantiate it.)
+// bwd_gate_grad: one workgroup of 1024 threads per (b,h).  dlog_a_r =
+// sum_{u >= r} (row_u - col_u), in passes of 16384 tokens from the end, read
+// as 16 rows of 1024 consecutive tokens (thread t takes token t of every row:
+// coalesced loads, all issued at once).  Each wave's 64 tokens of a row are
+// summed from the right by shuffles in float; the 16 x 16 segment totals are
+// scanned in float64 (each row by one thread, then the rows by one thread),
+// and a float64 carry runs across passes.  (A template only so that every
+// translation unit including this header may instantiate it.)
 template <int TILE_THREADS>
 __global__ __launch_bounds__(TILE_THREADS) void bwd_gate_grad(BwdArgs a) {
-  static_assert(TILE_THREADS == 256, "one float per thread and four tokens each");
-  __shared__ float sh[256];
+  static_assert(TILE_THREADS == 1024, "16 waves, 16 rows of 1024 tokens");
+  constexpr int NWV = TILE_THREADS / 64, ROWS = 16, SPAN = ROWS * TILE_THREADS;
+  __shared__ double seg[ROWS][NWV];     // segment totals, then the sum of the later segments of the row
+  __shared__ double rtot[ROWS];         // row totals
+  __shared__ double rsuf[ROWS + 1];     // sum of the later rows; [ROWS]: the pass total
   const int64_t bh = blockIdx.x, T = a.T;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   float* dl = a.dlog_a + bh * T;
   const float* dc = a.dcol + bh * T;
   double carry = 0.0;
-  for (int64_t hi = T; hi > 0; hi -= 1024) {
-    const int64_t lo = hi - 1024 > 0 ? hi - 1024 : 0;
-    float x[4];
+  for (int64_t hi = T; hi > 0; hi -= SPAN) {
+    const int64_t lo = hi - SPAN;                  // may be negative: the first pass is partial
+    float x[ROWS];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = lo + 4 * tid + u;
-      x[u] = i < hi ? dl[i] - dc[i] : 0.f;
+    for (int u = 0; u < ROWS; ++u) {
+      const int64_t i = lo + (int64_t)u * TILE_THREADS + tid;
+      x[u] = (i >= 0 && i < hi) ? dl[i] - dc[i] : 0.f;
     }
-    float sfx[4];
-    sfx[3] = x[3];
-    sfx[2] = x[2] + sfx[3];
-    sfx[1] = x[1] + sfx[2];
-    sfx[0] = x[0] + sfx[1];
-    sh[tid] = sfx[0];
-    __syncthreads();
-    for (int d = 1; d < 256; d <<= 1) {
-      const float y = tid + d < 256 ? sh[tid + d] : 0.f;
-      __syncthreads();
-      sh[tid] += y;
-      __syncthreads();
-    }
-    const float after = sh[tid] - sfx[0];      // tokens of later threads in the tile
-    const float tile = sh[0];
+    float sc[ROWS];                                // this token and the later ones of its wave's segment
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = lo + 4 * tid + u;
-      if (i < hi) dl[i] = (float)(carry + (double)(after + sfx[u]));
+    for (int u = 0; u < ROWS; ++u) {
+      float v = x[u];
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_down(v, d, 64);
+        if (lane + d < 64) v += y;
+      }
+      sc[u] = v;
+      if (lane == 0) seg[u][w] = (double)v;
     }
-    carry += (double)tile;
     __syncthreads();
+    if (tid < ROWS) {
+      double acc = 0.0;
+      for (int ww = NWV - 1; ww >= 0; --ww) {
+        const double t = seg[tid][ww];
+        seg[tid][ww] = acc;
+        acc += t;
+      }
+      rtot[tid] = acc;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double acc = 0.0;
+      for (int uu = ROWS - 1; uu >= 0; --uu) {
+        rsuf[uu] = acc;
+        acc += rtot[uu];
+      }
+      rsuf[ROWS] = acc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < ROWS; ++u) {
+      const int64_t i = lo + (int64_t)u * TILE_THREADS + tid;
+      if (i >= 0 && i < hi) dl[i] = (float)(carry + rsuf[u] + seg[u][w] + (double)sc[u]);
+    }
+    carry += rsuf[ROWS];
+    __syncthreads();                               // the shared sums are rewritten by the next pass
   }
 }
 
@@ -2192,7 +2216,7 @@ int launch_bwd_impl(const BwdPlan& P, FwdArgs fa, BwdArgs a, hipStream_t s, bool
                        P.lds_dkv, s, a);
     ok = ok && hipGetLastError() == hipSuccess;
   }
-  hipLaunchKernelGGL((bwd_gate_grad<256>), dim3((unsigned)p.BH), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bwd_gate_grad<1024>), dim3((unsigned)p.BH), dim3(1024), 0, s, a);
   ok = ok && hipGetLastError() == hipSuccess;
   return ok ? kOK : kEHIP;
 }
