@@ -1487,6 +1487,33 @@ void bwd_chunk_dkv(BwdArgs a) {
 // dv = P^T dout and the key-side nodes).  Each side's arithmetic is that of
 // its own kernel, so the results are the same bits; the key-side nodes must
 // be complete when it starts.
+// Tile reads of the fused kernel.  DIR: the chunk's tiles arrived by direct
+// global-to-LDS loads into swizzled rows of 2 D bytes (granule g of row r at
+// g ^ (r mod 8)); else they are padded rows of ld_row elements.
+template <bool BF16, int D, bool DIR>
+__device__ __forceinline__ typename Elem<BF16>::Frag fused_row(const unsigned char* tile, int ld_row, int r, int k0) {
+  using EL = Elem<BF16>;
+  if constexpr (DIR) return __builtin_bit_cast(typename EL::Frag, *reinterpret_cast<const u16x8*>(tile + swz_gran<D>(r, k0 / 8)));
+  else return EL::template load_k<D>(reinterpret_cast<const typename EL::T*>(tile) + r * ld_row + k0, k0);
+}
+// Column c0 + (lane mod 16) of the tile as an operand fragment over rows
+// kb + 8 (lane / 16) .. + 7 (ROWS rows in the tile).
+template <bool BF16, int ROWS, int D, bool DIR>
+__device__ __forceinline__ typename Elem<BF16>::Frag fused_col(const unsigned char* tile, int ld_row, int kb, int c0,
+                                                               int lane) {
+  using EL = Elem<BF16>;
+  if constexpr (DIR) return swz_tr_frag<D>(tile, kb, c0, lane);
+  else return gather_col<BF16, ROWS>(reinterpret_cast<const typename EL::T*>(tile), ld_row, kb + (lane >> 4) * EL::kPerLane,
+                                     c0 + (lane & 15));
+}
+// The four consecutive entries of row r from column c (c a multiple of 4).
+template <bool BF16, int D, bool DIR>
+__device__ __forceinline__ const typename Elem<BF16>::T* fused_quad(const unsigned char* tile, int ld_row, int r, int c) {
+  using T = typename Elem<BF16>::T;
+  if constexpr (DIR) return reinterpret_cast<const T*>(tile + swz_gran<D>(r, c / 8) + (c % 8) * (int)sizeof(T));
+  else return reinterpret_cast<const T*>(tile) + r * ld_row + c;
+}
+
 //
 // NT: the query-side nodes are the forward's own (saved by the caller's
 // forward pass over (k, v)), which hold the transposes of the nodes over
@@ -1508,10 +1535,13 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
   const int L = a.L;
   const int NI = L - LOG2C - 1;                                // levels above the chunk
   const BwdFusedLds lay = bwd_fused_lds(C, D, sizeof(E), L);
-  const E* Qs = reinterpret_cast<const E*>(smem + lay.q);
-  const E* Ks = reinterpret_cast<const E*>(smem + lay.k);
-  const E* Vs = reinterpret_cast<const E*>(smem + lay.v);
-  const E* Gs = reinterpret_cast<const E*>(smem + lay.g);
+  // d = 64: the chunk's tiles arrive by direct global-to-LDS loads into
+  // swizzled rows (inside the padded regions of the plan)
+  constexpr bool DIR = BF16 && D == 64 && C >= 32;
+  const unsigned char* Qt = smem + lay.q;
+  const unsigned char* Kt = smem + lay.k;
+  const unsigned char* Vt = smem + lay.v;
+  const unsigned char* Gt = smem + lay.g;
   E* S0 = reinterpret_cast<E*>(smem + lay.s0);                 // dS by query row
   E* S1 = reinterpret_cast<E*>(smem + lay.s1);                 // dS^T by key row
   E* S2 = reinterpret_cast<E*>(smem + lay.s2);                 // P^T by key row
@@ -1534,7 +1564,40 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
   const int64_t gam = c / G, cg0 = gam * G;
   const int ci = (int)(c - cg0);
 
-  bwd_load_chunk<BF16, C, D, NT2>(a, smem, lay, bh, tc, nv);
+  if constexpr (DIR) {
+    constexpr int ROWB = 2 * D, GPR = ROWB / 16, RPR = 1024 / ROWB, RUNS = C * ROWB / 1024;
+    static_assert(RPR == 8 && (4 * RUNS) % NW2 == 0, "1 KB runs of eight rows, dealt evenly over the waves");
+    const unsigned char* src[4] = {static_cast<const unsigned char*>(a.q), static_cast<const unsigned char*>(a.k),
+                                   static_cast<const unsigned char*>(a.v), static_cast<const unsigned char*>(a.dout)};
+    const int dst[4] = {lay.q, lay.k, lay.v, lay.g};
+    const size_t cbase = (size_t)(bh * T + tc) * ROWB;
+    if (nv == C) {
+      // lane l fills granule l mod GPR of row l / GPR of each run with the
+      // logical granule that XORs to it (the same offset in every run)
+      const int lrow = lane / GPR, lg16 = lane % GPR;
+      const unsigned off = (unsigned)(lrow * ROWB + ((lg16 ^ (lrow & 7)) << 4));
+#pragma unroll
+      for (int k = 0; k < 4 * RUNS / NW2; ++k) {
+        const int run = wg + k * NW2;              // wave-uniform
+        const int t = run / RUNS, ri = run % RUNS;
+        __builtin_amdgcn_global_load_lds(src[t] + cbase + (unsigned)(ri * 1024) + off,
+                                         (__attribute__((address_space(3))) void*)(smem + dst[t] + ri * 1024), 16, 0, 0);
+      }
+    } else {
+      // the partial last chunk: granule copies, zeros past the sequence
+      for (int i = tid; i < 4 * C * GPR; i += NT2) {
+        const int t = i / (C * GPR), rem = i % (C * GPR), r = rem / GPR, g = rem % GPR;
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (r < nv) x = *reinterpret_cast<const uint4*>(src[t] + cbase + (size_t)r * ROWB + g * 16);
+        *reinterpret_cast<uint4*>(smem + dst[t] + swz_gran<D>(r, g)) = x;
+      }
+    }
+    const float* lg = a.lam + (bh * T + tc) * L;
+    float* lamW = reinterpret_cast<float*>(smem + lay.lam);
+    for (int idx = tid; idx < C * L; idx += NT2) lamW[idx] = idx < nv * L ? lg[idx] : 0.f;
+  } else {
+    bwd_load_chunk<BF16, C, D, NT2>(a, smem, lay, bh, tc, nv);
+  }
   if (wg == 0) {
     // in-chunk inclusive prefix of log2(a), and the gate from each key to the
     // chunk end
@@ -1546,6 +1609,7 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
       e2c[lane] = __builtin_amdgcn_exp2f(tot - y);
     }
   }
+  if constexpr (DIR) __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
   __syncthreads();
 
   // ---- phase 1: tile tau = (query block qb, key block kb <= qb), S and dP
@@ -1560,10 +1624,10 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
 #pragma unroll
     for (int s = 0; s < KSD; ++s) {
       const int k0 = s * KST + lq * KPL;
-      const auto kf = EL::template load_k<D>(Ks + (16 * kb + lr) * lay.ld_row + k0, k0);
-      const auto qf = EL::template load_k<D>(Qs + (16 * qb + lr) * lay.ld_row + k0, k0);
-      const auto vf = EL::template load_k<D>(Vs + (16 * kb + lr) * lay.ld_row + k0, k0);
-      const auto gf = EL::template load_k<D>(Gs + (16 * qb + lr) * lay.ld_row + k0, k0);
+      const auto kf = fused_row<BF16, D, DIR>(Kt, lay.ld_row, 16 * kb + lr, k0);
+      const auto qf = fused_row<BF16, D, DIR>(Qt, lay.ld_row, 16 * qb + lr, k0);
+      const auto vf = fused_row<BF16, D, DIR>(Vt, lay.ld_row, 16 * kb + lr, k0);
+      const auto gf = fused_row<BF16, D, DIR>(Gt, lay.ld_row, 16 * qb + lr, k0);
       sq = EL::mma(kf, qf, sq);
       dpq = EL::mma(vf, gf, dpq);
       sk = EL::mma(qf, kf, sk);
@@ -1726,7 +1790,7 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
         for (int s = 0; s < KSC; ++s)
 #pragma unroll
           for (int n = 0; n < NCB; ++n)
-            kt[s][n] = gather_col<BF16, C>(Ks, lay.ld_row, s * KST + lq * KPL, 16 * (cb0 + n) + lr);
+            kt[s][n] = fused_col<BF16, C, D, DIR>(Kt, lay.ld_row, s * KST, 16 * (cb0 + n), lane);
 #pragma unroll
         for (int rb = 0; rb < QB; ++rb) {
 #pragma unroll
@@ -1746,7 +1810,7 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
       for (int rb = 0; rb < QB; ++rb)
 #pragma unroll
         for (int n = 0; n < NCB; ++n) {
-          const E* qrow = Qs + (16 * rb + lr) * lay.ld_row + 16 * (cb0 + n) + 4 * lq;
+          const E* qrow = fused_quad<BF16, D, DIR>(Qt, lay.ld_row, 16 * rb + lr, 16 * (cb0 + n) + 4 * lq);
 #pragma unroll
           for (int i = 0; i < 4; ++i) qv[rb][n][i] = qrow[i];
         }
@@ -1763,7 +1827,7 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
 #pragma unroll
           for (int s2 = 0; s2 < KSD; ++s2) {
             const int k0 = s2 * KST + lq * KPL;
-            const auto gf = EL::template load_k<D>(Gs + r * lay.ld_row + k0, k0);
+            const auto gf = fused_row<BF16, D, DIR>(Gt, lay.ld_row, r, k0);
 #pragma unroll
             for (int n = 0; n < NCB; ++n) tmp[n] = EL::mma(nfr[s2][n], gf, tmp[n]);
           }
@@ -1904,14 +1968,14 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
       // dk = dS^T Q and dv = P^T dout: columns of Q and of dout as the A operand
 #pragma unroll
       for (int side = 0; side < 2; ++side) {
-        const E* X = side == 0 ? Qs : Gs;
+        const unsigned char* X = side == 0 ? Qt : Gt;
         const E* SS = side == 0 ? S1 : S2;
         Frag ft[KSC][NCB];
 #pragma unroll
         for (int s = 0; s < KSC; ++s)
 #pragma unroll
           for (int n = 0; n < NCB; ++n)
-            ft[s][n] = gather_col<BF16, C>(X, lay.ld_row, s * KST + lq * KPL, 16 * (cb0 + n) + lr);
+            ft[s][n] = fused_col<BF16, C, D, DIR>(X, lay.ld_row, s * KST, 16 * (cb0 + n), lane);
 #pragma unroll
         for (int kb = 0; kb < QB; ++kb) {
 #pragma unroll
@@ -1946,7 +2010,7 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
 #pragma unroll
           for (int s2 = 0; s2 < KSD; ++s2) {
             const int k0 = s2 * KST + lq * KPL;
-            const auto vf = EL::template load_k<D>(Vs + skr * lay.ld_row + k0, k0);
+            const auto vf = fused_row<BF16, D, DIR>(Vt, lay.ld_row, skr, k0);
 #pragma unroll
             for (int n = 0; n < NCB; ++n) tk[n] = EL::mma(rf[s2][n], vf, tk[n]);
           }
@@ -1967,7 +2031,7 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
 #pragma unroll
           for (int s2 = 0; s2 < KSD; ++s2) {
             const int k0 = s2 * KST + lq * KPL;
-            const auto kf = EL::template load_k<D>(Ks + skr * lay.ld_row + k0, k0);
+            const auto kf = fused_row<BF16, D, DIR>(Kt, lay.ld_row, skr, k0);
 #pragma unroll
             for (int n = 0; n < NCB; ++n) tv[n] = EL::mma(rt[s2][n], kf, tv[n]);
           }
@@ -1986,7 +2050,7 @@ __global__ __launch_bounds__(128 * bwd_waves(C)) void bwd_chunk_fused(BwdArgs a)
         float cs = 0.f;
 #pragma unroll
         for (int n = 0; n < NCB; ++n) {
-          const E* vrow = Vs + skr * lay.ld_row + 16 * (cb0 + n) + 4 * lq;
+          const E* vrow = fused_quad<BF16, D, DIR>(Vt, lay.ld_row, skr, 16 * (cb0 + n) + 4 * lq);
 #pragma unroll
           for (int i = 0; i < 4; ++i) cs += av[kb][n][i] * EL::to_f32(vrow[i]);
         }
