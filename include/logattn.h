@@ -283,9 +283,10 @@ LA_API int loglinear_bwd(const void* q, const void* k, const void* v, const floa
  * its forward's workspace can hand it over, and the backward skips building
  * that structure again.
  *
- *   fwd_workspace        the workspace of an earlier loglinear_fwd call on the
- *                        same q, k, v, log_a and lambda (same B, H, T, dk, dv,
- *                        C, L and dtype), not written since; read only.
+ *   fwd_workspace        the workspace of an earlier loglinear_fwd (or
+ *                        loglinear_fwd_state) call on the same q, k, v, log_a
+ *                        and lambda (same B, H, T, dk, dv, C, L and dtype),
+ *                        not written since; read only.
  *                        At least loglinear_fwd_workspace() bytes, 256-byte
  *                        aligned (may be null when that size is 0).
  *   everything else      as for loglinear_bwd; workspace is this call's own
