@@ -1177,7 +1177,7 @@ void bwd_chunk_dkv(BwdArgs a) {
   using E = typename EL::T;
   using Frag = typename EL::Frag;
   constexpr int QB = SH::QB, DB = SH::DB, KSD = SH::KSD, KSC = SH::KSC, NCB = SH::NCB, NW = SH::NW, KT = SH::KT;
-  constexpr int KPL = EL::kPerLane, KST = EL::kStep, LOG2C = SH::LOG2C;
+  constexpr int KPL = EL::kPerLane, KST = EL::kStep;
   constexpr int G = state_group(D), LOG2G = cilog2(G);
   constexpr int NPRE = 1;                                      // node fragment buffers
   extern __shared__ __align__(16) unsigned char smem[];

@@ -451,7 +451,7 @@ __device__ __forceinline__ bool gdn_prep_chunk(const GdnArgs& a, unsigned char* 
   using EL = Elem<BF16>;
   using E = typename EL::T;
   constexpr int es = sizeof(E);
-  constexpr int LDD = gdn_lde(D, es), LDC = gdn_lde(C, es), LF = gdn_lde(C, 4);
+  constexpr int LDD = gdn_lde(D, es), LF = gdn_lde(C, 4);
   constexpr GdnPrepLds LY = gdn_prep_lds(C, D, es);
   // K row-major (padded), then the solve's scratch, then U^T; the token-major
   // tiles K^T, (gated beta V)^T (then W^T) and (beta K)^T are swizzled
