@@ -169,23 +169,26 @@ def test_split_key_side_matches_fused(d):
     check(x32, dout, C, "bf16", dev, f"split key side d={d} L=32")
 
 
-@pytest.mark.parametrize("d, C", [(64, 64), (64, 32), (32, 64), (16, 32), (128, 64)])
-def test_backward_from_forward_workspace(d, C):
+@pytest.mark.parametrize("d, C, T", [(64, 64, 4096 + 64 * 5 + 11), (64, 32, 4096 + 64 * 5 + 11),
+                                     (32, 64, 4096 + 64 * 5 + 11), (16, 32, 4096 + 64 * 5 + 11),
+                                     (128, 64, 4096 + 64 * 5 + 11), (64, 64, 64), (64, 64, 65), (64, 32, 700)])
+def test_backward_from_forward_workspace(d, C, T):
     """loglinear_bwd_from_fwd: the backward reading the forward's bucket
     nodes (their transposes serve the query side) instead of building the
-    structure over (v, k).  dk and dv come from the key side alone, so they
+    structure over (v, k); full groups and a ragged tail, one exact chunk, a
+    second chunk of one token (no node at all), a few chunks (no full group).  dk and dv come from the key side alone, so they
     are the plain backward's bits; dq, dlambda and dlog_a go through the
     forward's nodes (rounded with the other operand gated) and match the
     oracle.  At d = 128 the fused kernel does not run and the call is the
     plain backward, bit for bit."""
     dev = need_gpu()
     import fenwick_tree_hierarchical_amd as la
-    x, dout = case(4096 + 64 * 5 + 11, d, "bf16", "weak_decay", seed=8)
-    label = f"from fwd d={d} C={C}"
+    x, dout = case(T, d, "bf16", "weak_decay", seed=8)
+    label = f"from fwd d={d} C={C} T={T}"
     say(f"bwd {label}: shape={tuple(x['q'].shape)}")
     plain = gpu_bwd(x, dout, C, dev)
     xd = {k: v.to(dev) for k, v in x.items()}
-    B, H, T, _ = x["q"].shape
+    B, H = x["q"].shape[:2]
     fws = torch.empty(max(la.loglinear_fwd_workspace(B, H, T, d, d, C, torch.bfloat16), 1), dtype=torch.uint8,
                       device=dev)
     la.loglinear_fwd(xd["q"], xd["k"], xd["v"], xd["log_a"], xd["lam"], chunk=C, workspace=fws)
