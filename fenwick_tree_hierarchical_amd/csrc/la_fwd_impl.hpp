@@ -1075,19 +1075,46 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
     }
   }
 
-  // ---- store: four consecutive output columns of one row per lane and block
+  // ---- store.  Direct-load tiles whose columns every wave shares: the output
+  // tile is staged in the dead Q (or late V) tile, swizzled like it, and
+  // written as whole rows, 16 bytes per lane (1 KB of rows per wave
+  // instruction); else four consecutive output columns of one row per lane
+  // and block.
+  constexpr bool STAGE_OUT = DIRECT && NW * NCB == DB;
+  if constexpr (STAGE_OUT) {
+    unsigned char* Ot = smem + lay.q;
+    __syncthreads();                               // every wave is past its Q and V reads
 #pragma unroll
-  for (int rb = 0; rb < QB; ++rb) {
-    const int r = 16 * rb + lr;
-    if (r < nv) {
+    for (int rb = 0; rb < QB; ++rb) {
+      const int r = 16 * rb + lr;
 #pragma unroll
       for (int n = 0; n < NCB; ++n) {
-        E* o = og + (int64_t)r * D + 16 * (cb0 + n) + 4 * lq;
-        if constexpr (BF16) {
-          *reinterpret_cast<u16x4*>(o) = u16x4{f32_to_bf16(acc[rb][n][0]), f32_to_bf16(acc[rb][n][1]),
-                                               f32_to_bf16(acc[rb][n][2]), f32_to_bf16(acc[rb][n][3])};
-        } else {
-          *reinterpret_cast<float4*>(o) = make_float4(acc[rb][n][0], acc[rb][n][1], acc[rb][n][2], acc[rb][n][3]);
+        const int c = 16 * (cb0 + n) + 4 * lq;
+        *reinterpret_cast<u16x4*>(Ot + swz_gran<D>(r, c / 8) + (c % 8) * 2) =
+            u16x4{f32_to_bf16(acc[rb][n][0]), f32_to_bf16(acc[rb][n][1]), f32_to_bf16(acc[rb][n][2]),
+                  f32_to_bf16(acc[rb][n][3])};
+      }
+    }
+    __syncthreads();
+    constexpr int GPR = 2 * D / 16;
+    for (int idx = tid; idx < C * GPR; idx += SH::NT) {
+      const int r = idx / GPR, g = idx % GPR;
+      if (r < nv) *reinterpret_cast<uint4*>(og + (int64_t)r * D + g * 8) = *reinterpret_cast<const uint4*>(Ot + swz_gran<D>(r, g));
+    }
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < QB; ++rb) {
+      const int r = 16 * rb + lr;
+      if (r < nv) {
+#pragma unroll
+        for (int n = 0; n < NCB; ++n) {
+          E* o = og + (int64_t)r * D + 16 * (cb0 + n) + 4 * lq;
+          if constexpr (BF16) {
+            *reinterpret_cast<u16x4*>(o) = u16x4{f32_to_bf16(acc[rb][n][0]), f32_to_bf16(acc[rb][n][1]),
+                                                 f32_to_bf16(acc[rb][n][2]), f32_to_bf16(acc[rb][n][3])};
+          } else {
+            *reinterpret_cast<float4*>(o) = make_float4(acc[rb][n][0], acc[rb][n][1], acc[rb][n][2], acc[rb][n][3]);
+          }
         }
       }
     }
