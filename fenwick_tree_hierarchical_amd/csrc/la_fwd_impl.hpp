@@ -537,8 +537,9 @@ __device__ __forceinline__ bf16x8 swz_tr_frag(const unsigned char* tile, int k0,
 // row slice is one contiguous store.
 //
 // VL (late V): the level contractions run before P V, and V is loaded into
-// the Q tile once every wave is past its Q reads, so the tiles take one 32 KB
-// buffer less (C = d = 128, where that lets two workgroups share a CU).
+// the Q tile once every wave is past its Q reads, so the tiles take one buffer
+// less (32 KB at C = d = 128, where that lets two workgroups share a CU; 8 KB
+// at C = d = 64, seven workgroups per CU in place of five).
 template <bool BF16, int C, int D, bool FULL, bool VL = false>
 __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned char* smem, int64_t item) {
   using SH = ChunkShape<BF16, C, D>;
@@ -1147,10 +1148,13 @@ void fwd_chunk_output(FwdArgs a) {
   else chunk_output_body<BF16, C, D, false>(a, smem, item);
 }
 
-// The late-V output kernel (bfloat16, C = d = 128): two workgroups per CU,
-// so the register budget of four waves per SIMD.
+// The late-V output kernel (bfloat16, C = d = 64 or 128).  At C = 128 two
+// workgroups of eight waves share a CU: the register budget of four waves per
+// SIMD.  At C = 64 the LDS admits seven workgroups of four waves, so the
+// registers decide: the budget of six waves per SIMD (80 VGPRs).
+constexpr int output_vlate_min_waves(int C) { return C == 64 ? 6 : 4; }
 template <bool BF16, int C, int D>
-__global__ __launch_bounds__(64 * output_waves(C)) __attribute__((amdgpu_waves_per_eu(4, 8)))
+__global__ __launch_bounds__(64 * output_waves(C)) __attribute__((amdgpu_waves_per_eu(output_vlate_min_waves(C), 8)))
 void fwd_chunk_output_vlate(FwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t item = xcd_item(blockIdx.x, gridDim.x);

@@ -127,10 +127,10 @@ LA_HD constexpr OutLds output_lds(int C, int D, int es, int L) {
   o.total = off;
   return o;
 }
-// The late-V variant of the output kernel (bfloat16, C = d = 128): the level
-// contractions run before P V, so V is loaded into the Q tile once Q is dead
-// and the workgroup needs one 32 KB tile less.
-LA_HD constexpr bool output_vlate_shape(int C, int D, int es) { return es == 2 && C == 128 && D == 128; }
+// The late-V variant of the output kernel (bfloat16, C = d = 64 or 128): the
+// level contractions run before P V, so V is loaded into the Q tile once Q is
+// dead and the workgroup needs one tile less (8 KB or 32 KB).
+LA_HD constexpr bool output_vlate_shape(int C, int D, int es) { return es == 2 && ((C == 128 && D == 128) || (C == 64 && D == 64)); }
 LA_HD constexpr OutLds output_lds_vlate(int C, int D, int es, int L) {
   OutLds o = output_lds(C, D, es, L);
   const int vbytes = (C * o.ld_v * es + 255) / 256 * 256;
