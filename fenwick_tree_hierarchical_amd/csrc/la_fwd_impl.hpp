@@ -1076,11 +1076,11 @@ __device__ __forceinline__ void chunk_output_body(const FwdArgs& a, unsigned cha
     }
   }
 
-  // ---- store.  Direct-load tiles whose columns every wave shares: the output
-  // tile is staged in the dead Q (or late V) tile, swizzled like it, and
-  // written as whole rows, 16 bytes per lane (1 KB of rows per wave
-  // instruction); else four consecutive output columns of one row per lane
-  // and block.
+  // ---- store.  Direct-load tiles whose column blocks the waves cover
+  // exactly (every wave owns output columns): the output tile is staged in the
+  // dead Q (or late V) tile, swizzled like it, and written as whole rows, 16
+  // bytes per lane (1 KB of rows per wave instruction); else four consecutive
+  // output columns of one row per lane and block.
   constexpr bool STAGE_OUT = DIRECT && NW * NCB == DB;
   if constexpr (STAGE_OUT) {
     unsigned char* Ot = smem + lay.q;
